@@ -1,0 +1,95 @@
+/*
+ * w4a8_oracle.h -- plain CPU oracle for the W4AFP8 fused-MoE forward.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may include, link
+ * or call this code: only the tests, the smoke check and the CPU-baseline leg
+ * of the benchmark use it.  It shares no code, header, table or constant with
+ * the HIP library.
+ *
+ * Every routine is the plain definition of one step of the method, written
+ * for readability: single-threaded, fp64 where the method accumulates, and
+ * no blocking, fusion or reordering beyond what the definition states.
+ *
+ * Sources (page title, then the passage):
+ *   [P2] SGLang PR #7762 "feat: support DeepSeek-R1-W4AFP8 model with ep-moe
+ *        mode" -- "Model Info" (INT4 expert weights, FP8 activations),
+ *        "Cutlass W4A8 MoE" / "Kernel" (pre-reorder, w4a8 grouped GEMMs,
+ *        SiLU-and-Mul, post-reorder), the review thread on
+ *        run_cutlass_moe_ep_preproess (stable sort of the local top-k ids,
+ *        seg_indptr, src2dst), the review thread on expert_map, and the
+ *        review thread on the hard-coded group size 128.
+ *   [P3] SGLang PR #37796 "feat(moe_wna16): 2-bit experts, expert streaming,
+ *        N-contiguous GEMV" -- part-1 notes on the fp8 KV write path
+ *        (saturate to +-448 before the e4m3 cast).
+ *   [P4] DeepGEMM PR #53 "SM90 (Hopper) FP4 MegaMoE fused kernel with swapAB
+ *        small-batch path" -- commit note dropping the UE8M0 activation scale
+ *        (fp32 per-token activation scales; amax clamped before the
+ *        reciprocal 448/amax) and the "Changes" list (L1 GEMM -> SwiGLU ->
+ *        per-token FP8 requant -> L2 GEMM -> combine).
+ *
+ * Readings where the pages are silent (each fixed by the project spec):
+ *   - amax clamp constant 1e-10f; dequant scale amax_c/448; codes use the
+ *     reciprocal inv = 448/amax_c.
+ *   - int4: two's complement nibbles, low nibble = even k, no zero point.
+ *   - gate rows [0, I), up rows [I, 2I) of w13; plain SwiGLU (no clamp).
+ *   - top-k weights applied in the combine, after the down GEMM.
+ *   - non-local top-k ids are skipped; a token with no local pair outputs +0.
+ *
+ * Layouts (row-major, K contiguous):
+ *   activations bf16 [T, H] (uint16 bit patterns);
+ *   w13 [E_l, 2I, H/2] bytes, s13 [E_l, 2I, H/128] fp32;
+ *   w2  [E_l, H, I/2] bytes,  s2  [E_l, H, I/128] fp32.
+ */
+#ifndef W4A8_ORACLE_H
+#define W4A8_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ORC_GROUP 128
+
+/* ---- codecs ---- */
+double   orc_e4m3_decode(uint8_t code);
+uint8_t  orc_e4m3_encode(float v);
+int      orc_int4_value(uint8_t byte, int odd);
+double   orc_bf16_to_double(uint16_t bits);
+uint16_t orc_bf16_from_double(double v);
+
+/* ---- step: dynamic per-token-per-128 activation quantisation ---- */
+void orc_quantize_block(const float* x, uint8_t* codes, float* scale);
+void orc_quantize_rows_bf16(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                            uint8_t* codes, float* scales);
+void orc_quantize_rows_f32(const float* x, int64_t M, int64_t K,
+                           uint8_t* codes, float* scales);
+
+/* ---- step: routing permutation (align) ---- */
+int orc_moe_align(const int32_t* topk_ids, int64_t T, int64_t topk,
+                  int64_t expert_begin, int64_t num_local_experts, int64_t block_m,
+                  int32_t* expert_counts, int32_t* expert_offsets,
+                  int32_t* sorted_pair_ids, int32_t* src2dst,
+                  int32_t* block_expert, int32_t* block_row, int32_t* num_blocks);
+
+/* ---- step: W4A8 GEMM with per-group scale promotion ---- */
+void orc_gemm_f64(const uint8_t* a, const float* sa, int64_t M, int64_t K,
+                  const uint8_t* w, const float* sw, int64_t N, double* y);
+void orc_gemm_bf16(const uint8_t* a, const float* sa, int64_t M, int64_t K,
+                   const uint8_t* w, const float* sw, int64_t N, uint16_t* out);
+
+/* ---- the whole forward: align, quant, GEMM1, SwiGLU, requant, GEMM2, combine ----
+ * qh [P, I], sh [P, I/128] and y2 [P, H] (pair order = sorted order) are
+ * optional diagnostic outputs; pass NULL to skip.  P <= T*topk. */
+int orc_fused_moe(const uint16_t* hidden, int64_t T, int64_t H,
+                  const int32_t* topk_ids, const float* topk_weights, int64_t topk,
+                  int64_t expert_begin, int64_t num_local_experts, int64_t I,
+                  const uint8_t* w13, const float* s13,
+                  const uint8_t* w2, const float* s2,
+                  uint16_t* out,
+                  uint8_t* qh, float* sh, double* y2);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

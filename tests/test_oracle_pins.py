@@ -1,0 +1,433 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Each test ties one oracle routine to a library routine (torch's fp8 and bf16
+casts, numpy's IEEE float32 arithmetic, numpy's stable argsort and fp64
+matmul), a closed form, an invariant, a worked example written out by hand
+(tests/golden/), or brute force on small inputs, so that a plausible mistake
+in the oracle (a dropped term, a wrong sign or index, a transposed operand, a
+wrong constant or rounding rule) fails at least one of them.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from w4a8_moe_grouped_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------------------
+# helpers built on library routines only (never on the oracle)
+# ---------------------------------------------------------------------------
+
+def torch_e4m3_decode(codes):
+    t = torch.from_numpy(np.asarray(codes, np.uint8).copy()).view(torch.float8_e4m3fn)
+    return t.to(torch.float64).numpy()
+
+
+def torch_e4m3_encode(values_f32):
+    """torch's RNE cast (valid for |v| <= 448; beyond that torch returns NaN)."""
+    t = torch.from_numpy(np.asarray(values_f32, np.float32).copy()).to(torch.float8_e4m3fn)
+    return t.view(torch.uint8).numpy()
+
+
+def numpy_int4(bytes_, odd):
+    """Sign-extend a nibble with an arithmetic shift of int8 (no table, no compare)."""
+    b = np.asarray(bytes_, np.uint8)
+    nib = (b >> 4) if odd else (b & 0x0F)
+    return ((nib << 4).astype(np.uint8).view(np.int8) >> 4).astype(np.int64)
+
+
+def dequant_rows(codes, scales):
+    """fp64 matrix dec(code) * scale, broadcast over each 128-group."""
+    d = torch_e4m3_decode(codes)
+    s = np.repeat(np.asarray(scales, np.float64), 128, axis=1)
+    return d * s
+
+
+def dequant_w(w, sw):
+    K = w.shape[1] * 2
+    vals = np.empty((w.shape[0], K), np.float64)
+    vals[:, 0::2] = numpy_int4(w, 0)
+    vals[:, 1::2] = numpy_int4(w, 1)
+    return vals * np.repeat(np.asarray(sw, np.float64), 128, axis=1)
+
+
+def read_golden(name):
+    vals = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            k, v = line.split()
+            vals[k] = v
+    return vals
+
+
+# ---------------------------------------------------------------------------
+# codecs
+# ---------------------------------------------------------------------------
+
+def test_e4m3_decode_all_codes_match_torch(orc):
+    codes = np.arange(256, dtype=np.uint8)
+    mine = orc.e4m3_decode(codes)
+    ref = torch_e4m3_decode(codes)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(mine), nan)
+    assert set(np.nonzero(nan)[0].tolist()) == {0x7F, 0xFF}
+    assert np.array_equal(mine[~nan], ref[~nan])
+    assert mine[0x7E] == 448.0 and mine[0x01] == 2.0 ** -9
+
+
+def test_e4m3_encode_matches_torch_on_every_bf16_value(orc):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    vals = synth.bf16_bits_to_f32(bits)
+    ok = np.isfinite(vals) & (np.abs(vals) <= 448.0)
+    vals = vals[ok]
+    assert np.array_equal(orc.e4m3_encode(vals), torch_e4m3_encode(vals))
+
+
+def test_e4m3_encode_matches_torch_on_random_fp32_and_ties(orc):
+    rng = np.random.default_rng(1)
+    v = np.concatenate([
+        rng.uniform(-448, 448, 20000),
+        rng.uniform(-1, 1, 20000) * 2.0 ** rng.integers(-12, 0, 20000),
+    ]).astype(np.float32)
+    # every midpoint between consecutive finite codes, and one ulp either side
+    pos = torch_e4m3_decode(np.arange(0x7F, dtype=np.uint8))
+    mids = ((pos[:-1] + pos[1:]) / 2).astype(np.float32)
+    near = np.concatenate([mids, np.nextafter(mids, np.float32(0)), np.nextafter(mids, np.float32(1e9))])
+    v = np.concatenate([v, near, -near]).astype(np.float32)
+    assert np.array_equal(orc.e4m3_encode(v), torch_e4m3_encode(v))
+
+
+def test_e4m3_encode_saturates_beyond_448(orc):
+    # torch returns NaN above 464; the pages' rule clamps to +-448 first
+    v = np.array([448.0, 448.5, 463.9, 464.0, 500.0, 1e6, 3e38], np.float32)
+    assert orc.e4m3_encode(v).tolist() == [0x7E] * len(v)
+    assert orc.e4m3_encode(-v).tolist() == [0xFE] * len(v)
+
+
+def test_e4m3_landmarks(orc):
+    cases = [(1.0, 0x38), (2.0, 0x40), (7.0, 0x4E), (8.0, 0x50), (-8.0, 0xD0), (2.0 ** -6, 0x08),
+             (2.0 ** -9, 0x01), (2.0 ** -10, 0x00), (3 * 2.0 ** -10, 0x02), (5 * 2.0 ** -10, 0x02),
+             (2.0 ** -11, 0x00), (0.0, 0x00), (-0.0, 0x80), (-2.0 ** -12, 0x80)]
+    for v, c in cases:
+        assert orc.e4m3_encode(np.float32(v)) == c, (v, hex(c))
+
+
+def test_int4_values_all_bytes(orc):
+    for b in range(256):
+        assert orc.int4_value(b, 0) == numpy_int4(b, 0)
+        assert orc.int4_value(b, 1) == numpy_int4(b, 1)
+    assert [orc.int4_value(n, 0) for n in range(16)] == [0, 1, 2, 3, 4, 5, 6, 7, -8, -7, -6, -5, -4, -3, -2, -1]
+
+
+def test_bf16_round_matches_torch_on_fp32(orc):
+    rng = np.random.default_rng(2)
+    bits = rng.integers(0, 2 ** 32, 50000, dtype=np.uint64).astype(np.uint32)
+    f = bits.view(np.float32)
+    f = f[np.isfinite(f) & (np.abs(f) < 3.3e38)]
+    mine = orc.bf16_from_double(f.astype(np.float64))
+    ref = torch.from_numpy(f.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(mine, ref)
+    back = orc.bf16_to_double(ref)
+    assert np.array_equal(back, torch.from_numpy(ref.view(np.int16).copy()).view(torch.bfloat16).double().numpy())
+
+
+def test_bf16_round_from_double_rounds_once(orc):
+    # 1 + 2^-8 + 2^-30: one rounding goes up to 1 + 2^-7; via fp32 it would tie down to 1.0
+    v = 1.0 + 2.0 ** -8 + 2.0 ** -30
+    assert orc.bf16_from_double(v) == 0x3F81
+    assert orc.bf16_from_double(1.0 + 2.0 ** -8) == 0x3F80          # exact tie -> even
+    assert orc.bf16_from_double(1.0 + 3 * 2.0 ** -8) == 0x3F82      # exact tie -> even (up)
+    assert orc.bf16_from_double(-(1.0 + 2.0 ** -8 + 2.0 ** -30)) == 0xBF81
+
+
+# ---------------------------------------------------------------------------
+# activation quantisation
+# ---------------------------------------------------------------------------
+
+def test_quant_single_nonzero_closed_form(orc):
+    rng = np.random.default_rng(3)
+    vals = rng.normal(size=64).astype(np.float32) * 2.0 ** rng.integers(-20, 20, 64)
+    x = np.zeros((64, 128), np.float32)
+    pos = rng.integers(0, 128, 64)
+    x[np.arange(64), pos] = vals
+    bits = synth.to_bf16_bits(x)
+    xv = synth.bf16_bits_to_f32(bits)
+    codes, s = orc.quantize_bf16(bits)
+    for r in range(64):
+        v = xv[r, pos[r]]
+        assert codes[r, pos[r]] == (0xFE if v < 0 else 0x7E)
+        assert s[r, 0] == np.float32(abs(v)) / np.float32(448.0)
+        others = np.delete(codes[r], pos[r])
+        assert np.all(others == 0)
+
+
+def test_quant_zero_block_uses_clamped_amax(orc):
+    codes, s = orc.quantize_f32(np.zeros((2, 256), np.float32))
+    assert np.all(codes == 0)
+    assert np.all(s == np.float32(1e-10) / np.float32(448.0))
+    # a block far below the clamp keeps finite scales and codes (no 0*inf)
+    tiny = np.full((1, 128), 1e-30, np.float32)
+    codes, s = orc.quantize_f32(tiny)
+    assert s[0, 0] == np.float32(1e-10) / np.float32(448.0) and np.all(codes == 0)
+
+
+def test_quant_power_of_two_invariance(orc):
+    rng = np.random.default_rng(4)
+    x = rng.normal(size=(8, 512)).astype(np.float32)
+    c0, s0 = orc.quantize_f32(x)
+    for j in (-20, -3, 1, 7, 30):
+        c, s = orc.quantize_f32(x * np.float32(2.0 ** j))
+        assert np.array_equal(c, c0)
+        assert np.array_equal(s, s0 * np.float32(2.0 ** j))
+
+
+def test_quant_dequant_error_bound(orc):
+    rng = np.random.default_rng(5)
+    x = (rng.normal(size=(64, 1024)) * np.exp(rng.normal(size=(64, 1024)) * 3)).astype(np.float32)
+    codes, s = orc.quantize_f32(x)
+    deq = dequant_rows(codes, s)
+    sfull = np.repeat(s.astype(np.float64), 128, axis=1)
+    scaled = np.abs(x.astype(np.float64)) / sfull  # |x| * 448 / amax, in code units
+    err = np.abs(deq - x.astype(np.float64))
+    normal = scaled >= 2.0 ** -6
+    assert np.all(err[normal] <= (2.0 ** -4 + 2.0 ** -20) * np.abs(x[normal]))
+    assert np.all(err[~normal] <= (2.0 ** -10 + 2.0 ** -20) * sfull[~normal])
+    assert normal.mean() > 0.5 and (~normal).sum() > 1000
+
+
+def test_quant_scale_divide_exhaustive_over_bf16_amax(orc):
+    bits = np.arange(0x0001, 0x7F80, dtype=np.uint16)  # every positive finite bf16
+    amax = synth.bf16_bits_to_f32(bits)
+    x = np.zeros((bits.size, 128), np.uint16)
+    x[:, 5] = bits
+    x[:, 77] = bits | 0x8000  # -amax as well
+    codes, s = orc.quantize_bf16(x)
+    amax_c = np.maximum(amax, np.float32(1e-10))
+    assert np.array_equal(s[:, 0], amax_c / np.float32(448.0))
+    big = amax >= np.float32(1e-10)
+    assert np.all(codes[big, 5] == 0x7E) and np.all(codes[big, 77] == 0xFE)
+
+
+def test_quant_uses_reciprocal_then_multiply(orc):
+    # find (amax, x) where fl(x * fl(448/amax)) and fl(x / fl(amax/448)) land on
+    # different e4m3 codes; the pages put the reciprocal 448/amax in the path.
+    # Candidates sit within an ulp of the pre-image of an e4m3 rounding midpoint.
+    rng = np.random.default_rng(6)
+    a = rng.uniform(1, 2, 4000).astype(np.float32)
+    pos = torch_e4m3_decode(np.arange(0x7F, dtype=np.uint8))
+    mids = (pos[:-1] + pos[1:]) / 2
+    m = mids[rng.integers(40, mids.size, a.size)]
+    x0 = (m * a.astype(np.float64) / 448.0).astype(np.float32)
+    a = np.repeat(a, 3)
+    xs = np.stack([np.nextafter(x0, np.float32(0)), x0, np.nextafter(x0, np.float32(9))], 1).ravel()
+    p_mul = xs * (np.float32(448.0) / a)
+    p_div = xs / (a / np.float32(448.0))
+    diff = torch_e4m3_encode(p_mul) != torch_e4m3_encode(p_div)
+    idx = np.nonzero(diff & (xs < a))[0][:64]
+    assert idx.size > 8
+    blocks = np.zeros((idx.size, 128), np.float32)
+    blocks[:, 0] = a[idx]
+    blocks[:, 1] = xs[idx]
+    codes, _ = orc.quantize_f32(blocks)
+    assert np.array_equal(codes[:, 1], torch_e4m3_encode(p_mul[idx]))
+    assert not np.array_equal(codes[:, 1], torch_e4m3_encode(p_div[idx]))
+
+
+# ---------------------------------------------------------------------------
+# routing permutation
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T,k,eb,E,bm,seed", [
+    (1, 1, 0, 1, 16, 0), (16, 2, 0, 4, 16, 1), (64, 8, 0, 32, 16, 2),
+    (300, 8, 64, 32, 64, 3), (1000, 6, 5, 7, 128, 4), (257, 4, 0, 256, 32, 5)])
+def test_align_against_numpy_stable_sort(orc, T, k, eb, E, bm, seed):
+    rng = np.random.default_rng(seed)
+    ids = rng.integers(-1, max(eb + E + 20, 2), size=(T, k)).astype(np.int32)
+    ids[rng.uniform(size=(T, k)) < 0.05] = -1
+    r = orc.moe_align(ids, eb, E, bm)
+    flat = ids.ravel().astype(np.int64) - eb
+    local = (flat >= 0) & (flat < E)
+    assert np.array_equal(r["counts"], np.bincount(flat[local], minlength=E))
+    assert np.array_equal(r["offsets"], np.concatenate([[0], np.cumsum(r["counts"])]))
+    key = np.where(local, flat, E)  # non-local pairs sort last
+    order = np.argsort(key, kind="stable")[: int(local.sum())]
+    assert np.array_equal(r["sorted_pair_ids"], order)
+    s2d = r["src2dst"]
+    assert np.all(s2d[~local] == -1)
+    assert np.array_equal(r["sorted_pair_ids"][s2d[local]], np.nonzero(local)[0])
+    # blocks tile every segment exactly, in expert order, block_m rows each except the last
+    cover = np.zeros(int(local.sum()), np.int32)
+    for be, br in zip(r["block_expert"], r["block_row"]):
+        lo, hi = r["offsets"][be], r["offsets"][be + 1]
+        assert lo <= br < hi
+        cover[br:min(br + bm, hi)] += 1
+    assert np.all(cover == 1)
+    assert r["num_blocks"] == int(np.sum((r["counts"] + bm - 1) // bm))
+    assert np.all(np.diff(r["block_expert"]) >= 0)
+
+
+# ---------------------------------------------------------------------------
+# GEMM
+# ---------------------------------------------------------------------------
+
+def test_gemm_hand_worked_example(orc):
+    g = read_golden("hand_worked_gemm.txt")
+    x = np.full((1, 128), int(g["x_bf16_bits"], 16), np.uint16)
+    codes, sa = orc.quantize_bf16(x)
+    assert np.all(codes == int(g["code"], 16))
+    assert sa.view(np.uint32)[0, 0] == int(g["s_a_f32_bits"], 16)
+    w = np.full((1, 64), int(g["w_byte"], 16), np.uint8)
+    sw = np.array([[int(g["s_w_f32_bits"], 16)]], np.uint32).view(np.float32)
+    y = orc.gemm_f64(codes, sa, w, sw)
+    assert y[0, 0] == float(g["y_f64"])
+    assert orc.gemm_bf16(codes, sa, w, sw)[0, 0] == int(g["y_bf16_bits"], 16)
+
+
+def test_gemm_alternating_weights_cancel(orc):
+    codes, sa = orc.quantize_f32(np.full((3, 384), 0.37, np.float32))
+    w = np.full((2, 192), 0xF1, np.uint8)  # nibbles +1 (even k), -1 (odd k)
+    sw = np.full((2, 3), 0.011, np.float32)
+    assert np.all(orc.gemm_f64(codes, sa, w, sw) == 0.0)
+
+
+def test_gemm_matches_dequantised_fp64_matmul(orc):
+    rng = np.random.default_rng(7)
+    M, K, N = 5, 640, 33
+    x = rng.normal(size=(M, K)).astype(np.float32) * np.float32(3)
+    codes, sa = orc.quantize_f32(x)
+    w = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    sw = rng.uniform(0.002, 0.02, size=(N, K // 128)).astype(np.float32)
+    y = orc.gemm_f64(codes, sa, w, sw)
+    ref = dequant_rows(codes, sa) @ dequant_w(w, sw).T
+    assert np.max(np.abs(y - ref)) <= 1e-12 * np.max(np.abs(ref))
+
+
+def test_gemm_unit_scales_is_exact_integer_matmul(orc):
+    rng = np.random.default_rng(8)
+    M, K, N = 4, 256, 9
+    codes = rng.integers(0, 0x7F, size=(M, K), dtype=np.uint8)  # finite codes only
+    codes[rng.uniform(size=codes.shape) < 0.5] |= 0x80
+    w = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    y = orc.gemm_f64(codes, np.ones((M, 2), np.float32), w, np.ones((N, 2), np.float32))
+    ref = torch.from_numpy(torch_e4m3_decode(codes)) @ torch.from_numpy(dequant_w(w, np.ones((N, 2)))).T
+    assert np.array_equal(y, ref.numpy())
+
+
+# ---------------------------------------------------------------------------
+# fused MoE
+# ---------------------------------------------------------------------------
+
+def brute_force_moe(d, eb, E):
+    """Dense loop over tokens x top-k, no permutation, fp64 matmuls on fully
+    dequantised operands; the per-row quantiser is the (pinned) oracle's."""
+    import oracle
+    x, ids, tw = d["hidden"], d["topk_ids"], d["topk_weights"]
+    T, H = x.shape
+    I = d["w2"].shape[2] * 2
+    qx, sx = oracle.quantize_bf16(x)
+    A = dequant_rows(qx, sx)
+    out = np.zeros((T, H), np.float64)
+    for t in range(T):
+        for j in range(ids.shape[1]):
+            e = int(ids[t, j]) - eb
+            if not (0 <= e < E):
+                continue
+            y1 = dequant_w(d["w13"][e], d["s13"][e]) @ A[t]
+            g, u = y1[:I], y1[I:]
+            h = (g / (1.0 + np.exp(-g)) * u).astype(np.float32)
+            qh, sh = oracle.quantize_f32(h[None, :])
+            y2 = dequant_w(d["w2"][e], d["s2"][e]) @ dequant_rows(qh, sh)[0]
+            out[t] += np.float64(tw[t, j]) * y2
+    return out
+
+
+@pytest.mark.parametrize("T,H,I,Etot,k,eb,E,seed", [
+    (16, 256, 128, 4, 2, 0, 4, 0), (9, 384, 256, 16, 4, 4, 6, 1), (5, 128, 128, 8, 8, 0, 8, 2)])
+def test_fused_moe_matches_brute_force(orc, T, H, I, Etot, k, eb, E, seed):
+    _, d = synth.random_moe(T, H, I, Etot, k, eb, E, seed)
+    out = orc.fused_moe(d["hidden"], d["topk_ids"], d["topk_weights"], eb, E,
+                        d["w13"], d["s13"], d["w2"], d["s2"])
+    ref = brute_force_moe(d, eb, E)
+    got = synth.bf16_bits_to_f32(out).astype(np.float64)
+    # one bf16 rounding of the same fp64 value (plus fp64 noise)
+    assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-30)
+    assert np.array_equal(out, orc.bf16_from_double(ref))
+
+
+def test_fused_moe_token_permutation_invariance(orc):
+    _, d = synth.random_moe(24, 256, 128, 8, 3, 2, 5, seed=9)
+    out = orc.fused_moe(d["hidden"], d["topk_ids"], d["topk_weights"], 2, 5,
+                        d["w13"], d["s13"], d["w2"], d["s2"])
+    perm = np.random.default_rng(9).permutation(24)
+    out_p = orc.fused_moe(d["hidden"][perm], d["topk_ids"][perm], d["topk_weights"][perm], 2, 5,
+                          d["w13"], d["s13"], d["w2"], d["s2"])
+    assert np.array_equal(out_p, out[perm])
+
+
+def test_fused_moe_single_expert_reduces_to_dense_pieces(orc):
+    cfg, d = synth.random_moe(7, 256, 256, 1, 1, 0, 1, seed=10)
+    ones = np.ones_like(d["topk_weights"])
+    out = orc.fused_moe(d["hidden"], np.zeros_like(d["topk_ids"]), ones, 0, 1,
+                        d["w13"], d["s13"], d["w2"], d["s2"])
+    qx, sx = orc.quantize_bf16(d["hidden"])
+    y1 = orc.gemm_f64(qx, sx, d["w13"][0], d["s13"][0])
+    I = 256
+    h = (y1[:, :I] / (1.0 + np.exp(-y1[:, :I])) * y1[:, I:]).astype(np.float32)
+    qh, sh = orc.quantize_f32(h)
+    y2 = orc.gemm_f64(qh, sh, d["w2"][0], d["s2"][0])
+    assert np.array_equal(out, orc.bf16_from_double(y2))
+
+
+def test_fused_moe_down_scale_doubling_doubles_output(orc):
+    _, d = synth.random_moe(12, 256, 128, 4, 2, 0, 4, seed=11)
+    a = orc.fused_moe(d["hidden"], d["topk_ids"], d["topk_weights"], 0, 4,
+                      d["w13"], d["s13"], d["w2"], d["s2"])
+    b = orc.fused_moe(d["hidden"], d["topk_ids"], d["topk_weights"], 0, 4,
+                      d["w13"], d["s13"], d["w2"], d["s2"] * np.float32(2))
+    assert np.array_equal(synth.bf16_bits_to_f32(b), 2 * synth.bf16_bits_to_f32(a))
+
+
+def test_fused_moe_non_local_tokens_give_zero(orc):
+    _, d = synth.random_moe(10, 256, 128, 16, 2, 0, 4, seed=12)
+    ids = d["topk_ids"].copy()
+    ids[:4] = 9           # experts outside [0, 4)
+    ids[4:6] = -1         # padding ids
+    out = orc.fused_moe(d["hidden"], ids, d["topk_weights"], 0, 4,
+                        d["w13"], d["s13"], d["w2"], d["s2"])
+    assert np.all(out[:6] == 0)
+    local = ((ids[6:] >= 0) & (ids[6:] < 4)).any(axis=1)
+    assert np.all(np.any(out[6:][local] != 0, axis=1))
+
+
+def test_fused_moe_identical_experts_equal_single_expert(orc):
+    cfg, d = synth.random_moe(6, 256, 128, 4, 4, 0, 4, seed=13)
+    for key in ("w13", "s13", "w2", "s2"):
+        d[key] = np.repeat(d[key][:1], 4, axis=0)
+    ids = np.tile(np.arange(4, dtype=np.int32), (6, 1))
+    w = np.random.default_rng(13).uniform(0.1, 1, size=(6, 4))
+    w = (w / w.sum(axis=1, keepdims=True)).astype(np.float32)
+    multi = orc.fused_moe(d["hidden"], ids, w, 0, 4, d["w13"], d["s13"], d["w2"], d["s2"])
+    single = orc.fused_moe(d["hidden"], ids[:, :1], np.ones((6, 1), np.float32), 0, 4,
+                           d["w13"], d["s13"], d["w2"], d["s2"])
+    m = synth.bf16_bits_to_f32(multi).astype(np.float64)
+    s = synth.bf16_bits_to_f32(single).astype(np.float64)
+    assert np.all(np.abs(m - s) <= 2.0 ** -7 * np.abs(s) + 1e-30)
+
+
+def test_fused_moe_intermediates_consistent(orc):
+    _, d = synth.random_moe(8, 256, 128, 4, 2, 0, 4, seed=14)
+    out, inter = orc.fused_moe(d["hidden"], d["topk_ids"], d["topk_weights"], 0, 4,
+                               d["w13"], d["s13"], d["w2"], d["s2"], intermediates=True)
+    r = orc.moe_align(d["topk_ids"], 0, 4, 16)
+    assert inter["qh"].shape[0] == r["offsets"][-1]
+    y2 = orc.gemm_f64(inter["qh"][:1], inter["sh"][:1],
+                      d["w2"][int(np.searchsorted(r["offsets"], 0, side="right") - 1)],
+                      d["s2"][int(np.searchsorted(r["offsets"], 0, side="right") - 1)])
+    assert np.array_equal(y2[0], inter["y2"][0])
