@@ -1,0 +1,233 @@
+#!/usr/bin/env python3
+"""Benchmark of the W4AFP8 fused-MoE forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A step is one w4a8_fused_moe call (align -> quant -> gate_up + SwiGLU +
+requant -> down -> combine) on the decode workload: T=64 tokens, H=7168,
+I=2048, top-8 of 256 experts, this GPU's share = experts 0..31.  Inputs are
+seeded synthetic data already resident in HBM; successive steps rotate over
+distinct weight sets (>= 1 GB in total, so the weights stream from HBM rather
+than from the 256 MB last-level cache).
+
+Printed: one JSON line with the headline (decode µs per call), the roofline
+of the dominant kernel (timed live with HIP events on the library's stream),
+the prefill workloads (T=4096 and the EP8 rank share T=32768) and the CPU
+oracle baseline.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+FP8_PEAK_TFLOPS = 5000.0       # dense fp8 MFMA (published, no sparsity)
+F16_PEAK_TFLOPS = 2500.0       # dense fp16 MFMA
+METRIC = ("fused-MoE µs + TFLOP/s & HBM GB/s (% roofline) at T=64 decode and "
+          "T=4096 prefill")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def moe_bytes(cfg, stats):
+    """Algorithmic bytes of one fused forward: packed weights + scales of the
+    active local experts, bf16 activations in and out, routing in."""
+    H, I = cfg.H, cfg.I
+    per_expert = 2 * I * H // 2 + 2 * I * (H // 128) * 4 + H * I // 2 + H * (I // 128) * 4
+    return stats["A"] * per_expert + cfg.T * H * 2 * 2 + cfg.T * cfg.topk * 8
+
+
+def gate_up_bytes(cfg, stats):
+    """Algorithmic bytes of the gate_up kernel: w13 + scales of the active
+    experts, the fp8 activation rows and scales it reads, the fp8 intermediate
+    and its scales it writes."""
+    H, I = cfg.H, cfg.I
+    w = stats["A"] * (2 * I * H // 2 + 2 * I * (H // 128) * 4)
+    return w + cfg.T * (H + (H // 128) * 4) + stats["P"] * (I + (I // 128) * 4)
+
+
+def down_bytes(cfg, stats):
+    H, I = cfg.H, cfg.I
+    w = stats["A"] * (H * I // 2 + H * (I // 128) * 4)
+    return w + stats["P"] * (I + (I // 128) * 4) + stats["P"] * H * 4
+
+
+def moe_flops(cfg, stats):
+    return 2.0 * stats["P"] * (cfg.H * 2 * cfg.I + cfg.I * cfg.H)
+
+
+class Workload:
+    def __init__(self, name, nsets, dev):
+        import torch
+        from w4a8_moe_grouped_amd import lib, synth
+        self.cfg = cfg = synth.CONFIGS[name]
+        t0 = time.time()
+        ids, w = synth.gen_routing(cfg)
+        self.stats = synth.routing_stats(cfg, ids)
+        put = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+        self.hidden = put(synth.gen_hidden(cfg).view(np.int16)).view(torch.bfloat16)
+        self.ids, self.w = put(ids), put(w)
+        self.sets = []
+        for s in range(nsets):
+            w13, s13, w2, s2 = synth.gen_expert_weights(cfg, seed=cfg.seed + s)
+            self.sets.append(tuple(put(a) for a in (w13, s13, w2, s2)))
+        self.out = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device=dev)
+        nbytes = lib.fused_moe_workspace_bytes(cfg.T, cfg.H, cfg.topk, cfg.E_local, cfg.I)
+        self.ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        log("[bench] %s: T=%d P=%d A=%d, %d weight set(s), inputs in %.1fs"
+            % (name, cfg.T, self.stats["P"], self.stats["A"], nsets, time.time() - t0))
+
+    def step(self, i):
+        from w4a8_moe_grouped_amd import lib
+        cfg = self.cfg
+        w13, s13, w2, s2 = self.sets[i % len(self.sets)]
+        lib.fused_moe(self.hidden, self.ids, self.w, cfg.expert_begin, cfg.E_local, w13, s13,
+                      w2, s2, out=self.out, workspace=self.ws)
+
+
+def time_steps(wl, steps, warmup):
+    """Whole-step time: events + synchronize around exactly `steps` calls."""
+    import torch
+    for i in range(warmup):
+        wl.step(i)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        wl.step(i)
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) * 1e3 / steps  # µs per step
+
+
+def stage_breakdown(wl, steps):
+    """Per-stage µs from HIP events the library records on its own stream."""
+    import torch
+    from w4a8_moe_grouped_amd import lib
+    timer = lib.StageTimer()
+    acc = {k: [] for k in lib.STAGES}
+    for i in range(steps):
+        timer.arm()
+        wl.step(i)
+        for k, v in timer.read_ms().items():
+            acc[k].append(v * 1e3)
+    torch.cuda.synchronize()
+    timer.close()
+    return {k: float(np.mean(v)) for k, v in acc.items()}
+
+
+def cpu_baseline(name):
+    """The plain single-threaded C oracle on the full decode workload."""
+    import oracle
+    from w4a8_moe_grouped_amd import synth
+    cfg = synth.CONFIGS[name]
+    d = synth.gen_moe(cfg)
+    oracle.lib()
+    t0 = time.perf_counter()
+    oracle.fused_moe(d["hidden"], d["topk_ids"], d["topk_weights"], cfg.expert_begin,
+                     cfg.E_local, d["w13"], d["s13"], d["w2"], d["s2"])
+    dt = time.perf_counter() - t0
+    return {"value": dt * 1e6, "unit": "µs", "cores": 1, "kind": "oracle",
+            "sample": "the whole %s workload (T=%d, H=%d, I=%d, top-%d, experts 0..%d of %d), "
+                      "one call, single-threaded fp64 C" % (name, cfg.T, cfg.H, cfg.I, cfg.topk,
+                                                           cfg.E_local - 1, cfg.E_total)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", default=None, help="time just this workload (decode/prefill/...)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this library runs the fused MoE on one GPU's share of experts; "
+              "multi-GPU runs are not part of it (use --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from w4a8_moe_grouped_amd import lib
+    if not os.path.exists(lib.LIB_PATH):
+        from w4a8_moe_grouped_amd import build
+        build.build()
+    assert torch.cuda.is_available(), "bench.py needs the GPU"
+    dev = torch.device("cuda:0")
+    lib.load()
+
+    primary = args.only or "decode"
+    wl = Workload(primary, nsets=2, dev=dev)
+    cfg, st = wl.cfg, wl.stats
+    us = time_steps(wl, args.steps, args.warmup)
+    stages = stage_breakdown(wl, max(5, min(args.steps, 20)))
+    log("[bench] %s: %.1f us/call, stages %s" % (primary, us, {k: round(v, 1) for k, v in stages.items()}))
+    byts, flops = moe_bytes(cfg, st), moe_flops(cfg, st)
+    gb_s = byts / (us * 1e-6) / 1e9
+    tflops = flops / (us * 1e-6) / 1e12
+    dom = max(("gate_up", "down"), key=lambda k: stages[k])
+    dom_bytes = gate_up_bytes(cfg, st) if dom == "gate_up" else down_bytes(cfg, st)
+    dom_gbs = dom_bytes / (stages[dom] * 1e-6) / 1e9
+
+    result = {
+        "metric": METRIC,
+        "value": round(us, 2),
+        "unit": "µs",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(us / 1e3, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int4 x fp8 (gate_up on exact f16 MFMA with fp64 promotion, down on fp8 MFMA)",
+        "data": "synthetic (seeded; random int4 weights, N(0,1) activations and router logits)",
+        "config": {"workload": "%s: %s" % (primary, cfg.desc), "T": cfg.T, "H": cfg.H, "I": cfg.I,
+                   "experts_total": cfg.E_total, "experts_local": cfg.E_local, "topk": cfg.topk,
+                   "local_pairs": st["P"], "active_experts": st["A"], "weight_sets": 2},
+        "tflops": round(tflops, 2),
+        "hbm_gbs": round(gb_s, 1),
+        "roofline_frac_call": round(gb_s / HBM_PEAK_GBS, 4),
+        "stages_us": {k: round(v, 2) for k, v in stages.items()},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(dom_gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None, "bytes_per_launch": dom_bytes,
+                     "avg_launch_us": round(stages[dom], 2)},
+    }
+
+    if not args.no_prefill and args.only is None:
+        pre = {}
+        for name, steps, warm in (("prefill", 10, 3), ("prefill_ep8", 3, 1)):
+            p = Workload(name, nsets=1, dev=dev)
+            pu = time_steps(p, steps, warm)
+            pst = stage_breakdown(p, 2)
+            pfl = moe_flops(p.cfg, p.stats)
+            pby = moe_bytes(p.cfg, p.stats)
+            pre[name] = {"workload": p.cfg.desc, "us": round(pu, 1), "P": p.stats["P"],
+                         "tflops": round(pfl / (pu * 1e-6) / 1e12, 2),
+                         "frac_fp8_peak": round(pfl / (pu * 1e-6) / 1e12 / FP8_PEAK_TFLOPS, 4),
+                         "hbm_gbs": round(pby / (pu * 1e-6) / 1e9, 1),
+                         "stages_us": {k: round(v, 1) for k, v in pst.items()}}
+            log("[bench] %s: %s" % (name, pre[name]))
+            del p
+            torch.cuda.empty_cache()
+        result["prefill"] = pre
+
+    if not args.no_cpu_baseline:
+        cb = cpu_baseline(primary)
+        result["cpu_baseline"] = cb
+        log("[bench] cpu oracle: %.0f us" % cb["value"])
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,208 @@
+/*
+ * w4a8.h -- C ABI of libw4a8: the W4AFP8 fused-MoE forward on one MI355X
+ * (gfx950), as hand-written HIP kernels.
+ *
+ * The method (page titles; the passage in quotes or in brackets):
+ *  - SGLang PR #7762 "feat: support DeepSeek-R1-W4AFP8 model with ep-moe
+ *    mode": MoE experts hold INT4 weights and take FP8 activations ["Model
+ *    Info"]; the MoE op scales the input hidden states and the intermediate
+ *    values, permutes tokens before the w4a8 grouped GEMM and un-permutes
+ *    after it, with SiLU-and-Mul between the two GEMMs ["Cutlass W4A8 MoE",
+ *    "Kernel"]; the permutation is a stable sort of the local top-k ids with
+ *    per-expert segment offsets and a src2dst map [review thread on
+ *    run_cutlass_moe_ep_preproess]; global ids become local through the
+ *    expert map [review thread on expert_map]; weight groups are 128 wide
+ *    along K [review thread on the hard-coded chunk size].
+ *  - DeepGEMM PR #53 "SM90 (Hopper) FP4 MegaMoE fused kernel with swapAB
+ *    small-batch path": activation scales are plain fp32 per token (no
+ *    power-of-two rounding) and amax is clamped before the reciprocal
+ *    448/amax [commit note dropping UE8M0]; the fused order is L1 GEMM ->
+ *    SwiGLU -> per-token FP8 requant -> L2 GEMM -> combine ["Changes"].
+ *  - SGLang PR #37796 "feat(moe_wna16): 2-bit experts, expert streaming,
+ *    N-contiguous GEMV": values are saturated to +-448 before the e4m3 cast
+ *    [part-1 notes on the fp8 KV write path].
+ *
+ * Numerical contract (identical in every export):
+ *  - fp8 is OCP e4m3 ("fn", max 448).  Quantisation of one 128-wide block of
+ *    one row: amax = max|x|; amax_c = max(amax, 1e-10f); inv = 448/amax_c
+ *    (IEEE fp32 divide); scale = amax_c/448; code = e4m3(clamp(x*inv, +-448))
+ *    with round-to-nearest-even, subnormals kept, sign kept (-0 -> 0x80).
+ *  - int4 weights: byte b holds k even in b & 0xF and k odd in b >> 4, two's
+ *    complement (-8..7), no zero point; one fp32 scale per 128 K-elements.
+ *  - GEMM: y[m,n] = sum_g a_scale[m,g] * w_scale[n,g] * sum_{k in g}
+ *    dec(a[m,k]) * w[n,k], accumulated in fp32 on the GPU.
+ *
+ * Conventions:
+ *  - Every pointer is a device pointer on the current HIP device unless
+ *    noted, 16-byte aligned.  The caller owns all memory; the library never
+ *    allocates, keeps no state between calls, and never synchronises the
+ *    host: every launch is asynchronous on `stream` (0 = the null stream).
+ *  - Return value: W4A8_OK, or an error code.  Arguments are validated on the
+ *    host before anything is launched; on error nothing is launched and no
+ *    output is touched.  W4A8_ERR_HIP reports a failed launch.
+ *  - Workspace: pass workspace == NULL to query; the required size (a pure
+ *    function of the shape arguments) is written to *workspace_bytes and
+ *    W4A8_OK is returned.  Otherwise *workspace_bytes must hold the size of
+ *    the buffer supplied.
+ *  - Calls that share a workspace or outputs must be ordered by the caller.
+ */
+#ifndef W4A8_H
+#define W4A8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    W4A8_OK = 0,
+    W4A8_ERR_INVALID_ARG = 1, /* null pointer, negative or zero size, bad leading dim */
+    W4A8_ERR_UNSUPPORTED = 2, /* K/H/I not a multiple of 128, topk > 32, misaligned pointer */
+    W4A8_ERR_WORKSPACE = 3,   /* workspace smaller than the queried size */
+    W4A8_ERR_HIP = 4          /* a kernel launch failed */
+} w4a8_status;
+
+#define W4A8_GROUP 128
+#define W4A8_MAX_TOPK 32
+
+/* Library version as (major << 16) | minor. */
+int w4a8_version(void);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* w4a8_status_string(int status);
+
+/*
+ * w4a8_quantize_act -- dynamic per-token-per-128 fp8 quantisation
+ * (DeepGEMM PR #53, commit note dropping UE8M0; SGLang PR #37796 part-1
+ * saturation note).
+ *
+ *   x_bf16  [M, K] bf16, row stride ldx elements (ldx >= K)
+ *   q_e4m3  [M, K] fp8 e4m3 codes, row stride K, canonical K order
+ *   scales  [M, K/128] fp32 dequantisation scales (amax_c / 448)
+ * M >= 0 (M == 0 launches nothing), K > 0 and K % 128 == 0.
+ * Results are bit-exact with the rule above.
+ */
+int w4a8_quantize_act(const void* x_bf16, int64_t M, int64_t K, int64_t ldx,
+                      uint8_t* q_e4m3, float* scales, hipStream_t stream);
+
+/*
+ * w4a8_gemm -- dense W4AFP8 linear: out = bf16(A * W^T) with per-group
+ * promotion (SGLang PR #7762, "Model Info" and the chunk-size thread).
+ *
+ *   a_e4m3    [M, K] codes from w4a8_quantize_act; a_scales [M, K/128] fp32
+ *   b_int4    [N, K/2] packed int4;                 b_scales [N, K/128] fp32
+ *   out_bf16  [M, N] bf16, round to nearest even from the fp32 accumulator
+ *   workspace device scratch of *workspace_bytes bytes (query with NULL)
+ * M >= 0, N > 0, K > 0, K % 128 == 0.  fp32 accumulation order is the
+ * kernel's; the result matches the fp64 definition within rounding.
+ */
+int w4a8_gemm(const uint8_t* a_e4m3, const float* a_scales, int64_t M, int64_t K,
+              const uint8_t* b_int4, const float* b_scales, int64_t N,
+              void* out_bf16, void* workspace, size_t* workspace_bytes,
+              hipStream_t stream);
+
+/*
+ * w4a8_moe_align -- routing permutation (SGLang PR #7762, review threads on
+ * run_cutlass_moe_ep_preproess and expert_map).
+ *
+ * Pair f = t*topk + j routes token t to global expert topk_ids[f].  It is
+ * local when l = topk_ids[f] - expert_begin is in [0, num_local_experts);
+ * every other id (including -1 padding) is skipped.  Outputs:
+ *   expert_counts   [E_l]     local pairs per local expert
+ *   expert_offsets  [E_l+1]   exclusive prefix sum (offsets[E_l] = P)
+ *   sorted_pair_ids [T*topk]  the P local f's, stable-sorted by l (ties keep
+ *                             ascending f); entries >= P are left unspecified
+ *   src2dst         [T*topk]  position of f in that order, -1 if not local
+ *   block_expert, block_row [ceil(T*topk/block_m) + E_l]
+ *                             the m-blocks: for l ascending, rows
+ *                             offsets[l] + b*block_m for b < ceil(c_l/block_m)
+ *   num_blocks      [1]       number of m-blocks written
+ *   workspace       device scratch of *workspace_bytes bytes (query with NULL)
+ * T >= 0, 1 <= topk <= 32, E_l >= 1, block_m >= 1.  Bit-exact (one
+ * correct answer).  block_expert/block_row may be NULL to skip the blocks
+ * (num_blocks is then still written).
+ */
+int w4a8_moe_align(const int32_t* topk_ids, int64_t T, int64_t topk,
+                   int64_t expert_begin, int64_t num_local_experts, int64_t block_m,
+                   int32_t* expert_counts, int32_t* expert_offsets,
+                   int32_t* sorted_pair_ids, int32_t* src2dst,
+                   int32_t* block_expert, int32_t* block_row, int32_t* num_blocks,
+                   void* workspace, size_t* workspace_bytes, hipStream_t stream);
+
+/*
+ * w4a8_fused_moe -- the whole forward on this GPU's experts (SGLang PR
+ * #7762 "Cutlass W4A8 MoE" workflow; DeepGEMM PR #53 "Changes"):
+ *   align -> quantise hidden -> gate_up grouped GEMM (rows gathered through
+ *   the permutation) -> SwiGLU h = silu(y[:, :I]) * y[:, I:] -> fp8 requant
+ *   per 128 of I -> down grouped GEMM -> out[t] = bf16(sum over t's local
+ *   pairs of topk_weights * y2), +0 for a token with no local pair.
+ *
+ *   hidden_bf16  [T, H] bf16 (row stride H)
+ *   topk_ids     [T, topk] int32 global expert ids; topk_weights [T, topk] fp32
+ *   w13_int4     [E_l, 2I, H/2] (gate rows [0, I), up rows [I, 2I))
+ *   w13_scales   [E_l, 2I, H/128] fp32
+ *   w2_int4      [E_l, H, I/2];   w2_scales [E_l, H, I/128] fp32
+ *   out_bf16     [T, H] bf16
+ *   workspace    device scratch of *workspace_bytes bytes (query with NULL);
+ *                holds the routing permutation, the fp8 activations and the
+ *                intermediates between the kernels of one call
+ * T >= 0 (T == 0 launches nothing), H, I > 0 and multiples of 128,
+ * 1 <= topk <= 32, E_l >= 1.
+ */
+int w4a8_fused_moe(const void* hidden_bf16, int64_t T, int64_t H,
+                   const int32_t* topk_ids, const float* topk_weights, int64_t topk,
+                   int64_t expert_begin, int64_t num_local_experts, int64_t I,
+                   const uint8_t* w13_int4, const float* w13_scales,
+                   const uint8_t* w2_int4, const float* w2_scales,
+                   void* out_bf16, void* workspace, size_t* workspace_bytes,
+                   hipStream_t stream);
+
+/*
+ * w4a8_fused_moe_workspace_layout -- where w4a8_fused_moe keeps its
+ * intermediates inside the workspace (host-only query, no HIP call), so that
+ * tests and tools can read them after a call:
+ *   offsets[0]  expert_counts   int32 [E_l]
+ *   offsets[1]  expert_offsets  int32 [E_l+1]
+ *   offsets[2]  sorted_pair_ids int32 [T*topk]
+ *   offsets[3]  src2dst         int32 [T*topk]
+ *   offsets[4]  block_expert    int32 [nb]     offsets[5] block_row int32 [nb]
+ *   offsets[6]  num_blocks      int32 [1]      (nb <= ceil(T*topk/block_m)+E_l)
+ *   offsets[7]  gate_up operand: the fp8 hidden codes' exact values as fp16
+ *               [T, H]; inside each 128-group, 8-group b (k = 8b..8b+7) sits
+ *               at 16-byte chunk 4*(b%4) + b/4, in K order k0,k4,k1,k5,k2,k6,k3,k7
+ *   offsets[8]  float2 [T, H/128]  {scale, 0}
+ *   offsets[9]  requantised intermediate: fp8 codes [T*topk, I] (pair rows
+ *               in permuted order); inside each 128-group, 8-group b sits at
+ *               byte 16*(4*((b%4)/2) + b/4) + 8*(b%2), in K order
+ *               k0,k2,k4,k6,k1,k3,k5,k7
+ *   offsets[10] float2 [T*topk, I/128] {512*scale, -8*scale*sum of the block's
+ *               decoded codes}
+ *   offsets[11] down output fp32 [T*topk, H] (pair rows in permuted order)
+ * n must be 12; *block_m receives the m-block height the call uses.
+ */
+int w4a8_fused_moe_workspace_layout(int64_t T, int64_t H, int64_t topk,
+                                    int64_t num_local_experts, int64_t I,
+                                    size_t* offsets, int n, int64_t* block_m);
+
+/*
+ * w4a8_fused_moe_stage_events -- profiling hook for a per-stage breakdown
+ * (the five stages DeepGEMM PR #53 reports with its profile breakdown:
+ * dispatch/align, L1 GEMM, act+quant, L2 GEMM, combine).
+ *
+ * Arms the NEXT w4a8_fused_moe call made on the calling host thread to
+ * record events[i] (hipEvent_t handles created by the caller) on its stream:
+ *   [0] before align  [1] after align  [2] after the input quantisation
+ *   [3] after gate_up+SwiGLU+requant   [4] after down  [5] after combine
+ * n must be 6 (or 0 to disarm).  The call consumes the arming; it never
+ * synchronises.  Returns W4A8_ERR_INVALID_ARG for a bad n or null events.
+ */
+int w4a8_fused_moe_stage_events(void* const* events, int n);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* W4A8_H */

@@ -1,0 +1,119 @@
+"""Host-only checks of the C ABI (no GPU needed, no kernel is launched).
+
+The library must load, export every function include/w4a8.h declares, answer
+workspace queries as a pure function of the shapes, and reject bad arguments
+with the documented status before any HIP call is made.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from w4a8_moe_grouped_amd import lib as w4
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w4a8.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+BOGUS = ctypes.c_void_p(0x1000)  # 16-byte aligned, never dereferenced on these paths
+MISALIGNED = ctypes.c_void_p(0x1004)
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(w4.LIB_PATH):
+        from w4a8_moe_grouped_amd import build
+        build.build()
+    return w4.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(w4a8_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert set(names) == set(w4.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_status_strings(L):
+    assert L.w4a8_version() >= 1
+    for rc in range(5):
+        assert L.w4a8_status_string(rc)
+    assert L.w4a8_status_string(99) == b"unknown status"
+
+
+def test_workspace_queries_are_pure_functions_of_shape(L):
+    a = w4.fused_moe_workspace_bytes(64, 7168, 8, 32, 2048)
+    assert a == w4.fused_moe_workspace_bytes(64, 7168, 8, 32, 2048) and a > 0
+    assert w4.fused_moe_workspace_bytes(128, 7168, 8, 32, 2048) > a
+    assert w4.gemm_workspace_bytes(128, 7168, 2048) >= 128 * 7168
+    assert w4.align_workspace_bytes(64, 8, 32, 16) > 0
+    big = w4.align_workspace_bytes(32768, 8, 32, 64)
+    assert big >= 64 * 32 * 4  # per-chunk histograms
+
+
+def _fused(L, T=4, H=256, k=2, E=4, I=128, hidden=BOGUS, ids=BOGUS, wts=BOGUS, w13=BOGUS,
+           ws=BOGUS, nbytes=None):
+    n = ctypes.c_size_t(1 << 40 if nbytes is None else nbytes)
+    return L.w4a8_fused_moe(hidden, T, H, ids, wts, k, 0, E, I, w13, BOGUS, BOGUS, BOGUS, BOGUS,
+                            ws, ctypes.byref(n), None)
+
+
+def test_fused_moe_rejects_bad_arguments(L):
+    assert _fused(L, H=200) == UNSUPPORTED
+    assert _fused(L, I=100) == UNSUPPORTED
+    assert _fused(L, k=33) == UNSUPPORTED
+    assert _fused(L, E=2000) == UNSUPPORTED
+    assert _fused(L, T=-1) == INVALID
+    assert _fused(L, H=0) == INVALID
+    assert _fused(L, k=0) == INVALID
+    assert _fused(L, E=0) == INVALID
+    assert _fused(L, hidden=None) == INVALID
+    assert _fused(L, w13=None) == INVALID
+    assert _fused(L, hidden=MISALIGNED) == UNSUPPORTED
+    assert _fused(L, ws=MISALIGNED) == UNSUPPORTED
+    assert _fused(L, nbytes=16) == WORKSPACE
+    # T == 0 is valid and launches nothing
+    assert _fused(L, T=0) == OK
+
+
+def test_quantize_rejects_bad_arguments(L):
+    q = L.w4a8_quantize_act
+    assert q(BOGUS, 4, 100, 100, BOGUS, BOGUS, None) == UNSUPPORTED
+    assert q(BOGUS, 4, 128, 64, BOGUS, BOGUS, None) == INVALID     # ldx < K
+    assert q(BOGUS, 4, 128, 132, BOGUS, BOGUS, None) == UNSUPPORTED  # ldx % 8
+    assert q(None, 4, 128, 128, BOGUS, BOGUS, None) == INVALID
+    assert q(BOGUS, -1, 128, 128, BOGUS, BOGUS, None) == INVALID
+    assert q(MISALIGNED, 4, 128, 128, BOGUS, BOGUS, None) == UNSUPPORTED
+    assert q(None, 0, 128, 128, None, None, None) == OK
+
+
+def test_gemm_rejects_bad_arguments(L):
+    n = ctypes.c_size_t(1 << 40)
+    g = L.w4a8_gemm
+    assert g(BOGUS, BOGUS, 4, 100, BOGUS, BOGUS, 16, BOGUS, BOGUS, ctypes.byref(n), None) == UNSUPPORTED
+    assert g(BOGUS, BOGUS, 4, 128, BOGUS, BOGUS, 0, BOGUS, BOGUS, ctypes.byref(n), None) == INVALID
+    assert g(None, BOGUS, 4, 128, BOGUS, BOGUS, 16, BOGUS, BOGUS, ctypes.byref(n), None) == INVALID
+    assert g(BOGUS, BOGUS, 4, 128, BOGUS, BOGUS, 16, BOGUS, BOGUS, None, None) == INVALID
+    small = ctypes.c_size_t(8)
+    assert g(BOGUS, BOGUS, 4, 128, BOGUS, BOGUS, 16, BOGUS, BOGUS, ctypes.byref(small), None) == WORKSPACE
+
+
+def test_align_rejects_bad_arguments(L):
+    n = ctypes.c_size_t(1 << 40)
+    a = L.w4a8_moe_align
+    args = lambda T=4, k=2, E=4, bm=16, ids=BOGUS, be=BOGUS, br=BOGUS: a(
+        ids, T, k, 0, E, bm, BOGUS, BOGUS, BOGUS, BOGUS, be, br, BOGUS, BOGUS, ctypes.byref(n), None)
+    assert args(k=0) == INVALID
+    assert args(k=33) == UNSUPPORTED
+    assert args(E=0) == INVALID
+    assert args(E=1025) == UNSUPPORTED
+    assert args(bm=0) == INVALID
+    assert args(ids=None) == INVALID
+    assert args(be=None) == INVALID  # block_expert and block_row must both be given or both null

@@ -1,0 +1,82 @@
+"""The fused forward's intermediates against the oracle's (GPU).
+
+The requantised intermediate (fp8 codes + scales of h = SwiGLU(gate_up)) and
+the down GEMM output are read back from the workspace (its layout comes from
+w4a8_fused_moe_workspace_layout) and compared, pair by pair in the same
+permuted order, with the oracle's.  The codes are not required to match
+bit for bit (fp32 vs fp64 accumulation can move h across a rounding
+boundary); their mismatch rate is reported and bounded.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from w4a8_moe_grouped_amd import lib as w4
+from w4a8_moe_grouped_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+IL_FP8 = np.array([0, 2, 4, 6, 1, 3, 5, 7])  # position j of an 8-group holds k = IL_FP8[j]
+
+
+def fp8_group_pos(b):
+    """byte offset of 8-group b inside a 128-byte group of the fp8 operand layout"""
+    return 16 * (4 * ((b % 4) // 2) + b // 4) + 8 * (b % 2)
+
+
+def dput(a, dev):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+def deinterleave8(mem):
+    """fp8 operand layout -> canonical K order"""
+    P, K = mem.shape
+    g = mem.reshape(P, K // 128, 128)
+    out = np.empty((P, K // 128, 16, 8), mem.dtype)
+    for b in range(16):
+        chunk = g[:, :, fp8_group_pos(b):fp8_group_pos(b) + 8]
+        out[:, :, b, IL_FP8] = chunk
+    return out.reshape(P, K)
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "skew_id"])
+def test_requant_codes_and_down_output(name):
+    assert torch.cuda.is_available()
+    dev = torch.device("cuda:0")
+    cfg = synth.CONFIGS[name]
+    d = synth.gen_moe(cfg)
+    T, H, I, k, E = cfg.T, cfg.H, cfg.I, cfg.topk, cfg.E_local
+    if name == "skew_id":  # keep the oracle short: the first 40 tokens
+        T = 40
+        for key in ("hidden", "topk_ids", "topk_weights"):
+            d[key] = d[key][:T]
+    lay = w4.fused_moe_workspace_layout(T, H, k, E, I)
+    ws = torch.zeros(w4.fused_moe_workspace_bytes(T, H, k, E, I), dtype=torch.uint8, device=dev)
+    hid = dput(d["hidden"].view(np.int16), dev).view(torch.bfloat16)
+    w4.fused_moe(hid, dput(d["topk_ids"], dev), dput(d["topk_weights"], dev), cfg.expert_begin, E,
+                 dput(d["w13"], dev), dput(d["s13"], dev), dput(d["w2"], dev), dput(d["s2"], dev),
+                 workspace=ws)
+    torch.cuda.synchronize()
+    wsh = ws.cpu().numpy()
+    out, inter = oracle.fused_moe(d["hidden"], d["topk_ids"], d["topk_weights"], cfg.expert_begin,
+                                  E, d["w13"], d["s13"], d["w2"], d["s2"], intermediates=True)
+    P = inter["qh"].shape[0]
+    GI = I // 128
+    offs = wsh[lay["offsets"]:lay["offsets"] + 4 * (E + 1)].view(np.int32)
+    assert offs[-1] == P
+    qh = deinterleave8(wsh[lay["qh"]:lay["qh"] + P * I].reshape(P, I))
+    side = wsh[lay["qh_side"]:lay["qh_side"] + 8 * P * GI].view(np.float32).reshape(P, GI, 2)
+    y2 = wsh[lay["y2"]:lay["y2"] + 4 * P * H].view(np.float32).reshape(P, H).astype(np.float64)
+
+    code_mis = np.mean(qh != inter["qh"])
+    scale = side[:, :, 0] / np.float32(512)
+    scale_mis = np.mean(scale != inter["sh"])
+    y2_fro = np.linalg.norm(y2 - inter["y2"]) / np.linalg.norm(inter["y2"])
+    y2_max = np.max(np.abs(y2 - inter["y2"])) / np.max(np.abs(inter["y2"]))
+    # with the oracle's own codes, how far is the GPU's down GEMM alone?
+    print("%s: P=%d code mismatch=%.2e (%d of %d) scale mismatch=%.2e y2 rel_fro=%.3e max=%.3e"
+          % (name, P, code_mis, int(np.sum(qh != inter["qh"])), qh.size, scale_mis, y2_fro, y2_max))
+    assert code_mis <= 1e-3
+    assert scale_mis <= 1e-2
+    assert y2_fro <= 1e-3

@@ -1,0 +1,281 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bars:
+  * quantisation codes and scales, routing permutation: bit-exact;
+  * bf16 outputs of the GEMM and the fused MoE: relative Frobenius error
+    <= 1e-3 and max |diff| <= 2e-2 * max |ref| against the oracle's fp64 result
+    rounded to bf16; rows the oracle gives exactly +0 (no local pair) must be
+    exactly +0.
+Full-size workloads are checked on sampled tokens: every output row depends
+only on its own token (plus the weights), so the oracle run on the sampled
+tokens alone gives exactly those rows.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from w4a8_moe_grouped_amd import lib as w4
+from w4a8_moe_grouped_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+REL_FRO = 1e-3
+MAX_REL = 2e-2
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "the gpu tests need an MI355X"
+    w4.load()
+    return torch.device("cuda:0")
+
+
+def dput(a, dev):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+def bf16_dev(bits, dev):
+    return dput(np.ascontiguousarray(bits).view(np.int16), dev).view(torch.bfloat16)
+
+
+def bf16_host(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def assert_bf16_close(got_bits, ref_bits, what=""):
+    g = synth.bf16_bits_to_f32(got_bits).astype(np.float64)
+    r = synth.bf16_bits_to_f32(ref_bits).astype(np.float64)
+    assert np.all(np.isfinite(g)), what
+    zero_rows = np.all(r == 0, axis=-1)
+    if np.any(zero_rows):
+        assert np.all(got_bits[zero_rows] == 0), "%s: rows without local pairs must be +0" % what
+    nr = np.linalg.norm(r)
+    if nr == 0:
+        assert np.all(got_bits == 0), what
+        return
+    fro = np.linalg.norm(g - r) / nr
+    mx = np.max(np.abs(g - r)) / np.max(np.abs(r))
+    print("%s: rel_fro=%.3e max_rel=%.3e" % (what, fro, mx))
+    assert fro <= REL_FRO and mx <= MAX_REL, (what, fro, mx)
+
+
+_cache = {}
+
+
+def moe_inputs(name):
+    if name not in _cache:
+        cfg = synth.CONFIGS[name]
+        _cache[name] = (cfg, synth.gen_moe(cfg))
+    return _cache[name]
+
+
+# ---------------------------------------------------------------------------
+# activation quantisation: bit-exact
+# ---------------------------------------------------------------------------
+
+def check_quant(x_bits, dev, ldx_pad=0):
+    M, K = x_bits.shape
+    if ldx_pad:
+        buf = np.zeros((M, K + ldx_pad), np.uint16)
+        buf[:, :K] = x_bits
+        xd = bf16_dev(buf, dev)[:, :K]
+    else:
+        xd = bf16_dev(x_bits, dev)
+    q, s = w4.quantize_act(xd)
+    torch.cuda.synchronize()
+    rq, rs = oracle.quantize_bf16(x_bits)
+    gq, gs = q.cpu().numpy(), s.cpu().numpy()
+    assert np.array_equal(gq, rq), "codes differ at %s" % (np.argwhere(gq != rq)[:5],)
+    assert np.array_equal(gs.view(np.uint32), rs.view(np.uint32))
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "skew_perm"])
+def test_quant_bit_exact_moe_hidden(dev, name):
+    cfg = synth.CONFIGS[name]
+    check_quant(synth.gen_hidden(cfg), dev)
+
+
+def test_quant_bit_exact_dense_with_outliers(dev):
+    x, _, _ = synth.gen_dense(synth.CONFIGS["dense"])
+    check_quant(x, dev)
+    check_quant(x[:37], dev, ldx_pad=64)  # ragged M, row stride > K
+
+
+def test_quant_edge_rows(dev):
+    rng = np.random.default_rng(0)
+    rows = []
+    rows.append(np.zeros(256, np.float32))                       # all zero -> clamped amax
+    r = np.zeros(256, np.float32); r[3] = -2.5; rows.append(r)   # single nonzero
+    rows.append(np.full(256, 3e38, np.float32))                  # huge
+    rows.append(np.full(256, 1e-38, np.float32))                 # tiny, below the clamp
+    rows.append(rng.normal(size=256).astype(np.float32) * 1e-12)
+    r = rng.normal(size=256).astype(np.float32); r[::7] = 0; rows.append(r)
+    rows.append(np.linspace(-448, 448, 256).astype(np.float32))
+    x = synth.to_bf16_bits(np.stack(rows))
+    x[4, 10] = 0x0001   # bf16 subnormal
+    x[5, 11] = 0x8000   # -0
+    check_quant(x, dev)
+    check_quant(x[:1], dev)
+
+
+def test_quant_every_bf16_amax_and_element(dev):
+    bits = np.arange(0x0001, 0x7F80, dtype=np.uint16)  # every positive finite bf16
+    rng = np.random.default_rng(1)
+    x = np.zeros((bits.size, 128), np.uint16)
+    x[:, 5] = bits
+    x[:, 77] = bits | 0x8000
+    # the other entries: every bf16 value again, shuffled, scaled below the row's amax
+    other = rng.permutation(bits)
+    small = np.minimum(synth.bf16_bits_to_f32(other), synth.bf16_bits_to_f32(bits))
+    x[:, 9] = synth.to_bf16_bits(small)
+    x[:, 100] = synth.to_bf16_bits(-small * np.float32(0.7))
+    check_quant(x, dev)
+
+
+# ---------------------------------------------------------------------------
+# routing permutation: bit-exact
+# ---------------------------------------------------------------------------
+
+def check_align(ids, eb, E, bm, dev):
+    g = w4.moe_align(dput(ids.astype(np.int32), dev), eb, E, bm)
+    torch.cuda.synchronize()
+    r = oracle.moe_align(ids, eb, E, bm)
+    P = int(r["offsets"][-1])
+    nb = int(g["num_blocks"].item())
+    assert nb == r["num_blocks"]
+    assert np.array_equal(g["counts"].cpu().numpy(), r["counts"])
+    assert np.array_equal(g["offsets"].cpu().numpy(), r["offsets"])
+    assert np.array_equal(g["sorted_pair_ids"].cpu().numpy()[:P], r["sorted_pair_ids"])
+    F = ids.size
+    assert np.array_equal(g["src2dst"].cpu().numpy()[:F], r["src2dst"])
+    assert np.array_equal(g["block_expert"].cpu().numpy()[:nb], r["block_expert"])
+    assert np.array_equal(g["block_row"].cpu().numpy()[:nb], r["block_row"])
+
+
+@pytest.mark.parametrize("name,bm", [("tiny", 16), ("decode", 16), ("prefill", 64),
+                                     ("prefill_ep8", 128), ("skew_perm", 64), ("skew_id", 32)])
+def test_align_bit_exact_configs(dev, name, bm):
+    cfg = synth.CONFIGS[name]
+    ids, _ = synth.gen_routing(cfg)
+    check_align(ids, cfg.expert_begin, cfg.E_local, bm, dev)
+
+
+@pytest.mark.parametrize("T,k,eb,E,bm,seed", [
+    (1, 1, 0, 1, 1, 0), (1, 8, 0, 32, 16, 1), (3, 32, 5, 7, 3, 2), (600, 8, 40, 32, 16, 3),
+    (5000, 6, 0, 1024, 64, 4), (4097, 1, 0, 3, 100, 5), (20000, 8, 224, 32, 64, 6)])
+def test_align_bit_exact_random(dev, T, k, eb, E, bm, seed):
+    rng = np.random.default_rng(seed)
+    ids = rng.integers(-1, eb + E + 9, size=(T, k)).astype(np.int32)
+    ids[rng.uniform(size=(T, k)) < 0.1] = -1
+    check_align(ids, eb, E, bm, dev)
+
+
+def test_align_all_non_local_and_one_hot(dev):
+    ids = np.full((300, 4), 77, np.int32)
+    check_align(ids, 0, 8, 16, dev)             # P = 0
+    ids = np.full((300, 4), 3, np.int32)
+    check_align(ids, 0, 8, 16, dev)             # everything on one expert
+
+
+# ---------------------------------------------------------------------------
+# dense GEMM: tolerance
+# ---------------------------------------------------------------------------
+
+def check_gemm(x_bits, w, sw, dev, what):
+    xd = bf16_dev(x_bits, dev)
+    q, s = w4.quantize_act(xd)
+    out = w4.gemm(q, s, dput(w, dev), dput(sw, dev))
+    torch.cuda.synchronize()
+    rq, rs = oracle.quantize_bf16(x_bits)
+    ref = oracle.gemm_bf16(rq, rs, w, sw)
+    assert_bf16_close(bf16_host(out), ref, what)
+
+
+def test_gemm_dense_config(dev):
+    x, w, sw = synth.gen_dense(synth.CONFIGS["dense"])
+    check_gemm(x, w, sw, dev, "dense M=128 K=7168 N=2048")
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 128, 16), (5, 384, 40), (33, 256, 300), (70, 1024, 513),
+                                   (17, 7168, 256), (64, 2048, 7168)])
+def test_gemm_ragged_shapes(dev, M, K, N):
+    rng = np.random.default_rng(M * 7 + N)
+    x = synth.to_bf16_bits(rng.normal(size=(M, K)).astype(np.float32))
+    w = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    sw = rng.uniform(0.002, 0.02, size=(N, K // 128)).astype(np.float32)
+    check_gemm(x, w, sw, dev, "gemm %dx%dx%d" % (M, K, N))
+
+
+# ---------------------------------------------------------------------------
+# fused MoE: tolerance
+# ---------------------------------------------------------------------------
+
+def run_fused(d, cfg, dev):
+    out = w4.fused_moe(bf16_dev(d["hidden"], dev), dput(d["topk_ids"], dev),
+                       dput(d["topk_weights"], dev), cfg.expert_begin, cfg.E_local,
+                       dput(d["w13"], dev), dput(d["s13"], dev), dput(d["w2"], dev),
+                       dput(d["s2"], dev))
+    torch.cuda.synchronize()
+    return bf16_host(out)
+
+
+def oracle_rows(d, cfg, rows):
+    return oracle.fused_moe(d["hidden"][rows], d["topk_ids"][rows], d["topk_weights"][rows],
+                            cfg.expert_begin, cfg.E_local, d["w13"], d["s13"], d["w2"], d["s2"])
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode"])
+def test_fused_moe_full(dev, name):
+    cfg, d = moe_inputs(name)
+    got = run_fused(d, cfg, dev)
+    ref = oracle_rows(d, cfg, np.arange(cfg.T))
+    assert_bf16_close(got, ref, name)
+
+
+@pytest.mark.parametrize("name,nsample", [("skew_perm", 40), ("skew_id", 24), ("prefill", 24),
+                                          ("prefill_ep8", 16)])
+def test_fused_moe_sampled_tokens(dev, name, nsample):
+    cfg, d = moe_inputs(name)
+    got = run_fused(d, cfg, dev)
+    rng = np.random.default_rng(123)
+    rows = np.sort(rng.choice(cfg.T, size=nsample, replace=False))
+    rows[0], rows[-1] = 0, cfg.T - 1
+    ref = oracle_rows(d, cfg, rows)
+    assert_bf16_close(got[rows], ref, "%s (%d sampled tokens)" % (name, nsample))
+    # rows with no local pair must be exactly zero everywhere
+    ids = d["topk_ids"]
+    none_local = ~np.any((ids >= cfg.expert_begin) & (ids < cfg.expert_begin + cfg.E_local), axis=1)
+    assert np.all(got[none_local] == 0)
+
+
+@pytest.mark.parametrize("case", ["one_expert_many_rows", "single_token", "k1_e1",
+                                  "non_local_mix", "topk32", "small_dims"])
+def test_fused_moe_edge_cases(dev, case):
+    if case == "one_expert_many_rows":   # every pair on expert 2: many full blocks + a partial one
+        cfg, d = synth.random_moe(150, 256, 256, 8, 2, 0, 8, seed=21)
+        d["topk_ids"][:, 0] = 2
+    elif case == "single_token":
+        cfg, d = synth.random_moe(1, 7168, 2048, 256, 8, 0, 256, seed=22)
+    elif case == "k1_e1":
+        cfg, d = synth.random_moe(40, 384, 128, 1, 1, 0, 1, seed=23)
+        d["topk_weights"][:] = 1.0
+    elif case == "non_local_mix":
+        cfg, d = synth.random_moe(64, 256, 128, 16, 4, 8, 4, seed=24)
+        d["topk_ids"][:10] = -1
+    elif case == "topk32":
+        cfg, d = synth.random_moe(9, 256, 128, 64, 32, 0, 64, seed=25)
+    else:
+        cfg, d = synth.random_moe(33, 128, 128, 4, 3, 1, 2, seed=26)
+    got = run_fused(d, cfg, dev)
+    ref = oracle_rows(d, cfg, np.arange(cfg.T))
+    assert_bf16_close(got, ref, case)
+
+
+def test_fused_moe_repeatable_and_workspace_reuse(dev):
+    cfg, d = moe_inputs("tiny")
+    a = run_fused(d, cfg, dev)
+    b = run_fused(d, cfg, dev)
+    assert np.array_equal(a, b)

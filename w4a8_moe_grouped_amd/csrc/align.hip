@@ -1,0 +1,296 @@
+// align.hip -- routing permutation for the grouped GEMMs.
+//
+// SGLang PR #7762, review thread on run_cutlass_moe_ep_preproess: the local
+// top-k ids are stable-sorted, seg_indptr holds the per-expert segment
+// offsets and src2dst maps every (token, k) slot to its sorted position;
+// review thread on expert_map: global ids become local ids of this rank.
+// Here a pair f = t*topk + j is local when l = id[f] - expert_begin is in
+// [0, E); the stable sort by l is a counting sort that visits f in
+// ascending order:
+//   count   -- per chunk of CH pairs, a histogram of local ids (LDS atomics);
+//   scan    -- one block: counts, exclusive offsets, the per-chunk base of
+//              every expert, and the m-block list;
+//   scatter -- per chunk, rounds of 256 pairs in f order: the rank of a pair
+//              among earlier pairs of the same expert comes from wave ballots
+//              and per-wave counts in LDS, so equal keys keep ascending f.
+// When all pairs fit one chunk the three phases run in one block (decode).
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace w4a8 {
+
+constexpr int kAlignThreads = 256;
+constexpr int kAlignWaves = kAlignThreads / 64;
+constexpr int kAlignChunk = 4096;  // pairs per chunk
+constexpr int kMaxLocalExperts = 1024;
+
+int64_t align_chunk_count(int64_t F)
+{
+    return F <= 0 ? 1 : (F + kAlignChunk - 1) / kAlignChunk;
+}
+size_t align_workspace_bytes(int64_t F, int64_t E)
+{
+    return (size_t)align_chunk_count(F) * (size_t)E * sizeof(int32_t);
+}
+
+__device__ __forceinline__ int local_id(const int32_t* ids, int64_t f, int64_t F, int64_t eb,
+                                        int64_t E)
+{
+    if (f >= F)
+        return -1;
+    const int64_t l = (int64_t)ids[f] - eb;
+    return (l >= 0 && l < E) ? (int)l : -1;
+}
+
+// rank of this lane among lower lanes of the wave with the same key, and the
+// number of lanes with that key; keys < 0 are ignored.
+__device__ __forceinline__ void wave_rank(int key, int& rank, int& count)
+{
+    const int lane = threadIdx.x & 63;
+    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    uint64_t pending = __ballot(key >= 0);
+    rank = 0;
+    count = 0;
+    while (pending) {
+        const int leader = __ffsll((unsigned long long)pending) - 1;
+        const int k = __shfl(key, leader, 64);
+        const uint64_t same = __ballot(key == k);
+        if (key == k) {
+            rank = __popcll(same & lt);
+            count = __popcll(same);
+        }
+        pending &= ~same;
+    }
+}
+
+// block-wide exclusive scan of vals[0..n) in LDS (n <= 4 * kAlignThreads);
+// returns the total.  All threads must call it.
+__device__ int block_exclusive_scan(int* vals, int n, int* scratch /* >= kAlignWaves + 1 */)
+{
+    const int t = threadIdx.x;
+    const int lane = t & 63, wave = t >> 6;
+    int local[4];
+    int sum = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int idx = 4 * t + i;
+        local[i] = idx < n ? vals[idx] : 0;
+        sum += local[i];
+    }
+    // inclusive scan of the per-thread sums within the wave
+    int incl = sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o, 64);
+        if (lane >= o)
+            incl += y;
+    }
+    if (lane == 63)
+        scratch[wave] = incl;
+    __syncthreads();
+    if (t == 0) {
+        int run = 0;
+        for (int w = 0; w < kAlignWaves; ++w) {
+            const int c = scratch[w];
+            scratch[w] = run;
+            run += c;
+        }
+        scratch[kAlignWaves] = run;
+    }
+    __syncthreads();
+    int run = scratch[wave] + incl - sum;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int idx = 4 * t + i;
+        if (idx < n)
+            vals[idx] = run;
+        run += local[i];
+    }
+    const int total = scratch[kAlignWaves];
+    __syncthreads();
+    return total;
+}
+
+// counts[] (LDS, E entries) -> offsets, counts and block list in global memory;
+// leaves the exclusive offsets in counts_lds.  All threads call it.
+__device__ void finish_scan(int* counts_lds, int* tmp_lds, int* scratch, int64_t E,
+                            int64_t block_m, const AlignOut& o)
+{
+    const int t = threadIdx.x;
+    for (int e = t; e < E; e += kAlignThreads) {
+        const int c = counts_lds[e];
+        o.counts[e] = c;
+        tmp_lds[e] = (int)((c + block_m - 1) / block_m);  // m-blocks of expert e
+    }
+    __syncthreads();
+    const int P = block_exclusive_scan(counts_lds, (int)E, scratch);
+    const int nb = block_exclusive_scan(tmp_lds, (int)E, scratch);
+    for (int e = t; e < E; e += kAlignThreads)
+        o.offsets[e] = counts_lds[e];
+    if (t == 0) {
+        o.offsets[E] = P;
+        *o.num_blocks = nb;
+    }
+    if (o.block_expert != nullptr) {
+        for (int e = t; e < E; e += kAlignThreads) {
+            const int first = tmp_lds[e];
+            const int last = (e + 1 < E) ? tmp_lds[e + 1] : nb;
+            for (int b = first; b < last; ++b) {
+                o.block_expert[b] = e;
+                o.block_row[b] = counts_lds[e] + (int)((b - first) * block_m);
+            }
+        }
+    }
+    __syncthreads();
+}
+
+// scatter one chunk [f0, f1) given the running base position of every expert
+// (LDS); wcnt is [kAlignWaves][E] of zeros on entry and on exit.
+__device__ void scatter_chunk(const int32_t* ids, int64_t f0, int64_t f1, int64_t eb, int64_t E,
+                              int* base, int* wcnt, const AlignOut& o)
+{
+    const int t = threadIdx.x, wave = t >> 6;
+    for (int64_t r0 = f0; r0 < f1; r0 += kAlignThreads) {
+        const int64_t f = r0 + t;
+        const int key = local_id(ids, f, f1, eb, E);
+        int rank, count;
+        wave_rank(key, rank, count);
+        const bool leader = key >= 0 && rank == 0;
+        if (leader)
+            wcnt[wave * E + key] = count;
+        __syncthreads();
+        if (key >= 0) {
+            int pos = base[key] + rank;
+            for (int w = 0; w < wave; ++w)
+                pos += wcnt[w * E + key];
+            o.sorted[pos] = (int32_t)f;
+            o.src2dst[f] = pos;
+        } else if (f < f1) {
+            o.src2dst[f] = -1;
+        }
+        __syncthreads();
+        if (leader) {
+            atomicAdd(&base[key], count);
+            wcnt[wave * E + key] = 0;
+        }
+        __syncthreads();
+    }
+}
+
+struct AlignLds {
+    int a[kMaxLocalExperts];
+    int b[kMaxLocalExperts];
+    int wcnt[kAlignWaves * kMaxLocalExperts];
+    int scratch[kAlignWaves + 1];
+};
+
+// everything in one block (F <= kAlignChunk)
+__global__ __launch_bounds__(kAlignThreads) void align_single_kernel(const int32_t* __restrict__ ids,
+                                                                     int64_t F, int64_t eb,
+                                                                     int64_t E, int64_t block_m,
+                                                                     AlignOut o)
+{
+    __shared__ AlignLds L;
+    const int t = threadIdx.x;
+    for (int e = t; e < E; e += kAlignThreads)
+        L.a[e] = 0;
+    for (int i = t; i < kAlignWaves * E; i += kAlignThreads)
+        L.wcnt[i] = 0;
+    __syncthreads();
+    for (int64_t f = t; f < F; f += kAlignThreads) {
+        const int key = local_id(ids, f, F, eb, E);
+        if (key >= 0)
+            atomicAdd(&L.a[key], 1);
+    }
+    __syncthreads();
+    finish_scan(L.a, L.b, L.scratch, E, block_m, o);  // L.a now holds the offsets
+    scatter_chunk(ids, 0, F, eb, E, L.a, L.wcnt, o);
+}
+
+__global__ __launch_bounds__(kAlignThreads) void align_count_kernel(const int32_t* __restrict__ ids,
+                                                                    int64_t F, int64_t eb,
+                                                                    int64_t E,
+                                                                    int32_t* __restrict__ hist)
+{
+    __shared__ int cnt[kMaxLocalExperts];
+    const int t = threadIdx.x;
+    for (int e = t; e < E; e += kAlignThreads)
+        cnt[e] = 0;
+    __syncthreads();
+    const int64_t f0 = (int64_t)blockIdx.x * kAlignChunk;
+    const int64_t f1 = f0 + kAlignChunk < F ? f0 + kAlignChunk : F;
+    for (int64_t f = f0 + t; f < f1; f += kAlignThreads) {
+        const int key = local_id(ids, f, f1, eb, E);
+        if (key >= 0)
+            atomicAdd(&cnt[key], 1);
+    }
+    __syncthreads();
+    for (int e = t; e < E; e += kAlignThreads)
+        hist[(int64_t)blockIdx.x * E + e] = cnt[e];
+}
+
+__global__ __launch_bounds__(kAlignThreads) void align_scan_kernel(int32_t* __restrict__ hist,
+                                                                   int64_t nchunks, int64_t E,
+                                                                   int64_t block_m, AlignOut o)
+{
+    __shared__ AlignLds L;
+    const int t = threadIdx.x;
+    // per expert: chunk-exclusive prefix (in place) and the total
+    for (int e = t; e < E; e += kAlignThreads) {
+        int run = 0;
+        for (int64_t c = 0; c < nchunks; ++c) {
+            const int h = hist[c * E + e];
+            hist[c * E + e] = run;
+            run += h;
+        }
+        L.a[e] = run;
+    }
+    __syncthreads();
+    finish_scan(L.a, L.b, L.scratch, E, block_m, o);
+    for (int e = t; e < E; e += kAlignThreads) {
+        const int off = L.a[e];
+        for (int64_t c = 0; c < nchunks; ++c)
+            hist[c * E + e] += off;
+    }
+}
+
+__global__ __launch_bounds__(kAlignThreads) void align_scatter_kernel(const int32_t* __restrict__ ids,
+                                                                      int64_t F, int64_t eb,
+                                                                      int64_t E,
+                                                                      const int32_t* __restrict__ hist,
+                                                                      AlignOut o)
+{
+    __shared__ int base[kMaxLocalExperts];
+    __shared__ int wcnt[kAlignWaves * kMaxLocalExperts];
+    const int t = threadIdx.x;
+    for (int e = t; e < E; e += kAlignThreads)
+        base[e] = hist[(int64_t)blockIdx.x * E + e];
+    for (int i = t; i < kAlignWaves * E; i += kAlignThreads)
+        wcnt[i] = 0;
+    __syncthreads();
+    const int64_t f0 = (int64_t)blockIdx.x * kAlignChunk;
+    const int64_t f1 = f0 + kAlignChunk < F ? f0 + kAlignChunk : F;
+    scatter_chunk(ids, f0, f1, eb, E, base, wcnt, o);
+}
+
+hipError_t launch_align(const int32_t* ids, int64_t T, int64_t topk, int64_t expert_begin,
+                        int64_t E, int64_t block_m, const AlignOut& o, void* ws, hipStream_t s)
+{
+    const int64_t F = T * topk;
+    const int64_t nchunks = align_chunk_count(F);
+    if (nchunks == 1) {
+        hipLaunchKernelGGL(align_single_kernel, dim3(1), dim3(kAlignThreads), 0, s, ids, F,
+                           expert_begin, E, block_m, o);
+        return hipGetLastError();
+    }
+    int32_t* hist = (int32_t*)ws;
+    hipLaunchKernelGGL(align_count_kernel, dim3((unsigned)nchunks), dim3(kAlignThreads), 0, s, ids,
+                       F, expert_begin, E, hist);
+    hipLaunchKernelGGL(align_scan_kernel, dim3(1), dim3(kAlignThreads), 0, s, hist, nchunks, E,
+                       block_m, o);
+    hipLaunchKernelGGL(align_scatter_kernel, dim3((unsigned)nchunks), dim3(kAlignThreads), 0, s,
+                       ids, F, expert_begin, E, hist, o);
+    return hipGetLastError();
+}
+
+} // namespace w4a8

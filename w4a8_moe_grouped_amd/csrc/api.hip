@@ -1,0 +1,377 @@
+// api.hip -- the C ABI of libw4a8 (declared and documented in include/w4a8.h).
+//
+// Host-side only: argument validation (before any HIP call), workspace
+// planning and the launch sequence of each export.  No allocation, no
+// synchronisation, no state between calls.
+#include "w4a8.h"
+
+#include "internal.hpp"
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace {
+
+constexpr int64_t kMaxLocalExperts = 1024;
+constexpr size_t kAlign = 256;
+
+inline size_t round_up(size_t x)
+{
+    return (x + kAlign - 1) / kAlign * kAlign;
+}
+inline bool aligned16(const void* p)
+{
+    return ((uintptr_t)p & 15u) == 0;
+}
+
+// A bump allocator over the caller's workspace (or over nothing, to size it).
+struct Carve {
+    char* base;
+    size_t used = 0;
+    explicit Carve(void* b) : base((char*)b) {}
+    template <typename T>
+    T* take(size_t count)
+    {
+        T* p = base ? (T*)(base + used) : nullptr;
+        used += round_up(count * sizeof(T));
+        return p;
+    }
+};
+
+// rows per m-block for the skinny grouped GEMM: from the pairs each local
+// expert would get if every pair were local (the host does not see the routing)
+int pick_block_m(int64_t pairs, int64_t experts)
+{
+    const int64_t per = experts > 0 ? (pairs + experts - 1) / experts : pairs;
+    if (per <= 16)
+        return 16;
+    if (per <= 32)
+        return 32;
+    return 64;
+}
+
+int64_t ceil_div(int64_t a, int64_t b)
+{
+    return (a + b - 1) / b;
+}
+
+// The fused forward's workspace.  P is unknown on the host, so every
+// per-pair buffer is sized for F = T*topk pairs.
+struct MoePlan {
+    int block_m;
+    int64_t F, nb_max;
+    w4a8::AlignOut al;
+    void* align_ws;
+    uint8_t* qa;
+    float2* qa_side;
+    uint8_t* qh;
+    float2* qh_side;
+    float* y2;
+};
+
+size_t plan_moe(void* ws, int64_t T, int64_t H, int64_t topk, int64_t E, int64_t I, MoePlan& p)
+{
+    Carve c(ws);
+    p.F = T * topk;
+    p.block_m = pick_block_m(p.F, E);
+    p.nb_max = ceil_div(p.F, p.block_m) + E;
+    p.al.counts = c.take<int32_t>(E);
+    p.al.offsets = c.take<int32_t>(E + 1);
+    p.al.sorted = c.take<int32_t>(p.F);
+    p.al.src2dst = c.take<int32_t>(p.F);
+    p.al.block_expert = c.take<int32_t>(p.nb_max);
+    p.al.block_row = c.take<int32_t>(p.nb_max);
+    p.al.num_blocks = c.take<int32_t>(1);
+    p.align_ws = c.take<char>(w4a8::align_workspace_bytes(p.F, E));
+    p.qa = c.take<uint8_t>(T * H * 2);  // fp16 gate_up operand
+    p.qa_side = c.take<float2>(T * (H / W4A8_GROUP));
+    p.qh = c.take<uint8_t>(p.F * I);
+    p.qh_side = c.take<float2>(p.F * (I / W4A8_GROUP));
+    p.y2 = c.take<float>(p.F * H);
+    return c.used;
+}
+
+size_t plan_gemm(void* ws, int64_t M, int64_t K, uint8_t** q_il, float2** side)
+{
+    Carve c(ws);
+    *q_il = c.take<uint8_t>(M * K);
+    *side = c.take<float2>(M * (K / W4A8_GROUP));
+    return c.used;
+}
+
+int check_workspace(void* ws, size_t* bytes, size_t need)
+{
+    if (bytes == nullptr)
+        return W4A8_ERR_INVALID_ARG;
+    if (ws == nullptr) {
+        *bytes = need;
+        return W4A8_OK;
+    }
+    if (*bytes < need)
+        return W4A8_ERR_WORKSPACE;
+    if (!aligned16(ws))
+        return W4A8_ERR_UNSUPPORTED;
+    return -1;  // proceed
+}
+
+inline int hip_status(hipError_t e)
+{
+    return e == hipSuccess ? W4A8_OK : W4A8_ERR_HIP;
+}
+
+// events armed by w4a8_fused_moe_stage_events for the next call on this thread
+thread_local void* const* t_stage_events = nullptr;
+
+inline void mark(void* const* ev, int i, hipStream_t s)
+{
+    if (ev != nullptr)
+        (void)hipEventRecord((hipEvent_t)ev[i], s);
+}
+
+// largest K the skinny GEMM stages per-row side data for (LDS budget 48 KB)
+bool skinny_k_ok(int64_t K, int block_m)
+{
+    return (K / W4A8_GROUP) * block_m * 8 <= 48 * 1024;
+}
+
+}  // namespace
+
+extern "C" {
+
+int w4a8_version(void)
+{
+    return (0 << 16) | 1;
+}
+
+const char* w4a8_status_string(int status)
+{
+    switch (status) {
+    case W4A8_OK: return "ok";
+    case W4A8_ERR_INVALID_ARG: return "invalid argument";
+    case W4A8_ERR_UNSUPPORTED: return "unsupported shape or alignment";
+    case W4A8_ERR_WORKSPACE: return "workspace too small";
+    case W4A8_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+    }
+}
+
+int w4a8_quantize_act(const void* x_bf16, int64_t M, int64_t K, int64_t ldx, uint8_t* q_e4m3,
+                      float* scales, hipStream_t stream)
+{
+    if (M < 0 || K <= 0 || ldx < K)
+        return W4A8_ERR_INVALID_ARG;
+    if (M > 0 && (x_bf16 == nullptr || q_e4m3 == nullptr || scales == nullptr))
+        return W4A8_ERR_INVALID_ARG;
+    if (K % W4A8_GROUP != 0 || ldx % 8 != 0)
+        return W4A8_ERR_UNSUPPORTED;
+    if (!aligned16(x_bf16) || !aligned16(q_e4m3) || !aligned16(scales))
+        return W4A8_ERR_UNSUPPORTED;
+    if (M == 0)
+        return W4A8_OK;
+    return hip_status(w4a8::launch_quant_bf16((const uint16_t*)x_bf16, M, K, ldx, q_e4m3, scales,
+                                              nullptr, 0, stream));
+}
+
+int w4a8_gemm(const uint8_t* a_e4m3, const float* a_scales, int64_t M, int64_t K,
+              const uint8_t* b_int4, const float* b_scales, int64_t N, void* out_bf16,
+              void* workspace, size_t* workspace_bytes, hipStream_t stream)
+{
+    if (M < 0 || K <= 0 || N <= 0)
+        return W4A8_ERR_INVALID_ARG;
+    if (K % W4A8_GROUP != 0)
+        return W4A8_ERR_UNSUPPORTED;
+    const int block_m = M <= 16 ? 16 : (M <= 32 ? 32 : 64);
+    if (!skinny_k_ok(K, block_m))
+        return W4A8_ERR_UNSUPPORTED;
+    uint8_t* q_il;
+    float2* side;
+    const size_t need = plan_gemm(nullptr, M, K, &q_il, &side);
+    const int ws_rc = check_workspace(workspace, workspace_bytes, need);
+    if (ws_rc >= 0)
+        return ws_rc;
+    if (M > 0 && (a_e4m3 == nullptr || a_scales == nullptr || out_bf16 == nullptr))
+        return W4A8_ERR_INVALID_ARG;
+    if (b_int4 == nullptr || b_scales == nullptr)
+        return W4A8_ERR_INVALID_ARG;
+    if (!aligned16(a_e4m3) || !aligned16(b_int4) || !aligned16(out_bf16) ||
+        !aligned16(a_scales) || !aligned16(b_scales))
+        return W4A8_ERR_UNSUPPORTED;
+    if (M == 0)
+        return W4A8_OK;
+    plan_gemm(workspace, M, K, &q_il, &side);
+    hipError_t e = w4a8::launch_prep_codes(a_e4m3, a_scales, M, K, q_il, side, stream);
+    if (e != hipSuccess)
+        return W4A8_ERR_HIP;
+    w4a8::GemmArgs g = {};
+    g.act = q_il;
+    g.act_side = side;
+    g.sorted = nullptr;
+    g.topk = 1;
+    g.offsets = nullptr;
+    g.dense_rows = (int32_t)M;
+    g.w = b_int4;
+    g.ws = b_scales;
+    g.w_estride = 0;
+    g.s_estride = 0;
+    g.K = K;
+    g.N = N;
+    g.out_bf16 = (uint16_t*)out_bf16;
+    g.max_blocks = ceil_div(M, block_m);
+    return hip_status(w4a8::launch_gemm_skinny(g, w4a8::EPI_BF16, block_m, stream));
+}
+
+int w4a8_moe_align(const int32_t* topk_ids, int64_t T, int64_t topk, int64_t expert_begin,
+                   int64_t num_local_experts, int64_t block_m, int32_t* expert_counts,
+                   int32_t* expert_offsets, int32_t* sorted_pair_ids, int32_t* src2dst,
+                   int32_t* block_expert, int32_t* block_row, int32_t* num_blocks,
+                   void* workspace, size_t* workspace_bytes, hipStream_t stream)
+{
+    if (T < 0 || topk < 1 || num_local_experts < 1 || block_m < 1)
+        return W4A8_ERR_INVALID_ARG;
+    if (topk > W4A8_MAX_TOPK || num_local_experts > kMaxLocalExperts || T * topk > INT32_MAX / 2)
+        return W4A8_ERR_UNSUPPORTED;
+    const size_t need = round_up(w4a8::align_workspace_bytes(T * topk, num_local_experts));
+    const int ws_rc = check_workspace(workspace, workspace_bytes, need);
+    if (ws_rc >= 0)
+        return ws_rc;
+    if ((T > 0 && (topk_ids == nullptr || sorted_pair_ids == nullptr || src2dst == nullptr)) ||
+        expert_counts == nullptr || expert_offsets == nullptr || num_blocks == nullptr ||
+        ((block_expert == nullptr) != (block_row == nullptr)))
+        return W4A8_ERR_INVALID_ARG;
+    w4a8::AlignOut o = {expert_counts, expert_offsets, sorted_pair_ids, src2dst,
+                        block_expert, block_row, num_blocks};
+    return hip_status(w4a8::launch_align(topk_ids, T, topk, expert_begin, num_local_experts,
+                                         block_m, o, workspace, stream));
+}
+
+int w4a8_fused_moe(const void* hidden_bf16, int64_t T, int64_t H, const int32_t* topk_ids,
+                   const float* topk_weights, int64_t topk, int64_t expert_begin,
+                   int64_t num_local_experts, int64_t I, const uint8_t* w13_int4,
+                   const float* w13_scales, const uint8_t* w2_int4, const float* w2_scales,
+                   void* out_bf16, void* workspace, size_t* workspace_bytes, hipStream_t stream)
+{
+    const int64_t E = num_local_experts;
+    if (T < 0 || H <= 0 || I <= 0 || topk < 1 || E < 1)
+        return W4A8_ERR_INVALID_ARG;
+    if (H % W4A8_GROUP != 0 || I % W4A8_GROUP != 0 || topk > W4A8_MAX_TOPK ||
+        E > kMaxLocalExperts || T * topk > INT32_MAX / 2)
+        return W4A8_ERR_UNSUPPORTED;
+    MoePlan p;
+    const size_t need = plan_moe(nullptr, T, H, topk, E, I, p);
+    if (!skinny_k_ok(H, p.block_m) || !skinny_k_ok(I, p.block_m))
+        return W4A8_ERR_UNSUPPORTED;
+    const int ws_rc = check_workspace(workspace, workspace_bytes, need);
+    if (ws_rc >= 0)
+        return ws_rc;
+    if (T > 0 && (hidden_bf16 == nullptr || topk_ids == nullptr || topk_weights == nullptr ||
+                  out_bf16 == nullptr))
+        return W4A8_ERR_INVALID_ARG;
+    if (w13_int4 == nullptr || w13_scales == nullptr || w2_int4 == nullptr || w2_scales == nullptr)
+        return W4A8_ERR_INVALID_ARG;
+    if (!aligned16(hidden_bf16) || !aligned16(out_bf16) || !aligned16(w13_int4) ||
+        !aligned16(w2_int4) || !aligned16(w13_scales) || !aligned16(w2_scales))
+        return W4A8_ERR_UNSUPPORTED;
+    void* const* ev = t_stage_events;
+    t_stage_events = nullptr;
+    if (T == 0)
+        return W4A8_OK;
+    plan_moe(workspace, T, H, topk, E, I, p);
+
+    mark(ev, 0, stream);
+    hipError_t e = w4a8::launch_align(topk_ids, T, topk, expert_begin, E, p.block_m, p.al,
+                                      p.align_ws, stream);
+    if (e != hipSuccess)
+        return W4A8_ERR_HIP;
+    mark(ev, 1, stream);
+    e = w4a8::launch_quant_bf16((const uint16_t*)hidden_bf16, T, H, H, p.qa, nullptr, p.qa_side,
+                                2, stream);
+    if (e != hipSuccess)
+        return W4A8_ERR_HIP;
+    mark(ev, 2, stream);
+
+    w4a8::GemmArgs g = {};
+    g.block_expert = p.al.block_expert;
+    g.block_row = p.al.block_row;
+    g.num_blocks = p.al.num_blocks;
+    g.offsets = p.al.offsets;
+    g.max_blocks = p.nb_max;
+    // gate_up: rows gathered through the permutation, exact f16 MFMA path,
+    // SwiGLU + requant epilogue
+    g.act = p.qa;
+    g.f16 = 1;
+    g.act_side = p.qa_side;
+    g.sorted = p.al.sorted;
+    g.topk = (int32_t)topk;
+    g.w = w13_int4;
+    g.ws = w13_scales;
+    g.w_estride = 2 * I * (H / 2);
+    g.s_estride = 2 * I * (H / W4A8_GROUP);
+    g.K = H;
+    g.N = 2 * I;
+    g.I = I;
+    g.out_q = p.qh;
+    g.out_side = p.qh_side;
+    e = w4a8::launch_gemm_skinny(g, w4a8::EPI_SWIGLU_Q, p.block_m, stream);
+    if (e != hipSuccess)
+        return W4A8_ERR_HIP;
+    mark(ev, 3, stream);
+    // down: rows in pair order, fp8 MFMA path
+    g.act = p.qh;
+    g.f16 = 0;
+    g.act_side = p.qh_side;
+    g.sorted = nullptr;
+    g.w = w2_int4;
+    g.ws = w2_scales;
+    g.w_estride = H * (I / 2);
+    g.s_estride = H * (I / W4A8_GROUP);
+    g.K = I;
+    g.N = H;
+    g.out_f32 = p.y2;
+    e = w4a8::launch_gemm_skinny(g, w4a8::EPI_F32, p.block_m, stream);
+    if (e != hipSuccess)
+        return W4A8_ERR_HIP;
+    mark(ev, 4, stream);
+    e = w4a8::launch_combine(p.y2, p.al.src2dst, topk_weights, T, topk, H, (uint16_t*)out_bf16,
+                             stream);
+    if (e != hipSuccess)
+        return W4A8_ERR_HIP;
+    mark(ev, 5, stream);
+    return W4A8_OK;
+}
+
+int w4a8_fused_moe_workspace_layout(int64_t T, int64_t H, int64_t topk,
+                                    int64_t num_local_experts, int64_t I, size_t* offsets, int n,
+                                    int64_t* block_m)
+{
+    if (T < 0 || H <= 0 || I <= 0 || topk < 1 || num_local_experts < 1 || offsets == nullptr ||
+        n != 12 || block_m == nullptr)
+        return W4A8_ERR_INVALID_ARG;
+    MoePlan p;
+    // carve from a fake base so that pointers equal byte offsets (base != null)
+    char* const base = (char*)(uintptr_t)4096;
+    plan_moe(base, T, H, topk, num_local_experts, I, p);
+    const void* ptrs[12] = {p.al.counts, p.al.offsets, p.al.sorted, p.al.src2dst,
+                            p.al.block_expert, p.al.block_row, p.al.num_blocks, p.qa,
+                            p.qa_side, p.qh, p.qh_side, p.y2};
+    for (int i = 0; i < 12; ++i)
+        offsets[i] = (size_t)((const char*)ptrs[i] - base);
+    *block_m = p.block_m;
+    return W4A8_OK;
+}
+
+int w4a8_fused_moe_stage_events(void* const* events, int n)
+{
+    if (n == 0) {
+        t_stage_events = nullptr;
+        return W4A8_OK;
+    }
+    if (n != 6 || events == nullptr)
+        return W4A8_ERR_INVALID_ARG;
+    for (int i = 0; i < 6; ++i)
+        if (events[i] == nullptr)
+            return W4A8_ERR_INVALID_ARG;
+    t_stage_events = events;
+    return W4A8_OK;
+}
+
+}  // extern "C"

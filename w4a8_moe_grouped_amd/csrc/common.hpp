@@ -1,0 +1,207 @@
+// common.hpp -- device helpers shared by the libw4a8 kernels (gfx950 / CDNA4).
+//
+// Conventions used by every kernel of the library:
+//
+//  * fp8 is OCP e4m3 (max 448).  Quantising one 128-wide block of a row
+//    (DeepGEMM PR #53, commit note dropping UE8M0; SGLang PR #37796, part-1
+//    fp8 KV notes): amax -> max(amax, 1e-10f) -> inv = 448/amax_c,
+//    scale = amax_c/448 -> code = e4m3(clamp(x*inv, +-448)), round to nearest
+//    even.  gfx950's v_cvt_pk_fp8_f32 rounds to nearest even into OCP e4m3
+//    and keeps subnormals; the clamp comes first because the conversion does
+//    not saturate.
+//
+//  * int4 -> fp8 without a table.  A weight nibble n (two's complement value
+//    v = n - 16*(n >= 8)) is turned into u = n ^ 8 = v + 8 in 0..15, and the
+//    byte u is used directly as an e4m3 code: codes 0x00..0x0F are exactly
+//    u * 2^-9 (subnormals 0..7, then the first binade 8..15).  So one MFMA
+//    over a 128-group returns raw = 2^-9 * sum_k a_k * (v_k + 8) and
+//        sum_k a_k * v_k = 512 * raw - 8 * S,   S = sum_k a_k.
+//    S is produced with the activation codes by the quantiser, and the
+//    promotion of each group folds both constants into one FMA:
+//        y += w_scale * fma(raw, c1, c0),  c1 = 512*a_scale, c0 = -8*a_scale*S.
+//
+//  * Internal fp8 activation layout (down / dense operand).  The unpack of
+//    one packed dword x (8 nibbles k0..k7) gives lo = bytes k0,k2,k4,k6 and
+//    hi = k1,k3,k5,k7, so activation codes are stored in that order inside
+//    every aligned group of 8 K-positions: the bytes an MFMA lane holds for
+//    the weights and for the activations always name the same k.  The 16
+//    such 8-groups of a 128-group are then placed so that one 16-byte load
+//    per lane reads 64 contiguous bytes per row: 8-group b (k = 8b..8b+7) sits
+//    at byte 16*(4*((b%4)/2) + b/4) + 8*(b%2) of the group (fp8_group_pos).
+//    Per-row-per-group side data is float2 {c1, c0}.
+//
+//  * Internal fp16 activation layout (gate_up operand): the exact e4m3
+//    values as fp16, ordered k0,k4,k1,k5,k2,k6,k3,k7 inside every aligned
+//    group of 8 (the order unpack_int4_f16 produces); 8-group b sits at
+//    16-byte chunk 4*(b%4) + b/4 of the 256-byte group (f16_group_chunk), so
+//    again one 16-byte load per lane reads 64 contiguous bytes per row.  Side
+//    data {scale, 0}.
+//
+//  * MFMA v_mfma_f32_16x16x128_f8f6f4 (fp8 x fp8): lane l holds row l%16 of
+//    A and column l%16 of B, 32 K-bytes each (the lane's quarter q = l/16 of
+//    the 128-group); the result D[4*q + r][l%16] sits in register r.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w4a8 {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+
+constexpr int kGroup = 128;
+
+// byte offset of 8-group b (k = 8b..8b+7) inside a 128-byte fp8 activation group
+__host__ __device__ constexpr int fp8_group_pos(int b)
+{
+    return 16 * (4 * ((b % 4) / 2) + b / 4) + 8 * (b % 2);
+}
+// 16-byte chunk of 8-group b inside a 256-byte fp16 activation group
+__host__ __device__ constexpr int f16_group_chunk(int b)
+{
+    return 4 * (b % 4) + b / 4;
+}
+
+// One 16x16x128 fp8 MFMA (no block scales).
+__device__ __forceinline__ v4f mfma16x16x128(const v8i& a, const v8i& b, const v4f& c)
+{
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// One 16x16x32 f16 MFMA.  Unlike the fp8 forms, whose internal adder keeps
+// only ~13 bits below the largest product of a lane's slice, the f16 MFMA
+// returns the exactly rounded fp32 sum for these operands (int4 x e4m3
+// values), which the gate_up GEMM needs: its output is re-quantised to fp8,
+// and a relative error of a few 1e-6 there flips enough codes to move the
+// final output by ~1e-3.
+__device__ __forceinline__ v4f mfma16x16x32_f16(const v8h& a, const v8h& b, const v4f& c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// v_bitop3_b32 computing ((x ^ k) & m) | c for constant k, m, c in one
+// instruction: with A = ~m and B = (m & k) | (~m & c), the 3-input function
+// F(x, A, B) = A ? B : x ^ B (truth table 0x9A for inputs ordered x, A, B)
+// yields x, ~x, 0 or 1 bit by bit as required.
+template <uint32_t K, uint32_t M, uint32_t C>
+__device__ __forceinline__ uint32_t xor_and_or(uint32_t x)
+{
+    constexpr uint32_t A = ~M, B = (M & K) | (~M & C);
+    return __builtin_amdgcn_bitop3_b32(x, A, B, 0x9A);
+}
+
+// 4 bytes of packed int4 (k0..k7) -> 8 exact fp16 values in the order
+// k0,k4,k1,k5,k2,k6,k3,k7: with u = n ^ 8 = v + 8, the half 0x6400|u is
+// 1024 + u, and subtracting 1032 leaves v.
+__device__ __forceinline__ v8h unpack_int4_f16(uint32_t x)
+{
+    constexpr uint32_t k = 0x00080008u, m = 0x000F000Fu, magic = 0x64006400u;
+    const uint32_t d[4] = {xor_and_or<k, m, magic>(x), xor_and_or<k, m, magic>(x >> 4),
+                           xor_and_or<k, m, magic>(x >> 8), xor_and_or<k, m, magic>(x >> 12)};
+    const v2h bias = {(_Float16)1032.0f, (_Float16)1032.0f};
+    v8h r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const v2h h = __builtin_bit_cast(v2h, d[i]) - bias;
+        r[2 * i] = h[0];
+        r[2 * i + 1] = h[1];
+    }
+    return r;
+}
+
+// 16 bytes of packed int4 (32 nibbles) -> 32 fp8 bytes (u * 2^-9 codes) in
+// the K-interleaved order described above.
+__device__ __forceinline__ v8i unpack_int4_u(const v4i& w)
+{
+    v8i r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t x = (uint32_t)w[i];
+        r[2 * i] = (int)xor_and_or<0x08080808u, 0x0F0F0F0Fu, 0u>(x);
+        r[2 * i + 1] = (int)xor_and_or<0x08080808u, 0x0F0F0F0Fu, 0u>(x >> 4);
+    }
+    return r;
+}
+
+// canonical 8 codes (two dwords k0..k3, k4..k7) -> interleaved (k0,k2,k4,k6 | k1,k3,k5,k7)
+__device__ __forceinline__ void interleave8(uint32_t d0, uint32_t d1, uint32_t& lo, uint32_t& hi)
+{
+    lo = __builtin_amdgcn_perm(d1, d0, 0x06040200u);
+    hi = __builtin_amdgcn_perm(d1, d0, 0x07050301u);
+}
+
+// e4m3 code of clamp(v, -448, 448), round to nearest even; two values at once
+__device__ __forceinline__ uint32_t cvt_e4m3x2(float a, float b)
+{
+    a = __builtin_fminf(__builtin_fmaxf(a, -448.0f), 448.0f);
+    b = __builtin_fminf(__builtin_fmaxf(b, -448.0f), 448.0f);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
+}
+
+// exact decode of two e4m3 codes in the low half-word
+__device__ __forceinline__ float2 dec_e4m3x2(uint32_t codes16)
+{
+    auto f = __builtin_amdgcn_cvt_pk_f32_fp8((int)codes16, false);
+    return make_float2(f[0], f[1]);
+}
+
+// 448 / amax_c rounded once to fp32: the fp64 quotient rounded to fp32 equals
+// the correctly rounded fp32 quotient (53 >= 2*24 + 2, so double rounding is
+// innocuous for division).
+__device__ __forceinline__ float recip448(float amax_c)
+{
+    return (float)(448.0 / (double)amax_c);
+}
+__device__ __forceinline__ float scale_of(float amax_c)
+{
+    return (float)((double)amax_c / 448.0);
+}
+__device__ __forceinline__ float clamp_amax(float amax)
+{
+    return amax > 1e-10f ? amax : 1e-10f;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b)
+{
+    return __uint_as_float((uint32_t)b << 16);
+}
+// fp32 -> bf16, round to nearest even (finite inputs)
+__device__ __forceinline__ uint16_t f32_to_bf16(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// butterfly reductions over aligned lane groups of width W (power of two <= 64)
+template <int W>
+__device__ __forceinline__ float group_max(float v)
+{
+#pragma unroll
+    for (int o = W / 2; o > 0; o >>= 1)
+        v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+template <int W>
+__device__ __forceinline__ float group_sum(float v)
+{
+#pragma unroll
+    for (int o = W / 2; o > 0; o >>= 1)
+        v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+__device__ __forceinline__ v4i ldg16(const void* p)
+{
+    return *(const v4i*)p;
+}
+__device__ __forceinline__ v4i ldg16_nt(const void* p)
+{
+    return __builtin_nontemporal_load((const v4i*)p);
+}
+
+} // namespace w4a8

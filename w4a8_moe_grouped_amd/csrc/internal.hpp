@@ -1,0 +1,75 @@
+// internal.hpp -- host-side launchers shared between the translation units of
+// libw4a8.  Not part of the public ABI (see include/w4a8.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace w4a8 {
+
+// ---- activation quantisation (quant.hip) ----
+// mode 0: canonical codes + fp32 scales (the public export)
+// mode 1: K-interleaved codes + {c1, c0} side data (fp8 GEMM operand)
+// mode 2: exact fp16 values (k0,k4,k1,k5,... per 8) + {scale, 0} (f16 GEMM operand);
+//         q is then a [M, K] fp16 buffer
+hipError_t launch_quant_bf16(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
+                             float* scales, float2* side, int mode, hipStream_t s);
+// canonical codes + scales (from w4a8_quantize_act) -> interleaved codes + side data
+hipError_t launch_prep_codes(const uint8_t* q, const float* scales, int64_t M, int64_t K,
+                             uint8_t* q_il, float2* side, hipStream_t s);
+
+// ---- routing permutation (align.hip) ----
+struct AlignOut {
+    int32_t* counts;        // [E]
+    int32_t* offsets;       // [E+1]
+    int32_t* sorted;        // [F]
+    int32_t* src2dst;       // [F]
+    int32_t* block_expert;  // [nb_max] or null
+    int32_t* block_row;     // [nb_max] or null
+    int32_t* num_blocks;    // [1]
+};
+int64_t align_chunk_count(int64_t F);
+size_t align_workspace_bytes(int64_t F, int64_t E);
+hipError_t launch_align(const int32_t* ids, int64_t T, int64_t topk, int64_t expert_begin,
+                        int64_t E, int64_t block_m, const AlignOut& o, void* ws, hipStream_t s);
+
+// ---- grouped GEMMs (gemm_skinny.hip) ----
+struct GemmArgs {
+    // activation operand, row stride K elements, + side data [rows, K/128]:
+    // fp8 path: K-interleaved codes; f16 path (f16 != 0): fp16 values
+    const uint8_t* act;
+    int f16;
+    const float2* act_side;
+    // row map: GEMM row p of an m-block -> activation row.  If sorted != null,
+    // act_row = sorted[p] / topk (gather through the permutation), else p.
+    const int32_t* sorted;
+    int32_t topk;
+    // m-blocks
+    const int32_t* block_expert;
+    const int32_t* block_row;
+    const int32_t* num_blocks;
+    const int32_t* offsets;  // [E+1] segment ends (rows of expert e: [offsets[e], offsets[e+1]))
+    int32_t dense_rows;      // used when offsets == null: rows [0, dense_rows)
+    // weights of expert e: w + e*w_estride, scales ws + e*s_estride; row n at n*K/2, n*K/128
+    const uint8_t* w;
+    const float* ws;
+    int64_t w_estride, s_estride;
+    int64_t K;       // reduction length
+    int64_t N;       // output features of the weight matrix
+    int64_t I;       // SwiGLU epilogue: intermediate size (gate rows [0,I), up rows [I,2I))
+    // outputs
+    float* out_f32;        // [rows, N]           (store epilogue)
+    uint16_t* out_bf16;    // [rows, N]           (bf16 epilogue)
+    uint8_t* out_q;        // [rows, I] codes     (SwiGLU+requant epilogue, interleaved)
+    float2* out_side;      // [rows, I/128]
+    int64_t max_blocks;    // grid bound on m-blocks
+};
+enum Epilogue { EPI_F32 = 0, EPI_BF16 = 1, EPI_SWIGLU_Q = 2 };
+hipError_t launch_gemm_skinny(const GemmArgs& a, int epilogue, int block_m, hipStream_t s);
+
+// ---- combine (combine.hip) ----
+hipError_t launch_combine(const float* y2, const int32_t* src2dst, const float* topk_w,
+                          int64_t T, int64_t topk, int64_t H, uint16_t* out, hipStream_t s);
+
+} // namespace w4a8

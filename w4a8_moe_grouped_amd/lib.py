@@ -1,0 +1,261 @@
+"""Thin Python binding of libw4a8 (include/w4a8.h).
+
+Argument marshalling only: torch supplies device memory and the current HIP
+stream, every step of the computation runs in the library's HIP kernels.
+There is no fallback: if libw4a8.so is missing or the call fails, an
+exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libw4a8.so")
+
+W4A8_OK = 0
+GROUP = 128
+EXPORTS = ("w4a8_version", "w4a8_status_string", "w4a8_quantize_act", "w4a8_gemm",
+           "w4a8_moe_align", "w4a8_fused_moe", "w4a8_fused_moe_workspace_layout",
+           "w4a8_fused_moe_stage_events")
+
+_lock = threading.Lock()
+_lib = None
+
+
+class W4A8Error(RuntimeError):
+    pass
+
+
+def load(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load libw4a8.so (built by ``python -m w4a8_moe_grouped_amd.build``)."""
+    global _lib
+    with _lock:
+        if _lib is not None and path is None:
+            return _lib
+        p = path or LIB_PATH
+        if not os.path.exists(p):
+            raise W4A8Error("libw4a8.so not built at %s (run python -m w4a8_moe_grouped_amd.build)" % p)
+        L = ctypes.CDLL(p)
+        vp, i64, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.POINTER(ctypes.c_size_t)
+        L.w4a8_version.restype = ctypes.c_int
+        L.w4a8_version.argtypes = []
+        L.w4a8_status_string.restype = ctypes.c_char_p
+        L.w4a8_status_string.argtypes = [ctypes.c_int]
+        L.w4a8_quantize_act.restype = ctypes.c_int
+        L.w4a8_quantize_act.argtypes = [vp, i64, i64, i64, vp, vp, vp]
+        L.w4a8_gemm.restype = ctypes.c_int
+        L.w4a8_gemm.argtypes = [vp, vp, i64, i64, vp, vp, i64, vp, vp, sz, vp]
+        L.w4a8_moe_align.restype = ctypes.c_int
+        L.w4a8_moe_align.argtypes = [vp, i64, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp,
+                                     vp, sz, vp]
+        L.w4a8_fused_moe.restype = ctypes.c_int
+        L.w4a8_fused_moe.argtypes = [vp, i64, i64, vp, vp, i64, i64, i64, i64, vp, vp, vp, vp,
+                                     vp, vp, sz, vp]
+        L.w4a8_fused_moe_workspace_layout.restype = ctypes.c_int
+        L.w4a8_fused_moe_workspace_layout.argtypes = [i64, i64, i64, i64, i64,
+                                                      ctypes.POINTER(ctypes.c_size_t), ctypes.c_int,
+                                                      ctypes.POINTER(ctypes.c_int64)]
+        L.w4a8_fused_moe_stage_events.restype = ctypes.c_int
+        L.w4a8_fused_moe_stage_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
+        if path is None:
+            _lib = L
+        return L
+
+
+def _check(rc: int, what: str):
+    if rc != W4A8_OK:
+        msg = load().w4a8_status_string(rc).decode()
+        raise W4A8Error("%s failed: %s (%d)" % (what, msg, rc))
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise W4A8Error("all tensors must be on the GPU")
+
+
+# ---- workspace sizes (host-only queries) ----------------------------------------
+
+def gemm_workspace_bytes(M: int, K: int, N: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load().w4a8_gemm(None, None, M, K, None, None, N, None, None, ctypes.byref(n), None),
+           "w4a8_gemm(query)")
+    return n.value
+
+
+def align_workspace_bytes(T: int, topk: int, num_local_experts: int, block_m: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load().w4a8_moe_align(None, T, topk, 0, num_local_experts, block_m, None, None, None,
+                                 None, None, None, None, None, ctypes.byref(n), None),
+           "w4a8_moe_align(query)")
+    return n.value
+
+
+def fused_moe_workspace_bytes(T: int, H: int, topk: int, num_local_experts: int, I: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load().w4a8_fused_moe(None, T, H, None, None, topk, 0, num_local_experts, I, None, None,
+                                 None, None, None, None, ctypes.byref(n), None),
+           "w4a8_fused_moe(query)")
+    return n.value
+
+
+LAYOUT_KEYS = ("counts", "offsets", "sorted_pair_ids", "src2dst", "block_expert", "block_row",
+               "num_blocks", "qa16", "qa_side", "qh", "qh_side", "y2")
+
+
+def fused_moe_workspace_layout(T: int, H: int, topk: int, num_local_experts: int, I: int):
+    """Byte offsets of the intermediates inside the fused forward's workspace."""
+    offs = (ctypes.c_size_t * 12)()
+    bm = ctypes.c_int64(0)
+    _check(load().w4a8_fused_moe_workspace_layout(T, H, topk, num_local_experts, I, offs, 12,
+                                                  ctypes.byref(bm)),
+           "w4a8_fused_moe_workspace_layout")
+    d = dict(zip(LAYOUT_KEYS, [int(o) for o in offs]))
+    d["block_m"] = int(bm.value)
+    return d
+
+
+# ---- exports ----------------------------------------------------------------------
+
+def quantize_act(x: torch.Tensor, out_q: Optional[torch.Tensor] = None,
+                 out_scales: Optional[torch.Tensor] = None):
+    """bf16 [M, K] -> (uint8 e4m3 codes [M, K], fp32 scales [M, K/128])."""
+    _need_cuda(x)
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.stride(1) != 1:
+        raise W4A8Error("x must be a 2-D bf16 tensor with unit column stride")
+    M, K = x.shape
+    q = out_q if out_q is not None else torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    s = out_scales if out_scales is not None else \
+        torch.empty((M, K // GROUP), dtype=torch.float32, device=x.device)
+    _check(load().w4a8_quantize_act(_ptr(x), M, K, x.stride(0), _ptr(q), _ptr(s), _stream(x.device)),
+           "w4a8_quantize_act")
+    return q, s
+
+
+def gemm(a_q: torch.Tensor, a_scales: torch.Tensor, w: torch.Tensor, w_scales: torch.Tensor,
+         out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """codes [M, K] x packed int4 [N, K/2] -> bf16 [M, N]."""
+    _need_cuda(a_q, a_scales, w, w_scales)
+    M, K = a_q.shape
+    N = w.shape[0]
+    assert w.shape == (N, K // 2) and a_scales.shape == (M, K // GROUP) \
+        and w_scales.shape == (N, K // GROUP)
+    out = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=a_q.device)
+    need = gemm_workspace_bytes(M, K, N)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=a_q.device)
+    n = ctypes.c_size_t(workspace.numel())
+    _check(load().w4a8_gemm(_ptr(a_q), _ptr(a_scales), M, K, _ptr(w), _ptr(w_scales), N,
+                            _ptr(out), _ptr(workspace), ctypes.byref(n), _stream(a_q.device)),
+           "w4a8_gemm")
+    return out
+
+
+def moe_align(topk_ids: torch.Tensor, expert_begin: int, num_local_experts: int, block_m: int):
+    """Routing permutation; returns a dict of device tensors (see w4a8.h)."""
+    _need_cuda(topk_ids)
+    T, k = topk_ids.shape
+    F = T * k
+    E = num_local_experts
+    dev = topk_ids.device
+    nb_max = (F + block_m - 1) // block_m + E
+    o = dict(counts=torch.empty(E, dtype=torch.int32, device=dev),
+             offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
+             sorted_pair_ids=torch.empty(max(F, 1), dtype=torch.int32, device=dev),
+             src2dst=torch.empty(max(F, 1), dtype=torch.int32, device=dev),
+             block_expert=torch.empty(max(nb_max, 1), dtype=torch.int32, device=dev),
+             block_row=torch.empty(max(nb_max, 1), dtype=torch.int32, device=dev),
+             num_blocks=torch.empty(1, dtype=torch.int32, device=dev))
+    need = align_workspace_bytes(T, k, E, block_m)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    n = ctypes.c_size_t(ws.numel())
+    _check(load().w4a8_moe_align(_ptr(topk_ids), T, k, expert_begin, E, block_m,
+                                 _ptr(o["counts"]), _ptr(o["offsets"]), _ptr(o["sorted_pair_ids"]),
+                                 _ptr(o["src2dst"]), _ptr(o["block_expert"]), _ptr(o["block_row"]),
+                                 _ptr(o["num_blocks"]), _ptr(ws), ctypes.byref(n), _stream(dev)),
+           "w4a8_moe_align")
+    return o
+
+
+STAGES = ("align", "quant", "gate_up", "down", "combine")
+
+
+class StageTimer:
+    """HIP events around the five stages of the next fused_moe call(s).
+
+    Uses the HIP runtime's own event API (through ctypes) so the events sit on
+    the very stream the library launches on."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.ev = (ctypes.c_void_p * 6)()
+        for i in range(6):
+            h = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(h)) != 0:
+                raise W4A8Error("hipEventCreate failed")
+            self.ev[i] = h
+
+    def arm(self):
+        _check(load().w4a8_fused_moe_stage_events(self.ev, 6), "w4a8_fused_moe_stage_events")
+
+    def read_ms(self):
+        """Per-stage milliseconds of the last armed call (synchronises on its last event)."""
+        self.hip.hipEventSynchronize(self.ev[5])
+        out = []
+        for i in range(5):
+            ms = ctypes.c_float()
+            self.hip.hipEventElapsedTime(ctypes.byref(ms), self.ev[i], self.ev[i + 1])
+            out.append(ms.value)
+        return dict(zip(STAGES, out))
+
+    def close(self):
+        for i in range(6):
+            self.hip.hipEventDestroy(self.ev[i])
+
+
+def fused_moe(hidden: torch.Tensor, topk_ids: torch.Tensor, topk_weights: torch.Tensor,
+              expert_begin: int, num_local_experts: int, w13: torch.Tensor, s13: torch.Tensor,
+              w2: torch.Tensor, s2: torch.Tensor, out: Optional[torch.Tensor] = None,
+              workspace: Optional[torch.Tensor] = None):
+    """The fused forward; bf16 [T, H] out."""
+    _need_cuda(hidden, topk_ids, topk_weights, w13, s13, w2, s2)
+    T, H = hidden.shape
+    k = topk_ids.shape[1]
+    E = num_local_experts
+    I = w2.shape[2] * 2
+    assert hidden.dtype == torch.bfloat16 and topk_ids.dtype == torch.int32 \
+        and topk_weights.dtype == torch.float32
+    assert w13.shape == (E, 2 * I, H // 2) and s13.shape == (E, 2 * I, H // GROUP)
+    assert w2.shape == (E, H, I // 2) and s2.shape == (E, H, I // GROUP)
+    assert topk_ids.shape == (T, k) and topk_weights.shape == (T, k)
+    for t in (hidden, topk_ids, topk_weights, w13, s13, w2, s2):
+        assert t.is_contiguous()
+    out = out if out is not None else torch.empty((T, H), dtype=torch.bfloat16, device=hidden.device)
+    if workspace is None:
+        need = fused_moe_workspace_bytes(T, H, k, E, I)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=hidden.device)
+    n = ctypes.c_size_t(workspace.numel())
+    _check(load().w4a8_fused_moe(_ptr(hidden), T, H, _ptr(topk_ids), _ptr(topk_weights), k,
+                                 expert_begin, E, I, _ptr(w13), _ptr(s13), _ptr(w2), _ptr(s2),
+                                 _ptr(out), _ptr(workspace), ctypes.byref(n),
+                                 _stream(hidden.device)),
+           "w4a8_fused_moe")
+    return out

@@ -25,7 +25,9 @@ benchmark configurations):
 """
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
+import os
 from typing import Dict, Optional
 
 import numpy as np
@@ -33,7 +35,8 @@ import numpy as np
 GOLDEN = np.uint64(0x9E3779B97F4A7C15)
 _M1 = np.uint64(0xBF58476D1CE4E5B9)
 _M2 = np.uint64(0x94D049BB133111EB)
-_CHUNK = 1 << 22
+_CHUNK = 1 << 21
+_WORKERS = max(1, min(16, os.cpu_count() or 1))
 
 STREAM_LOGITS, STREAM_X, STREAM_OUTLIER, STREAM_W13, STREAM_S13, STREAM_W2, STREAM_S2, \
     STREAM_PERM = 1, 2, 3, 4, 5, 6, 7, 8
@@ -61,14 +64,30 @@ def draw_uniform(seed: int, stream: int, start: int, count: int) -> np.ndarray:
     return u.astype(np.float64) * (1.0 / 9007199254740992.0)
 
 
+def _parallel_chunks(total: int, fn) -> None:
+    """Run fn(c0, c1) over [0, total) in chunks; numpy releases the GIL inside
+    its ufuncs, so threads overlap.  Each chunk depends only on its own counter
+    range, so the result does not depend on the scheduling."""
+    spans = [(c0, min(total, c0 + _CHUNK)) for c0 in range(0, total, _CHUNK)]
+    if len(spans) <= 1:
+        for c0, c1 in spans:
+            fn(c0, c1)
+        return
+    with concurrent.futures.ThreadPoolExecutor(max_workers=_WORKERS) as ex:
+        for _ in ex.map(lambda sp: fn(*sp), spans):
+            pass
+
+
 def draw_normal(seed: int, stream: int, start: int, count: int) -> np.ndarray:
     """N(0, 1) doubles; normal i uses uniforms 2i and 2i+1 (Box-Muller, cos branch)."""
     out = np.empty(count, np.float64)
-    for c0 in range(0, count, _CHUNK):
-        c1 = min(count, c0 + _CHUNK)
+
+    def fill(c0, c1):
         u = draw_uniform(seed, stream, 2 * (start + c0), 2 * (c1 - c0))
         u1, u2 = u[0::2], u[1::2]
         out[c0:c1] = np.sqrt(-2.0 * np.log1p(-u1)) * np.cos(2.0 * np.pi * u2)
+
+    _parallel_chunks(count, fill)
     return out
 
 
@@ -76,9 +95,11 @@ def draw_bytes(seed: int, stream: int, count: int) -> np.ndarray:
     """Uniform random bytes: byte b of draw i is element 8i+b (little endian)."""
     n64 = (count + 7) // 8
     out = np.empty(n64 * 8, np.uint8)
-    for c0 in range(0, n64, _CHUNK):
-        c1 = min(n64, c0 + _CHUNK)
+
+    def fill(c0, c1):
         out[8 * c0:8 * c1] = draw_u64(seed, stream, c0, c1 - c0).view(np.uint8)
+
+    _parallel_chunks(n64, fill)
     return out[:count]
 
 
@@ -149,8 +170,14 @@ CONFIGS: Dict[str, object] = {
 def gen_hidden(cfg: MoEConfig, t0: int = 0, t1: Optional[int] = None) -> np.ndarray:
     """bf16 bits [t1-t0, H] of tokens t0..t1-1 (stream 2, element t*H + h)."""
     t1 = cfg.T if t1 is None else t1
-    z = draw_normal(cfg.seed, STREAM_X, t0 * cfg.H, (t1 - t0) * cfg.H)
-    return to_bf16_bits(z).reshape(t1 - t0, cfg.H)
+    n = (t1 - t0) * cfg.H
+    out = np.empty(n, np.uint16)
+
+    def fill(c0, c1):
+        out[c0:c1] = to_bf16_bits(draw_normal(cfg.seed, STREAM_X, t0 * cfg.H + c0, c1 - c0))
+
+    _parallel_chunks(n, fill)
+    return out.reshape(t1 - t0, cfg.H)
 
 
 def popularity_ranks(cfg: MoEConfig) -> np.ndarray:
