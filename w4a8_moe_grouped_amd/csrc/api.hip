@@ -83,7 +83,7 @@ size_t plan_moe(void* ws, int64_t T, int64_t H, int64_t topk, int64_t E, int64_t
     p.al.block_row = c.take<int32_t>(p.nb_max);
     p.al.num_blocks = c.take<int32_t>(1);
     p.align_ws = c.take<char>(w4a8::align_workspace_bytes(p.F, E));
-    p.qa = c.take<uint8_t>(T * H * 2);  // fp16 gate_up operand
+    p.qa = c.take<uint8_t>(T * H);  // fp8 gate_up operand
     p.qa_side = c.take<float2>(T * (H / W4A8_GROUP));
     p.qh = c.take<uint8_t>(p.F * I);
     p.qh_side = c.take<float2>(p.F * (I / W4A8_GROUP));
@@ -204,6 +204,7 @@ int w4a8_gemm(const uint8_t* a_e4m3, const float* a_scales, int64_t M, int64_t K
         return W4A8_ERR_HIP;
     w4a8::GemmArgs g = {};
     g.act = q_il;
+    g.act_rows = M;
     g.act_side = side;
     g.sorted = nullptr;
     g.topk = 1;
@@ -298,6 +299,7 @@ int w4a8_fused_moe(const void* hidden_bf16, int64_t T, int64_t H, const int32_t*
     // gate_up: rows gathered through the permutation, exact f16 MFMA path,
     // SwiGLU + requant epilogue
     g.act = p.qa;
+    g.act_rows = T;
     g.f16 = 1;
     g.act_side = p.qa_side;
     g.sorted = p.al.sorted;
@@ -317,6 +319,7 @@ int w4a8_fused_moe(const void* hidden_bf16, int64_t T, int64_t H, const int32_t*
     mark(ev, 3, stream);
     // down: rows in pair order, fp8 MFMA path
     g.act = p.qh;
+    g.act_rows = p.F;
     g.f16 = 0;
     g.act_side = p.qh_side;
     g.sorted = nullptr;

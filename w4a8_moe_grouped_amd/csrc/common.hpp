@@ -30,12 +30,11 @@
 //    at byte 16*(4*((b%4)/2) + b/4) + 8*(b%2) of the group (fp8_group_pos).
 //    Per-row-per-group side data is float2 {c1, c0}.
 //
-//  * Internal fp16 activation layout (gate_up operand): the exact e4m3
-//    values as fp16, ordered k0,k4,k1,k5,k2,k6,k3,k7 inside every aligned
-//    group of 8 (the order unpack_int4_f16 produces); 8-group b sits at
-//    16-byte chunk 4*(b%4) + b/4 of the 256-byte group (f16_group_chunk), so
-//    again one 16-byte load per lane reads 64 contiguous bytes per row.  Side
-//    data {scale, 0}.
+//  * Internal gate_up activation layout: fp8 codes ordered k0,k4,k1,k5 |
+//    k2,k6,k3,k7 inside every aligned group of 8, so that each 16-bit pair
+//    converts (v_cvt_scalef32_pk_f16_fp8, exact) into the f16 pair the int4
+//    unpack produces for the same k's; 8-groups placed by fp8_group_pos.
+//    Side data {scale, 0}.
 //
 //  * MFMA v_mfma_f32_16x16x128_f8f6f4 (fp8 x fp8): lane l holds row l%16 of
 //    A and column l%16 of B, 32 K-bytes each (the lane's quarter q = l/16 of
@@ -59,11 +58,6 @@ constexpr int kGroup = 128;
 __host__ __device__ constexpr int fp8_group_pos(int b)
 {
     return 16 * (4 * ((b % 4) / 2) + b / 4) + 8 * (b % 2);
-}
-// 16-byte chunk of 8-group b inside a 256-byte fp16 activation group
-__host__ __device__ constexpr int f16_group_chunk(int b)
-{
-    return 4 * (b % 4) + b / 4;
 }
 
 // One 16x16x128 fp8 MFMA (no block scales).
@@ -193,6 +187,23 @@ __device__ __forceinline__ float group_sum(float v)
     for (int o = W / 2; o > 0; o >>= 1)
         v += __shfl_xor(v, o, 64);
     return v;
+}
+
+// Raw buffer resource over [base, base + bytes) (bytes < 2^32): loads take a
+// 32-bit per-lane offset plus a wave-uniform (scalar) offset, so a streaming
+// loop keeps its per-group advance in an SGPR instead of 64-bit VGPR pointers.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+__device__ __forceinline__ v4i bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
+}
+__device__ __forceinline__ float bload4f(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0));
 }
 
 __device__ __forceinline__ v4i ldg16(const void* p)

@@ -29,24 +29,23 @@
 namespace w4a8 {
 
 constexpr int kNF = 4;  // weight fragments (16 rows) per wave
+
 constexpr int kWaves = 4;
 
-template <int NT, int EPI, int D, bool F16>
+template <int NT, int EPI, int DW, bool F16, bool SW4>
 __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs a)
 {
     constexpr int BM = 16 * NT;
-    constexpr int ESZ = F16 ? 2 : 1;   // activation element size
-    constexpr int AV = F16 ? 4 : 2;    // 16-byte activation loads per lane per group
     extern __shared__ float4 lds_side4[];  // [G][BM] float2 {c1, c0}, 16-byte aligned
     float2* lds_side = (float2*)lds_side4;
-    __shared__ int s_rows[BM];
     __shared__ float s_red[kWaves][BM];
     __shared__ float s_red2[kWaves][BM];
     __shared__ __attribute__((aligned(16))) uint8_t s_q[EPI == EPI_SWIGLU_Q ? BM * kGroup : 16];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6, q = lane >> 4, c16 = lane & 15;
-    const int64_t K = a.K, N = a.N, G = K / kGroup;
+    const int64_t K = a.K, N = a.N;
+    const int G = (int)(K / kGroup);
 
     int e, row0, rows;
     if (a.offsets != nullptr) {
@@ -62,16 +61,10 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs a)
             return;
         rows = min(BM, a.dense_rows - row0);
     }
-
-    for (int i = tid; i < BM; i += 256)
-        s_rows[i] = i < rows ? (a.sorted != nullptr ? a.sorted[row0 + i] / a.topk : row0 + i) : -1;
-    __syncthreads();
-    for (int i = tid; i < G * BM; i += 256) {
-        const int g = i / BM, c = i - g * BM;
-        const int r = s_rows[c];
-        lds_side[i] = r >= 0 ? a.act_side[(int64_t)r * G + g] : make_float2(0.0f, 0.0f);
-    }
-    __syncthreads();
+    auto act_row = [&](int i) {  // activation row of block row i (padding rows reuse row 0)
+        const int ii = i < rows ? i : 0;
+        return a.sorted != nullptr ? a.sorted[row0 + ii] / a.topk : row0 + ii;
+    };
 
     // weight rows of this lane (one per fragment)
     int64_t nrow[kNF];
@@ -86,23 +79,41 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs a)
         nvalid[f] = n < N;
         nrow[f] = nvalid[f] ? n : N - 1;
     }
-    const uint8_t* wbase = a.w + (int64_t)e * a.w_estride;
-    const float* sbase = a.ws + (int64_t)e * a.s_estride;
-    const uint8_t* wp[kNF];
-    const float* sp[kNF];
+    // Streaming loads go through buffer resources: a per-lane 32-bit offset
+    // (row and quarter) and the per-group advance in a scalar offset.  The
+    // activation operand is fp8 on both paths (one byte per element); the
+    // lane's two 16-byte chunks of a group are q and 4+q (fp8_group_pos).
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.w + (int64_t)e * a.w_estride, (uint32_t)(N * (K / 2)));
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.ws + (int64_t)e * a.s_estride, (uint32_t)(N * G * 4));
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.act, (uint32_t)(a.act_rows * K));
+    uint32_t vw[kNF], vs[kNF], va[NT];
 #pragma unroll
     for (int f = 0; f < kNF; ++f) {
-        wp[f] = wbase + nrow[f] * (K / 2) + 16 * q;
-        sp[f] = sbase + nrow[f] * G;
+        vw[f] = (uint32_t)(nrow[f] * (K / 2) + 16 * q);
+        vs[f] = (uint32_t)(nrow[f] * G * 4);
     }
-    const uint8_t* ap[NT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-        int r = s_rows[16 * t + c16];
-        if (r < 0)
-            r = s_rows[0];
-        // the lane's 16-byte chunks are q, 4+q, 8+q, 12+q (f16) or q, 4+q (fp8)
-        ap[t] = a.act + (int64_t)r * K * ESZ + 16 * q;
+    for (int t = 0; t < NT; ++t)
+        va[t] = (uint32_t)((int64_t)act_row(16 * t + c16) * K + 16 * q);
+
+    // Side data of the block's rows for every group, staged in LDS: its loads
+    // are issued first, the ring's behind them, so waiting for the side data
+    // does not wait for the ring.
+    constexpr int kSidePer = 8;  // side loads per thread held in registers
+    float2 side_v[kSidePer];
+    const int nside = G * BM;
+    const bool side_in_regs = nside <= 256 * kSidePer;
+    auto side_of = [&](int i) {
+        const int g = i / BM, c = i - g * BM;
+        return c < rows ? a.act_side[(int64_t)act_row(c) * G + g] : make_float2(0.0f, 0.0f);
+    };
+    if (side_in_regs) {
+#pragma unroll
+        for (int j = 0; j < kSidePer; ++j) {
+            const int i = tid + 256 * j;
+            if (i < nside)
+                side_v[j] = side_of(i);
+        }
     }
 
     // The f16 (gate_up) path promotes in fp64: each group's MFMA sum is the
@@ -120,114 +131,157 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs a)
             for (int r = 0; r < 4; ++r)
                 acc[f][t][r] = 0;
 
-    // Ring of D groups in flight.  The loop runs over ceil(G/D)*D groups with
-    // no branches: a refill past the last group reloads group G-1 (in bounds,
-    // never used), and a padding group g >= G gets weight scale 0.
-    // Weight scales: with G % 4 == 0 (and D == 4) one float4 per fragment
-    // covers a whole turn of the ring, loaded one turn ahead.
-    const bool sw4 = (G % 4 == 0) && (D == 4);
-    v4i wb[D][kNF];
-    v4i ab[D][NT][AV];
-    float sb[D][kNF];
-    float4 sw_cur[kNF], sw_next[kNF];
-
-    auto load_group = [&](int s, int64_t g) {
+    // One ring of DW groups in flight for everything a group needs (weights,
+    // weight scales, activations).  Vector-memory loads retire in issue order,
+    // so loads consumed at different distances would make the nearest one
+    // drain the rest; one common distance keeps DW-1 groups in flight.  The
+    // loop runs over ceil(G/DW)*DW groups without branches: a refill past the
+    // last group reloads group G-1 (never used) and a padding group gets
+    // weight scale 0.
+    //
+    // Weight scales: with SW4 (G % 4 == 0, DW % 4 == 0) one float4 per
+    // fragment carries groups g..g+3 and rides in the ring slot of group g,
+    // a quarter of the memory instructions of one float per group.  It lands
+    // in the next turn's bank (sb4n) while this turn still reads sb4c; the
+    // banks swap at the turn boundary.
+    static_assert(!SW4 || DW % 4 == 0, "float4 scales need a ring of whole 4-group blocks");
+    constexpr int NS = SW4 ? DW / 4 : DW;
+    v4i wb[DW][kNF];
+    float sb[NS][kNF];
+    float4 sb4c[SW4 ? NS : 1][kNF], sb4n[SW4 ? NS : 1][kNF];
+    v4i ab[DW][NT][2];
+    auto load_group = [&](int s, int g) {
 #pragma unroll
         for (int f = 0; f < kNF; ++f) {
-            wb[s][f] = ldg16(wp[f] + g * 64);
-            if (!sw4)
-                sb[s][f] = sp[f][g];
+            wb[s][f] = bload16(rw, vw[f], (uint32_t)g * 64u);
+            if (!SW4)
+                sb[s][f] = bload4f(rs, vs[f], (uint32_t)g * 4u);
+            else if (s % 4 == 0)  // g % 4 == 0 here, and g + 3 < G (G % 4 == 0)
+                sb4n[s / 4][f] = __builtin_bit_cast(float4, bload16(rs, vs[f], (uint32_t)g * 4u));
         }
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
-            for (int v = 0; v < AV; ++v)
-                ab[s][t][v] = ldg16(ap[t] + g * kGroup * ESZ + 64 * v);
+            for (int v = 0; v < 2; ++v)
+                ab[s][t][v] = bload16(ra, va[t], (uint32_t)g * kGroup + 64u * v);
     };
-    auto load_sw4 = [&](int64_t g4) {  // groups g4..g4+3, g4 % 4 == 0, g4 + 3 < G
-#pragma unroll
-        for (int f = 0; f < kNF; ++f)
-            sw_next[f] = *(const float4*)(sp[f] + g4);
-    };
-
-    if (sw4) {
-        load_sw4(0);
-#pragma unroll
-        for (int f = 0; f < kNF; ++f)
-            sw_cur[f] = sw_next[f];
-    }
-#pragma unroll
-    for (int s = 0; s < D; ++s)
-        load_group(s, s < G ? s : G - 1);
     __builtin_amdgcn_sched_barrier(0);
-
-    const int64_t Gr = (G + D - 1) / D * D;
-    for (int64_t g0 = 0; g0 < Gr; g0 += D) {
 #pragma unroll
-        for (int s = 0; s < D; ++s) {
-            const int64_t g = g0 + s;
-            const int64_t gl = g < G ? g : G - 1;  // side data row (padding groups: any valid one)
-            const bool live = g < G;
+    for (int s = 0; s < DW; ++s)
+        load_group(s, s < G ? s : (SW4 ? G - 4 + (s % 4) : G - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    auto swap_scales = [&]() {
+        if (SW4) {
+#pragma unroll
+            for (int j = 0; j < NS; ++j)
+#pragma unroll
+                for (int f = 0; f < kNF; ++f)
+                    sb4c[j][f] = sb4n[j][f];
+        }
+    };
+    swap_scales();
+
+    if (side_in_regs) {
+#pragma unroll
+        for (int j = 0; j < kSidePer; ++j) {
+            const int i = tid + 256 * j;
+            if (i < nside)
+                lds_side[i] = side_v[j];
+        }
+    } else {
+        for (int i = tid; i < nside; i += 256)
+            lds_side[i] = side_of(i);
+    }
+    __syncthreads();
+
+    const int Gr = (G + DW - 1) / DW * DW;
+    for (int g0 = 0; g0 < Gr; g0 += DW) {
+#pragma unroll
+        for (int s = 0; s < DW; ++s) {
+            const int g = g0 + s;
+            const int gl = g < G ? g : G - 1;  // side data row (padding groups: any valid one)
+            float swf[kNF];
+#pragma unroll
+            for (int f = 0; f < kNF; ++f) {
+                float v;
+                if (SW4) {
+                    const float4 v4 = sb4c[s / 4][f];
+                    v = (s % 4) == 0 ? v4.x : (s % 4) == 1 ? v4.y : (s % 4) == 2 ? v4.z : v4.w;
+                } else {
+                    v = sb[s][f];
+                }
+                swf[f] = g < G ? v : 0.0f;
+            }
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
                 const float4* sd = (const float4*)&lds_side[gl * BM + 16 * t + 4 * q];
                 const float4 s01 = sd[0], s23 = sd[1];
                 const float c1[4] = {s01.x, s01.z, s23.x, s23.z};
                 const float c0[4] = {s01.y, s01.w, s23.y, s23.w};
-                v8i at;
-                v8h ah[4];
+                uint32_t at[8];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    at[i] = (uint32_t)ab[s][t][0][i];
+                    at[4 + i] = (uint32_t)ab[s][t][1][i];
+                }
+                // all MFMAs of the step first, each fragment into its own
+                // accumulator, so they issue back to back; then the promotion
+                v4f raw[kNF];
                 if (F16) {
+                    // fp8 activation codes -> exact f16 (8-group c of the lane
+                    // is dwords 2c, 2c+1 in the order k0,k4,k1,k5 | k2,k6,k3,k7)
+                    v8h ah[4];
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const v2h h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(at[2 * c], 1.0f, false);
+                        const v2h h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(at[2 * c], 1.0f, true);
+                        const v2h h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(at[2 * c + 1], 1.0f, false);
+                        const v2h h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(at[2 * c + 1], 1.0f, true);
+                        ah[c] = v8h{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
+                    }
+#pragma unroll
+                    for (int f = 0; f < kNF; ++f)
+                        raw[f] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                     for (int c = 0; c < 4; ++c)
-                        ah[c] = __builtin_bit_cast(v8h, ab[s][t][c]);
-                } else {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        at[i] = ab[s][t][0][i];
-                        at[4 + i] = ab[s][t][1][i];
-                    }
-                }
+                        for (int f = 0; f < kNF; ++f)
+                            raw[f] = mfma16x16x32_f16(ah[c], unpack_int4_f16((uint32_t)wb[s][f][c]), raw[f]);
 #pragma unroll
-                for (int f = 0; f < kNF; ++f) {
-                    float swsel;
-                    if (sw4)
-                        swsel = s == 0 ? sw_cur[f].x : s == 1 ? sw_cur[f].y : s == 2 ? sw_cur[f].z : sw_cur[f].w;
-                    else
-                        swsel = sb[s][f];
-                    const float swf = live ? swsel : 0.0f;
-                    v4f raw = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-                    if (F16) {
-#pragma unroll
-                        for (int c = 0; c < 4; ++c)
-                            raw = mfma16x16x32_f16(ah[c], unpack_int4_f16((uint32_t)wb[s][f][c]), raw);
+                    for (int f = 0; f < kNF; ++f) {
                         // c0 == 0 on this path; sw * c1 is exact in fp64
-                        const double swd = (double)swf;
+                        const double swd = (double)swf[f];
 #pragma unroll
                         for (int r = 0; r < 4; ++r)
-                            acc[f][t][r] = fma((double)raw[r], swd * (double)c1[r], (double)acc[f][t][r]);
-                    } else {
-                        raw = mfma16x16x128(at, unpack_int4_u(wb[s][f]), raw);
-#pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            acc[f][t][r] = fmaf(swf, fmaf(raw[r], c1[r], c0[r]), (float)acc[f][t][r]);
+                            acc[f][t][r] = fma((double)raw[f][r], swd * (double)c1[r], (double)acc[f][t][r]);
                     }
+                } else {
+                    v8i av;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        av[i] = (int)at[i];
+#pragma unroll
+                    for (int f = 0; f < kNF; ++f)
+                        raw[f] = mfma16x16x128(av, unpack_int4_u(wb[s][f]), v4f{0.0f, 0.0f, 0.0f, 0.0f});
+#pragma unroll
+                    for (int f = 0; f < kNF; ++f)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            acc[f][t][r] = fmaf(swf[f], fmaf(raw[f][r], c1[r], c0[r]), (float)acc[f][t][r]);
                 }
             }
-            // keep the refill here, D groups ahead of its use: without the
+            // keep the refill here, DW groups ahead of its use: without the
             // barrier the scheduler sinks each load next to its consumer and
             // only one load stays in flight
             __builtin_amdgcn_sched_barrier(0);
-            const int64_t gn = g + D < G ? g + D : G - 1;
-            load_group(s, gn);
-            if (sw4 && s == 0)
-                load_sw4(g0 + D + 3 < G ? g0 + D : G - 4);
+            {
+                // past the end: reload a valid group (aligned to 4 for SW4)
+                const int gn = g + DW < G ? g + DW : (SW4 ? G - 4 + (s % 4) : G - 1);
+                load_group(s, gn);
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
-        if (sw4) {
-#pragma unroll
-            for (int f = 0; f < kNF; ++f)
-                sw_cur[f] = sw_next[f];
-        }
+        swap_scales();
     }
 
     // ---- epilogues ----  output element (row 16t+4q+r of the block, weight row nrow[f])
@@ -331,7 +385,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs a)
     }
 }
 
-template <int NT, int EPI, int D, bool F16>
+template <int NT, int EPI, int DW, bool F16, bool SW4>
 static hipError_t launch_one(const GemmArgs& a, hipStream_t s)
 {
     const int64_t G = a.K / kGroup;
@@ -345,26 +399,32 @@ static hipError_t launch_one(const GemmArgs& a, hipStream_t s)
     grid.z = 1;
     if (grid.x == 0 || grid.y == 0)
         return hipSuccess;
-    hipLaunchKernelGGL((gemm_skinny_kernel<NT, EPI, D, F16>), grid, dim3(256), lds, s, a);
+    hipLaunchKernelGGL((gemm_skinny_kernel<NT, EPI, DW, F16, SW4>), grid, dim3(256), lds, s, a);
     return hipGetLastError();
-}
-
-size_t skinny_lds_bytes(int64_t K, int block_m)
-{
-    return (size_t)(K / kGroup) * (size_t)block_m * sizeof(float2);
 }
 
 hipError_t launch_gemm_skinny(const GemmArgs& a, int epilogue, int block_m, hipStream_t s)
 {
-    // gate_up (SwiGLU epilogue) runs on the exact f16 path, the others on fp8
-#define W4A8_SKINNY(NT, D)                                                         \
-    switch (epilogue) {                                                            \
-    case EPI_F32: return launch_one<NT, EPI_F32, D, false>(a, s);                  \
-    case EPI_BF16: return launch_one<NT, EPI_BF16, D, false>(a, s);                \
-    default: return launch_one<NT, EPI_SWIGLU_Q, D, true>(a, s);                   \
+    // gate_up (SwiGLU epilogue) runs on the exact f16 path, the others on fp8;
+    // ring depth per m-block height
+#ifndef W4A8_DW16
+#define W4A8_DW16 4
+#endif
+    const bool g4 = (a.K / kGroup) % 4 == 0;
+#define W4A8_SKINNY(NT, DW)                                                              \
+    switch (epilogue) {                                                                  \
+    case EPI_F32:                                                                        \
+        return g4 ? launch_one<NT, EPI_F32, DW, false, DW % 4 == 0>(a, s)                 \
+                  : launch_one<NT, EPI_F32, DW, false, false>(a, s);                      \
+    case EPI_BF16:                                                                       \
+        return g4 ? launch_one<NT, EPI_BF16, DW, false, DW % 4 == 0>(a, s)                \
+                  : launch_one<NT, EPI_BF16, DW, false, false>(a, s);                     \
+    default:                                                                             \
+        return g4 ? launch_one<NT, EPI_SWIGLU_Q, DW, true, DW % 4 == 0>(a, s)             \
+                  : launch_one<NT, EPI_SWIGLU_Q, DW, true, false>(a, s);                  \
     }
     if (block_m <= 16) {
-        W4A8_SKINNY(1, 4)
+        W4A8_SKINNY(1, W4A8_DW16)
     } else if (block_m <= 32) {
         W4A8_SKINNY(2, 3)
     } else {

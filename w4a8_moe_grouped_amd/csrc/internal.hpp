@@ -11,8 +11,8 @@ namespace w4a8 {
 // ---- activation quantisation (quant.hip) ----
 // mode 0: canonical codes + fp32 scales (the public export)
 // mode 1: K-interleaved codes + {c1, c0} side data (fp8 GEMM operand)
-// mode 2: exact fp16 values (k0,k4,k1,k5,... per 8) + {scale, 0} (f16 GEMM operand);
-//         q is then a [M, K] fp16 buffer
+// mode 2: codes ordered k0,k4,k1,k5,k2,k6,k3,k7 per 8-group + {scale, 0}
+//         (f16 GEMM operand, converted to f16 in registers)
 hipError_t launch_quant_bf16(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
                              float* scales, float2* side, int mode, hipStream_t s);
 // canonical codes + scales (from w4a8_quantize_act) -> interleaved codes + side data
@@ -36,10 +36,11 @@ hipError_t launch_align(const int32_t* ids, int64_t T, int64_t topk, int64_t exp
 
 // ---- grouped GEMMs (gemm_skinny.hip) ----
 struct GemmArgs {
-    // activation operand, row stride K elements, + side data [rows, K/128]:
-    // fp8 path: K-interleaved codes; f16 path (f16 != 0): fp16 values
+    // activation operand (fp8 codes, row stride K) + side data [rows, K/128];
+    // the K order inside each 8-group depends on the path (see common.hpp)
     const uint8_t* act;
     int f16;
+    int64_t act_rows;   // rows of the activation buffer (bounds of its buffer resource)
     const float2* act_side;
     // row map: GEMM row p of an m-block -> activation row.  If sorted != null,
     // act_row = sorted[p] / topk (gather through the permutation), else p.

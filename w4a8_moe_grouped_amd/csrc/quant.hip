@@ -17,8 +17,8 @@ namespace w4a8 {
 
 // MODE 0: canonical codes + scales (the public export)
 // MODE 1: K-interleaved codes + {512*s, -8*s*sum(dec)} (fp8 GEMM operand)
-// MODE 2: the exact e4m3 values as fp16, order k0,k4,k1,k5,k2,k6,k3,k7 per 8,
-//         + {s, 0} (f16 GEMM operand); q then points at [M, K] fp16
+// MODE 2: codes in the order k0,k4,k1,k5,k2,k6,k3,k7 per 8-group (fp8_group_pos
+//         placement) + {s, 0} (the f16 GEMM operand, converted in registers)
 template <int MODE>
 __global__ __launch_bounds__(256) void quant_bf16_kernel(const uint16_t* __restrict__ x, int64_t M,
                                                          int64_t K, int64_t ldx,
@@ -56,22 +56,12 @@ __global__ __launch_bounds__(256) void quant_bf16_kernel(const uint16_t* __restr
     uint32_t d0 = c[0] | (c[1] << 16), d1 = c[2] | (c[3] << 16);
 
     if (MODE == 2) {
-        float f[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float2 d = dec_e4m3x2(c[i]);
-            f[2 * i] = d.x;
-            f[2 * i + 1] = d.y;
-        }
-        // e4m3 values are exact in fp16 (subnormals down to 2^-9 included)
-        const int order[8] = {0, 4, 1, 5, 2, 6, 3, 7};
-        v4i o;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const v2h h = {(_Float16)f[order[2 * i]], (_Float16)f[order[2 * i + 1]]};
-            o[i] = __builtin_bit_cast(int, h);
-        }
-        *(v4i*)((uint16_t*)q + m * K + g * kGroup + f16_group_chunk(sub) * 8) = o;
+        // fp8 codes for the f16 gate_up path: inside the 8-group the order is
+        // k0,k4,k1,k5 | k2,k6,k3,k7 (pairs converted to f16 with one
+        // instruction line up with the int4 -> f16 unpack)
+        const uint32_t p0 = __builtin_amdgcn_perm(d1, d0, 0x05010400u);
+        const uint32_t p1 = __builtin_amdgcn_perm(d1, d0, 0x07030602u);
+        *(uint2*)(q + m * K + g * kGroup + fp8_group_pos(sub)) = make_uint2(p0, p1);
         if (sub == 0)
             side[m * G + g] = make_float2(scale, 0.0f);
         return;
