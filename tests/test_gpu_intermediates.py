@@ -5,7 +5,10 @@ the down GEMM output are read back from the workspace (its layout comes from
 w4a8_fused_moe_workspace_layout) and compared, pair by pair in the same
 permuted order, with the oracle's.  The codes are not required to match
 bit for bit (fp32 vs fp64 accumulation can move h across a rounding
-boundary); their mismatch rate is reported and bounded.
+boundary); their mismatch rate is reported and bounded.  Likewise the
+scale amax/448 of a block follows the GPU's value of its largest |h|: it is
+held to a relative bound of a few fp32 ulps, not to bit equality (the
+block-tiled path promotes in fp32, so most scales sit one ulp away).
 """
 import numpy as np
 import pytest
@@ -40,12 +43,15 @@ def deinterleave8(mem):
     return out.reshape(P, K)
 
 
-@pytest.mark.parametrize("name", ["tiny", "decode", "skew_id"])
+@pytest.mark.parametrize("name", ["tiny", "decode", "skew_id", "tile_small"])
 def test_requant_codes_and_down_output(name):
     assert torch.cuda.is_available()
     dev = torch.device("cuda:0")
-    cfg = synth.CONFIGS[name]
-    d = synth.gen_moe(cfg)
+    if name == "tile_small":  # block-tiled path (128-row m-blocks)
+        cfg, d = synth.random_moe(512, 256, 256, 8, 2, 0, 4, seed=31)
+    else:
+        cfg = synth.CONFIGS[name]
+        d = synth.gen_moe(cfg)
     T, H, I, k, E = cfg.T, cfg.H, cfg.I, cfg.topk, cfg.E_local
     if name == "skew_id":  # keep the oracle short: the first 40 tokens
         T = 40
@@ -72,11 +78,14 @@ def test_requant_codes_and_down_output(name):
     code_mis = np.mean(qh != inter["qh"])
     scale = side[:, :, 0] / np.float32(512)
     scale_mis = np.mean(scale != inter["sh"])
+    scale_rel = np.max(np.abs(scale.astype(np.float64) - inter["sh"]) / inter["sh"])
     y2_fro = np.linalg.norm(y2 - inter["y2"]) / np.linalg.norm(inter["y2"])
     y2_max = np.max(np.abs(y2 - inter["y2"])) / np.max(np.abs(inter["y2"]))
     # with the oracle's own codes, how far is the GPU's down GEMM alone?
-    print("%s: P=%d code mismatch=%.2e (%d of %d) scale mismatch=%.2e y2 rel_fro=%.3e max=%.3e"
-          % (name, P, code_mis, int(np.sum(qh != inter["qh"])), qh.size, scale_mis, y2_fro, y2_max))
+    print("%s: P=%d code mismatch=%.2e (%d of %d) scale mismatch=%.2e (max rel %.1e) "
+          "y2 rel_fro=%.3e max=%.3e"
+          % (name, P, code_mis, int(np.sum(qh != inter["qh"])), qh.size, scale_mis, scale_rel,
+             y2_fro, y2_max))
     assert code_mis <= 1e-3
-    assert scale_mis <= 1e-2
+    assert scale_rel <= 2e-6
     assert y2_fro <= 1e-3

@@ -130,7 +130,12 @@ __device__ void finish_scan(int* counts_lds, int* tmp_lds, int* scratch, int64_t
     if (t == 0) {
         o.offsets[E] = P;
         *o.num_blocks = nb;
+        if (o.block_start != nullptr)
+            o.block_start[E] = nb;
     }
+    if (o.block_start != nullptr)
+        for (int e = t; e < E; e += kAlignThreads)
+            o.block_start[e] = tmp_lds[e];
     if (o.block_expert != nullptr) {
         for (int e = t; e < E; e += kAlignThreads) {
             const int first = tmp_lds[e];

@@ -55,9 +55,20 @@ int64_t ceil_div(int64_t a, int64_t b)
     return (a + b - 1) / b;
 }
 
+// Many rows per expert: the block-tiled GEMM (128-row m-blocks, weights
+// reused across the rows of an m-block from LDS) beats streaming the weights
+// once per small m-block.  Decided from the pairs per expert if every pair
+// were local, like pick_block_m.
+constexpr int64_t kTilePairsPerExpert = 256;
+bool use_tile(int64_t pairs, int64_t experts)
+{
+    return pairs >= kTilePairsPerExpert * experts;
+}
+
 // The fused forward's workspace.  P is unknown on the host, so every
 // per-pair buffer is sized for F = T*topk pairs.
 struct MoePlan {
+    bool tile;
     int block_m;
     int64_t F, nb_max;
     w4a8::AlignOut al;
@@ -67,13 +78,15 @@ struct MoePlan {
     uint8_t* qh;
     float2* qh_side;
     float* y2;
+    int32_t* block_start;
 };
 
 size_t plan_moe(void* ws, int64_t T, int64_t H, int64_t topk, int64_t E, int64_t I, MoePlan& p)
 {
     Carve c(ws);
     p.F = T * topk;
-    p.block_m = pick_block_m(p.F, E);
+    p.tile = use_tile(p.F, E);
+    p.block_m = p.tile ? w4a8::kTileRows : pick_block_m(p.F, E);
     p.nb_max = ceil_div(p.F, p.block_m) + E;
     p.al.counts = c.take<int32_t>(E);
     p.al.offsets = c.take<int32_t>(E + 1);
@@ -88,6 +101,8 @@ size_t plan_moe(void* ws, int64_t T, int64_t H, int64_t topk, int64_t E, int64_t
     p.qh = c.take<uint8_t>(p.F * I);
     p.qh_side = c.take<float2>(p.F * (I / W4A8_GROUP));
     p.y2 = c.take<float>(p.F * H);
+    p.al.block_start = c.take<int32_t>(E + 1);
+    p.block_start = p.al.block_start;
     return c.used;
 }
 
@@ -259,7 +274,7 @@ int w4a8_fused_moe(const void* hidden_bf16, int64_t T, int64_t H, const int32_t*
         return W4A8_ERR_UNSUPPORTED;
     MoePlan p;
     const size_t need = plan_moe(nullptr, T, H, topk, E, I, p);
-    if (!skinny_k_ok(H, p.block_m) || !skinny_k_ok(I, p.block_m))
+    if (!p.tile && (!skinny_k_ok(H, p.block_m) || !skinny_k_ok(I, p.block_m)))
         return W4A8_ERR_UNSUPPORTED;
     const int ws_rc = check_workspace(workspace, workspace_bytes, need);
     if (ws_rc >= 0)
@@ -284,8 +299,10 @@ int w4a8_fused_moe(const void* hidden_bf16, int64_t T, int64_t H, const int32_t*
     if (e != hipSuccess)
         return W4A8_ERR_HIP;
     mark(ev, 1, stream);
+    // activation operand of gate_up: f16-ordered codes for the skinny kernel,
+    // the fp8 layout for the tile kernel
     e = w4a8::launch_quant_bf16((const uint16_t*)hidden_bf16, T, H, H, p.qa, nullptr, p.qa_side,
-                                2, stream);
+                                p.tile ? 1 : 2, stream);
     if (e != hipSuccess)
         return W4A8_ERR_HIP;
     mark(ev, 2, stream);
@@ -295,6 +312,8 @@ int w4a8_fused_moe(const void* hidden_bf16, int64_t T, int64_t H, const int32_t*
     g.block_row = p.al.block_row;
     g.num_blocks = p.al.num_blocks;
     g.offsets = p.al.offsets;
+    g.block_start = p.block_start;
+    g.num_experts = (int32_t)E;
     g.max_blocks = p.nb_max;
     // gate_up: rows gathered through the permutation, exact f16 MFMA path,
     // SwiGLU + requant epilogue
@@ -313,7 +332,8 @@ int w4a8_fused_moe(const void* hidden_bf16, int64_t T, int64_t H, const int32_t*
     g.I = I;
     g.out_q = p.qh;
     g.out_side = p.qh_side;
-    e = w4a8::launch_gemm_skinny(g, w4a8::EPI_SWIGLU_Q, p.block_m, stream);
+    e = p.tile ? w4a8::launch_gemm_tile(g, w4a8::TILE_GATEUP, stream)
+               : w4a8::launch_gemm_skinny(g, w4a8::EPI_SWIGLU_Q, p.block_m, stream);
     if (e != hipSuccess)
         return W4A8_ERR_HIP;
     mark(ev, 3, stream);
@@ -330,7 +350,8 @@ int w4a8_fused_moe(const void* hidden_bf16, int64_t T, int64_t H, const int32_t*
     g.K = I;
     g.N = H;
     g.out_f32 = p.y2;
-    e = w4a8::launch_gemm_skinny(g, w4a8::EPI_F32, p.block_m, stream);
+    e = p.tile ? w4a8::launch_gemm_tile(g, w4a8::TILE_DOWN, stream)
+               : w4a8::launch_gemm_skinny(g, w4a8::EPI_F32, p.block_m, stream);
     if (e != hipSuccess)
         return W4A8_ERR_HIP;
     mark(ev, 4, stream);

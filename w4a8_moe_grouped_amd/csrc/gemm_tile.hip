@@ -1,0 +1,423 @@
+// gemm_tile.hip -- grouped W4A8 GEMM for many rows per expert (prefill).
+//
+// y[p, n] = sum_g w_scale[n, g] * a_scale[p, g] * sum_{k in g} a[p, k] * w[n, k]
+// over the rows p of one m-block of one expert (SGLang PR #7762: grouped
+// GEMM over expert segments with 128-wide weight groups along K; DeepGEMM
+// PR #53 "Changes": large batches are MMA-bound, so a block tile reuses each
+// weight byte across many token rows).
+//
+// Work decomposition.  A workgroup of 8 waves owns a tile of 128 rows (one
+// m-block) x 256 weight rows and walks K one 128-group at a time.  Waves sit
+// on a 2 x 4 grid, each with a 64 x 64 register tile (4 x 4 fragments of
+// 16 x 16).  For every group the workgroup copies, straight from global memory
+// into LDS (buffer_load ... lds, no register staging), the 128 activation rows
+// (fp8 codes, gathered through the permutation), their {c1, c0} side data, the
+// 256 packed int4 weight rows and their scales: 34 KB per stage, 4 stages in
+// flight.  Stage slots are XOR-swizzled so that the 16-byte fragment reads hit
+// distinct LDS banks.
+//
+// MFMAs: the down GEMM runs on v_mfma_f32_16x16x128_f8f6f4 with the weights
+// turned into u * 2^-9 fp8 codes (u = nibble ^ 8, see common.hpp); gate_up runs
+// the same operands converted exactly to f16 through
+// v_mfma_f32_16x16x32_f16, whose fp32 sum of each 32-wide step is exact to
+// rounding (the fp8 form truncates, and the requantised SwiGLU output of
+// gate_up is sensitive to that).  Either way one group's raw sum is promoted
+// as y += w_scale * fma(raw, c1, c0).
+//
+// Tile order: tiles are numbered expert by expert, weight block by weight
+// block, m-block fastest (the m-blocks of one expert share its weight panel
+// while they run), and the numbering is cut into 8 contiguous ranges, one per
+// XCD (workgroups are dealt to the XCDs round robin), so that the panel and the
+// activation rows of an expert stay in one XCD's L2.
+//
+// Epilogues:
+//   TILE_DOWN    out_f32[p, n]
+//   TILE_GATEUP  the tile holds gate rows i and up rows I+i of one 128-block of
+//                i: h = silu(gate) * up (fp64, rounded once to fp32), then the
+//                fp8 requant of the block (DeepGEMM PR #53 "Changes": SwiGLU ->
+//                per-token FP8 requant).
+#include "common.hpp"
+#include "internal.hpp"
+
+#include <type_traits>
+
+namespace w4a8 {
+
+namespace {
+
+constexpr int kTBM = 128;     // rows per tile
+constexpr int kTBN = 256;     // weight rows per tile
+constexpr int kTThreads = 512;
+constexpr int kStages = 4;
+constexpr int kLoadsPerStage = 5;  // per wave: 2 A + 2 B + 1 side-or-scale
+
+constexpr int kAOff = 0;
+constexpr int kBOff = kAOff + kTBM * kGroup;         // 16 KB of activation codes
+constexpr int kSideOff = kBOff + kTBN * kGroup / 2;  // 16 KB of packed weights
+constexpr int kSwOff = kSideOff + kTBM * 8;          // {c1, c0} per row
+constexpr int kStageBytes = kSwOff + kTBN * 4;       // weight scale per weight row
+constexpr int kSmemBytes = kStages * kStageBytes;
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Buffer descriptor in SGPRs (raw, stride 0, num_records = bytes).
+__device__ __forceinline__ v4i sgpr_rsrc(const void* base, uint32_t bytes)
+{
+    const uint64_t b = (uint64_t)base;
+    v4i r;
+    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+    r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+    r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+    r[3] = 0x00020000;
+    return r;
+}
+
+// 64 lanes x 16 (or 4) bytes from the buffer into LDS at lds + lane * 16 (or
+// 4).  Issued from inline assembly so that the compiler's wait-count pass,
+// which cannot tell the stages apart, does not drain every stage in flight
+// before each LDS read; the kernel waits explicitly (wait_vmcnt + barrier).
+__device__ __forceinline__ void lds_load16(const v4i& r, uint32_t lds, uint32_t voff, uint32_t soff)
+{
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :
+                 : "s"(lds), "v"(voff), "s"(r), "s"(soff)
+                 : "memory", "m0");
+}
+__device__ __forceinline__ void lds_load4(const v4i& r, uint32_t lds, uint32_t voff, uint32_t soff)
+{
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+                 :
+                 : "s"(lds), "v"(voff), "s"(r), "s"(soff)
+                 : "memory", "m0");
+}
+
+// s_waitcnt vmcnt(N), leaving the other counters alone
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// A workgroup barrier that is also a compiler memory barrier, without the
+// release/acquire fence of __syncthreads (which would wait for every load in
+// flight, including the stages still being filled).
+__device__ __forceinline__ void barrier()
+{
+    asm volatile("s_barrier" ::: "memory");
+}
+
+// 16-byte slot of (activation row, chunk 0..7) and of (weight row, chunk 0..3)
+__device__ __forceinline__ int a_slot(int row, int chunk)
+{
+    return row * 8 + (chunk ^ (row & 7));
+}
+__device__ __forceinline__ int b_slot(int wrow, int chunk)
+{
+    return wrow * 4 + (chunk ^ ((wrow >> 1) & 3));
+}
+
+// two fp8 dwords (4 + 4 codes) -> 8 exact halves, in dword order
+__device__ __forceinline__ v8h fp8x8_to_f16(uint32_t d0, uint32_t d1)
+{
+    const v2h h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d0, 1.0f, false);
+    const v2h h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d0, 1.0f, true);
+    const v2h h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d1, 1.0f, false);
+    const v2h h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d1, 1.0f, true);
+    return v8h{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
+}
+
+}  // namespace
+
+template <int MODE, bool F64>
+__global__ __launch_bounds__(kTThreads) void gemm_tile_kernel(GemmArgs a)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
+    __shared__ int s_expert;
+
+    const int tid = threadIdx.x;
+    // the wave index in an SGPR: LDS destinations of the direct loads go
+    // through M0 and must be provably wave-uniform
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, q = lane >> 4, c16 = lane & 15;
+    const int wm = wave & 1, wn = wave >> 1;
+    const int64_t K = a.K, N = a.N;
+    const int G = (int)(K / kGroup);
+    const int E = a.num_experts;
+    const int nbn = MODE == TILE_GATEUP ? (int)(a.I / kGroup) : (int)((N + kTBN - 1) / kTBN);
+
+    // ---- the tile of this workgroup ----
+    const int total = *a.num_blocks * nbn;
+    const int per_xcd = (total + 7) >> 3;
+    const int xslot = (int)(blockIdx.x >> 3);
+    if (xslot >= per_xcd)
+        return;
+    const int L = (int)(blockIdx.x & 7) * per_xcd + xslot;
+    if (L >= total)
+        return;
+    if (tid == 0)
+        s_expert = -1;
+    __syncthreads();
+    for (int e = tid; e < E; e += kTThreads) {
+        const int b0 = a.block_start[e], b1 = a.block_start[e + 1];
+        if (L >= b0 * nbn && L < b1 * nbn)  // exactly one expert owns tile L
+            s_expert = e;
+    }
+    __syncthreads();
+    const int e = __builtin_amdgcn_readfirstlane(s_expert);
+    if (e < 0)
+        return;
+    const int bs = a.block_start[e];
+    const int nbe = a.block_start[e + 1] - bs;
+    if (nbe <= 0)
+        return;
+    const int local = L - bs * nbn;
+    const int nb = local / nbe;
+    const int blk = bs + (local - nb * nbe);
+    const int row0 = a.block_row[blk];
+    const int rows = min(kTBM, a.offsets[e + 1] - row0);
+
+    auto act_row = [&](int i) {  // activation row of tile row i (padding rows reuse row 0)
+        const int ii = i < rows ? i : 0;
+        return a.sorted != nullptr ? a.sorted[row0 + ii] / a.topk : row0 + ii;
+    };
+    auto weight_row = [&](int wrow) -> int64_t {  // weight row of tile weight row wrow
+        int64_t n;
+        if (MODE == TILE_GATEUP)
+            n = (wrow >= 128 ? a.I : 0) + (int64_t)nb * kGroup + (wrow & 127);
+        else
+            n = (int64_t)nb * kTBN + wrow;
+        return n < N ? n : N - 1;
+    };
+
+    // ---- this thread's share of every stage's loads ----
+    const v4i ra = sgpr_rsrc(a.act, (uint32_t)(a.act_rows * K));
+    const v4i rsd = sgpr_rsrc(a.act_side, (uint32_t)(a.act_rows * G * 8));
+    const v4i rw = sgpr_rsrc(a.w + (int64_t)e * a.w_estride, (uint32_t)(N * (K / 2)));
+    const v4i rws = sgpr_rsrc(a.ws + (int64_t)e * a.s_estride, (uint32_t)(N * G * 4));
+    uint32_t va[2], vb[2], vx;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int s = (2 * wave + j) * 64 + lane;
+        const int r = s >> 3, ca = (s & 7) ^ (r & 7);
+        va[j] = (uint32_t)((int64_t)act_row(r) * K + 16 * ca);
+        const int wr = s >> 2, cb = (s & 3) ^ ((wr >> 1) & 3);
+        vb[j] = (uint32_t)(weight_row(wr) * (K / 2) + 16 * cb);
+    }
+    if (wave < 4) {  // side data: dword d = 2 * row + component
+        const int d = wave * 64 + lane;
+        vx = (uint32_t)(((int64_t)act_row(d >> 1) * G) * 8 + 4 * (d & 1));
+    } else {  // weight scales: one per weight row
+        vx = (uint32_t)(weight_row((wave - 4) * 64 + lane) * G * 4);
+    }
+    const uint32_t smem_lds = (uint32_t)(uintptr_t)(lds_ptr_t)smem;
+    auto issue = [&](int g, int st) {
+        const uint32_t base = smem_lds + (uint32_t)(st * kStageBytes);
+        lds_load16(ra, base + kAOff + (2 * wave) * 1024, va[0], (uint32_t)g * kGroup);
+        lds_load16(ra, base + kAOff + (2 * wave + 1) * 1024, va[1], (uint32_t)g * kGroup);
+        lds_load16(rw, base + kBOff + (2 * wave) * 1024, vb[0], (uint32_t)g * 64u);
+        lds_load16(rw, base + kBOff + (2 * wave + 1) * 1024, vb[1], (uint32_t)g * 64u);
+        if (wave < 4)
+            lds_load4(rsd, base + kSideOff + wave * 256, vx, (uint32_t)g * 8u);
+        else
+            lds_load4(rws, base + kSwOff + (wave - 4) * 256, vx, (uint32_t)g * 4u);
+    };
+
+    // weight rows of this lane's fragments (tile-local)
+    int wrow_f[4];
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+        wrow_f[f] = MODE == TILE_GATEUP ? (f >= 2 ? 128 : 0) + 32 * wn + 16 * (f & 1) + c16
+                                        : 64 * wn + 16 * f + c16;
+
+    using Acc = typename std::conditional<F64, double, float>::type;
+    Acc acc[4][4][4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int f = 0; f < 4; ++f)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                acc[m][f][r] = 0;
+
+#pragma unroll
+    for (int s = 0; s < kStages - 1; ++s)
+        issue(s < G ? s : G - 1, s);
+
+    for (int g = 0; g < G; ++g) {
+        wait_vmcnt<kLoadsPerStage * (kStages - 2)>();  // this wave's loads of group g landed
+        barrier();  // everyone's did, and stage (g - 1) % kStages is no longer read
+        {
+            const int gn = g + kStages - 1;
+            issue(gn < G ? gn : G - 1, gn % kStages);
+        }
+        const uint8_t* base = smem + (g % kStages) * kStageBytes;
+
+        float sw[4];
+        v4i wb[4];
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+            wb[f] = *(const v4i*)(base + kBOff + 16 * b_slot(wrow_f[f], q));
+            sw[f] = *(const float*)(base + kSwOff + 4 * wrow_f[f]);
+        }
+        v8i b8[4];
+#pragma unroll
+        for (int f = 0; f < 4; ++f)
+            b8[f] = unpack_int4_u(wb[f]);
+        v8h bh[MODE == TILE_GATEUP ? 4 : 1][4];
+        if (MODE == TILE_GATEUP) {
+#pragma unroll
+            for (int f = 0; f < 4; ++f)
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    bh[f][c] = fp8x8_to_f16((uint32_t)b8[f][2 * c], (uint32_t)b8[f][2 * c + 1]);
+        }
+
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int trow = 64 * wm + 16 * m;
+            if (trow >= rows)  // wave-uniform: no valid row in this fragment
+                continue;
+            const v4i a0 = *(const v4i*)(base + kAOff + 16 * a_slot(trow + c16, q));
+            const v4i a1 = *(const v4i*)(base + kAOff + 16 * a_slot(trow + c16, 4 + q));
+            const float4* sd = (const float4*)(base + kSideOff + 8 * (trow + 4 * q));
+            const float4 s01 = sd[0], s23 = sd[1];
+            const float c1[4] = {s01.x, s01.z, s23.x, s23.z};
+            const float c0[4] = {s01.y, s01.w, s23.y, s23.w};
+            v4f raw[4];
+            if (MODE == TILE_GATEUP) {
+                v8h ah[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const v4i& src = c < 2 ? a0 : a1;
+                    ah[c] = fp8x8_to_f16((uint32_t)src[2 * (c & 1)], (uint32_t)src[2 * (c & 1) + 1]);
+                }
+#pragma unroll
+                for (int f = 0; f < 4; ++f)
+                    raw[f] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+#pragma unroll
+                    for (int f = 0; f < 4; ++f)
+                        raw[f] = mfma16x16x32_f16(ah[c], bh[f][c], raw[f]);
+            } else {
+                const v8i av = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+#pragma unroll
+                for (int f = 0; f < 4; ++f)
+                    raw[f] = mfma16x16x128(av, b8[f], v4f{0.0f, 0.0f, 0.0f, 0.0f});
+            }
+#pragma unroll
+            for (int f = 0; f < 4; ++f)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    if (F64)
+                        acc[m][f][r] = fma((double)sw[f], fma((double)raw[f][r], (double)c1[r], (double)c0[r]),
+                                           (double)acc[m][f][r]);
+                    else
+                        acc[m][f][r] = fmaf(sw[f], fmaf(raw[f][r], c1[r], c0[r]), (float)acc[m][f][r]);
+                }
+        }
+    }
+
+    // ---- epilogues: element (tile row 64wm + 16m + 4q + r, fragment f) ----
+    if (MODE == TILE_DOWN) {
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+            const int64_t n = (int64_t)nb * kTBN + wrow_f[f];
+            if (n >= N)
+                continue;
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = 64 * wm + 16 * m + 4 * q + r;
+                    if (row < rows)
+                        a.out_f32[(int64_t)(row0 + row) * N + n] = (float)acc[m][f][r];
+                }
+        }
+        return;
+    }
+
+    // TILE_GATEUP: fragments f and f + 2 hold gate and up of i = 32wn + 16f + c16
+    wait_vmcnt<0>();  // the trailing (unused) stage loads still write LDS
+    barrier();
+    float* s_red = (float*)smem;                        // [4][128] amax per wave column
+    float* s_sum = s_red + 4 * kTBM;                    // [4][128] sum of decoded codes
+    uint8_t* s_q = (uint8_t*)(s_sum + 4 * kTBM);        // [128][128] codes
+    float h[4][2][4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const double gt = (double)acc[m][j][r], up = (double)acc[m][j + 2][r];
+                h[m][j][r] = (float)(gt / (1.0 + exp(-gt)) * up);
+            }
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float mx = fmaxf(fabsf(h[m][0][r]), fabsf(h[m][1][r]));
+            mx = group_max<16>(mx);
+            if (c16 == 0)
+                s_red[wn * kTBM + 64 * wm + 16 * m + 4 * q + r] = mx;
+        }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = 64 * wm + 16 * m + 4 * q + r;
+            const float mx = fmaxf(fmaxf(s_red[row], s_red[kTBM + row]),
+                                   fmaxf(s_red[2 * kTBM + row], s_red[3 * kTBM + row]));
+            const float inv = recip448(clamp_amax(mx));
+            const uint32_t cc = cvt_e4m3x2(h[m][0][r] * inv, h[m][1][r] * inv);
+            const float2 dv = dec_e4m3x2(cc);
+            const float sum = group_sum<16>(dv.x + dv.y);
+            if (c16 == 0)
+                s_sum[wn * kTBM + row] = sum;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int il = 32 * wn + 16 * j + c16;
+                const int b = il & 7;
+                const int pos = fp8_group_pos(il >> 3) + ((b & 1) ? 4 + (b >> 1) : (b >> 1));
+                s_q[row * kGroup + pos] = (uint8_t)((cc >> (8 * j)) & 0xFFu);
+            }
+        }
+    __syncthreads();
+    const int64_t GI = a.I / kGroup;
+    for (int i = tid; i < kTBM * 8; i += kTThreads) {
+        const int row = i >> 3, chunk = i & 7;
+        if (row < rows)
+            *(v4i*)(a.out_q + (int64_t)(row0 + row) * a.I + (int64_t)nb * kGroup + chunk * 16) =
+                *(const v4i*)(s_q + row * kGroup + chunk * 16);
+    }
+    if (tid < kTBM && tid < rows) {
+        const int row = tid;
+        const float sum = s_sum[row] + s_sum[kTBM + row] + s_sum[2 * kTBM + row] + s_sum[3 * kTBM + row];
+        const float mx = fmaxf(fmaxf(s_red[row], s_red[kTBM + row]),
+                               fmaxf(s_red[2 * kTBM + row], s_red[3 * kTBM + row]));
+        const float sc = scale_of(clamp_amax(mx));
+        a.out_side[(int64_t)(row0 + row) * GI + nb] = make_float2(512.0f * sc, -8.0f * (sc * sum));
+    }
+}
+
+hipError_t launch_gemm_tile(const GemmArgs& a, int mode, hipStream_t s)
+{
+    const int64_t nbn = mode == TILE_GATEUP ? a.I / kGroup : (a.N + kTBN - 1) / kTBN;
+    const int64_t tiles = nbn * a.max_blocks;
+    if (tiles == 0)
+        return hipSuccess;
+    const dim3 grid((unsigned)((tiles + 7) / 8 * 8));
+#ifndef W4A8_TILE_F64
+#define W4A8_TILE_F64 0
+#endif
+    if (mode == TILE_GATEUP)
+        hipLaunchKernelGGL((gemm_tile_kernel<TILE_GATEUP, W4A8_TILE_F64 != 0>), grid, dim3(kTThreads), 0, s, a);
+    else
+        hipLaunchKernelGGL((gemm_tile_kernel<TILE_DOWN, false>), grid, dim3(kTThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace w4a8

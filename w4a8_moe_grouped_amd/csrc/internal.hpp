@@ -28,6 +28,7 @@ struct AlignOut {
     int32_t* block_expert;  // [nb_max] or null
     int32_t* block_row;     // [nb_max] or null
     int32_t* num_blocks;    // [1]
+    int32_t* block_start;   // [E+1] index of each expert's first m-block, or null
 };
 int64_t align_chunk_count(int64_t F);
 size_t align_workspace_bytes(int64_t F, int64_t E);
@@ -51,6 +52,8 @@ struct GemmArgs {
     const int32_t* block_row;
     const int32_t* num_blocks;
     const int32_t* offsets;  // [E+1] segment ends (rows of expert e: [offsets[e], offsets[e+1]))
+    const int32_t* block_start;  // [E+1] first m-block of each expert (tile GEMM)
+    int32_t num_experts;
     int32_t dense_rows;      // used when offsets == null: rows [0, dense_rows)
     // weights of expert e: w + e*w_estride, scales ws + e*s_estride; row n at n*K/2, n*K/128
     const uint8_t* w;
@@ -68,6 +71,13 @@ struct GemmArgs {
 };
 enum Epilogue { EPI_F32 = 0, EPI_BF16 = 1, EPI_SWIGLU_Q = 2 };
 hipError_t launch_gemm_skinny(const GemmArgs& a, int epilogue, int block_m, hipStream_t s);
+
+// ---- grouped GEMM for many rows per expert (gemm_tile.hip) ----
+// m-blocks of kTileRows rows; activation operand in the fp8 layout (quant
+// mode 1) for both modes.
+constexpr int kTileRows = 128;
+enum TileMode { TILE_DOWN = 0, TILE_GATEUP = 1 };
+hipError_t launch_gemm_tile(const GemmArgs& a, int mode, hipStream_t s);
 
 // ---- combine (combine.hip) ----
 hipError_t launch_combine(const float* y2, const int32_t* src2dst, const float* topk_w,
