@@ -104,7 +104,8 @@ __device__ __forceinline__ void wait_vmcnt()
 // flight, including the stages still being filled).
 __device__ __forceinline__ void barrier()
 {
-    asm volatile("s_barrier" ::: "memory");
+    // this wave's LDS reads are complete before anyone may overwrite them
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // 16-byte slot of (activation row, chunk 0..7) and of (weight row, chunk 0..3)
@@ -129,12 +130,11 @@ __device__ __forceinline__ v8h fp8x8_to_f16(uint32_t d0, uint32_t d1)
 
 }  // namespace
 
+// One tile: rows [row0, row0 + 128) of m-block L's expert x weight block nb.
 template <int MODE, bool F64>
-__global__ __launch_bounds__(kTThreads) void gemm_tile_kernel(GemmArgs a)
+__device__ __forceinline__ void tile_body(const GemmArgs& a, const int L, uint8_t* smem, int* s_expert_p)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
-    __shared__ int s_expert;
-
+    int& s_expert = *s_expert_p;
     const int tid = threadIdx.x;
     // the wave index in an SGPR: LDS destinations of the direct loads go
     // through M0 and must be provably wave-uniform
@@ -146,15 +146,6 @@ __global__ __launch_bounds__(kTThreads) void gemm_tile_kernel(GemmArgs a)
     const int E = a.num_experts;
     const int nbn = MODE == TILE_GATEUP ? (int)(a.I / kGroup) : (int)((N + kTBN - 1) / kTBN);
 
-    // ---- the tile of this workgroup ----
-    const int total = *a.num_blocks * nbn;
-    const int per_xcd = (total + 7) >> 3;
-    const int xslot = (int)(blockIdx.x >> 3);
-    if (xslot >= per_xcd)
-        return;
-    const int L = (int)(blockIdx.x & 7) * per_xcd + xslot;
-    if (L >= total)
-        return;
     if (tid == 0)
         s_expert = -1;
     __syncthreads();
@@ -230,6 +221,8 @@ __global__ __launch_bounds__(kTThreads) void gemm_tile_kernel(GemmArgs a)
         wrow_f[f] = MODE == TILE_GATEUP ? (f >= 2 ? 128 : 0) + 32 * wn + 16 * (f & 1) + c16
                                         : 64 * wn + 16 * f + c16;
 
+    const bool wave_idle = 64 * wm >= rows;
+
     using Acc = typename std::conditional<F64, double, float>::type;
     Acc acc[4][4][4];
 #pragma unroll
@@ -240,82 +233,128 @@ __global__ __launch_bounds__(kTThreads) void gemm_tile_kernel(GemmArgs a)
             for (int r = 0; r < 4; ++r)
                 acc[m][f][r] = 0;
 
-#pragma unroll
-    for (int s = 0; s < kStages - 1; ++s)
-        issue(s < G ? s : G - 1, s);
-
-    for (int g = 0; g < G; ++g) {
-        wait_vmcnt<kLoadsPerStage * (kStages - 2)>();  // this wave's loads of group g landed
-        barrier();  // everyone's did, and stage (g - 1) % kStages is no longer read
-        {
-            const int gn = g + kStages - 1;
-            issue(gn < G ? gn : G - 1, gn % kStages);
-        }
-        const uint8_t* base = smem + (g % kStages) * kStageBytes;
-
-        float sw[4];
-        v4i wb[4];
+    // this wave's loads of group h landed (the younger groups in flight may
+    // stay so: loads retire in order)
+    auto wait_group = [&](int h) {
+        const int behind = min(kStages - 2, G - 1 - h);
+        if (behind >= 2)
+            wait_vmcnt<2 * kLoadsPerStage>();
+        else if (behind == 1)
+            wait_vmcnt<kLoadsPerStage>();
+        else
+            wait_vmcnt<0>();
+    };
+    // LDS fragment reads: the weight fragments of a stage, and the activation
+    // fragment + side data of one 16-row slice m
+    auto read_b = [&](const uint8_t* base, v4i (&wb)[4], float (&sw)[4]) {
 #pragma unroll
         for (int f = 0; f < 4; ++f) {
             wb[f] = *(const v4i*)(base + kBOff + 16 * b_slot(wrow_f[f], q));
             sw[f] = *(const float*)(base + kSwOff + 4 * wrow_f[f]);
         }
-        v8i b8[4];
-#pragma unroll
-        for (int f = 0; f < 4; ++f)
-            b8[f] = unpack_int4_u(wb[f]);
-        v8h bh[MODE == TILE_GATEUP ? 4 : 1][4];
-        if (MODE == TILE_GATEUP) {
-#pragma unroll
-            for (int f = 0; f < 4; ++f)
-#pragma unroll
-                for (int c = 0; c < 4; ++c)
-                    bh[f][c] = fp8x8_to_f16((uint32_t)b8[f][2 * c], (uint32_t)b8[f][2 * c + 1]);
-        }
+    };
+    auto read_a = [&](const uint8_t* base, int m, v4i& a0, v4i& a1, float4& s01, float4& s23) {
+        const int trow = 64 * wm + 16 * m;
+        a0 = *(const v4i*)(base + kAOff + 16 * a_slot(trow + c16, q));
+        a1 = *(const v4i*)(base + kAOff + 16 * a_slot(trow + c16, 4 + q));
+        const float4* sd = (const float4*)(base + kSideOff + 8 * (trow + 4 * q));
+        s01 = sd[0];
+        s23 = sd[1];
+    };
 
+    // Software pipeline.  Stages: groups g+1..g+3 are in flight while group g
+    // is computed.  Registers: the LDS fragments of the next slice (and, across
+    // the group boundary, of the next group) are read while the current one
+    // runs its MFMAs, so LDS latency hides behind them.
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const int trow = 64 * wm + 16 * m;
-            if (trow >= rows)  // wave-uniform: no valid row in this fragment
-                continue;
-            const v4i a0 = *(const v4i*)(base + kAOff + 16 * a_slot(trow + c16, q));
-            const v4i a1 = *(const v4i*)(base + kAOff + 16 * a_slot(trow + c16, 4 + q));
-            const float4* sd = (const float4*)(base + kSideOff + 8 * (trow + 4 * q));
-            const float4 s01 = sd[0], s23 = sd[1];
-            const float c1[4] = {s01.x, s01.z, s23.x, s23.z};
-            const float c0[4] = {s01.y, s01.w, s23.y, s23.w};
-            v4f raw[4];
+    for (int s = 0; s < kStages - 1; ++s)
+        if (s < G)
+            issue(s, s);
+    wait_group(0);
+    barrier();
+    if (kStages - 1 < G)
+        issue(kStages - 1, kStages - 1);
+    v4i wb[4], a0 = {}, a1 = {};
+    float sw[4];
+    float4 s01 = {}, s23 = {};
+    if (!wave_idle) {
+        read_b(smem, wb, sw);
+        read_a(smem, 0, a0, a1, s01, s23);
+    }
+
+    for (int g = 0; g < G; ++g) {
+        const uint8_t* base = smem + (g % kStages) * kStageBytes;
+        if (!wave_idle) {
+            float swc[4];
+            v8i b8[4];
+#pragma unroll
+            for (int f = 0; f < 4; ++f) {
+                swc[f] = sw[f];
+                b8[f] = unpack_int4_u(wb[f]);
+            }
+            v8h bh[MODE == TILE_GATEUP ? 4 : 1][4];
             if (MODE == TILE_GATEUP) {
-                v8h ah[4];
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const v4i& src = c < 2 ? a0 : a1;
-                    ah[c] = fp8x8_to_f16((uint32_t)src[2 * (c & 1)], (uint32_t)src[2 * (c & 1) + 1]);
-                }
 #pragma unroll
                 for (int f = 0; f < 4; ++f)
-                    raw[f] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-                for (int c = 0; c < 4; ++c)
+                    for (int c = 0; c < 4; ++c)
+                        bh[f][c] = fp8x8_to_f16((uint32_t)b8[f][2 * c], (uint32_t)b8[f][2 * c + 1]);
+            }
+            // all four slices in one basic block (padding rows are computed and
+            // dropped at the store)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const v4i ca0 = a0, ca1 = a1;
+                const float c1[4] = {s01.x, s01.z, s23.x, s23.z};
+                const float c0[4] = {s01.y, s01.w, s23.y, s23.w};
+                if (m < 3)
+                    read_a(base, m + 1, a0, a1, s01, s23);
+                v4f raw[4];
+                if (MODE == TILE_GATEUP) {
+                    v8h ah[4];
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const v4i& src = c < 2 ? ca0 : ca1;
+                        ah[c] = fp8x8_to_f16((uint32_t)src[2 * (c & 1)], (uint32_t)src[2 * (c & 1) + 1]);
+                    }
 #pragma unroll
                     for (int f = 0; f < 4; ++f)
-                        raw[f] = mfma16x16x32_f16(ah[c], bh[f][c], raw[f]);
-            } else {
-                const v8i av = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+                        raw[f] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+#pragma unroll
+                        for (int f = 0; f < 4; ++f)
+                            raw[f] = mfma16x16x32_f16(ah[c], bh[f][c], raw[f]);
+                } else {
+                    const v8i av = {ca0[0], ca0[1], ca0[2], ca0[3], ca1[0], ca1[1], ca1[2], ca1[3]};
+#pragma unroll
+                    for (int f = 0; f < 4; ++f)
+                        raw[f] = mfma16x16x128(av, b8[f], v4f{0.0f, 0.0f, 0.0f, 0.0f});
+                }
 #pragma unroll
                 for (int f = 0; f < 4; ++f)
-                    raw[f] = mfma16x16x128(av, b8[f], v4f{0.0f, 0.0f, 0.0f, 0.0f});
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        if (F64)
+                            acc[m][f][r] = fma((double)swc[f], fma((double)raw[f][r], (double)c1[r], (double)c0[r]),
+                                               (double)acc[m][f][r]);
+                        else
+                            acc[m][f][r] = fmaf(swc[f], fmaf(raw[f][r], c1[r], c0[r]), (float)acc[m][f][r]);
+                    }
             }
-#pragma unroll
-            for (int f = 0; f < 4; ++f)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    if (F64)
-                        acc[m][f][r] = fma((double)sw[f], fma((double)raw[f][r], (double)c1[r], (double)c0[r]),
-                                           (double)acc[m][f][r]);
-                    else
-                        acc[m][f][r] = fmaf(sw[f], fmaf(raw[f][r], c1[r], c0[r]), (float)acc[m][f][r]);
-                }
+        }
+        if (g + 1 < G) {
+            wait_group(g + 1);
+            // everyone's loads of group g+1 landed, and every wave's reads of
+            // stage g are complete: refill it with group g+4
+            barrier();
+            if (g + kStages < G)
+                issue(g + kStages, g % kStages);
+            if (!wave_idle) {
+                const uint8_t* nbase = smem + ((g + 1) % kStages) * kStageBytes;
+                read_b(nbase, wb, sw);
+                read_a(nbase, 0, a0, a1, s01, s23);
+            }
         }
     }
 
@@ -339,8 +378,7 @@ __global__ __launch_bounds__(kTThreads) void gemm_tile_kernel(GemmArgs a)
     }
 
     // TILE_GATEUP: fragments f and f + 2 hold gate and up of i = 32wn + 16f + c16
-    wait_vmcnt<0>();  // the trailing (unused) stage loads still write LDS
-    barrier();
+    barrier();  // every wave is done with the stages (no load is in flight)
     float* s_red = (float*)smem;                        // [4][128] amax per wave column
     float* s_sum = s_red + 4 * kTBM;                    // [4][128] sum of decoded codes
     uint8_t* s_q = (uint8_t*)(s_sum + 4 * kTBM);        // [128][128] codes
@@ -403,13 +441,39 @@ __global__ __launch_bounds__(kTThreads) void gemm_tile_kernel(GemmArgs a)
     }
 }
 
+// Persistent: each workgroup walks the tiles of its XCD's range.
+template <int MODE, bool F64>
+__global__ __launch_bounds__(kTThreads) void gemm_tile_kernel(GemmArgs a)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
+    __shared__ int s_expert;
+    const int nbn = MODE == TILE_GATEUP ? (int)(a.I / kGroup) : (int)((a.N + kTBN - 1) / kTBN);
+    const int total = *a.num_blocks * nbn;
+    const int per_xcd = (total + 7) >> 3;
+    const int x = (int)(blockIdx.x & 7);
+    const int stride = (int)(gridDim.x >> 3);
+    for (int t = (int)(blockIdx.x >> 3); t < per_xcd; t += stride) {
+        const int L = x * per_xcd + t;
+        if (L >= total)
+            break;
+        tile_body<MODE, F64>(a, L, smem, &s_expert);
+        __syncthreads();  // the next tile's loads overwrite LDS the epilogue may still read
+    }
+}
+
 hipError_t launch_gemm_tile(const GemmArgs& a, int mode, hipStream_t s)
 {
     const int64_t nbn = mode == TILE_GATEUP ? a.I / kGroup : (a.N + kTBN - 1) / kTBN;
     const int64_t tiles = nbn * a.max_blocks;
     if (tiles == 0)
         return hipSuccess;
-    const dim3 grid((unsigned)((tiles + 7) / 8 * 8));
+    // one workgroup per CU (the LDS stages allow no more), a multiple of the 8 XCDs
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 8)
+        cus = 256;
+    const int64_t wgs = tiles < cus ? tiles : cus;
+    const dim3 grid((unsigned)((wgs + 7) / 8 * 8));
 #ifndef W4A8_TILE_F64
 #define W4A8_TILE_F64 0
 #endif
