@@ -16,8 +16,10 @@ the prefill workloads (T=4096 and the EP8 rank share T=32768) and the CPU
 oracle baseline.
 """
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -93,8 +95,10 @@ class Workload:
                       w2, s2, out=self.out, workspace=self.ws)
 
 
-def time_steps(wl, steps, warmup):
-    """Whole-step time: events + synchronize around exactly `steps` calls."""
+def time_steps(wl, steps, warmup, span=None):
+    """Whole-step time: events + synchronize around exactly `steps` calls.
+    With a SpanTimer, each timed call also records the two events of one
+    stage on the library's stream; their mean span is returned too."""
     import torch
     for i in range(warmup):
         wl.step(i)
@@ -102,10 +106,15 @@ def time_steps(wl, steps, warmup):
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
     for i in range(steps):
+        if span is not None:
+            span.arm(i)
         wl.step(i)
     end.record()
     torch.cuda.synchronize()
-    return start.elapsed_time(end) * 1e3 / steps  # µs per step
+    us = start.elapsed_time(end) * 1e3 / steps  # µs per step
+    if span is None:
+        return us
+    return us, float(np.mean(span.read_ms())) * 1e3
 
 
 def stage_breakdown(wl, steps):
@@ -122,6 +131,48 @@ def stage_breakdown(wl, steps):
     torch.cuda.synchronize()
     timer.close()
     return {k: float(np.mean(v)) for k, v in acc.items()}
+
+
+# Kernel sources whose HBM traffic the committed counter summary describes;
+# the summary's figure is reported only while they are unchanged.
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "decode_T64_gate_up_traffic.md")
+TRAFFIC_SOURCES = ("gemm_skinny.hip", "common.hpp", "internal.hpp")
+
+
+def kernel_source_digest(names=TRAFFIC_SOURCES):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "w4a8_moe_grouped_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch of the decode gate_up kernel from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary (scaled by a device-copy
+    calibration), or None if absent or taken on other kernel sources."""
+    try:
+        text = open(TRAFFIC_SUMMARY).read()
+    except OSError:
+        return None
+    m = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    d = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    if not m or not d or d.group(1) != kernel_source_digest():
+        return None
+    return float(m.group(1))
+
+
+def copy_calibration(nbytes=1 << 30, reps=4):
+    """A plain device copy of known size, for scaling the HBM byte counters."""
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "reps": reps}), flush=True)
 
 
 def cpu_baseline(name):
@@ -149,6 +200,8 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default=None, help="time just this workload (decode/prefill/...)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a 1 GiB device copy (scales the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this library runs the fused MoE on one GPU's share of experts; "
@@ -156,6 +209,9 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_calibration:
+        copy_calibration()
+        return
     from w4a8_moe_grouped_amd import lib
     if not os.path.exists(lib.LIB_PATH):
         from w4a8_moe_grouped_amd import build
@@ -167,15 +223,19 @@ def main():
     primary = args.only or "decode"
     wl = Workload(primary, nsets=2, dev=dev)
     cfg, st = wl.cfg, wl.stats
-    us = time_steps(wl, args.steps, args.warmup)
+    # the dominant kernel of the decode step is gate_up (stage hook events 2 -> 3)
+    span = lib.SpanTimer(2, 3, args.steps)
+    us, dom_us = time_steps(wl, args.steps, args.warmup, span=span)
+    span.close()
     stages = stage_breakdown(wl, max(5, min(args.steps, 20)))
     log("[bench] %s: %.1f us/call, stages %s" % (primary, us, {k: round(v, 1) for k, v in stages.items()}))
     byts, flops = moe_bytes(cfg, st), moe_flops(cfg, st)
     gb_s = byts / (us * 1e-6) / 1e9
     tflops = flops / (us * 1e-6) / 1e12
-    dom = max(("gate_up", "down"), key=lambda k: stages[k])
-    dom_bytes = gate_up_bytes(cfg, st) if dom == "gate_up" else down_bytes(cfg, st)
-    dom_gbs = dom_bytes / (stages[dom] * 1e-6) / 1e9
+    dom = "gate_up"
+    dom_bytes = gate_up_bytes(cfg, st)
+    dom_gbs = dom_bytes / (dom_us * 1e-6) / 1e9
+    traffic = measured_traffic() if primary == "decode" else None
 
     result = {
         "metric": METRIC,
@@ -199,8 +259,8 @@ def main():
         "stages_us": {k: round(v, 2) for k, v in stages.items()},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(dom_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": None, "bytes_per_launch": dom_bytes,
-                     "avg_launch_us": round(stages[dom], 2)},
+                     "traffic": None if traffic is None else int(traffic),
+                     "bytes_per_launch": dom_bytes, "avg_launch_us": round(dom_us, 2)},
     }
 
     if not args.no_prefill and args.only is None:

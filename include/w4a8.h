@@ -30,13 +30,18 @@
  *  - int4 weights: byte b holds k even in b & 0xF and k odd in b >> 4, two's
  *    complement (-8..7), no zero point; one fp32 scale per 128 K-elements.
  *  - GEMM: y[m,n] = sum_g a_scale[m,g] * w_scale[n,g] * sum_{k in g}
- *    dec(a[m,k]) * w[n,k], accumulated in fp32 on the GPU.
+ *    dec(a[m,k]) * w[n,k].  On the GPU each group's sum comes from an MFMA
+ *    and is promoted with its two scales into an fp32 accumulator (fp64 in
+ *    the fused forward's decode-size gate_up GEMM); the gate_up GEMM of
+ *    w4a8_fused_moe runs on fp16 MFMA with exactly converted operands, whose
+ *    group sums are correctly rounded, because its output is re-quantised.
  *
  * Conventions:
  *  - Every pointer is a device pointer on the current HIP device unless
  *    noted, 16-byte aligned.  The caller owns all memory; the library never
- *    allocates, keeps no state between calls, and never synchronises the
- *    host: every launch is asynchronous on `stream` (0 = the null stream).
+ *    allocates and never synchronises the host: every launch is asynchronous
+ *    on `stream` (0 = the null stream).  The only state between calls is the
+ *    per-thread arming of w4a8_fused_moe_stage_events (a profiling hook).
  *  - Return value: W4A8_OK, or an error code.  Arguments are validated on the
  *    host before anything is launched; on error nothing is launched and no
  *    output is touched.  W4A8_ERR_HIP reports a failed launch.
@@ -171,10 +176,14 @@ int w4a8_fused_moe(const void* hidden_bf16, int64_t T, int64_t H,
  *   offsets[3]  src2dst         int32 [T*topk]
  *   offsets[4]  block_expert    int32 [nb]     offsets[5] block_row int32 [nb]
  *   offsets[6]  num_blocks      int32 [1]      (nb <= ceil(T*topk/block_m)+E_l)
- *   offsets[7]  gate_up operand: the fp8 hidden codes' exact values as fp16
- *               [T, H]; inside each 128-group, 8-group b (k = 8b..8b+7) sits
- *               at 16-byte chunk 4*(b%4) + b/4, in K order k0,k4,k1,k5,k2,k6,k3,k7
- *   offsets[8]  float2 [T, H/128]  {scale, 0}
+ *   offsets[7]  gate_up operand: fp8 codes of the hidden states [T, H];
+ *               inside each 128-group, 8-group b (k = 8b..8b+7) sits at byte
+ *               16*(4*((b%4)/2) + b/4) + 8*(b%2).  In K order
+ *               k0,k4,k1,k5,k2,k6,k3,k7 when block_m <= 64 (few rows per
+ *               expert), k0,k2,k4,k6,k1,k3,k5,k7 when block_m == 128
+ *   offsets[8]  float2 [T, H/128]: {scale, 0} when block_m <= 64,
+ *               {512*scale, -8*scale*sum of the block's decoded codes} when
+ *               block_m == 128
  *   offsets[9]  requantised intermediate: fp8 codes [T*topk, I] (pair rows
  *               in permuted order); inside each 128-group, 8-group b sits at
  *               byte 16*(4*((b%4)/2) + b/4) + 8*(b%2), in K order
@@ -197,8 +206,9 @@ int w4a8_fused_moe_workspace_layout(int64_t T, int64_t H, int64_t topk,
  * record events[i] (hipEvent_t handles created by the caller) on its stream:
  *   [0] before align  [1] after align  [2] after the input quantisation
  *   [3] after gate_up+SwiGLU+requant   [4] after down  [5] after combine
+ * A null entry is skipped (so a caller can time one stage with two events).
  * n must be 6 (or 0 to disarm).  The call consumes the arming; it never
- * synchronises.  Returns W4A8_ERR_INVALID_ARG for a bad n or null events.
+ * synchronises.  Returns W4A8_ERR_INVALID_ARG for a bad n or a null array.
  */
 int w4a8_fused_moe_stage_events(void* const* events, int n);
 

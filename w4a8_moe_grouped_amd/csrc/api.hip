@@ -139,7 +139,7 @@ thread_local void* const* t_stage_events = nullptr;
 
 inline void mark(void* const* ev, int i, hipStream_t s)
 {
-    if (ev != nullptr)
+    if (ev != nullptr && ev[i] != nullptr)
         (void)hipEventRecord((hipEvent_t)ev[i], s);
 }
 
@@ -391,9 +391,6 @@ int w4a8_fused_moe_stage_events(void* const* events, int n)
     }
     if (n != 6 || events == nullptr)
         return W4A8_ERR_INVALID_ARG;
-    for (int i = 0; i < 6; ++i)
-        if (events[i] == nullptr)
-            return W4A8_ERR_INVALID_ARG;
     t_stage_events = events;
     return W4A8_OK;
 }

@@ -231,6 +231,53 @@ class StageTimer:
             self.hip.hipEventDestroy(self.ev[i])
 
 
+class SpanTimer:
+    """HIP events around one stage (events `first` -> `last` of the stage
+    hook, see STAGES) of each of the next `n` fused_moe calls, one event pair
+    per call, recorded on the library's stream; the other hook slots stay
+    empty so a call records only two events."""
+
+    def __init__(self, first: int, last: int, n: int):
+        if not (0 <= first < last <= 5) or n < 1:
+            raise W4A8Error("bad span")
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.first, self.last, self.n = first, last, n
+        self.ev = []
+        for _ in range(2 * n):
+            h = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(h)) != 0:
+                raise W4A8Error("hipEventCreate failed")
+            self.ev.append(h)
+        self.slots = []
+        for j in range(n):
+            arr = (ctypes.c_void_p * 6)()
+            arr[first] = self.ev[2 * j]
+            arr[last] = self.ev[2 * j + 1]
+            self.slots.append(arr)
+
+    def arm(self, j: int):
+        _check(load().w4a8_fused_moe_stage_events(self.slots[j], 6), "w4a8_fused_moe_stage_events")
+
+    def read_ms(self):
+        """Milliseconds of the span in each of the n calls (synchronises)."""
+        out = []
+        for j in range(self.n):
+            self.hip.hipEventSynchronize(self.ev[2 * j + 1])
+            ms = ctypes.c_float()
+            self.hip.hipEventElapsedTime(ctypes.byref(ms), self.ev[2 * j], self.ev[2 * j + 1])
+            out.append(ms.value)
+        return out
+
+    def close(self):
+        for h in self.ev:
+            self.hip.hipEventDestroy(h)
+
+
 def fused_moe(hidden: torch.Tensor, topk_ids: torch.Tensor, topk_weights: torch.Tensor,
               expert_begin: int, num_local_experts: int, w13: torch.Tensor, s13: torch.Tensor,
               w2: torch.Tensor, s2: torch.Tensor, out: Optional[torch.Tensor] = None,
