@@ -178,12 +178,10 @@ int w4a8_fused_moe(const void* hidden_bf16, int64_t T, int64_t H,
  *   offsets[6]  num_blocks      int32 [1]      (nb <= ceil(T*topk/block_m)+E_l)
  *   offsets[7]  gate_up operand: fp8 codes of the hidden states [T, H];
  *               inside each 128-group, 8-group b (k = 8b..8b+7) sits at byte
- *               16*(4*((b%4)/2) + b/4) + 8*(b%2).  In K order
- *               k0,k4,k1,k5,k2,k6,k3,k7 when block_m <= 64 (few rows per
- *               expert), k0,k2,k4,k6,k1,k3,k5,k7 when block_m == 128
- *   offsets[8]  float2 [T, H/128]: {scale, 0} when block_m <= 64,
- *               {512*scale, -8*scale*sum of the block's decoded codes} when
- *               block_m == 128
+ *               16*(4*((b%4)/2) + b/4) + 8*(b%2), in K order
+ *               k0,k2,k4,k6,k1,k3,k5,k7
+ *   offsets[8]  float2 [T, H/128] {512*scale, -8*scale*sum of the block's
+ *               decoded codes}
  *   offsets[9]  requantised intermediate: fp8 codes [T*topk, I] (pair rows
  *               in permuted order); inside each 128-group, 8-group b sits at
  *               byte 16*(4*((b%4)/2) + b/4) + 8*(b%2), in K order
@@ -205,6 +203,8 @@ int w4a8_fused_moe_workspace_layout(int64_t T, int64_t H, int64_t topk,
  * Arms the NEXT w4a8_fused_moe call made on the calling host thread to
  * record events[i] (hipEvent_t handles created by the caller) on its stream:
  *   [0] before align  [1] after align  [2] after the input quantisation
+ *   (with T*topk <= 4096 align and quantisation are one launch, so [1] and
+ *   [2] are both recorded after it)
  *   [3] after gate_up+SwiGLU+requant   [4] after down  [5] after combine
  * A null entry is skipped (so a caller can time one stage with two events).
  * n must be 6 (or 0 to disarm).  The call consumes the arming; it never

@@ -16,17 +16,19 @@
 // When all pairs fit one chunk the three phases run in one block (decode).
 #include "common.hpp"
 #include "internal.hpp"
+#include "quant_block.hpp"
 
 namespace w4a8 {
 
 constexpr int kAlignThreads = 256;
 constexpr int kAlignWaves = kAlignThreads / 64;
-constexpr int kAlignChunk = 4096;  // pairs per chunk
+constexpr int kAlignSingle = 4096;  // up to this many pairs: one block does everything
+constexpr int kAlignChunk = 1024;   // otherwise pairs per chunk (one block each)
 constexpr int kMaxLocalExperts = 1024;
 
 int64_t align_chunk_count(int64_t F)
 {
-    return F <= 0 ? 1 : (F + kAlignChunk - 1) / kAlignChunk;
+    return F <= kAlignSingle ? 1 : (F + kAlignChunk - 1) / kAlignChunk;
 }
 size_t align_workspace_bytes(int64_t F, int64_t E)
 {
@@ -189,13 +191,11 @@ struct AlignLds {
     int scratch[kAlignWaves + 1];
 };
 
-// everything in one block (F <= kAlignChunk)
-__global__ __launch_bounds__(kAlignThreads) void align_single_kernel(const int32_t* __restrict__ ids,
-                                                                     int64_t F, int64_t eb,
-                                                                     int64_t E, int64_t block_m,
-                                                                     AlignOut o)
+// everything in one block (F <= kAlignSingle)
+__device__ __forceinline__ void align_single_body(const int32_t* __restrict__ ids, int64_t F,
+                                                  int64_t eb, int64_t E, int64_t block_m,
+                                                  const AlignOut& o, AlignLds& L)
 {
-    __shared__ AlignLds L;
     const int t = threadIdx.x;
     for (int e = t; e < E; e += kAlignThreads)
         L.a[e] = 0;
@@ -210,6 +210,34 @@ __global__ __launch_bounds__(kAlignThreads) void align_single_kernel(const int32
     __syncthreads();
     finish_scan(L.a, L.b, L.scratch, E, block_m, o);  // L.a now holds the offsets
     scatter_chunk(ids, 0, F, eb, E, L.a, L.wcnt, o);
+}
+
+__global__ __launch_bounds__(kAlignThreads) void align_single_kernel(const int32_t* __restrict__ ids,
+                                                                     int64_t F, int64_t eb,
+                                                                     int64_t E, int64_t block_m,
+                                                                     AlignOut o)
+{
+    __shared__ AlignLds L;
+    align_single_body(ids, F, eb, E, block_m, o, L);
+}
+
+// The routing permutation and the activation quantisation are independent:
+// one launch does both.  Block 0 runs the single-block align (and clears
+// `clear`, counters a later kernel of the call may use); blocks 1.. quantise
+// (mode 1).
+__global__ __launch_bounds__(kAlignThreads) void align_quant_kernel(
+    const int32_t* __restrict__ ids, int64_t F, int64_t eb, int64_t E, int64_t block_m, AlignOut o,
+    int32_t* __restrict__ clear, int32_t nclear, const uint16_t* __restrict__ x, int64_t M,
+    int64_t K, int64_t ldx, uint8_t* __restrict__ q, float2* __restrict__ side)
+{
+    __shared__ AlignLds L;
+    if (blockIdx.x == 0) {
+        for (int i = threadIdx.x; i < nclear; i += kAlignThreads)
+            clear[i] = 0;
+        align_single_body(ids, F, eb, E, block_m, o, L);
+        return;
+    }
+    quant_block<1>(x, M, K, ldx, q, nullptr, side, (int64_t)blockIdx.x - 1);
 }
 
 __global__ __launch_bounds__(kAlignThreads) void align_count_kernel(const int32_t* __restrict__ ids,
@@ -240,13 +268,22 @@ __global__ __launch_bounds__(kAlignThreads) void align_scan_kernel(int32_t* __re
 {
     __shared__ AlignLds L;
     const int t = threadIdx.x;
-    // per expert: chunk-exclusive prefix (in place) and the total
+    // per expert: chunk-exclusive prefix (in place) and the total; the
+    // counts are read 16 chunks at a time so the loads overlap
+    constexpr int kBatch = 16;
     for (int e = t; e < E; e += kAlignThreads) {
         int run = 0;
-        for (int64_t c = 0; c < nchunks; ++c) {
-            const int h = hist[c * E + e];
-            hist[c * E + e] = run;
-            run += h;
+        for (int64_t c0 = 0; c0 < nchunks; c0 += kBatch) {
+            int h[kBatch];
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j)
+                h[j] = c0 + j < nchunks ? hist[(c0 + j) * E + e] : 0;
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) {
+                if (c0 + j < nchunks)
+                    hist[(c0 + j) * E + e] = run;
+                run += h[j];
+            }
         }
         L.a[e] = run;
     }
@@ -276,6 +313,18 @@ __global__ __launch_bounds__(kAlignThreads) void align_scatter_kernel(const int3
     const int64_t f0 = (int64_t)blockIdx.x * kAlignChunk;
     const int64_t f1 = f0 + kAlignChunk < F ? f0 + kAlignChunk : F;
     scatter_chunk(ids, f0, f1, eb, E, base, wcnt, o);
+}
+
+hipError_t launch_align_quant(const int32_t* ids, int64_t T, int64_t topk, int64_t expert_begin,
+                              int64_t E, int64_t block_m, const AlignOut& o, int32_t* clear,
+                              int32_t nclear, const uint16_t* x, int64_t H, uint8_t* q,
+                              float2* side, hipStream_t s)
+{
+    const int64_t F = T * topk;
+    const int64_t qblocks = (T * (H / kGroup) + 15) / 16;
+    hipLaunchKernelGGL(align_quant_kernel, dim3((unsigned)(1 + qblocks)), dim3(kAlignThreads), 0, s,
+                       ids, F, expert_begin, E, block_m, o, clear, nclear, x, T, H, H, q, side);
+    return hipGetLastError();
 }
 
 hipError_t launch_align(const int32_t* ids, int64_t T, int64_t topk, int64_t expert_begin,

@@ -294,17 +294,26 @@ int w4a8_fused_moe(const void* hidden_bf16, int64_t T, int64_t H, const int32_t*
     plan_moe(workspace, T, H, topk, E, I, p);
 
     mark(ev, 0, stream);
-    hipError_t e = w4a8::launch_align(topk_ids, T, topk, expert_begin, E, p.block_m, p.al,
-                                      p.align_ws, stream);
-    if (e != hipSuccess)
-        return W4A8_ERR_HIP;
-    mark(ev, 1, stream);
-    // activation operand of gate_up: f16-ordered codes for the skinny kernel,
-    // the fp8 layout for the tile kernel
-    e = w4a8::launch_quant_bf16((const uint16_t*)hidden_bf16, T, H, H, p.qa, nullptr, p.qa_side,
-                                p.tile ? 1 : 2, stream);
-    if (e != hipSuccess)
-        return W4A8_ERR_HIP;
+    hipError_t e;
+    if (w4a8::align_chunk_count(p.F) == 1) {
+        // few pairs: align and quantisation in one launch (both stage events
+        // are recorded after it)
+        e = w4a8::launch_align_quant(topk_ids, T, topk, expert_begin, E, p.block_m, p.al, nullptr,
+                                     0, (const uint16_t*)hidden_bf16, H, p.qa, p.qa_side, stream);
+        if (e != hipSuccess)
+            return W4A8_ERR_HIP;
+        mark(ev, 1, stream);
+    } else {
+        e = w4a8::launch_align(topk_ids, T, topk, expert_begin, E, p.block_m, p.al, p.align_ws,
+                               stream);
+        if (e != hipSuccess)
+            return W4A8_ERR_HIP;
+        mark(ev, 1, stream);
+        e = w4a8::launch_quant_bf16((const uint16_t*)hidden_bf16, T, H, H, p.qa, nullptr,
+                                    p.qa_side, 1, stream);
+        if (e != hipSuccess)
+            return W4A8_ERR_HIP;
+    }
     mark(ev, 2, stream);
 
     w4a8::GemmArgs g = {};

@@ -30,11 +30,10 @@
 //    at byte 16*(4*((b%4)/2) + b/4) + 8*(b%2) of the group (fp8_group_pos).
 //    Per-row-per-group side data is float2 {c1, c0}.
 //
-//  * Internal gate_up activation layout: fp8 codes ordered k0,k4,k1,k5 |
-//    k2,k6,k3,k7 inside every aligned group of 8, so that each 16-bit pair
-//    converts (v_cvt_scalef32_pk_f16_fp8, exact) into the f16 pair the int4
-//    unpack produces for the same k's; 8-groups placed by fp8_group_pos.
-//    Side data {scale, 0}.
+//  * The gate_up GEMMs use the same fp8 operand layout and side data, and
+//    convert both operands exactly to fp16 in registers (the weight codes
+//    u * 2^-9 and every e4m3 value are fp16 numbers) for the fp16 MFMA, whose
+//    group sums are correctly rounded.
 //
 //  * MFMA v_mfma_f32_16x16x128_f8f6f4 (fp8 x fp8): lane l holds row l%16 of
 //    A and column l%16 of B, 32 K-bytes each (the lane's quarter q = l/16 of
@@ -88,25 +87,6 @@ __device__ __forceinline__ uint32_t xor_and_or(uint32_t x)
     return __builtin_amdgcn_bitop3_b32(x, A, B, 0x9A);
 }
 
-// 4 bytes of packed int4 (k0..k7) -> 8 exact fp16 values in the order
-// k0,k4,k1,k5,k2,k6,k3,k7: with u = n ^ 8 = v + 8, the half 0x6400|u is
-// 1024 + u, and subtracting 1032 leaves v.
-__device__ __forceinline__ v8h unpack_int4_f16(uint32_t x)
-{
-    constexpr uint32_t k = 0x00080008u, m = 0x000F000Fu, magic = 0x64006400u;
-    const uint32_t d[4] = {xor_and_or<k, m, magic>(x), xor_and_or<k, m, magic>(x >> 4),
-                           xor_and_or<k, m, magic>(x >> 8), xor_and_or<k, m, magic>(x >> 12)};
-    const v2h bias = {(_Float16)1032.0f, (_Float16)1032.0f};
-    v8h r;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const v2h h = __builtin_bit_cast(v2h, d[i]) - bias;
-        r[2 * i] = h[0];
-        r[2 * i + 1] = h[1];
-    }
-    return r;
-}
-
 // 16 bytes of packed int4 (32 nibbles) -> 32 fp8 bytes (u * 2^-9 codes) in
 // the K-interleaved order described above.
 __device__ __forceinline__ v8i unpack_int4_u(const v4i& w)
@@ -119,6 +99,17 @@ __device__ __forceinline__ v8i unpack_int4_u(const v4i& w)
         r[2 * i + 1] = (int)xor_and_or<0x08080808u, 0x0F0F0F0Fu, 0u>(x >> 4);
     }
     return r;
+}
+
+// two fp8 dwords (4 + 4 codes) -> 8 exact halves, in dword order (e4m3
+// values, the u * 2^-9 weight codes included, are all exact in fp16)
+__device__ __forceinline__ v8h fp8x8_to_f16(uint32_t d0, uint32_t d1)
+{
+    const v2h h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d0, 1.0f, false);
+    const v2h h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d0, 1.0f, true);
+    const v2h h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d1, 1.0f, false);
+    const v2h h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d1, 1.0f, true);
+    return v8h{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
 }
 
 // canonical 8 codes (two dwords k0..k3, k4..k7) -> interleaved (k0,k2,k4,k6 | k1,k3,k5,k7)

@@ -118,8 +118,8 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs a)
 
     // The f16 (gate_up) path promotes in fp64: each group's MFMA sum is the
     // correctly rounded fp32 value of an exact dot product, and keeping the
-    // running sum in fp64 leaves y within ~2^-25 of the exact result, so the
-    // SwiGLU + fp8 requant that follows almost never lands on another code.
+    // running sum in fp64 leaves y within a few 2^-24 of the exact result, so
+    // the SwiGLU + fp8 requant that follows rarely lands on another code.
     // The fp8 path promotes in fp32.
     using Acc = typename std::conditional<F16, double, float>::type;
     Acc acc[kNF][NT][4];
@@ -131,24 +131,26 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs a)
             for (int r = 0; r < 4; ++r)
                 acc[f][t][r] = 0;
 
-    // One ring of DW groups in flight for everything a group needs (weights,
-    // weight scales, activations).  Vector-memory loads retire in issue order,
-    // so loads consumed at different distances would make the nearest one
-    // drain the rest; one common distance keeps DW-1 groups in flight.  The
-    // loop runs over ceil(G/DW)*DW groups without branches: a refill past the
-    // last group reloads group G-1 (never used) and a padding group gets
-    // weight scale 0.
+    // One ring of DW groups in flight for the weights and activations of a
+    // group.  Vector-memory loads retire in issue order, so loads consumed at
+    // different distances would make the nearest one drain the rest; the ring
+    // keeps one common distance.  The loop runs over whole turns without
+    // branches: a refill past the last group reloads group G-1 (never used)
+    // and a padding group gets weight scale 0.
     //
-    // Weight scales: with SW4 (G % 4 == 0, DW % 4 == 0) one float4 per
-    // fragment carries groups g..g+3 and rides in the ring slot of group g,
-    // a quarter of the memory instructions of one float per group.  It lands
-    // in the next turn's bank (sb4n) while this turn still reads sb4c; the
-    // banks swap at the turn boundary.
-    static_assert(!SW4 || DW % 4 == 0, "float4 scales need a ring of whole 4-group blocks");
-    constexpr int NS = SW4 ? DW / 4 : DW;
+    // Weight scales: with SW4 (G % 4 == 0) one float4 per fragment carries a
+    // block of 4 groups, a quarter of the memory instructions of one float per
+    // group.  The next block's float4 is issued at the first group of a block,
+    // before that group's ring refill, so it retires no later than the
+    // weights it is consumed with; the banks swap at the block boundary.  The
+    // loop is unrolled over U = 4 groups (DW divides 4) so that slots and
+    // lanes of the float4 are static.  Otherwise one float per group rides in
+    // the ring slot.
+    static_assert(!SW4 || 4 % DW == 0, "float4 scales need DW to divide 4");
+    constexpr int U = SW4 ? 4 : DW;
     v4i wb[DW][kNF];
-    float sb[NS][kNF];
-    float4 sb4c[SW4 ? NS : 1][kNF], sb4n[SW4 ? NS : 1][kNF];
+    float sb[SW4 ? 1 : DW][kNF];
+    float4 sc4[SW4 ? kNF : 1], sn4[SW4 ? kNF : 1];
     v4i ab[DW][NT][2];
     auto load_group = [&](int s, int g) {
 #pragma unroll
@@ -156,8 +158,6 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs a)
             wb[s][f] = bload16(rw, vw[f], (uint32_t)g * 64u);
             if (!SW4)
                 sb[s][f] = bload4f(rs, vs[f], (uint32_t)g * 4u);
-            else if (s % 4 == 0)  // g % 4 == 0 here, and g + 3 < G (G % 4 == 0)
-                sb4n[s / 4][f] = __builtin_bit_cast(float4, bload16(rs, vs[f], (uint32_t)g * 4u));
         }
 #pragma unroll
         for (int t = 0; t < NT; ++t)
@@ -165,21 +165,19 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs a)
             for (int v = 0; v < 2; ++v)
                 ab[s][t][v] = bload16(ra, va[t], (uint32_t)g * kGroup + 64u * v);
     };
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int s = 0; s < DW; ++s)
-        load_group(s, s < G ? s : (SW4 ? G - 4 + (s % 4) : G - 1));
-    __builtin_amdgcn_sched_barrier(0);
-    auto swap_scales = [&]() {
+    auto load_scales4 = [&](float4 (&dst)[SW4 ? kNF : 1], int blk) {  // groups 4blk..4blk+3
         if (SW4) {
 #pragma unroll
-            for (int j = 0; j < NS; ++j)
-#pragma unroll
-                for (int f = 0; f < kNF; ++f)
-                    sb4c[j][f] = sb4n[j][f];
+            for (int f = 0; f < kNF; ++f)
+                dst[f] = __builtin_bit_cast(float4, bload16(rs, vs[f], (uint32_t)blk * 16u));
         }
     };
-    swap_scales();
+    __builtin_amdgcn_sched_barrier(0);
+    load_scales4(sc4, 0);
+#pragma unroll
+    for (int s = 0; s < DW; ++s)
+        load_group(s, s < G ? s : G - 1);
+    __builtin_amdgcn_sched_barrier(0);
 
     if (side_in_regs) {
 #pragma unroll
@@ -194,19 +192,28 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs a)
     }
     __syncthreads();
 
-    const int Gr = (G + DW - 1) / DW * DW;
-    for (int g0 = 0; g0 < Gr; g0 += DW) {
+    const int G4 = G / 4;
+    const int Gr = (G + U - 1) / U * U;
+    for (int g0 = 0; g0 < Gr; g0 += U) {
 #pragma unroll
-        for (int s = 0; s < DW; ++s) {
-            const int g = g0 + s;
+        for (int u = 0; u < U; ++u) {
+            const int g = g0 + u;
+            const int s = u % DW;  // ring slot
             const int gl = g < G ? g : G - 1;  // side data row (padding groups: any valid one)
+            if (SW4 && u == 0) {
+                // next block's scales, ahead of this turn's refills (the last
+                // block reloads itself; never used)
+                __builtin_amdgcn_sched_barrier(0);
+                load_scales4(sn4, g0 / 4 + 1 < G4 ? g0 / 4 + 1 : G4 - 1);
+                __builtin_amdgcn_sched_barrier(0);
+            }
             float swf[kNF];
 #pragma unroll
             for (int f = 0; f < kNF; ++f) {
                 float v;
                 if (SW4) {
-                    const float4 v4 = sb4c[s / 4][f];
-                    v = (s % 4) == 0 ? v4.x : (s % 4) == 1 ? v4.y : (s % 4) == 2 ? v4.z : v4.w;
+                    const float4 v4 = sc4[f];
+                    v = u == 0 ? v4.x : u == 1 ? v4.y : u == 2 ? v4.z : v4.w;
                 } else {
                     v = sb[s][f];
                 }
@@ -228,32 +235,31 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs a)
                 // accumulator, so they issue back to back; then the promotion
                 v4f raw[kNF];
                 if (F16) {
-                    // fp8 activation codes -> exact f16 (8-group c of the lane
-                    // is dwords 2c, 2c+1 in the order k0,k4,k1,k5 | k2,k6,k3,k7)
+                    // fp8 codes -> exact f16: the lane's 8-group c is dwords
+                    // 2c, 2c+1 of both operands (k0,k2,k4,k6 | k1,k3,k5,k7)
                     v8h ah[4];
 #pragma unroll
-                    for (int c = 0; c < 4; ++c) {
-                        const v2h h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(at[2 * c], 1.0f, false);
-                        const v2h h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(at[2 * c], 1.0f, true);
-                        const v2h h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(at[2 * c + 1], 1.0f, false);
-                        const v2h h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(at[2 * c + 1], 1.0f, true);
-                        ah[c] = v8h{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
-                    }
+                    for (int c = 0; c < 4; ++c)
+                        ah[c] = fp8x8_to_f16(at[2 * c], at[2 * c + 1]);
+                    v8i b8[kNF];
 #pragma unroll
-                    for (int f = 0; f < kNF; ++f)
+                    for (int f = 0; f < kNF; ++f) {
+                        b8[f] = unpack_int4_u(wb[s][f]);
                         raw[f] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+                    }
 #pragma unroll
                     for (int c = 0; c < 4; ++c)
 #pragma unroll
                         for (int f = 0; f < kNF; ++f)
-                            raw[f] = mfma16x16x32_f16(ah[c], unpack_int4_f16((uint32_t)wb[s][f][c]), raw[f]);
+                            raw[f] = mfma16x16x32_f16(
+                                ah[c], fp8x8_to_f16((uint32_t)b8[f][2 * c], (uint32_t)b8[f][2 * c + 1]), raw[f]);
 #pragma unroll
                     for (int f = 0; f < kNF; ++f) {
-                        // c0 == 0 on this path; sw * c1 is exact in fp64
                         const double swd = (double)swf[f];
 #pragma unroll
                         for (int r = 0; r < 4; ++r)
-                            acc[f][t][r] = fma((double)raw[f][r], swd * (double)c1[r], (double)acc[f][t][r]);
+                            acc[f][t][r] = fma(swd, fma((double)raw[f][r], (double)c1[r], (double)c0[r]),
+                                               (double)acc[f][t][r]);
                     }
                 } else {
                     v8i av;
@@ -274,14 +280,14 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs a)
             // barrier the scheduler sinks each load next to its consumer and
             // only one load stays in flight
             __builtin_amdgcn_sched_barrier(0);
-            {
-                // past the end: reload a valid group (aligned to 4 for SW4)
-                const int gn = g + DW < G ? g + DW : (SW4 ? G - 4 + (s % 4) : G - 1);
-                load_group(s, gn);
-            }
+            load_group(s, g + DW < G ? g + DW : G - 1);
             __builtin_amdgcn_sched_barrier(0);
         }
-        swap_scales();
+        if (SW4) {
+#pragma unroll
+            for (int f = 0; f < kNF; ++f)
+                sc4[f] = sn4[f];
+        }
     }
 
     // ---- epilogues ----  output element (row 16t+4q+r of the block, weight row nrow[f])
@@ -408,19 +414,19 @@ hipError_t launch_gemm_skinny(const GemmArgs& a, int epilogue, int block_m, hipS
     // gate_up (SwiGLU epilogue) runs on the exact f16 path, the others on fp8;
     // ring depth per m-block height
 #ifndef W4A8_DW16
-#define W4A8_DW16 4
+#define W4A8_DW16 2
 #endif
     const bool g4 = (a.K / kGroup) % 4 == 0;
 #define W4A8_SKINNY(NT, DW)                                                              \
     switch (epilogue) {                                                                  \
     case EPI_F32:                                                                        \
-        return g4 ? launch_one<NT, EPI_F32, DW, false, DW % 4 == 0>(a, s)                 \
+        return g4 ? launch_one<NT, EPI_F32, DW, false, 4 % DW == 0>(a, s)                 \
                   : launch_one<NT, EPI_F32, DW, false, false>(a, s);                      \
     case EPI_BF16:                                                                       \
-        return g4 ? launch_one<NT, EPI_BF16, DW, false, DW % 4 == 0>(a, s)                \
+        return g4 ? launch_one<NT, EPI_BF16, DW, false, 4 % DW == 0>(a, s)                \
                   : launch_one<NT, EPI_BF16, DW, false, false>(a, s);                     \
     default:                                                                             \
-        return g4 ? launch_one<NT, EPI_SWIGLU_Q, DW, true, DW % 4 == 0>(a, s)             \
+        return g4 ? launch_one<NT, EPI_SWIGLU_Q, DW, true, 4 % DW == 0>(a, s)             \
                   : launch_one<NT, EPI_SWIGLU_Q, DW, true, false>(a, s);                  \
     }
     if (block_m <= 16) {

@@ -118,16 +118,6 @@ __device__ __forceinline__ int b_slot(int wrow, int chunk)
     return wrow * 4 + (chunk ^ ((wrow >> 1) & 3));
 }
 
-// two fp8 dwords (4 + 4 codes) -> 8 exact halves, in dword order
-__device__ __forceinline__ v8h fp8x8_to_f16(uint32_t d0, uint32_t d1)
-{
-    const v2h h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d0, 1.0f, false);
-    const v2h h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d0, 1.0f, true);
-    const v2h h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d1, 1.0f, false);
-    const v2h h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d1, 1.0f, true);
-    return v8h{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
-}
-
 }  // namespace
 
 // One tile: rows [row0, row0 + 128) of m-block L's expert x weight block nb.

@@ -10,9 +10,8 @@ namespace w4a8 {
 
 // ---- activation quantisation (quant.hip) ----
 // mode 0: canonical codes + fp32 scales (the public export)
-// mode 1: K-interleaved codes + {c1, c0} side data (fp8 GEMM operand)
-// mode 2: codes ordered k0,k4,k1,k5,k2,k6,k3,k7 per 8-group + {scale, 0}
-//         (f16 GEMM operand, converted to f16 in registers)
+// mode 1: K-interleaved codes + {c1, c0} side data (the GEMM operand of
+//         every path, converted to f16 in registers by the gate_up GEMMs)
 hipError_t launch_quant_bf16(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
                              float* scales, float2* side, int mode, hipStream_t s);
 // canonical codes + scales (from w4a8_quantize_act) -> interleaved codes + side data
@@ -34,6 +33,12 @@ int64_t align_chunk_count(int64_t F);
 size_t align_workspace_bytes(int64_t F, int64_t E);
 hipError_t launch_align(const int32_t* ids, int64_t T, int64_t topk, int64_t expert_begin,
                         int64_t E, int64_t block_m, const AlignOut& o, void* ws, hipStream_t s);
+// align (single chunk: align_chunk_count(T*topk) == 1) and the mode-1
+// quantisation of x [T, H] in one launch; also zeroes clear[0, nclear)
+hipError_t launch_align_quant(const int32_t* ids, int64_t T, int64_t topk, int64_t expert_begin,
+                              int64_t E, int64_t block_m, const AlignOut& o, int32_t* clear,
+                              int32_t nclear, const uint16_t* x, int64_t H, uint8_t* q,
+                              float2* side, hipStream_t s);
 
 // ---- grouped GEMMs (gemm_skinny.hip) ----
 struct GemmArgs {
@@ -73,8 +78,7 @@ enum Epilogue { EPI_F32 = 0, EPI_BF16 = 1, EPI_SWIGLU_Q = 2 };
 hipError_t launch_gemm_skinny(const GemmArgs& a, int epilogue, int block_m, hipStream_t s);
 
 // ---- grouped GEMM for many rows per expert (gemm_tile.hip) ----
-// m-blocks of kTileRows rows; activation operand in the fp8 layout (quant
-// mode 1) for both modes.
+// m-blocks of kTileRows rows.
 constexpr int kTileRows = 128;
 enum TileMode { TILE_DOWN = 0, TILE_GATEUP = 1 };
 hipError_t launch_gemm_tile(const GemmArgs& a, int mode, hipStream_t s);
