@@ -3,8 +3,9 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 
-A step is one w4a8_fused_moe call (align -> quant -> gate_up + SwiGLU +
-requant -> down -> combine) on the decode workload: T=64 tokens, H=7168,
+A step is one fused-MoE call (align -> quant -> gate_up + SwiGLU + requant ->
+down -> combine; w4a8_fused_moe_prepacked on weights re-laid out once before
+timing, or w4a8_fused_moe with --layout canonical) on the decode workload: T=64 tokens, H=7168,
 I=2048, top-8 of 256 experts, this GPU's share = experts 0..31.  Inputs are
 seeded synthetic data already resident in HBM; successive steps rotate over
 distinct weight sets (>= 1 GB in total, so the weights stream from HBM rather
@@ -67,7 +68,7 @@ def moe_flops(cfg, stats):
 
 
 class Workload:
-    def __init__(self, name, nsets, dev):
+    def __init__(self, name, nsets, dev, prepack=True):
         import torch
         from w4a8_moe_grouped_amd import lib, synth
         self.cfg = cfg = synth.CONFIGS[name]
@@ -81,6 +82,11 @@ class Workload:
         for s in range(nsets):
             w13, s13, w2, s2 = synth.gen_expert_weights(cfg, seed=cfg.seed + s)
             self.sets.append(tuple(put(a) for a in (w13, s13, w2, s2)))
+        # the load-time re-layout of the weights (w4a8_prepack_weights), done
+        # once here, outside every timed region
+        self.psets = [lib.prepack_weights(w13, s13) + lib.prepack_weights(w2, s2)
+                      for (w13, s13, w2, s2) in self.sets] if prepack else None
+        self.use_packed = prepack
         self.out = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device=dev)
         nbytes = lib.fused_moe_workspace_bytes(cfg.T, cfg.H, cfg.topk, cfg.E_local, cfg.I)
         self.ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
@@ -90,9 +96,11 @@ class Workload:
     def step(self, i):
         from w4a8_moe_grouped_amd import lib
         cfg = self.cfg
-        w13, s13, w2, s2 = self.sets[i % len(self.sets)]
+        j = i % len(self.sets)
+        w13, s13, w2, s2 = self.sets[j]
         lib.fused_moe(self.hidden, self.ids, self.w, cfg.expert_begin, cfg.E_local, w13, s13,
-                      w2, s2, out=self.out, workspace=self.ws)
+                      w2, s2, out=self.out, workspace=self.ws,
+                      prepacked=self.psets[j] if self.use_packed else None)
 
 
 def time_steps(wl, steps, warmup, span=None):
@@ -200,6 +208,8 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default=None, help="time just this workload (decode/prefill/...)")
+    ap.add_argument("--layout", choices=("prepacked", "canonical"), default="prepacked",
+                    help="weight layout the timed calls read (prepacked once before timing)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a 1 GiB device copy (scales the HBM byte counters)")
     args = ap.parse_args()
@@ -221,9 +231,15 @@ def main():
     lib.load()
 
     primary = args.only or "decode"
-    wl = Workload(primary, nsets=2, dev=dev)
+    packed = args.layout == "prepacked"
+    wl = Workload(primary, nsets=2, dev=dev, prepack=packed)
     cfg, st = wl.cfg, wl.stats
     us = time_steps(wl, args.steps, args.warmup)
+    other_us = None
+    if packed:  # the same calls on the canonical [E, N, K/2] weights, for comparison
+        wl.use_packed = False
+        other_us = time_steps(wl, args.steps, args.warmup)
+        wl.use_packed = True
     # The dominant kernel of the decode step is gate_up (stage hook events
     # 2 -> 3).  Recording events costs GPU time of its own (a few µs each on
     # this stack), so its launches are timed in a second pass of the same
@@ -233,7 +249,10 @@ def main():
     _, dom_us = time_steps(wl, args.steps, 0, span=span)
     span.close()
     stages = stage_breakdown(wl, max(5, min(args.steps, 20)))
-    log("[bench] %s: %.1f us/call, stages %s" % (primary, us, {k: round(v, 1) for k, v in stages.items()}))
+    log("[bench] %s: %.1f us/call (%s weights), stages %s"
+        % (primary, us, args.layout, {k: round(v, 1) for k, v in stages.items()}))
+    if other_us is not None:
+        log("[bench] %s: %.1f us/call on the canonical weight layout" % (primary, other_us))
     byts, flops = moe_bytes(cfg, st), moe_flops(cfg, st)
     gb_s = byts / (us * 1e-6) / 1e9
     tflops = flops / (us * 1e-6) / 1e12
@@ -257,7 +276,9 @@ def main():
         "data": "synthetic (seeded; random int4 weights, N(0,1) activations and router logits)",
         "config": {"workload": "%s: %s" % (primary, cfg.desc), "T": cfg.T, "H": cfg.H, "I": cfg.I,
                    "experts_total": cfg.E_total, "experts_local": cfg.E_local, "topk": cfg.topk,
-                   "local_pairs": st["P"], "active_experts": st["A"], "weight_sets": 2},
+                   "local_pairs": st["P"], "active_experts": st["A"], "weight_sets": 2,
+                   "weight_layout": args.layout},
+        "canonical_layout_us": None if other_us is None else round(other_us, 2),
         "tflops": round(tflops, 2),
         "hbm_gbs": round(gb_s, 1),
         "roofline_frac_call": round(gb_s / HBM_PEAK_GBS, 4),
@@ -271,7 +292,7 @@ def main():
     if not args.no_prefill and args.only is None:
         pre = {}
         for name, steps, warm in (("prefill", 10, 3), ("prefill_ep8", 3, 1)):
-            p = Workload(name, nsets=1, dev=dev)
+            p = Workload(name, nsets=1, dev=dev, prepack=packed)
             pu = time_steps(p, steps, warm)
             pst = stage_breakdown(p, 2)
             pfl = moe_flops(p.cfg, p.stats)

@@ -167,6 +167,46 @@ int w4a8_fused_moe(const void* hidden_bf16, int64_t T, int64_t H,
                    hipStream_t stream);
 
 /*
+ * w4a8_prepack_weights -- one-time re-layout of int4 weights and their
+ * scales for w4a8_fused_moe_prepacked (the load-time weight processing of
+ * SGLang PR #7762, "W4AFp8MoEMethod": process_weights_after_loading; the
+ * layout is this library's own).  Pure data movement, asynchronous.
+ *   w_int4    [E, N, K/2] packed int4 (canonical layout, see above)
+ *   w_scales  [E, N, K/128] fp32
+ *   w_packed  E*N*K/2 bytes: [E][N/16][K/128][16][64]: the 64 bytes of row n
+ *             for K-group g at ((n/16 * (K/128) + g) * 16 + n%16) * 64
+ *             within the expert's E-slice of N*K/2 bytes
+ *   s_packed  w4a8_prepacked_scale_count(E, N, K) floats:
+ *             [E][N/16][G4][16][4], G4 = ceil(K/512): the scale of row n,
+ *             group g at ((n/16 * G4 + g/4) * 16 + n%16) * 4 + g%4 within the
+ *             expert's slice of N*G4*4 floats; zero past the last group
+ * N % 16 == 0, K % 128 == 0; outputs must not alias the inputs.  Errors:
+ * INVALID_ARG (null, non-positive sizes, in place), UNSUPPORTED (shape or
+ * alignment), HIP.
+ */
+int w4a8_prepack_weights(const uint8_t* w_int4, const float* w_scales, int64_t E, int64_t N,
+                         int64_t K, uint8_t* w_packed, float* s_packed, hipStream_t stream);
+
+/* Floats of the prepacked scales of E experts of N x K (host-only; -1 for a
+ * bad shape). */
+int64_t w4a8_prepacked_scale_count(int64_t E, int64_t N, int64_t K);
+
+/*
+ * w4a8_fused_moe_prepacked -- w4a8_fused_moe on weights prepacked by
+ * w4a8_prepack_weights (w13: N = 2I, K = H; w2: N = H, K = I).  Same
+ * arguments, results, workspace and errors as w4a8_fused_moe.  Each 16-row x
+ * 128-K weight block is one contiguous kilobyte, which the GEMM kernels
+ * stream with one load per wave.
+ */
+int w4a8_fused_moe_prepacked(const void* hidden_bf16, int64_t T, int64_t H,
+                             const int32_t* topk_ids, const float* topk_weights, int64_t topk,
+                             int64_t expert_begin, int64_t num_local_experts, int64_t I,
+                             const uint8_t* w13_packed, const float* w13_scales_packed,
+                             const uint8_t* w2_packed, const float* w2_scales_packed,
+                             void* out_bf16, void* workspace, size_t* workspace_bytes,
+                             hipStream_t stream);
+
+/*
  * w4a8_fused_moe_workspace_layout -- where w4a8_fused_moe keeps its
  * intermediates inside the workspace (host-only query, no HIP call), so that
  * tests and tools can read them after a call:

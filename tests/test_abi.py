@@ -117,3 +117,41 @@ def test_align_rejects_bad_arguments(L):
     assert args(bm=0) == INVALID
     assert args(ids=None) == INVALID
     assert args(be=None) == INVALID  # block_expert and block_row must both be given or both null
+
+
+def test_prepack_rejects_bad_arguments(L):
+    p = L.w4a8_prepack_weights
+    other = ctypes.c_void_p(0x2000)
+    args = lambda E=2, N=32, K=256, w=BOGUS, s=BOGUS, wp=other, sp=other: p(w, s, E, N, K, wp, sp, None)
+    assert args(E=0) == INVALID
+    assert args(N=0) == INVALID
+    assert args(K=-128) == INVALID
+    assert args(w=None) == INVALID
+    assert args(sp=None) == INVALID
+    assert args(N=24) == UNSUPPORTED        # N % 16
+    assert args(K=192) == UNSUPPORTED       # K % 128
+    assert args(w=MISALIGNED) == UNSUPPORTED
+    assert args(sp=MISALIGNED) == UNSUPPORTED
+    assert args(wp=BOGUS) == INVALID        # in place
+
+
+def test_prepacked_scale_count(L):
+    c = L.w4a8_prepacked_scale_count
+    # groups are padded to a multiple of 4 per row
+    assert c(1, 16, 128) == 16 * 4
+    assert c(3, 32, 512) == 3 * 32 * 4
+    assert c(2, 48, 640) == 2 * 48 * 8      # 5 groups -> 8
+    assert c(256, 4096, 7168) == 256 * 4096 * 56
+    assert c(0, 16, 128) == -1
+    assert c(1, 16, 100) == -1
+
+
+def test_fused_moe_prepacked_rejects_bad_arguments(L):
+    n = ctypes.c_size_t(1 << 40)
+    f = lambda H=256, I=128, w13=BOGUS, nbytes=n: L.w4a8_fused_moe_prepacked(
+        BOGUS, 4, H, BOGUS, BOGUS, 2, 0, 4, I, w13, BOGUS, BOGUS, BOGUS, BOGUS, BOGUS,
+        ctypes.byref(nbytes), None)
+    assert f(H=200) == UNSUPPORTED
+    assert f(I=100) == UNSUPPORTED
+    assert f(w13=None) == INVALID
+    assert f(nbytes=ctypes.c_size_t(16)) == WORKSPACE

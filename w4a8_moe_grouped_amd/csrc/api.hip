@@ -260,11 +260,16 @@ int w4a8_moe_align(const int32_t* topk_ids, int64_t T, int64_t topk, int64_t exp
                                          block_m, o, workspace, stream));
 }
 
-int w4a8_fused_moe(const void* hidden_bf16, int64_t T, int64_t H, const int32_t* topk_ids,
+}  // extern "C"
+
+namespace {
+
+int fused_moe_impl(const void* hidden_bf16, int64_t T, int64_t H, const int32_t* topk_ids,
                    const float* topk_weights, int64_t topk, int64_t expert_begin,
                    int64_t num_local_experts, int64_t I, const uint8_t* w13_int4,
                    const float* w13_scales, const uint8_t* w2_int4, const float* w2_scales,
-                   void* out_bf16, void* workspace, size_t* workspace_bytes, hipStream_t stream)
+                   void* out_bf16, void* workspace, size_t* workspace_bytes, hipStream_t stream,
+                   bool packed)
 {
     const int64_t E = num_local_experts;
     if (T < 0 || H <= 0 || I <= 0 || topk < 1 || E < 1)
@@ -332,10 +337,11 @@ int w4a8_fused_moe(const void* hidden_bf16, int64_t T, int64_t H, const int32_t*
     g.act_side = p.qa_side;
     g.sorted = p.al.sorted;
     g.topk = (int32_t)topk;
+    g.packed = packed ? 1 : 0;
     g.w = w13_int4;
     g.ws = w13_scales;
     g.w_estride = 2 * I * (H / 2);
-    g.s_estride = 2 * I * (H / W4A8_GROUP);
+    g.s_estride = 2 * I * (packed ? 4 * ceil_div(H / W4A8_GROUP, 4) : H / W4A8_GROUP);
     g.K = H;
     g.N = 2 * I;
     g.I = I;
@@ -355,7 +361,7 @@ int w4a8_fused_moe(const void* hidden_bf16, int64_t T, int64_t H, const int32_t*
     g.w = w2_int4;
     g.ws = w2_scales;
     g.w_estride = H * (I / 2);
-    g.s_estride = H * (I / W4A8_GROUP);
+    g.s_estride = H * (packed ? 4 * ceil_div(I / W4A8_GROUP, 4) : I / W4A8_GROUP);
     g.K = I;
     g.N = H;
     g.out_f32 = p.y2;
@@ -370,6 +376,57 @@ int w4a8_fused_moe(const void* hidden_bf16, int64_t T, int64_t H, const int32_t*
         return W4A8_ERR_HIP;
     mark(ev, 5, stream);
     return W4A8_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int w4a8_fused_moe(const void* hidden_bf16, int64_t T, int64_t H, const int32_t* topk_ids,
+                   const float* topk_weights, int64_t topk, int64_t expert_begin,
+                   int64_t num_local_experts, int64_t I, const uint8_t* w13_int4,
+                   const float* w13_scales, const uint8_t* w2_int4, const float* w2_scales,
+                   void* out_bf16, void* workspace, size_t* workspace_bytes, hipStream_t stream)
+{
+    return fused_moe_impl(hidden_bf16, T, H, topk_ids, topk_weights, topk, expert_begin,
+                          num_local_experts, I, w13_int4, w13_scales, w2_int4, w2_scales, out_bf16,
+                          workspace, workspace_bytes, stream, false);
+}
+
+int w4a8_fused_moe_prepacked(const void* hidden_bf16, int64_t T, int64_t H,
+                             const int32_t* topk_ids, const float* topk_weights, int64_t topk,
+                             int64_t expert_begin, int64_t num_local_experts, int64_t I,
+                             const uint8_t* w13_packed, const float* w13_scales_packed,
+                             const uint8_t* w2_packed, const float* w2_scales_packed,
+                             void* out_bf16, void* workspace, size_t* workspace_bytes,
+                             hipStream_t stream)
+{
+    return fused_moe_impl(hidden_bf16, T, H, topk_ids, topk_weights, topk, expert_begin,
+                          num_local_experts, I, w13_packed, w13_scales_packed, w2_packed,
+                          w2_scales_packed, out_bf16, workspace, workspace_bytes, stream, true);
+}
+
+int w4a8_prepack_weights(const uint8_t* w_int4, const float* w_scales, int64_t E, int64_t N,
+                         int64_t K, uint8_t* w_packed, float* s_packed, hipStream_t stream)
+{
+    if (E < 1 || N <= 0 || K <= 0)
+        return W4A8_ERR_INVALID_ARG;
+    if (w_int4 == nullptr || w_scales == nullptr || w_packed == nullptr || s_packed == nullptr)
+        return W4A8_ERR_INVALID_ARG;
+    if (N % 16 != 0 || K % W4A8_GROUP != 0)
+        return W4A8_ERR_UNSUPPORTED;
+    if (!aligned16(w_int4) || !aligned16(w_packed) || !aligned16(w_scales) || !aligned16(s_packed))
+        return W4A8_ERR_UNSUPPORTED;
+    if ((const void*)w_int4 == (const void*)w_packed || (const void*)w_scales == (const void*)s_packed)
+        return W4A8_ERR_INVALID_ARG;  // not in place
+    return hip_status(w4a8::launch_prepack(w_int4, w_scales, E, N, K, w_packed, s_packed, stream));
+}
+
+int64_t w4a8_prepacked_scale_count(int64_t E, int64_t N, int64_t K)
+{
+    if (E < 1 || N <= 0 || K <= 0 || K % W4A8_GROUP != 0)
+        return -1;
+    return E * N * 4 * ceil_div(K / W4A8_GROUP, 4);
 }
 
 int w4a8_fused_moe_workspace_layout(int64_t T, int64_t H, int64_t topk,

@@ -53,6 +53,18 @@ typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 
 constexpr int kGroup = 128;
 
+// Prepacked weights (w4a8_prepack_weights): 16-row fragments, and inside a
+// fragment one 1 KB block per 128-K group, so that the 64 lanes of one load
+// read 1 KB contiguous.  Packed bytes of row n, group g at
+//   ((n/16 * G + g) * 16 + n%16) * 64.
+// Scales: blocks of 4 groups, 16 bytes per row, zero past the last group:
+// the scale of row n, group g at float index
+//   ((n/16 * G4 + g/4) * 16 + n%16) * 4 + g%4,   G4 = ceil(G/4).
+__host__ __device__ constexpr int64_t packed_groups4(int64_t G)
+{
+    return (G + 3) / 4;
+}
+
 // byte offset of 8-group b (k = 8b..8b+7) inside a 128-byte fp8 activation group
 __host__ __device__ constexpr int fp8_group_pos(int b)
 {

@@ -32,7 +32,7 @@ constexpr int kNF = 4;  // weight fragments (16 rows) per wave
 
 constexpr int kWaves = 4;
 
-template <int NT, int EPI, int DW, bool F16, bool SW4>
+template <int NT, int EPI, int DW, bool F16, bool SW4, bool PK>
 __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs a)
 {
     constexpr int BM = 16 * NT;
@@ -84,13 +84,19 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs a)
     // activation operand is fp8 on both paths (one byte per element); the
     // lane's two 16-byte chunks of a group are q and 4+q (fp8_group_pos).
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.w + (int64_t)e * a.w_estride, (uint32_t)(N * (K / 2)));
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.ws + (int64_t)e * a.s_estride, (uint32_t)(N * G * 4));
+    const int64_t PG4 = packed_groups4(G);  // 4-group scale blocks per row (prepacked)
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(a.ws + (int64_t)e * a.s_estride, (uint32_t)(PK ? N * PG4 * 16 : N * G * 4));
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.act, (uint32_t)(a.act_rows * K));
     uint32_t vw[kNF], vs[kNF], va[NT];
 #pragma unroll
     for (int f = 0; f < kNF; ++f) {
-        vw[f] = (uint32_t)(nrow[f] * (K / 2) + 16 * q);
-        vs[f] = (uint32_t)(nrow[f] * G * 4);
+        // (prepacked: the rows of a fragment are 16-aligned, nrow % 16 == c16
+        // except for clamped rows, which read a valid row of no consequence)
+        vw[f] = PK ? (uint32_t)(((nrow[f] >> 4) * G * 16 + (nrow[f] & 15)) * 64 + 16 * q)
+                   : (uint32_t)(nrow[f] * (K / 2) + 16 * q);
+        vs[f] = PK ? (uint32_t)(((nrow[f] >> 4) * PG4 * 16 + (nrow[f] & 15)) * 16)
+                   : (uint32_t)(nrow[f] * G * 4);
     }
 #pragma unroll
     for (int t = 0; t < NT; ++t)
@@ -155,9 +161,10 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs a)
     auto load_group = [&](int s, int g) {
 #pragma unroll
         for (int f = 0; f < kNF; ++f) {
-            wb[s][f] = bload16(rw, vw[f], (uint32_t)g * 64u);
+            wb[s][f] = bload16(rw, vw[f], (uint32_t)g * (PK ? 1024u : 64u));
             if (!SW4)
-                sb[s][f] = bload4f(rs, vs[f], (uint32_t)g * 4u);
+                sb[s][f] = bload4f(rs, vs[f], PK ? (uint32_t)(g >> 2) * 256u + (uint32_t)(g & 3) * 4u
+                                                  : (uint32_t)g * 4u);
         }
 #pragma unroll
         for (int t = 0; t < NT; ++t)
@@ -169,7 +176,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs a)
         if (SW4) {
 #pragma unroll
             for (int f = 0; f < kNF; ++f)
-                dst[f] = __builtin_bit_cast(float4, bload16(rs, vs[f], (uint32_t)blk * 16u));
+                dst[f] = __builtin_bit_cast(float4, bload16(rs, vs[f], (uint32_t)blk * (PK ? 256u : 16u)));
         }
     };
     __builtin_amdgcn_sched_barrier(0);
@@ -391,7 +398,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs a)
     }
 }
 
-template <int NT, int EPI, int DW, bool F16, bool SW4>
+template <int NT, int EPI, int DW, bool F16, bool SW4, bool PK>
 static hipError_t launch_one(const GemmArgs& a, hipStream_t s)
 {
     const int64_t G = a.K / kGroup;
@@ -405,38 +412,44 @@ static hipError_t launch_one(const GemmArgs& a, hipStream_t s)
     grid.z = 1;
     if (grid.x == 0 || grid.y == 0)
         return hipSuccess;
-    hipLaunchKernelGGL((gemm_skinny_kernel<NT, EPI, DW, F16, SW4>), grid, dim3(256), lds, s, a);
+    hipLaunchKernelGGL((gemm_skinny_kernel<NT, EPI, DW, F16, SW4, PK>), grid, dim3(256), lds, s, a);
     return hipGetLastError();
+}
+
+// gate_up (SwiGLU epilogue) runs on the exact f16 path, the others on fp8;
+// ring depth per m-block height
+#ifndef W4A8_DW16
+#define W4A8_DW16 2
+#endif
+template <int NT, int DW, bool PK>
+static hipError_t launch_nt(const GemmArgs& a, int epilogue, hipStream_t s)
+{
+    const bool g4 = (a.K / kGroup) % 4 == 0;
+    switch (epilogue) {
+    case EPI_F32:
+        return g4 ? launch_one<NT, EPI_F32, DW, false, 4 % DW == 0, PK>(a, s)
+                  : launch_one<NT, EPI_F32, DW, false, false, PK>(a, s);
+    case EPI_BF16:
+        if constexpr (PK) {
+            return hipErrorInvalidValue;  // the dense GEMM takes canonical weights only
+        } else {
+            return g4 ? launch_one<NT, EPI_BF16, DW, false, 4 % DW == 0, false>(a, s)
+                      : launch_one<NT, EPI_BF16, DW, false, false, false>(a, s);
+        }
+    default:
+        return g4 ? launch_one<NT, EPI_SWIGLU_Q, DW, true, 4 % DW == 0, PK>(a, s)
+                  : launch_one<NT, EPI_SWIGLU_Q, DW, true, false, PK>(a, s);
+    }
 }
 
 hipError_t launch_gemm_skinny(const GemmArgs& a, int epilogue, int block_m, hipStream_t s)
 {
-    // gate_up (SwiGLU epilogue) runs on the exact f16 path, the others on fp8;
-    // ring depth per m-block height
-#ifndef W4A8_DW16
-#define W4A8_DW16 2
-#endif
-    const bool g4 = (a.K / kGroup) % 4 == 0;
-#define W4A8_SKINNY(NT, DW)                                                              \
-    switch (epilogue) {                                                                  \
-    case EPI_F32:                                                                        \
-        return g4 ? launch_one<NT, EPI_F32, DW, false, 4 % DW == 0>(a, s)                 \
-                  : launch_one<NT, EPI_F32, DW, false, false>(a, s);                      \
-    case EPI_BF16:                                                                       \
-        return g4 ? launch_one<NT, EPI_BF16, DW, false, 4 % DW == 0>(a, s)                \
-                  : launch_one<NT, EPI_BF16, DW, false, false>(a, s);                     \
-    default:                                                                             \
-        return g4 ? launch_one<NT, EPI_SWIGLU_Q, DW, true, 4 % DW == 0>(a, s)             \
-                  : launch_one<NT, EPI_SWIGLU_Q, DW, true, false>(a, s);                  \
-    }
-    if (block_m <= 16) {
-        W4A8_SKINNY(1, W4A8_DW16)
-    } else if (block_m <= 32) {
-        W4A8_SKINNY(2, 3)
-    } else {
-        W4A8_SKINNY(4, 2)
-    }
-#undef W4A8_SKINNY
+    if (block_m <= 16)
+        return a.packed ? launch_nt<1, W4A8_DW16, true>(a, epilogue, s)
+                        : launch_nt<1, W4A8_DW16, false>(a, epilogue, s);
+    if (block_m <= 32)
+        return a.packed ? launch_nt<2, 3, true>(a, epilogue, s) : launch_nt<2, 3, false>(a, epilogue, s);
+    return a.packed ? launch_nt<4, 2, true>(a, epilogue, s) : launch_nt<4, 2, false>(a, epilogue, s);
 }
 
 } // namespace w4a8

@@ -121,7 +121,7 @@ __device__ __forceinline__ int b_slot(int wrow, int chunk)
 }  // namespace
 
 // One tile: rows [row0, row0 + 128) of m-block L's expert x weight block nb.
-template <int MODE, bool F64>
+template <int MODE, bool F64, bool PK>
 __device__ __forceinline__ void tile_body(const GemmArgs& a, const int L, uint8_t* smem, int* s_expert_p)
 {
     int& s_expert = *s_expert_p;
@@ -175,7 +175,8 @@ __device__ __forceinline__ void tile_body(const GemmArgs& a, const int L, uint8_
     const v4i ra = sgpr_rsrc(a.act, (uint32_t)(a.act_rows * K));
     const v4i rsd = sgpr_rsrc(a.act_side, (uint32_t)(a.act_rows * G * 8));
     const v4i rw = sgpr_rsrc(a.w + (int64_t)e * a.w_estride, (uint32_t)(N * (K / 2)));
-    const v4i rws = sgpr_rsrc(a.ws + (int64_t)e * a.s_estride, (uint32_t)(N * G * 4));
+    const int64_t G4 = packed_groups4(G);
+    const v4i rws = sgpr_rsrc(a.ws + (int64_t)e * a.s_estride, (uint32_t)(PK ? N * G4 * 16 : N * G * 4));
     uint32_t va[2], vb[2], vx;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -183,25 +184,30 @@ __device__ __forceinline__ void tile_body(const GemmArgs& a, const int L, uint8_
         const int r = s >> 3, ca = (s & 7) ^ (r & 7);
         va[j] = (uint32_t)((int64_t)act_row(r) * K + 16 * ca);
         const int wr = s >> 2, cb = (s & 3) ^ ((wr >> 1) & 3);
-        vb[j] = (uint32_t)(weight_row(wr) * (K / 2) + 16 * cb);
+        const int64_t n = weight_row(wr);
+        vb[j] = PK ? (uint32_t)(((n >> 4) * G * 16 + (n & 15)) * 64 + 16 * cb)
+                   : (uint32_t)(n * (K / 2) + 16 * cb);
     }
     if (wave < 4) {  // side data: dword d = 2 * row + component
         const int d = wave * 64 + lane;
         vx = (uint32_t)(((int64_t)act_row(d >> 1) * G) * 8 + 4 * (d & 1));
     } else {  // weight scales: one per weight row
-        vx = (uint32_t)(weight_row((wave - 4) * 64 + lane) * G * 4);
+        const int64_t n = weight_row((wave - 4) * 64 + lane);
+        vx = PK ? (uint32_t)(((n >> 4) * G4 * 16 + (n & 15)) * 16) : (uint32_t)(n * G * 4);
     }
     const uint32_t smem_lds = (uint32_t)(uintptr_t)(lds_ptr_t)smem;
     auto issue = [&](int g, int st) {
         const uint32_t base = smem_lds + (uint32_t)(st * kStageBytes);
         lds_load16(ra, base + kAOff + (2 * wave) * 1024, va[0], (uint32_t)g * kGroup);
         lds_load16(ra, base + kAOff + (2 * wave + 1) * 1024, va[1], (uint32_t)g * kGroup);
-        lds_load16(rw, base + kBOff + (2 * wave) * 1024, vb[0], (uint32_t)g * 64u);
-        lds_load16(rw, base + kBOff + (2 * wave + 1) * 1024, vb[1], (uint32_t)g * 64u);
+        const uint32_t gw = (uint32_t)g * (PK ? 1024u : 64u);
+        lds_load16(rw, base + kBOff + (2 * wave) * 1024, vb[0], gw);
+        lds_load16(rw, base + kBOff + (2 * wave + 1) * 1024, vb[1], gw);
         if (wave < 4)
             lds_load4(rsd, base + kSideOff + wave * 256, vx, (uint32_t)g * 8u);
         else
-            lds_load4(rws, base + kSwOff + (wave - 4) * 256, vx, (uint32_t)g * 4u);
+            lds_load4(rws, base + kSwOff + (wave - 4) * 256, vx,
+                      PK ? (uint32_t)(g >> 2) * 256u + (uint32_t)(g & 3) * 4u : (uint32_t)g * 4u);
     };
 
     // weight rows of this lane's fragments (tile-local)
@@ -432,7 +438,7 @@ __device__ __forceinline__ void tile_body(const GemmArgs& a, const int L, uint8_
 }
 
 // Persistent: each workgroup walks the tiles of its XCD's range.
-template <int MODE, bool F64>
+template <int MODE, bool F64, bool PK>
 __global__ __launch_bounds__(kTThreads) void gemm_tile_kernel(GemmArgs a)
 {
     __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
@@ -446,7 +452,7 @@ __global__ __launch_bounds__(kTThreads) void gemm_tile_kernel(GemmArgs a)
         const int L = x * per_xcd + t;
         if (L >= total)
             break;
-        tile_body<MODE, F64>(a, L, smem, &s_expert);
+        tile_body<MODE, F64, PK>(a, L, smem, &s_expert);
         __syncthreads();  // the next tile's loads overwrite LDS the epilogue may still read
     }
 }
@@ -467,10 +473,19 @@ hipError_t launch_gemm_tile(const GemmArgs& a, int mode, hipStream_t s)
 #ifndef W4A8_TILE_F64
 #define W4A8_TILE_F64 0
 #endif
-    if (mode == TILE_GATEUP)
-        hipLaunchKernelGGL((gemm_tile_kernel<TILE_GATEUP, W4A8_TILE_F64 != 0>), grid, dim3(kTThreads), 0, s, a);
-    else
-        hipLaunchKernelGGL((gemm_tile_kernel<TILE_DOWN, false>), grid, dim3(kTThreads), 0, s, a);
+    if (mode == TILE_GATEUP) {
+        if (a.packed)
+            hipLaunchKernelGGL((gemm_tile_kernel<TILE_GATEUP, W4A8_TILE_F64 != 0, true>), grid,
+                               dim3(kTThreads), 0, s, a);
+        else
+            hipLaunchKernelGGL((gemm_tile_kernel<TILE_GATEUP, W4A8_TILE_F64 != 0, false>), grid,
+                               dim3(kTThreads), 0, s, a);
+    } else {
+        if (a.packed)
+            hipLaunchKernelGGL((gemm_tile_kernel<TILE_DOWN, false, true>), grid, dim3(kTThreads), 0, s, a);
+        else
+            hipLaunchKernelGGL((gemm_tile_kernel<TILE_DOWN, false, false>), grid, dim3(kTThreads), 0, s, a);
+    }
     return hipGetLastError();
 }
 

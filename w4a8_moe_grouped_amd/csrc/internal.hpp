@@ -60,7 +60,9 @@ struct GemmArgs {
     const int32_t* block_start;  // [E+1] first m-block of each expert (tile GEMM)
     int32_t num_experts;
     int32_t dense_rows;      // used when offsets == null: rows [0, dense_rows)
-    // weights of expert e: w + e*w_estride, scales ws + e*s_estride; row n at n*K/2, n*K/128
+    // weights of expert e: w + e*w_estride, scales ws + e*s_estride; row n at
+    // n*K/2, n*K/128, or in the prepacked layout if packed (see common.hpp)
+    int packed;
     const uint8_t* w;
     const float* ws;
     int64_t w_estride, s_estride;
@@ -82,6 +84,11 @@ hipError_t launch_gemm_skinny(const GemmArgs& a, int epilogue, int block_m, hipS
 constexpr int kTileRows = 128;
 enum TileMode { TILE_DOWN = 0, TILE_GATEUP = 1 };
 hipError_t launch_gemm_tile(const GemmArgs& a, int mode, hipStream_t s);
+
+// ---- weight prepack (prepack.hip) ----
+// [E, N, K/2] int4 + [E, N, K/128] fp32 -> the prepacked layouts (common.hpp)
+hipError_t launch_prepack(const uint8_t* w, const float* ws, int64_t E, int64_t N, int64_t K,
+                          uint8_t* wp, float* sp, hipStream_t s);
 
 // ---- combine (combine.hip) ----
 hipError_t launch_combine(const float* y2, const int32_t* src2dst, const float* topk_w,

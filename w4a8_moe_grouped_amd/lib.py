@@ -21,7 +21,8 @@ W4A8_OK = 0
 GROUP = 128
 EXPORTS = ("w4a8_version", "w4a8_status_string", "w4a8_quantize_act", "w4a8_gemm",
            "w4a8_moe_align", "w4a8_fused_moe", "w4a8_fused_moe_workspace_layout",
-           "w4a8_fused_moe_stage_events")
+           "w4a8_fused_moe_stage_events", "w4a8_prepack_weights", "w4a8_prepacked_scale_count",
+           "w4a8_fused_moe_prepacked")
 
 _lock = threading.Lock()
 _lib = None
@@ -56,6 +57,12 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         L.w4a8_fused_moe.restype = ctypes.c_int
         L.w4a8_fused_moe.argtypes = [vp, i64, i64, vp, vp, i64, i64, i64, i64, vp, vp, vp, vp,
                                      vp, vp, sz, vp]
+        L.w4a8_fused_moe_prepacked.restype = ctypes.c_int
+        L.w4a8_fused_moe_prepacked.argtypes = L.w4a8_fused_moe.argtypes
+        L.w4a8_prepack_weights.restype = ctypes.c_int
+        L.w4a8_prepack_weights.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp]
+        L.w4a8_prepacked_scale_count.restype = ctypes.c_int64
+        L.w4a8_prepacked_scale_count.argtypes = [i64, i64, i64]
         L.w4a8_fused_moe_workspace_layout.restype = ctypes.c_int
         L.w4a8_fused_moe_workspace_layout.argtypes = [i64, i64, i64, i64, i64,
                                                       ctypes.POINTER(ctypes.c_size_t), ctypes.c_int,
@@ -129,6 +136,24 @@ def fused_moe_workspace_layout(T: int, H: int, topk: int, num_local_experts: int
 
 
 # ---- exports ----------------------------------------------------------------------
+
+def prepack_weights(w: torch.Tensor, w_scales: torch.Tensor):
+    """int4 [E, N, K/2] + fp32 scales [E, N, K/128] -> (packed uint8 [E, N*K/2],
+    packed fp32 scales [E, count/E]) in the layout of w4a8_prepack_weights."""
+    _need_cuda(w, w_scales)
+    if w.dim() != 3 or w.dtype != torch.uint8 or not w.is_contiguous() or not w_scales.is_contiguous():
+        raise W4A8Error("w must be a contiguous uint8 [E, N, K/2] tensor")
+    E, N, K2 = w.shape
+    K = 2 * K2
+    cnt = int(load().w4a8_prepacked_scale_count(E, N, K))
+    if cnt < 0 or w_scales.shape != (E, N, K // GROUP) or w_scales.dtype != torch.float32:
+        raise W4A8Error("bad weight / scale shapes")
+    wp = torch.empty((E, N * K2), dtype=torch.uint8, device=w.device)
+    sp = torch.empty((E, cnt // E), dtype=torch.float32, device=w.device)
+    _check(load().w4a8_prepack_weights(_ptr(w), _ptr(w_scales), E, N, K, _ptr(wp), _ptr(sp),
+                                       _stream(w.device)), "w4a8_prepack_weights")
+    return wp, sp
+
 
 def quantize_act(x: torch.Tensor, out_q: Optional[torch.Tensor] = None,
                  out_scales: Optional[torch.Tensor] = None):
@@ -281,8 +306,10 @@ class SpanTimer:
 def fused_moe(hidden: torch.Tensor, topk_ids: torch.Tensor, topk_weights: torch.Tensor,
               expert_begin: int, num_local_experts: int, w13: torch.Tensor, s13: torch.Tensor,
               w2: torch.Tensor, s2: torch.Tensor, out: Optional[torch.Tensor] = None,
-              workspace: Optional[torch.Tensor] = None):
-    """The fused forward; bf16 [T, H] out."""
+              workspace: Optional[torch.Tensor] = None, prepacked: Optional[tuple] = None):
+    """The fused forward; bf16 [T, H] out.  w13/s13/w2/s2 are the canonical
+    weights (they give the shapes); with prepacked = (w13p, s13p, w2p, s2p)
+    from prepack_weights, w4a8_fused_moe_prepacked runs on those instead."""
     _need_cuda(hidden, topk_ids, topk_weights, w13, s13, w2, s2)
     T, H = hidden.shape
     k = topk_ids.shape[1]
@@ -300,9 +327,18 @@ def fused_moe(hidden: torch.Tensor, topk_ids: torch.Tensor, topk_weights: torch.
         need = fused_moe_workspace_bytes(T, H, k, E, I)
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=hidden.device)
     n = ctypes.c_size_t(workspace.numel())
-    _check(load().w4a8_fused_moe(_ptr(hidden), T, H, _ptr(topk_ids), _ptr(topk_weights), k,
-                                 expert_begin, E, I, _ptr(w13), _ptr(s13), _ptr(w2), _ptr(s2),
-                                 _ptr(out), _ptr(workspace), ctypes.byref(n),
-                                 _stream(hidden.device)),
-           "w4a8_fused_moe")
+    if prepacked is not None:
+        w13p, s13p, w2p, s2p = prepacked
+        _need_cuda(w13p, s13p, w2p, s2p)
+        assert w13p.numel() == w13.numel() and w2p.numel() == w2.numel()
+        assert s13p.numel() == load().w4a8_prepacked_scale_count(E, 2 * I, H)
+        assert s2p.numel() == load().w4a8_prepacked_scale_count(E, H, I)
+        fn, name = load().w4a8_fused_moe_prepacked, "w4a8_fused_moe_prepacked"
+        ws = (w13p, s13p, w2p, s2p)
+    else:
+        fn, name = load().w4a8_fused_moe, "w4a8_fused_moe"
+        ws = (w13, s13, w2, s2)
+    _check(fn(_ptr(hidden), T, H, _ptr(topk_ids), _ptr(topk_weights), k, expert_begin, E, I,
+              _ptr(ws[0]), _ptr(ws[1]), _ptr(ws[2]), _ptr(ws[3]), _ptr(out), _ptr(workspace),
+              ctypes.byref(n), _stream(hidden.device)), name)
     return out
