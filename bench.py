@@ -272,7 +272,7 @@ def main():
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int4 x fp8 (gate_up on exact f16 MFMA with fp64 promotion, down on fp8 MFMA)",
+        "dtype": "int4 x fp8 (gate_up operands converted exactly to f16 for the MFMA, down on fp8 MFMA; fp32 accumulation and promotion)",
         "data": "synthetic (seeded; random int4 weights, N(0,1) activations and router logits)",
         "config": {"workload": "%s: %s" % (primary, cfg.desc), "T": cfg.T, "H": cfg.H, "I": cfg.I,
                    "experts_total": cfg.E_total, "experts_local": cfg.E_local, "topk": cfg.topk,

@@ -31,10 +31,10 @@
  *    complement (-8..7), no zero point; one fp32 scale per 128 K-elements.
  *  - GEMM: y[m,n] = sum_g a_scale[m,g] * w_scale[n,g] * sum_{k in g}
  *    dec(a[m,k]) * w[n,k].  On the GPU each group's sum comes from an MFMA
- *    and is promoted with its two scales into an fp32 accumulator (fp64 in
- *    the fused forward's decode-size gate_up GEMM); the gate_up GEMM of
- *    w4a8_fused_moe runs on fp16 MFMA with exactly converted operands, whose
- *    group sums are correctly rounded, because its output is re-quantised.
+ *    and is promoted with its two scales into an fp32 accumulator; the
+ *    gate_up GEMM of w4a8_fused_moe runs on fp16 MFMA with exactly converted
+ *    operands, whose group sums are correctly rounded, because its output is
+ *    re-quantised.
  *
  * Conventions:
  *  - Every pointer is a device pointer on the current HIP device unless

@@ -7,7 +7,7 @@
 // MMA -- the swapAB idea).
 //
 // Work decomposition: a workgroup (4 waves) owns one m-block of BM = 16*NT
-// rows of one expert and 256 weight rows (4 waves x 4 fragments of 16).  The
+// rows of one expert and 64*NF weight rows (4 waves x NF fragments of 16).  The
 // rows sit on the A side of v_mfma_f32_16x16x128_f8f6f4 and the weight rows
 // on the B side, so every weight byte is loaded from HBM exactly once per
 // m-block, straight into VGPRs (16 bytes per lane, no LDS), through a ring of
@@ -24,17 +24,17 @@
 #include "common.hpp"
 #include "internal.hpp"
 
-#include <type_traits>
 
 namespace w4a8 {
 
-constexpr int kNF = 4;  // weight fragments (16 rows) per wave
-
 constexpr int kWaves = 4;
 
-template <int NT, int EPI, int DW, bool F16, bool SW4, bool PK>
+// NF: weight fragments (16 rows) per wave
+template <int NT, int EPI, int DW, bool F16, bool SW4, bool PK, int NF>
 __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs a)
 {
+    constexpr int kNF = NF;
+    static_assert(EPI != EPI_SWIGLU_Q || NF == 4, "the SwiGLU tile pairs 2 gate and 2 up fragments");
     constexpr int BM = 16 * NT;
     extern __shared__ float4 lds_side4[];  // [G][BM] float2 {c1, c0}, 16-byte aligned
     float2* lds_side = (float2*)lds_side4;
@@ -75,7 +75,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs a)
         if (EPI == EPI_SWIGLU_Q)
             n = (f >= 2 ? a.I : 0) + (int64_t)blockIdx.x * kGroup + 32 * wave + 16 * (f & 1) + c16;
         else
-            n = (int64_t)blockIdx.x * 256 + 64 * wave + 16 * f + c16;
+            n = (int64_t)blockIdx.x * (64 * NF) + 16 * NF * wave + 16 * f + c16;
         nvalid[f] = n < N;
         nrow[f] = nvalid[f] ? n : N - 1;
     }
@@ -122,13 +122,13 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs a)
         }
     }
 
-    // The f16 (gate_up) path promotes in fp64: each group's MFMA sum is the
-    // correctly rounded fp32 value of an exact dot product, and keeping the
-    // running sum in fp64 leaves y within a few 2^-24 of the exact result, so
-    // the SwiGLU + fp8 requant that follows rarely lands on another code.
-    // The fp8 path promotes in fp32.
-    using Acc = typename std::conditional<F16, double, float>::type;
-    Acc acc[kNF][NT][4];
+    // Promotion in fp32 on both paths.  On the f16 (gate_up) path each group's
+    // MFMA sum is the correctly rounded fp32 value of an exact dot product, so
+    // y carries only the fp32 roundings of the running sum, and the SwiGLU +
+    // fp8 requant that follows lands on another code than the exact result's
+    // for a few in 10^5 elements.  (An fp64 running sum removes even those,
+    // at a VALU cost this HBM-bound kernel shows in its time.)
+    float acc[kNF][NT][4];
 #pragma unroll
     for (int f = 0; f < kNF; ++f)
 #pragma unroll
@@ -260,14 +260,6 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs a)
                         for (int f = 0; f < kNF; ++f)
                             raw[f] = mfma16x16x32_f16(
                                 ah[c], fp8x8_to_f16((uint32_t)b8[f][2 * c], (uint32_t)b8[f][2 * c + 1]), raw[f]);
-#pragma unroll
-                    for (int f = 0; f < kNF; ++f) {
-                        const double swd = (double)swf[f];
-#pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            acc[f][t][r] = fma(swd, fma((double)raw[f][r], (double)c1[r], (double)c0[r]),
-                                               (double)acc[f][t][r]);
-                    }
                 } else {
                     v8i av;
 #pragma unroll
@@ -276,12 +268,12 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs a)
 #pragma unroll
                     for (int f = 0; f < kNF; ++f)
                         raw[f] = mfma16x16x128(av, unpack_int4_u(wb[s][f]), v4f{0.0f, 0.0f, 0.0f, 0.0f});
-#pragma unroll
-                    for (int f = 0; f < kNF; ++f)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            acc[f][t][r] = fmaf(swf[f], fmaf(raw[f][r], c1[r], c0[r]), (float)acc[f][t][r]);
                 }
+#pragma unroll
+                for (int f = 0; f < kNF; ++f)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        acc[f][t][r] = fmaf(swf[f], fmaf(raw[f][r], c1[r], c0[r]), acc[f][t][r]);
             }
             // keep the refill here, DW groups ahead of its use: without the
             // barrier the scheduler sinks each load next to its consumer and
@@ -311,9 +303,9 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs a)
                     if (row < rows) {
                         const int64_t o = (int64_t)(row0 + row) * N + nrow[f];
                         if (EPI == EPI_F32)
-                            a.out_f32[o] = (float)acc[f][t][r];
+                            a.out_f32[o] = acc[f][t][r];
                         else
-                            a.out_bf16[o] = f32_to_bf16((float)acc[f][t][r]);
+                            a.out_bf16[o] = f32_to_bf16(acc[f][t][r]);
                     }
                 }
         }
@@ -398,7 +390,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs a)
     }
 }
 
-template <int NT, int EPI, int DW, bool F16, bool SW4, bool PK>
+template <int NT, int EPI, int DW, bool F16, bool SW4, bool PK, int NF = 4>
 static hipError_t launch_one(const GemmArgs& a, hipStream_t s)
 {
     const int64_t G = a.K / kGroup;
@@ -407,28 +399,35 @@ static hipError_t launch_one(const GemmArgs& a, hipStream_t s)
     if (EPI == EPI_SWIGLU_Q)
         grid.x = (unsigned)(a.I / kGroup);
     else
-        grid.x = (unsigned)((a.N + 255) / 256);
+        grid.x = (unsigned)((a.N + 64 * NF - 1) / (64 * NF));
     grid.y = (unsigned)a.max_blocks;
     grid.z = 1;
     if (grid.x == 0 || grid.y == 0)
         return hipSuccess;
-    hipLaunchKernelGGL((gemm_skinny_kernel<NT, EPI, DW, F16, SW4, PK>), grid, dim3(256), lds, s, a);
+    hipLaunchKernelGGL((gemm_skinny_kernel<NT, EPI, DW, F16, SW4, PK, NF>), grid, dim3(256), lds, s, a);
     return hipGetLastError();
 }
 
 // gate_up (SwiGLU epilogue) runs on the exact f16 path, the others on fp8;
-// ring depth per m-block height
+// ring depth per m-block height.  The down GEMM of 16-row m-blocks takes
+// 128 weight rows per workgroup: its K is short, so a workgroup lives briefly,
+// and twice as many smaller ones leave less of the machine idle in the last
+// round of workgroups.
 #ifndef W4A8_DW16
-#define W4A8_DW16 2
+#define W4A8_DW16 4
+#endif
+#ifndef W4A8_DOWN_NF16
+#define W4A8_DOWN_NF16 2
 #endif
 template <int NT, int DW, bool PK>
 static hipError_t launch_nt(const GemmArgs& a, int epilogue, hipStream_t s)
 {
     const bool g4 = (a.K / kGroup) % 4 == 0;
+    constexpr int NFD = NT == 1 ? W4A8_DOWN_NF16 : 4;
     switch (epilogue) {
     case EPI_F32:
-        return g4 ? launch_one<NT, EPI_F32, DW, false, 4 % DW == 0, PK>(a, s)
-                  : launch_one<NT, EPI_F32, DW, false, false, PK>(a, s);
+        return g4 ? launch_one<NT, EPI_F32, DW, false, 4 % DW == 0, PK, NFD>(a, s)
+                  : launch_one<NT, EPI_F32, DW, false, false, PK, NFD>(a, s);
     case EPI_BF16:
         if constexpr (PK) {
             return hipErrorInvalidValue;  // the dense GEMM takes canonical weights only
