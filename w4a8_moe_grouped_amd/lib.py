@@ -218,6 +218,28 @@ def moe_align(topk_ids: torch.Tensor, expert_begin: int, num_local_experts: int,
 STAGES = ("align", "quant", "gate_up", "down", "combine")
 
 
+# Timing-only events skip the system-scope release fence (a cache writeback
+# that otherwise lands inside the measured span and inflates it by a few us).
+_HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
+
+
+def _hip_timing_api():
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                        ctypes.c_void_p]
+    hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    return hip
+
+
+def _timing_event(hip):
+    h = ctypes.c_void_p()
+    if hip.hipEventCreateWithFlags(ctypes.byref(h), _HIP_EVENT_DISABLE_SYSTEM_FENCE) != 0:
+        raise W4A8Error("hipEventCreateWithFlags failed")
+    return h
+
+
 class StageTimer:
     """HIP events around the five stages of the next fused_moe call(s).
 
@@ -225,18 +247,10 @@ class StageTimer:
     the very stream the library launches on."""
 
     def __init__(self):
-        self.hip = ctypes.CDLL("libamdhip64.so")
-        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
-        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
-                                                 ctypes.c_void_p]
-        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
-        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip = _hip_timing_api()
         self.ev = (ctypes.c_void_p * 6)()
         for i in range(6):
-            h = ctypes.c_void_p()
-            if self.hip.hipEventCreate(ctypes.byref(h)) != 0:
-                raise W4A8Error("hipEventCreate failed")
-            self.ev[i] = h
+            self.ev[i] = _timing_event(self.hip)
 
     def arm(self):
         _check(load().w4a8_fused_moe_stage_events(self.ev, 6), "w4a8_fused_moe_stage_events")
@@ -265,19 +279,9 @@ class SpanTimer:
     def __init__(self, first: int, last: int, n: int):
         if not (0 <= first < last <= 5) or n < 1:
             raise W4A8Error("bad span")
-        self.hip = ctypes.CDLL("libamdhip64.so")
-        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
-        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
-                                                 ctypes.c_void_p]
-        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
-        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip = _hip_timing_api()
         self.first, self.last, self.n = first, last, n
-        self.ev = []
-        for _ in range(2 * n):
-            h = ctypes.c_void_p()
-            if self.hip.hipEventCreate(ctypes.byref(h)) != 0:
-                raise W4A8Error("hipEventCreate failed")
-            self.ev.append(h)
+        self.ev = [_timing_event(self.hip) for _ in range(2 * n)]
         self.slots = []
         for j in range(n):
             arr = (ctypes.c_void_p * 6)()
