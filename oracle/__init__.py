@@ -74,6 +74,15 @@ def lib():
             L.orc_fused_moe.restype = ctypes.c_int
             L.orc_fused_moe.argtypes = [u16p, i64, i64, i32p, f32p, i64, i64, i64, i64,
                                         u8p, f32p, u8p, f32p, u16p, u8p, f32p, f64p]
+            L.orc_e2m1_decode.restype = ctypes.c_double
+            L.orc_e2m1_decode.argtypes = [ctypes.c_uint8]
+            L.orc_ue8m0_decode.restype = ctypes.c_double
+            L.orc_ue8m0_decode.argtypes = [ctypes.c_uint8]
+            L.orc_gemm_fp4_f64.restype = None
+            L.orc_gemm_fp4_f64.argtypes = [u8p, f32p, i64, i64, u8p, u8p, i64, f64p]
+            L.orc_fused_moe_fp4.restype = ctypes.c_int
+            L.orc_fused_moe_fp4.argtypes = [u16p, i64, i64, i32p, f32p, i64, i64, i64, i64,
+                                            u8p, u8p, u8p, u8p, u16p, u8p, f32p, f64p]
             _lib = L
     return _lib
 
@@ -98,6 +107,18 @@ def e4m3_encode(values) -> np.ndarray:
 
 def int4_value(byte: int, odd: int) -> int:
     return lib().orc_int4_value(int(byte), int(odd))
+
+
+def e2m1_decode(nibbles) -> np.ndarray:
+    L = lib()
+    c = np.asarray(nibbles, dtype=np.uint8)
+    return np.array([L.orc_e2m1_decode(int(x)) for x in c.ravel()], dtype=np.float64).reshape(c.shape)
+
+
+def ue8m0_decode(exps) -> np.ndarray:
+    L = lib()
+    c = np.asarray(exps, dtype=np.uint8)
+    return np.array([L.orc_ue8m0_decode(int(x)) for x in c.ravel()], dtype=np.float64).reshape(c.shape)
 
 
 def bf16_from_double(values) -> np.ndarray:
@@ -189,24 +210,48 @@ def gemm_bf16(a, sa, w, sw) -> np.ndarray:
     return out
 
 
+def gemm_fp4_f64(a, sa, w, sw) -> np.ndarray:
+    """codes [M, K] x fp4 e2m1 [N, K/2] with UE8M0 scales sw [N, K/32] -> fp64 [M, N]."""
+    a = _c(a, np.uint8)
+    sa = _c(sa, np.float32)
+    w = _c(w, np.uint8)
+    sw = _c(sw, np.uint8)
+    M, K = a.shape
+    N = w.shape[0]
+    assert w.shape == (N, K // 2) and sa.shape == (M, K // 128) and sw.shape == (N, K // 32)
+    y = np.empty((M, N), np.float64)
+    lib().orc_gemm_fp4_f64(_p(a, ctypes.c_uint8), _p(sa, ctypes.c_float), M, K,
+                           _p(w, ctypes.c_uint8), _p(sw, ctypes.c_uint8), N, _p(y, ctypes.c_double))
+    return y
+
+
+def fused_moe_fp4(hidden_bits, topk_ids, topk_weights, expert_begin, num_local_experts,
+                  w13, s13, w2, s2, intermediates: bool = False):
+    """The forward on fp4 weights: w13 [E, 2I, H/2] / w2 [E, H, I/2] e2m1
+    nibbles, s13 [E, 2I, H/32] / s2 [E, H, I/32] UE8M0 bytes."""
+    return fused_moe(hidden_bits, topk_ids, topk_weights, expert_begin, num_local_experts,
+                     w13, s13, w2, s2, intermediates, fp4=True)
+
+
 def fused_moe(hidden_bits, topk_ids, topk_weights, expert_begin, num_local_experts,
-              w13, s13, w2, s2, intermediates: bool = False):
+              w13, s13, w2, s2, intermediates: bool = False, fp4: bool = False):
     """The whole forward.  Returns bf16 bits [T, H]; with ``intermediates``
     also a dict of qh [P, I] codes, sh [P, I/128] scales and y2 [P, H] (fp64),
     in permuted pair order."""
     x = _c(hidden_bits, np.uint16)
     ids = _c(topk_ids, np.int32)
     tw = _c(topk_weights, np.float32)
+    sdt, sblk = (np.uint8, 32) if fp4 else (np.float32, 128)
     w13 = _c(w13, np.uint8)
-    s13 = _c(s13, np.float32)
+    s13 = _c(s13, sdt)
     w2 = _c(w2, np.uint8)
-    s2 = _c(s2, np.float32)
+    s2 = _c(s2, sdt)
     T, H = x.shape
     k = ids.shape[1]
     E = num_local_experts
     I = w2.shape[2] * 2
-    assert w13.shape == (E, 2 * I, H // 2) and s13.shape == (E, 2 * I, H // 128)
-    assert w2.shape == (E, H, I // 2) and s2.shape == (E, H, I // 128)
+    assert w13.shape == (E, 2 * I, H // 2) and s13.shape == (E, 2 * I, H // sblk)
+    assert w2.shape == (E, H, I // 2) and s2.shape == (E, H, I // sblk)
     assert ids.shape == (T, k) and tw.shape == (T, k)
     out = np.empty((T, H), np.uint16)
     qh = sh = y2 = None
@@ -215,14 +260,16 @@ def fused_moe(hidden_bits, topk_ids, topk_weights, expert_begin, num_local_exper
         qh = np.zeros((max(P, 1), I), np.uint8)
         sh = np.zeros((max(P, 1), I // 128), np.float32)
         y2 = np.zeros((max(P, 1), H), np.float64)
-    rc = lib().orc_fused_moe(_p(x, ctypes.c_uint16), T, H, _p(ids, ctypes.c_int32),
-                             _p(tw, ctypes.c_float), k, expert_begin, E, I,
-                             _p(w13, ctypes.c_uint8), _p(s13, ctypes.c_float),
-                             _p(w2, ctypes.c_uint8), _p(s2, ctypes.c_float),
-                             _p(out, ctypes.c_uint16), _p(qh, ctypes.c_uint8),
-                             _p(sh, ctypes.c_float), _p(y2, ctypes.c_double))
+    sct = ctypes.c_uint8 if fp4 else ctypes.c_float
+    fn = lib().orc_fused_moe_fp4 if fp4 else lib().orc_fused_moe
+    rc = fn(_p(x, ctypes.c_uint16), T, H, _p(ids, ctypes.c_int32),
+            _p(tw, ctypes.c_float), k, expert_begin, E, I,
+            _p(w13, ctypes.c_uint8), _p(s13, sct),
+            _p(w2, ctypes.c_uint8), _p(s2, sct),
+            _p(out, ctypes.c_uint16), _p(qh, ctypes.c_uint8),
+            _p(sh, ctypes.c_float), _p(y2, ctypes.c_double))
     if rc:
-        raise ValueError("orc_fused_moe failed: %d" % rc)
+        raise ValueError("orc fused forward failed: %d" % rc)
     if not intermediates:
         return out
     ids_flat = ids.ravel()

@@ -77,6 +77,35 @@ int orc_int4_value(uint8_t byte, int odd)
     return n >= 8 ? n - 16 : n;
 }
 
+/* OCP MX fp4 e2m1 ([P4] "Changes": packed FP4 (E2M1) expert weights).
+ * Field layout of the nibble: sign | 2-bit exponent, bias 1 | 1-bit
+ * mantissa; exponent field 0 encodes the subnormal m * 2^-1 (so 0 and 0.5),
+ * otherwise (1 + m/2) * 2^(e-1).  No infinities or NaNs. */
+double orc_e2m1_decode(uint8_t nibble)
+{
+    int sign = (nibble >> 3) & 1;
+    int e = (nibble >> 1) & 0x3;
+    int m = nibble & 0x1;
+    double mag = (e == 0) ? ldexp((double)m, -1) : ldexp(1.0 + (double)m / 2.0, e - 1);
+    return sign ? -mag : mag;
+}
+
+/* fp4 weights packed two per byte like the int4 ones: k even in the low
+ * nibble, k odd in the high nibble. */
+double orc_fp4_value(uint8_t byte, int odd)
+{
+    return orc_e2m1_decode((uint8_t)(odd ? (byte >> 4) : (byte & 0xF)));
+}
+
+/* OCP MX E8M0 scale ([P4] "Changes": per-32-K UE8M0 weight scales): an
+ * unsigned power-of-two exponent with bias 127, 0xFF = NaN. */
+double orc_ue8m0_decode(uint8_t e)
+{
+    if (e == 0xFF)
+        return NAN;
+    return ldexp(1.0, (int)e - 127);
+}
+
 double orc_bf16_to_double(uint16_t bits)
 {
     uint32_t u = (uint32_t)bits << 16;
@@ -277,17 +306,51 @@ void orc_gemm_bf16(const uint8_t* a, const float* sa, int64_t M, int64_t K,
     free(y);
 }
 
+/* W4A8 GEMM with fp4 weights: each weight is its e2m1 value times the UE8M0
+ * scale of its 32-K block; the activation scale still applies per 128-K
+ * group.  y[m,n] = sum_g sa[m,g] * sum_{k in g} a[m,k] * w[n,k] * sw[n,k/32],
+ * every group sum exact in fp64 for these operands. */
+void orc_gemm_fp4_f64(const uint8_t* a, const float* sa, int64_t M, int64_t K,
+                      const uint8_t* w, const uint8_t* sw, int64_t N, double* y)
+{
+    int64_t G = K / ORC_GROUP;
+    int64_t B = K / ORC_FP4_BLOCK;
+    double* arow = (double*)malloc(sizeof(double) * (size_t)K);
+    if (!arow)
+        return;
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t k = 0; k < K; ++k)
+            arow[k] = orc_e4m3_decode(a[m * K + k]);
+        for (int64_t n = 0; n < N; ++n) {
+            const uint8_t* wrow = w + n * (K / 2);
+            const uint8_t* srow = sw + n * B;
+            double total = 0.0;
+            for (int64_t g = 0; g < G; ++g) {
+                double acc = 0.0;
+                for (int64_t k = g * ORC_GROUP; k < (g + 1) * ORC_GROUP; ++k)
+                    acc += arow[k] * (orc_fp4_value(wrow[k / 2], (int)(k & 1)) *
+                                      orc_ue8m0_decode(srow[k / ORC_FP4_BLOCK]));
+                total += acc * (double)sa[m * G + g];
+            }
+            y[m * N + n] = total;
+        }
+    }
+    free(arow);
+}
+
 /* ------------------------------------------------------------------------ */
 /* The fused-MoE forward ([P2] "Cutlass W4A8 MoE" workflow; [P4] "Changes") */
 /* ------------------------------------------------------------------------ */
 
-int orc_fused_moe(const uint16_t* hidden, int64_t T, int64_t H,
-                  const int32_t* topk_ids, const float* topk_weights, int64_t topk,
-                  int64_t expert_begin, int64_t num_local_experts, int64_t I,
-                  const uint8_t* w13, const float* s13,
-                  const uint8_t* w2, const float* s2,
-                  uint16_t* out,
-                  uint8_t* qh_out, float* sh_out, double* y2_out)
+/* fp4: weights e2m1 with UE8M0 scales per 32 K (s13 [E,2I,H/32], s2
+ * [E,H,I/32] bytes); otherwise int4 with fp32 scales per 128 K. */
+static int fused_moe_impl(const uint16_t* hidden, int64_t T, int64_t H,
+                          const int32_t* topk_ids, const float* topk_weights, int64_t topk,
+                          int64_t expert_begin, int64_t num_local_experts, int64_t I,
+                          const uint8_t* w13, const void* s13,
+                          const uint8_t* w2, const void* s2, int fp4,
+                          uint16_t* out,
+                          uint8_t* qh_out, float* sh_out, double* y2_out)
 {
     int64_t E = num_local_experts;
     int64_t F = T * topk;
@@ -327,13 +390,18 @@ int orc_fused_moe(const uint16_t* hidden, int64_t T, int64_t H,
      * gate_up GEMM, SwiGLU, requantise, down GEMM */
     for (int64_t e = 0; e < E; ++e) {
         const uint8_t* w13e = w13 + e * (2 * I) * (H / 2);
-        const float* s13e = s13 + e * (2 * I) * GH;
         const uint8_t* w2e = w2 + e * H * (I / 2);
-        const float* s2e = s2 + e * H * GI;
+        const float* s13e = fp4 ? NULL : (const float*)s13 + e * (2 * I) * GH;
+        const float* s2e = fp4 ? NULL : (const float*)s2 + e * H * GI;
+        const uint8_t* b13e = fp4 ? (const uint8_t*)s13 + e * (2 * I) * (H / ORC_FP4_BLOCK) : NULL;
+        const uint8_t* b2e = fp4 ? (const uint8_t*)s2 + e * H * (I / ORC_FP4_BLOCK) : NULL;
         for (int64_t p = offsets[e]; p < offsets[e + 1]; ++p) {
             int64_t t = sorted[p] / topk;
             /* 3. GEMM1: y1 = gate_up(x_t), 2I outputs */
-            orc_gemm_f64(qx + t * H, sx + t * GH, 1, H, w13e, s13e, 2 * I, y1);
+            if (fp4)
+                orc_gemm_fp4_f64(qx + t * H, sx + t * GH, 1, H, w13e, b13e, 2 * I, y1);
+            else
+                orc_gemm_f64(qx + t * H, sx + t * GH, 1, H, w13e, s13e, 2 * I, y1);
             /* 4. SwiGLU in fp64: silu(gate) * up, then one rounding to fp32 */
             for (int64_t i = 0; i < I; ++i) {
                 double g = y1[i], u = y1[I + i];
@@ -347,7 +415,10 @@ int orc_fused_moe(const uint16_t* hidden, int64_t T, int64_t H,
             if (sh_out)
                 memcpy(sh_out + p * GI, sh, sizeof(float) * (size_t)GI);
             /* 6. GEMM2: y2 = down(h), H outputs */
-            orc_gemm_f64(qh, sh, 1, I, w2e, s2e, H, y2 + p * H);
+            if (fp4)
+                orc_gemm_fp4_f64(qh, sh, 1, I, w2e, b2e, H, y2 + p * H);
+            else
+                orc_gemm_f64(qh, sh, 1, I, w2e, s2e, H, y2 + p * H);
         }
     }
     if (y2_out)
@@ -380,4 +451,30 @@ done:
     free(sh);
     free(y2);
     return rc;
+}
+
+int orc_fused_moe(const uint16_t* hidden, int64_t T, int64_t H,
+                  const int32_t* topk_ids, const float* topk_weights, int64_t topk,
+                  int64_t expert_begin, int64_t num_local_experts, int64_t I,
+                  const uint8_t* w13, const float* s13,
+                  const uint8_t* w2, const float* s2,
+                  uint16_t* out,
+                  uint8_t* qh_out, float* sh_out, double* y2_out)
+{
+    return fused_moe_impl(hidden, T, H, topk_ids, topk_weights, topk, expert_begin,
+                          num_local_experts, I, w13, s13, w2, s2, 0, out, qh_out, sh_out, y2_out);
+}
+
+int orc_fused_moe_fp4(const uint16_t* hidden, int64_t T, int64_t H,
+                      const int32_t* topk_ids, const float* topk_weights, int64_t topk,
+                      int64_t expert_begin, int64_t num_local_experts, int64_t I,
+                      const uint8_t* w13, const uint8_t* s13,
+                      const uint8_t* w2, const uint8_t* s2,
+                      uint16_t* out,
+                      uint8_t* qh_out, float* sh_out, double* y2_out)
+{
+    if (H % ORC_FP4_BLOCK || I % ORC_FP4_BLOCK)
+        return 1;
+    return fused_moe_impl(hidden, T, H, topk_ids, topk_weights, topk, expert_begin,
+                          num_local_experts, I, w13, s13, w2, s2, 1, out, qh_out, sh_out, y2_out);
 }

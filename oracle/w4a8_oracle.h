@@ -25,7 +25,8 @@
  *        small-batch path" -- commit note dropping the UE8M0 activation scale
  *        (fp32 per-token activation scales; amax clamped before the
  *        reciprocal 448/amax) and the "Changes" list (L1 GEMM -> SwiGLU ->
- *        per-token FP8 requant -> L2 GEMM -> combine).
+ *        per-token FP8 requant -> L2 GEMM -> combine; FP8 E4M3 activations
+ *        x packed FP4 E2M1 expert weights with per-32-K UE8M0 weight scales).
  *
  * Readings where the pages are silent (each fixed by the project spec):
  *   - amax clamp constant 1e-10f; dequant scale amax_c/448; codes use the
@@ -34,6 +35,9 @@
  *   - gate rows [0, I), up rows [I, 2I) of w13; plain SwiGLU (no clamp).
  *   - top-k weights applied in the combine, after the down GEMM.
  *   - non-local top-k ids are skipped; a token with no local pair outputs +0.
+ *   - fp4 weights: e2m1 and E8M0 as the OCP MX formats define them; nibble
+ *     order as for int4; one scale byte per 32 consecutive K of a row
+ *     (s [E_l, N, K/32]); activations keep their per-128 fp32 scales.
  *
  * Layouts (row-major, K contiguous):
  *   activations bf16 [T, H] (uint16 bit patterns);
@@ -50,11 +54,15 @@ extern "C" {
 #endif
 
 #define ORC_GROUP 128
+#define ORC_FP4_BLOCK 32
 
 /* ---- codecs ---- */
 double   orc_e4m3_decode(uint8_t code);
 uint8_t  orc_e4m3_encode(float v);
 int      orc_int4_value(uint8_t byte, int odd);
+double   orc_e2m1_decode(uint8_t nibble);
+double   orc_fp4_value(uint8_t byte, int odd);
+double   orc_ue8m0_decode(uint8_t e);
 double   orc_bf16_to_double(uint16_t bits);
 uint16_t orc_bf16_from_double(double v);
 
@@ -77,6 +85,9 @@ void orc_gemm_f64(const uint8_t* a, const float* sa, int64_t M, int64_t K,
                   const uint8_t* w, const float* sw, int64_t N, double* y);
 void orc_gemm_bf16(const uint8_t* a, const float* sa, int64_t M, int64_t K,
                    const uint8_t* w, const float* sw, int64_t N, uint16_t* out);
+/* fp4 weights w [N, K/2] (e2m1 nibbles), UE8M0 scales sw [N, K/32] */
+void orc_gemm_fp4_f64(const uint8_t* a, const float* sa, int64_t M, int64_t K,
+                      const uint8_t* w, const uint8_t* sw, int64_t N, double* y);
 
 /* ---- the whole forward: align, quant, GEMM1, SwiGLU, requant, GEMM2, combine ----
  * qh [P, I], sh [P, I/128] and y2 [P, H] (pair order = sorted order) are
@@ -88,6 +99,15 @@ int orc_fused_moe(const uint16_t* hidden, int64_t T, int64_t H,
                   const uint8_t* w2, const float* s2,
                   uint16_t* out,
                   uint8_t* qh, float* sh, double* y2);
+/* the same forward on fp4 weights: s13 [E_l, 2I, H/32], s2 [E_l, H, I/32]
+ * UE8M0 bytes; H and I multiples of 128 */
+int orc_fused_moe_fp4(const uint16_t* hidden, int64_t T, int64_t H,
+                      const int32_t* topk_ids, const float* topk_weights, int64_t topk,
+                      int64_t expert_begin, int64_t num_local_experts, int64_t I,
+                      const uint8_t* w13, const uint8_t* s13,
+                      const uint8_t* w2, const uint8_t* s2,
+                      uint16_t* out,
+                      uint8_t* qh, float* sh, double* y2);
 
 #ifdef __cplusplus
 }

@@ -431,3 +431,135 @@ def test_fused_moe_intermediates_consistent(orc):
                       d["w2"][int(np.searchsorted(r["offsets"], 0, side="right") - 1)],
                       d["s2"][int(np.searchsorted(r["offsets"], 0, side="right") - 1)])
     assert np.array_equal(y2[0], inter["y2"][0])
+
+
+# ---------------------------------------------------------------------------
+# fp4 (E2M1) weights with per-32 UE8M0 scales
+# ---------------------------------------------------------------------------
+
+def e2m1_table():
+    """code -> value from the fixture written out from the OCP MX definition."""
+    tab = np.zeros(16)
+    with open(os.path.join(GOLDEN, "e2m1_codes.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                c, v = line.split()
+                tab[int(c, 16)] = float(v)
+    return tab
+
+
+def torch_ue8m0(exps):
+    t = torch.from_numpy(np.asarray(exps, np.uint8).copy()).view(torch.float8_e8m0fnu)
+    return t.to(torch.float64).numpy()
+
+
+def dequant_fp4(w, sb):
+    """fp4 weights [N, K/2] and UE8M0 bytes [N, K/32] -> fp64 [N, K] from the
+    fixture table and torch's E8M0 decode."""
+    tab = e2m1_table()
+    K = w.shape[1] * 2
+    vals = np.empty((w.shape[0], K), np.float64)
+    vals[:, 0::2] = tab[w & 0x0F]
+    vals[:, 1::2] = tab[w >> 4]
+    return vals * np.repeat(torch_ue8m0(sb), 32, axis=1)
+
+
+def test_e2m1_decode_matches_spec_table(orc):
+    got = orc.e2m1_decode(np.arange(16))
+    tab = e2m1_table()
+    assert np.array_equal(got, tab)
+    assert np.array_equal(np.signbit(got), np.signbit(tab))  # -0 for code 8
+
+
+def test_ue8m0_decode_matches_torch_on_every_code(orc):
+    codes = np.arange(256)
+    got, ref = orc.ue8m0_decode(codes), torch_ue8m0(codes)
+    assert np.isnan(got[255]) and np.isnan(ref[255])
+    assert np.array_equal(got[:255], ref[:255])
+
+
+def test_fp4_gemm_matches_dequantised_fp64_matmul(orc):
+    rng = np.random.default_rng(17)
+    M, K, N = 4, 512, 21
+    x = rng.normal(size=(M, K)).astype(np.float32)
+    codes, sa = orc.quantize_f32(x)
+    w = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    sb = rng.integers(115, 125, size=(N, K // 32), dtype=np.uint8)
+    y = orc.gemm_fp4_f64(codes, sa, w, sb)
+    ref = dequant_rows(codes, sa) @ dequant_fp4(w, sb).T
+    assert np.max(np.abs(y - ref)) <= 1e-12 * np.max(np.abs(ref))
+
+
+def test_fp4_gemm_block_scale_acts_on_its_32_k_only(orc):
+    """Raising the scale byte of block b by one doubles exactly that block's
+    contribution (its weights alone, others zeroed): pins the k/32 index."""
+    rng = np.random.default_rng(18)
+    M, K, N = 3, 256, 5
+    codes, sa = orc.quantize_f32(rng.normal(size=(M, K)).astype(np.float32))
+    w = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    sb = rng.integers(118, 122, size=(N, K // 32), dtype=np.uint8)
+    y = orc.gemm_fp4_f64(codes, sa, w, sb)
+    for b in (0, 3, 5, 7):
+        only = np.zeros_like(w)
+        only[:, 16 * b:16 * (b + 1)] = w[:, 16 * b:16 * (b + 1)]
+        part = orc.gemm_fp4_f64(codes, sa, only, sb)
+        bumped = sb.copy()
+        bumped[:, b] += 1
+        assert np.allclose(orc.gemm_fp4_f64(codes, sa, w, bumped), y + part, rtol=1e-13, atol=0)
+
+
+# fp4 codes with integer values and the int4 nibble of the same value
+FP4_INT_CODES = np.array([0x0, 0x2, 0x4, 0x5, 0x6, 0x7, 0xA, 0xC, 0xD, 0xE, 0xF], np.uint8)
+
+
+def fp4_to_int4_nibble(codes):
+    v = e2m1_table()[codes].astype(np.int64)
+    return (v & 0xF).astype(np.uint8)
+
+
+def test_fp4_fused_equals_int4_fused_on_integer_codes(orc):
+    """fp4 weights restricted to integer values with one UE8M0 exponent per
+    128-group give the int4 forward with fp32 scale 2^(e-127), bit for bit."""
+    _, d = synth.random_moe(10, 256, 128, 8, 2, 2, 4, seed=19)
+    rng = np.random.default_rng(19)
+    out4 = {}
+    fp4 = {}
+    for key, skey in (("w13", "s13"), ("w2", "s2")):
+        shp = d[key].shape
+        lo = FP4_INT_CODES[rng.integers(0, FP4_INT_CODES.size, size=shp)]
+        hi = FP4_INT_CODES[rng.integers(0, FP4_INT_CODES.size, size=shp)]
+        fp4[key] = lo | (hi << 4)
+        out4[key] = fp4_to_int4_nibble(lo) | (fp4_to_int4_nibble(hi) << 4)
+        ngroups = shp[2] * 2 // 128
+        e = rng.integers(118, 124, size=shp[:2] + (ngroups,), dtype=np.uint8)
+        fp4[skey] = np.repeat(e, 4, axis=2)
+        out4[skey] = np.ldexp(1.0, e.astype(np.int64) - 127).astype(np.float32)
+    a = orc.fused_moe_fp4(d["hidden"], d["topk_ids"], d["topk_weights"], 2, 4,
+                          fp4["w13"], fp4["s13"], fp4["w2"], fp4["s2"])
+    b = orc.fused_moe(d["hidden"], d["topk_ids"], d["topk_weights"], 2, 4,
+                      out4["w13"], out4["s13"], out4["w2"], out4["s2"])
+    assert np.array_equal(a, b)
+    assert np.any(a != 0)
+
+
+def test_fp4_fused_matches_brute_force(orc):
+    import oracle
+    _, d = synth.random_moe_fp4(7, 256, 128, 8, 3, 0, 5, seed=20)
+    out = orc.fused_moe_fp4(d["hidden"], d["topk_ids"], d["topk_weights"], 0, 5,
+                            d["w13"], d["s13"], d["w2"], d["s2"])
+    x, ids, tw = d["hidden"], d["topk_ids"], d["topk_weights"]
+    I = 128
+    qx, sx = oracle.quantize_bf16(x)
+    A = dequant_rows(qx, sx)
+    ref = np.zeros((x.shape[0], 256))
+    for t in range(x.shape[0]):
+        for j in range(ids.shape[1]):
+            e = int(ids[t, j])
+            if not 0 <= e < 5:
+                continue
+            y1 = dequant_fp4(d["w13"][e], d["s13"][e]) @ A[t]
+            h = (y1[:I] / (1.0 + np.exp(-y1[:I])) * y1[I:]).astype(np.float32)
+            qh, sh = oracle.quantize_f32(h[None, :])
+            ref[t] += np.float64(tw[t, j]) * (dequant_fp4(d["w2"][e], d["s2"][e]) @ dequant_rows(qh, sh)[0])
+    assert np.array_equal(out, orc.bf16_from_double(ref))

@@ -18,6 +18,9 @@ benchmark configurations):
     the dense case multiplies an entry by 20 with probability 0.01;
   * int4 weights: uniform random bytes (each nibble uniform on -8..7);
   * weight scales: fp32 uniform on [0.002, 0.02];
+  * fp4 weights (the FP4 E2M1 variant): uniform random bytes (each nibble
+    uniform over the 16 e2m1 codes), one UE8M0 scale byte per 32 K drawn
+    uniformly from 2^-9 .. 2^-6 (streams 5 and 7, top two bits of a draw);
   * routing: N(0, 1) logits over all experts (plus a Zipf(s) popularity bias
     -s*ln(rank) for the skewed cases), softmax in fp64, top-k with ties to
     the lower expert id, weights renormalised over the top-k, stored fp32.
@@ -224,6 +227,26 @@ def gen_expert_weights(cfg: MoEConfig, seed: Optional[int] = None):
     return w13, s13, w2, s2
 
 
+def gen_expert_weights_fp4(cfg: MoEConfig, seed: Optional[int] = None):
+    """(w13 [E_l, 2I, H/2] u8 e2m1 nibbles, s13 [E_l, 2I, H/32] u8 UE8M0,
+    w2 [E_l, H, I/2] u8, s2 [E_l, H, I/32] u8) for the local experts."""
+    seed = cfg.seed if seed is None else seed
+    E, H, I = cfg.E_local, cfg.H, cfg.I
+    w13 = draw_bytes(seed, STREAM_W13, E * 2 * I * H // 2).reshape(E, 2 * I, H // 2)
+    w2 = draw_bytes(seed, STREAM_W2, E * H * I // 2).reshape(E, H, I // 2)
+    ue = lambda stream, n: (118 + (draw_u64(seed, stream, 0, n) >> np.uint64(62))).astype(np.uint8)
+    s13 = ue(STREAM_S13, E * 2 * I * (H // 32)).reshape(E, 2 * I, H // 32)
+    s2 = ue(STREAM_S2, E * H * (I // 32)).reshape(E, H, I // 32)
+    return w13, s13, w2, s2
+
+
+def gen_moe_fp4(cfg: MoEConfig, seed: Optional[int] = None) -> dict:
+    ids, w = gen_routing(cfg)
+    w13, s13, w2, s2 = gen_expert_weights_fp4(cfg, seed)
+    return dict(hidden=gen_hidden(cfg), topk_ids=ids, topk_weights=w,
+                w13=w13, s13=s13, w2=w2, s2=s2)
+
+
 def gen_moe(cfg: MoEConfig, seed: Optional[int] = None) -> dict:
     ids, w = gen_routing(cfg)
     w13, s13, w2, s2 = gen_expert_weights(cfg, seed)
@@ -261,3 +284,11 @@ def random_moe(T: int, H: int, I: int, E_total: int, topk: int, expert_begin: in
     cfg = MoEConfig("adhoc", T=T, H=H, I=I, E_total=E_total, topk=topk,
                     expert_begin=expert_begin, E_local=E_local, routing=routing, seed=seed)
     return cfg, gen_moe(cfg)
+
+
+def random_moe_fp4(T: int, H: int, I: int, E_total: int, topk: int, expert_begin: int,
+                   E_local: int, seed: int, routing: str = "uniform") -> tuple:
+    """As random_moe, with fp4 e2m1 weights and UE8M0 per-32 scales."""
+    cfg = MoEConfig("adhoc", T=T, H=H, I=I, E_total=E_total, topk=topk,
+                    expert_begin=expert_begin, E_local=E_local, routing=routing, seed=seed)
+    return cfg, gen_moe_fp4(cfg)
