@@ -187,8 +187,8 @@ int w4a8_fused_moe(const void* hidden_bf16, int64_t T, int64_t H,
 int w4a8_prepack_weights(const uint8_t* w_int4, const float* w_scales, int64_t E, int64_t N,
                          int64_t K, uint8_t* w_packed, float* s_packed, hipStream_t stream);
 
-/* Floats of the prepacked scales of E experts of N x K (host-only; -1 for a
- * bad shape). */
+/* 4-byte elements of the prepacked scales of E experts of N x K, for both
+ * weight formats (host-only; -1 for a bad shape). */
 int64_t w4a8_prepacked_scale_count(int64_t E, int64_t N, int64_t K);
 
 /*
@@ -205,6 +205,56 @@ int w4a8_fused_moe_prepacked(const void* hidden_bf16, int64_t T, int64_t H,
                              const uint8_t* w2_packed, const float* w2_scales_packed,
                              void* out_bf16, void* workspace, size_t* workspace_bytes,
                              hipStream_t stream);
+
+/*
+ * FP4 weights (DeepGEMM PR #53, "Changes": FP8 E4M3 activations x packed FP4
+ * E2M1 expert weights with per-32-K UE8M0 weight scales).  Canonical input
+ * layout: w_fp4 [E, N, K/2] e2m1 codes, two per byte, k even in the low
+ * nibble; w_scales_ue8m0 [E, N, K/32] bytes, the weight at (n, k) being
+ * e2m1 * 2^(scale[n, k/32] - 127).  Activations keep their dynamic per-token
+ * per-128 fp32 scales.
+ *
+ * w4a8_prepack_weights_fp4 -- one-time re-layout for
+ * w4a8_fused_moe_fp4_prepacked; pure data movement, asynchronous.
+ *   role      W4A8_FP4_GATE_UP for w13 (N = 2I, K = H), W4A8_FP4_DOWN for
+ *             w2 (N = H, K = I): the gate_up GEMM converts its weights to
+ *             f16 in the activation operand's K order, so its nibbles are
+ *             reordered; the down GEMM feeds them to the scaled MFMA as they are
+ *   w_packed  E*N*K/2 bytes, blocked as w4a8_prepack_weights does; with
+ *             W4A8_FP4_GATE_UP each dword's nibbles k0..k7 become
+ *             k0,k2,k4,k6,k1,k3,k5,k7
+ *   s_packed  w4a8_prepacked_scale_count(E, N, K) dwords, placed as the fp32
+ *             scales of w4a8_prepack_weights; the dword of row n, group g
+ *             holds the group's four UE8M0 bytes (32-K block b in byte b)
+ * N % 16 == 0, K % 128 == 0; w_scales_ue8m0 4-byte aligned, the rest
+ * 16-byte aligned; outputs must not alias the inputs.  Errors: INVALID_ARG
+ * (null, non-positive sizes, unknown role, in place), UNSUPPORTED (shape or
+ * alignment), HIP.
+ */
+#define W4A8_FP4_GATE_UP 0
+#define W4A8_FP4_DOWN 1
+int w4a8_prepack_weights_fp4(const uint8_t* w_fp4, const uint8_t* w_scales_ue8m0, int64_t E,
+                             int64_t N, int64_t K, int role, uint8_t* w_packed,
+                             uint32_t* s_packed, hipStream_t stream);
+
+/*
+ * w4a8_fused_moe_fp4_prepacked -- the fused forward on fp4 weights prepacked
+ * by w4a8_prepack_weights_fp4 (w13 with W4A8_FP4_GATE_UP, w2 with
+ * W4A8_FP4_DOWN).  Same arguments, workspace and errors as
+ * w4a8_fused_moe_prepacked; the result follows the same definition with each
+ * weight e2m1 * 2^(e - 127).  The gate_up GEMM stays exact (f16 MFMA on
+ * exactly converted operands) while the four block exponents of a row's
+ * 128-group lie within 23 binades of their maximum; the down GEMM applies the
+ * block scales in the MFMA itself.  The requantised intermediate in the
+ * workspace (offsets[9]) is stored in natural K order on this path.
+ */
+int w4a8_fused_moe_fp4_prepacked(const void* hidden_bf16, int64_t T, int64_t H,
+                                 const int32_t* topk_ids, const float* topk_weights, int64_t topk,
+                                 int64_t expert_begin, int64_t num_local_experts, int64_t I,
+                                 const uint8_t* w13_packed, const uint32_t* w13_scales_packed,
+                                 const uint8_t* w2_packed, const uint32_t* w2_scales_packed,
+                                 void* out_bf16, void* workspace, size_t* workspace_bytes,
+                                 hipStream_t stream);
 
 /*
  * w4a8_fused_moe_workspace_layout -- where w4a8_fused_moe keeps its

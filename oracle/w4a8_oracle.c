@@ -315,6 +315,12 @@ void orc_gemm_fp4_f64(const uint8_t* a, const float* sa, int64_t M, int64_t K,
 {
     int64_t G = K / ORC_GROUP;
     int64_t B = K / ORC_FP4_BLOCK;
+    /* the codecs tabulated once (16 and 256 entries), for speed only */
+    double vtab[16], stab[256];
+    for (int c = 0; c < 16; ++c)
+        vtab[c] = orc_e2m1_decode((uint8_t)c);
+    for (int e = 0; e < 256; ++e)
+        stab[e] = orc_ue8m0_decode((uint8_t)e);
     double* arow = (double*)malloc(sizeof(double) * (size_t)K);
     if (!arow)
         return;
@@ -327,9 +333,10 @@ void orc_gemm_fp4_f64(const uint8_t* a, const float* sa, int64_t M, int64_t K,
             double total = 0.0;
             for (int64_t g = 0; g < G; ++g) {
                 double acc = 0.0;
-                for (int64_t k = g * ORC_GROUP; k < (g + 1) * ORC_GROUP; ++k)
-                    acc += arow[k] * (orc_fp4_value(wrow[k / 2], (int)(k & 1)) *
-                                      orc_ue8m0_decode(srow[k / ORC_FP4_BLOCK]));
+                for (int64_t k = g * ORC_GROUP; k < (g + 1) * ORC_GROUP; ++k) {
+                    const uint8_t nib = (k & 1) ? (uint8_t)(wrow[k / 2] >> 4) : (uint8_t)(wrow[k / 2] & 0xF);
+                    acc += arow[k] * (vtab[nib] * stab[srow[k / ORC_FP4_BLOCK]]);
+                }
                 total += acc * (double)sa[m * G + g];
             }
             y[m * N + n] = total;

@@ -155,3 +155,29 @@ def test_fused_moe_prepacked_rejects_bad_arguments(L):
     assert f(I=100) == UNSUPPORTED
     assert f(w13=None) == INVALID
     assert f(nbytes=ctypes.c_size_t(16)) == WORKSPACE
+
+
+def test_prepack_fp4_rejects_bad_arguments(L):
+    p = L.w4a8_prepack_weights_fp4
+    other = ctypes.c_void_p(0x2000)
+    args = lambda E=2, N=32, K=256, role=0, w=BOGUS, s=BOGUS, wp=other, sp=other: p(
+        w, s, E, N, K, role, wp, sp, None)
+    assert args(role=2) == INVALID
+    assert args(role=-1) == INVALID
+    assert args(E=0) == INVALID
+    assert args(s=None) == INVALID
+    assert args(N=40) == UNSUPPORTED
+    assert args(K=160) == UNSUPPORTED
+    assert args(s=ctypes.c_void_p(0x1002)) == UNSUPPORTED   # scales need 4-byte alignment
+    assert args(wp=MISALIGNED) == UNSUPPORTED
+    assert args(sp=BOGUS) == INVALID                        # in place
+
+
+def test_fused_moe_fp4_rejects_bad_arguments(L):
+    n = ctypes.c_size_t(1 << 40)
+    f = lambda H=256, I=128, w13=BOGUS, nbytes=n: L.w4a8_fused_moe_fp4_prepacked(
+        BOGUS, 4, H, BOGUS, BOGUS, 2, 0, 4, I, w13, BOGUS, BOGUS, BOGUS, BOGUS, BOGUS,
+        ctypes.byref(nbytes), None)
+    assert f(H=200) == UNSUPPORTED
+    assert f(w13=None) == INVALID
+    assert f(nbytes=ctypes.c_size_t(16)) == WORKSPACE

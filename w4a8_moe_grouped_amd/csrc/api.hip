@@ -264,13 +264,17 @@ int w4a8_moe_align(const int32_t* topk_ids, int64_t T, int64_t topk, int64_t exp
 
 namespace {
 
+// weight formats of the fused forward
+enum WeightFormat { kInt4 = 0, kInt4Packed = 1, kFp4Packed = 2 };
+
 int fused_moe_impl(const void* hidden_bf16, int64_t T, int64_t H, const int32_t* topk_ids,
                    const float* topk_weights, int64_t topk, int64_t expert_begin,
                    int64_t num_local_experts, int64_t I, const uint8_t* w13_int4,
-                   const float* w13_scales, const uint8_t* w2_int4, const float* w2_scales,
+                   const void* w13_scales, const uint8_t* w2_int4, const void* w2_scales,
                    void* out_bf16, void* workspace, size_t* workspace_bytes, hipStream_t stream,
-                   bool packed)
+                   WeightFormat format)
 {
+    const bool packed = format != kInt4;
     const int64_t E = num_local_experts;
     if (T < 0 || H <= 0 || I <= 0 || topk < 1 || E < 1)
         return W4A8_ERR_INVALID_ARG;
@@ -338,8 +342,9 @@ int fused_moe_impl(const void* hidden_bf16, int64_t T, int64_t H, const int32_t*
     g.sorted = p.al.sorted;
     g.topk = (int32_t)topk;
     g.packed = packed ? 1 : 0;
+    g.fp4 = format == kFp4Packed ? 1 : 0;
     g.w = w13_int4;
-    g.ws = w13_scales;
+    g.ws = (const float*)w13_scales;
     g.w_estride = 2 * I * (H / 2);
     g.s_estride = 2 * I * (packed ? 4 * ceil_div(H / W4A8_GROUP, 4) : H / W4A8_GROUP);
     g.K = H;
@@ -359,7 +364,7 @@ int fused_moe_impl(const void* hidden_bf16, int64_t T, int64_t H, const int32_t*
     g.act_side = p.qh_side;
     g.sorted = nullptr;
     g.w = w2_int4;
-    g.ws = w2_scales;
+    g.ws = (const float*)w2_scales;
     g.w_estride = H * (I / 2);
     g.s_estride = H * (packed ? 4 * ceil_div(I / W4A8_GROUP, 4) : I / W4A8_GROUP);
     g.K = I;
@@ -390,7 +395,7 @@ int w4a8_fused_moe(const void* hidden_bf16, int64_t T, int64_t H, const int32_t*
 {
     return fused_moe_impl(hidden_bf16, T, H, topk_ids, topk_weights, topk, expert_begin,
                           num_local_experts, I, w13_int4, w13_scales, w2_int4, w2_scales, out_bf16,
-                          workspace, workspace_bytes, stream, false);
+                          workspace, workspace_bytes, stream, kInt4);
 }
 
 int w4a8_fused_moe_prepacked(const void* hidden_bf16, int64_t T, int64_t H,
@@ -403,7 +408,20 @@ int w4a8_fused_moe_prepacked(const void* hidden_bf16, int64_t T, int64_t H,
 {
     return fused_moe_impl(hidden_bf16, T, H, topk_ids, topk_weights, topk, expert_begin,
                           num_local_experts, I, w13_packed, w13_scales_packed, w2_packed,
-                          w2_scales_packed, out_bf16, workspace, workspace_bytes, stream, true);
+                          w2_scales_packed, out_bf16, workspace, workspace_bytes, stream, kInt4Packed);
+}
+
+int w4a8_fused_moe_fp4_prepacked(const void* hidden_bf16, int64_t T, int64_t H,
+                                 const int32_t* topk_ids, const float* topk_weights, int64_t topk,
+                                 int64_t expert_begin, int64_t num_local_experts, int64_t I,
+                                 const uint8_t* w13_packed, const uint32_t* w13_scales_packed,
+                                 const uint8_t* w2_packed, const uint32_t* w2_scales_packed,
+                                 void* out_bf16, void* workspace, size_t* workspace_bytes,
+                                 hipStream_t stream)
+{
+    return fused_moe_impl(hidden_bf16, T, H, topk_ids, topk_weights, topk, expert_begin,
+                          num_local_experts, I, w13_packed, w13_scales_packed, w2_packed,
+                          w2_scales_packed, out_bf16, workspace, workspace_bytes, stream, kFp4Packed);
 }
 
 int w4a8_prepack_weights(const uint8_t* w_int4, const float* w_scales, int64_t E, int64_t N,
@@ -419,7 +437,30 @@ int w4a8_prepack_weights(const uint8_t* w_int4, const float* w_scales, int64_t E
         return W4A8_ERR_UNSUPPORTED;
     if ((const void*)w_int4 == (const void*)w_packed || (const void*)w_scales == (const void*)s_packed)
         return W4A8_ERR_INVALID_ARG;  // not in place
-    return hip_status(w4a8::launch_prepack(w_int4, w_scales, E, N, K, w_packed, s_packed, stream));
+    return hip_status(w4a8::launch_prepack(w_int4, w_scales, E, N, K, false, w_packed, s_packed, stream));
+}
+
+int w4a8_prepack_weights_fp4(const uint8_t* w_fp4, const uint8_t* w_scales_ue8m0, int64_t E,
+                             int64_t N, int64_t K, int role, uint8_t* w_packed,
+                             uint32_t* s_packed, hipStream_t stream)
+{
+    if (E < 1 || N <= 0 || K <= 0)
+        return W4A8_ERR_INVALID_ARG;
+    if (role != W4A8_FP4_GATE_UP && role != W4A8_FP4_DOWN)
+        return W4A8_ERR_INVALID_ARG;
+    if (w_fp4 == nullptr || w_scales_ue8m0 == nullptr || w_packed == nullptr || s_packed == nullptr)
+        return W4A8_ERR_INVALID_ARG;
+    if (N % 16 != 0 || K % W4A8_GROUP != 0)
+        return W4A8_ERR_UNSUPPORTED;
+    // the scales are moved as one dword per row and 128-group
+    if (!aligned16(w_fp4) || !aligned16(w_packed) || ((uintptr_t)w_scales_ue8m0 & 3u) != 0 ||
+        !aligned16(s_packed))
+        return W4A8_ERR_UNSUPPORTED;
+    if ((const void*)w_fp4 == (const void*)w_packed ||
+        (const void*)w_scales_ue8m0 == (const void*)s_packed)
+        return W4A8_ERR_INVALID_ARG;  // not in place
+    return hip_status(w4a8::launch_prepack(w_fp4, w_scales_ue8m0, E, N, K, role == W4A8_FP4_GATE_UP,
+                                           w_packed, s_packed, stream));
 }
 
 int64_t w4a8_prepacked_scale_count(int64_t E, int64_t N, int64_t K)

@@ -60,6 +60,10 @@ constexpr int kGroup = 128;
 // Scales: blocks of 4 groups, 16 bytes per row, zero past the last group:
 // the scale of row n, group g at float index
 //   ((n/16 * G4 + g/4) * 16 + n%16) * 4 + g%4,   G4 = ceil(G/4).
+// fp4 weights (w4a8_prepack_weights_fp4) use the same blocks; their scale
+// elements are dwords holding the four UE8M0 bytes of a row's group, and for
+// the gate_up GEMM the nibbles of every weight dword are reordered to
+// k0,k2,k4,k6,k1,k3,k5,k7, the order of the fp8 activation operand.
 __host__ __device__ constexpr int64_t packed_groups4(int64_t G)
 {
     return (G + 3) / 4;
@@ -122,6 +126,49 @@ __device__ __forceinline__ v8h fp8x8_to_f16(uint32_t d0, uint32_t d1)
     const v2h h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d1, 1.0f, false);
     const v2h h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d1, 1.0f, true);
     return v8h{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
+}
+
+// one dword of 8 fp4 (e2m1) codes, low nibble first, each times a power-of-two
+// scale -> 8 halves in nibble order (exact while the scaled values stay in
+// f16's range, down to its subnormals)
+__device__ __forceinline__ v8h fp4x8_to_f16(uint32_t d, float scale)
+{
+    const v2h h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, scale, 0);
+    const v2h h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, scale, 1);
+    const v2h h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, scale, 2);
+    const v2h h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, scale, 3);
+    return v8h{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
+}
+
+// One fp8 x fp4 MFMA over a 128-K group: A fp8 codes (scale 2^0), B the
+// lane's 32 e2m1 codes (low nibble first) times 2^(e - 127) for the lane's
+// UE8M0 byte e.  On gfx950 lane quarter q of B holds K [32q, 32q + 32), so a
+// per-32-K weight scale is exactly one lane's scale operand; A lane quarter q
+// holds K [16q, 16q + 16) and [64 + 16q, 64 + 16q + 16), i.e. an A row in
+// its natural K order loaded as the two 16-byte chunks q and 4 + q.
+__device__ __forceinline__ v4f mfma16x16x128_fp4(const v8i& a, const v4i& b, int e)
+{
+    const v8i bb = {b[0], b[1], b[2], b[3], 0, 0, 0, 0};
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, bb, v4f{0.0f, 0.0f, 0.0f, 0.0f}, 0, 4, 0,
+                                                             127, 0, e);
+}
+
+// fp4 weight scales of one row and 128-K group: the dword holds the four
+// UE8M0 bytes of its 32-K blocks (block b in byte b).  For the exact f16 path
+// the lane converts its block (quarter q) with 2^(e_q - e_max), whose values
+// stay <= 6, and the group is promoted with 2^(e_max - 127 - 9) (the 2^-9
+// matches the activation side data, whose c1 is 512 * scale).
+struct Fp4GroupScale {
+    float conv;     // 2^(e_q - e_max)
+    float promote;  // 2^(e_max - 136)
+};
+__device__ __forceinline__ Fp4GroupScale fp4_group_scale(uint32_t sd, int q)
+{
+    const int e0 = (int)(sd & 0xFFu), e1 = (int)((sd >> 8) & 0xFFu);
+    const int e2 = (int)((sd >> 16) & 0xFFu), e3 = (int)(sd >> 24);
+    const int emax = max(max(e0, e1), max(e2, e3));
+    const int eq = (int)((sd >> (8 * q)) & 0xFFu);
+    return Fp4GroupScale{__builtin_amdgcn_ldexpf(1.0f, eq - emax), __builtin_amdgcn_ldexpf(1.0f, emax - 136)};
 }
 
 // canonical 8 codes (two dwords k0..k3, k4..k7) -> interleaved (k0,k2,k4,k6 | k1,k3,k5,k7)

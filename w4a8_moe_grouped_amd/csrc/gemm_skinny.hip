@@ -29,12 +29,16 @@ namespace w4a8 {
 
 constexpr int kWaves = 4;
 
-// NF: weight fragments (16 rows) per wave
-template <int NT, int EPI, int DW, bool F16, bool SW4, bool PK, int NF>
+// NF: weight fragments (16 rows) per wave.  FP4: prepacked fp4 e2m1 weights
+// with UE8M0 scale dwords (DeepGEMM PR #53, Changes): the f16 path converts
+// them exactly with the lane's relative block scale, the fp8 path hands them
+// to the scaled MFMA with the lane's block scale.
+template <int NT, int EPI, int DW, bool F16, bool SW4, bool PK, bool FP4, int NF>
 __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs a)
 {
     constexpr int kNF = NF;
     static_assert(EPI != EPI_SWIGLU_Q || NF == 4, "the SwiGLU tile pairs 2 gate and 2 up fragments");
+    static_assert(!FP4 || PK, "fp4 weights are read in the prepacked layout only");
     constexpr int BM = 16 * NT;
     extern __shared__ float4 lds_side4[];  // [G][BM] float2 {c1, c0}, 16-byte aligned
     float2* lds_side = (float2*)lds_side4;
@@ -214,6 +218,8 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs a)
                 load_scales4(sn4, g0 / 4 + 1 < G4 ? g0 / 4 + 1 : G4 - 1);
                 __builtin_amdgcn_sched_barrier(0);
             }
+            // int4: the weight scale (0 on padding groups); fp4: the bits of
+            // the group's UE8M0 dword
             float swf[kNF];
 #pragma unroll
             for (int f = 0; f < kNF; ++f) {
@@ -224,7 +230,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs a)
                 } else {
                     v = sb[s][f];
                 }
-                swf[f] = g < G ? v : 0.0f;
+                swf[f] = (FP4 || g < G) ? v : 0.0f;
             }
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
@@ -241,7 +247,26 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs a)
                 // all MFMAs of the step first, each fragment into its own
                 // accumulator, so they issue back to back; then the promotion
                 v4f raw[kNF];
-                if (F16) {
+                float wsc[kNF];  // fp4 gate_up: promotion scale 2^(e_max - 136), 0 on padding groups
+                if (F16 && FP4) {
+                    v8h ah[4];
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        ah[c] = fp8x8_to_f16(at[2 * c], at[2 * c + 1]);
+                    float conv[kNF];
+#pragma unroll
+                    for (int f = 0; f < kNF; ++f) {
+                        const Fp4GroupScale fs = fp4_group_scale(__builtin_bit_cast(uint32_t, swf[f]), q);
+                        conv[f] = fs.conv;
+                        wsc[f] = g < G ? fs.promote : 0.0f;
+                        raw[f] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+                    }
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+#pragma unroll
+                        for (int f = 0; f < kNF; ++f)
+                            raw[f] = mfma16x16x32_f16(ah[c], fp4x8_to_f16((uint32_t)wb[s][f][c], conv[f]), raw[f]);
+                } else if (F16) {
                     // fp8 codes -> exact f16: the lane's 8-group c is dwords
                     // 2c, 2c+1 of both operands (k0,k2,k4,k6 | k1,k3,k5,k7)
                     v8h ah[4];
@@ -267,13 +292,35 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs a)
                         av[i] = (int)at[i];
 #pragma unroll
                     for (int f = 0; f < kNF; ++f)
-                        raw[f] = mfma16x16x128(av, unpack_int4_u(wb[s][f]), v4f{0.0f, 0.0f, 0.0f, 0.0f});
+                        raw[f] = FP4 ? mfma16x16x128_fp4(av, wb[s][f],
+                                                         (int)((__builtin_bit_cast(uint32_t, swf[f]) >> (8 * q)) & 0xFFu))
+                                     : mfma16x16x128(av, unpack_int4_u(wb[s][f]), v4f{0.0f, 0.0f, 0.0f, 0.0f});
                 }
+                if (FP4 && F16) {
+                    // y += 2^(e_max - 136) * (raw * 512 sa)
 #pragma unroll
-                for (int f = 0; f < kNF; ++f)
+                    for (int f = 0; f < kNF; ++f)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            acc[f][t][r] = fmaf(raw[f][r] * c1[r], wsc[f], acc[f][t][r]);
+                } else if (FP4) {
+                    // the weight scales are inside raw: y += sa * raw, sa = c1 * 2^-9
+                    float sa[4];
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
-                        acc[f][t][r] = fmaf(swf[f], fmaf(raw[f][r], c1[r], c0[r]), acc[f][t][r]);
+                        sa[r] = g < G ? c1[r] * 0x1p-9f : 0.0f;
+#pragma unroll
+                    for (int f = 0; f < kNF; ++f)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            acc[f][t][r] = fmaf(raw[f][r], sa[r], acc[f][t][r]);
+                } else {
+#pragma unroll
+                    for (int f = 0; f < kNF; ++f)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            acc[f][t][r] = fmaf(swf[f], fmaf(raw[f][r], c1[r], c0[r]), acc[f][t][r]);
+                }
             }
             // keep the refill here, DW groups ahead of its use: without the
             // barrier the scheduler sinks each load next to its consumer and
@@ -361,9 +408,10 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs a)
                     s_red2[wave][row] = sum;
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
+                    // int4 down GEMM: the interleaved operand order; fp4: natural K order
                     const int il = 32 * wave + 16 * j + c16;
                     const int b = il & 7;
-                    const int pos = fp8_group_pos(il >> 3) + ((b & 1) ? 4 + (b >> 1) : (b >> 1));
+                    const int pos = FP4 ? il : fp8_group_pos(il >> 3) + ((b & 1) ? 4 + (b >> 1) : (b >> 1));
                     s_q[row * kGroup + pos] = (uint8_t)((cc >> (8 * j)) & 0xFFu);
                 }
             }
@@ -390,7 +438,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs a)
     }
 }
 
-template <int NT, int EPI, int DW, bool F16, bool SW4, bool PK, int NF = 4>
+template <int NT, int EPI, int DW, bool F16, bool SW4, bool PK, bool FP4, int NF = 4>
 static hipError_t launch_one(const GemmArgs& a, hipStream_t s)
 {
     const int64_t G = a.K / kGroup;
@@ -404,7 +452,7 @@ static hipError_t launch_one(const GemmArgs& a, hipStream_t s)
     grid.z = 1;
     if (grid.x == 0 || grid.y == 0)
         return hipSuccess;
-    hipLaunchKernelGGL((gemm_skinny_kernel<NT, EPI, DW, F16, SW4, PK, NF>), grid, dim3(256), lds, s, a);
+    hipLaunchKernelGGL((gemm_skinny_kernel<NT, EPI, DW, F16, SW4, PK, FP4, NF>), grid, dim3(256), lds, s, a);
     return hipGetLastError();
 }
 
@@ -419,36 +467,44 @@ static hipError_t launch_one(const GemmArgs& a, hipStream_t s)
 #ifndef W4A8_DOWN_NF16
 #define W4A8_DOWN_NF16 2
 #endif
-template <int NT, int DW, bool PK>
+template <int NT, int DW, bool PK, bool FP4>
 static hipError_t launch_nt(const GemmArgs& a, int epilogue, hipStream_t s)
 {
     const bool g4 = (a.K / kGroup) % 4 == 0;
     constexpr int NFD = NT == 1 ? W4A8_DOWN_NF16 : 4;
     switch (epilogue) {
     case EPI_F32:
-        return g4 ? launch_one<NT, EPI_F32, DW, false, 4 % DW == 0, PK, NFD>(a, s)
-                  : launch_one<NT, EPI_F32, DW, false, false, PK, NFD>(a, s);
+        return g4 ? launch_one<NT, EPI_F32, DW, false, 4 % DW == 0, PK, FP4, NFD>(a, s)
+                  : launch_one<NT, EPI_F32, DW, false, false, PK, FP4, NFD>(a, s);
     case EPI_BF16:
         if constexpr (PK) {
             return hipErrorInvalidValue;  // the dense GEMM takes canonical weights only
         } else {
-            return g4 ? launch_one<NT, EPI_BF16, DW, false, 4 % DW == 0, false>(a, s)
-                      : launch_one<NT, EPI_BF16, DW, false, false, false>(a, s);
+            return g4 ? launch_one<NT, EPI_BF16, DW, false, 4 % DW == 0, false, false>(a, s)
+                      : launch_one<NT, EPI_BF16, DW, false, false, false, false>(a, s);
         }
     default:
-        return g4 ? launch_one<NT, EPI_SWIGLU_Q, DW, true, 4 % DW == 0, PK>(a, s)
-                  : launch_one<NT, EPI_SWIGLU_Q, DW, true, false, PK>(a, s);
+        return g4 ? launch_one<NT, EPI_SWIGLU_Q, DW, true, 4 % DW == 0, PK, FP4>(a, s)
+                  : launch_one<NT, EPI_SWIGLU_Q, DW, true, false, PK, FP4>(a, s);
     }
+}
+
+template <int NT, int DW>
+static hipError_t launch_layout(const GemmArgs& a, int epilogue, hipStream_t s)
+{
+    if (a.fp4)
+        return a.packed ? launch_nt<NT, DW, true, true>(a, epilogue, s) : hipErrorInvalidValue;
+    return a.packed ? launch_nt<NT, DW, true, false>(a, epilogue, s)
+                    : launch_nt<NT, DW, false, false>(a, epilogue, s);
 }
 
 hipError_t launch_gemm_skinny(const GemmArgs& a, int epilogue, int block_m, hipStream_t s)
 {
     if (block_m <= 16)
-        return a.packed ? launch_nt<1, W4A8_DW16, true>(a, epilogue, s)
-                        : launch_nt<1, W4A8_DW16, false>(a, epilogue, s);
+        return launch_layout<1, W4A8_DW16>(a, epilogue, s);
     if (block_m <= 32)
-        return a.packed ? launch_nt<2, 3, true>(a, epilogue, s) : launch_nt<2, 3, false>(a, epilogue, s);
-    return a.packed ? launch_nt<4, 2, true>(a, epilogue, s) : launch_nt<4, 2, false>(a, epilogue, s);
+        return launch_layout<2, 3>(a, epilogue, s);
+    return launch_layout<4, 2>(a, epilogue, s);
 }
 
 } // namespace w4a8

@@ -39,7 +39,6 @@
 #include "common.hpp"
 #include "internal.hpp"
 
-#include <type_traits>
 
 namespace w4a8 {
 
@@ -121,9 +120,10 @@ __device__ __forceinline__ int b_slot(int wrow, int chunk)
 }  // namespace
 
 // One tile: rows [row0, row0 + 128) of m-block L's expert x weight block nb.
-template <int MODE, bool F64, bool PK>
+template <int MODE, bool PK, bool FP4>
 __device__ __forceinline__ void tile_body(const GemmArgs& a, const int L, uint8_t* smem, int* s_expert_p)
 {
+    static_assert(!FP4 || PK, "fp4 weights are read in the prepacked layout only");
     int& s_expert = *s_expert_p;
     const int tid = threadIdx.x;
     // the wave index in an SGPR: LDS destinations of the direct loads go
@@ -219,8 +219,7 @@ __device__ __forceinline__ void tile_body(const GemmArgs& a, const int L, uint8_
 
     const bool wave_idle = 64 * wm >= rows;
 
-    using Acc = typename std::conditional<F64, double, float>::type;
-    Acc acc[4][4][4];
+    float acc[4][4][4];
 #pragma unroll
     for (int m = 0; m < 4; ++m)
 #pragma unroll
@@ -281,20 +280,31 @@ __device__ __forceinline__ void tile_body(const GemmArgs& a, const int L, uint8_
     for (int g = 0; g < G; ++g) {
         const uint8_t* base = smem + (g % kStages) * kStageBytes;
         if (!wave_idle) {
+            // int4: weight scales; fp4: gate_up promotion scales 2^(e_max - 136)
             float swc[4];
+            int eq[4];  // fp4 down: the lane's UE8M0 byte
             v8i b8[4];
+            v8h bh[MODE == TILE_GATEUP ? 4 : 1][4];
 #pragma unroll
             for (int f = 0; f < 4; ++f) {
-                swc[f] = sw[f];
-                b8[f] = unpack_int4_u(wb[f]);
-            }
-            v8h bh[MODE == TILE_GATEUP ? 4 : 1][4];
-            if (MODE == TILE_GATEUP) {
-#pragma unroll
-                for (int f = 0; f < 4; ++f)
+                const uint32_t sd = __builtin_bit_cast(uint32_t, sw[f]);
+                if (FP4 && MODE == TILE_GATEUP) {
+                    const Fp4GroupScale fs = fp4_group_scale(sd, q);
+                    swc[f] = fs.promote;
 #pragma unroll
                     for (int c = 0; c < 4; ++c)
-                        bh[f][c] = fp8x8_to_f16((uint32_t)b8[f][2 * c], (uint32_t)b8[f][2 * c + 1]);
+                        bh[f][c] = fp4x8_to_f16((uint32_t)wb[f][c], fs.conv);
+                } else if (FP4) {
+                    eq[f] = (int)((sd >> (8 * q)) & 0xFFu);
+                } else {
+                    swc[f] = sw[f];
+                    b8[f] = unpack_int4_u(wb[f]);
+                    if (MODE == TILE_GATEUP) {
+#pragma unroll
+                        for (int c = 0; c < 4; ++c)
+                            bh[f][c] = fp8x8_to_f16((uint32_t)b8[f][2 * c], (uint32_t)b8[f][2 * c + 1]);
+                    }
+                }
             }
             // all four slices in one basic block (padding rows are computed and
             // dropped at the store)
@@ -325,17 +335,19 @@ __device__ __forceinline__ void tile_body(const GemmArgs& a, const int L, uint8_
                     const v8i av = {ca0[0], ca0[1], ca0[2], ca0[3], ca1[0], ca1[1], ca1[2], ca1[3]};
 #pragma unroll
                     for (int f = 0; f < 4; ++f)
-                        raw[f] = mfma16x16x128(av, b8[f], v4f{0.0f, 0.0f, 0.0f, 0.0f});
+                        raw[f] = FP4 ? mfma16x16x128_fp4(av, wb[f], eq[f])
+                                     : mfma16x16x128(av, b8[f], v4f{0.0f, 0.0f, 0.0f, 0.0f});
                 }
 #pragma unroll
                 for (int f = 0; f < 4; ++f)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        if (F64)
-                            acc[m][f][r] = fma((double)swc[f], fma((double)raw[f][r], (double)c1[r], (double)c0[r]),
-                                               (double)acc[m][f][r]);
+                        if (FP4 && MODE == TILE_GATEUP)  // y += 2^(e_max - 136) * (raw * 512 sa)
+                            acc[m][f][r] = fmaf(raw[f][r] * c1[r], swc[f], acc[m][f][r]);
+                        else if (FP4)  // weight scales inside raw: y += sa * raw
+                            acc[m][f][r] = fmaf(raw[f][r], c1[r] * 0x1p-9f, acc[m][f][r]);
                         else
-                            acc[m][f][r] = fmaf(swc[f], fmaf(raw[f][r], c1[r], c0[r]), (float)acc[m][f][r]);
+                            acc[m][f][r] = fmaf(swc[f], fmaf(raw[f][r], c1[r], c0[r]), acc[m][f][r]);
                     }
             }
         }
@@ -413,9 +425,10 @@ __device__ __forceinline__ void tile_body(const GemmArgs& a, const int L, uint8_
                 s_sum[wn * kTBM + row] = sum;
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
+                // int4 down GEMM: the interleaved operand order; fp4: natural K order
                 const int il = 32 * wn + 16 * j + c16;
                 const int b = il & 7;
-                const int pos = fp8_group_pos(il >> 3) + ((b & 1) ? 4 + (b >> 1) : (b >> 1));
+                const int pos = FP4 ? il : fp8_group_pos(il >> 3) + ((b & 1) ? 4 + (b >> 1) : (b >> 1));
                 s_q[row * kGroup + pos] = (uint8_t)((cc >> (8 * j)) & 0xFFu);
             }
         }
@@ -438,7 +451,7 @@ __device__ __forceinline__ void tile_body(const GemmArgs& a, const int L, uint8_
 }
 
 // Persistent: each workgroup walks the tiles of its XCD's range.
-template <int MODE, bool F64, bool PK>
+template <int MODE, bool PK, bool FP4>
 __global__ __launch_bounds__(kTThreads) void gemm_tile_kernel(GemmArgs a)
 {
     __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
@@ -452,7 +465,7 @@ __global__ __launch_bounds__(kTThreads) void gemm_tile_kernel(GemmArgs a)
         const int L = x * per_xcd + t;
         if (L >= total)
             break;
-        tile_body<MODE, F64, PK>(a, L, smem, &s_expert);
+        tile_body<MODE, PK, FP4>(a, L, smem, &s_expert);
         __syncthreads();  // the next tile's loads overwrite LDS the epilogue may still read
     }
 }
@@ -470,21 +483,23 @@ hipError_t launch_gemm_tile(const GemmArgs& a, int mode, hipStream_t s)
         cus = 256;
     const int64_t wgs = tiles < cus ? tiles : cus;
     const dim3 grid((unsigned)((wgs + 7) / 8 * 8));
-#ifndef W4A8_TILE_F64
-#define W4A8_TILE_F64 0
-#endif
+    if (a.fp4 && !a.packed)
+        return hipErrorInvalidValue;
+    const dim3 block(kTThreads);
     if (mode == TILE_GATEUP) {
-        if (a.packed)
-            hipLaunchKernelGGL((gemm_tile_kernel<TILE_GATEUP, W4A8_TILE_F64 != 0, true>), grid,
-                               dim3(kTThreads), 0, s, a);
+        if (a.fp4)
+            hipLaunchKernelGGL((gemm_tile_kernel<TILE_GATEUP, true, true>), grid, block, 0, s, a);
+        else if (a.packed)
+            hipLaunchKernelGGL((gemm_tile_kernel<TILE_GATEUP, true, false>), grid, block, 0, s, a);
         else
-            hipLaunchKernelGGL((gemm_tile_kernel<TILE_GATEUP, W4A8_TILE_F64 != 0, false>), grid,
-                               dim3(kTThreads), 0, s, a);
+            hipLaunchKernelGGL((gemm_tile_kernel<TILE_GATEUP, false, false>), grid, block, 0, s, a);
     } else {
-        if (a.packed)
-            hipLaunchKernelGGL((gemm_tile_kernel<TILE_DOWN, false, true>), grid, dim3(kTThreads), 0, s, a);
+        if (a.fp4)
+            hipLaunchKernelGGL((gemm_tile_kernel<TILE_DOWN, true, true>), grid, block, 0, s, a);
+        else if (a.packed)
+            hipLaunchKernelGGL((gemm_tile_kernel<TILE_DOWN, true, false>), grid, block, 0, s, a);
         else
-            hipLaunchKernelGGL((gemm_tile_kernel<TILE_DOWN, false, false>), grid, dim3(kTThreads), 0, s, a);
+            hipLaunchKernelGGL((gemm_tile_kernel<TILE_DOWN, false, false>), grid, block, 0, s, a);
     }
     return hipGetLastError();
 }

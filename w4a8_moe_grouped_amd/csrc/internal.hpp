@@ -63,6 +63,7 @@ struct GemmArgs {
     // weights of expert e: w + e*w_estride, scales ws + e*s_estride; row n at
     // n*K/2, n*K/128, or in the prepacked layout if packed (see common.hpp)
     int packed;
+    int fp4;   // prepacked fp4 e2m1 weights; ws then holds UE8M0 dwords
     const uint8_t* w;
     const float* ws;
     int64_t w_estride, s_estride;
@@ -86,9 +87,10 @@ enum TileMode { TILE_DOWN = 0, TILE_GATEUP = 1 };
 hipError_t launch_gemm_tile(const GemmArgs& a, int mode, hipStream_t s);
 
 // ---- weight prepack (prepack.hip) ----
-// [E, N, K/2] int4 + [E, N, K/128] fp32 -> the prepacked layouts (common.hpp)
-hipError_t launch_prepack(const uint8_t* w, const float* ws, int64_t E, int64_t N, int64_t K,
-                          uint8_t* wp, float* sp, hipStream_t s);
+// [E, N, K/2] int4 + [E, N, K/128] fp32 (or fp4 + [E, N, K/32] UE8M0 bytes)
+// -> the prepacked layouts (common.hpp); 4-byte scale elements either way
+hipError_t launch_prepack(const uint8_t* w, const void* ws, int64_t E, int64_t N, int64_t K,
+                          bool shuffle_nibbles, uint8_t* wp, void* sp, hipStream_t s);
 
 // ---- combine (combine.hip) ----
 hipError_t launch_combine(const float* y2, const int32_t* src2dst, const float* topk_w,

@@ -22,7 +22,7 @@ GROUP = 128
 EXPORTS = ("w4a8_version", "w4a8_status_string", "w4a8_quantize_act", "w4a8_gemm",
            "w4a8_moe_align", "w4a8_fused_moe", "w4a8_fused_moe_workspace_layout",
            "w4a8_fused_moe_stage_events", "w4a8_prepack_weights", "w4a8_prepacked_scale_count",
-           "w4a8_fused_moe_prepacked")
+           "w4a8_fused_moe_prepacked", "w4a8_prepack_weights_fp4", "w4a8_fused_moe_fp4_prepacked")
 
 _lock = threading.Lock()
 _lib = None
@@ -61,6 +61,10 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         L.w4a8_fused_moe_prepacked.argtypes = L.w4a8_fused_moe.argtypes
         L.w4a8_prepack_weights.restype = ctypes.c_int
         L.w4a8_prepack_weights.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp]
+        L.w4a8_fused_moe_fp4_prepacked.restype = ctypes.c_int
+        L.w4a8_fused_moe_fp4_prepacked.argtypes = L.w4a8_fused_moe.argtypes
+        L.w4a8_prepack_weights_fp4.restype = ctypes.c_int
+        L.w4a8_prepack_weights_fp4.argtypes = [vp, vp, i64, i64, i64, ctypes.c_int, vp, vp, vp]
         L.w4a8_prepacked_scale_count.restype = ctypes.c_int64
         L.w4a8_prepacked_scale_count.argtypes = [i64, i64, i64]
         L.w4a8_fused_moe_workspace_layout.restype = ctypes.c_int
@@ -153,6 +157,58 @@ def prepack_weights(w: torch.Tensor, w_scales: torch.Tensor):
     _check(load().w4a8_prepack_weights(_ptr(w), _ptr(w_scales), E, N, K, _ptr(wp), _ptr(sp),
                                        _stream(w.device)), "w4a8_prepack_weights")
     return wp, sp
+
+
+FP4_GATE_UP, FP4_DOWN = 0, 1
+
+
+def prepack_weights_fp4(w: torch.Tensor, w_scales: torch.Tensor, role: int):
+    """fp4 e2m1 [E, N, K/2] + UE8M0 uint8 scales [E, N, K/32] -> (packed
+    uint8 [E, N*K/2], packed scale dwords int32 [E, count/E]) in the layout of
+    w4a8_prepack_weights_fp4 (role FP4_GATE_UP for w13, FP4_DOWN for w2)."""
+    _need_cuda(w, w_scales)
+    if w.dim() != 3 or w.dtype != torch.uint8 or not w.is_contiguous() or not w_scales.is_contiguous():
+        raise W4A8Error("w must be a contiguous uint8 [E, N, K/2] tensor")
+    E, N, K2 = w.shape
+    K = 2 * K2
+    cnt = int(load().w4a8_prepacked_scale_count(E, N, K))
+    if cnt < 0 or w_scales.shape != (E, N, K // 32) or w_scales.dtype != torch.uint8:
+        raise W4A8Error("bad weight / scale shapes")
+    wp = torch.empty((E, N * K2), dtype=torch.uint8, device=w.device)
+    sp = torch.empty((E, cnt // E), dtype=torch.int32, device=w.device)
+    _check(load().w4a8_prepack_weights_fp4(_ptr(w), _ptr(w_scales), E, N, K, int(role), _ptr(wp),
+                                           _ptr(sp), _stream(w.device)), "w4a8_prepack_weights_fp4")
+    return wp, sp
+
+
+def fused_moe_fp4(hidden: torch.Tensor, topk_ids: torch.Tensor, topk_weights: torch.Tensor,
+                  expert_begin: int, num_local_experts: int, I: int, prepacked: tuple,
+                  out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """The fused forward on fp4 weights; prepacked = (w13p, s13p, w2p, s2p)
+    from prepack_weights_fp4 (w13 with FP4_GATE_UP, w2 with FP4_DOWN)."""
+    w13p, s13p, w2p, s2p = prepacked
+    _need_cuda(hidden, topk_ids, topk_weights, w13p, s13p, w2p, s2p)
+    T, H = hidden.shape
+    k = topk_ids.shape[1]
+    E = num_local_experts
+    assert hidden.dtype == torch.bfloat16 and topk_ids.dtype == torch.int32 \
+        and topk_weights.dtype == torch.float32
+    assert topk_ids.shape == (T, k) and topk_weights.shape == (T, k)
+    assert w13p.numel() == E * 2 * I * H // 2 and w2p.numel() == E * H * I // 2
+    assert s13p.numel() == load().w4a8_prepacked_scale_count(E, 2 * I, H)
+    assert s2p.numel() == load().w4a8_prepacked_scale_count(E, H, I)
+    for t in (hidden, topk_ids, topk_weights, w13p, s13p, w2p, s2p):
+        assert t.is_contiguous()
+    out = out if out is not None else torch.empty((T, H), dtype=torch.bfloat16, device=hidden.device)
+    if workspace is None:
+        need = fused_moe_workspace_bytes(T, H, k, E, I)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=hidden.device)
+    n = ctypes.c_size_t(workspace.numel())
+    _check(load().w4a8_fused_moe_fp4_prepacked(
+        _ptr(hidden), T, H, _ptr(topk_ids), _ptr(topk_weights), k, expert_begin, E, I,
+        _ptr(w13p), _ptr(s13p), _ptr(w2p), _ptr(s2p), _ptr(out), _ptr(workspace),
+        ctypes.byref(n), _stream(hidden.device)), "w4a8_fused_moe_fp4_prepacked")
+    return out
 
 
 def quantize_act(x: torch.Tensor, out_q: Optional[torch.Tensor] = None,
