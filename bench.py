@@ -68,16 +68,33 @@ def moe_flops(cfg, stats):
 
 
 class Workload:
-    def __init__(self, name, nsets, dev, prepack=True):
+    def __init__(self, name, nsets, dev, prepack=True, fp4=False):
         import torch
         from w4a8_moe_grouped_amd import lib, synth
         self.cfg = cfg = synth.CONFIGS[name]
+        self.fp4 = fp4
         t0 = time.time()
         ids, w = synth.gen_routing(cfg)
         self.stats = synth.routing_stats(cfg, ids)
         put = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
         self.hidden = put(synth.gen_hidden(cfg).view(np.int16)).view(torch.bfloat16)
         self.ids, self.w = put(ids), put(w)
+        self.out = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device=dev)
+        nbytes = lib.fused_moe_workspace_bytes(cfg.T, cfg.H, cfg.topk, cfg.E_local, cfg.I)
+        self.ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        if fp4:
+            # fp4 e2m1 weights with UE8M0 scales, prepacked once (not timed)
+            self.psets = []
+            for st in range(nsets):
+                w13, s13, w2, s2 = (put(a) for a in synth.gen_expert_weights_fp4(cfg, seed=cfg.seed + st))
+                self.psets.append(lib.prepack_weights_fp4(w13, s13, lib.FP4_GATE_UP) +
+                                  lib.prepack_weights_fp4(w2, s2, lib.FP4_DOWN))
+                del w13, s13, w2, s2
+            self.sets = self.psets
+            self.use_packed = True
+            log("[bench] %s fp4: T=%d P=%d A=%d, %d weight set(s), inputs in %.1fs"
+                % (name, cfg.T, self.stats["P"], self.stats["A"], nsets, time.time() - t0))
+            return
         self.sets = []
         for s in range(nsets):
             w13, s13, w2, s2 = synth.gen_expert_weights(cfg, seed=cfg.seed + s)
@@ -87,15 +104,16 @@ class Workload:
         self.psets = [lib.prepack_weights(w13, s13) + lib.prepack_weights(w2, s2)
                       for (w13, s13, w2, s2) in self.sets] if prepack else None
         self.use_packed = prepack
-        self.out = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device=dev)
-        nbytes = lib.fused_moe_workspace_bytes(cfg.T, cfg.H, cfg.topk, cfg.E_local, cfg.I)
-        self.ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
         log("[bench] %s: T=%d P=%d A=%d, %d weight set(s), inputs in %.1fs"
             % (name, cfg.T, self.stats["P"], self.stats["A"], nsets, time.time() - t0))
 
     def step(self, i):
         from w4a8_moe_grouped_amd import lib
         cfg = self.cfg
+        if self.fp4:
+            lib.fused_moe_fp4(self.hidden, self.ids, self.w, cfg.expert_begin, cfg.E_local, cfg.I,
+                              self.psets[i % len(self.psets)], out=self.out, workspace=self.ws)
+            return
         j = i % len(self.sets)
         w13, s13, w2, s2 = self.sets[j]
         lib.fused_moe(self.hidden, self.ids, self.w, cfg.expert_begin, cfg.E_local, w13, s13,
@@ -207,6 +225,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-fp4", action="store_true", help="skip the fp4-weight workloads")
     ap.add_argument("--only", default=None, help="time just this workload (decode/prefill/...)")
     ap.add_argument("--layout", choices=("prepacked", "canonical"), default="prepacked",
                     help="weight layout the timed calls read (prepacked once before timing)")
@@ -306,6 +325,32 @@ def main():
             del p
             torch.cuda.empty_cache()
         result["prefill"] = pre
+
+    if not args.no_fp4 and args.only is None:
+        # the same workloads on fp4 e2m1 weights with per-32-K UE8M0 scales
+        # (weight and scale bytes equal the int4 path's, so the same roofline)
+        fp4 = {}
+        for name, steps, warm, nsets in (("decode", args.steps, args.warmup, 2), ("prefill", 10, 3, 1),
+                                         ("prefill_ep8", 3, 1, 1)):
+            if name != "decode" and args.no_prefill:
+                continue
+            q = Workload(name, nsets=nsets, dev=dev, fp4=True)
+            qu = time_steps(q, steps, warm)
+            qst = stage_breakdown(q, 5 if name == "decode" else 2)
+            ent = {"workload": q.cfg.desc, "us": round(qu, 2), "P": q.stats["P"],
+                   "tflops": round(moe_flops(q.cfg, q.stats) / (qu * 1e-6) / 1e12, 2),
+                   "hbm_gbs": round(moe_bytes(q.cfg, q.stats) / (qu * 1e-6) / 1e9, 1),
+                   "stages_us": {k: round(v, 2) for k, v in qst.items()}}
+            if name == "decode":
+                ent["gate_up_hbm_frac"] = round(gate_up_bytes(q.cfg, q.stats) / (qst["gate_up"] * 1e-6)
+                                                / 1e9 / HBM_PEAK_GBS, 4)
+            else:
+                ent["frac_fp8_peak"] = round(moe_flops(q.cfg, q.stats) / (qu * 1e-6) / 1e12 / FP8_PEAK_TFLOPS, 4)
+            fp4[name] = ent
+            log("[bench] fp4 %s: %s" % (name, ent))
+            del q
+            torch.cuda.empty_cache()
+        result["fp4_weights"] = fp4
 
     if not args.no_cpu_baseline:
         cb = cpu_baseline(primary)

@@ -89,3 +89,42 @@ def test_requant_codes_and_down_output(name):
     assert code_mis <= 1e-3
     assert scale_rel <= 2e-6
     assert y2_fro <= 1e-3
+
+
+@pytest.mark.parametrize("name", ["decode", "tile_small"])
+def test_requant_codes_and_down_output_fp4(name):
+    """The same checks on the fp4-weight path, whose requantised intermediate
+    is stored in natural K order."""
+    assert torch.cuda.is_available()
+    dev = torch.device("cuda:0")
+    if name == "tile_small":
+        cfg, d = synth.random_moe_fp4(512, 256, 256, 8, 2, 0, 4, seed=31)
+    else:
+        cfg = synth.CONFIGS[name]
+        d = synth.gen_moe_fp4(cfg)
+    T, H, I, k, E = cfg.T, cfg.H, cfg.I, cfg.topk, cfg.E_local
+    lay = w4.fused_moe_workspace_layout(T, H, k, E, I)
+    ws = torch.zeros(w4.fused_moe_workspace_bytes(T, H, k, E, I), dtype=torch.uint8, device=dev)
+    hid = dput(d["hidden"].view(np.int16), dev).view(torch.bfloat16)
+    packed = w4.prepack_weights_fp4(dput(d["w13"], dev), dput(d["s13"], dev), w4.FP4_GATE_UP) + \
+        w4.prepack_weights_fp4(dput(d["w2"], dev), dput(d["s2"], dev), w4.FP4_DOWN)
+    w4.fused_moe_fp4(hid, dput(d["topk_ids"], dev), dput(d["topk_weights"], dev), cfg.expert_begin, E, I,
+                     packed, workspace=ws)
+    torch.cuda.synchronize()
+    wsh = ws.cpu().numpy()
+    _, inter = oracle.fused_moe_fp4(d["hidden"], d["topk_ids"], d["topk_weights"], cfg.expert_begin,
+                                    E, d["w13"], d["s13"], d["w2"], d["s2"], intermediates=True)
+    P = inter["qh"].shape[0]
+    GI = I // 128
+    qh = wsh[lay["qh"]:lay["qh"] + P * I].reshape(P, I)
+    side = wsh[lay["qh_side"]:lay["qh_side"] + 8 * P * GI].view(np.float32).reshape(P, GI, 2)
+    y2 = wsh[lay["y2"]:lay["y2"] + 4 * P * H].view(np.float32).reshape(P, H).astype(np.float64)
+    code_mis = np.mean(qh != inter["qh"])
+    scale = side[:, :, 0] / np.float32(512)
+    scale_rel = np.max(np.abs(scale.astype(np.float64) - inter["sh"]) / inter["sh"])
+    y2_fro = np.linalg.norm(y2 - inter["y2"]) / np.linalg.norm(inter["y2"])
+    print("fp4 %s: P=%d code mismatch=%.2e (%d of %d) scale max rel %.1e y2 rel_fro=%.3e"
+          % (name, P, code_mis, int(np.sum(qh != inter["qh"])), qh.size, scale_rel, y2_fro))
+    assert code_mis <= 1e-3
+    assert scale_rel <= 2e-6
+    assert y2_fro <= 1e-3
