@@ -9,7 +9,9 @@ timing, or w4a8_fused_moe with --layout canonical) on the decode workload: T=64 
 I=2048, top-8 of 256 experts, this GPU's share = experts 0..31.  Inputs are
 seeded synthetic data already resident in HBM; successive steps rotate over
 distinct weight sets (>= 1 GB in total, so the weights stream from HBM rather
-than from the 256 MB last-level cache).
+than from the 256 MB last-level cache).  The same calls replayed from HIP
+graphs (one captured call per weight set, as a serving decode loop may run
+them) are reported too.
 
 Printed: one JSON line with the headline (decode µs per call), the roofline
 of the dominant kernel (timed live with HIP events on the library's stream),
@@ -143,6 +145,38 @@ def time_steps(wl, steps, warmup, span=None):
     return us, float(np.mean(span.read_ms())) * 1e3
 
 
+def graph_steps(wl, steps, warmup):
+    """The same steps replayed from HIP graphs (one captured call per weight
+    set, torch.cuda.CUDAGraph): the host's launch overhead leaves the timed
+    region, as in a serving decode loop.  Returns µs per step."""
+    import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for j in range(len(wl.sets)):
+            wl.step(j)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graphs = []
+    for j in range(len(wl.sets)):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            wl.step(j)
+        graphs.append(g)
+    for i in range(warmup):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        graphs[i % len(graphs)].replay()
+    end.record()
+    torch.cuda.synchronize()
+    us = start.elapsed_time(end) * 1e3 / steps
+    del graphs
+    return us
+
+
 def stage_breakdown(wl, steps):
     """Per-stage µs from HIP events the library records on its own stream."""
     import torch
@@ -201,21 +235,119 @@ def copy_calibration(nbytes=1 << 30, reps=4):
     print(json.dumps({"copy_bytes": nbytes, "reps": reps}), flush=True)
 
 
+def _oracle_slices(d, cfg, rows, threads):
+    """The oracle on disjoint token slices, one thread each (the C library
+    releases the GIL; every output row depends only on its own token, so the
+    result equals one single-threaded call on the same rows)."""
+    import concurrent.futures
+    import oracle
+    parts = [p for p in np.array_split(rows, threads) if p.size]
+
+    def run(r):
+        return oracle.fused_moe(d["hidden"][r], d["topk_ids"][r], d["topk_weights"][r],
+                                cfg.expert_begin, cfg.E_local, d["w13"], d["s13"], d["w2"], d["s2"])
+    t0 = time.perf_counter()
+    with concurrent.futures.ThreadPoolExecutor(len(parts)) as ex:
+        list(ex.map(run, parts))
+    return time.perf_counter() - t0, len(parts)
+
+
+def copy_bandwidth(nbytes=1 << 30, reps=10):
+    """GB/s of a plain 1 GiB device-to-device copy (read + write bytes), the
+    box's measured HBM figure printed beside the 8 TB/s datasheet peak."""
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    s = a.elapsed_time(b) * 1e-3 / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * nbytes / s / 1e9
+
+
+def extra_workloads(dev, steps):
+    """The skewed-routing MoE configs and the dense linear: µs and rates."""
+    import torch
+    from w4a8_moe_grouped_amd import lib, synth
+    res = {}
+    for name in ("skew_perm", "skew_id"):
+        q = Workload(name, nsets=2, dev=dev)
+        us = time_steps(q, steps, 5)
+        res[name] = {"workload": q.cfg.desc, "us": round(us, 2), "P": q.stats["P"], "A": q.stats["A"],
+                     "hbm_gbs": round(moe_bytes(q.cfg, q.stats) / (us * 1e-6) / 1e9, 1),
+                     "frac_hbm": round(moe_bytes(q.cfg, q.stats) / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        log("[bench] %s: %s" % (name, res[name]))
+        del q
+    cfg = synth.CONFIGS["dense"]
+    x, w, sw = synth.gen_dense(cfg)
+    put = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    xt = put(x.view(np.int16)).view(torch.bfloat16)
+    wt, swt = put(w), put(sw)
+    q, qs = lib.quantize_act(xt)
+    gws = torch.empty(max(lib.gemm_workspace_bytes(cfg.M, cfg.K, cfg.N), 1), dtype=torch.uint8, device=dev)
+    out = lib.gemm(q, qs, wt, swt, workspace=gws)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        lib.gemm(q, qs, wt, swt, out=out, workspace=gws)
+    b.record()
+    torch.cuda.synchronize()
+    g_us = a.elapsed_time(b) * 1e3 / steps
+    a.record()
+    for _ in range(steps):
+        lib.quantize_act(xt, out_q=q, out_scales=qs)
+    b.record()
+    torch.cuda.synchronize()
+    q_us = a.elapsed_time(b) * 1e3 / steps
+    M, K, N = cfg.M, cfg.K, cfg.N
+    byts = N * K // 2 + N * (K // 128) * 4 + M * K + M * (K // 128) * 4 + M * N * 2
+    res["dense"] = {"workload": cfg.desc, "gemm_us": round(g_us, 2), "quant_us": round(q_us, 2),
+                    "gemm_tflops": round(2.0 * M * N * K / (g_us * 1e-6) / 1e12, 2),
+                    "gemm_hbm_gbs": round(byts / (g_us * 1e-6) / 1e9, 1)}
+    log("[bench] dense: %s" % res["dense"])
+    return res
+
+
 def cpu_baseline(name):
-    """The plain single-threaded C oracle on the full decode workload."""
+    """The plain C oracle (fp64) on the host: the whole decode call on all the
+    host's cores (token slices), the same call single-threaded, and the
+    T=4096 prefill on every 16th token (extrapolated, labelled as such)."""
     import oracle
     from w4a8_moe_grouped_amd import synth
+    oracle.lib()
     cfg = synth.CONFIGS[name]
     d = synth.gen_moe(cfg)
-    oracle.lib()
-    t0 = time.perf_counter()
-    oracle.fused_moe(d["hidden"], d["topk_ids"], d["topk_weights"], cfg.expert_begin,
-                     cfg.E_local, d["w13"], d["s13"], d["w2"], d["s2"])
-    dt = time.perf_counter() - t0
-    return {"value": dt * 1e6, "unit": "µs", "cores": 1, "kind": "oracle",
-            "sample": "the whole %s workload (T=%d, H=%d, I=%d, top-%d, experts 0..%d of %d), "
-                      "one call, single-threaded fp64 C" % (name, cfg.T, cfg.H, cfg.I, cfg.topk,
-                                                           cfg.E_local - 1, cfg.E_total)}
+    # the box's CPU share for one GPU is 16 threads, whatever os.cpu_count() says
+    threads = max(1, min(16, os.cpu_count() or 1, cfg.T))
+    rows = np.arange(cfg.T)
+    t1, _ = _oracle_slices(d, cfg, rows, 1)
+    tn, used = _oracle_slices(d, cfg, rows, threads)
+    out = {"value": round(tn * 1e6, 1), "unit": "µs", "cores": used, "kind": "oracle",
+           "sample": "the whole %s workload (T=%d, H=%d, I=%d, top-%d, experts 0..%d of %d), "
+                     "one call, fp64 C, token slices over %d threads"
+                     % (name, cfg.T, cfg.H, cfg.I, cfg.topk, cfg.E_local - 1, cfg.E_total, used),
+           "single_thread_us": round(t1 * 1e6, 1)}
+    try:
+        import platform
+        out["cpu"] = platform.processor() or platform.machine()
+    except Exception:
+        pass
+    pc = synth.CONFIGS["prefill"]
+    pd = synth.gen_moe(pc)
+    sample = np.arange(0, pc.T, 16)
+    tp, usedp = _oracle_slices(pd, pc, sample, threads)
+    out["prefill_T4096_extrapolated_us"] = round(tp * 16 * 1e6, 1)
+    out["prefill_sample"] = "every 16th token (%d of %d) on %d threads, time x16" % (sample.size, pc.T, usedp)
+    return out
 
 
 def main():
@@ -254,6 +386,7 @@ def main():
     wl = Workload(primary, nsets=2, dev=dev, prepack=packed)
     cfg, st = wl.cfg, wl.stats
     us = time_steps(wl, args.steps, args.warmup)
+    graph_us = graph_steps(wl, args.steps, args.warmup)
     other_us = None
     if packed:  # the same calls on the canonical [E, N, K/2] weights, for comparison
         wl.use_packed = False
@@ -267,9 +400,14 @@ def main():
     span = lib.SpanTimer(2, 3, args.steps)
     _, dom_us = time_steps(wl, args.steps, 0, span=span)
     span.close()
+    # per-call spread: one event pair around each whole call (stage hooks 0 -> 5)
+    whole = lib.SpanTimer(0, 5, args.steps)
+    time_steps(wl, args.steps, 0, span=whole)
+    per_call = np.array(whole.read_ms()) * 1e3
+    whole.close()
     stages = stage_breakdown(wl, max(5, min(args.steps, 20)))
-    log("[bench] %s: %.1f us/call (%s weights), stages %s"
-        % (primary, us, args.layout, {k: round(v, 1) for k, v in stages.items()}))
+    log("[bench] %s: %.1f us/call (%s weights; %.1f us/call replayed from HIP graphs), stages %s"
+        % (primary, us, args.layout, graph_us, {k: round(v, 1) for k, v in stages.items()}))
     if other_us is not None:
         log("[bench] %s: %.1f us/call on the canonical weight layout" % (primary, other_us))
     byts, flops = moe_bytes(cfg, st), moe_flops(cfg, st)
@@ -297,11 +435,18 @@ def main():
                    "experts_total": cfg.E_total, "experts_local": cfg.E_local, "topk": cfg.topk,
                    "local_pairs": st["P"], "active_experts": st["A"], "weight_sets": 2,
                    "weight_layout": args.layout},
+        "timing": "value: K consecutive calls launched back to back between two events; graph_us: "
+                  "the same calls replayed from HIP graphs (one captured call per weight set)",
+        "graph_us": round(graph_us, 2),
         "canonical_layout_us": None if other_us is None else round(other_us, 2),
         "tflops": round(tflops, 2),
         "hbm_gbs": round(gb_s, 1),
         "roofline_frac_call": round(gb_s / HBM_PEAK_GBS, 4),
         "stages_us": {k: round(v, 2) for k, v in stages.items()},
+        "per_call_us": {"median": round(float(np.median(per_call)), 2),
+                        "p10": round(float(np.percentile(per_call, 10)), 2),
+                        "p90": round(float(np.percentile(per_call, 90)), 2), "calls": int(per_call.size)},
+        "hbm_copy_gbs": round(copy_bandwidth(), 1),
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(dom_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
                      "traffic": None if traffic is None else int(traffic),
@@ -325,6 +470,9 @@ def main():
             del p
             torch.cuda.empty_cache()
         result["prefill"] = pre
+
+    if not args.no_prefill and args.only is None:
+        result["other_configs"] = extra_workloads(dev, args.steps)
 
     if not args.no_fp4 and args.only is None:
         # the same workloads on fp4 e2m1 weights with per-32-K UE8M0 scales
