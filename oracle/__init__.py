@@ -74,6 +74,11 @@ def lib():
             L.orc_fused_moe.restype = ctypes.c_int
             L.orc_fused_moe.argtypes = [u16p, i64, i64, i32p, f32p, i64, i64, i64, i64,
                                         u8p, f32p, u8p, f32p, u16p, u8p, f32p, f64p]
+            L.orc_quantize_rows_bf16_static.restype = None
+            L.orc_quantize_rows_bf16_static.argtypes = [u16p, i64, i64, i64, ctypes.c_float, u8p, f32p]
+            L.orc_fused_moe_static.restype = ctypes.c_int
+            L.orc_fused_moe_static.argtypes = [u16p, i64, i64, i32p, f32p, i64, i64, i64, i64,
+                                               u8p, f32p, u8p, f32p, f32p, f32p, u16p, u8p, f32p, f64p]
             L.orc_e2m1_decode.restype = ctypes.c_double
             L.orc_e2m1_decode.argtypes = [ctypes.c_uint8]
             L.orc_ue8m0_decode.restype = ctypes.c_double
@@ -144,6 +149,42 @@ def quantize_bf16(x_bits: np.ndarray):
     lib().orc_quantize_rows_bf16(_p(x, ctypes.c_uint16), M, K, K, _p(codes, ctypes.c_uint8),
                                  _p(scales, ctypes.c_float))
     return codes, scales
+
+
+def quantize_bf16_static(x_bits: np.ndarray, s: float):
+    """bf16 bit patterns [M, K] with a static per-tensor scale s -> (codes, scales)."""
+    x = _c(x_bits, np.uint16)
+    M, K = x.shape
+    codes = np.empty((M, K), np.uint8)
+    scales = np.empty((M, K // 128), np.float32)
+    lib().orc_quantize_rows_bf16_static(_p(x, ctypes.c_uint16), M, K, K, float(np.float32(s)),
+                                        _p(codes, ctypes.c_uint8), _p(scales, ctypes.c_float))
+    return codes, scales
+
+
+def fused_moe_static(hidden_bits, topk_ids, topk_weights, expert_begin, num_local_experts,
+                     w13, s13, w2, s2, a1_scale=None, a2_scale=None):
+    """The forward with static per-tensor activation scales (None = dynamic)."""
+    x = _c(hidden_bits, np.uint16)
+    ids = _c(topk_ids, np.int32)
+    tw = _c(topk_weights, np.float32)
+    w13, w2 = _c(w13, np.uint8), _c(w2, np.uint8)
+    s13, s2 = _c(s13, np.float32), _c(s2, np.float32)
+    T, H = x.shape
+    k = ids.shape[1]
+    I = w2.shape[2] * 2
+    a1 = None if a1_scale is None else np.array([a1_scale], np.float32)
+    a2 = None if a2_scale is None else np.array([a2_scale], np.float32)
+    out = np.empty((T, H), np.uint16)
+    rc = lib().orc_fused_moe_static(_p(x, ctypes.c_uint16), T, H, _p(ids, ctypes.c_int32),
+                                    _p(tw, ctypes.c_float), k, expert_begin, num_local_experts, I,
+                                    _p(w13, ctypes.c_uint8), _p(s13, ctypes.c_float),
+                                    _p(w2, ctypes.c_uint8), _p(s2, ctypes.c_float),
+                                    _p(a1, ctypes.c_float), _p(a2, ctypes.c_float),
+                                    _p(out, ctypes.c_uint16), None, None, None)
+    if rc:
+        raise ValueError("orc_fused_moe_static failed: %d" % rc)
+    return out
 
 
 def quantize_f32(x: np.ndarray):

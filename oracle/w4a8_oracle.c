@@ -170,6 +170,55 @@ void orc_quantize_block(const float* x, uint8_t* codes, float* scale)
     }
 }
 
+/* The static variant: one per-tensor scale s, fixed ahead of time (the input
+ * scales [P2] loads with the weights) instead of each block's amax/448.  The
+ * codes follow the same reciprocal-then-multiply rule with inv = 1/s rounded
+ * once to fp32, and s is every block's dequant scale. */
+void orc_quantize_block_static(const float* x, float s, uint8_t* codes)
+{
+    float inv = 1.0f / s;
+    for (int k = 0; k < ORC_GROUP; ++k) {
+        float p = x[k] * inv;
+        codes[k] = orc_e4m3_encode(p);
+    }
+}
+
+static void quantize_rows_f32_any(const float* x, int64_t M, int64_t K, const float* s,
+                                  uint8_t* codes, float* scales)
+{
+    int64_t G = K / ORC_GROUP;
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t g = 0; g < G; ++g) {
+            if (s) {
+                orc_quantize_block_static(x + m * K + g * ORC_GROUP, *s, codes + m * K + g * ORC_GROUP);
+                scales[m * G + g] = *s;
+            } else {
+                orc_quantize_block(x + m * K + g * ORC_GROUP, codes + m * K + g * ORC_GROUP,
+                                   scales + m * G + g);
+            }
+        }
+}
+
+static void quantize_rows_bf16_any(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                                   const float* s, uint8_t* codes, float* scales)
+{
+    int64_t G = K / ORC_GROUP;
+    float block[ORC_GROUP];
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t g = 0; g < G; ++g) {
+            for (int k = 0; k < ORC_GROUP; ++k)
+                block[k] = (float)orc_bf16_to_double(x[m * ldx + g * ORC_GROUP + k]);
+            quantize_rows_f32_any(block, 1, ORC_GROUP, s, codes + m * K + g * ORC_GROUP,
+                                  scales + m * G + g);
+        }
+}
+
+void orc_quantize_rows_bf16_static(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, float s,
+                                   uint8_t* codes, float* scales)
+{
+    quantize_rows_bf16_any(x, M, K, ldx, &s, codes, scales);
+}
+
 void orc_quantize_rows_f32(const float* x, int64_t M, int64_t K,
                            uint8_t* codes, float* scales)
 {
@@ -356,6 +405,7 @@ static int fused_moe_impl(const uint16_t* hidden, int64_t T, int64_t H,
                           int64_t expert_begin, int64_t num_local_experts, int64_t I,
                           const uint8_t* w13, const void* s13,
                           const uint8_t* w2, const void* s2, int fp4,
+                          const float* a1_scale, const float* a2_scale,
                           uint16_t* out,
                           uint8_t* qh_out, float* sh_out, double* y2_out)
 {
@@ -391,7 +441,7 @@ static int fused_moe_impl(const uint16_t* hidden, int64_t T, int64_t H,
         goto done;
 
     /* 2. dynamic per-token-per-128 quantisation of the hidden states */
-    orc_quantize_rows_bf16(hidden, T, H, H, qx, sx);
+    quantize_rows_bf16_any(hidden, T, H, H, a1_scale, qx, sx);
 
     /* 3.-6. per local pair, in permuted order: gather the token's row,
      * gate_up GEMM, SwiGLU, requantise, down GEMM */
@@ -416,7 +466,7 @@ static int fused_moe_impl(const uint16_t* hidden, int64_t T, int64_t H,
                 h32[i] = (float)hval;
             }
             /* 5. requantise with the same per-128 rule as the input */
-            orc_quantize_rows_f32(h32, 1, I, qh, sh);
+            quantize_rows_f32_any(h32, 1, I, a2_scale, qh, sh);
             if (qh_out)
                 memcpy(qh_out + p * I, qh, (size_t)I);
             if (sh_out)
@@ -469,7 +519,22 @@ int orc_fused_moe(const uint16_t* hidden, int64_t T, int64_t H,
                   uint8_t* qh_out, float* sh_out, double* y2_out)
 {
     return fused_moe_impl(hidden, T, H, topk_ids, topk_weights, topk, expert_begin,
-                          num_local_experts, I, w13, s13, w2, s2, 0, out, qh_out, sh_out, y2_out);
+                          num_local_experts, I, w13, s13, w2, s2, 0, NULL, NULL, out, qh_out, sh_out,
+                          y2_out);
+}
+
+int orc_fused_moe_static(const uint16_t* hidden, int64_t T, int64_t H,
+                         const int32_t* topk_ids, const float* topk_weights, int64_t topk,
+                         int64_t expert_begin, int64_t num_local_experts, int64_t I,
+                         const uint8_t* w13, const float* s13,
+                         const uint8_t* w2, const float* s2,
+                         const float* a1_scale, const float* a2_scale,
+                         uint16_t* out,
+                         uint8_t* qh_out, float* sh_out, double* y2_out)
+{
+    return fused_moe_impl(hidden, T, H, topk_ids, topk_weights, topk, expert_begin,
+                          num_local_experts, I, w13, s13, w2, s2, 0, a1_scale, a2_scale, out, qh_out,
+                          sh_out, y2_out);
 }
 
 int orc_fused_moe_fp4(const uint16_t* hidden, int64_t T, int64_t H,
@@ -483,5 +548,6 @@ int orc_fused_moe_fp4(const uint16_t* hidden, int64_t T, int64_t H,
     if (H % ORC_FP4_BLOCK || I % ORC_FP4_BLOCK)
         return 1;
     return fused_moe_impl(hidden, T, H, topk_ids, topk_weights, topk, expert_begin,
-                          num_local_experts, I, w13, s13, w2, s2, 1, out, qh_out, sh_out, y2_out);
+                          num_local_experts, I, w13, s13, w2, s2, 1, NULL, NULL, out, qh_out, sh_out,
+                          y2_out);
 }

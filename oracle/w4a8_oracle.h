@@ -35,6 +35,9 @@
  *   - gate rows [0, I), up rows [I, 2I) of w13; plain SwiGLU (no clamp).
  *   - top-k weights applied in the combine, after the down GEMM.
  *   - non-local top-k ids are skipped; a token with no local pair outputs +0.
+ *   - static activation scales (the input scales [P2] loads with the
+ *     weights): one per-tensor fp32 s per quantisation point; codes use
+ *     inv = 1/s rounded to fp32, then the same multiply, clamp and rounding.
  *   - fp4 weights: e2m1 and E8M0 as the OCP MX formats define them; nibble
  *     order as for int4; one scale byte per 32 consecutive K of a row
  *     (s [E_l, N, K/32]); activations keep their per-128 fp32 scales.
@@ -72,6 +75,10 @@ void orc_quantize_rows_bf16(const uint16_t* x, int64_t M, int64_t K, int64_t ldx
                             uint8_t* codes, float* scales);
 void orc_quantize_rows_f32(const float* x, int64_t M, int64_t K,
                            uint8_t* codes, float* scales);
+/* static per-tensor scale s: codes = e4m3(clamp(x * fl32(1/s))), scales = s */
+void orc_quantize_block_static(const float* x, float s, uint8_t* codes);
+void orc_quantize_rows_bf16_static(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, float s,
+                                   uint8_t* codes, float* scales);
 
 /* ---- step: routing permutation (align) ---- */
 int orc_moe_align(const int32_t* topk_ids, int64_t T, int64_t topk,
@@ -99,6 +106,17 @@ int orc_fused_moe(const uint16_t* hidden, int64_t T, int64_t H,
                   const uint8_t* w2, const float* s2,
                   uint16_t* out,
                   uint8_t* qh, float* sh, double* y2);
+/* the forward with static per-tensor activation scales: a1_scale for the
+ * hidden states, a2_scale for the SwiGLU output (host pointers to one fp32;
+ * NULL keeps that quantisation dynamic) */
+int orc_fused_moe_static(const uint16_t* hidden, int64_t T, int64_t H,
+                         const int32_t* topk_ids, const float* topk_weights, int64_t topk,
+                         int64_t expert_begin, int64_t num_local_experts, int64_t I,
+                         const uint8_t* w13, const float* s13,
+                         const uint8_t* w2, const float* s2,
+                         const float* a1_scale, const float* a2_scale,
+                         uint16_t* out,
+                         uint8_t* qh, float* sh, double* y2);
 /* the same forward on fp4 weights: s13 [E_l, 2I, H/32], s2 [E_l, H, I/32]
  * UE8M0 bytes; H and I multiples of 128 */
 int orc_fused_moe_fp4(const uint16_t* hidden, int64_t T, int64_t H,

@@ -563,3 +563,66 @@ def test_fp4_fused_matches_brute_force(orc):
             qh, sh = oracle.quantize_f32(h[None, :])
             ref[t] += np.float64(tw[t, j]) * (dequant_fp4(d["w2"][e], d["s2"][e]) @ dequant_rows(qh, sh)[0])
     assert np.array_equal(out, orc.bf16_from_double(ref))
+
+
+# ---------------------------------------------------------------------------
+# static per-tensor activation scales
+# ---------------------------------------------------------------------------
+
+def torch_static_codes(x_bits, s):
+    """torch's RNE e4m3 cast of fl32(x * fl32(1/s)), clamped to +-448 first."""
+    x = synth.bf16_bits_to_f32(x_bits)
+    inv = np.float32(1.0) / np.float32(s)
+    p = np.clip(x * inv, np.float32(-448), np.float32(448)).astype(np.float32)
+    return torch_e4m3_encode(p)
+
+
+def test_static_quant_matches_torch_cast(orc):
+    rng = np.random.default_rng(31)
+    x = synth.to_bf16_bits(rng.normal(size=(6, 384)) * 3.0)
+    for s in (0.0123, 0.5, 1.0 / 448.0, 0.003):
+        codes, scales = orc.quantize_bf16_static(x, s)
+        assert np.array_equal(codes, torch_static_codes(x, s))
+        assert np.all(scales == np.float32(s))
+
+
+def test_static_quant_power_of_two_scale_is_exact(orc):
+    """x = c * 2^-3 for every finite e4m3 value c: x * (1/s) is exactly c."""
+    vals = torch_e4m3_decode(np.arange(0x7F, dtype=np.uint8))
+    c = np.concatenate([vals, -vals[1:]])
+    c = np.resize(c, 256).reshape(2, 128)
+    x = synth.to_bf16_bits(c * 0.125)
+    assert np.array_equal(synth.bf16_bits_to_f32(x).astype(np.float64), c * 0.125)  # exact in bf16
+    codes, _ = orc.quantize_bf16_static(x, 0.125)
+    assert np.array_equal(torch_e4m3_decode(codes), c)
+
+
+def test_fused_static_without_scales_is_dynamic(orc):
+    _, d = synth.random_moe(9, 256, 128, 4, 2, 0, 4, seed=33)
+    a = orc.fused_moe_static(d["hidden"], d["topk_ids"], d["topk_weights"], 0, 4,
+                             d["w13"], d["s13"], d["w2"], d["s2"])
+    b = orc.fused_moe(d["hidden"], d["topk_ids"], d["topk_weights"], 0, 4,
+                      d["w13"], d["s13"], d["w2"], d["s2"])
+    assert np.array_equal(a, b)
+
+
+def test_fused_static_matches_brute_force(orc):
+    _, d = synth.random_moe(7, 256, 128, 8, 2, 0, 5, seed=34)
+    a1, a2 = 0.011, 0.0007
+    out = orc.fused_moe_static(d["hidden"], d["topk_ids"], d["topk_weights"], 0, 5,
+                               d["w13"], d["s13"], d["w2"], d["s2"], a1, a2)
+    x, ids, tw = d["hidden"], d["topk_ids"], d["topk_weights"]
+    A = torch_e4m3_decode(torch_static_codes(x, a1)) * np.float64(np.float32(a1))
+    I, H = 128, 256
+    ref = np.zeros((x.shape[0], H))
+    for t in range(x.shape[0]):
+        for j in range(ids.shape[1]):
+            e = int(ids[t, j])
+            if not 0 <= e < 5:
+                continue
+            y1 = dequant_w(d["w13"][e], d["s13"][e]) @ A[t]
+            h = (y1[:I] / (1.0 + np.exp(-y1[:I])) * y1[I:]).astype(np.float32)
+            hb = np.clip(h * (np.float32(1.0) / np.float32(a2)), np.float32(-448), np.float32(448))
+            hq = torch_e4m3_decode(torch_e4m3_encode(hb.astype(np.float32))) * np.float64(np.float32(a2))
+            ref[t] += np.float64(tw[t, j]) * (dequant_w(d["w2"][e], d["s2"][e]) @ hq)
+    assert np.array_equal(out, orc.bf16_from_double(ref))
