@@ -187,6 +187,18 @@ int w4a8_fused_moe(const void* hidden_bf16, int64_t T, int64_t H,
 int w4a8_prepack_weights(const uint8_t* w_int4, const float* w_scales, int64_t E, int64_t N,
                          int64_t K, uint8_t* w_packed, float* s_packed, hipStream_t stream);
 
+/*
+ * w4a8_prepack_weights_bf16_scales -- w4a8_prepack_weights for checkpoints
+ * that store the int4 weights' per-128 scales as bf16 ([E, N, K/128] bf16,
+ * 2-byte aligned).  Each scale is widened to fp32 (exact), so the prepacked
+ * output equals w4a8_prepack_weights' on the widened scales, and
+ * w4a8_fused_moe_prepacked runs on it unchanged.  Same layout, arguments and
+ * errors as w4a8_prepack_weights.
+ */
+int w4a8_prepack_weights_bf16_scales(const uint8_t* w_int4, const uint16_t* w_scales_bf16, int64_t E,
+                                     int64_t N, int64_t K, uint8_t* w_packed, float* s_packed,
+                                     hipStream_t stream);
+
 /* 4-byte elements of the prepacked scales of E experts of N x K, for both
  * weight formats (host-only; -1 for a bad shape). */
 int64_t w4a8_prepacked_scale_count(int64_t E, int64_t N, int64_t K);
@@ -205,6 +217,29 @@ int w4a8_fused_moe_prepacked(const void* hidden_bf16, int64_t T, int64_t H,
                              const uint8_t* w2_packed, const float* w2_scales_packed,
                              void* out_bf16, void* workspace, size_t* workspace_bytes,
                              hipStream_t stream);
+
+/*
+ * w4a8_fused_moe_prepacked_static -- w4a8_fused_moe_prepacked with static
+ * per-tensor activation scales, as a checkpoint that ships input scales with
+ * its weights provides them (SGLang PR #7762 loads input and weight scales
+ * for the W4AFP8 MoE layers).
+ *   a1_scale  device pointer to one fp32 scale s for the hidden states, or
+ *             NULL for the dynamic per-token-per-128 rule
+ *   a2_scale  the same for the requantised SwiGLU output
+ * With a static s a 128-block's codes are e4m3(clamp(x * inv, +-448)), inv =
+ * 1/s rounded once to fp32, and its dequant scale is s (values beyond
+ * 448*s saturate).  The scales are read on the device when the kernels run,
+ * so a captured graph follows later updates of them.  Same workspace and
+ * errors as w4a8_fused_moe_prepacked, plus UNSUPPORTED for a scale pointer
+ * that is not 4-byte aligned.
+ */
+int w4a8_fused_moe_prepacked_static(const void* hidden_bf16, int64_t T, int64_t H,
+                                    const int32_t* topk_ids, const float* topk_weights, int64_t topk,
+                                    int64_t expert_begin, int64_t num_local_experts, int64_t I,
+                                    const uint8_t* w13_packed, const float* w13_scales_packed,
+                                    const uint8_t* w2_packed, const float* w2_scales_packed,
+                                    const float* a1_scale, const float* a2_scale, void* out_bf16,
+                                    void* workspace, size_t* workspace_bytes, hipStream_t stream);
 
 /*
  * FP4 weights (DeepGEMM PR #53, "Changes": FP8 E4M3 activations x packed FP4

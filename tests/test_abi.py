@@ -181,3 +181,25 @@ def test_fused_moe_fp4_rejects_bad_arguments(L):
     assert f(H=200) == UNSUPPORTED
     assert f(w13=None) == INVALID
     assert f(nbytes=ctypes.c_size_t(16)) == WORKSPACE
+
+
+def test_prepack_bf16_scales_rejects_bad_arguments(L):
+    p = L.w4a8_prepack_weights_bf16_scales
+    other = ctypes.c_void_p(0x2000)
+    args = lambda E=2, N=32, K=256, w=BOGUS, s=BOGUS, wp=other, sp=other: p(w, s, E, N, K, wp, sp, None)
+    assert args(E=0) == INVALID
+    assert args(s=None) == INVALID
+    assert args(N=24) == UNSUPPORTED
+    assert args(s=ctypes.c_void_p(0x1001)) == UNSUPPORTED   # bf16 needs 2-byte alignment
+    assert args(sp=MISALIGNED) == UNSUPPORTED
+    assert args(wp=BOGUS) == INVALID                         # in place
+
+
+def test_fused_moe_static_rejects_bad_arguments(L):
+    n = ctypes.c_size_t(1 << 40)
+    f = lambda H=256, a1=None, a2=None, nbytes=n: L.w4a8_fused_moe_prepacked_static(
+        BOGUS, 4, H, BOGUS, BOGUS, 2, 0, 4, 128, BOGUS, BOGUS, BOGUS, BOGUS, a1, a2, BOGUS, BOGUS,
+        ctypes.byref(nbytes), None)
+    assert f(H=200) == UNSUPPORTED
+    assert f(a1=ctypes.c_void_p(0x1002)) == UNSUPPORTED   # scale pointers need 4-byte alignment
+    assert f(nbytes=ctypes.c_size_t(16)) == WORKSPACE

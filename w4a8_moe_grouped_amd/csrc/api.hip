@@ -184,7 +184,7 @@ int w4a8_quantize_act(const void* x_bf16, int64_t M, int64_t K, int64_t ldx, uin
     if (M == 0)
         return W4A8_OK;
     return hip_status(w4a8::launch_quant_bf16((const uint16_t*)x_bf16, M, K, ldx, q_e4m3, scales,
-                                              nullptr, 0, stream));
+                                              nullptr, 0, nullptr, stream));
 }
 
 int w4a8_gemm(const uint8_t* a_e4m3, const float* a_scales, int64_t M, int64_t K,
@@ -272,7 +272,8 @@ int fused_moe_impl(const void* hidden_bf16, int64_t T, int64_t H, const int32_t*
                    int64_t num_local_experts, int64_t I, const uint8_t* w13_int4,
                    const void* w13_scales, const uint8_t* w2_int4, const void* w2_scales,
                    void* out_bf16, void* workspace, size_t* workspace_bytes, hipStream_t stream,
-                   WeightFormat format)
+                   WeightFormat format, const float* a1_scale = nullptr,
+                   const float* a2_scale = nullptr)
 {
     const bool packed = format != kInt4;
     const int64_t E = num_local_experts;
@@ -308,7 +309,8 @@ int fused_moe_impl(const void* hidden_bf16, int64_t T, int64_t H, const int32_t*
         // few pairs: align and quantisation in one launch (both stage events
         // are recorded after it)
         e = w4a8::launch_align_quant(topk_ids, T, topk, expert_begin, E, p.block_m, p.al, nullptr,
-                                     0, (const uint16_t*)hidden_bf16, H, p.qa, p.qa_side, stream);
+                                     0, (const uint16_t*)hidden_bf16, H, p.qa, p.qa_side, a1_scale,
+                                     stream);
         if (e != hipSuccess)
             return W4A8_ERR_HIP;
         mark(ev, 1, stream);
@@ -319,7 +321,7 @@ int fused_moe_impl(const void* hidden_bf16, int64_t T, int64_t H, const int32_t*
             return W4A8_ERR_HIP;
         mark(ev, 1, stream);
         e = w4a8::launch_quant_bf16((const uint16_t*)hidden_bf16, T, H, H, p.qa, nullptr,
-                                    p.qa_side, 1, stream);
+                                    p.qa_side, 1, a1_scale, stream);
         if (e != hipSuccess)
             return W4A8_ERR_HIP;
     }
@@ -352,6 +354,7 @@ int fused_moe_impl(const void* hidden_bf16, int64_t T, int64_t H, const int32_t*
     g.I = I;
     g.out_q = p.qh;
     g.out_side = p.qh_side;
+    g.requant_scale = a2_scale;
     e = p.tile ? w4a8::launch_gemm_tile(g, w4a8::TILE_GATEUP, stream)
                : w4a8::launch_gemm_skinny(g, w4a8::EPI_SWIGLU_Q, p.block_m, stream);
     if (e != hipSuccess)
@@ -411,6 +414,22 @@ int w4a8_fused_moe_prepacked(const void* hidden_bf16, int64_t T, int64_t H,
                           w2_scales_packed, out_bf16, workspace, workspace_bytes, stream, kInt4Packed);
 }
 
+int w4a8_fused_moe_prepacked_static(const void* hidden_bf16, int64_t T, int64_t H,
+                                    const int32_t* topk_ids, const float* topk_weights, int64_t topk,
+                                    int64_t expert_begin, int64_t num_local_experts, int64_t I,
+                                    const uint8_t* w13_packed, const float* w13_scales_packed,
+                                    const uint8_t* w2_packed, const float* w2_scales_packed,
+                                    const float* a1_scale, const float* a2_scale, void* out_bf16,
+                                    void* workspace, size_t* workspace_bytes, hipStream_t stream)
+{
+    if (((uintptr_t)a1_scale & 3u) != 0 || ((uintptr_t)a2_scale & 3u) != 0)
+        return W4A8_ERR_UNSUPPORTED;
+    return fused_moe_impl(hidden_bf16, T, H, topk_ids, topk_weights, topk, expert_begin,
+                          num_local_experts, I, w13_packed, w13_scales_packed, w2_packed,
+                          w2_scales_packed, out_bf16, workspace, workspace_bytes, stream, kInt4Packed,
+                          a1_scale, a2_scale);
+}
+
 int w4a8_fused_moe_fp4_prepacked(const void* hidden_bf16, int64_t T, int64_t H,
                                  const int32_t* topk_ids, const float* topk_weights, int64_t topk,
                                  int64_t expert_begin, int64_t num_local_experts, int64_t I,
@@ -437,7 +456,28 @@ int w4a8_prepack_weights(const uint8_t* w_int4, const float* w_scales, int64_t E
         return W4A8_ERR_UNSUPPORTED;
     if ((const void*)w_int4 == (const void*)w_packed || (const void*)w_scales == (const void*)s_packed)
         return W4A8_ERR_INVALID_ARG;  // not in place
-    return hip_status(w4a8::launch_prepack(w_int4, w_scales, E, N, K, false, w_packed, s_packed, stream));
+    return hip_status(w4a8::launch_prepack(w_int4, w_scales, E, N, K, false, false, w_packed, s_packed,
+                                           stream));
+}
+
+int w4a8_prepack_weights_bf16_scales(const uint8_t* w_int4, const uint16_t* w_scales_bf16, int64_t E,
+                                     int64_t N, int64_t K, uint8_t* w_packed, float* s_packed,
+                                     hipStream_t stream)
+{
+    if (E < 1 || N <= 0 || K <= 0)
+        return W4A8_ERR_INVALID_ARG;
+    if (w_int4 == nullptr || w_scales_bf16 == nullptr || w_packed == nullptr || s_packed == nullptr)
+        return W4A8_ERR_INVALID_ARG;
+    if (N % 16 != 0 || K % W4A8_GROUP != 0)
+        return W4A8_ERR_UNSUPPORTED;
+    if (!aligned16(w_int4) || !aligned16(w_packed) || ((uintptr_t)w_scales_bf16 & 1u) != 0 ||
+        !aligned16(s_packed))
+        return W4A8_ERR_UNSUPPORTED;
+    if ((const void*)w_int4 == (const void*)w_packed ||
+        (const void*)w_scales_bf16 == (const void*)s_packed)
+        return W4A8_ERR_INVALID_ARG;  // not in place
+    return hip_status(w4a8::launch_prepack(w_int4, w_scales_bf16, E, N, K, false, true, w_packed,
+                                           s_packed, stream));
 }
 
 int w4a8_prepack_weights_fp4(const uint8_t* w_fp4, const uint8_t* w_scales_ue8m0, int64_t E,
@@ -460,7 +500,7 @@ int w4a8_prepack_weights_fp4(const uint8_t* w_fp4, const uint8_t* w_scales_ue8m0
         (const void*)w_scales_ue8m0 == (const void*)s_packed)
         return W4A8_ERR_INVALID_ARG;  // not in place
     return hip_status(w4a8::launch_prepack(w_fp4, w_scales_ue8m0, E, N, K, role == W4A8_FP4_GATE_UP,
-                                           w_packed, s_packed, stream));
+                                           false, w_packed, s_packed, stream));
 }
 
 int64_t w4a8_prepacked_scale_count(int64_t E, int64_t N, int64_t K)

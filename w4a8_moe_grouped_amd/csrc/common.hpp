@@ -200,6 +200,12 @@ __device__ __forceinline__ float recip448(float amax_c)
 {
     return (float)(448.0 / (double)amax_c);
 }
+// 1/s of a static activation scale, rounded once to fp32 (the fp64 quotient
+// of two floats rounds to the correctly rounded fp32 quotient)
+__device__ __forceinline__ float recip_static(float s)
+{
+    return (float)(1.0 / (double)s);
+}
 __device__ __forceinline__ float scale_of(float amax_c)
 {
     return (float)((double)amax_c / 448.0);

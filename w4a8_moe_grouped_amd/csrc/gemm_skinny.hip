@@ -383,6 +383,8 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs a)
                     s_red[wave][16 * t + 4 * q + r] = m;
             }
         __syncthreads();
+        // a static requant scale (per tensor) replaces each row's amax / 448
+        const float* fixed = a.requant_scale;
         float inv[NT][4], scl[NT][4];
 #pragma unroll
         for (int t = 0; t < NT; ++t)
@@ -392,8 +394,8 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs a)
                 const float m = fmaxf(fmaxf(s_red[0][row], s_red[1][row]),
                                       fmaxf(s_red[2][row], s_red[3][row]));
                 const float amax_c = clamp_amax(m);
-                inv[t][r] = recip448(amax_c);
-                scl[t][r] = scale_of(amax_c);
+                inv[t][r] = fixed ? recip_static(*fixed) : recip448(amax_c);
+                scl[t][r] = fixed ? *fixed : scale_of(amax_c);
             }
         // codes, sum of decoded codes, and the interleaved byte position of each i
 #pragma unroll
@@ -430,7 +432,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs a)
                 const float sum = s_red2[0][row] + s_red2[1][row] + s_red2[2][row] + s_red2[3][row];
                 const float m = fmaxf(fmaxf(s_red[0][row], s_red[1][row]),
                                       fmaxf(s_red[2][row], s_red[3][row]));
-                const float sc = scale_of(clamp_amax(m));
+                const float sc = fixed ? *fixed : scale_of(clamp_amax(m));
                 a.out_side[(int64_t)(row0 + row) * GI + blockIdx.x] =
                     make_float2(512.0f * sc, -8.0f * (sc * sum));
             }

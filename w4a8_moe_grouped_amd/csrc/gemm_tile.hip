@@ -417,7 +417,7 @@ __device__ __forceinline__ void tile_body(const GemmArgs& a, const int L, uint8_
             const int row = 64 * wm + 16 * m + 4 * q + r;
             const float mx = fmaxf(fmaxf(s_red[row], s_red[kTBM + row]),
                                    fmaxf(s_red[2 * kTBM + row], s_red[3 * kTBM + row]));
-            const float inv = recip448(clamp_amax(mx));
+            const float inv = a.requant_scale ? recip_static(*a.requant_scale) : recip448(clamp_amax(mx));
             const uint32_t cc = cvt_e4m3x2(h[m][0][r] * inv, h[m][1][r] * inv);
             const float2 dv = dec_e4m3x2(cc);
             const float sum = group_sum<16>(dv.x + dv.y);
@@ -445,7 +445,7 @@ __device__ __forceinline__ void tile_body(const GemmArgs& a, const int L, uint8_
         const float sum = s_sum[row] + s_sum[kTBM + row] + s_sum[2 * kTBM + row] + s_sum[3 * kTBM + row];
         const float mx = fmaxf(fmaxf(s_red[row], s_red[kTBM + row]),
                                fmaxf(s_red[2 * kTBM + row], s_red[3 * kTBM + row]));
-        const float sc = scale_of(clamp_amax(mx));
+        const float sc = a.requant_scale ? *a.requant_scale : scale_of(clamp_amax(mx));
         a.out_side[(int64_t)(row0 + row) * GI + nb] = make_float2(512.0f * sc, -8.0f * (sc * sum));
     }
 }

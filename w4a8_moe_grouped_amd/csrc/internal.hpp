@@ -12,8 +12,11 @@ namespace w4a8 {
 // mode 0: canonical codes + fp32 scales (the public export)
 // mode 1: K-interleaved codes + {c1, c0} side data (the GEMM operand of
 //         every path, converted to f16 in registers by the gate_up GEMMs)
+// fixed_scale: null for the dynamic rule, else a device pointer to a static
+// per-tensor scale
 hipError_t launch_quant_bf16(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
-                             float* scales, float2* side, int mode, hipStream_t s);
+                             float* scales, float2* side, int mode, const float* fixed_scale,
+                             hipStream_t s);
 // canonical codes + scales (from w4a8_quantize_act) -> interleaved codes + side data
 hipError_t launch_prep_codes(const uint8_t* q, const float* scales, int64_t M, int64_t K,
                              uint8_t* q_il, float2* side, hipStream_t s);
@@ -38,7 +41,7 @@ hipError_t launch_align(const int32_t* ids, int64_t T, int64_t topk, int64_t exp
 hipError_t launch_align_quant(const int32_t* ids, int64_t T, int64_t topk, int64_t expert_begin,
                               int64_t E, int64_t block_m, const AlignOut& o, int32_t* clear,
                               int32_t nclear, const uint16_t* x, int64_t H, uint8_t* q,
-                              float2* side, hipStream_t s);
+                              float2* side, const float* fixed_scale, hipStream_t s);
 
 // ---- grouped GEMMs (gemm_skinny.hip) ----
 struct GemmArgs {
@@ -75,6 +78,7 @@ struct GemmArgs {
     uint16_t* out_bf16;    // [rows, N]           (bf16 epilogue)
     uint8_t* out_q;        // [rows, I] codes     (SwiGLU+requant epilogue, interleaved)
     float2* out_side;      // [rows, I/128]
+    const float* requant_scale;  // static per-tensor scale of the requant, or null (dynamic)
     int64_t max_blocks;    // grid bound on m-blocks
 };
 enum Epilogue { EPI_F32 = 0, EPI_BF16 = 1, EPI_SWIGLU_Q = 2 };
@@ -87,10 +91,10 @@ enum TileMode { TILE_DOWN = 0, TILE_GATEUP = 1 };
 hipError_t launch_gemm_tile(const GemmArgs& a, int mode, hipStream_t s);
 
 // ---- weight prepack (prepack.hip) ----
-// [E, N, K/2] int4 + [E, N, K/128] fp32 (or fp4 + [E, N, K/32] UE8M0 bytes)
-// -> the prepacked layouts (common.hpp); 4-byte scale elements either way
+// [E, N, K/2] int4 + [E, N, K/128] fp32 or bf16 scales (or fp4 + [E, N, K/32]
+// UE8M0 bytes) -> the prepacked layouts (common.hpp); 4-byte scale elements
 hipError_t launch_prepack(const uint8_t* w, const void* ws, int64_t E, int64_t N, int64_t K,
-                          bool shuffle_nibbles, uint8_t* wp, void* sp, hipStream_t s);
+                          bool shuffle_nibbles, bool bf16_scales, uint8_t* wp, void* sp, hipStream_t s);
 
 // ---- combine (combine.hip) ----
 hipError_t launch_combine(const float* y2, const int32_t* src2dst, const float* topk_w,

@@ -58,9 +58,10 @@ __global__ __launch_bounds__(256) void prepack_weights_kernel(const uint8_t* __r
     *(v4i*)(wp + i * 16) = v;
 }
 
-// one thread per packed 4-byte scale element (an fp32 scale, or the dword of
-// four UE8M0 bytes); pure data movement
-__global__ __launch_bounds__(256) void prepack_scales_kernel(const uint32_t* __restrict__ ws, int64_t E,
+// one thread per packed 4-byte scale element: an fp32 scale, the dword of
+// four UE8M0 bytes, or (BF16) a bf16 scale widened to fp32, which is exact
+template <bool BF16>
+__global__ __launch_bounds__(256) void prepack_scales_kernel(const void* __restrict__ wsv, int64_t E,
                                                              int64_t N, int64_t K,
                                                              uint32_t* __restrict__ sp)
 {
@@ -78,11 +79,15 @@ __global__ __launch_bounds__(256) void prepack_scales_kernel(const uint32_t* __r
     const int64_t nf = rest % (N / 16);
     const int64_t e = rest / (N / 16);
     const int64_t g = b * 4 + j;
-    sp[i] = g < G ? ws[(e * N + nf * 16 + r) * G + g] : 0u;
+    const int64_t src = (e * N + nf * 16 + r) * G + g;
+    uint32_t v = 0u;
+    if (g < G)
+        v = BF16 ? (uint32_t)((const uint16_t*)wsv)[src] << 16 : ((const uint32_t*)wsv)[src];
+    sp[i] = v;
 }
 
 hipError_t launch_prepack(const uint8_t* w, const void* ws, int64_t E, int64_t N, int64_t K,
-                          bool shuffle_nibbles, uint8_t* wp, void* sp, hipStream_t s)
+                          bool shuffle_nibbles, bool bf16_scales, uint8_t* wp, void* sp, hipStream_t s)
 {
     const int64_t G = K / kGroup;
     const int64_t chunks = E * N * G * 4;
@@ -92,9 +97,11 @@ hipError_t launch_prepack(const uint8_t* w, const void* ws, int64_t E, int64_t N
         hipLaunchKernelGGL(prepack_weights_kernel<true>, wgrid, dim3(256), 0, s, w, E, N, K, wp);
     else if (chunks > 0)
         hipLaunchKernelGGL(prepack_weights_kernel<false>, wgrid, dim3(256), 0, s, w, E, N, K, wp);
-    if (scales > 0)
-        hipLaunchKernelGGL(prepack_scales_kernel, dim3((unsigned)((scales + 255) / 256)), dim3(256), 0,
-                           s, (const uint32_t*)ws, E, N, K, (uint32_t*)sp);
+    const dim3 sgrid((unsigned)((scales + 255) / 256));
+    if (scales > 0 && bf16_scales)
+        hipLaunchKernelGGL(prepack_scales_kernel<true>, sgrid, dim3(256), 0, s, ws, E, N, K, (uint32_t*)sp);
+    else if (scales > 0)
+        hipLaunchKernelGGL(prepack_scales_kernel<false>, sgrid, dim3(256), 0, s, ws, E, N, K, (uint32_t*)sp);
     return hipGetLastError();
 }
 

@@ -19,11 +19,14 @@ namespace w4a8 {
 
 // MODE 0: canonical codes + scales (the public export)
 // MODE 1: K-interleaved codes + {512*s, -8*s*sum(dec)} (the GEMM operand)
+// fixed_scale: null for the dynamic rule; else a static per-tensor scale s
+// (the input scales SGLang PR #7762 loads with the weights): inv = 1/s
+// rounded once to fp32, and s is every block's scale.
 template <int MODE>
 __device__ __forceinline__ void quant_block(const uint16_t* __restrict__ x, int64_t M, int64_t K,
                                             int64_t ldx, uint8_t* __restrict__ q,
                                             float* __restrict__ scales, float2* __restrict__ side,
-                                            int64_t block)
+                                            int64_t block, const float* __restrict__ fixed_scale)
 {
     const int64_t G = K / kGroup;
     const int64_t gid = block * 16 + (threadIdx.x >> 4);
@@ -39,14 +42,20 @@ __device__ __forceinline__ void quant_block(const uint16_t* __restrict__ x, int6
         v[2 * i] = bf16_to_f32((uint16_t)((uint32_t)raw[i] & 0xFFFFu));
         v[2 * i + 1] = bf16_to_f32((uint16_t)((uint32_t)raw[i] >> 16));
     }
-    float amax = 0.0f;
+    float inv, scale;
+    if (fixed_scale != nullptr) {
+        scale = *fixed_scale;
+        inv = recip_static(scale);
+    } else {
+        float amax = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-        amax = fmaxf(amax, fabsf(v[i]));
-    amax = group_max<16>(amax);
-    const float amax_c = clamp_amax(amax);
-    const float inv = recip448(amax_c);
-    const float scale = scale_of(amax_c);
+        for (int i = 0; i < 8; ++i)
+            amax = fmaxf(amax, fabsf(v[i]));
+        amax = group_max<16>(amax);
+        const float amax_c = clamp_amax(amax);
+        inv = recip448(amax_c);
+        scale = scale_of(amax_c);
+    }
 
     uint32_t c[4];
 #pragma unroll

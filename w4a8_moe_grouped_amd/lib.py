@@ -22,7 +22,8 @@ GROUP = 128
 EXPORTS = ("w4a8_version", "w4a8_status_string", "w4a8_quantize_act", "w4a8_gemm",
            "w4a8_moe_align", "w4a8_fused_moe", "w4a8_fused_moe_workspace_layout",
            "w4a8_fused_moe_stage_events", "w4a8_prepack_weights", "w4a8_prepacked_scale_count",
-           "w4a8_fused_moe_prepacked", "w4a8_prepack_weights_fp4", "w4a8_fused_moe_fp4_prepacked")
+           "w4a8_fused_moe_prepacked", "w4a8_prepack_weights_fp4", "w4a8_fused_moe_fp4_prepacked",
+           "w4a8_prepack_weights_bf16_scales", "w4a8_fused_moe_prepacked_static")
 
 _lock = threading.Lock()
 _lib = None
@@ -65,6 +66,11 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         L.w4a8_fused_moe_fp4_prepacked.argtypes = L.w4a8_fused_moe.argtypes
         L.w4a8_prepack_weights_fp4.restype = ctypes.c_int
         L.w4a8_prepack_weights_fp4.argtypes = [vp, vp, i64, i64, i64, ctypes.c_int, vp, vp, vp]
+        L.w4a8_fused_moe_prepacked_static.restype = ctypes.c_int
+        L.w4a8_fused_moe_prepacked_static.argtypes = L.w4a8_fused_moe.argtypes[:13] + [vp, vp] + \
+            L.w4a8_fused_moe.argtypes[13:]
+        L.w4a8_prepack_weights_bf16_scales.restype = ctypes.c_int
+        L.w4a8_prepack_weights_bf16_scales.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp]
         L.w4a8_prepacked_scale_count.restype = ctypes.c_int64
         L.w4a8_prepacked_scale_count.argtypes = [i64, i64, i64]
         L.w4a8_fused_moe_workspace_layout.restype = ctypes.c_int
@@ -142,20 +148,24 @@ def fused_moe_workspace_layout(T: int, H: int, topk: int, num_local_experts: int
 # ---- exports ----------------------------------------------------------------------
 
 def prepack_weights(w: torch.Tensor, w_scales: torch.Tensor):
-    """int4 [E, N, K/2] + fp32 scales [E, N, K/128] -> (packed uint8 [E, N*K/2],
-    packed fp32 scales [E, count/E]) in the layout of w4a8_prepack_weights."""
+    """int4 [E, N, K/2] + fp32 or bf16 scales [E, N, K/128] -> (packed uint8
+    [E, N*K/2], packed fp32 scales [E, count/E]) in the layout of w4a8_prepack_weights."""
     _need_cuda(w, w_scales)
     if w.dim() != 3 or w.dtype != torch.uint8 or not w.is_contiguous() or not w_scales.is_contiguous():
         raise W4A8Error("w must be a contiguous uint8 [E, N, K/2] tensor")
     E, N, K2 = w.shape
     K = 2 * K2
     cnt = int(load().w4a8_prepacked_scale_count(E, N, K))
-    if cnt < 0 or w_scales.shape != (E, N, K // GROUP) or w_scales.dtype != torch.float32:
+    if cnt < 0 or w_scales.shape != (E, N, K // GROUP) or \
+            w_scales.dtype not in (torch.float32, torch.bfloat16):
         raise W4A8Error("bad weight / scale shapes")
     wp = torch.empty((E, N * K2), dtype=torch.uint8, device=w.device)
     sp = torch.empty((E, cnt // E), dtype=torch.float32, device=w.device)
-    _check(load().w4a8_prepack_weights(_ptr(w), _ptr(w_scales), E, N, K, _ptr(wp), _ptr(sp),
-                                       _stream(w.device)), "w4a8_prepack_weights")
+    if w_scales.dtype == torch.bfloat16:  # a checkpoint's bf16 scales, widened exactly
+        fn, name = load().w4a8_prepack_weights_bf16_scales, "w4a8_prepack_weights_bf16_scales"
+    else:
+        fn, name = load().w4a8_prepack_weights, "w4a8_prepack_weights"
+    _check(fn(_ptr(w), _ptr(w_scales), E, N, K, _ptr(wp), _ptr(sp), _stream(w.device)), name)
     return wp, sp
 
 
@@ -366,10 +376,13 @@ class SpanTimer:
 def fused_moe(hidden: torch.Tensor, topk_ids: torch.Tensor, topk_weights: torch.Tensor,
               expert_begin: int, num_local_experts: int, w13: torch.Tensor, s13: torch.Tensor,
               w2: torch.Tensor, s2: torch.Tensor, out: Optional[torch.Tensor] = None,
-              workspace: Optional[torch.Tensor] = None, prepacked: Optional[tuple] = None):
+              workspace: Optional[torch.Tensor] = None, prepacked: Optional[tuple] = None,
+              a1_scale: Optional[torch.Tensor] = None, a2_scale: Optional[torch.Tensor] = None):
     """The fused forward; bf16 [T, H] out.  w13/s13/w2/s2 are the canonical
     weights (they give the shapes); with prepacked = (w13p, s13p, w2p, s2p)
-    from prepack_weights, w4a8_fused_moe_prepacked runs on those instead."""
+    from prepack_weights, w4a8_fused_moe_prepacked runs on those instead, and
+    with static activation scales (one-element fp32 device tensors, either may
+    be None = dynamic) w4a8_fused_moe_prepacked_static."""
     _need_cuda(hidden, topk_ids, topk_weights, w13, s13, w2, s2)
     T, H = hidden.shape
     k = topk_ids.shape[1]
@@ -395,7 +408,18 @@ def fused_moe(hidden: torch.Tensor, topk_ids: torch.Tensor, topk_weights: torch.
         assert s2p.numel() == load().w4a8_prepacked_scale_count(E, H, I)
         fn, name = load().w4a8_fused_moe_prepacked, "w4a8_fused_moe_prepacked"
         ws = (w13p, s13p, w2p, s2p)
+        if a1_scale is not None or a2_scale is not None:
+            for t in (a1_scale, a2_scale):
+                assert t is None or (t.is_cuda and t.dtype == torch.float32 and t.numel() == 1)
+            stat = (_ptr(a1_scale) if a1_scale is not None else None,
+                    _ptr(a2_scale) if a2_scale is not None else None)
+            _check(load().w4a8_fused_moe_prepacked_static(
+                _ptr(hidden), T, H, _ptr(topk_ids), _ptr(topk_weights), k, expert_begin, E, I,
+                _ptr(ws[0]), _ptr(ws[1]), _ptr(ws[2]), _ptr(ws[3]), stat[0], stat[1], _ptr(out),
+                _ptr(workspace), ctypes.byref(n), _stream(hidden.device)), "w4a8_fused_moe_prepacked_static")
+            return out
     else:
+        assert a1_scale is None and a2_scale is None, "static scales need prepacked weights"
         fn, name = load().w4a8_fused_moe, "w4a8_fused_moe"
         ws = (w13, s13, w2, s2)
     _check(fn(_ptr(hidden), T, H, _ptr(topk_ids), _ptr(topk_weights), k, expert_begin, E, I,
