@@ -79,6 +79,14 @@ def lib():
             L.orc_fused_moe_static.restype = ctypes.c_int
             L.orc_fused_moe_static.argtypes = [u16p, i64, i64, i32p, f32p, i64, i64, i64, i64,
                                                u8p, f32p, u8p, f32p, f32p, f32p, u16p, u8p, f32p, f64p]
+            L.orc_quantize_block_n.restype = None
+            L.orc_quantize_block_n.argtypes = [f32p, ctypes.c_int, u8p, f32p]
+            L.orc_gemm_ag_f64.restype = None
+            L.orc_gemm_ag_f64.argtypes = [u8p, f32p, i64, i64, i64, u8p, f32p, u8p, i64, f64p]
+            L.orc_fused_moe_recipe.restype = ctypes.c_int
+            L.orc_fused_moe_recipe.argtypes = [u16p, i64, i64, i32p, f32p, i64, i64, i64, i64,
+                                               ctypes.c_int, u8p, ctypes.c_void_p, u8p, ctypes.c_void_p,
+                                               ctypes.c_int, u16p, u8p, f32p, f64p]
             L.orc_e2m1_decode.restype = ctypes.c_double
             L.orc_e2m1_decode.argtypes = [ctypes.c_uint8]
             L.orc_ue8m0_decode.restype = ctypes.c_double
@@ -185,6 +193,66 @@ def fused_moe_static(hidden_bits, topk_ids, topk_weights, expert_begin, num_loca
     if rc:
         raise ValueError("orc_fused_moe_static failed: %d" % rc)
     return out
+
+
+def quantize_block_n(x: np.ndarray):
+    """One block of n fp32 values -> (codes u8 [n], scale f32)."""
+    x = _c(x, np.float32).ravel()
+    codes = np.empty(x.size, np.uint8)
+    sc = np.empty(1, np.float32)
+    lib().orc_quantize_block_n(_p(x, ctypes.c_float), x.size, _p(codes, ctypes.c_uint8),
+                               _p(sc, ctypes.c_float))
+    return codes, sc[0]
+
+
+def gemm_ag_f64(a, sa, ag, w, sw=None, sb=None) -> np.ndarray:
+    """codes [M, K] with activation scales sa [M, K/ag] x int4 (sw [N, K/128])
+    or fp4 (sb [N, K/32]) weights -> fp64 [M, N]."""
+    a, sa, w = _c(a, np.uint8), _c(sa, np.float32), _c(w, np.uint8)
+    M, K = a.shape
+    N = w.shape[0]
+    assert sa.shape == (M, K // ag) and (sw is None) != (sb is None)
+    swc = None if sw is None else _c(sw, np.float32)
+    sbc = None if sb is None else _c(sb, np.uint8)
+    y = np.empty((M, N), np.float64)
+    lib().orc_gemm_ag_f64(_p(a, ctypes.c_uint8), _p(sa, ctypes.c_float), ag, M, K,
+                          _p(w, ctypes.c_uint8), _p(swc, ctypes.c_float), _p(sbc, ctypes.c_uint8), N,
+                          _p(y, ctypes.c_double))
+    return y
+
+
+def fused_moe_recipe(hidden_bits, topk_ids, topk_weights, expert_begin, num_local_experts,
+                     w13, s13, w2, s2, down_act_group, fp4=False, intermediates=False):
+    """The forward with the down GEMM's input quantised per down_act_group K
+    (128, 64 or 32); int4 (fp32 scales) or fp4 (UE8M0) weights."""
+    x = _c(hidden_bits, np.uint16)
+    ids = _c(topk_ids, np.int32)
+    tw = _c(topk_weights, np.float32)
+    sdt = np.uint8 if fp4 else np.float32
+    w13, w2, s13, s2 = _c(w13, np.uint8), _c(w2, np.uint8), _c(s13, sdt), _c(s2, sdt)
+    T, H = x.shape
+    k = ids.shape[1]
+    E = num_local_experts
+    I = w2.shape[2] * 2
+    out = np.empty((T, H), np.uint16)
+    P = T * k
+    qh = sh = y2 = None
+    if intermediates:
+        qh = np.zeros((max(P, 1), I), np.uint8)
+        sh = np.zeros((max(P, 1), I // down_act_group), np.float32)
+        y2 = np.zeros((max(P, 1), H), np.float64)
+    rc = lib().orc_fused_moe_recipe(_p(x, ctypes.c_uint16), T, H, _p(ids, ctypes.c_int32),
+                                    _p(tw, ctypes.c_float), k, expert_begin, E, I, 1 if fp4 else 0,
+                                    _p(w13, ctypes.c_uint8), s13.ctypes.data, _p(w2, ctypes.c_uint8),
+                                    s2.ctypes.data, int(down_act_group), _p(out, ctypes.c_uint16),
+                                    _p(qh, ctypes.c_uint8), _p(sh, ctypes.c_float), _p(y2, ctypes.c_double))
+    if rc:
+        raise ValueError("orc_fused_moe_recipe failed: %d" % rc)
+    if not intermediates:
+        return out
+    fl = ids.ravel()
+    Pl = int(np.count_nonzero((fl >= expert_begin) & (fl < expert_begin + E)))
+    return out, dict(qh=qh[:Pl], sh=sh[:Pl], y2=y2[:Pl])
 
 
 def quantize_f32(x: np.ndarray):

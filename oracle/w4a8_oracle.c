@@ -155,8 +155,15 @@ uint16_t orc_bf16_from_double(double v)
  *   code   = e4m3(fl32(x * inv)) */
 void orc_quantize_block(const float* x, uint8_t* codes, float* scale)
 {
+    orc_quantize_block_n(x, ORC_GROUP, codes, scale);
+}
+
+/* the same rule over a block of n elements (the finer activation-scale
+ * recipes of [P4]: one scale per 64 or per 32 K) */
+void orc_quantize_block_n(const float* x, int n, uint8_t* codes, float* scale)
+{
     float amax = 0.0f;
-    for (int k = 0; k < ORC_GROUP; ++k) {
+    for (int k = 0; k < n; ++k) {
         float m = fabsf(x[k]);
         if (m > amax)
             amax = m;
@@ -164,7 +171,7 @@ void orc_quantize_block(const float* x, uint8_t* codes, float* scale)
     float amax_c = amax > 1e-10f ? amax : 1e-10f;
     float inv = 448.0f / amax_c;
     *scale = amax_c / 448.0f;
-    for (int k = 0; k < ORC_GROUP; ++k) {
+    for (int k = 0; k < n; ++k) {
         float p = x[k] * inv;
         codes[k] = orc_e4m3_encode(p);
     }
@@ -176,27 +183,38 @@ void orc_quantize_block(const float* x, uint8_t* codes, float* scale)
  * once to fp32, and s is every block's dequant scale. */
 void orc_quantize_block_static(const float* x, float s, uint8_t* codes)
 {
+    orc_quantize_block_static_n(x, ORC_GROUP, s, codes);
+}
+
+void orc_quantize_block_static_n(const float* x, int n, float s, uint8_t* codes)
+{
     float inv = 1.0f / s;
-    for (int k = 0; k < ORC_GROUP; ++k) {
+    for (int k = 0; k < n; ++k) {
         float p = x[k] * inv;
         codes[k] = orc_e4m3_encode(p);
     }
 }
 
-static void quantize_rows_f32_any(const float* x, int64_t M, int64_t K, const float* s,
-                                  uint8_t* codes, float* scales)
+/* rows of K in blocks of n (n divides 128), dynamic or with a static scale */
+static void quantize_rows_f32_n(const float* x, int64_t M, int64_t K, int n, const float* s,
+                                uint8_t* codes, float* scales)
 {
-    int64_t G = K / ORC_GROUP;
+    int64_t G = K / n;
     for (int64_t m = 0; m < M; ++m)
         for (int64_t g = 0; g < G; ++g) {
             if (s) {
-                orc_quantize_block_static(x + m * K + g * ORC_GROUP, *s, codes + m * K + g * ORC_GROUP);
+                orc_quantize_block_static_n(x + m * K + g * n, n, *s, codes + m * K + g * n);
                 scales[m * G + g] = *s;
             } else {
-                orc_quantize_block(x + m * K + g * ORC_GROUP, codes + m * K + g * ORC_GROUP,
-                                   scales + m * G + g);
+                orc_quantize_block_n(x + m * K + g * n, n, codes + m * K + g * n, scales + m * G + g);
             }
         }
+}
+
+static void quantize_rows_f32_any(const float* x, int64_t M, int64_t K, const float* s,
+                                  uint8_t* codes, float* scales)
+{
+    quantize_rows_f32_n(x, M, K, ORC_GROUP, s, codes, scales);
 }
 
 static void quantize_rows_bf16_any(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
@@ -394,6 +412,46 @@ void orc_gemm_fp4_f64(const uint8_t* a, const float* sa, int64_t M, int64_t K,
     free(arow);
 }
 
+/* The GEMM with the activation scales per ag-block of K (ag divides 128;
+ * [P4]'s 128/64 and per-32 activation recipes): each 128-K weight group's sum
+ * splits into its ag-blocks, each block sum promoted with its own activation
+ * scale and the group's weight scale.  Weights: int4 with fp32 scales sw
+ * [N, K/128] (sb NULL), or fp4 with UE8M0 bytes sb [N, K/32] (sw NULL).
+ *   y[m,n] = sum_g sum_{b in g} sa[m,b] * s_w(n,g) * sum_{k in b} a[m,k] * w[n,k] */
+void orc_gemm_ag_f64(const uint8_t* a, const float* sa, int64_t ag, int64_t M, int64_t K,
+                     const uint8_t* w, const float* sw, const uint8_t* sb, int64_t N, double* y)
+{
+    int64_t G = K / ORC_GROUP, NB = K / ag;
+    double* arow = (double*)malloc(sizeof(double) * (size_t)K);
+    if (!arow)
+        return;
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t k = 0; k < K; ++k)
+            arow[k] = orc_e4m3_decode(a[m * K + k]);
+        for (int64_t n = 0; n < N; ++n) {
+            const uint8_t* wrow = w + n * (K / 2);
+            double total = 0.0;
+            for (int64_t g = 0; g < G; ++g)
+                for (int64_t b = g * (ORC_GROUP / ag); b < (g + 1) * (ORC_GROUP / ag); ++b) {
+                    double acc = 0.0;
+                    for (int64_t k = b * ag; k < (b + 1) * ag; ++k) {
+                        double wv;
+                        if (sb)
+                            wv = orc_fp4_value(wrow[k / 2], (int)(k & 1)) *
+                                 orc_ue8m0_decode(sb[n * (K / ORC_FP4_BLOCK) + k / ORC_FP4_BLOCK]);
+                        else
+                            wv = (double)orc_int4_value(wrow[k / 2], (int)(k & 1));
+                        acc += arow[k] * wv;
+                    }
+                    total += acc * (sb ? (double)sa[m * NB + b]
+                                       : (double)sa[m * NB + b] * (double)sw[n * G + g]);
+                }
+            y[m * N + n] = total;
+        }
+    }
+    free(arow);
+}
+
 /* ------------------------------------------------------------------------ */
 /* The fused-MoE forward ([P2] "Cutlass W4A8 MoE" workflow; [P4] "Changes") */
 /* ------------------------------------------------------------------------ */
@@ -405,13 +463,15 @@ static int fused_moe_impl(const uint16_t* hidden, int64_t T, int64_t H,
                           int64_t expert_begin, int64_t num_local_experts, int64_t I,
                           const uint8_t* w13, const void* s13,
                           const uint8_t* w2, const void* s2, int fp4,
-                          const float* a1_scale, const float* a2_scale,
+                          const float* a1_scale, const float* a2_scale, int down_group,
                           uint16_t* out,
                           uint8_t* qh_out, float* sh_out, double* y2_out)
 {
     int64_t E = num_local_experts;
     int64_t F = T * topk;
-    int64_t GH = H / ORC_GROUP, GI = I / ORC_GROUP;
+    int64_t GH = H / ORC_GROUP, GI = I / down_group;
+    if (down_group != 128 && down_group != 64 && down_group != 32)
+        return 1;
     if (T < 0 || H <= 0 || I <= 0 || topk <= 0 || E <= 0 || H % ORC_GROUP || I % ORC_GROUP)
         return 1;
 
@@ -449,7 +509,7 @@ static int fused_moe_impl(const uint16_t* hidden, int64_t T, int64_t H,
         const uint8_t* w13e = w13 + e * (2 * I) * (H / 2);
         const uint8_t* w2e = w2 + e * H * (I / 2);
         const float* s13e = fp4 ? NULL : (const float*)s13 + e * (2 * I) * GH;
-        const float* s2e = fp4 ? NULL : (const float*)s2 + e * H * GI;
+        const float* s2e = fp4 ? NULL : (const float*)s2 + e * H * (I / ORC_GROUP);
         const uint8_t* b13e = fp4 ? (const uint8_t*)s13 + e * (2 * I) * (H / ORC_FP4_BLOCK) : NULL;
         const uint8_t* b2e = fp4 ? (const uint8_t*)s2 + e * H * (I / ORC_FP4_BLOCK) : NULL;
         for (int64_t p = offsets[e]; p < offsets[e + 1]; ++p) {
@@ -466,13 +526,15 @@ static int fused_moe_impl(const uint16_t* hidden, int64_t T, int64_t H,
                 h32[i] = (float)hval;
             }
             /* 5. requantise with the same per-128 rule as the input */
-            quantize_rows_f32_any(h32, 1, I, a2_scale, qh, sh);
+            quantize_rows_f32_n(h32, 1, I, (int)down_group, a2_scale, qh, sh);
             if (qh_out)
                 memcpy(qh_out + p * I, qh, (size_t)I);
             if (sh_out)
                 memcpy(sh_out + p * GI, sh, sizeof(float) * (size_t)GI);
             /* 6. GEMM2: y2 = down(h), H outputs */
-            if (fp4)
+            if (down_group != ORC_GROUP)
+                orc_gemm_ag_f64(qh, sh, down_group, 1, I, w2e, s2e, b2e, H, y2 + p * H);
+            else if (fp4)
                 orc_gemm_fp4_f64(qh, sh, 1, I, w2e, b2e, H, y2 + p * H);
             else
                 orc_gemm_f64(qh, sh, 1, I, w2e, s2e, H, y2 + p * H);
@@ -519,8 +581,8 @@ int orc_fused_moe(const uint16_t* hidden, int64_t T, int64_t H,
                   uint8_t* qh_out, float* sh_out, double* y2_out)
 {
     return fused_moe_impl(hidden, T, H, topk_ids, topk_weights, topk, expert_begin,
-                          num_local_experts, I, w13, s13, w2, s2, 0, NULL, NULL, out, qh_out, sh_out,
-                          y2_out);
+                          num_local_experts, I, w13, s13, w2, s2, 0, NULL, NULL, ORC_GROUP, out, qh_out,
+                          sh_out, y2_out);
 }
 
 int orc_fused_moe_static(const uint16_t* hidden, int64_t T, int64_t H,
@@ -533,8 +595,8 @@ int orc_fused_moe_static(const uint16_t* hidden, int64_t T, int64_t H,
                          uint8_t* qh_out, float* sh_out, double* y2_out)
 {
     return fused_moe_impl(hidden, T, H, topk_ids, topk_weights, topk, expert_begin,
-                          num_local_experts, I, w13, s13, w2, s2, 0, a1_scale, a2_scale, out, qh_out,
-                          sh_out, y2_out);
+                          num_local_experts, I, w13, s13, w2, s2, 0, a1_scale, a2_scale, ORC_GROUP, out,
+                          qh_out, sh_out, y2_out);
 }
 
 int orc_fused_moe_fp4(const uint16_t* hidden, int64_t T, int64_t H,
@@ -548,6 +610,21 @@ int orc_fused_moe_fp4(const uint16_t* hidden, int64_t T, int64_t H,
     if (H % ORC_FP4_BLOCK || I % ORC_FP4_BLOCK)
         return 1;
     return fused_moe_impl(hidden, T, H, topk_ids, topk_weights, topk, expert_begin,
-                          num_local_experts, I, w13, s13, w2, s2, 1, NULL, NULL, out, qh_out, sh_out,
-                          y2_out);
+                          num_local_experts, I, w13, s13, w2, s2, 1, NULL, NULL, ORC_GROUP, out, qh_out,
+                          sh_out, y2_out);
+}
+
+int orc_fused_moe_recipe(const uint16_t* hidden, int64_t T, int64_t H,
+                         const int32_t* topk_ids, const float* topk_weights, int64_t topk,
+                         int64_t expert_begin, int64_t num_local_experts, int64_t I,
+                         int fp4, const uint8_t* w13, const void* s13,
+                         const uint8_t* w2, const void* s2, int down_act_group,
+                         uint16_t* out,
+                         uint8_t* qh_out, float* sh_out, double* y2_out)
+{
+    if (fp4 && (H % ORC_FP4_BLOCK || I % ORC_FP4_BLOCK))
+        return 1;
+    return fused_moe_impl(hidden, T, H, topk_ids, topk_weights, topk, expert_begin,
+                          num_local_experts, I, w13, s13, w2, s2, fp4 ? 1 : 0, NULL, NULL,
+                          down_act_group, out, qh_out, sh_out, y2_out);
 }

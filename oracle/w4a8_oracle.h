@@ -71,12 +71,14 @@ uint16_t orc_bf16_from_double(double v);
 
 /* ---- step: dynamic per-token-per-128 activation quantisation ---- */
 void orc_quantize_block(const float* x, uint8_t* codes, float* scale);
+void orc_quantize_block_n(const float* x, int n, uint8_t* codes, float* scale);
 void orc_quantize_rows_bf16(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                             uint8_t* codes, float* scales);
 void orc_quantize_rows_f32(const float* x, int64_t M, int64_t K,
                            uint8_t* codes, float* scales);
 /* static per-tensor scale s: codes = e4m3(clamp(x * fl32(1/s))), scales = s */
 void orc_quantize_block_static(const float* x, float s, uint8_t* codes);
+void orc_quantize_block_static_n(const float* x, int n, float s, uint8_t* codes);
 void orc_quantize_rows_bf16_static(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, float s,
                                    uint8_t* codes, float* scales);
 
@@ -92,6 +94,10 @@ void orc_gemm_f64(const uint8_t* a, const float* sa, int64_t M, int64_t K,
                   const uint8_t* w, const float* sw, int64_t N, double* y);
 void orc_gemm_bf16(const uint8_t* a, const float* sa, int64_t M, int64_t K,
                    const uint8_t* w, const float* sw, int64_t N, uint16_t* out);
+/* activation scales sa [M, K/ag] per ag-block (ag in {128, 64, 32}); int4
+ * weights with sw [N, K/128] (sb NULL) or fp4 with sb [N, K/32] (sw NULL) */
+void orc_gemm_ag_f64(const uint8_t* a, const float* sa, int64_t ag, int64_t M, int64_t K,
+                     const uint8_t* w, const float* sw, const uint8_t* sb, int64_t N, double* y);
 /* fp4 weights w [N, K/2] (e2m1 nibbles), UE8M0 scales sw [N, K/32] */
 void orc_gemm_fp4_f64(const uint8_t* a, const float* sa, int64_t M, int64_t K,
                       const uint8_t* w, const uint8_t* sw, int64_t N, double* y);
@@ -115,6 +121,17 @@ int orc_fused_moe_static(const uint16_t* hidden, int64_t T, int64_t H,
                          const uint8_t* w13, const float* s13,
                          const uint8_t* w2, const float* s2,
                          const float* a1_scale, const float* a2_scale,
+                         uint16_t* out,
+                         uint8_t* qh, float* sh, double* y2);
+/* the forward with the down GEMM's input quantised per down_act_group
+ * (128, 64 or 32) K instead of 128 ([P4]'s 128/64 and per-32 activation
+ * recipes); int4 (fp4 = 0, fp32 scales) or fp4 (UE8M0) weights; sh [P,
+ * I/down_act_group] */
+int orc_fused_moe_recipe(const uint16_t* hidden, int64_t T, int64_t H,
+                         const int32_t* topk_ids, const float* topk_weights, int64_t topk,
+                         int64_t expert_begin, int64_t num_local_experts, int64_t I,
+                         int fp4, const uint8_t* w13, const void* s13,
+                         const uint8_t* w2, const void* s2, int down_act_group,
                          uint16_t* out,
                          uint8_t* qh, float* sh, double* y2);
 /* the same forward on fp4 weights: s13 [E_l, 2I, H/32], s2 [E_l, H, I/32]

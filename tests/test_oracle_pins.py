@@ -626,3 +626,76 @@ def test_fused_static_matches_brute_force(orc):
             hq = torch_e4m3_decode(torch_e4m3_encode(hb.astype(np.float32))) * np.float64(np.float32(a2))
             ref[t] += np.float64(tw[t, j]) * (dequant_w(d["w2"][e], d["s2"][e]) @ hq)
     assert np.array_equal(out, orc.bf16_from_double(ref))
+
+
+# ---------------------------------------------------------------------------
+# finer activation-scale recipes for the down GEMM (per 64 / per 32 K)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n", [64, 32])
+def test_quant_block_n_equals_128_block_of_repeats(orc, n):
+    """A block of n values repeated to 128 has the same amax: the 128-rule's
+    codes are the n-rule's codes repeated, with the same scale."""
+    rng = np.random.default_rng(n)
+    x = (rng.normal(size=n) * 2).astype(np.float32)
+    codes_n, s_n = orc.quantize_block_n(x)
+    codes_128, s_128 = orc.quantize_f32(np.tile(x, 128 // n)[None, :])
+    assert np.array_equal(np.tile(codes_n, 128 // n), codes_128[0]) and s_n == s_128[0, 0]
+
+
+@pytest.mark.parametrize("ag", [64, 32])
+def test_gemm_ag_matches_dequantised_matmul(orc, ag):
+    rng = np.random.default_rng(ag + 1)
+    M, K, N = 3, 384, 11
+    codes = rng.integers(0, 0x7F, size=(M, K), dtype=np.uint8)
+    codes[rng.uniform(size=codes.shape) < 0.5] |= 0x80
+    sa = rng.uniform(0.001, 0.01, size=(M, K // ag)).astype(np.float32)
+    w = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    sw = rng.uniform(0.002, 0.02, size=(N, K // 128)).astype(np.float32)
+    A = torch_e4m3_decode(codes) * np.repeat(sa.astype(np.float64), ag, axis=1)
+    y = orc.gemm_ag_f64(codes, sa, ag, w, sw=sw)
+    assert np.max(np.abs(y - A @ dequant_w(w, sw).T)) <= 1e-12 * np.max(np.abs(y))
+    sb = rng.integers(115, 125, size=(N, K // 32), dtype=np.uint8)
+    y4 = orc.gemm_ag_f64(codes, sa, ag, w, sb=sb)
+    assert np.max(np.abs(y4 - A @ dequant_fp4(w, sb).T)) <= 1e-12 * np.max(np.abs(y4))
+
+
+def test_gemm_ag_128_and_equal_sub_scales_reduce_to_plain(orc):
+    rng = np.random.default_rng(3)
+    M, K, N = 2, 256, 7
+    codes, sa = orc.quantize_f32(rng.normal(size=(M, K)).astype(np.float32))
+    w = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    sw = rng.uniform(0.002, 0.02, size=(N, K // 128)).astype(np.float32)
+    plain = orc.gemm_f64(codes, sa, w, sw)
+    assert np.array_equal(orc.gemm_ag_f64(codes, sa, 128, w, sw=sw), plain)
+    # the same scale on both 64-halves: the same sums, regrouped (fp64 rounding only)
+    y64 = orc.gemm_ag_f64(codes, np.repeat(sa, 2, axis=1), 64, w, sw=sw)
+    assert np.max(np.abs(y64 - plain)) <= 1e-13 * np.max(np.abs(plain))
+
+
+@pytest.mark.parametrize("ag,fp4", [(64, False), (32, True)])
+def test_fused_recipe_matches_brute_force(orc, ag, fp4):
+    import oracle
+    gen = synth.random_moe_fp4 if fp4 else synth.random_moe
+    _, d = gen(6, 256, 128, 8, 2, 0, 4, seed=50 + ag)
+    out = orc.fused_moe_recipe(d["hidden"], d["topk_ids"], d["topk_weights"], 0, 4,
+                               d["w13"], d["s13"], d["w2"], d["s2"], ag, fp4=fp4)
+    deq = (lambda w, s: dequant_fp4(w, s)) if fp4 else dequant_w
+    x, ids, tw = d["hidden"], d["topk_ids"], d["topk_weights"]
+    qx, sx = oracle.quantize_bf16(x)
+    A = dequant_rows(qx, sx)
+    I = 128
+    ref = np.zeros((x.shape[0], 256))
+    for t in range(x.shape[0]):
+        for j in range(ids.shape[1]):
+            e = int(ids[t, j])
+            if not 0 <= e < 4:
+                continue
+            y1 = deq(d["w13"][e], d["s13"][e]) @ A[t]
+            h = (y1[:I] / (1.0 + np.exp(-y1[:I])) * y1[I:]).astype(np.float32)
+            hq = np.empty(I)
+            for b in range(I // ag):
+                c, sc = oracle.quantize_block_n(h[b * ag:(b + 1) * ag])
+                hq[b * ag:(b + 1) * ag] = torch_e4m3_decode(c) * np.float64(sc)
+            ref[t] += np.float64(tw[t, j]) * (deq(d["w2"][e], d["s2"][e]) @ hq)
+    assert np.array_equal(out, orc.bf16_from_double(ref))
