@@ -242,6 +242,30 @@ int w4a8_fused_moe_prepacked_static(const void* hidden_bf16, int64_t T, int64_t 
                                     void* workspace, size_t* workspace_bytes, hipStream_t stream);
 
 /*
+ * w4a8_fused_moe_recipe -- the fused forward with a finer dynamic activation
+ * scale for the down GEMM's input (DeepGEMM PR #53 commit notes: the per-32
+ * recipe and the 128/64 recipe): the SwiGLU output is requantised with one
+ * scale per down_act_group K (128, 64 or 32) and the down GEMM promotes each
+ * such block with its own scale; the gate_up input keeps per-128 scales.
+ *   weight_format   W4A8_WEIGHTS_INT4_PACKED (w4a8_prepack_weights output,
+ *                   fp32 scales) or W4A8_WEIGHTS_FP4_PACKED
+ *                   (w4a8_prepack_weights_fp4 output, UE8M0 dwords)
+ *   down_act_group  128, 64 or 32
+ * Other arguments, workspace and errors as w4a8_fused_moe_prepacked
+ * (INVALID_ARG for an unknown format or group).  With a group below 128 the
+ * call runs on the few-rows-per-expert GEMM at every size, and the side data
+ * at offsets[10] is [T*topk, I/down_act_group].
+ */
+#define W4A8_WEIGHTS_INT4_PACKED 1
+#define W4A8_WEIGHTS_FP4_PACKED 2
+int w4a8_fused_moe_recipe(const void* hidden_bf16, int64_t T, int64_t H, const int32_t* topk_ids,
+                          const float* topk_weights, int64_t topk, int64_t expert_begin,
+                          int64_t num_local_experts, int64_t I, int weight_format,
+                          const uint8_t* w13_packed, const void* w13_scales_packed,
+                          const uint8_t* w2_packed, const void* w2_scales_packed, int down_act_group,
+                          void* out_bf16, void* workspace, size_t* workspace_bytes, hipStream_t stream);
+
+/*
  * FP4 weights (DeepGEMM PR #53, "Changes": FP8 E4M3 activations x packed FP4
  * E2M1 expert weights with per-32-K UE8M0 weight scales).  Canonical input
  * layout: w_fp4 [E, N, K/2] e2m1 codes, two per byte, k even in the low
@@ -312,7 +336,8 @@ int w4a8_fused_moe_fp4_prepacked(const void* hidden_bf16, int64_t T, int64_t H,
  *               byte 16*(4*((b%4)/2) + b/4) + 8*(b%2), in K order
  *               k0,k2,k4,k6,k1,k3,k5,k7
  *   offsets[10] float2 [T*topk, I/128] {512*scale, -8*scale*sum of the block's
- *               decoded codes}
+ *               decoded codes} ([T*topk, I/g] under w4a8_fused_moe_recipe with
+ *               a group g of 64 or 32; the region has room for I/32)
  *   offsets[11] down output fp32 [T*topk, H] (pair rows in permuted order)
  * n must be 12; *block_m receives the m-block height the call uses.
  */

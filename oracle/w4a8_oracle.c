@@ -422,6 +422,12 @@ void orc_gemm_ag_f64(const uint8_t* a, const float* sa, int64_t ag, int64_t M, i
                      const uint8_t* w, const float* sw, const uint8_t* sb, int64_t N, double* y)
 {
     int64_t G = K / ORC_GROUP, NB = K / ag;
+    /* the fp4 codecs tabulated once, for speed only */
+    double vtab[16], stab[256];
+    for (int c = 0; c < 16; ++c)
+        vtab[c] = orc_e2m1_decode((uint8_t)c);
+    for (int e = 0; e < 256; ++e)
+        stab[e] = orc_ue8m0_decode((uint8_t)e);
     double* arow = (double*)malloc(sizeof(double) * (size_t)K);
     if (!arow)
         return;
@@ -437,8 +443,8 @@ void orc_gemm_ag_f64(const uint8_t* a, const float* sa, int64_t ag, int64_t M, i
                     for (int64_t k = b * ag; k < (b + 1) * ag; ++k) {
                         double wv;
                         if (sb)
-                            wv = orc_fp4_value(wrow[k / 2], (int)(k & 1)) *
-                                 orc_ue8m0_decode(sb[n * (K / ORC_FP4_BLOCK) + k / ORC_FP4_BLOCK]);
+                            wv = vtab[(k & 1) ? (wrow[k / 2] >> 4) : (wrow[k / 2] & 0xF)] *
+                                 stab[sb[n * (K / ORC_FP4_BLOCK) + k / ORC_FP4_BLOCK]];
                         else
                             wv = (double)orc_int4_value(wrow[k / 2], (int)(k & 1));
                         acc += arow[k] * wv;

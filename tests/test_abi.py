@@ -203,3 +203,16 @@ def test_fused_moe_static_rejects_bad_arguments(L):
     assert f(H=200) == UNSUPPORTED
     assert f(a1=ctypes.c_void_p(0x1002)) == UNSUPPORTED   # scale pointers need 4-byte alignment
     assert f(nbytes=ctypes.c_size_t(16)) == WORKSPACE
+
+
+def test_fused_moe_recipe_rejects_bad_arguments(L):
+    n = ctypes.c_size_t(1 << 40)
+    f = lambda fmt=1, group=64, nbytes=n: L.w4a8_fused_moe_recipe(
+        BOGUS, 4, 256, BOGUS, BOGUS, 2, 0, 4, 128, fmt, BOGUS, BOGUS, BOGUS, BOGUS, group, BOGUS,
+        BOGUS, ctypes.byref(nbytes), None)
+    assert f(fmt=0) == INVALID       # canonical weights are not a recipe format
+    assert f(fmt=3) == INVALID
+    assert f(group=48) == INVALID
+    assert f(group=16) == INVALID
+    assert f(nbytes=ctypes.c_size_t(16)) == WORKSPACE
+    assert f(group=32, nbytes=ctypes.c_size_t(16)) == WORKSPACE

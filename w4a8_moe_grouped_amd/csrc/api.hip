@@ -81,11 +81,13 @@ struct MoePlan {
     int32_t* block_start;
 };
 
-size_t plan_moe(void* ws, int64_t T, int64_t H, int64_t topk, int64_t E, int64_t I, MoePlan& p)
+// down_group < 128 (the finer activation recipes) runs on the skinny kernel
+size_t plan_moe(void* ws, int64_t T, int64_t H, int64_t topk, int64_t E, int64_t I, MoePlan& p,
+                int down_group = W4A8_GROUP)
 {
     Carve c(ws);
     p.F = T * topk;
-    p.tile = use_tile(p.F, E);
+    p.tile = down_group == W4A8_GROUP && use_tile(p.F, E);
     p.block_m = p.tile ? w4a8::kTileRows : pick_block_m(p.F, E);
     p.nb_max = ceil_div(p.F, p.block_m) + E;
     p.al.counts = c.take<int32_t>(E);
@@ -99,7 +101,9 @@ size_t plan_moe(void* ws, int64_t T, int64_t H, int64_t topk, int64_t E, int64_t
     p.qa = c.take<uint8_t>(T * H);  // fp8 gate_up operand
     p.qa_side = c.take<float2>(T * (H / W4A8_GROUP));
     p.qh = c.take<uint8_t>(p.F * I);
-    p.qh_side = c.take<float2>(p.F * (I / W4A8_GROUP));
+    // side data of the requantised intermediate: room for the finest recipe
+    // (one block per 32 K), whatever the call uses
+    p.qh_side = c.take<float2>(p.F * (I / 32));
     p.y2 = c.take<float>(p.F * H);
     p.al.block_start = c.take<int32_t>(E + 1);
     p.block_start = p.al.block_start;
@@ -143,10 +147,11 @@ inline void mark(void* const* ev, int i, hipStream_t s)
         (void)hipEventRecord((hipEvent_t)ev[i], s);
 }
 
-// largest K the skinny GEMM stages per-row side data for (LDS budget 48 KB)
-bool skinny_k_ok(int64_t K, int block_m)
+// largest K the skinny GEMM stages per-row side data for (LDS budget 48 KB),
+// with `group` K per activation scale
+bool skinny_k_ok(int64_t K, int block_m, int64_t group = W4A8_GROUP)
 {
-    return (K / W4A8_GROUP) * block_m * 8 <= 48 * 1024;
+    return (K / group) * block_m * 8 <= 48 * 1024;
 }
 
 }  // namespace
@@ -218,6 +223,7 @@ int w4a8_gemm(const uint8_t* a_e4m3, const float* a_scales, int64_t M, int64_t K
     if (e != hipSuccess)
         return W4A8_ERR_HIP;
     w4a8::GemmArgs g = {};
+    g.sub_group = W4A8_GROUP;
     g.act = q_il;
     g.act_rows = M;
     g.act_side = side;
@@ -273,9 +279,13 @@ int fused_moe_impl(const void* hidden_bf16, int64_t T, int64_t H, const int32_t*
                    const void* w13_scales, const uint8_t* w2_int4, const void* w2_scales,
                    void* out_bf16, void* workspace, size_t* workspace_bytes, hipStream_t stream,
                    WeightFormat format, const float* a1_scale = nullptr,
-                   const float* a2_scale = nullptr)
+                   const float* a2_scale = nullptr, int down_group = W4A8_GROUP)
 {
     const bool packed = format != kInt4;
+    if (down_group != 128 && down_group != 64 && down_group != 32)
+        return W4A8_ERR_INVALID_ARG;
+    if (down_group != W4A8_GROUP && !packed)
+        return W4A8_ERR_UNSUPPORTED;  // the finer recipes read prepacked weights
     const int64_t E = num_local_experts;
     if (T < 0 || H <= 0 || I <= 0 || topk < 1 || E < 1)
         return W4A8_ERR_INVALID_ARG;
@@ -283,8 +293,8 @@ int fused_moe_impl(const void* hidden_bf16, int64_t T, int64_t H, const int32_t*
         E > kMaxLocalExperts || T * topk > INT32_MAX / 2)
         return W4A8_ERR_UNSUPPORTED;
     MoePlan p;
-    const size_t need = plan_moe(nullptr, T, H, topk, E, I, p);
-    if (!p.tile && (!skinny_k_ok(H, p.block_m) || !skinny_k_ok(I, p.block_m)))
+    const size_t need = plan_moe(nullptr, T, H, topk, E, I, p, down_group);
+    if (!p.tile && (!skinny_k_ok(H, p.block_m) || !skinny_k_ok(I, p.block_m, down_group)))
         return W4A8_ERR_UNSUPPORTED;
     const int ws_rc = check_workspace(workspace, workspace_bytes, need);
     if (ws_rc >= 0)
@@ -301,7 +311,7 @@ int fused_moe_impl(const void* hidden_bf16, int64_t T, int64_t H, const int32_t*
     t_stage_events = nullptr;
     if (T == 0)
         return W4A8_OK;
-    plan_moe(workspace, T, H, topk, E, I, p);
+    plan_moe(workspace, T, H, topk, E, I, p, down_group);
 
     mark(ev, 0, stream);
     hipError_t e;
@@ -328,6 +338,7 @@ int fused_moe_impl(const void* hidden_bf16, int64_t T, int64_t H, const int32_t*
     mark(ev, 2, stream);
 
     w4a8::GemmArgs g = {};
+    g.sub_group = W4A8_GROUP;
     g.block_expert = p.al.block_expert;
     g.block_row = p.al.block_row;
     g.num_blocks = p.al.num_blocks;
@@ -355,6 +366,7 @@ int fused_moe_impl(const void* hidden_bf16, int64_t T, int64_t H, const int32_t*
     g.out_q = p.qh;
     g.out_side = p.qh_side;
     g.requant_scale = a2_scale;
+    g.sub_group = down_group;
     e = p.tile ? w4a8::launch_gemm_tile(g, w4a8::TILE_GATEUP, stream)
                : w4a8::launch_gemm_skinny(g, w4a8::EPI_SWIGLU_Q, p.block_m, stream);
     if (e != hipSuccess)
@@ -428,6 +440,22 @@ int w4a8_fused_moe_prepacked_static(const void* hidden_bf16, int64_t T, int64_t 
                           num_local_experts, I, w13_packed, w13_scales_packed, w2_packed,
                           w2_scales_packed, out_bf16, workspace, workspace_bytes, stream, kInt4Packed,
                           a1_scale, a2_scale);
+}
+
+int w4a8_fused_moe_recipe(const void* hidden_bf16, int64_t T, int64_t H, const int32_t* topk_ids,
+                          const float* topk_weights, int64_t topk, int64_t expert_begin,
+                          int64_t num_local_experts, int64_t I, int weight_format,
+                          const uint8_t* w13_packed, const void* w13_scales_packed,
+                          const uint8_t* w2_packed, const void* w2_scales_packed, int down_act_group,
+                          void* out_bf16, void* workspace, size_t* workspace_bytes, hipStream_t stream)
+{
+    if (weight_format != W4A8_WEIGHTS_INT4_PACKED && weight_format != W4A8_WEIGHTS_FP4_PACKED)
+        return W4A8_ERR_INVALID_ARG;
+    return fused_moe_impl(hidden_bf16, T, H, topk_ids, topk_weights, topk, expert_begin,
+                          num_local_experts, I, w13_packed, w13_scales_packed, w2_packed,
+                          w2_scales_packed, out_bf16, workspace, workspace_bytes, stream,
+                          weight_format == W4A8_WEIGHTS_FP4_PACKED ? kFp4Packed : kInt4Packed,
+                          nullptr, nullptr, down_act_group);
 }
 
 int w4a8_fused_moe_fp4_prepacked(const void* hidden_bf16, int64_t T, int64_t H,

@@ -33,14 +33,23 @@ constexpr int kWaves = 4;
 // with UE8M0 scale dwords (DeepGEMM PR #53, Changes): the f16 path converts
 // them exactly with the lane's relative block scale, the fp8 path hands them
 // to the scaled MFMA with the lane's block scale.
-template <int NT, int EPI, int DW, bool F16, bool SW4, bool PK, bool FP4, int NF>
+//
+// SG: the finer activation-scale recipes of DeepGEMM PR #53 (one dynamic scale
+// per 64 or 32 K of the down GEMM's input instead of 128).  The SwiGLU
+// epilogue then emits SG-blocks, and the down GEMM splits each 128-K group into
+// 128/SG lane-masked MFMAs, each promoted with its own block scale.
+template <int NT, int EPI, int DW, bool F16, bool SW4, bool PK, bool FP4, int NF, int SG>
 __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs a)
 {
     constexpr int kNF = NF;
+    static_assert(SG == 128 || SG == 64 || SG == 32, "activation block of 128, 64 or 32 K");
+    static_assert(SG == 128 || EPI != EPI_BF16, "the dense GEMM keeps per-128 scales");
+    constexpr int ASPG = EPI == EPI_F32 ? 128 / SG : 1;       // A-side scale blocks per group
+    constexpr int OSPG = EPI == EPI_SWIGLU_Q ? 128 / SG : 1;  // requant blocks per 128 i
     static_assert(EPI != EPI_SWIGLU_Q || NF == 4, "the SwiGLU tile pairs 2 gate and 2 up fragments");
     static_assert(!FP4 || PK, "fp4 weights are read in the prepacked layout only");
     constexpr int BM = 16 * NT;
-    extern __shared__ float4 lds_side4[];  // [G][BM] float2 {c1, c0}, 16-byte aligned
+    extern __shared__ float4 lds_side4[];  // [G * ASPG][BM] float2 {c1, c0}, 16-byte aligned
     float2* lds_side = (float2*)lds_side4;
     __shared__ float s_red[kWaves][BM];
     __shared__ float s_red2[kWaves][BM];
@@ -111,11 +120,11 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs a)
     // does not wait for the ring.
     constexpr int kSidePer = 8;  // side loads per thread held in registers
     float2 side_v[kSidePer];
-    const int nside = G * BM;
+    const int nside = G * ASPG * BM;
     const bool side_in_regs = nside <= 256 * kSidePer;
     auto side_of = [&](int i) {
-        const int g = i / BM, c = i - g * BM;
-        return c < rows ? a.act_side[(int64_t)act_row(c) * G + g] : make_float2(0.0f, 0.0f);
+        const int gb = i / BM, c = i - gb * BM;
+        return c < rows ? a.act_side[(int64_t)act_row(c) * (G * ASPG) + gb] : make_float2(0.0f, 0.0f);
     };
     if (side_in_regs) {
 #pragma unroll
@@ -285,6 +294,47 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs a)
                         for (int f = 0; f < kNF; ++f)
                             raw[f] = mfma16x16x32_f16(
                                 ah[c], fp8x8_to_f16((uint32_t)b8[f][2 * c], (uint32_t)b8[f][2 * c + 1]), raw[f]);
+                } else if (ASPG > 1) {
+                    // finer activation scales: one masked MFMA per SG-block of
+                    // the group, each promoted with its own {c1, c0}.  The
+                    // lane's A dwords hold K (real order) of one 32-block q
+                    // (int4 operand order) or of [16q, 16q+16) and
+                    // [64+16q, 64+16q+16) (fp4, natural order).
+                    v8i b8[kNF];
+                    int eq[kNF];
+#pragma unroll
+                    for (int f = 0; f < kNF; ++f) {
+                        if (FP4)
+                            eq[f] = (int)((__builtin_bit_cast(uint32_t, swf[f]) >> (8 * q)) & 0xFFu);
+                        else
+                            b8[f] = unpack_int4_u(wb[s][f]);
+                    }
+#pragma unroll
+                    for (int b = 0; b < ASPG; ++b) {
+                        const float4* sdb = (const float4*)&lds_side[(gl * ASPG + b) * BM + 16 * t + 4 * q];
+                        const float4 b01 = sdb[0], b23 = sdb[1];
+                        const float c1b[4] = {b01.x, b01.z, b23.x, b23.z};
+                        const float c0b[4] = {b01.y, b01.w, b23.y, b23.w};
+                        v8i av;
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) {
+                            const int kb = FP4 ? (i < 4 ? 16 * q : 64 + 16 * q) : 32 * q;
+                            av[i] = kb / SG == b ? (int)at[i] : 0;
+                        }
+#pragma unroll
+                        for (int f = 0; f < kNF; ++f) {
+                            const v4f rb = FP4 ? mfma16x16x128_fp4(av, wb[s][f], eq[f])
+                                               : mfma16x16x128(av, b8[f], v4f{0.0f, 0.0f, 0.0f, 0.0f});
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) {
+                                if (FP4)
+                                    acc[f][t][r] = fmaf(rb[r], g < G ? c1b[r] * 0x1p-9f : 0.0f, acc[f][t][r]);
+                                else
+                                    acc[f][t][r] = fmaf(swf[f], fmaf(rb[r], c1b[r], c0b[r]), acc[f][t][r]);
+                            }
+                        }
+                    }
+                    continue;
                 } else {
                     v8i av;
 #pragma unroll
@@ -383,17 +433,32 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs a)
                     s_red[wave][16 * t + 4 * q + r] = m;
             }
         __syncthreads();
-        // a static requant scale (per tensor) replaces each row's amax / 448
+        // a static requant scale (per tensor) replaces each row's amax / 448.
+        // The requant blocks are SG i's: waves [ob*SG/32, (ob+1)*SG/32) of
+        // block ob (a wave's 32 i's never straddle two blocks).
         const float* fixed = a.requant_scale;
+        constexpr int kWB = SG / 32;  // waves per requant block
+        auto block_amax = [&](int ob, int row) {
+            float m = s_red[ob * kWB][row];
+#pragma unroll
+            for (int w = 1; w < kWB; ++w)
+                m = fmaxf(m, s_red[ob * kWB + w][row]);
+            return m;
+        };
+        auto block_sum = [&](int ob, int row) {
+            float sm = s_red2[ob * kWB][row];
+#pragma unroll
+            for (int w = 1; w < kWB; ++w)
+                sm += s_red2[ob * kWB + w][row];
+            return sm;
+        };
         float inv[NT][4], scl[NT][4];
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int row = 16 * t + 4 * q + r;
-                const float m = fmaxf(fmaxf(s_red[0][row], s_red[1][row]),
-                                      fmaxf(s_red[2][row], s_red[3][row]));
-                const float amax_c = clamp_amax(m);
+                const float amax_c = clamp_amax(block_amax(wave / kWB, row));
                 inv[t][r] = fixed ? recip_static(*fixed) : recip448(amax_c);
                 scl[t][r] = fixed ? *fixed : scale_of(amax_c);
             }
@@ -418,7 +483,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs a)
                 }
             }
         __syncthreads();
-        const int64_t GI = a.I / kGroup;
+        const int64_t GI = a.I / SG;  // requant blocks per row
         for (int i = tid; i < BM * 8; i += 256) {
             const int row = i >> 3, chunk = i & 7;
             if (row < rows) {
@@ -427,24 +492,23 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs a)
                     *(const v4i*)(s_q + row * kGroup + chunk * 16);
             }
         }
-        for (int row = tid; row < BM; row += 256) {
+        for (int i = tid; i < BM * OSPG; i += 256) {
+            const int row = i / OSPG, ob = i - row * OSPG;
             if (row < rows) {
-                const float sum = s_red2[0][row] + s_red2[1][row] + s_red2[2][row] + s_red2[3][row];
-                const float m = fmaxf(fmaxf(s_red[0][row], s_red[1][row]),
-                                      fmaxf(s_red[2][row], s_red[3][row]));
-                const float sc = fixed ? *fixed : scale_of(clamp_amax(m));
-                a.out_side[(int64_t)(row0 + row) * GI + blockIdx.x] =
+                const float sum = block_sum(ob, row);
+                const float sc = fixed ? *fixed : scale_of(clamp_amax(block_amax(ob, row)));
+                a.out_side[(int64_t)(row0 + row) * GI + (int64_t)blockIdx.x * OSPG + ob] =
                     make_float2(512.0f * sc, -8.0f * (sc * sum));
             }
         }
     }
 }
 
-template <int NT, int EPI, int DW, bool F16, bool SW4, bool PK, bool FP4, int NF = 4>
+template <int NT, int EPI, int DW, bool F16, bool SW4, bool PK, bool FP4, int NF = 4, int SG = 128>
 static hipError_t launch_one(const GemmArgs& a, hipStream_t s)
 {
     const int64_t G = a.K / kGroup;
-    const size_t lds = (size_t)G * 16 * NT * sizeof(float2);
+    const size_t lds = (size_t)G * (EPI == EPI_F32 ? 128 / SG : 1) * 16 * NT * sizeof(float2);
     dim3 grid;
     if (EPI == EPI_SWIGLU_Q)
         grid.x = (unsigned)(a.I / kGroup);
@@ -454,7 +518,7 @@ static hipError_t launch_one(const GemmArgs& a, hipStream_t s)
     grid.z = 1;
     if (grid.x == 0 || grid.y == 0)
         return hipSuccess;
-    hipLaunchKernelGGL((gemm_skinny_kernel<NT, EPI, DW, F16, SW4, PK, FP4, NF>), grid, dim3(256), lds, s, a);
+    hipLaunchKernelGGL((gemm_skinny_kernel<NT, EPI, DW, F16, SW4, PK, FP4, NF, SG>), grid, dim3(256), lds, s, a);
     return hipGetLastError();
 }
 
@@ -469,35 +533,48 @@ static hipError_t launch_one(const GemmArgs& a, hipStream_t s)
 #ifndef W4A8_DOWN_NF16
 #define W4A8_DOWN_NF16 2
 #endif
-template <int NT, int DW, bool PK, bool FP4>
+template <int NT, int DW, bool PK, bool FP4, int SG>
 static hipError_t launch_nt(const GemmArgs& a, int epilogue, hipStream_t s)
 {
     const bool g4 = (a.K / kGroup) % 4 == 0;
     constexpr int NFD = NT == 1 ? W4A8_DOWN_NF16 : 4;
     switch (epilogue) {
     case EPI_F32:
-        return g4 ? launch_one<NT, EPI_F32, DW, false, 4 % DW == 0, PK, FP4, NFD>(a, s)
-                  : launch_one<NT, EPI_F32, DW, false, false, PK, FP4, NFD>(a, s);
+        return g4 ? launch_one<NT, EPI_F32, DW, false, 4 % DW == 0, PK, FP4, NFD, SG>(a, s)
+                  : launch_one<NT, EPI_F32, DW, false, false, PK, FP4, NFD, SG>(a, s);
     case EPI_BF16:
-        if constexpr (PK) {
-            return hipErrorInvalidValue;  // the dense GEMM takes canonical weights only
+        if constexpr (PK || SG != 128) {
+            return hipErrorInvalidValue;  // the dense GEMM: canonical weights, per-128 scales
         } else {
             return g4 ? launch_one<NT, EPI_BF16, DW, false, 4 % DW == 0, false, false>(a, s)
                       : launch_one<NT, EPI_BF16, DW, false, false, false, false>(a, s);
         }
     default:
-        return g4 ? launch_one<NT, EPI_SWIGLU_Q, DW, true, 4 % DW == 0, PK, FP4>(a, s)
-                  : launch_one<NT, EPI_SWIGLU_Q, DW, true, false, PK, FP4>(a, s);
+        return g4 ? launch_one<NT, EPI_SWIGLU_Q, DW, true, 4 % DW == 0, PK, FP4, 4, SG>(a, s)
+                  : launch_one<NT, EPI_SWIGLU_Q, DW, true, false, PK, FP4, 4, SG>(a, s);
+    }
+}
+
+// the finer activation recipes (sub_group 64 or 32) run on prepacked weights
+template <int NT, int DW, bool FP4>
+static hipError_t launch_packed(const GemmArgs& a, int epilogue, hipStream_t s)
+{
+    switch (a.sub_group) {
+    case 128: return launch_nt<NT, DW, true, FP4, 128>(a, epilogue, s);
+    case 64: return launch_nt<NT, DW, true, FP4, 64>(a, epilogue, s);
+    case 32: return launch_nt<NT, DW, true, FP4, 32>(a, epilogue, s);
+    default: return hipErrorInvalidValue;
     }
 }
 
 template <int NT, int DW>
 static hipError_t launch_layout(const GemmArgs& a, int epilogue, hipStream_t s)
 {
-    if (a.fp4)
-        return a.packed ? launch_nt<NT, DW, true, true>(a, epilogue, s) : hipErrorInvalidValue;
-    return a.packed ? launch_nt<NT, DW, true, false>(a, epilogue, s)
-                    : launch_nt<NT, DW, false, false>(a, epilogue, s);
+    if (a.packed)
+        return a.fp4 ? launch_packed<NT, DW, true>(a, epilogue, s) : launch_packed<NT, DW, false>(a, epilogue, s);
+    if (a.fp4 || a.sub_group != 128)
+        return hipErrorInvalidValue;
+    return launch_nt<NT, DW, false, false, 128>(a, epilogue, s);
 }
 
 hipError_t launch_gemm_skinny(const GemmArgs& a, int epilogue, int block_m, hipStream_t s)

@@ -483,8 +483,8 @@ hipError_t launch_gemm_tile(const GemmArgs& a, int mode, hipStream_t s)
         cus = 256;
     const int64_t wgs = tiles < cus ? tiles : cus;
     const dim3 grid((unsigned)((wgs + 7) / 8 * 8));
-    if (a.fp4 && !a.packed)
-        return hipErrorInvalidValue;
+    if ((a.fp4 && !a.packed) || a.sub_group != 128)
+        return hipErrorInvalidValue;  // the finer activation recipes run on the skinny kernel
     const dim3 block(kTThreads);
     if (mode == TILE_GATEUP) {
         if (a.fp4)

@@ -79,6 +79,10 @@ struct GemmArgs {
     uint8_t* out_q;        // [rows, I] codes     (SwiGLU+requant epilogue, interleaved)
     float2* out_side;      // [rows, I/128]
     const float* requant_scale;  // static per-tensor scale of the requant, or null (dynamic)
+    // K per dynamic activation scale of the down GEMM's input: 128, or 64 / 32
+    // (finer recipes; the SwiGLU epilogue emits such blocks, the down GEMM
+    // reads them; side data [rows, K/sub_group]); skinny kernel only
+    int sub_group;
     int64_t max_blocks;    // grid bound on m-blocks
 };
 enum Epilogue { EPI_F32 = 0, EPI_BF16 = 1, EPI_SWIGLU_Q = 2 };

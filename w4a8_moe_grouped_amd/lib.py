@@ -23,7 +23,8 @@ EXPORTS = ("w4a8_version", "w4a8_status_string", "w4a8_quantize_act", "w4a8_gemm
            "w4a8_moe_align", "w4a8_fused_moe", "w4a8_fused_moe_workspace_layout",
            "w4a8_fused_moe_stage_events", "w4a8_prepack_weights", "w4a8_prepacked_scale_count",
            "w4a8_fused_moe_prepacked", "w4a8_prepack_weights_fp4", "w4a8_fused_moe_fp4_prepacked",
-           "w4a8_prepack_weights_bf16_scales", "w4a8_fused_moe_prepacked_static")
+           "w4a8_prepack_weights_bf16_scales", "w4a8_fused_moe_prepacked_static",
+           "w4a8_fused_moe_recipe")
 
 _lock = threading.Lock()
 _lib = None
@@ -69,6 +70,9 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         L.w4a8_fused_moe_prepacked_static.restype = ctypes.c_int
         L.w4a8_fused_moe_prepacked_static.argtypes = L.w4a8_fused_moe.argtypes[:13] + [vp, vp] + \
             L.w4a8_fused_moe.argtypes[13:]
+        L.w4a8_fused_moe_recipe.restype = ctypes.c_int
+        L.w4a8_fused_moe_recipe.argtypes = [vp, i64, i64, vp, vp, i64, i64, i64, i64, ctypes.c_int,
+                                            vp, vp, vp, vp, ctypes.c_int, vp, vp, sz, vp]
         L.w4a8_prepack_weights_bf16_scales.restype = ctypes.c_int
         L.w4a8_prepack_weights_bf16_scales.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp]
         L.w4a8_prepacked_scale_count.restype = ctypes.c_int64
@@ -218,6 +222,39 @@ def fused_moe_fp4(hidden: torch.Tensor, topk_ids: torch.Tensor, topk_weights: to
         _ptr(hidden), T, H, _ptr(topk_ids), _ptr(topk_weights), k, expert_begin, E, I,
         _ptr(w13p), _ptr(s13p), _ptr(w2p), _ptr(s2p), _ptr(out), _ptr(workspace),
         ctypes.byref(n), _stream(hidden.device)), "w4a8_fused_moe_fp4_prepacked")
+    return out
+
+
+WEIGHTS_INT4_PACKED, WEIGHTS_FP4_PACKED = 1, 2
+
+
+def fused_moe_recipe(hidden: torch.Tensor, topk_ids: torch.Tensor, topk_weights: torch.Tensor,
+                     expert_begin: int, num_local_experts: int, I: int, prepacked: tuple,
+                     weight_format: int, down_act_group: int, out: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None):
+    """The fused forward with the down GEMM's input quantised per
+    down_act_group (128, 64 or 32) K; prepacked = (w13p, s13p, w2p, s2p) from
+    prepack_weights (WEIGHTS_INT4_PACKED) or prepack_weights_fp4
+    (WEIGHTS_FP4_PACKED)."""
+    w13p, s13p, w2p, s2p = prepacked
+    _need_cuda(hidden, topk_ids, topk_weights, w13p, s13p, w2p, s2p)
+    T, H = hidden.shape
+    k = topk_ids.shape[1]
+    E = num_local_experts
+    assert hidden.dtype == torch.bfloat16 and topk_ids.dtype == torch.int32 \
+        and topk_weights.dtype == torch.float32
+    assert w13p.numel() == E * 2 * I * H // 2 and w2p.numel() == E * H * I // 2
+    for t in (hidden, topk_ids, topk_weights, w13p, s13p, w2p, s2p):
+        assert t.is_contiguous()
+    out = out if out is not None else torch.empty((T, H), dtype=torch.bfloat16, device=hidden.device)
+    if workspace is None:
+        need = fused_moe_workspace_bytes(T, H, k, E, I)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=hidden.device)
+    n = ctypes.c_size_t(workspace.numel())
+    _check(load().w4a8_fused_moe_recipe(
+        _ptr(hidden), T, H, _ptr(topk_ids), _ptr(topk_weights), k, expert_begin, E, I,
+        int(weight_format), _ptr(w13p), _ptr(s13p), _ptr(w2p), _ptr(s2p), int(down_act_group),
+        _ptr(out), _ptr(workspace), ctypes.byref(n), _stream(hidden.device)), "w4a8_fused_moe_recipe")
     return out
 
 
