@@ -70,11 +70,12 @@ def moe_flops(cfg, stats):
 
 
 class Workload:
-    def __init__(self, name, nsets, dev, prepack=True, fp4=False):
+    def __init__(self, name, nsets, dev, prepack=True, fp4=False, recipe=0):
         import torch
         from w4a8_moe_grouped_amd import lib, synth
         self.cfg = cfg = synth.CONFIGS[name]
         self.fp4 = fp4
+        self.recipe = recipe  # down-GEMM activation block (64 / 32), 0 = the plain call
         t0 = time.time()
         ids, w = synth.gen_routing(cfg)
         self.stats = synth.routing_stats(cfg, ids)
@@ -112,6 +113,12 @@ class Workload:
     def step(self, i):
         from w4a8_moe_grouped_amd import lib
         cfg = self.cfg
+        if self.recipe:
+            lib.fused_moe_recipe(self.hidden, self.ids, self.w, cfg.expert_begin, cfg.E_local, cfg.I,
+                                 self.psets[i % len(self.psets)],
+                                 lib.WEIGHTS_FP4_PACKED if self.fp4 else lib.WEIGHTS_INT4_PACKED,
+                                 self.recipe, out=self.out, workspace=self.ws)
+            return
         if self.fp4:
             lib.fused_moe_fp4(self.hidden, self.ids, self.w, cfg.expert_begin, cfg.E_local, cfg.I,
                               self.psets[i % len(self.psets)], out=self.out, workspace=self.ws)
@@ -517,6 +524,18 @@ def main():
             del q
             torch.cuda.empty_cache()
         result["fp4_weights"] = fp4
+
+    if not args.no_fp4 and args.only is None:
+        # the finer activation-scale recipes (down GEMM input per 64 / 32 K)
+        rec = {}
+        for fp4w in (False, True):
+            for group in (64, 32):
+                q = Workload("decode", nsets=2, dev=dev, fp4=fp4w, recipe=group)
+                qu = time_steps(q, args.steps, args.warmup)
+                rec["decode_%s_per%d" % ("fp4" if fp4w else "int4", group)] = round(qu, 2)
+                del q
+        log("[bench] recipes: %s" % rec)
+        result["activation_recipes_us"] = rec
 
     if not args.no_cpu_baseline:
         cb = cpu_baseline(primary)
