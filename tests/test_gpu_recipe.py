@@ -67,3 +67,21 @@ def test_fused_moe_recipe_matches_oracle(dev, case, fp4, group):
         rel = np.max(np.abs(scale.astype(np.float64) - inter["sh"]) / inter["sh"])
         print("per-%d %s: scale max rel %.1e" % (group, "fp4" if fp4 else "int4", rel))
         assert rel <= 2e-6
+
+
+@pytest.mark.parametrize("fp4", [False, True])
+def test_recipe_degenerate_routings(dev, fp4):
+    """No local pair at all (output +0) and T = 0 (nothing launched)."""
+    gen = synth.random_moe_fp4 if fp4 else synth.random_moe
+    cfg, d = gen(48, 256, 128, 8, 2, 4, 4, seed=64)
+    d["topk_ids"][:] = d["topk_ids"] % 4          # every id below expert_begin
+    fmt = w4.WEIGHTS_FP4_PACKED if fp4 else w4.WEIGHTS_INT4_PACKED
+    out = w4.fused_moe_recipe(bf16_dev(d["hidden"], dev), dput(d["topk_ids"], dev), dput(d["topk_weights"], dev),
+                              cfg.expert_begin, cfg.E_local, cfg.I, packed(d, fp4, dev), fmt, 32)
+    torch.cuda.synchronize()
+    assert np.all(bf16_host(out) == 0)
+    empty = torch.empty((0, cfg.H), dtype=torch.bfloat16, device=dev)
+    o0 = w4.fused_moe_recipe(empty, torch.empty((0, 2), dtype=torch.int32, device=dev),
+                             torch.empty((0, 2), dtype=torch.float32, device=dev), cfg.expert_begin,
+                             cfg.E_local, cfg.I, packed(d, fp4, dev), fmt, 64)
+    assert o0.shape == (0, cfg.H)
