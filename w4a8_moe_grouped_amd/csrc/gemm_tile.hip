@@ -12,7 +12,7 @@
 // 16 x 16).  For every group the workgroup copies, straight from global memory
 // into LDS (buffer_load ... lds, no register staging), the 128 activation rows
 // (fp8 codes, gathered through the permutation), their {c1, c0} side data, the
-// 256 packed int4 weight rows and their scales: 34 KB per stage, 4 stages in
+// 256 packed int4 (or fp4) weight rows and their scales: 34 KB per stage, 4 stages in
 // flight.  Stage slots are XOR-swizzled so that the 16-byte fragment reads hit
 // distinct LDS banks.
 //
@@ -22,7 +22,12 @@
 // v_mfma_f32_16x16x32_f16, whose fp32 sum of each 32-wide step is exact to
 // rounding (the fp8 form truncates, and the requantised SwiGLU output of
 // gate_up is sensitive to that).  Either way one group's raw sum is promoted
-// as y += w_scale * fma(raw, c1, c0).
+// as y += w_scale * fma(raw, c1, c0).  With prepacked fp4 weights (FP4;
+// DeepGEMM PR #53, Changes: FP4 E2M1 with per-32-K UE8M0 scales) gate_up
+// converts the nibbles to f16 at the lane's relative block scale and promotes
+// with 2^(e_max - 136), and the down GEMM hands them to the scaled fp8 x fp4
+// MFMA with the lane's block exponent, promoting with the activation scale
+// alone.
 //
 // Tile order: tiles are numbered expert by expert, weight block by weight
 // block, m-block fastest (the m-blocks of one expert share its weight panel

@@ -1,7 +1,6 @@
 // quant.hip -- per-token-per-128 fp8 activation quantisation, dynamic or with
 // a static per-tensor scale (the rules and the block layout are in
-// quant_block.hpp).  HBM-bound: 2 bytes read
-// and ~1 byte written per element.
+// quant_block.hpp).  HBM-bound: 2 bytes read and ~1 byte written per element.
 #include "common.hpp"
 #include "internal.hpp"
 #include "quant_block.hpp"
