@@ -261,7 +261,7 @@ int w4a8_moe_align(const int32_t* topk_ids, int64_t T, int64_t topk, int64_t exp
         ((block_expert == nullptr) != (block_row == nullptr)))
         return W4A8_ERR_INVALID_ARG;
     w4a8::AlignOut o = {expert_counts, expert_offsets, sorted_pair_ids, src2dst,
-                        block_expert, block_row, num_blocks};
+                        block_expert, block_row, num_blocks, nullptr};
     return hip_status(w4a8::launch_align(topk_ids, T, topk, expert_begin, num_local_experts,
                                          block_m, o, workspace, stream));
 }

@@ -80,6 +80,10 @@ __device__ __forceinline__ v4i sgpr_rsrc(const void* base, uint32_t bytes)
 // 4).  Issued from inline assembly so that the compiler's wait-count pass,
 // which cannot tell the stages apart, does not drain every stage in flight
 // before each LDS read; the kernel waits explicitly (wait_vmcnt + barrier).
+// M0 (the LDS destination) is set inside each block.  The compiler treats M0
+// as reserved and ignores the clobber; it sets M0 itself right before any
+// instruction of its own that reads it, and in these kernels M0 appears only
+// in these sequences, so no value of the compiler's is live across them.
 __device__ __forceinline__ void lds_load16(const v4i& r, uint32_t lds, uint32_t voff, uint32_t soff)
 {
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
