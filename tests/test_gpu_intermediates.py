@@ -47,7 +47,7 @@ def deinterleave8(mem):
 def test_requant_codes_and_down_output(name):
     assert torch.cuda.is_available()
     dev = torch.device("cuda:0")
-    if name == "tile_small":  # block-tiled path (128-row m-blocks)
+    if name == "tile_small":  # block-tiled path (160-row m-blocks)
         cfg, d = synth.random_moe(512, 256, 256, 8, 2, 0, 4, seed=31)
     else:
         cfg = synth.CONFIGS[name]

@@ -277,24 +277,26 @@ def test_fused_moe_edge_cases(dev, case):
     assert_bf16_close(got, ref, case)
 
 
-# Block-tiled path (many rows per local expert): 128-row m-blocks, ragged
+# Block-tiled path (many rows per local expert): 160-row m-blocks, ragged
 # last blocks, a partial 256-wide weight block, fewer K-groups than pipeline
 # stages, an expert with no rows next to one with many.
 def tile_case(case):
-    if case == "tile_small":        # ~128 rows per expert: full + nearly empty m-blocks
+    if case == "tile_small":        # ~128 rows per expert: one m-block, partial second half
         return synth.random_moe(512, 256, 256, 8, 2, 0, 4, seed=31)
+    if case == "tile_two_blocks":   # ~170 rows per expert: full + nearly empty m-blocks
+        return synth.random_moe(680, 256, 256, 8, 2, 0, 4, seed=34)
     if case == "tile_ragged":       # H = 384: down weight blocks 256 + 128; 3 and 1 K-groups
         return synth.random_moe(700, 384, 128, 5, 2, 1, 3, seed=32)
     cfg, d = synth.random_moe(300, 256, 256, 4, 2, 0, 2, seed=33)
-    d["topk_ids"][:] = 1            # every pair on local expert 1, expert 0 empty: 5 m-blocks
+    d["topk_ids"][:] = 1            # every pair on local expert 1, expert 0 empty: 4 m-blocks
     return cfg, d
 
 
-@pytest.mark.parametrize("case", ["tile_small", "tile_ragged", "tile_one_expert"])
+@pytest.mark.parametrize("case", ["tile_small", "tile_two_blocks", "tile_ragged", "tile_one_expert"])
 def test_fused_moe_tile_path(dev, case):
     cfg, d = tile_case(case)
     lay = w4.fused_moe_workspace_layout(cfg.T, cfg.H, cfg.topk, cfg.E_local, cfg.I)
-    assert lay["block_m"] == 128, "expected the block-tiled path"
+    assert lay["block_m"] == 160, "expected the block-tiled path"
     got = run_fused(d, cfg, dev)
     ref = oracle_rows(d, cfg, np.arange(cfg.T))
     assert_bf16_close(got, ref, case)

@@ -6,15 +6,20 @@
 // PR #53 "Changes": large batches are MMA-bound, so a block tile reuses each
 // weight byte across many token rows).
 //
-// Work decomposition.  A workgroup of 8 waves owns a tile of 128 rows (one
+// Work decomposition.  A workgroup of 8 waves owns a tile of 160 rows (one
 // m-block) x 256 weight rows and walks K one 128-group at a time.  Waves sit
-// on a 2 x 4 grid, each with a 64 x 64 register tile (4 x 4 fragments of
-// 16 x 16).  For every group the workgroup copies, straight from global memory
-// into LDS (buffer_load ... lds, no register staging), the 128 activation rows
-// (fp8 codes, gathered through the permutation), their {c1, c0} side data, the
-// 256 packed int4 (or fp4) weight rows and their scales: 34 KB per stage, 4 stages in
-// flight.  Stage slots are XOR-swizzled so that the 16-byte fragment reads hit
-// distinct LDS banks.
+// on a 2 x 4 grid, each with an 80 x 64 register tile (5 x 4 fragments of
+// 16 x 16); the two row halves go to waves 0-3 and 4-7, so that each SIMD
+// holds one wave of each half.  A wave whose half holds no row of the
+// m-block skips the K loop.  160 rows: with ~130 rows per local expert (a
+// 4096-token batch over 256 experts, top-8) every expert's rows fit one
+// m-block, where 128-row blocks leave a nearly empty second block for half of
+// the experts.  For every group the workgroup copies, straight from global memory into LDS
+// (buffer_load ... lds, no register staging), the 160 activation rows (fp8
+// codes, gathered through the permutation), their {c1, c0} side data, the
+// 256 packed int4 (or fp4) weight rows and their scales: 38 KB per stage, 4
+// stages in flight.  Stage slots are XOR-swizzled so that the 16-byte
+// fragment reads hit distinct LDS banks.
 //
 // MFMAs: the down GEMM runs on v_mfma_f32_16x16x128_f8f6f4 with the weights
 // turned into u * 2^-9 fp8 codes (u = nibble ^ 8, see common.hpp); gate_up runs
@@ -49,18 +54,32 @@ namespace w4a8 {
 
 namespace {
 
-constexpr int kTBM = 128;     // rows per tile
-constexpr int kTBN = 256;     // weight rows per tile
+constexpr int kTBM = kTileRows;    // rows per tile
+constexpr int kHalf = kTBM / 2;    // rows per wave (two row halves)
+constexpr int kSlices = kHalf / 16;
+constexpr int kTBN = 256;          // weight rows per tile
 constexpr int kTThreads = 512;
 constexpr int kStages = 4;
-constexpr int kLoadsPerStage = 5;  // per wave: 2 A + 2 B + 1 side-or-scale
+static_assert(kHalf % 16 == 0, "row halves are whole 16-row slices");
 
 constexpr int kAOff = 0;
-constexpr int kBOff = kAOff + kTBM * kGroup;         // 16 KB of activation codes
+constexpr int kBOff = kAOff + kTBM * kGroup;         // 20 KB of activation codes
 constexpr int kSideOff = kBOff + kTBN * kGroup / 2;  // 16 KB of packed weights
 constexpr int kSwOff = kSideOff + kTBM * 8;          // {c1, c0} per row
 constexpr int kStageBytes = kSwOff + kTBN * 4;       // weight scale per weight row
 constexpr int kSmemBytes = kStages * kStageBytes;
+static_assert(kSmemBytes + 64 <= 160 * 1024, "stages exceed the LDS of a CU");
+
+// Direct loads per stage, in 64-lane wave loads: 16-byte chunks of the
+// activation rows and of the weight rows, dwords of the side data and of the
+// weight scales.  Wave w issues activation loads w, w + 8, w + 16 (those
+// below kALoads) and weight loads w, w + 8; waves 0-3 load the weight
+// scales, waves 4-7 the side data (wave 4 also its fifth load).
+constexpr int kALoads = kTBM * kGroup / 16 / 64;        // 20
+constexpr int kBLoads = kTBN * kGroup / 2 / 16 / 64;    // 16
+constexpr int kSideLoads = kTBM * 2 / 64;               // 5
+static_assert(kALoads > 16 && kALoads <= 24 && kBLoads == 16 && kSideLoads == 5,
+              "the load assignment below is written for a 160 x 256 tile");
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -128,7 +147,7 @@ __device__ __forceinline__ int b_slot(int wrow, int chunk)
 
 }  // namespace
 
-// One tile: rows [row0, row0 + 128) of m-block L's expert x weight block nb.
+// One tile: rows [row0, row0 + kTBM) of m-block L's expert x weight block nb.
 template <int MODE, bool PK, bool FP4>
 __device__ __forceinline__ void tile_body(const GemmArgs& a, const int L, uint8_t* smem, int* s_expert_p)
 {
@@ -139,7 +158,7 @@ __device__ __forceinline__ void tile_body(const GemmArgs& a, const int L, uint8_
     // through M0 and must be provably wave-uniform
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, q = lane >> 4, c16 = lane & 15;
-    const int wm = wave & 1, wn = wave >> 1;
+    const int wm = wave >> 2, wn = wave & 3;
     const int64_t K = a.K, N = a.N;
     const int G = (int)(K / kGroup);
     const int E = a.num_experts;
@@ -186,38 +205,54 @@ __device__ __forceinline__ void tile_body(const GemmArgs& a, const int L, uint8_
     const v4i rw = sgpr_rsrc(a.w + (int64_t)e * a.w_estride, (uint32_t)(N * (K / 2)));
     const int64_t G4 = packed_groups4(G);
     const v4i rws = sgpr_rsrc(a.ws + (int64_t)e * a.s_estride, (uint32_t)(PK ? N * G4 * 16 : N * G * 4));
-    uint32_t va[2], vb[2], vx;
+    // load L covers 16-byte slots [64 L, 64 L + 64) of its region
+    uint32_t va[3] = {0u, 0u, 0u}, vb[2], vx[2] = {0u, 0u};
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+        const int s = (wave + 8 * j) * 64 + lane;
+        const int r = min(s >> 3, kTBM - 1), ca = (s & 7) ^ (r & 7);
+        va[j] = (uint32_t)((int64_t)act_row(r) * K + 16 * ca);
+    }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-        const int s = (2 * wave + j) * 64 + lane;
-        const int r = s >> 3, ca = (s & 7) ^ (r & 7);
-        va[j] = (uint32_t)((int64_t)act_row(r) * K + 16 * ca);
+        const int s = (wave + 8 * j) * 64 + lane;
         const int wr = s >> 2, cb = (s & 3) ^ ((wr >> 1) & 3);
         const int64_t n = weight_row(wr);
         vb[j] = PK ? (uint32_t)(((n >> 4) * G * 16 + (n & 15)) * 64 + 16 * cb)
                    : (uint32_t)(n * (K / 2) + 16 * cb);
     }
-    if (wave < 4) {  // side data: dword d = 2 * row + component
-        const int d = wave * 64 + lane;
-        vx = (uint32_t)(((int64_t)act_row(d >> 1) * G) * 8 + 4 * (d & 1));
-    } else {  // weight scales: one per weight row
-        const int64_t n = weight_row((wave - 4) * 64 + lane);
-        vx = PK ? (uint32_t)(((n >> 4) * G4 * 16 + (n & 15)) * 16) : (uint32_t)(n * G * 4);
+    if (wave < 4) {  // weight scales: one per weight row
+        const int64_t n = weight_row(wave * 64 + lane);
+        vx[0] = PK ? (uint32_t)(((n >> 4) * G4 * 16 + (n & 15)) * 16) : (uint32_t)(n * G * 4);
+    } else {  // side data: dword d = 2 * row + component
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int d = min((wave - 4 + 4 * j) * 64 + lane, 2 * kTBM - 1);
+            vx[j] = (uint32_t)(((int64_t)act_row(d >> 1) * G) * 8 + 4 * (d & 1));
+        }
     }
     const uint32_t smem_lds = (uint32_t)(uintptr_t)(lds_ptr_t)smem;
     auto issue = [&](int g, int st) {
         const uint32_t base = smem_lds + (uint32_t)(st * kStageBytes);
-        lds_load16(ra, base + kAOff + (2 * wave) * 1024, va[0], (uint32_t)g * kGroup);
-        lds_load16(ra, base + kAOff + (2 * wave + 1) * 1024, va[1], (uint32_t)g * kGroup);
+#pragma unroll
+        for (int j = 0; j < 3; ++j)
+            if (wave + 8 * j < kALoads)
+                lds_load16(ra, base + kAOff + (uint32_t)(wave + 8 * j) * 1024u, va[j], (uint32_t)g * kGroup);
         const uint32_t gw = (uint32_t)g * (PK ? 1024u : 64u);
-        lds_load16(rw, base + kBOff + (2 * wave) * 1024, vb[0], gw);
-        lds_load16(rw, base + kBOff + (2 * wave + 1) * 1024, vb[1], gw);
-        if (wave < 4)
-            lds_load4(rsd, base + kSideOff + wave * 256, vx, (uint32_t)g * 8u);
-        else
-            lds_load4(rws, base + kSwOff + (wave - 4) * 256, vx,
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            lds_load16(rw, base + kBOff + (uint32_t)(wave + 8 * j) * 1024u, vb[j], gw);
+        if (wave < 4) {
+            lds_load4(rws, base + kSwOff + wave * 256, vx[0],
                       PK ? (uint32_t)(g >> 2) * 256u + (uint32_t)(g & 3) * 4u : (uint32_t)g * 4u);
+        } else {
+            lds_load4(rsd, base + kSideOff + (wave - 4) * 256, vx[0], (uint32_t)g * 8u);
+            if (wave == 4)
+                lds_load4(rsd, base + kSideOff + 4 * 256, vx[1], (uint32_t)g * 8u);
+        }
     };
+    // this wave's loads per stage: waves 0-4 issue 6, waves 5-7 issue 5
+    const bool six_loads = wave <= 4;
 
     // weight rows of this lane's fragments (tile-local)
     int wrow_f[4];
@@ -226,11 +261,14 @@ __device__ __forceinline__ void tile_body(const GemmArgs& a, const int L, uint8_
         wrow_f[f] = MODE == TILE_GATEUP ? (f >= 2 ? 128 : 0) + 32 * wn + 16 * (f & 1) + c16
                                         : 64 * wn + 16 * f + c16;
 
-    const bool wave_idle = 64 * wm >= rows;
+    // a wave whose half holds no row of the m-block skips the K loop; the
+    // others compute all five slices (skipping the slices past the last row
+    // measured slower: the branches split the MFMA/VALU schedule)
+    const bool wave_idle = kHalf * wm >= rows;
 
-    float acc[4][4][4];
+    float acc[kSlices][4][4];
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+    for (int m = 0; m < kSlices; ++m)
 #pragma unroll
         for (int f = 0; f < 4; ++f)
 #pragma unroll
@@ -241,12 +279,19 @@ __device__ __forceinline__ void tile_body(const GemmArgs& a, const int L, uint8_
     // stay so: loads retire in order)
     auto wait_group = [&](int h) {
         const int behind = min(kStages - 2, G - 1 - h);
-        if (behind >= 2)
-            wait_vmcnt<2 * kLoadsPerStage>();
-        else if (behind == 1)
-            wait_vmcnt<kLoadsPerStage>();
-        else
+        if (behind >= 2) {
+            if (six_loads)
+                wait_vmcnt<12>();
+            else
+                wait_vmcnt<10>();
+        } else if (behind == 1) {
+            if (six_loads)
+                wait_vmcnt<6>();
+            else
+                wait_vmcnt<5>();
+        } else {
             wait_vmcnt<0>();
+        }
     };
     // LDS fragment reads: the weight fragments of a stage, and the activation
     // fragment + side data of one 16-row slice m
@@ -257,19 +302,26 @@ __device__ __forceinline__ void tile_body(const GemmArgs& a, const int L, uint8_
             sw[f] = *(const float*)(base + kSwOff + 4 * wrow_f[f]);
         }
     };
-    auto read_a = [&](const uint8_t* base, int m, v4i& a0, v4i& a1, float4& s01, float4& s23) {
-        const int trow = 64 * wm + 16 * m;
+    auto read_a = [&](const uint8_t* base, int m, v4i& a0, v4i& a1) {
+        const int trow = kHalf * wm + 16 * m;
         a0 = *(const v4i*)(base + kAOff + 16 * a_slot(trow + c16, q));
         a1 = *(const v4i*)(base + kAOff + 16 * a_slot(trow + c16, 4 + q));
-        const float4* sd = (const float4*)(base + kSideOff + 8 * (trow + 4 * q));
+    };
+    // {c1, c0} of the lane's four rows 4q + r of slice m
+    auto read_side = [&](const uint8_t* base, int m, float4& s01, float4& s23) {
+        const float4* sd = (const float4*)(base + kSideOff + 8 * (kHalf * wm + 16 * m + 4 * q));
         s01 = sd[0];
         s23 = sd[1];
     };
 
     // Software pipeline.  Stages: groups g+1..g+3 are in flight while group g
-    // is computed.  Registers: the LDS fragments of the next slice (and, across
-    // the group boundary, of the next group) are read while the current one
-    // runs its MFMAs, so LDS latency hides behind them.
+    // is computed.  Registers: the operand fragments of the next slice (and,
+    // across the group boundary, of the next group) are read while the
+    // current one runs its MFMAs, so LDS latency hides behind them.  The side
+    // data is needed only after a slice's MFMAs: gate_up (16 MFMAs per slice,
+    // no registers to spare) reads it as the slice starts, the down GEMM (4
+    // MFMAs per slice) with the next slice's fragments.
+    constexpr bool kSidePre = MODE == TILE_DOWN;
 #pragma unroll
     for (int s = 0; s < kStages - 1; ++s)
         if (s < G)
@@ -278,12 +330,15 @@ __device__ __forceinline__ void tile_body(const GemmArgs& a, const int L, uint8_
     barrier();
     if (kStages - 1 < G)
         issue(kStages - 1, kStages - 1);
+
     v4i wb[4], a0 = {}, a1 = {};
     float sw[4];
-    float4 s01 = {}, s23 = {};
+    float4 s01 = {}, s23 = {};  // prefetched side data (down GEMM)
     if (!wave_idle) {
         read_b(smem, wb, sw);
-        read_a(smem, 0, a0, a1, s01, s23);
+        read_a(smem, 0, a0, a1);
+        if (kSidePre)
+            read_side(smem, 0, s01, s23);
     }
 
     for (int g = 0; g < G; ++g) {
@@ -315,31 +370,34 @@ __device__ __forceinline__ void tile_body(const GemmArgs& a, const int L, uint8_
                     }
                 }
             }
-            // all four slices in one basic block (padding rows are computed and
-            // dropped at the store)
+            // all five slices (padding rows are computed and dropped at the
+            // store)
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
+            for (int m = 0; m < kSlices; ++m) {
                 const v4i ca0 = a0, ca1 = a1;
-                const float c1[4] = {s01.x, s01.z, s23.x, s23.z};
-                const float c0[4] = {s01.y, s01.w, s23.y, s23.w};
-                if (m < 3)
-                    read_a(base, m + 1, a0, a1, s01, s23);
+                float4 cs01 = s01, cs23 = s23;
+                if (!kSidePre)
+                    read_side(base, m, cs01, cs23);
+                if (m + 1 < kSlices) {
+                    read_a(base, m + 1, a0, a1);
+                    if (kSidePre)
+                        read_side(base, m + 1, s01, s23);
+                }
                 v4f raw[4];
                 if (MODE == TILE_GATEUP) {
-                    v8h ah[4];
-#pragma unroll
-                    for (int c = 0; c < 4; ++c) {
-                        const v4i& src = c < 2 ? ca0 : ca1;
-                        ah[c] = fp8x8_to_f16((uint32_t)src[2 * (c & 1)], (uint32_t)src[2 * (c & 1) + 1]);
-                    }
 #pragma unroll
                     for (int f = 0; f < 4; ++f)
                         raw[f] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+                    // one 32-K step at a time: its converted fragment feeds
+                    // the four MFMAs right away
 #pragma unroll
-                    for (int c = 0; c < 4; ++c)
+                    for (int c = 0; c < 4; ++c) {
+                        const v4i& src = c < 2 ? ca0 : ca1;
+                        const v8h ah = fp8x8_to_f16((uint32_t)src[2 * (c & 1)], (uint32_t)src[2 * (c & 1) + 1]);
 #pragma unroll
                         for (int f = 0; f < 4; ++f)
-                            raw[f] = mfma16x16x32_f16(ah[c], bh[f][c], raw[f]);
+                            raw[f] = mfma16x16x32_f16(ah, bh[f][c], raw[f]);
+                    }
                 } else {
                     const v8i av = {ca0[0], ca0[1], ca0[2], ca0[3], ca1[0], ca1[1], ca1[2], ca1[3]};
 #pragma unroll
@@ -347,6 +405,8 @@ __device__ __forceinline__ void tile_body(const GemmArgs& a, const int L, uint8_
                         raw[f] = FP4 ? mfma16x16x128_fp4(av, wb[f], eq[f])
                                      : mfma16x16x128(av, b8[f], v4f{0.0f, 0.0f, 0.0f, 0.0f});
                 }
+                const float c1[4] = {cs01.x, cs01.z, cs23.x, cs23.z};
+                const float c0[4] = {cs01.y, cs01.w, cs23.y, cs23.w};
 #pragma unroll
                 for (int f = 0; f < 4; ++f)
 #pragma unroll
@@ -370,12 +430,14 @@ __device__ __forceinline__ void tile_body(const GemmArgs& a, const int L, uint8_
             if (!wave_idle) {
                 const uint8_t* nbase = smem + ((g + 1) % kStages) * kStageBytes;
                 read_b(nbase, wb, sw);
-                read_a(nbase, 0, a0, a1, s01, s23);
+                read_a(nbase, 0, a0, a1);
+                if (kSidePre)
+                    read_side(nbase, 0, s01, s23);
             }
         }
     }
 
-    // ---- epilogues: element (tile row 64wm + 16m + 4q + r, fragment f) ----
+    // ---- epilogues: element (tile row 80wm + 16m + 4q + r, fragment f) ----
     if (MODE == TILE_DOWN) {
 #pragma unroll
         for (int f = 0; f < 4; ++f) {
@@ -383,10 +445,10 @@ __device__ __forceinline__ void tile_body(const GemmArgs& a, const int L, uint8_
             if (n >= N)
                 continue;
 #pragma unroll
-            for (int m = 0; m < 4; ++m)
+            for (int m = 0; m < kSlices; ++m)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int row = 64 * wm + 16 * m + 4 * q + r;
+                    const int row = kHalf * wm + 16 * m + 4 * q + r;
                     if (row < rows)
                         a.out_f32[(int64_t)(row0 + row) * N + n] = (float)acc[m][f][r];
                 }
@@ -396,12 +458,12 @@ __device__ __forceinline__ void tile_body(const GemmArgs& a, const int L, uint8_
 
     // TILE_GATEUP: fragments f and f + 2 hold gate and up of i = 32wn + 16f + c16
     barrier();  // every wave is done with the stages (no load is in flight)
-    float* s_red = (float*)smem;                        // [4][128] amax per wave column
-    float* s_sum = s_red + 4 * kTBM;                    // [4][128] sum of decoded codes
-    uint8_t* s_q = (uint8_t*)(s_sum + 4 * kTBM);        // [128][128] codes
-    float h[4][2][4];
+    float* s_red = (float*)smem;                        // [4][kTBM] amax per wave column
+    float* s_sum = s_red + 4 * kTBM;                    // [4][kTBM] sum of decoded codes
+    uint8_t* s_q = (uint8_t*)(s_sum + 4 * kTBM);        // [kTBM][128] codes
+    float h[kSlices][2][4];
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+    for (int m = 0; m < kSlices; ++m)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -410,20 +472,20 @@ __device__ __forceinline__ void tile_body(const GemmArgs& a, const int L, uint8_
                 h[m][j][r] = (float)(gt / (1.0 + exp(-gt)) * up);
             }
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+    for (int m = 0; m < kSlices; ++m)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             float mx = fmaxf(fabsf(h[m][0][r]), fabsf(h[m][1][r]));
             mx = group_max<16>(mx);
             if (c16 == 0)
-                s_red[wn * kTBM + 64 * wm + 16 * m + 4 * q + r] = mx;
+                s_red[wn * kTBM + kHalf * wm + 16 * m + 4 * q + r] = mx;
         }
     __syncthreads();
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+    for (int m = 0; m < kSlices; ++m)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int row = 64 * wm + 16 * m + 4 * q + r;
+            const int row = kHalf * wm + 16 * m + 4 * q + r;
             const float mx = fmaxf(fmaxf(s_red[row], s_red[kTBM + row]),
                                    fmaxf(s_red[2 * kTBM + row], s_red[3 * kTBM + row]));
             const float inv = a.requant_scale ? recip_static(*a.requant_scale) : recip448(clamp_amax(mx));

@@ -89,8 +89,8 @@ enum Epilogue { EPI_F32 = 0, EPI_BF16 = 1, EPI_SWIGLU_Q = 2 };
 hipError_t launch_gemm_skinny(const GemmArgs& a, int epilogue, int block_m, hipStream_t s);
 
 // ---- grouped GEMM for many rows per expert (gemm_tile.hip) ----
-// m-blocks of kTileRows rows.
-constexpr int kTileRows = 128;
+// m-blocks of kTileRows rows (two halves of five 16-row slices).
+constexpr int kTileRows = 160;
 enum TileMode { TILE_DOWN = 0, TILE_GATEUP = 1 };
 hipError_t launch_gemm_tile(const GemmArgs& a, int mode, hipStream_t s);
 
