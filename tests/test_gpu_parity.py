@@ -287,12 +287,20 @@ def tile_case(case):
         return synth.random_moe(680, 256, 256, 8, 2, 0, 4, seed=34)
     if case == "tile_ragged":       # H = 384: down weight blocks 256 + 128; 3 and 1 K-groups
         return synth.random_moe(700, 384, 128, 5, 2, 1, 3, seed=32)
+    if case == "tile_boundaries":   # 80 / 81 / 160 / 161 rows: idle half, one-row half, full, one-row block
+        cfg, d = synth.random_moe(512, 256, 256, 8, 2, 0, 4, seed=35)
+        rows = np.concatenate([np.full(n, e) for e, n in enumerate((80, 81, 160, 161))])
+        rng = np.random.default_rng(35)
+        flat = np.concatenate([rows, rng.integers(4, 8, size=cfg.T * cfg.topk - rows.size)])
+        d["topk_ids"][:] = rng.permutation(flat).reshape(cfg.T, cfg.topk).astype(np.int32)
+        return cfg, d
     cfg, d = synth.random_moe(300, 256, 256, 4, 2, 0, 2, seed=33)
     d["topk_ids"][:] = 1            # every pair on local expert 1, expert 0 empty: 4 m-blocks
     return cfg, d
 
 
-@pytest.mark.parametrize("case", ["tile_small", "tile_two_blocks", "tile_ragged", "tile_one_expert"])
+@pytest.mark.parametrize("case", ["tile_small", "tile_two_blocks", "tile_ragged", "tile_one_expert",
+                                  "tile_boundaries"])
 def test_fused_moe_tile_path(dev, case):
     cfg, d = tile_case(case)
     lay = w4.fused_moe_workspace_layout(cfg.T, cfg.H, cfg.topk, cfg.E_local, cfg.I)
