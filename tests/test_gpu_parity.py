@@ -165,7 +165,8 @@ def test_align_bit_exact_configs(dev, name, bm):
 
 @pytest.mark.parametrize("T,k,eb,E,bm,seed", [
     (1, 1, 0, 1, 1, 0), (1, 8, 0, 32, 16, 1), (3, 32, 5, 7, 3, 2), (600, 8, 40, 32, 16, 3),
-    (5000, 6, 0, 1024, 64, 4), (4097, 1, 0, 3, 100, 5), (20000, 8, 224, 32, 64, 6)])
+    (5000, 6, 0, 1024, 64, 4), (4097, 1, 0, 3, 100, 5), (20000, 8, 224, 32, 64, 6),
+    (512, 8, 0, 1024, 16, 7), (256, 8, 0, 32, 64, 8), (1024, 4, 2, 2, 160, 9)])
 def test_align_bit_exact_random(dev, T, k, eb, E, bm, seed):
     rng = np.random.default_rng(seed)
     ids = rng.integers(-1, eb + E + 9, size=(T, k)).astype(np.int32)

@@ -11,8 +11,9 @@
 //   scan    -- one block: counts, exclusive offsets, the per-chunk base of
 //              every expert, and the m-block list;
 //   scatter -- per chunk, rounds of 256 pairs in f order: the rank of a pair
-//              among earlier pairs of the same expert comes from wave ballots
-//              and per-wave counts in LDS, so equal keys keep ascending f.
+//              among earlier pairs of the same expert comes from per-wave
+//              64-bit lane masks in LDS and per-wave counts, so equal keys
+//              keep ascending f.
 // When all pairs fit one chunk the three phases run in one block (decode).
 #include "common.hpp"
 #include "internal.hpp"
@@ -45,23 +46,25 @@ __device__ __forceinline__ int local_id(const int32_t* ids, int64_t f, int64_t F
 }
 
 // rank of this lane among lower lanes of the wave with the same key, and the
-// number of lanes with that key; keys < 0 are ignored.
-__device__ __forceinline__ void wave_rank(int key, int& rank, int& count)
+// number of lanes with that key; keys < 0 are ignored.  masks: this wave's
+// [E] 64-bit lane masks in LDS, zero on entry and on exit.  Every lane ORs
+// its bit into the mask of its key, then reads it back; a wave's LDS
+// operations complete in order, so the read sees every lane's bit and the
+// clear (by the lowest lane of each key) follows every lane's read.  The
+// cost does not depend on how many distinct keys the wave holds.
+__device__ __forceinline__ void wave_rank(int key, unsigned long long* masks, int& rank, int& count)
 {
     const int lane = threadIdx.x & 63;
-    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    uint64_t pending = __ballot(key >= 0);
+    const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     rank = 0;
     count = 0;
-    while (pending) {
-        const int leader = __ffsll((unsigned long long)pending) - 1;
-        const int k = __shfl(key, leader, 64);
-        const uint64_t same = __ballot(key == k);
-        if (key == k) {
-            rank = __popcll(same & lt);
-            count = __popcll(same);
-        }
-        pending &= ~same;
+    if (key >= 0) {
+        atomicOr(&masks[key], 1ull << lane);
+        const unsigned long long m = masks[key];
+        rank = __popcll(m & lt);
+        count = __popcll(m);
+        if (rank == 0)
+            masks[key] = 0ull;
     }
 }
 
@@ -151,17 +154,35 @@ __device__ void finish_scan(int* counts_lds, int* tmp_lds, int* scratch, int64_t
     __syncthreads();
 }
 
-// scatter one chunk [f0, f1) given the running base position of every expert
-// (LDS); wcnt is [kAlignWaves][E] of zeros on entry and on exit.
-__device__ void scatter_chunk(const int32_t* ids, int64_t f0, int64_t f1, int64_t eb, int64_t E,
-                              int* base, int* wcnt, const AlignOut& o)
+// the local ids of pairs f0 + r * kAlignThreads + t, r < R (-1 past f1),
+// loaded once: every round below uses registers
+template <int R>
+__device__ __forceinline__ void load_keys(const int32_t* ids, int64_t f0, int64_t f1, int64_t eb,
+                                          int64_t E, int (&keys)[R])
+{
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        keys[r] = local_id(ids, f0 + (int64_t)r * kAlignThreads + threadIdx.x, f1, eb, E);
+}
+
+// scatter one chunk [f0, f1) (at most R rounds of kAlignThreads pairs, keys
+// from load_keys) given the running base position of every expert (LDS);
+// wcnt ([kAlignWaves][E] ints) and masks ([kAlignWaves][E] lane masks) are
+// zero on entry and on exit.
+template <int R>
+__device__ void scatter_chunk(const int (&keys)[R], int64_t f0, int64_t f1, int64_t E, int* base,
+                              int* wcnt, unsigned long long* masks, const AlignOut& o)
 {
     const int t = threadIdx.x, wave = t >> 6;
-    for (int64_t r0 = f0; r0 < f1; r0 += kAlignThreads) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int64_t r0 = f0 + (int64_t)r * kAlignThreads;
+        if (r0 >= f1)
+            break;
         const int64_t f = r0 + t;
-        const int key = local_id(ids, f, f1, eb, E);
+        const int key = keys[r];
         int rank, count;
-        wave_rank(key, rank, count);
+        wave_rank(key, masks + wave * E, rank, count);
         const bool leader = key >= 0 && rank == 0;
         if (leader)
             wcnt[wave * E + key] = count;
@@ -190,6 +211,14 @@ struct AlignLds {
     int wcnt[kAlignWaves * kMaxLocalExperts];
     int scratch[kAlignWaves + 1];
 };
+constexpr int kSingleRounds = kAlignSingle / kAlignThreads;  // 16
+constexpr int kChunkRounds = kAlignChunk / kAlignThreads;    // 4
+// the lane masks of wave_rank, [kAlignWaves][E]: dynamic LDS of the launch
+extern __shared__ unsigned long long align_masks[];
+size_t align_mask_bytes(int64_t E)
+{
+    return (size_t)kAlignWaves * (size_t)E * sizeof(unsigned long long);
+}
 
 // everything in one block (F <= kAlignSingle)
 __device__ __forceinline__ void align_single_body(const int32_t* __restrict__ ids, int64_t F,
@@ -197,19 +226,22 @@ __device__ __forceinline__ void align_single_body(const int32_t* __restrict__ id
                                                   const AlignOut& o, AlignLds& L)
 {
     const int t = threadIdx.x;
+    int keys[kSingleRounds];
+    load_keys(ids, 0, F, eb, E, keys);
     for (int e = t; e < E; e += kAlignThreads)
         L.a[e] = 0;
-    for (int i = t; i < kAlignWaves * E; i += kAlignThreads)
+    for (int i = t; i < kAlignWaves * E; i += kAlignThreads) {
         L.wcnt[i] = 0;
-    __syncthreads();
-    for (int64_t f = t; f < F; f += kAlignThreads) {
-        const int key = local_id(ids, f, F, eb, E);
-        if (key >= 0)
-            atomicAdd(&L.a[key], 1);
+        align_masks[i] = 0ull;
     }
     __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kSingleRounds; ++r)
+        if (keys[r] >= 0)
+            atomicAdd(&L.a[keys[r]], 1);
+    __syncthreads();
     finish_scan(L.a, L.b, L.scratch, E, block_m, o);  // L.a now holds the offsets
-    scatter_chunk(ids, 0, F, eb, E, L.a, L.wcnt, o);
+    scatter_chunk(keys, 0, F, E, L.a, L.wcnt, align_masks, o);
 }
 
 __global__ __launch_bounds__(kAlignThreads) void align_single_kernel(const int32_t* __restrict__ ids,
@@ -306,14 +338,18 @@ __global__ __launch_bounds__(kAlignThreads) void align_scatter_kernel(const int3
     __shared__ int base[kMaxLocalExperts];
     __shared__ int wcnt[kAlignWaves * kMaxLocalExperts];
     const int t = threadIdx.x;
-    for (int e = t; e < E; e += kAlignThreads)
-        base[e] = hist[(int64_t)blockIdx.x * E + e];
-    for (int i = t; i < kAlignWaves * E; i += kAlignThreads)
-        wcnt[i] = 0;
-    __syncthreads();
     const int64_t f0 = (int64_t)blockIdx.x * kAlignChunk;
     const int64_t f1 = f0 + kAlignChunk < F ? f0 + kAlignChunk : F;
-    scatter_chunk(ids, f0, f1, eb, E, base, wcnt, o);
+    int keys[kChunkRounds];
+    load_keys(ids, f0, f1, eb, E, keys);
+    for (int e = t; e < E; e += kAlignThreads)
+        base[e] = hist[(int64_t)blockIdx.x * E + e];
+    for (int i = t; i < kAlignWaves * E; i += kAlignThreads) {
+        wcnt[i] = 0;
+        align_masks[i] = 0ull;
+    }
+    __syncthreads();
+    scatter_chunk(keys, f0, f1, E, base, wcnt, align_masks, o);
 }
 
 hipError_t launch_align_quant(const int32_t* ids, int64_t T, int64_t topk, int64_t expert_begin,
@@ -323,7 +359,8 @@ hipError_t launch_align_quant(const int32_t* ids, int64_t T, int64_t topk, int64
 {
     const int64_t F = T * topk;
     const int64_t qblocks = (T * (H / kGroup) + 15) / 16;
-    hipLaunchKernelGGL(align_quant_kernel, dim3((unsigned)(1 + qblocks)), dim3(kAlignThreads), 0, s,
+    hipLaunchKernelGGL(align_quant_kernel, dim3((unsigned)(1 + qblocks)), dim3(kAlignThreads),
+                       (unsigned)align_mask_bytes(E), s,
                        ids, F, expert_begin, E, block_m, o, clear, nclear, x, T, H, H, q, side,
                        fixed_scale);
     return hipGetLastError();
@@ -335,8 +372,8 @@ hipError_t launch_align(const int32_t* ids, int64_t T, int64_t topk, int64_t exp
     const int64_t F = T * topk;
     const int64_t nchunks = align_chunk_count(F);
     if (nchunks == 1) {
-        hipLaunchKernelGGL(align_single_kernel, dim3(1), dim3(kAlignThreads), 0, s, ids, F,
-                           expert_begin, E, block_m, o);
+        hipLaunchKernelGGL(align_single_kernel, dim3(1), dim3(kAlignThreads),
+                           (unsigned)align_mask_bytes(E), s, ids, F, expert_begin, E, block_m, o);
         return hipGetLastError();
     }
     int32_t* hist = (int32_t*)ws;
@@ -344,8 +381,8 @@ hipError_t launch_align(const int32_t* ids, int64_t T, int64_t topk, int64_t exp
                        F, expert_begin, E, hist);
     hipLaunchKernelGGL(align_scan_kernel, dim3(1), dim3(kAlignThreads), 0, s, hist, nchunks, E,
                        block_m, o);
-    hipLaunchKernelGGL(align_scatter_kernel, dim3((unsigned)nchunks), dim3(kAlignThreads), 0, s,
-                       ids, F, expert_begin, E, hist, o);
+    hipLaunchKernelGGL(align_scatter_kernel, dim3((unsigned)nchunks), dim3(kAlignThreads),
+                       (unsigned)align_mask_bytes(E), s, ids, F, expert_begin, E, hist, o);
     return hipGetLastError();
 }
 
