@@ -55,7 +55,7 @@ int64_t ceil_div(int64_t a, int64_t b)
     return (a + b - 1) / b;
 }
 
-// Many rows per expert: the block-tiled GEMM (128-row m-blocks, weights
+// Many rows per expert: the block-tiled GEMM (160-row m-blocks, weights
 // reused across the rows of an m-block from LDS) beats streaming the weights
 // once per small m-block.  Decided from the pairs per expert if every pair
 // were local, like pick_block_m.
