@@ -243,6 +243,10 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs a)
             }
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
+                // 16-row slices past the block's last row: nothing to compute
+                // (slice 0 always holds a row)
+                if (t > 0 && 16 * t >= rows)
+                    continue;
                 const float4* sd = (const float4*)&lds_side[gl * BM + 16 * t + 4 * q];
                 const float4 s01 = sd[0], s23 = sd[1];
                 const float c1[4] = {s01.x, s01.z, s23.x, s23.z};
