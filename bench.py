@@ -480,8 +480,10 @@ def main():
 
     if not args.no_prefill and args.only is None:
         pre = {}
-        for name, steps, warm in (("prefill", 10, 3), ("prefill_ep8", 3, 1)):
-            p = Workload(name, nsets=1, dev=dev, prepack=packed)
+        # steady state: ~20 ms of warm-up and two weight sets alternating, as
+        # for decode, so no step reads the previous step's weights from cache
+        for name, steps, warm in (("prefill", 30, 10), ("prefill_ep8", 8, 3)):
+            p = Workload(name, nsets=2, dev=dev, prepack=packed)
             pu = time_steps(p, steps, warm)
             pst = stage_breakdown(p, 2)
             pfl = moe_flops(p.cfg, p.stats)
@@ -503,8 +505,8 @@ def main():
         # the same workloads on fp4 e2m1 weights with per-32-K UE8M0 scales
         # (weight and scale bytes equal the int4 path's, so the same roofline)
         fp4 = {}
-        for name, steps, warm, nsets in (("decode", args.steps, args.warmup, 2), ("prefill", 10, 3, 1),
-                                         ("prefill_ep8", 3, 1, 1)):
+        for name, steps, warm, nsets in (("decode", args.steps, args.warmup, 2), ("prefill", 30, 10, 2),
+                                         ("prefill_ep8", 8, 3, 2)):
             if name != "decode" and args.no_prefill:
                 continue
             q = Workload(name, nsets=nsets, dev=dev, fp4=True)
