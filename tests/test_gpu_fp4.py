@@ -77,6 +77,8 @@ def fp4_case(case):
         return synth.random_moe_fp4(24, 640, 384, 8, 2, 2, 4, seed=41)
     if case == "k1_e1":
         return synth.random_moe_fp4(40, 384, 128, 1, 1, 0, 1, seed=23)
+    if case == "two_slices":       # ~30 rows per expert: 32-row blocks with both 16-row slices
+        return synth.random_moe_fp4(120, 256, 128, 4, 1, 0, 4, seed=42)
     assert case == "all_non_local"
     cfg, d = synth.random_moe_fp4(48, 256, 128, 8, 2, 4, 4, seed=27)
     d["topk_ids"][:] = d["topk_ids"] % 4
@@ -84,7 +86,7 @@ def fp4_case(case):
 
 
 @pytest.mark.parametrize("case", ["tiny", "decode", "tile_small", "tile_ragged", "single_token",
-                                  "five_groups", "k1_e1", "all_non_local"])
+                                  "five_groups", "k1_e1", "two_slices", "all_non_local"])
 def test_fused_moe_fp4_matches_oracle(dev, case):
     cfg, d = fp4_case(case)
     packed = w4.prepack_weights_fp4(dput(d["w13"], dev), dput(d["s13"], dev), w4.FP4_GATE_UP) + \

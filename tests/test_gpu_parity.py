@@ -253,7 +253,8 @@ def test_fused_moe_sampled_tokens(dev, name, nsample):
 
 
 @pytest.mark.parametrize("case", ["one_expert_many_rows", "single_token", "k1_e1",
-                                  "non_local_mix", "topk32", "small_dims", "all_non_local"])
+                                  "non_local_mix", "topk32", "small_dims", "all_non_local",
+                                  "two_slices"])
 def test_fused_moe_edge_cases(dev, case):
     if case == "one_expert_many_rows":   # every pair on expert 2: many full blocks + a partial one
         cfg, d = synth.random_moe(150, 256, 256, 8, 2, 0, 8, seed=21)
@@ -268,6 +269,8 @@ def test_fused_moe_edge_cases(dev, case):
         d["topk_ids"][:10] = -1
     elif case == "topk32":
         cfg, d = synth.random_moe(9, 256, 128, 64, 32, 0, 64, seed=25)
+    elif case == "two_slices":      # ~30 rows per expert: 32-row blocks with both 16-row slices
+        cfg, d = synth.random_moe(120, 256, 128, 4, 1, 0, 4, seed=28)
     elif case == "all_non_local":   # no m-block at all: the output is +0 everywhere
         cfg, d = synth.random_moe(48, 256, 128, 8, 2, 4, 4, seed=27)
         d["topk_ids"][:] = d["topk_ids"] % 4

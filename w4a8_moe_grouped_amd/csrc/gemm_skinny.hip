@@ -39,7 +39,7 @@ constexpr int kWaves = 4;
 // epilogue then emits SG-blocks, and the down GEMM splits each 128-K group into
 // 128/SG lane-masked MFMAs, each promoted with its own block scale.
 template <int NT, int EPI, int DW, bool F16, bool SW4, bool PK, bool FP4, int NF, int SG>
-__global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs a)
+__global__ __launch_bounds__(256, NT == 2 ? 2 : 1) void gemm_skinny_kernel(GemmArgs a)
 {
     constexpr int kNF = NF;
     static_assert(SG == 128 || SG == 64 || SG == 32, "activation block of 128, 64 or 32 K");
@@ -241,6 +241,62 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs a)
                 }
                 swf[f] = (FP4 || g < G) ? v : 0.0f;
             }
+            if constexpr (F16 && NT == 2) {
+                // two slices: 32-K step outer, slices inner, so that each
+                // step's weight fragments are converted once for both slices
+                // and only one step's f16 fragments are live (with the ring of
+                // 2 groups this instance fits two waves per SIMD; for four
+                // slices the per-slice order below measured faster)
+                float conv[kNF], wsc[kNF];
+                if (FP4) {
+#pragma unroll
+                    for (int f = 0; f < kNF; ++f) {
+                        const Fp4GroupScale fs = fp4_group_scale(__builtin_bit_cast(uint32_t, swf[f]), q);
+                        conv[f] = fs.conv;
+                        wsc[f] = g < G ? fs.promote : 0.0f;
+                    }
+                }
+                v4f raws[NT][kNF];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    v8h bc[kNF];
+#pragma unroll
+                    for (int f = 0; f < kNF; ++f) {
+                        const uint32_t x = (uint32_t)wb[s][f][c];
+                        bc[f] = FP4 ? fp4x8_to_f16(x, conv[f])
+                                    : fp8x8_to_f16(xor_and_or<0x08080808u, 0x0F0F0F0Fu, 0u>(x),
+                                                   xor_and_or<0x08080808u, 0x0F0F0F0Fu, 0u>(x >> 4));
+                    }
+#pragma unroll
+                    for (int t = 0; t < NT; ++t) {
+                        if (t > 0 && 16 * t >= rows)
+                            continue;
+                        const v8h ah = fp8x8_to_f16((uint32_t)ab[s][t][c >> 1][2 * (c & 1)],
+                                                    (uint32_t)ab[s][t][c >> 1][2 * (c & 1) + 1]);
+#pragma unroll
+                        for (int f = 0; f < kNF; ++f)
+                            raws[t][f] = mfma16x16x32_f16(ah, bc[f], c == 0 ? v4f{0.0f, 0.0f, 0.0f, 0.0f} : raws[t][f]);
+                    }
+                }
+#pragma unroll
+                for (int t = 0; t < NT; ++t) {
+                    if (t > 0 && 16 * t >= rows)
+                        continue;
+                    const float4* sd = (const float4*)&lds_side[gl * BM + 16 * t + 4 * q];
+                    const float4 s01 = sd[0], s23 = sd[1];
+                    const float c1[4] = {s01.x, s01.z, s23.x, s23.z};
+                    const float c0[4] = {s01.y, s01.w, s23.y, s23.w};
+#pragma unroll
+                    for (int f = 0; f < kNF; ++f)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            if (FP4)  // y += 2^(e_max - 136) * (raw * 512 sa)
+                                acc[f][t][r] = fmaf(raws[t][f][r] * c1[r], wsc[f], acc[f][t][r]);
+                            else
+                                acc[f][t][r] = fmaf(swf[f], fmaf(raws[t][f][r], c1[r], c0[r]), acc[f][t][r]);
+                        }
+                }
+            } else
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
                 // 16-row slices past the block's last row: nothing to compute
@@ -530,7 +586,10 @@ static hipError_t launch_one(const GemmArgs& a, hipStream_t s)
 // ring depth per m-block height.  The down GEMM of 16-row m-blocks takes
 // 128 weight rows per workgroup: its K is short, so a workgroup lives briefly,
 // and twice as many smaller ones leave less of the machine idle in the last
-// round of workgroups.
+// round of workgroups.  32-row m-blocks run two waves per SIMD: a ring of 2
+// groups and one scale load per group (the float4 scale blocks would not fit
+// the register budget); measured against one wave per SIMD with a ring of 3,
+// 128 tokens on 32 of 256 experts: 202 -> 181 us per fused call.
 #ifndef W4A8_DW16
 #define W4A8_DW16 4
 #endif
@@ -544,7 +603,7 @@ static hipError_t launch_nt(const GemmArgs& a, int epilogue, hipStream_t s)
     constexpr int NFD = NT == 1 ? W4A8_DOWN_NF16 : 4;
     switch (epilogue) {
     case EPI_F32:
-        return g4 ? launch_one<NT, EPI_F32, DW, false, 4 % DW == 0, PK, FP4, NFD, SG>(a, s)
+        return g4 && NT != 2 ? launch_one<NT, EPI_F32, DW, false, 4 % DW == 0, PK, FP4, NFD, SG>(a, s)
                   : launch_one<NT, EPI_F32, DW, false, false, PK, FP4, NFD, SG>(a, s);
     case EPI_BF16:
         if constexpr (PK || SG != 128) {
@@ -554,7 +613,7 @@ static hipError_t launch_nt(const GemmArgs& a, int epilogue, hipStream_t s)
                       : launch_one<NT, EPI_BF16, DW, false, false, false, false>(a, s);
         }
     default:
-        return g4 ? launch_one<NT, EPI_SWIGLU_Q, DW, true, 4 % DW == 0, PK, FP4, 4, SG>(a, s)
+        return g4 && NT != 2 ? launch_one<NT, EPI_SWIGLU_Q, DW, true, 4 % DW == 0, PK, FP4, 4, SG>(a, s)
                   : launch_one<NT, EPI_SWIGLU_Q, DW, true, false, PK, FP4, 4, SG>(a, s);
     }
 }
@@ -586,7 +645,7 @@ hipError_t launch_gemm_skinny(const GemmArgs& a, int epilogue, int block_m, hipS
     if (block_m <= 16)
         return launch_layout<1, W4A8_DW16>(a, epilogue, s);
     if (block_m <= 32)
-        return launch_layout<2, 3>(a, epilogue, s);
+        return launch_layout<2, 2>(a, epilogue, s);
     return launch_layout<4, 2>(a, epilogue, s);
 }
 
