@@ -216,3 +216,26 @@ def test_fused_moe_recipe_rejects_bad_arguments(L):
     assert f(group=16) == INVALID
     assert f(nbytes=ctypes.c_size_t(16)) == WORKSPACE
     assert f(group=32, nbytes=ctypes.c_size_t(16)) == WORKSPACE
+
+
+@pytest.mark.parametrize("T,topk,E,want", [
+    (64, 8, 32, 16),      # decode share: 16 pairs per local expert if all were local
+    (1, 8, 256, 16),
+    (128, 8, 32, 32),
+    (256, 8, 32, 64),
+    (1023, 8, 32, 64),    # 8184 pairs: one short of 256 per expert
+    (1024, 8, 32, 160),   # 8192 pairs: the block-tiled kernel's 160-row m-blocks
+    (4096, 8, 32, 160),
+])
+def test_block_height_rule(L, T, topk, E, want):
+    """The m-block height the fused call picks from the pairs per local expert
+    (host-side, from the shapes alone), and a layout consistent with it."""
+    lay = w4.fused_moe_workspace_layout(T, 7168, topk, E, 2048)
+    assert lay["block_m"] == want
+    F = T * topk
+    keys = list(w4.LAYOUT_KEYS)
+    offs = [lay[k] for k in keys]
+    assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+    # block lists hold at most ceil(F / block_m) + E entries
+    nb_max = (F + want - 1) // want + E
+    assert lay["block_row"] - lay["block_expert"] >= 4 * nb_max
