@@ -11,8 +11,10 @@
 // rows sit on the A side of v_mfma_f32_16x16x128_f8f6f4 and the weight rows
 // on the B side, so every weight byte is loaded from HBM exactly once per
 // m-block, straight into VGPRs (16 bytes per lane, no LDS), through a ring of
-// D groups in flight.  One MFMA covers one 128-group, so the per-group scale
-// promotion is exact: acc += w_scale * fma(raw, c1, c0) (see common.hpp).
+// D groups in flight.  The block's activation rows ride in the same ring,
+// either per wave in VGPRs or once per workgroup into LDS (SHARED, below).
+// One MFMA covers one 128-group, so the per-group scale promotion is exact:
+// acc += w_scale * fma(raw, c1, c0) (see common.hpp).
 //
 // Epilogues:
 //   EPI_F32      out_f32[p, n]                       (down GEMM)
@@ -28,6 +30,44 @@
 namespace w4a8 {
 
 constexpr int kWaves = 4;
+
+namespace {
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// buffer descriptor in SGPRs (raw, stride 0, num_records = bytes)
+__device__ __forceinline__ v4i sgpr_rsrc(const void* base, uint32_t bytes)
+{
+    const uint64_t b = (uint64_t)base;
+    v4i r;
+    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+    r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+    r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+    r[3] = 0x00020000;
+    return r;
+}
+// 64 lanes x 16 bytes from the buffer into LDS at lds + 16 * lane
+__device__ __forceinline__ void lds_load16(const v4i& r, uint32_t lds, uint32_t voff, uint32_t soff)
+{
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :
+                 : "s"(lds), "v"(voff), "s"(r), "s"(soff)
+                 : "memory", "m0");
+}
+// 64 lanes x 4 bytes from the buffer into LDS at lds + 4 * lane
+__device__ __forceinline__ void lds_load4(const v4i& r, uint32_t lds, uint32_t voff, uint32_t soff)
+{
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+                 :
+                 : "s"(lds), "v"(voff), "s"(r), "s"(soff)
+                 : "memory", "m0");
+}
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+}  // namespace
 
 // NF: weight fragments (16 rows) per wave.  FP4: prepacked fp4 e2m1 weights
 // with UE8M0 scale dwords (DeepGEMM PR #53, Changes): the f16 path converts
@@ -100,8 +140,7 @@ __global__ __launch_bounds__(256, NT == 2 ? 2 : 1) void gemm_skinny_kernel(GemmA
     const int64_t PG4 = packed_groups4(G);  // 4-group scale blocks per row (prepacked)
     const __amdgpu_buffer_rsrc_t rs =
         make_rsrc(a.ws + (int64_t)e * a.s_estride, (uint32_t)(PK ? N * PG4 * 16 : N * G * 4));
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.act, (uint32_t)(a.act_rows * K));
-    uint32_t vw[kNF], vs[kNF], va[NT];
+    uint32_t vw[kNF], vs[kNF];
 #pragma unroll
     for (int f = 0; f < kNF; ++f) {
         // (prepacked: the rows of a fragment are 16-aligned, nrow % 16 == c16
@@ -111,9 +150,47 @@ __global__ __launch_bounds__(256, NT == 2 ? 2 : 1) void gemm_skinny_kernel(GemmA
         vs[f] = PK ? (uint32_t)(((nrow[f] >> 4) * PG4 * 16 + (nrow[f] & 15)) * 16)
                    : (uint32_t)(nrow[f] * G * 4);
     }
+    // Activation rows of a group (BM x 128 bytes), two ways:
+    //  * SHARED: loaded once per workgroup straight into LDS (kAPer loads of
+    //    kALane bytes per lane and wave) and read from there by all four
+    //    waves.  Byte b of a buffer is byte b % 16 of slot b / 16, and slot s
+    //    holds chunk (s % 8) ^ (row % 8) of row s / 8 (the XOR keeps the
+    //    readers' 16-byte reads on distinct banks); a ring of DW + 1 buffers,
+    //    one per group in flight plus the one being read, and a workgroup
+    //    barrier per group.
+    //  * otherwise every wave loads all BM rows into its registers through
+    //    the ring, 2 x 16 bytes per lane and row slice.
+    // Sharing cuts the L2-to-CU traffic of the activations by 4x; the barrier
+    // makes the waves run in step.  Measured per fused call (32 of 256
+    // experts, top-8): the 16-row down GEMM 45.7 -> 43.0 us, 128 tokens
+    // (32-row blocks) 180.7 -> 172.3 us; the 16-row gate_up GEMM (heavier
+    // per group, two waves per SIMD) 86.1 -> 88.6 us and 64-row blocks (one
+    // wave per SIMD) 231 -> 249 us at 256 tokens lose, so they keep the
+    // per-wave loads.
+    constexpr bool SHARED = NT == 2 || (NT == 1 && EPI == EPI_F32);
+    constexpr int kABytes = BM * kGroup;
+    constexpr int kALane = kABytes >= 16 * 64 * kWaves ? 16 : 4;  // bytes per lane per load
+    constexpr int kAPer = SHARED ? kABytes / (kALane * 64 * kWaves) : 0;  // loads per wave per group
+    static_assert(!SHARED || kAPer * kALane * 64 * kWaves == kABytes, "the waves cover the rows exactly");
+    constexpr int kABuf = DW + 1;
+    __shared__ __attribute__((aligned(16))) uint8_t s_act[SHARED ? kABuf * kABytes : 16];
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);  // M0 operands must be wave-uniform
+    const v4i ras = sgpr_rsrc(a.act, (uint32_t)(a.act_rows * K));
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.act, (uint32_t)(a.act_rows * K));
+    const uint32_t s_act_lds = (uint32_t)(uintptr_t)(lds_ptr_t)s_act;
+    uint32_t va[SHARED ? kAPer : NT];
+    if constexpr (SHARED) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
-        va[t] = (uint32_t)((int64_t)act_row(16 * t + c16) * K + 16 * q);
+        for (int j = 0; j < kAPer; ++j) {
+            const int b = (wave + kWaves * j) * 64 * kALane + kALane * lane;  // LDS byte of the lane
+            const int sl = b >> 4, row = sl >> 3;
+            va[j] = (uint32_t)((int64_t)act_row(row) * K + 16 * ((sl & 7) ^ (row & 7)) + (b & 15));
+        }
+    } else {
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            va[t] = (uint32_t)((int64_t)act_row(16 * t + c16) * K + 16 * q);
+    }
 
     // Side data of the block's rows for every group, staged in LDS: its loads
     // are issued first, the ring's behind them, so waiting for the side data
@@ -170,8 +247,29 @@ __global__ __launch_bounds__(256, NT == 2 ? 2 : 1) void gemm_skinny_kernel(GemmA
     v4i wb[DW][kNF];
     float sb[SW4 ? 1 : DW][kNF];
     float4 sc4[SW4 ? kNF : 1], sn4[SW4 ? kNF : 1];
-    v4i ab[DW][NT][2];
-    auto load_group = [&](int s, int g) {
+    v4i ab[SHARED ? 1 : DW][NT][2];
+    // SHARED: the loads issued after a group's activation chunks up to its
+    // consumption (the count of the explicit wait before the group's
+    // barrier): the group's weight (and scale) loads, the DW - 1 groups
+    // behind it and, in the first DW groups of a turn of U, the next scale
+    // block issued at the turn's start.  The direct-to-LDS loads are inline
+    // assembly the compiler does not count, so its own waits for the weights
+    // only ever wait longer than needed.
+    constexpr int kWLoads = SW4 ? kNF : 2 * kNF;
+    constexpr int kAfter = kWLoads + (DW - 1) * (kAPer + kWLoads);
+    auto load_group = [&](int s, int g, int buf) {
+        if constexpr (SHARED) {
+            // activation chunks first, so that the wait for them has the same
+            // count on every group
+#pragma unroll
+            for (int j = 0; j < kAPer; ++j) {
+                const uint32_t d = s_act_lds + (uint32_t)(buf * kABytes + (wave_s + kWaves * j) * 64 * kALane);
+                if (kALane == 16)
+                    lds_load16(ras, d, va[j], (uint32_t)g * kGroup);
+                else
+                    lds_load4(ras, d, va[j], (uint32_t)g * kGroup);
+            }
+        }
 #pragma unroll
         for (int f = 0; f < kNF; ++f) {
             wb[s][f] = bload16(rw, vw[f], (uint32_t)g * (PK ? 1024u : 64u));
@@ -179,11 +277,13 @@ __global__ __launch_bounds__(256, NT == 2 ? 2 : 1) void gemm_skinny_kernel(GemmA
                 sb[s][f] = bload4f(rs, vs[f], PK ? (uint32_t)(g >> 2) * 256u + (uint32_t)(g & 3) * 4u
                                                   : (uint32_t)g * 4u);
         }
+        if constexpr (!SHARED) {
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
+            for (int t = 0; t < NT; ++t)
 #pragma unroll
-            for (int v = 0; v < 2; ++v)
-                ab[s][t][v] = bload16(ra, va[t], (uint32_t)g * kGroup + 64u * v);
+                for (int v = 0; v < 2; ++v)
+                    ab[s][t][v] = bload16(ra, va[t], (uint32_t)g * kGroup + 64u * v);
+        }
     };
     auto load_scales4 = [&](float4 (&dst)[SW4 ? kNF : 1], int blk) {  // groups 4blk..4blk+3
         if (SW4) {
@@ -196,7 +296,7 @@ __global__ __launch_bounds__(256, NT == 2 ? 2 : 1) void gemm_skinny_kernel(GemmA
     load_scales4(sc4, 0);
 #pragma unroll
     for (int s = 0; s < DW; ++s)
-        load_group(s, s < G ? s : G - 1);
+        load_group(s, s < G ? s : G - 1, s);
     __builtin_amdgcn_sched_barrier(0);
 
     if (side_in_regs) {
@@ -227,6 +327,26 @@ __global__ __launch_bounds__(256, NT == 2 ? 2 : 1) void gemm_skinny_kernel(GemmA
                 load_scales4(sn4, g0 / 4 + 1 < G4 ? g0 / 4 + 1 : G4 - 1);
                 __builtin_amdgcn_sched_barrier(0);
             }
+            // SHARED: group g's activation chunks have landed in LDS (each wave
+            // waits for its own; the barrier publishes them and orders every
+            // wave's reads of group g - 1, whose buffer the refill below
+            // overwrites, before that refill)
+            const uint8_t* sa = s_act + (g % kABuf) * kABytes;
+            if constexpr (SHARED) {
+                __builtin_amdgcn_sched_barrier(0);
+                if (SW4 && u < DW)
+                    wait_vmcnt<kAfter + (SW4 ? kNF : 0)>();
+                else
+                    wait_vmcnt<kAfter>();
+                asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            auto act16 = [&](int t, int v) {  // the lane's chunk 4v + q of row 16t + c16
+                if constexpr (SHARED)
+                    return *(const v4i*)(sa + 16 * ((16 * t + c16) * 8 + ((4 * v + q) ^ (c16 & 7))));
+                else
+                    return ab[s][t][v];
+            };
             // int4: the weight scale (0 on padding groups); fp4: the bits of
             // the group's UE8M0 dword
             float swf[kNF];
@@ -271,8 +391,8 @@ __global__ __launch_bounds__(256, NT == 2 ? 2 : 1) void gemm_skinny_kernel(GemmA
                     for (int t = 0; t < NT; ++t) {
                         if (t > 0 && 16 * t >= rows)
                             continue;
-                        const v8h ah = fp8x8_to_f16((uint32_t)ab[s][t][c >> 1][2 * (c & 1)],
-                                                    (uint32_t)ab[s][t][c >> 1][2 * (c & 1) + 1]);
+                        const v4i ac = act16(t, c >> 1);
+                        const v8h ah = fp8x8_to_f16((uint32_t)ac[2 * (c & 1)], (uint32_t)ac[2 * (c & 1) + 1]);
 #pragma unroll
                         for (int f = 0; f < kNF; ++f)
                             raws[t][f] = mfma16x16x32_f16(ah, bc[f], c == 0 ? v4f{0.0f, 0.0f, 0.0f, 0.0f} : raws[t][f]);
@@ -308,10 +428,11 @@ __global__ __launch_bounds__(256, NT == 2 ? 2 : 1) void gemm_skinny_kernel(GemmA
                 const float c1[4] = {s01.x, s01.z, s23.x, s23.z};
                 const float c0[4] = {s01.y, s01.w, s23.y, s23.w};
                 uint32_t at[8];
+                const v4i a0 = act16(t, 0), a1 = act16(t, 1);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    at[i] = (uint32_t)ab[s][t][0][i];
-                    at[4 + i] = (uint32_t)ab[s][t][1][i];
+                    at[i] = (uint32_t)a0[i];
+                    at[4 + i] = (uint32_t)a1[i];
                 }
                 // all MFMAs of the step first, each fragment into its own
                 // accumulator, so they issue back to back; then the promotion
@@ -436,7 +557,7 @@ __global__ __launch_bounds__(256, NT == 2 ? 2 : 1) void gemm_skinny_kernel(GemmA
             // barrier the scheduler sinks each load next to its consumer and
             // only one load stays in flight
             __builtin_amdgcn_sched_barrier(0);
-            load_group(s, g + DW < G ? g + DW : G - 1);
+            load_group(s, g + DW < G ? g + DW : G - 1, (g + DW) % kABuf);
             __builtin_amdgcn_sched_barrier(0);
         }
         if (SW4) {
@@ -445,6 +566,9 @@ __global__ __launch_bounds__(256, NT == 2 ? 2 : 1) void gemm_skinny_kernel(GemmA
                 sc4[f] = sn4[f];
         }
     }
+    // the last turns' refills (never read) land before the block's LDS is freed
+    if constexpr (SHARED)
+        wait_vmcnt<0>();
 
     // ---- epilogues ----  output element (row 16t+4q+r of the block, weight row nrow[f])
     if (EPI == EPI_F32 || EPI == EPI_BF16) {
