@@ -257,6 +257,12 @@ __device__ __forceinline__ v4i bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff, 
 {
     return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
 }
+// The same load with the non-temporal cache policy (nt): for streams read
+// once, so that they do not push the data that is reused out of the caches.
+__device__ __forceinline__ v4i bload16_nt(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 2);
+}
 __device__ __forceinline__ float bload4f(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
 {
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0));
