@@ -319,3 +319,38 @@ def test_fused_moe_repeatable_and_workspace_reuse(dev):
     a = run_fused(d, cfg, dev)
     b = run_fused(d, cfg, dev)
     assert np.array_equal(a, b)
+
+
+# The output and the workspace start as all-ones bytes (bf16 NaN, counters at
+# -1): every output element, including the +0 rows of tokens without a local
+# expert, must be written by the call, and the summation counters of the
+# fused combine must be cleared by the call itself.  Two calls in a row on the
+# same buffers, the second with other routing and fewer tokens.
+@pytest.mark.parametrize("case", ["skinny16", "skinny32", "skinny64", "tile"])
+def test_fused_moe_poisoned_buffers(dev, case):
+    shapes = {"skinny16": (64, 256, 128, 64, 8, 0, 32),
+              "skinny32": (96, 256, 128, 32, 4, 8, 16),
+              "skinny64": (160, 256, 128, 16, 4, 0, 8),
+              "tile": (512, 256, 256, 8, 2, 0, 4)}[case]
+    T, H, I, E, k, eb, El = shapes
+    cfg1, d1 = synth.random_moe(T, H, I, E, k, eb, El, seed=61)
+    cfg2, d2 = synth.random_moe(T - 7, H, I, E, k, eb, El, seed=62)
+    d2["topk_ids"][:5] = -1  # tokens with no expert at all
+    need = w4.fused_moe_workspace_bytes(T, H, k, El, I)
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device=dev)
+    out = torch.full((T, H), -1, dtype=torch.int16, device=dev).view(torch.bfloat16)
+    lay = w4.fused_moe_workspace_layout(T, H, k, El, I)
+    assert lay["block_m"] == {"skinny16": 16, "skinny32": 32, "skinny64": 64, "tile": 160}[case]
+    w = [tuple(dput(d[n], dev) for n in ("w13", "s13", "w2", "s2")) for d in (d1, d2)]
+    for cfg, d, wt in ((cfg1, d1, w[0]), (cfg2, d2, w[1])):
+        o = out[:cfg.T]
+        w4.fused_moe(bf16_dev(d["hidden"], dev), dput(d["topk_ids"], dev), dput(d["topk_weights"], dev),
+                     cfg.expert_begin, cfg.E_local, *wt, out=o, workspace=ws)
+        torch.cuda.synchronize()
+        got = bf16_host(o)
+        ref = oracle_rows(d, cfg, np.arange(cfg.T))
+        assert not np.any(np.isnan(got)), case
+        ids = d["topk_ids"]
+        none_local = ~np.any((ids >= cfg.expert_begin) & (ids < cfg.expert_begin + cfg.E_local), axis=1)
+        assert np.all(got[none_local] == 0), case
+        assert_bf16_close(got, ref, case)
