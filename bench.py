@@ -203,7 +203,7 @@ def stage_breakdown(wl, steps):
 # Kernel sources whose HBM traffic the committed counter summary describes;
 # the summary's figure is reported only while they are unchanged.
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "decode_T64_gate_up_traffic.md")
-TRAFFIC_SOURCES = ("gemm_skinny.hip", "common.hpp", "internal.hpp")
+TRAFFIC_SOURCES = ("gemm_skinny.hip", "common.hpp", "internal.hpp", "lds_direct.hpp")
 
 
 def kernel_source_digest(names=TRAFFIC_SOURCES):

@@ -25,49 +25,13 @@
 //                SGLang PR #7762: SiLU-and-Mul between the grouped GEMMs).
 #include "common.hpp"
 #include "internal.hpp"
+#include "lds_direct.hpp"
 
 
 namespace w4a8 {
 
 constexpr int kWaves = 4;
 
-namespace {
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
-// buffer descriptor in SGPRs (raw, stride 0, num_records = bytes)
-__device__ __forceinline__ v4i sgpr_rsrc(const void* base, uint32_t bytes)
-{
-    const uint64_t b = (uint64_t)base;
-    v4i r;
-    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)b);
-    r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
-    r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
-    r[3] = 0x00020000;
-    return r;
-}
-// 64 lanes x 16 bytes from the buffer into LDS at lds + 16 * lane
-__device__ __forceinline__ void lds_load16(const v4i& r, uint32_t lds, uint32_t voff, uint32_t soff)
-{
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                 :
-                 : "s"(lds), "v"(voff), "s"(r), "s"(soff)
-                 : "memory", "m0");
-}
-// 64 lanes x 4 bytes from the buffer into LDS at lds + 4 * lane
-__device__ __forceinline__ void lds_load4(const v4i& r, uint32_t lds, uint32_t voff, uint32_t soff)
-{
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
-                 :
-                 : "s"(lds), "v"(voff), "s"(r), "s"(soff)
-                 : "memory", "m0");
-}
-template <int N>
-__device__ __forceinline__ void wait_vmcnt()
-{
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-}  // namespace
 
 // NF: weight fragments (16 rows) per wave.  FP4: prepacked fp4 e2m1 weights
 // with UE8M0 scale dwords (DeepGEMM PR #53, Changes): the f16 path converts
@@ -345,7 +309,7 @@ __global__ __launch_bounds__(256, NT == 2 ? 2 : 1) void gemm_skinny_kernel(GemmA
                     wait_vmcnt<kAfter + (SW4 ? kNF : 0)>();
                 else
                     wait_vmcnt<kAfter>();
-                asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+                barrier();
                 __builtin_amdgcn_sched_barrier(0);
             }
             auto act16 = [&](int t, int v) {  // the lane's chunk 4v + q of row 16t + c16

@@ -48,6 +48,7 @@
 //                per-token FP8 requant).
 #include "common.hpp"
 #include "internal.hpp"
+#include "lds_direct.hpp"
 
 
 namespace w4a8 {
@@ -80,60 +81,6 @@ constexpr int kBLoads = kTBN * kGroup / 2 / 16 / 64;    // 16
 constexpr int kSideLoads = kTBM * 2 / 64;               // 5
 static_assert(kALoads > 16 && kALoads <= 24 && kBLoads == 16 && kSideLoads == 5,
               "the load assignment below is written for a 160 x 256 tile");
-
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
-// Buffer descriptor in SGPRs (raw, stride 0, num_records = bytes).
-__device__ __forceinline__ v4i sgpr_rsrc(const void* base, uint32_t bytes)
-{
-    const uint64_t b = (uint64_t)base;
-    v4i r;
-    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)b);
-    r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
-    r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
-    r[3] = 0x00020000;
-    return r;
-}
-
-// 64 lanes x 16 (or 4) bytes from the buffer into LDS at lds + lane * 16 (or
-// 4).  Issued from inline assembly so that the compiler's wait-count pass,
-// which cannot tell the stages apart, does not drain every stage in flight
-// before each LDS read; the kernel waits explicitly (wait_vmcnt + barrier).
-// M0 (the LDS destination) is set inside each block.  The compiler treats M0
-// as reserved and ignores the clobber; it sets M0 itself right before any
-// instruction of its own that reads it, and in these kernels M0 appears only
-// in these sequences, so no value of the compiler's is live across them.
-__device__ __forceinline__ void lds_load16(const v4i& r, uint32_t lds, uint32_t voff, uint32_t soff)
-{
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                 :
-                 : "s"(lds), "v"(voff), "s"(r), "s"(soff)
-                 : "memory", "m0");
-}
-__device__ __forceinline__ void lds_load4(const v4i& r, uint32_t lds, uint32_t voff, uint32_t soff)
-{
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
-                 :
-                 : "s"(lds), "v"(voff), "s"(r), "s"(soff)
-                 : "memory", "m0");
-}
-
-// s_waitcnt vmcnt(N), leaving the other counters alone
-template <int N>
-__device__ __forceinline__ void wait_vmcnt()
-{
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
-// A workgroup barrier that is also a compiler memory barrier, without the
-// release/acquire fence of __syncthreads (which would wait for every load in
-// flight, including the stages still being filled).
-__device__ __forceinline__ void barrier()
-{
-    // this wave's LDS reads are complete before anyone may overwrite them
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
 
 // 16-byte slot of (activation row, chunk 0..7) and of (weight row, chunk 0..3)
 __device__ __forceinline__ int a_slot(int row, int chunk)
