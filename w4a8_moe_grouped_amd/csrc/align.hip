@@ -299,33 +299,61 @@ __global__ __launch_bounds__(kAlignThreads) void align_scan_kernel(int32_t* __re
                                                                    int64_t nchunks, int64_t E,
                                                                    int64_t block_m, AlignOut o)
 {
+    // hist[c * E + e] = pairs of local expert e in chunk c  ->  the sorted
+    // position of the first of them.  Two levels, so that every thread has
+    // work: thread i = g * E + e sums expert e over chunk group g (ng groups
+    // of cpg consecutive chunks; one group when E exceeds the block), the
+    // group sums are prefixed per expert in LDS, the experts' totals go
+    // through finish_scan, and each thread writes its group's running bases.
     __shared__ AlignLds L;
+    __shared__ int part[kMaxLocalExperts];  // [g][e]: group sums, then their exclusive prefix
     const int t = threadIdx.x;
-    // per expert: chunk-exclusive prefix (in place) and the total; the
-    // counts are read 16 chunks at a time so the loads overlap
-    constexpr int kBatch = 16;
-    for (int e = t; e < E; e += kAlignThreads) {
+    const int ng = E <= kAlignThreads ? kAlignThreads / (int)E : 1;
+    const int64_t cpg = (nchunks + ng - 1) / ng;
+    constexpr int kBatch = 8;  // counts read per batch, so the loads overlap
+    for (int i = t; i < ng * E; i += kAlignThreads) {
+        const int g = i / (int)E, e = i - g * (int)E;
+        const int64_t c0 = g * cpg, c1 = c0 + cpg < nchunks ? c0 + cpg : nchunks;
         int run = 0;
-        for (int64_t c0 = 0; c0 < nchunks; c0 += kBatch) {
+        for (int64_t c = c0; c < c1; c += kBatch) {
             int h[kBatch];
 #pragma unroll
             for (int j = 0; j < kBatch; ++j)
-                h[j] = c0 + j < nchunks ? hist[(c0 + j) * E + e] : 0;
+                h[j] = c + j < c1 ? hist[(c + j) * E + e] : 0;
 #pragma unroll
-            for (int j = 0; j < kBatch; ++j) {
-                if (c0 + j < nchunks)
-                    hist[(c0 + j) * E + e] = run;
+            for (int j = 0; j < kBatch; ++j)
                 run += h[j];
-            }
+        }
+        part[i] = run;
+    }
+    __syncthreads();
+    for (int e = t; e < E; e += kAlignThreads) {
+        int run = 0;
+        for (int g = 0; g < ng; ++g) {
+            const int v = part[g * E + e];
+            part[g * E + e] = run;
+            run += v;
         }
         L.a[e] = run;
     }
     __syncthreads();
-    finish_scan(L.a, L.b, L.scratch, E, block_m, o);
-    for (int e = t; e < E; e += kAlignThreads) {
-        const int off = L.a[e];
-        for (int64_t c = 0; c < nchunks; ++c)
-            hist[c * E + e] += off;
+    finish_scan(L.a, L.b, L.scratch, E, block_m, o);  // L.a now holds the experts' offsets
+    for (int i = t; i < ng * E; i += kAlignThreads) {
+        const int g = i / (int)E, e = i - g * (int)E;
+        const int64_t c0 = g * cpg, c1 = c0 + cpg < nchunks ? c0 + cpg : nchunks;
+        int run = L.a[e] + part[i];
+        for (int64_t c = c0; c < c1; c += kBatch) {
+            int h[kBatch];
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j)
+                h[j] = c + j < c1 ? hist[(c + j) * E + e] : 0;
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) {
+                if (c + j < c1)
+                    hist[(c + j) * E + e] = run;
+                run += h[j];
+            }
+        }
     }
 }
 
