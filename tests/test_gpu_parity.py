@@ -252,6 +252,20 @@ def test_fused_moe_sampled_tokens(dev, name, nsample):
     assert np.all(got[none_local] == 0)
 
 
+# 32-row m-blocks at the model's dimensions (H=7168, I=2048: 56 and 16 K-groups),
+# the path whose activation rows go through LDS once per workgroup
+def test_fused_moe_32_row_blocks_full_dims(dev):
+    cfg, d = synth.random_moe(128, 7168, 2048, 256, 8, 0, 32, seed=71)
+    lay = w4.fused_moe_workspace_layout(cfg.T, cfg.H, cfg.topk, cfg.E_local, cfg.I)
+    assert lay["block_m"] == 32, lay["block_m"]
+    got = run_fused(d, cfg, dev)
+    rng = np.random.default_rng(72)
+    rows = np.sort(rng.choice(cfg.T, size=16, replace=False))
+    rows[0], rows[-1] = 0, cfg.T - 1
+    ref = oracle_rows(d, cfg, rows)
+    assert_bf16_close(got[rows], ref, "T=128 32-row blocks (16 sampled tokens)")
+
+
 @pytest.mark.parametrize("case", ["one_expert_many_rows", "single_token", "k1_e1",
                                   "non_local_mix", "topk32", "small_dims", "all_non_local",
                                   "two_slices"])
