@@ -27,6 +27,8 @@
 #include "internal.hpp"
 #include "lds_direct.hpp"
 
+#include <type_traits>
+
 
 namespace w4a8 {
 
@@ -176,6 +178,32 @@ __global__ __launch_bounds__(256, NT == 2 ? 2 : 1) void gemm_skinny_kernel(GemmA
         }
     }
 
+    // STAGED (16-row blocks of the down and dense GEMMs whose rows fit the
+    // stage capacity the launch set aside; at decode a block holds 1-6 real
+    // rows): the block's activation rows over the whole K are loaded once,
+    // straight into LDS, before the ring starts, and every group reads them
+    // from there: no activation loads and no barriers inside the K loop.  Row
+    // stride K + 16 bytes, so the 16 rows' reads of one column spread over the
+    // banks.  Other blocks take the loop below with the rows shared per group;
+    // the choice is per workgroup and the two K loops are separate instances.
+    // Measured per fused call (32 of 256 experts, 64 tokens, median of 7
+    // interleaved runs): down 42.4 -> 40.9 us; the same for the 16-row gate_up
+    // (K = 7168, 9 rows of capacity) measured 80.2 -> 81.0 us and is not used.
+    constexpr bool kStage = NT == 1 && SG == 128 && EPI != EPI_SWIGLU_Q;
+    const bool staged = kStage && rows <= a.stage_rows;
+    const int64_t KS = K + 16;
+    uint8_t* const stage = (uint8_t*)lds_side4 + ((int64_t)nside * 8 + 15) / 16 * 16;
+    if (kStage && staged) {
+        const uint32_t st_lds = (uint32_t)(uintptr_t)(lds_ptr_t)stage;
+        const int per_row = (int)(K / 1024);  // 1 KB pieces (K % 1024 == 0 when stage_rows > 0)
+        const int npieces = rows * per_row;
+        for (int p = wave_s; p < npieces; p += kWaves) {
+            const int r = p / per_row, j = p - r * per_row;
+            lds_load16(ras, st_lds + (uint32_t)(r * KS + j * 1024), (uint32_t)(16 * lane),
+                       (uint32_t)((int64_t)act_row(r) * K + j * 1024));
+        }
+    }
+
     // Promotion in fp32 on both paths.  On the f16 (gate_up) path each group's
     // MFMA sum is the correctly rounded fp32 value of an exact dot product, so
     // y carries only the fp32 roundings of the running sum, and the SwiGLU +
@@ -215,10 +243,14 @@ __global__ __launch_bounds__(256, NT == 2 ? 2 : 1) void gemm_skinny_kernel(GemmA
     // the ring slot.
     static_assert(!SW4 || 4 % DW == 0, "float4 scales need DW to divide 4");
     constexpr int U = SW4 ? 4 : DW;
+    // (always_inline: not inlined, the lambda took the fp4 down instance from
+    // 100 to 156 VGPRs)
+    auto k_loop = [&](auto staged_tag) __attribute__((always_inline)) {
+    constexpr bool ST = decltype(staged_tag)::value;
     v4i wb[DW][kNF];
     float sb[SW4 ? 1 : DW][kNF];
     float4 sc4[SW4 ? kNF : 1], sn4[SW4 ? kNF : 1];
-    v4i ab[SHARED ? 1 : DW][NT][2];
+    v4i ab[SHARED || ST ? 1 : DW][NT][2];
     // SHARED: the loads issued after a group's activation chunks up to its
     // consumption (the count of the explicit wait before the group's
     // barrier): the group's weight (and scale) loads, the DW - 1 groups
@@ -229,7 +261,7 @@ __global__ __launch_bounds__(256, NT == 2 ? 2 : 1) void gemm_skinny_kernel(GemmA
     constexpr int kWLoads = SW4 ? kNF : 2 * kNF;
     constexpr int kAfter = kWLoads + (DW - 1) * (kAPer + kWLoads);
     auto load_group = [&](int s, int g, int buf) {
-        if constexpr (SHARED) {
+        if constexpr (SHARED && !ST) {
             // activation chunks first, so that the wait for them has the same
             // count on every group
 #pragma unroll
@@ -248,7 +280,7 @@ __global__ __launch_bounds__(256, NT == 2 ? 2 : 1) void gemm_skinny_kernel(GemmA
                 sb[s][f] = bload4f(rs, vs[f], PK ? (uint32_t)(g >> 2) * 256u + (uint32_t)(g & 3) * 4u
                                                   : (uint32_t)g * 4u);
         }
-        if constexpr (!SHARED) {
+        if constexpr (!SHARED && !ST) {
 #pragma unroll
             for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -281,6 +313,10 @@ __global__ __launch_bounds__(256, NT == 2 ? 2 : 1) void gemm_skinny_kernel(GemmA
         for (int i = tid; i < nside; i += 256)
             lds_side[i] = side_of(i);
     }
+    // STAGED: the rows have landed (loads after them: the first scale block
+    // and the ring); the barrier below publishes them
+    if constexpr (ST)
+        wait_vmcnt<(SW4 ? kNF : 0) + DW * kWLoads>();
     __syncthreads();
 
     const int G4 = G / 4;
@@ -303,7 +339,9 @@ __global__ __launch_bounds__(256, NT == 2 ? 2 : 1) void gemm_skinny_kernel(GemmA
             // wave's reads of group g - 1, whose buffer the refill below
             // overwrites, before that refill)
             const uint8_t* sa = s_act + (g % kABuf) * kABytes;
-            if constexpr (SHARED) {
+            if constexpr (ST)  // keep each group's LDS reads in its group (no hoisting across groups)
+                asm volatile("" ::: "memory");
+            if constexpr (SHARED && !ST) {
                 __builtin_amdgcn_sched_barrier(0);
                 if (SW4 && u < DW)
                     wait_vmcnt<kAfter + (SW4 ? kNF : 0)>();
@@ -313,7 +351,10 @@ __global__ __launch_bounds__(256, NT == 2 ? 2 : 1) void gemm_skinny_kernel(GemmA
                 __builtin_amdgcn_sched_barrier(0);
             }
             auto act16 = [&](int t, int v) {  // the lane's chunk 4v + q of row 16t + c16
-                if constexpr (SHARED)
+                if constexpr (ST)  // (padding rows read row 0)
+                    return *(const v4i*)(stage + (16 * t + c16 < rows ? 16 * t + c16 : 0) * KS +
+                                         (int64_t)gl * kGroup + 16 * (4 * v + q));
+                else if constexpr (SHARED)
                     return *(const v4i*)(sa + 16 * ((16 * t + c16) * 8 + ((4 * v + q) ^ (c16 & 7))));
                 else
                     return ab[s][t][v];
@@ -538,8 +579,17 @@ __global__ __launch_bounds__(256, NT == 2 ? 2 : 1) void gemm_skinny_kernel(GemmA
         }
     }
     // the last turns' refills (never read) land before the block's LDS is freed
-    if constexpr (SHARED)
+    if constexpr (SHARED && !ST)
         wait_vmcnt<0>();
+    };
+    if constexpr (kStage) {
+        if (staged)
+            k_loop(std::true_type{});
+        else
+            k_loop(std::false_type{});
+    } else {
+        k_loop(std::false_type{});
+    }
 
     // ---- epilogues ----  output element (row 16t+4q+r of the block, weight row nrow[f])
     if (EPI == EPI_F32 || EPI == EPI_BF16) {
@@ -660,10 +710,24 @@ __global__ __launch_bounds__(256, NT == 2 ? 2 : 1) void gemm_skinny_kernel(GemmA
 }
 
 template <int NT, int EPI, int DW, bool F16, bool SW4, bool PK, bool FP4, int NF = 4, int SG = 128>
-static hipError_t launch_one(const GemmArgs& a, hipStream_t s)
+static hipError_t launch_one(const GemmArgs& a0, hipStream_t s)
 {
-    const int64_t G = a.K / kGroup;
-    const size_t lds = (size_t)G * (EPI == EPI_F32 ? 128 / SG : 1) * 16 * NT * sizeof(float2);
+    const int64_t G = a0.K / kGroup;
+    const size_t side = (size_t)G * (EPI == EPI_F32 ? 128 / SG : 1) * 16 * NT * sizeof(float2);
+    // 16-row blocks of the down and dense GEMMs: LDS for the whole-K
+    // activation rows of up to stage_rows rows (1 KB pieces, so K % 1024 ==
+    // 0), within a quarter of the CU's LDS (the down instance runs four
+    // workgroups per CU) less the side data, the shared-rows ring of the
+    // fallback loop (static LDS) and 4 KB of other static LDS
+    GemmArgs a = a0;
+    a.stage_rows = 0;
+    if (NT == 1 && SG == 128 && EPI != EPI_SWIGLU_Q && a.K % 1024 == 0) {
+        const int64_t ring = EPI == EPI_F32 ? (DW + 1) * 16 * kGroup : 0;
+        const int64_t share = 160 * 1024 / 4 - 4096 - (int64_t)side - ring;
+        const int64_t r = share / (a.K + 16);
+        a.stage_rows = (int32_t)(r < 16 ? (r > 0 ? r : 0) : 16);
+    }
+    const size_t lds = side + (a.stage_rows > 0 ? 16 + (size_t)a.stage_rows * (size_t)(a.K + 16) : 0);
     dim3 grid;
     if (EPI == EPI_SWIGLU_Q)
         grid.x = (unsigned)(a.I / kGroup);

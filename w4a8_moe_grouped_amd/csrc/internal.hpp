@@ -84,6 +84,9 @@ struct GemmArgs {
     // reads them; side data [rows, K/sub_group]); skinny kernel only
     int sub_group;
     int64_t max_blocks;    // grid bound on m-blocks
+    // skinny kernel, 16-row m-blocks: blocks of at most this many rows read
+    // their activations from a whole-K copy in LDS (set by the launcher)
+    int32_t stage_rows;
 };
 enum Epilogue { EPI_F32 = 0, EPI_BF16 = 1, EPI_SWIGLU_Q = 2 };
 hipError_t launch_gemm_skinny(const GemmArgs& a, int epilogue, int block_m, hipStream_t s);
