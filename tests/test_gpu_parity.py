@@ -268,7 +268,7 @@ def test_fused_moe_32_row_blocks_full_dims(dev):
 
 @pytest.mark.parametrize("case", ["one_expert_many_rows", "single_token", "k1_e1",
                                   "non_local_mix", "topk32", "small_dims", "all_non_local",
-                                  "two_slices", "g3_16row", "g3_32row"])
+                                  "two_slices", "g3_16row", "g3_32row", "staged_and_not_16row"])
 def test_fused_moe_edge_cases(dev, case):
     if case == "one_expert_many_rows":   # every pair on expert 2: many full blocks + a partial one
         cfg, d = synth.random_moe(150, 256, 256, 8, 2, 0, 8, seed=21)
@@ -289,6 +289,9 @@ def test_fused_moe_edge_cases(dev, case):
         cfg, d = synth.random_moe(64, 256, 384, 64, 8, 0, 32, seed=29)
     elif case == "g3_32row":        # 32-row blocks, K = 384 both GEMMs: 3 groups, ring of 2, shared rows
         cfg, d = synth.random_moe(96, 384, 384, 32, 4, 8, 16, seed=30)
+    elif case == "staged_and_not_16row":  # ~16 rows per expert, down K = 2048: blocks with up to
+        # 11 rows read a whole-K copy from LDS, fuller ones the per-group path
+        cfg, d = synth.random_moe(128, 256, 2048, 64, 8, 0, 64, seed=37)
     elif case == "all_non_local":   # no m-block at all: the output is +0 everywhere
         cfg, d = synth.random_moe(48, 256, 128, 8, 2, 4, 4, seed=27)
         d["topk_ids"][:] = d["topk_ids"] % 4
