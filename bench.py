@@ -69,6 +69,21 @@ def moe_flops(cfg, stats):
     return 2.0 * stats["P"] * (cfg.H * 2 * cfg.I + cfg.I * cfg.H)
 
 
+def prefill_entry(cfg, stats, us):
+    """Flat summary of one prefill workload: µs, TFLOP/s, GB/s, the fraction
+    of the dense fp8 MFMA peak and the roofline fraction max(bytes / HBM peak,
+    flops / fp8 peak) / t (whichever bound is the larger)."""
+    fl, by = moe_flops(cfg, stats), moe_bytes(cfg, stats)
+    t = us * 1e-6
+    t_hbm, t_mfma = by / (HBM_PEAK_GBS * 1e9), fl / (FP8_PEAK_TFLOPS * 1e12)
+    return {"workload": cfg.desc, "us": round(us, 1), "P": stats["P"], "A": stats["A"],
+            "tflops": round(fl / t / 1e12, 2), "hbm_gbs": round(by / t / 1e9, 1),
+            "frac_fp8_peak": round(fl / t / 1e12 / FP8_PEAK_TFLOPS, 4),
+            "frac_hbm_peak": round(by / t / 1e9 / HBM_PEAK_GBS, 4),
+            "bound": "mfma" if t_mfma >= t_hbm else "hbm",
+            "roofline_frac": round(max(t_hbm, t_mfma) / t, 4)}
+
+
 class Workload:
     def __init__(self, name, nsets, dev, prepack=True, fp4=False, recipe=0):
         import torch
@@ -479,24 +494,20 @@ def main():
     }
 
     if not args.no_prefill and args.only is None:
-        pre = {}
         # steady state: ~20 ms of warm-up and two weight sets alternating, as
-        # for decode, so no step reads the previous step's weights from cache
+        # for decode, so no step reads the previous step's weights from cache.
+        # Each workload is a flat object of scalars under its own key; its
+        # per-stage µs sit beside it under <key>_stages_us.
         for name, steps, warm in (("prefill", 30, 10), ("prefill_ep8", 8, 3)):
             p = Workload(name, nsets=2, dev=dev, prepack=packed)
             pu = time_steps(p, steps, warm)
             pst = stage_breakdown(p, 2)
-            pfl = moe_flops(p.cfg, p.stats)
-            pby = moe_bytes(p.cfg, p.stats)
-            pre[name] = {"workload": p.cfg.desc, "us": round(pu, 1), "P": p.stats["P"],
-                         "tflops": round(pfl / (pu * 1e-6) / 1e12, 2),
-                         "frac_fp8_peak": round(pfl / (pu * 1e-6) / 1e12 / FP8_PEAK_TFLOPS, 4),
-                         "hbm_gbs": round(pby / (pu * 1e-6) / 1e9, 1),
-                         "stages_us": {k: round(v, 1) for k, v in pst.items()}}
-            log("[bench] %s: %s" % (name, pre[name]))
+            ent = prefill_entry(p.cfg, p.stats, pu)
+            result[name] = ent
+            result[name + "_stages_us"] = {k: round(v, 1) for k, v in pst.items()}
+            log("[bench] %s: %s stages %s" % (name, ent, result[name + "_stages_us"]))
             del p
             torch.cuda.empty_cache()
-        result["prefill"] = pre
 
     if not args.no_prefill and args.only is None:
         result["other_configs"] = extra_workloads(dev, args.steps)

@@ -50,6 +50,11 @@
  *    W4A8_OK is returned.  Otherwise *workspace_bytes must hold the size of
  *    the buffer supplied.
  *  - Calls that share a workspace or outputs must be ordered by the caller.
+ *  - Size limits (W4A8_ERR_UNSUPPORTED beyond them): the kernels address each
+ *    operand through a buffer resource with 32-bit extent and offsets, so the
+ *    byte size of every activation matrix a GEMM reads (M*K for w4a8_gemm;
+ *    T*H and T*topk*I for the fused forward, every pair counted as local) and
+ *    of one expert's weights (N*K/2; I*H for w13) must stay below 2^32.
  */
 #ifndef W4A8_H
 #define W4A8_H
@@ -102,7 +107,8 @@ int w4a8_quantize_act(const void* x_bf16, int64_t M, int64_t K, int64_t ldx,
  *   b_int4    [N, K/2] packed int4;                 b_scales [N, K/128] fp32
  *   out_bf16  [M, N] bf16, round to nearest even from the fp32 accumulator
  *   workspace device scratch of *workspace_bytes bytes (query with NULL)
- * M >= 0, N > 0, K > 0, K % 128 == 0.  fp32 accumulation order is the
+ * M >= 0, N > 0, K > 0, K % 128 == 0; M*K < 2^32 and N*K/2 < 2^32 bytes,
+ * M <= 4194240 (UNSUPPORTED otherwise).  fp32 accumulation order is the
  * kernel's; the result matches the fp64 definition within rounding.
  */
 int w4a8_gemm(const uint8_t* a_e4m3, const float* a_scales, int64_t M, int64_t K,
@@ -156,7 +162,8 @@ int w4a8_moe_align(const int32_t* topk_ids, int64_t T, int64_t topk,
  *                holds the routing permutation, the fp8 activations and the
  *                intermediates between the kernels of one call
  * T >= 0 (T == 0 launches nothing), H, I > 0 and multiples of 128,
- * 1 <= topk <= 32, E_l >= 1.
+ * 1 <= topk <= 32, 1 <= E_l <= 1024, T*topk <= 2^30 - 1, and the byte
+ * ranges T*H, T*topk*I and I*H below 2^32 (UNSUPPORTED otherwise).
  */
 int w4a8_fused_moe(const void* hidden_bf16, int64_t T, int64_t H,
                    const int32_t* topk_ids, const float* topk_weights, int64_t topk,
@@ -357,8 +364,12 @@ int w4a8_fused_moe_workspace_layout(int64_t T, int64_t H, int64_t topk,
  *   [2] are both recorded after it)
  *   [3] after gate_up+SwiGLU+requant   [4] after down  [5] after combine
  * A null entry is skipped (so a caller can time one stage with two events).
- * n must be 6 (or 0 to disarm).  The call consumes the arming; it never
- * synchronises.  Returns W4A8_ERR_INVALID_ARG for a bad n or a null array.
+ * n must be 6 (or 0 to disarm).  The six handles are copied, so the array
+ * need not outlive this call; the events must stay valid until the armed
+ * call has returned.  The next call of the fused family on this thread
+ * consumes the arming whatever it does: a workspace-size query and a
+ * rejected call disarm it too (and record nothing).  Never synchronises.
+ * Returns W4A8_ERR_INVALID_ARG for a bad n or a null array.
  */
 int w4a8_fused_moe_stage_events(void* const* events, int n);
 

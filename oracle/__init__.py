@@ -93,6 +93,8 @@ def lib():
             L.orc_ue8m0_decode.argtypes = [ctypes.c_uint8]
             L.orc_gemm_fp4_f64.restype = None
             L.orc_gemm_fp4_f64.argtypes = [u8p, f32p, i64, i64, u8p, u8p, i64, f64p]
+            L.orc_swiglu.restype = None
+            L.orc_swiglu.argtypes = [f64p, f64p, i64, f32p]
             L.orc_fused_moe_fp4.restype = ctypes.c_int
             L.orc_fused_moe_fp4.argtypes = [u16p, i64, i64, i32p, f32p, i64, i64, i64, i64,
                                             u8p, u8p, u8p, u8p, u16p, u8p, f32p, f64p]
@@ -253,6 +255,16 @@ def fused_moe_recipe(hidden_bits, topk_ids, topk_weights, expert_begin, num_loca
     fl = ids.ravel()
     Pl = int(np.count_nonzero((fl >= expert_begin) & (fl < expert_begin + E)))
     return out, dict(qh=qh[:Pl], sh=sh[:Pl], y2=y2[:Pl])
+
+
+def swiglu(gate, up) -> np.ndarray:
+    """h = silu(gate) * up (fp64), rounded once to fp32 -- the oracle's SwiGLU step."""
+    g = _c(np.ravel(gate), np.float64)
+    u = _c(np.ravel(up), np.float64)
+    assert g.shape == u.shape
+    h = np.empty(g.size, np.float32)
+    lib().orc_swiglu(_p(g, ctypes.c_double), _p(u, ctypes.c_double), g.size, _p(h, ctypes.c_float))
+    return h.reshape(np.shape(gate))
 
 
 def quantize_f32(x: np.ndarray):

@@ -90,13 +90,6 @@ double orc_e2m1_decode(uint8_t nibble)
     return sign ? -mag : mag;
 }
 
-/* fp4 weights packed two per byte like the int4 ones: k even in the low
- * nibble, k odd in the high nibble. */
-double orc_fp4_value(uint8_t byte, int odd)
-{
-    return orc_e2m1_decode((uint8_t)(odd ? (byte >> 4) : (byte & 0xF)));
-}
-
 /* OCP MX E8M0 scale ([P4] "Changes": per-32-K UE8M0 weight scales): an
  * unsigned power-of-two exponent with bias 127, 0xFF = NaN. */
 double orc_ue8m0_decode(uint8_t e)
@@ -459,6 +452,23 @@ void orc_gemm_ag_f64(const uint8_t* a, const float* sa, int64_t ag, int64_t M, i
 }
 
 /* ------------------------------------------------------------------------ */
+/* SwiGLU between the GEMMs ([P2] "Cutlass W4A8 MoE": SiLU and Mul; [P4]    */
+/* "Changes": L1 GEMM -> SwiGLU)                                             */
+/* ------------------------------------------------------------------------ */
+
+/* h[i] = silu(gate[i]) * up[i] with silu(g) = g * sigmoid(g) = g / (1 + e^-g),
+ * evaluated in fp64 (exp from libm), then rounded once to fp32: the value
+ * the requantisation step reads.  No clamp of g (plain SwiGLU). */
+void orc_swiglu(const double* gate, const double* up, int64_t n, float* h)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        double g = gate[i];
+        double silu = g / (1.0 + exp(-g));
+        h[i] = (float)(silu * up[i]);
+    }
+}
+
+/* ------------------------------------------------------------------------ */
 /* The fused-MoE forward ([P2] "Cutlass W4A8 MoE" workflow; [P4] "Changes") */
 /* ------------------------------------------------------------------------ */
 
@@ -525,12 +535,8 @@ static int fused_moe_impl(const uint16_t* hidden, int64_t T, int64_t H,
                 orc_gemm_fp4_f64(qx + t * H, sx + t * GH, 1, H, w13e, b13e, 2 * I, y1);
             else
                 orc_gemm_f64(qx + t * H, sx + t * GH, 1, H, w13e, s13e, 2 * I, y1);
-            /* 4. SwiGLU in fp64: silu(gate) * up, then one rounding to fp32 */
-            for (int64_t i = 0; i < I; ++i) {
-                double g = y1[i], u = y1[I + i];
-                double hval = g / (1.0 + exp(-g)) * u;
-                h32[i] = (float)hval;
-            }
+            /* 4. SwiGLU: gate rows [0, I), up rows [I, 2I) */
+            orc_swiglu(y1, y1 + I, I, h32);
             /* 5. requantise with the same per-128 rule as the input */
             quantize_rows_f32_n(h32, 1, I, (int)down_group, a2_scale, qh, sh);
             if (qh_out)

@@ -64,7 +64,6 @@ double   orc_e4m3_decode(uint8_t code);
 uint8_t  orc_e4m3_encode(float v);
 int      orc_int4_value(uint8_t byte, int odd);
 double   orc_e2m1_decode(uint8_t nibble);
-double   orc_fp4_value(uint8_t byte, int odd);
 double   orc_ue8m0_decode(uint8_t e);
 double   orc_bf16_to_double(uint16_t bits);
 uint16_t orc_bf16_from_double(double v);
@@ -101,6 +100,9 @@ void orc_gemm_ag_f64(const uint8_t* a, const float* sa, int64_t ag, int64_t M, i
 /* fp4 weights w [N, K/2] (e2m1 nibbles), UE8M0 scales sw [N, K/32] */
 void orc_gemm_fp4_f64(const uint8_t* a, const float* sa, int64_t M, int64_t K,
                       const uint8_t* w, const uint8_t* sw, int64_t N, double* y);
+
+/* ---- step: SwiGLU, h = silu(gate) * up in fp64, rounded once to fp32 ---- */
+void orc_swiglu(const double* gate, const double* up, int64_t n, float* h);
 
 /* ---- the whole forward: align, quant, GEMM1, SwiGLU, requant, GEMM2, combine ----
  * qh [P, I], sh [P, I/128] and y2 [P, H] (pair order = sorted order) are

@@ -94,6 +94,50 @@ def test_quantize_rejects_bad_arguments(L):
     assert q(None, 0, 128, 128, None, None, None) == OK
 
 
+def test_fused_moe_rejects_32bit_range_overflow(L):
+    """Every operand a kernel reads through a buffer resource (32-bit extent
+    and offsets) must stay below 2^32 bytes; validation returns before any
+    launch (the pointers here are bogus and never touched)."""
+    # T*topk*I = 262144 * 8 * 2048 = 2^32: the down GEMM's activation rows
+    assert _fused(L, T=262144, H=128, k=8, E=32, I=2048) == UNSUPPORTED
+    # T*H = 2^32: the gate_up operand
+    assert _fused(L, T=1 << 19, H=8192, k=1, E=32, I=128) == UNSUPPORTED
+    # one expert's w13 (I*H bytes) reaches 2^32
+    assert _fused(L, T=1, H=65536, k=1, E=1, I=65536) == UNSUPPORTED
+    # huge T: no int64 overflow in the checks
+    assert _fused(L, T=1 << 61, H=128, k=32, E=1, I=128) == UNSUPPORTED
+
+
+def test_gemm_rejects_32bit_range_overflow(L):
+    n = ctypes.c_size_t(1 << 62)
+    g = L.w4a8_gemm
+    # M*K = 2^32
+    assert g(BOGUS, BOGUS, 1 << 19, 8192, BOGUS, BOGUS, 16, BOGUS, BOGUS, ctypes.byref(n), None) == UNSUPPORTED
+    # N*K/2 = 2^32
+    assert g(BOGUS, BOGUS, 4, 8192, BOGUS, BOGUS, 1 << 20, BOGUS, BOGUS, ctypes.byref(n), None) == UNSUPPORTED
+    assert g(BOGUS, BOGUS, 1 << 40, 128, BOGUS, BOGUS, 16, BOGUS, BOGUS, ctypes.byref(n), None) == UNSUPPORTED
+
+
+def test_prepack_rejects_32bit_range_overflow(L):
+    other = ctypes.c_void_p(0x2000)
+    # one expert's weights N*K/2 = 2^32
+    assert L.w4a8_prepack_weights(BOGUS, BOGUS, 1, 1 << 20, 8192, other, other, None) == UNSUPPORTED
+
+
+def test_stage_events_arming_is_copied_and_consumed(L):
+    """The handles are copied at arming; any fused call (here a size query)
+    consumes the arming; arming rejects a bad count."""
+    arr = (ctypes.c_void_p * 6)()
+    assert L.w4a8_fused_moe_stage_events(arr, 5) == INVALID
+    assert L.w4a8_fused_moe_stage_events(None, 6) == INVALID
+    assert L.w4a8_fused_moe_stage_events(arr, 6) == OK
+    del arr
+    n = ctypes.c_size_t(0)
+    assert L.w4a8_fused_moe(None, 4, 256, None, None, 2, 0, 4, 128, None, None, None, None, None,
+                            None, ctypes.byref(n), None) == OK
+    assert L.w4a8_fused_moe_stage_events(None, 0) == OK
+
+
 def test_gemm_rejects_bad_arguments(L):
     n = ctypes.c_size_t(1 << 40)
     g = L.w4a8_gemm

@@ -43,6 +43,20 @@ def deinterleave8(mem):
     return out.reshape(P, K)
 
 
+def scale_ulps(got, ref):
+    """fp32 ulp distance of positive scales (bit patterns of positive floats
+    are ordered like their values)."""
+    g = np.asarray(got, np.float32).view(np.int32).astype(np.int64)
+    r = np.asarray(ref, np.float32).view(np.int32).astype(np.int64)
+    return np.abs(g - r)
+
+
+def ulp_hist(ulps):
+    n = ulps.size
+    return "0:%.3f 1:%.3f 2:%.3f >2:%.3f" % tuple(
+        np.count_nonzero(c) / n for c in (ulps == 0, ulps == 1, ulps == 2, ulps > 2))
+
+
 @pytest.mark.parametrize("name", ["tiny", "decode", "skew_id", "tile_small"])
 def test_requant_codes_and_down_output(name):
     assert torch.cuda.is_available()
@@ -76,16 +90,15 @@ def test_requant_codes_and_down_output(name):
     y2 = wsh[lay["y2"]:lay["y2"] + 4 * P * H].view(np.float32).reshape(P, H).astype(np.float64)
 
     code_mis = np.mean(qh != inter["qh"])
-    scale = side[:, :, 0] / np.float32(512)
-    scale_mis = np.mean(scale != inter["sh"])
+    scale = side[:, :, 0] / np.float32(512)  # c1 = 512 * scale: exact
+    ulps = scale_ulps(scale, inter["sh"])
     scale_rel = np.max(np.abs(scale.astype(np.float64) - inter["sh"]) / inter["sh"])
     y2_fro = np.linalg.norm(y2 - inter["y2"]) / np.linalg.norm(inter["y2"])
     y2_max = np.max(np.abs(y2 - inter["y2"])) / np.max(np.abs(inter["y2"]))
-    # with the oracle's own codes, how far is the GPU's down GEMM alone?
-    print("%s: P=%d code mismatch=%.2e (%d of %d) scale mismatch=%.2e (max rel %.1e) "
+    print("%s: P=%d code mismatch=%.2e (%d of %d) scale ulps: %s (max %d, max rel %.1e) "
           "y2 rel_fro=%.3e max=%.3e"
-          % (name, P, code_mis, int(np.sum(qh != inter["qh"])), qh.size, scale_mis, scale_rel,
-             y2_fro, y2_max))
+          % (name, P, code_mis, int(np.sum(qh != inter["qh"])), qh.size, ulp_hist(ulps),
+             int(ulps.max()), scale_rel, y2_fro, y2_max))
     assert code_mis <= 1e-3
     assert scale_rel <= 2e-6
     assert y2_fro <= 1e-3
@@ -121,10 +134,13 @@ def test_requant_codes_and_down_output_fp4(name):
     y2 = wsh[lay["y2"]:lay["y2"] + 4 * P * H].view(np.float32).reshape(P, H).astype(np.float64)
     code_mis = np.mean(qh != inter["qh"])
     scale = side[:, :, 0] / np.float32(512)
+    ulps = scale_ulps(scale, inter["sh"])
     scale_rel = np.max(np.abs(scale.astype(np.float64) - inter["sh"]) / inter["sh"])
     y2_fro = np.linalg.norm(y2 - inter["y2"]) / np.linalg.norm(inter["y2"])
-    print("fp4 %s: P=%d code mismatch=%.2e (%d of %d) scale max rel %.1e y2 rel_fro=%.3e"
-          % (name, P, code_mis, int(np.sum(qh != inter["qh"])), qh.size, scale_rel, y2_fro))
+    print("fp4 %s: P=%d code mismatch=%.2e (%d of %d) scale ulps: %s (max %d, max rel %.1e) "
+          "y2 rel_fro=%.3e"
+          % (name, P, code_mis, int(np.sum(qh != inter["qh"])), qh.size, ulp_hist(ulps),
+             int(ulps.max()), scale_rel, y2_fro))
     assert code_mis <= 1e-3
     assert scale_rel <= 2e-6
     assert y2_fro <= 1e-3

@@ -1,0 +1,231 @@
+"""GPU parity in the numerically hard regimes of the method (through the C ABI,
+against the CPU oracle, at the same bars as test_gpu_parity.py).
+
+* Same-sign activations.  The fp8 MFMA paths (down GEMM, dense linear) feed
+  the int4 weights as the biased codes u = v + 8 and subtract 8 * (sum of the
+  block's activations) in the promotion, so a 128-block whose activations
+  share a sign multiplies the MFMA's own rounding by sum|a|(v+8) / |sum a v|.
+  Hidden states with a consistent sign (x = |N(0,1)| + 3) and an intermediate
+  h that is positive everywhere (gate and up weights with non-negative
+  nibbles) put every GEMM of the call in that regime, at the model's sizes
+  (H = 7168, I = 2048), on the few-rows and the block-tiled kernels.
+* All-zero 128-blocks of a token (amax clamped before the reciprocal) inside
+  the fused call, on both kernels.
+* fp4 weights whose four UE8M0 block exponents in one 128-group span more
+  than 24 binades (the exact f16 conversion of the small blocks underflows).
+* Full-size prefill and its EP8 rank share, with one token from every 16-row
+  slice of every 160-row m-block of every local expert.
+"""
+import concurrent.futures
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from w4a8_moe_grouped_amd import lib as w4
+from w4a8_moe_grouped_amd import synth
+
+from test_gpu_parity import assert_bf16_close, bf16_dev, bf16_host, dput
+
+pytestmark = pytest.mark.gpu
+
+ORACLE_THREADS = 16  # the host's share of the box
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "the gpu tests need an MI355X"
+    w4.load()
+    return torch.device("cuda:0")
+
+
+def oracle_rows_parallel(d, cfg, rows, fn=None, threads=ORACLE_THREADS):
+    """The oracle on the given tokens, split over threads (every output row
+    depends only on its own token, so the slices' rows equal one call's)."""
+    fn = fn or oracle.fused_moe
+    rows = np.asarray(rows)
+    parts = [p for p in np.array_split(rows, min(threads, rows.size)) if p.size]
+
+    def run(r):
+        return fn(d["hidden"][r], d["topk_ids"][r], d["topk_weights"][r], cfg.expert_begin,
+                  cfg.E_local, d["w13"], d["s13"], d["w2"], d["s2"])
+    with concurrent.futures.ThreadPoolExecutor(len(parts)) as ex:
+        outs = list(ex.map(run, parts))
+    return np.concatenate(outs, axis=0)
+
+
+def run_fused(d, cfg, dev, fp4=False):
+    args = (bf16_dev(d["hidden"], dev), dput(d["topk_ids"], dev), dput(d["topk_weights"], dev),
+            cfg.expert_begin, cfg.E_local)
+    if fp4:
+        packed = w4.prepack_weights_fp4(dput(d["w13"], dev), dput(d["s13"], dev), w4.FP4_GATE_UP) + \
+            w4.prepack_weights_fp4(dput(d["w2"], dev), dput(d["s2"], dev), w4.FP4_DOWN)
+        out = w4.fused_moe_fp4(*args, cfg.I, packed)
+    else:
+        out = w4.fused_moe(*args, dput(d["w13"], dev), dput(d["s13"], dev), dput(d["w2"], dev),
+                           dput(d["s2"], dev))
+    torch.cuda.synchronize()
+    return bf16_host(out)
+
+
+def slice_rows(d, cfg, block_m=160, seed=0):
+    """One token from every 16-row slice of every block_m-row m-block of
+    every local expert (a random row inside the slice), sorted and unique."""
+    al = oracle.moe_align(d["topk_ids"], cfg.expert_begin, cfg.E_local, block_m)
+    offs, srt = al["offsets"], al["sorted_pair_ids"]
+    rng = np.random.default_rng(seed)
+    toks = set()
+    for e in range(cfg.E_local):
+        for r0 in range(int(offs[e]), int(offs[e + 1]), 16):
+            r1 = min(r0 + 16, int(offs[e + 1]))
+            p = int(rng.integers(r0, r1))
+            toks.add(int(srt[p]) // cfg.topk)
+    toks.add(0)
+    toks.add(cfg.T - 1)
+    return np.array(sorted(toks))
+
+
+def biased_hidden(cfg, seed):
+    """bf16 |N(0,1)| + 3: every 128-block of every token has one sign."""
+    z = synth.draw_normal(seed, synth.STREAM_X, 0, cfg.T * cfg.H)
+    return synth.to_bf16_bits(np.abs(z) + 3.0).reshape(cfg.T, cfg.H)
+
+
+# ---------------------------------------------------------------------------
+# same-sign activations
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,N", [(128, 2048), (4, 256)])
+def test_gemm_same_sign_activations(dev, M, N):
+    """Dense linear (fp8 MFMA, biased weight codes) on x = |N(0,1)| + 3 at
+    K = 7168; M = 4 takes the 16-row whole-K staged path."""
+    K = 7168
+    z = synth.draw_normal(40 + M, synth.STREAM_X, 0, M * K)
+    x = synth.to_bf16_bits(np.abs(z) + 3.0).reshape(M, K)
+    rng = np.random.default_rng(M)
+    w = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    sw = rng.uniform(0.002, 0.02, size=(N, K // 128)).astype(np.float32)
+    q, s = w4.quantize_act(bf16_dev(x, dev))
+    out = w4.gemm(q, s, dput(w, dev), dput(sw, dev))
+    torch.cuda.synchronize()
+    rq, rs = oracle.quantize_bf16(x)
+    ref = oracle.gemm_bf16(rq, rs, w, sw)
+    assert_bf16_close(bf16_host(out), ref, "gemm same-sign %dx%dx%d" % (M, K, N))
+
+
+def same_sign_moe(T, Etot, k, El, seed):
+    """Model-size experts, hidden |N(0,1)| + 3, gate and up weights with
+    non-negative nibbles (so gate, up and h = silu(gate) * up are positive and
+    the down GEMM's activations share a sign), down weights signed."""
+    cfg, d = synth.random_moe(T, 7168, 2048, Etot, k, 0, El, seed=seed)
+    d["hidden"] = biased_hidden(cfg, seed)
+    d["w13"] = d["w13"] & np.uint8(0x77)
+    return cfg, d
+
+
+def test_fused_same_sign_skinny(dev):
+    """64 tokens, 32 of 256 experts, top-8: 16-row blocks on the few-rows kernel."""
+    cfg, d = same_sign_moe(64, 256, 8, 32, seed=81)
+    lay = w4.fused_moe_workspace_layout(cfg.T, cfg.H, cfg.topk, cfg.E_local, cfg.I)
+    assert lay["block_m"] == 16
+    got = run_fused(d, cfg, dev)
+    ref = oracle_rows_parallel(d, cfg, np.arange(cfg.T))
+    assert_bf16_close(got, ref, "same-sign fused, 16-row blocks")
+
+
+def test_fused_same_sign_tile(dev):
+    """512 tokens, 4 local of 8 experts, top-2: 160-row blocks on the
+    block-tiled kernel; one token from every 16-row slice is compared."""
+    cfg, d = same_sign_moe(512, 8, 2, 4, seed=82)
+    lay = w4.fused_moe_workspace_layout(cfg.T, cfg.H, cfg.topk, cfg.E_local, cfg.I)
+    assert lay["block_m"] == 160
+    got = run_fused(d, cfg, dev)
+    rows = slice_rows(d, cfg)
+    ref = oracle_rows_parallel(d, cfg, rows)
+    assert_bf16_close(got[rows], ref, "same-sign fused, 160-row blocks (%d tokens)" % rows.size)
+
+
+# ---------------------------------------------------------------------------
+# all-zero 128-blocks inside the fused call
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("path", ["skinny", "tile"])
+def test_fused_zero_blocks(dev, path):
+    if path == "skinny":
+        cfg, d = synth.random_moe(48, 1024, 256, 16, 4, 0, 8, seed=83)
+    else:
+        cfg, d = synth.random_moe(600, 1024, 256, 8, 2, 0, 4, seed=84)
+    x = d["hidden"].copy()
+    G = cfg.H // 128
+    rng = np.random.default_rng(85)
+    for t in range(0, cfg.T, 3):  # every third token: one or more zero blocks
+        for g in rng.choice(G, size=1 + t % 3, replace=False):
+            x[t, 128 * g:128 * (g + 1)] = 0
+    x[1] = 0           # a whole token of zeros: y1 = 0, h = 0, its requant blocks too
+    x[2, ::2] = 0x8000  # -0 entries inside otherwise normal blocks
+    d["hidden"] = x
+    lay = w4.fused_moe_workspace_layout(cfg.T, cfg.H, cfg.topk, cfg.E_local, cfg.I)
+    assert lay["block_m"] == (160 if path == "tile" else 32)
+    got = run_fused(d, cfg, dev)
+    ref = oracle_rows_parallel(d, cfg, np.arange(cfg.T))
+    assert_bf16_close(got, ref, "zero blocks (%s)" % path)
+
+
+# ---------------------------------------------------------------------------
+# fp4: block exponents spread beyond the exact f16 window
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("path", ["skinny", "tile"])
+def test_fp4_wide_block_exponents(dev, path):
+    """Per 128-group the four UE8M0 exponents are {e0 - 30, e0 - 12, e0, e0 + 3}
+    in a random order (33 binades): the gate_up GEMM converts each block with
+    2^(e_b - e_max), so the smallest block falls below f16's subnormal range;
+    its contribution is below 2^-24 of the group's, and the result stays
+    within the bars."""
+    if path == "skinny":
+        cfg, d = synth.random_moe_fp4(64, 1024, 512, 64, 8, 0, 32, seed=86)
+    else:
+        cfg, d = synth.random_moe_fp4(600, 1024, 512, 8, 2, 0, 4, seed=87)
+    rng = np.random.default_rng(88)
+    for key in ("s13", "s2"):
+        s = d[key]
+        E, N, B = s.shape
+        spread = np.array([-30, -12, 0, 3], np.int64)
+        base = rng.integers(118, 124, size=(E, N, B // 4, 1))
+        order = np.argsort(rng.random(size=(E, N, B // 4, 4)), axis=-1)
+        d[key] = (base + spread[order]).reshape(E, N, B).astype(np.uint8)
+    got = run_fused(d, cfg, dev, fp4=True)
+    ref = oracle_rows_parallel(d, cfg, np.arange(cfg.T), fn=oracle.fused_moe_fp4)
+    assert_bf16_close(got, ref, "fp4 wide exponents (%s)" % path)
+
+
+# ---------------------------------------------------------------------------
+# full-size prefill: every 16-row slice of every m-block
+# ---------------------------------------------------------------------------
+
+_cache = {}
+
+
+def moe_inputs(name):
+    if name not in _cache:
+        _cache.clear()  # one full-size workload at a time in host memory
+        cfg = synth.CONFIGS[name]
+        _cache[name] = (cfg, synth.gen_moe(cfg))
+    return _cache[name]
+
+
+@pytest.mark.parametrize("name", ["prefill", "prefill_ep8"])
+def test_fused_prefill_every_slice(dev, name):
+    cfg, d = moe_inputs(name)
+    got = run_fused(d, cfg, dev)
+    rows = slice_rows(d, cfg, seed=7)
+    ids = d["topk_ids"][rows]
+    hit = np.unique(ids[(ids >= cfg.expert_begin) & (ids < cfg.expert_begin + cfg.E_local)])
+    assert hit.size == cfg.E_local, "every local expert is compared"
+    print("%s: %d tokens compared" % (name, rows.size), flush=True)
+    ref = oracle_rows_parallel(d, cfg, rows)
+    assert_bf16_close(got[rows], ref, "%s (%d tokens, one per 16-row slice)" % (name, rows.size))
+    ids = d["topk_ids"]
+    none_local = ~np.any((ids >= cfg.expert_begin) & (ids < cfg.expert_begin + cfg.E_local), axis=1)
+    assert np.all(got[none_local] == 0)

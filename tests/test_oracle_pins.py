@@ -321,6 +321,70 @@ def test_gemm_unit_scales_is_exact_integer_matmul(orc):
 
 
 # ---------------------------------------------------------------------------
+# SwiGLU between the GEMMs
+# ---------------------------------------------------------------------------
+
+def read_swiglu_golden():
+    rows = []
+    with open(os.path.join(GOLDEN, "swiglu.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append(line.split())
+    return rows
+
+
+def test_swiglu_hand_worked_values(orc):
+    """Closed-form values of silu(g) * u (tests/golden/swiglu.txt, 60-digit
+    decimal arithmetic): the oracle's fp32 result is the correctly rounded
+    fp32 value of each (checked in exact decimal arithmetic)."""
+    from decimal import Decimal
+    rows = read_swiglu_golden()
+    assert len(rows) >= 8
+    g = np.array([float(r[0]) for r in rows])
+    u = np.array([float(r[1]) for r in rows])
+    h = orc.swiglu(g, u)
+    for (gs, us, hs), got in zip(rows, h):
+        exact = Decimal(hs)
+        err = abs(Decimal(float(got)) - exact)
+        ulp = Decimal(float(np.spacing(np.float32(abs(float(exact)))))) if exact != 0 else Decimal(0)
+        assert err <= ulp / 2 * Decimal("1.000001"), (gs, us, hs, float(got))
+    # the worked example g = 1, u = 2: 2 / (1 + e^-1) = 1.4621171572600098 (fp64)
+    assert np.float32(orc.swiglu(np.array([1.0]), np.array([2.0]))[0]) == np.float32(1.4621171572600098)
+
+
+def test_swiglu_matches_torch_silu_fp64(orc):
+    """The oracle's SwiGLU against torch.nn.functional.silu(g) * u in fp64 over
+    g in [-60, 60] (dense grid plus random values and |g| up to 700), both
+    rounded once to fp32: equal except where the fp64 results straddle an fp32
+    rounding boundary (at most one fp32 ulp)."""
+    rng = np.random.default_rng(11)
+    g = np.concatenate([np.linspace(-60.0, 60.0, 240001), rng.normal(size=20000) * 8.0,
+                        [-700.0, -100.0, -40.0, 40.0, 100.0, 700.0, 0.0, -0.0]])
+    u = rng.normal(size=g.size) * np.exp(rng.uniform(-5, 5, size=g.size))
+    got = orc.swiglu(g, u)
+    ref = (torch.nn.functional.silu(torch.from_numpy(g)) * torch.from_numpy(u)).numpy().astype(np.float32)
+    ulps = np.abs(got.view(np.int32).astype(np.int64) - ref.view(np.int32).astype(np.int64))
+    same_sign = np.signbit(got) == np.signbit(ref)
+    assert np.all((ulps <= 1) & (same_sign | (got == 0))), np.max(ulps)
+    assert np.count_nonzero(ulps) <= 3
+
+
+def test_swiglu_limits(orc):
+    """silu(g) -> g for large g and -> 0 (from below) for very negative g;
+    silu(0) = 0; the gate and up inputs are not swapped."""
+    h = orc.swiglu(np.array([80.0, -80.0, 0.0, 2.0]), np.array([1.0, 1.0, 3.0, 0.0]))
+    assert h[0] == np.float32(80.0)
+    assert h[1] < 0 and h[1] > -1e-30
+    assert h[2] == 0.0 and h[3] == 0.0
+    # silu(3) * 1 != silu(1) * 3: the first argument is the gate
+    a = orc.swiglu(np.array([3.0]), np.array([1.0]))[0]
+    b = orc.swiglu(np.array([1.0]), np.array([3.0]))[0]
+    silu3 = torch.nn.functional.silu(torch.tensor(3.0, dtype=torch.float64)).item()
+    assert a == np.float32(silu3) and a != b
+
+
+# ---------------------------------------------------------------------------
 # fused MoE
 # ---------------------------------------------------------------------------
 
@@ -340,8 +404,8 @@ def brute_force_moe(d, eb, E):
             if not (0 <= e < E):
                 continue
             y1 = dequant_w(d["w13"][e], d["s13"][e]) @ A[t]
-            g, u = y1[:I], y1[I:]
-            h = (g / (1.0 + np.exp(-g)) * u).astype(np.float32)
+            g, u = torch.from_numpy(y1[:I]), torch.from_numpy(y1[I:])
+            h = (torch.nn.functional.silu(g) * u).numpy().astype(np.float32)
             qh, sh = oracle.quantize_f32(h[None, :])
             y2 = dequant_w(d["w2"][e], d["s2"][e]) @ dequant_rows(qh, sh)[0]
             out[t] += np.float64(tw[t, j]) * y2

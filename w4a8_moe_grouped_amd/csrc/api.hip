@@ -118,6 +118,25 @@ size_t plan_gemm(void* ws, int64_t M, int64_t K, uint8_t** q_il, float2** side)
     return c.used;
 }
 
+// The GEMM kernels address their operands through buffer resources, whose
+// extent and per-lane offsets are 32-bit: every byte range one resource
+// covers (activation rows x K, one expert's weights or scales) must stay
+// below 2^32.  The skinny GEMM puts m-blocks on grid.y (at most 65535).
+constexpr int64_t kRangeLimit = (int64_t)1 << 32;
+constexpr int64_t kMaxGridY = 65535;
+inline bool below_u32(int64_t bytes)
+{
+    return bytes >= 0 && bytes < kRangeLimit;
+}
+// products of non-negative sizes without int64 overflow (limit 2^62)
+inline int64_t mul_sat(int64_t a, int64_t b)
+{
+    const int64_t cap = (int64_t)1 << 62;
+    if (a <= 0 || b <= 0)
+        return 0;
+    return a > cap / b ? cap : a * b;
+}
+
 int check_workspace(void* ws, size_t* bytes, size_t need)
 {
     if (bytes == nullptr)
@@ -138,8 +157,10 @@ inline int hip_status(hipError_t e)
     return e == hipSuccess ? W4A8_OK : W4A8_ERR_HIP;
 }
 
-// events armed by w4a8_fused_moe_stage_events for the next call on this thread
-thread_local void* const* t_stage_events = nullptr;
+// events armed by w4a8_fused_moe_stage_events for the next call on this
+// thread (the handles are copied, the caller's array may go away)
+thread_local void* t_stage_events[6] = {nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
+thread_local bool t_stage_armed = false;
 
 inline void mark(void* const* ev, int i, hipStream_t s)
 {
@@ -184,6 +205,9 @@ int w4a8_quantize_act(const void* x_bf16, int64_t M, int64_t K, int64_t ldx, uin
         return W4A8_ERR_INVALID_ARG;
     if (K % W4A8_GROUP != 0 || ldx % 8 != 0)
         return W4A8_ERR_UNSUPPORTED;
+    // one workgroup per 16 blocks of 128: the grid stays within 2^31 - 1
+    if (ceil_div(mul_sat(M, K / W4A8_GROUP), 16) > INT32_MAX)
+        return W4A8_ERR_UNSUPPORTED;
     if (!aligned16(x_bf16) || !aligned16(q_e4m3) || !aligned16(scales))
         return W4A8_ERR_UNSUPPORTED;
     if (M == 0)
@@ -200,7 +224,12 @@ int w4a8_gemm(const uint8_t* a_e4m3, const float* a_scales, int64_t M, int64_t K
         return W4A8_ERR_INVALID_ARG;
     if (K % W4A8_GROUP != 0)
         return W4A8_ERR_UNSUPPORTED;
+    // 32-bit buffer ranges: the activation codes [M, K] and the weights [N, K/2]
+    if (!below_u32(mul_sat(M, K)) || !below_u32(mul_sat(N, K / 2)) || M > INT32_MAX)
+        return W4A8_ERR_UNSUPPORTED;
     const int block_m = M <= 16 ? 16 : (M <= 32 ? 32 : 64);
+    if (ceil_div(M, block_m) > kMaxGridY)
+        return W4A8_ERR_UNSUPPORTED;
     if (!skinny_k_ok(K, block_m))
         return W4A8_ERR_UNSUPPORTED;
     uint8_t* q_il;
@@ -250,7 +279,7 @@ int w4a8_moe_align(const int32_t* topk_ids, int64_t T, int64_t topk, int64_t exp
 {
     if (T < 0 || topk < 1 || num_local_experts < 1 || block_m < 1)
         return W4A8_ERR_INVALID_ARG;
-    if (topk > W4A8_MAX_TOPK || num_local_experts > kMaxLocalExperts || T * topk > INT32_MAX / 2)
+    if (topk > W4A8_MAX_TOPK || num_local_experts > kMaxLocalExperts || mul_sat(T, topk) > INT32_MAX / 2)
         return W4A8_ERR_UNSUPPORTED;
     const size_t need = round_up(w4a8::align_workspace_bytes(T * topk, num_local_experts));
     const int ws_rc = check_workspace(workspace, workspace_bytes, need);
@@ -281,6 +310,10 @@ int fused_moe_impl(const void* hidden_bf16, int64_t T, int64_t H, const int32_t*
                    WeightFormat format, const float* a1_scale = nullptr,
                    const float* a2_scale = nullptr, int down_group = W4A8_GROUP)
 {
+    // any call of the family consumes the stage-event arming (see the header)
+    const bool timed = t_stage_armed;
+    t_stage_armed = false;
+    void* const* ev = timed ? t_stage_events : nullptr;
     const bool packed = format != kInt4;
     if (down_group != 128 && down_group != 64 && down_group != 32)
         return W4A8_ERR_INVALID_ARG;
@@ -290,11 +323,17 @@ int fused_moe_impl(const void* hidden_bf16, int64_t T, int64_t H, const int32_t*
     if (T < 0 || H <= 0 || I <= 0 || topk < 1 || E < 1)
         return W4A8_ERR_INVALID_ARG;
     if (H % W4A8_GROUP != 0 || I % W4A8_GROUP != 0 || topk > W4A8_MAX_TOPK ||
-        E > kMaxLocalExperts || T * topk > INT32_MAX / 2)
+        E > kMaxLocalExperts || mul_sat(T, topk) > INT32_MAX / 2)
+        return W4A8_ERR_UNSUPPORTED;
+    // 32-bit buffer ranges: the gate_up operand [T, H], the down operand
+    // [T*topk, I] (every pair may be local), one expert's w13 [2I, H/2]
+    if (!below_u32(mul_sat(T, H)) || !below_u32(mul_sat(mul_sat(T, topk), I)) ||
+        !below_u32(mul_sat(I, H)))
         return W4A8_ERR_UNSUPPORTED;
     MoePlan p;
     const size_t need = plan_moe(nullptr, T, H, topk, E, I, p, down_group);
-    if (!p.tile && (!skinny_k_ok(H, p.block_m) || !skinny_k_ok(I, p.block_m, down_group)))
+    if (!p.tile && (!skinny_k_ok(H, p.block_m) || !skinny_k_ok(I, p.block_m, down_group) ||
+                    p.nb_max > kMaxGridY))
         return W4A8_ERR_UNSUPPORTED;
     const int ws_rc = check_workspace(workspace, workspace_bytes, need);
     if (ws_rc >= 0)
@@ -307,8 +346,6 @@ int fused_moe_impl(const void* hidden_bf16, int64_t T, int64_t H, const int32_t*
     if (!aligned16(hidden_bf16) || !aligned16(out_bf16) || !aligned16(w13_int4) ||
         !aligned16(w2_int4) || !aligned16(w13_scales) || !aligned16(w2_scales))
         return W4A8_ERR_UNSUPPORTED;
-    void* const* ev = t_stage_events;
-    t_stage_events = nullptr;
     if (T == 0)
         return W4A8_OK;
     plan_moe(workspace, T, H, topk, E, I, p, down_group);
@@ -480,6 +517,10 @@ int w4a8_prepack_weights(const uint8_t* w_int4, const float* w_scales, int64_t E
         return W4A8_ERR_INVALID_ARG;
     if (N % 16 != 0 || K % W4A8_GROUP != 0)
         return W4A8_ERR_UNSUPPORTED;
+    // one expert's weights stay below 2^32 bytes (the GEMMs' buffer ranges);
+    // one thread per 16 bytes: the grid stays within 2^31 - 1 workgroups
+    if (!below_u32(mul_sat(N, K / 2)) || ceil_div(mul_sat(E, N * (K / 2)), 16 * 256) > INT32_MAX)
+        return W4A8_ERR_UNSUPPORTED;
     if (!aligned16(w_int4) || !aligned16(w_packed) || !aligned16(w_scales) || !aligned16(s_packed))
         return W4A8_ERR_UNSUPPORTED;
     if ((const void*)w_int4 == (const void*)w_packed || (const void*)w_scales == (const void*)s_packed)
@@ -497,6 +538,10 @@ int w4a8_prepack_weights_bf16_scales(const uint8_t* w_int4, const uint16_t* w_sc
     if (w_int4 == nullptr || w_scales_bf16 == nullptr || w_packed == nullptr || s_packed == nullptr)
         return W4A8_ERR_INVALID_ARG;
     if (N % 16 != 0 || K % W4A8_GROUP != 0)
+        return W4A8_ERR_UNSUPPORTED;
+    // one expert's weights stay below 2^32 bytes (the GEMMs' buffer ranges);
+    // one thread per 16 bytes: the grid stays within 2^31 - 1 workgroups
+    if (!below_u32(mul_sat(N, K / 2)) || ceil_div(mul_sat(E, N * (K / 2)), 16 * 256) > INT32_MAX)
         return W4A8_ERR_UNSUPPORTED;
     if (!aligned16(w_int4) || !aligned16(w_packed) || ((uintptr_t)w_scales_bf16 & 1u) != 0 ||
         !aligned16(s_packed))
@@ -519,6 +564,10 @@ int w4a8_prepack_weights_fp4(const uint8_t* w_fp4, const uint8_t* w_scales_ue8m0
     if (w_fp4 == nullptr || w_scales_ue8m0 == nullptr || w_packed == nullptr || s_packed == nullptr)
         return W4A8_ERR_INVALID_ARG;
     if (N % 16 != 0 || K % W4A8_GROUP != 0)
+        return W4A8_ERR_UNSUPPORTED;
+    // one expert's weights stay below 2^32 bytes (the GEMMs' buffer ranges);
+    // one thread per 16 bytes: the grid stays within 2^31 - 1 workgroups
+    if (!below_u32(mul_sat(N, K / 2)) || ceil_div(mul_sat(E, N * (K / 2)), 16 * 256) > INT32_MAX)
         return W4A8_ERR_UNSUPPORTED;
     // the scales are moved as one dword per row and 128-group
     if (!aligned16(w_fp4) || !aligned16(w_packed) || ((uintptr_t)w_scales_ue8m0 & 3u) != 0 ||
@@ -561,12 +610,14 @@ int w4a8_fused_moe_workspace_layout(int64_t T, int64_t H, int64_t topk,
 int w4a8_fused_moe_stage_events(void* const* events, int n)
 {
     if (n == 0) {
-        t_stage_events = nullptr;
+        t_stage_armed = false;
         return W4A8_OK;
     }
     if (n != 6 || events == nullptr)
         return W4A8_ERR_INVALID_ARG;
-    t_stage_events = events;
+    for (int i = 0; i < 6; ++i)
+        t_stage_events[i] = events[i];
+    t_stage_armed = true;
     return W4A8_OK;
 }
 

@@ -17,8 +17,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
                                                       int64_t topk, int64_t H,
                                                       uint16_t* __restrict__ out)
 {
-    const int64_t t = blockIdx.y;
-    const int64_t col = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+    // 1-D grid: xb workgroups per token (grid.y would cap T at 65535)
+    const int64_t xb = (H / 8 + 255) / 256;
+    const int64_t t = (int64_t)blockIdx.x / xb;
+    const int64_t col = (((int64_t)blockIdx.x - t * xb) * 256 + threadIdx.x) * 8;
     if (col >= H)
         return;
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -51,7 +53,7 @@ hipError_t launch_combine(const float* y2, const int32_t* src2dst, const float* 
 {
     if (T == 0)
         return hipSuccess;
-    dim3 grid((unsigned)((H / 8 + 255) / 256), (unsigned)T);
+    dim3 grid((unsigned)((H / 8 + 255) / 256 * T));
     hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, s, y2, src2dst, topk_w, topk, H, out);
     return hipGetLastError();
 }
