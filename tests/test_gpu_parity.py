@@ -202,10 +202,11 @@ def test_gemm_dense_config(dev):
 
 @pytest.mark.parametrize("M,K,N", [(1, 128, 16), (5, 384, 40), (33, 256, 300), (70, 1024, 513),
                                    (17, 7168, 256), (64, 2048, 7168),
-                                   # 16-row blocks with K % 1024 == 0: the whole-K staged rows
-                                   # (stage capacity 4 rows at K = 7168, 16 at K = 2048) and,
-                                   # past the capacity, the per-group path
-                                   (1, 7168, 2048), (4, 7168, 256), (5, 7168, 256), (16, 2048, 512)])
+                                   # few tiles: K split over workgroups, partials reduced in order
+                                   (1, 7168, 2048), (4, 7168, 256), (5, 7168, 256), (16, 2048, 512),
+                                   # 16-row blocks, K % 1024 == 0 and enough tiles to run unsplit:
+                                   # the whole-K rows staged in LDS
+                                   (3, 1024, 65536)])
 def test_gemm_ragged_shapes(dev, M, K, N):
     rng = np.random.default_rng(M * 7 + N)
     x = synth.to_bf16_bits(rng.normal(size=(M, K)).astype(np.float32))

@@ -110,11 +110,44 @@ size_t plan_moe(void* ws, int64_t T, int64_t H, int64_t topk, int64_t E, int64_t
     return c.used;
 }
 
-size_t plan_gemm(void* ws, int64_t M, int64_t K, uint8_t** q_il, float2** side)
+// The dense GEMM's launch: m-block height and the K split.  M x N tiles of
+// block_m x 256 alone give few workgroups at decode-like M (M = 128, N = 2048:
+// 16 of them on 256 CUs, each walking all of K), so K is split until about
+// 256 workgroups run, in slices of a multiple of 4 groups (the float4 scale
+// blocks) of at least 4 groups; the fp32 partial sums are then reduced in
+// split order by a second kernel.
+struct GemmPlan {
+    int block_m;
+    int32_t split_groups;  // 128-groups per K slice
+    int32_t splits;
+};
+constexpr int64_t kGemmTargetWgs = 256;
+GemmPlan gemm_plan(int64_t M, int64_t K, int64_t N)
+{
+    GemmPlan g;
+    g.block_m = M <= 16 ? 16 : (M <= 32 ? 32 : 64);
+    const int64_t G = K / W4A8_GROUP;
+    const int64_t tiles = ceil_div(N, 256) * ceil_div(M, g.block_m);
+    int64_t gps = G;
+    if (N % 4 == 0 && G % 4 == 0 && tiles < kGemmTargetWgs && G >= 8) {
+        const int64_t want = ceil_div(kGemmTargetWgs, tiles);  // splits wanted
+        gps = ceil_div(ceil_div(G, want), 4) * 4;
+        if (gps < 4)
+            gps = 4;
+    }
+    g.split_groups = (int32_t)gps;
+    g.splits = (int32_t)ceil_div(G, gps);
+    return g;
+}
+
+size_t plan_gemm(void* ws, int64_t M, int64_t K, int64_t N, uint8_t** q_il, float2** side,
+                 float** part)
 {
     Carve c(ws);
+    const GemmPlan g = gemm_plan(M, K, N);
     *q_il = c.take<uint8_t>(M * K);
     *side = c.take<float2>(M * (K / W4A8_GROUP));
+    *part = g.splits > 1 ? c.take<float>((size_t)g.splits * M * N) : nullptr;
     return c.used;
 }
 
@@ -227,14 +260,16 @@ int w4a8_gemm(const uint8_t* a_e4m3, const float* a_scales, int64_t M, int64_t K
     // 32-bit buffer ranges: the activation codes [M, K] and the weights [N, K/2]
     if (!below_u32(mul_sat(M, K)) || !below_u32(mul_sat(N, K / 2)) || M > INT32_MAX)
         return W4A8_ERR_UNSUPPORTED;
-    const int block_m = M <= 16 ? 16 : (M <= 32 ? 32 : 64);
+    const GemmPlan gp = gemm_plan(M, K, N);
+    const int block_m = gp.block_m;
     if (ceil_div(M, block_m) > kMaxGridY)
         return W4A8_ERR_UNSUPPORTED;
     if (!skinny_k_ok(K, block_m))
         return W4A8_ERR_UNSUPPORTED;
     uint8_t* q_il;
     float2* side;
-    const size_t need = plan_gemm(nullptr, M, K, &q_il, &side);
+    float* part;
+    const size_t need = plan_gemm(nullptr, M, K, N, &q_il, &side, &part);
     const int ws_rc = check_workspace(workspace, workspace_bytes, need);
     if (ws_rc >= 0)
         return ws_rc;
@@ -247,7 +282,7 @@ int w4a8_gemm(const uint8_t* a_e4m3, const float* a_scales, int64_t M, int64_t K
         return W4A8_ERR_UNSUPPORTED;
     if (M == 0)
         return W4A8_OK;
-    plan_gemm(workspace, M, K, &q_il, &side);
+    plan_gemm(workspace, M, K, N, &q_il, &side, &part);
     hipError_t e = w4a8::launch_prep_codes(a_e4m3, a_scales, M, K, q_il, side, stream);
     if (e != hipSuccess)
         return W4A8_ERR_HIP;
@@ -268,7 +303,16 @@ int w4a8_gemm(const uint8_t* a_e4m3, const float* a_scales, int64_t M, int64_t K
     g.N = N;
     g.out_bf16 = (uint16_t*)out_bf16;
     g.max_blocks = ceil_div(M, block_m);
-    return hip_status(w4a8::launch_gemm_skinny(g, w4a8::EPI_BF16, block_m, stream));
+    if (gp.splits == 1)
+        return hip_status(w4a8::launch_gemm_skinny(g, w4a8::EPI_BF16, block_m, stream));
+    // K split: fp32 partials [splits, M, N], then their sum in split order
+    g.split_groups = gp.split_groups;
+    g.split_stride = M * N;
+    g.out_f32 = part;
+    e = w4a8::launch_gemm_skinny(g, w4a8::EPI_F32, block_m, stream);
+    if (e != hipSuccess)
+        return W4A8_ERR_HIP;
+    return hip_status(w4a8::launch_split_reduce(part, gp.splits, M, N, (uint16_t*)out_bf16, stream));
 }
 
 int w4a8_moe_align(const int32_t* topk_ids, int64_t T, int64_t topk, int64_t expert_begin,

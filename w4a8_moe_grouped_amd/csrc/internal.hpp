@@ -87,9 +87,17 @@ struct GemmArgs {
     // skinny kernel, 16-row m-blocks: blocks of at most this many rows read
     // their activations from a whole-K copy in LDS (set by the launcher)
     int32_t stage_rows;
+    // skinny kernel, K split over grid.z (dense GEMM): each workgroup reduces
+    // split_groups 128-groups of K (0 = all of them) and the store epilogue
+    // writes split z at out_f32 + z * split_stride
+    int32_t split_groups;
+    int64_t split_stride;
 };
 enum Epilogue { EPI_F32 = 0, EPI_BF16 = 1, EPI_SWIGLU_Q = 2 };
 hipError_t launch_gemm_skinny(const GemmArgs& a, int epilogue, int block_m, hipStream_t s);
+// out[M, N] bf16 = sum over `splits` fp32 partials part[z][M, N] (N % 4 == 0)
+hipError_t launch_split_reduce(const float* part, int32_t splits, int64_t M, int64_t N, uint16_t* out,
+                               hipStream_t s);
 
 // ---- grouped GEMM for many rows per expert (gemm_tile.hip) ----
 // m-blocks of kTileRows rows (two halves of five 16-row slices).
