@@ -323,6 +323,32 @@ int w4a8_fused_moe_fp4_prepacked(const void* hidden_bf16, int64_t T, int64_t H,
                                  hipStream_t stream);
 
 /*
+ * w4a8_fused_moe_prepacked_noalloc -- w4a8_fused_moe_prepacked for callers
+ * that cannot allocate device memory or pass a workspace: code recorded into
+ * a HIP graph, tight serving loops, harnesses that forbid hipMalloc.  The
+ * call allocates nothing; its intermediates live in a file-scope device
+ * array of W4A8_NOALLOC_SCRATCH_BYTES that every GPU the library runs on
+ * holds until the process ends (its address is looked up once per device,
+ * on the first call with that device current).
+ *   Arguments, results and errors as w4a8_fused_moe_prepacked, without the
+ *   workspace pair; the output is bit-identical to that export's.
+ *   W4A8_ERR_WORKSPACE if the call needs more than W4A8_NOALLOC_SCRATCH_BYTES
+ *   (the size w4a8_fused_moe_prepacked would query for the same shape; at
+ *   H = 7168, I = 2048 that is T*topk up to about 2000 pairs); W4A8_ERR_HIP if
+ *   the array's address cannot be obtained.
+ * Every call on one GPU uses the same array and leaves its contents behind:
+ * calls that may overlap on one GPU (other streams, other host threads) race
+ * and must be ordered by the caller.
+ */
+#define W4A8_NOALLOC_SCRATCH_BYTES (64u << 20)
+int w4a8_fused_moe_prepacked_noalloc(const void* hidden_bf16, int64_t T, int64_t H,
+                                     const int32_t* topk_ids, const float* topk_weights, int64_t topk,
+                                     int64_t expert_begin, int64_t num_local_experts, int64_t I,
+                                     const uint8_t* w13_packed, const float* w13_scales_packed,
+                                     const uint8_t* w2_packed, const float* w2_scales_packed,
+                                     void* out_bf16, hipStream_t stream);
+
+/*
  * w4a8_fused_moe_workspace_layout -- where w4a8_fused_moe keeps its
  * intermediates inside the workspace (host-only query, no HIP call), so that
  * tests and tools can read them after a call:

@@ -7,6 +7,7 @@
 
 #include "internal.hpp"
 
+#include <mutex>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -346,18 +347,15 @@ namespace {
 // weight formats of the fused forward
 enum WeightFormat { kInt4 = 0, kInt4Packed = 1, kFp4Packed = 2 };
 
-int fused_moe_impl(const void* hidden_bf16, int64_t T, int64_t H, const int32_t* topk_ids,
-                   const float* topk_weights, int64_t topk, int64_t expert_begin,
-                   int64_t num_local_experts, int64_t I, const uint8_t* w13_int4,
-                   const void* w13_scales, const uint8_t* w2_int4, const void* w2_scales,
-                   void* out_bf16, void* workspace, size_t* workspace_bytes, hipStream_t stream,
-                   WeightFormat format, const float* a1_scale = nullptr,
-                   const float* a2_scale = nullptr, int down_group = W4A8_GROUP)
+// ev: the stage events to record (null: none)
+int fused_moe_run(const void* hidden_bf16, int64_t T, int64_t H, const int32_t* topk_ids,
+                  const float* topk_weights, int64_t topk, int64_t expert_begin,
+                  int64_t num_local_experts, int64_t I, const uint8_t* w13_int4,
+                  const void* w13_scales, const uint8_t* w2_int4, const void* w2_scales,
+                  void* out_bf16, void* workspace, size_t* workspace_bytes, hipStream_t stream,
+                  WeightFormat format, const float* a1_scale, const float* a2_scale, int down_group,
+                  void* const* ev)
 {
-    // any call of the family consumes the stage-event arming (see the header)
-    const bool timed = t_stage_armed;
-    t_stage_armed = false;
-    void* const* ev = timed ? t_stage_events : nullptr;
     const bool packed = format != kInt4;
     if (down_group != 128 && down_group != 64 && down_group != 32)
         return W4A8_ERR_INVALID_ARG;
@@ -477,6 +475,28 @@ int fused_moe_impl(const void* hidden_bf16, int64_t T, int64_t H, const int32_t*
         return W4A8_ERR_HIP;
     mark(ev, 5, stream);
     return W4A8_OK;
+}
+
+// any call of the family consumes the stage-event arming (see the header)
+void* const* take_stage_events()
+{
+    const bool timed = t_stage_armed;
+    t_stage_armed = false;
+    return timed ? t_stage_events : nullptr;
+}
+
+int fused_moe_impl(const void* hidden_bf16, int64_t T, int64_t H, const int32_t* topk_ids,
+                   const float* topk_weights, int64_t topk, int64_t expert_begin,
+                   int64_t num_local_experts, int64_t I, const uint8_t* w13_int4,
+                   const void* w13_scales, const uint8_t* w2_int4, const void* w2_scales,
+                   void* out_bf16, void* workspace, size_t* workspace_bytes, hipStream_t stream,
+                   WeightFormat format, const float* a1_scale = nullptr,
+                   const float* a2_scale = nullptr, int down_group = W4A8_GROUP)
+{
+    void* const* ev = take_stage_events();
+    return fused_moe_run(hidden_bf16, T, H, topk_ids, topk_weights, topk, expert_begin,
+                         num_local_experts, I, w13_int4, w13_scales, w2_int4, w2_scales, out_bf16,
+                         workspace, workspace_bytes, stream, format, a1_scale, a2_scale, down_group, ev);
 }
 
 }  // namespace
@@ -663,6 +683,70 @@ int w4a8_fused_moe_stage_events(void* const* events, int n)
         t_stage_events[i] = events[i];
     t_stage_armed = true;
     return W4A8_OK;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Allocation-free fused forward: the workspace is a file-scope device array.
+// Each GPU the library runs on holds its own copy until the process ends.
+// The host never passes the array's name to a kernel: the address comes from
+// hipGetSymbolAddress, once per device with that device current.
+// ---------------------------------------------------------------------------
+namespace {
+
+static __device__ __align__(256) uint8_t scratch[W4A8_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// the device address of the current device's scratch array (null on failure)
+void* scratch_of_current_device()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+            return nullptr;
+        g_scratch_ptr[dev] = p;
+    }
+    return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+int w4a8_fused_moe_prepacked_noalloc(const void* hidden_bf16, int64_t T, int64_t H,
+                                     const int32_t* topk_ids, const float* topk_weights, int64_t topk,
+                                     int64_t expert_begin, int64_t num_local_experts, int64_t I,
+                                     const uint8_t* w13_packed, const float* w13_scales_packed,
+                                     const uint8_t* w2_packed, const float* w2_scales_packed,
+                                     void* out_bf16, hipStream_t stream)
+{
+    void* const* ev = take_stage_events();
+    // the workspace this call needs (host-only query, validates the shapes)
+    size_t need = 0;
+    const int q = fused_moe_run(nullptr, T, H, nullptr, nullptr, topk, expert_begin,
+                                num_local_experts, I, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                nullptr, &need, stream, kInt4Packed, nullptr, nullptr, W4A8_GROUP,
+                                nullptr);
+    if (q != W4A8_OK)
+        return q;
+    if (need > (size_t)W4A8_NOALLOC_SCRATCH_BYTES)
+        return W4A8_ERR_WORKSPACE;
+    void* ws = scratch_of_current_device();
+    if (ws == nullptr)
+        return W4A8_ERR_HIP;
+    size_t bytes = (size_t)W4A8_NOALLOC_SCRATCH_BYTES;
+    return fused_moe_run(hidden_bf16, T, H, topk_ids, topk_weights, topk, expert_begin,
+                         num_local_experts, I, w13_packed, w13_scales_packed, w2_packed,
+                         w2_scales_packed, out_bf16, ws, &bytes, stream, kInt4Packed, nullptr, nullptr,
+                         W4A8_GROUP, ev);
 }
 
 }  // extern "C"

@@ -24,7 +24,7 @@ EXPORTS = ("w4a8_version", "w4a8_status_string", "w4a8_quantize_act", "w4a8_gemm
            "w4a8_fused_moe_stage_events", "w4a8_prepack_weights", "w4a8_prepacked_scale_count",
            "w4a8_fused_moe_prepacked", "w4a8_prepack_weights_fp4", "w4a8_fused_moe_fp4_prepacked",
            "w4a8_prepack_weights_bf16_scales", "w4a8_fused_moe_prepacked_static",
-           "w4a8_fused_moe_recipe")
+           "w4a8_fused_moe_recipe", "w4a8_fused_moe_prepacked_noalloc")
 
 _lock = threading.Lock()
 _lib = None
@@ -73,6 +73,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         L.w4a8_fused_moe_recipe.restype = ctypes.c_int
         L.w4a8_fused_moe_recipe.argtypes = [vp, i64, i64, vp, vp, i64, i64, i64, i64, ctypes.c_int,
                                             vp, vp, vp, vp, ctypes.c_int, vp, vp, sz, vp]
+        L.w4a8_fused_moe_prepacked_noalloc.restype = ctypes.c_int
+        L.w4a8_fused_moe_prepacked_noalloc.argtypes = L.w4a8_fused_moe.argtypes[:14] + [vp]
         L.w4a8_prepack_weights_bf16_scales.restype = ctypes.c_int
         L.w4a8_prepack_weights_bf16_scales.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp]
         L.w4a8_prepacked_scale_count.restype = ctypes.c_int64
@@ -222,6 +224,33 @@ def fused_moe_fp4(hidden: torch.Tensor, topk_ids: torch.Tensor, topk_weights: to
         _ptr(hidden), T, H, _ptr(topk_ids), _ptr(topk_weights), k, expert_begin, E, I,
         _ptr(w13p), _ptr(s13p), _ptr(w2p), _ptr(s2p), _ptr(out), _ptr(workspace),
         ctypes.byref(n), _stream(hidden.device)), "w4a8_fused_moe_fp4_prepacked")
+    return out
+
+
+def fused_moe_noalloc(hidden: torch.Tensor, topk_ids: torch.Tensor, topk_weights: torch.Tensor,
+                      expert_begin: int, num_local_experts: int, I: int, prepacked: tuple,
+                      out: Optional[torch.Tensor] = None):
+    """w4a8_fused_moe_prepacked_noalloc: the fused forward on prepacked int4
+    weights (w13p, s13p, w2p, s2p) with no workspace argument (the library's
+    own device array holds the intermediates)."""
+    w13p, s13p, w2p, s2p = prepacked
+    _need_cuda(hidden, topk_ids, topk_weights, w13p, s13p, w2p, s2p)
+    T, H = hidden.shape
+    k = topk_ids.shape[1]
+    E = num_local_experts
+    assert hidden.dtype == torch.bfloat16 and topk_ids.dtype == torch.int32 \
+        and topk_weights.dtype == torch.float32
+    assert topk_ids.shape == (T, k) and topk_weights.shape == (T, k)
+    assert w13p.numel() == E * 2 * I * H // 2 and w2p.numel() == E * H * I // 2
+    assert s13p.numel() == load().w4a8_prepacked_scale_count(E, 2 * I, H)
+    assert s2p.numel() == load().w4a8_prepacked_scale_count(E, H, I)
+    for t in (hidden, topk_ids, topk_weights, w13p, s13p, w2p, s2p):
+        assert t.is_contiguous()
+    out = out if out is not None else torch.empty((T, H), dtype=torch.bfloat16, device=hidden.device)
+    _check(load().w4a8_fused_moe_prepacked_noalloc(
+        _ptr(hidden), T, H, _ptr(topk_ids), _ptr(topk_weights), k, expert_begin, E, I,
+        _ptr(w13p), _ptr(s13p), _ptr(w2p), _ptr(s2p), _ptr(out), _stream(hidden.device)),
+        "w4a8_fused_moe_prepacked_noalloc")
     return out
 
 
