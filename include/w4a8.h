@@ -106,10 +106,14 @@ int w4a8_quantize_act(const void* x_bf16, int64_t M, int64_t K, int64_t ldx,
  *   a_e4m3    [M, K] codes from w4a8_quantize_act; a_scales [M, K/128] fp32
  *   b_int4    [N, K/2] packed int4;                 b_scales [N, K/128] fp32
  *   out_bf16  [M, N] bf16, round to nearest even from the fp32 accumulator
- *   workspace device scratch of *workspace_bytes bytes (query with NULL)
+ *   workspace device scratch of *workspace_bytes bytes (query with NULL):
+ *             fp32 partial sums when K is cut into slices that run in
+ *             parallel (the query returns 0 when it is not)
  * M >= 0, N > 0, K > 0, K % 128 == 0; M*K < 2^32 and N*K/2 < 2^32 bytes,
- * M <= 4194240 (UNSUPPORTED otherwise).  fp32 accumulation order is the
- * kernel's; the result matches the fp64 definition within rounding.
+ * M <= 8388480 (UNSUPPORTED otherwise).  Reads the codes and scales exactly
+ * as w4a8_quantize_act writes them (no re-layout).  fp32 accumulation order
+ * is the kernel's (slices are added in K order); the result matches the fp64
+ * definition within rounding.
  */
 int w4a8_gemm(const uint8_t* a_e4m3, const float* a_scales, int64_t M, int64_t K,
               const uint8_t* b_int4, const float* b_scales, int64_t N,

@@ -145,8 +145,14 @@ def test_gemm_rejects_bad_arguments(L):
     assert g(BOGUS, BOGUS, 4, 128, BOGUS, BOGUS, 0, BOGUS, BOGUS, ctypes.byref(n), None) == INVALID
     assert g(None, BOGUS, 4, 128, BOGUS, BOGUS, 16, BOGUS, BOGUS, ctypes.byref(n), None) == INVALID
     assert g(BOGUS, BOGUS, 4, 128, BOGUS, BOGUS, 16, BOGUS, BOGUS, None, None) == INVALID
+    # K = 7168 is cut into slices whose partial sums need a workspace; the
+    # shape is checked to need one before a too-small one is passed (with
+    # bogus pointers a call must never get past validation)
+    need = ctypes.c_size_t(0)
+    assert g(None, None, 4, 7168, None, None, 16, None, None, ctypes.byref(need), None) == OK
+    assert need.value > 8
     small = ctypes.c_size_t(8)
-    assert g(BOGUS, BOGUS, 4, 128, BOGUS, BOGUS, 16, BOGUS, BOGUS, ctypes.byref(small), None) == WORKSPACE
+    assert g(BOGUS, BOGUS, 4, 7168, BOGUS, BOGUS, 16, BOGUS, BOGUS, ctypes.byref(small), None) == WORKSPACE
 
 
 def test_align_rejects_bad_arguments(L):

@@ -3,12 +3,21 @@
 The requantised intermediate (fp8 codes + scales of h = SwiGLU(gate_up)) and
 the down GEMM output are read back from the workspace (its layout comes from
 w4a8_fused_moe_workspace_layout) and compared, pair by pair in the same
-permuted order, with the oracle's.  The codes are not required to match
-bit for bit (fp32 vs fp64 accumulation can move h across a rounding
-boundary); their mismatch rate is reported and bounded.  Likewise the
-scale amax/448 of a block follows the GPU's value of its largest |h|: it is
-held to a relative bound of a few fp32 ulps, not to bit equality (the
-block-tiled path promotes in fp32, so most scales sit one ulp away).
+permuted order, with the oracle's.
+
+The codes are not required to match bit for bit: the GPU's gate and up are
+fp32 running sums (two roundings per 128-group), the oracle's are exact, so h
+can land on the other side of an e4m3 rounding boundary.  Their mismatch rate
+is reported and bounded by 1e-4 (measured: 2e-5 at 56 groups, 0 to 1e-5
+elsewhere).
+
+The scale amax/448 of a block follows the GPU's value of its largest |h|, so
+it carries that element's relative error.  With G groups and two fp32
+roundings per group the running sum's error grows like sqrt(2G) ulps (about
+10 at G = 56), and h = silu(gate) * up adds the errors of both factors; so a
+scale is held to 16 fp32 ulps (2^-19 relative), with at least half of them
+within 2 ulps, and the histogram is printed (measured at G = 56: 22% equal,
+34% one ulp, 22% two, 23% more, at most 12).
 """
 import numpy as np
 import pytest
@@ -57,6 +66,17 @@ def ulp_hist(ulps):
         np.count_nonzero(c) / n for c in (ulps == 0, ulps == 1, ulps == 2, ulps > 2))
 
 
+MAX_SCALE_ULPS = 16
+MAX_CODE_MISMATCH = 1e-4
+
+
+def check_bounds(code_mis, ulps, y2_fro):
+    assert code_mis <= MAX_CODE_MISMATCH, code_mis
+    assert int(ulps.max()) <= MAX_SCALE_ULPS, int(ulps.max())
+    assert np.mean(ulps <= 2) >= 0.5, np.mean(ulps <= 2)
+    assert y2_fro <= 1e-3, y2_fro
+
+
 @pytest.mark.parametrize("name", ["tiny", "decode", "skew_id", "tile_small"])
 def test_requant_codes_and_down_output(name):
     assert torch.cuda.is_available()
@@ -99,9 +119,7 @@ def test_requant_codes_and_down_output(name):
           "y2 rel_fro=%.3e max=%.3e"
           % (name, P, code_mis, int(np.sum(qh != inter["qh"])), qh.size, ulp_hist(ulps),
              int(ulps.max()), scale_rel, y2_fro, y2_max))
-    assert code_mis <= 1e-3
-    assert scale_rel <= 2e-6
-    assert y2_fro <= 1e-3
+    check_bounds(code_mis, ulps, y2_fro)
 
 
 @pytest.mark.parametrize("name", ["decode", "tile_small"])
@@ -141,6 +159,4 @@ def test_requant_codes_and_down_output_fp4(name):
           "y2 rel_fro=%.3e"
           % (name, P, code_mis, int(np.sum(qh != inter["qh"])), qh.size, ulp_hist(ulps),
              int(ulps.max()), scale_rel, y2_fro))
-    assert code_mis <= 1e-3
-    assert scale_rel <= 2e-6
-    assert y2_fro <= 1e-3
+    check_bounds(code_mis, ulps, y2_fro)

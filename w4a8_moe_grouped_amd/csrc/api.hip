@@ -111,44 +111,27 @@ size_t plan_moe(void* ws, int64_t T, int64_t H, int64_t topk, int64_t E, int64_t
     return c.used;
 }
 
-// The dense GEMM's launch: m-block height and the K split.  M x N tiles of
-// block_m x 256 alone give few workgroups at decode-like M (M = 128, N = 2048:
-// 16 of them on 256 CUs, each walking all of K), so K is split until about
-// 256 workgroups run, in slices of a multiple of 4 groups (the float4 scale
-// blocks) of at least 4 groups; the fp32 partial sums are then reduced in
-// split order by a second kernel.
-struct GemmPlan {
-    int block_m;
-    int32_t split_groups;  // 128-groups per K slice
-    int32_t splits;
-};
+// The dense GEMM's launch (dense.hip): workgroups of 128 rows x 64 weight
+// rows; K is cut into slices of at most 16 groups, and further while fewer
+// than ~256 workgroups would run (M = 128, N = 2048: 32 column blocks, 8
+// slices of 7 groups), the slices' fp32 partial sums added in slice order by
+// a second kernel.
 constexpr int64_t kGemmTargetWgs = 256;
-GemmPlan gemm_plan(int64_t M, int64_t K, int64_t N)
+int32_t gemm_split_groups(int64_t M, int64_t K, int64_t N)
 {
-    GemmPlan g;
-    g.block_m = M <= 16 ? 16 : (M <= 32 ? 32 : 64);
     const int64_t G = K / W4A8_GROUP;
-    const int64_t tiles = ceil_div(N, 256) * ceil_div(M, g.block_m);
-    int64_t gps = G;
-    if (N % 4 == 0 && G % 4 == 0 && tiles < kGemmTargetWgs && G >= 8) {
-        const int64_t want = ceil_div(kGemmTargetWgs, tiles);  // splits wanted
-        gps = ceil_div(ceil_div(G, want), 4) * 4;
-        if (gps < 4)
-            gps = 4;
-    }
-    g.split_groups = (int32_t)gps;
-    g.splits = (int32_t)ceil_div(G, gps);
-    return g;
+    const int64_t tiles = ceil_div(N, 64) * ceil_div(M, 128);
+    const int64_t want = tiles >= kGemmTargetWgs ? 1 : ceil_div(kGemmTargetWgs, tiles);
+    const int64_t gps = ceil_div(G, want);
+    const int64_t cap = w4a8::dense_max_split_groups();
+    return (int32_t)(gps < cap ? gps : cap);
 }
 
-size_t plan_gemm(void* ws, int64_t M, int64_t K, int64_t N, uint8_t** q_il, float2** side,
-                 float** part)
+size_t plan_gemm(void* ws, int64_t M, int64_t K, int64_t N, float** part)
 {
     Carve c(ws);
-    const GemmPlan g = gemm_plan(M, K, N);
-    *q_il = c.take<uint8_t>(M * K);
-    *side = c.take<float2>(M * (K / W4A8_GROUP));
-    *part = g.splits > 1 ? c.take<float>((size_t)g.splits * M * N) : nullptr;
+    const int64_t splits = ceil_div(K / W4A8_GROUP, gemm_split_groups(M, K, N));
+    *part = splits > 1 ? c.take<float>((size_t)splits * M * N) : nullptr;
     return c.used;
 }
 
@@ -258,19 +241,12 @@ int w4a8_gemm(const uint8_t* a_e4m3, const float* a_scales, int64_t M, int64_t K
         return W4A8_ERR_INVALID_ARG;
     if (K % W4A8_GROUP != 0)
         return W4A8_ERR_UNSUPPORTED;
-    // 32-bit buffer ranges: the activation codes [M, K] and the weights [N, K/2]
-    if (!below_u32(mul_sat(M, K)) || !below_u32(mul_sat(N, K / 2)) || M > INT32_MAX)
+    // 32-bit buffer ranges: the activation codes [M, K] and the weights [N, K/2];
+    // 128-row blocks on grid.y
+    if (!below_u32(mul_sat(M, K)) || !below_u32(mul_sat(N, K / 2)) || ceil_div(M, 128) > kMaxGridY)
         return W4A8_ERR_UNSUPPORTED;
-    const GemmPlan gp = gemm_plan(M, K, N);
-    const int block_m = gp.block_m;
-    if (ceil_div(M, block_m) > kMaxGridY)
-        return W4A8_ERR_UNSUPPORTED;
-    if (!skinny_k_ok(K, block_m))
-        return W4A8_ERR_UNSUPPORTED;
-    uint8_t* q_il;
-    float2* side;
     float* part;
-    const size_t need = plan_gemm(nullptr, M, K, N, &q_il, &side, &part);
+    const size_t need = plan_gemm(nullptr, M, K, N, &part);
     const int ws_rc = check_workspace(workspace, workspace_bytes, need);
     if (ws_rc >= 0)
         return ws_rc;
@@ -283,37 +259,15 @@ int w4a8_gemm(const uint8_t* a_e4m3, const float* a_scales, int64_t M, int64_t K
         return W4A8_ERR_UNSUPPORTED;
     if (M == 0)
         return W4A8_OK;
-    plan_gemm(workspace, M, K, N, &q_il, &side, &part);
-    hipError_t e = w4a8::launch_prep_codes(a_e4m3, a_scales, M, K, q_il, side, stream);
-    if (e != hipSuccess)
-        return W4A8_ERR_HIP;
-    w4a8::GemmArgs g = {};
-    g.sub_group = W4A8_GROUP;
-    g.act = q_il;
-    g.act_rows = M;
-    g.act_side = side;
-    g.sorted = nullptr;
-    g.topk = 1;
-    g.offsets = nullptr;
-    g.dense_rows = (int32_t)M;
-    g.w = b_int4;
-    g.ws = b_scales;
-    g.w_estride = 0;
-    g.s_estride = 0;
-    g.K = K;
-    g.N = N;
-    g.out_bf16 = (uint16_t*)out_bf16;
-    g.max_blocks = ceil_div(M, block_m);
-    if (gp.splits == 1)
-        return hip_status(w4a8::launch_gemm_skinny(g, w4a8::EPI_BF16, block_m, stream));
-    // K split: fp32 partials [splits, M, N], then their sum in split order
-    g.split_groups = gp.split_groups;
-    g.split_stride = M * N;
-    g.out_f32 = part;
-    e = w4a8::launch_gemm_skinny(g, w4a8::EPI_F32, block_m, stream);
-    if (e != hipSuccess)
-        return W4A8_ERR_HIP;
-    return hip_status(w4a8::launch_split_reduce(part, gp.splits, M, N, (uint16_t*)out_bf16, stream));
+    plan_gemm(workspace, M, K, N, &part);
+    const int32_t gps = gemm_split_groups(M, K, N);
+    hipError_t e = w4a8::launch_dense_gemm(a_e4m3, a_scales, M, K, b_int4, b_scales, N, gps, part,
+                                           (uint16_t*)out_bf16, stream);
+    if (e != hipSuccess || part == nullptr)
+        return hip_status(e);
+    // the slices' partial sums, in slice order, one bf16 rounding
+    return hip_status(w4a8::launch_split_reduce(part, (int32_t)ceil_div(K / W4A8_GROUP, gps), M, N,
+                                                (uint16_t*)out_bf16, stream));
 }
 
 int w4a8_moe_align(const int32_t* topk_ids, int64_t T, int64_t topk, int64_t expert_begin,

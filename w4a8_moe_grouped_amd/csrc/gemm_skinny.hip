@@ -18,7 +18,6 @@
 //
 // Epilogues:
 //   EPI_F32      out_f32[p, n]                       (down GEMM)
-//   EPI_BF16     out_bf16[p, n]                      (dense linear)
 //   EPI_SWIGLU_Q the tile holds gate rows i and up rows I+i of one 128-block
 //                of i: h = silu(gate) * up, then fp8 requant of the block
 //                (DeepGEMM PR #53 "Changes": SwiGLU -> per-token FP8 requant;
@@ -49,7 +48,6 @@ __global__ __launch_bounds__(256, NT == 2 ? 2 : 1) void gemm_skinny_kernel(GemmA
 {
     constexpr int kNF = NF;
     static_assert(SG == 128 || SG == 64 || SG == 32, "activation block of 128, 64 or 32 K");
-    static_assert(SG == 128 || EPI != EPI_BF16, "the dense GEMM keeps per-128 scales");
     constexpr int ASPG = EPI == EPI_F32 ? 128 / SG : 1;       // A-side scale blocks per group
     constexpr int OSPG = EPI == EPI_SWIGLU_Q ? 128 / SG : 1;  // requant blocks per 128 i
     static_assert(EPI != EPI_SWIGLU_Q || NF == 4, "the SwiGLU tile pairs 2 gate and 2 up fragments");
@@ -64,11 +62,7 @@ __global__ __launch_bounds__(256, NT == 2 ? 2 : 1) void gemm_skinny_kernel(GemmA
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6, q = lane >> 4, c16 = lane & 15;
     const int64_t K = a.K, N = a.N;
-    // K split across blockIdx.z (dense GEMM): this workgroup reduces groups
-    // [gbase, gbase + G) of the Gt groups of K; strides use Gt
-    const int Gt = (int)(K / kGroup);
-    const int gbase = (int)blockIdx.z * a.split_groups;
-    const int G = min(a.split_groups, Gt - gbase);
+    const int G = (int)(K / kGroup);
 
     int e, row0, rows;
     if (a.offsets != nullptr) {
@@ -107,18 +101,18 @@ __global__ __launch_bounds__(256, NT == 2 ? 2 : 1) void gemm_skinny_kernel(GemmA
     // activation operand is fp8 on both paths (one byte per element); the
     // lane's two 16-byte chunks of a group are q and 4+q (fp8_group_pos).
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.w + (int64_t)e * a.w_estride, (uint32_t)(N * (K / 2)));
-    const int64_t PG4 = packed_groups4(Gt);  // 4-group scale blocks per row (prepacked)
+    const int64_t PG4 = packed_groups4(G);  // 4-group scale blocks per row (prepacked)
     const __amdgpu_buffer_rsrc_t rs =
-        make_rsrc(a.ws + (int64_t)e * a.s_estride, (uint32_t)(PK ? N * PG4 * 16 : N * Gt * 4));
+        make_rsrc(a.ws + (int64_t)e * a.s_estride, (uint32_t)(PK ? N * PG4 * 16 : N * G * 4));
     uint32_t vw[kNF], vs[kNF];
 #pragma unroll
     for (int f = 0; f < kNF; ++f) {
         // (prepacked: the rows of a fragment are 16-aligned, nrow % 16 == c16
         // except for clamped rows, which read a valid row of no consequence)
-        vw[f] = PK ? (uint32_t)(((nrow[f] >> 4) * Gt * 16 + (nrow[f] & 15)) * 64 + 16 * q)
+        vw[f] = PK ? (uint32_t)(((nrow[f] >> 4) * G * 16 + (nrow[f] & 15)) * 64 + 16 * q)
                    : (uint32_t)(nrow[f] * (K / 2) + 16 * q);
         vs[f] = PK ? (uint32_t)(((nrow[f] >> 4) * PG4 * 16 + (nrow[f] & 15)) * 16)
-                   : (uint32_t)(nrow[f] * Gt * 4);
+                   : (uint32_t)(nrow[f] * G * 4);
     }
     // Activation rows of a group (BM x 128 bytes), two ways:
     //  * SHARED: loaded once per workgroup straight into LDS (kAPer loads of
@@ -171,8 +165,7 @@ __global__ __launch_bounds__(256, NT == 2 ? 2 : 1) void gemm_skinny_kernel(GemmA
     const bool side_in_regs = nside <= 256 * kSidePer;
     auto side_of = [&](int i) {
         const int gb = i / BM, c = i - gb * BM;
-        return c < rows ? a.act_side[(int64_t)act_row(c) * (Gt * ASPG) + gbase * ASPG + gb]
-                        : make_float2(0.0f, 0.0f);
+        return c < rows ? a.act_side[(int64_t)act_row(c) * (G * ASPG) + gb] : make_float2(0.0f, 0.0f);
     };
     if (side_in_regs) {
 #pragma unroll
@@ -265,8 +258,7 @@ __global__ __launch_bounds__(256, NT == 2 ? 2 : 1) void gemm_skinny_kernel(GemmA
     // only ever wait longer than needed.
     constexpr int kWLoads = SW4 ? kNF : 2 * kNF;
     constexpr int kAfter = kWLoads + (DW - 1) * (kAPer + kWLoads);
-    auto load_group = [&](int s, int gloc, int buf) {
-        const int g = gbase + gloc;  // absolute group
+    auto load_group = [&](int s, int g, int buf) {
         if constexpr (SHARED && !ST) {
             // activation chunks first, so that the wait for them has the same
             // count on every group
@@ -294,12 +286,11 @@ __global__ __launch_bounds__(256, NT == 2 ? 2 : 1) void gemm_skinny_kernel(GemmA
                     ab[s][t][v] = bload16(ra, va[t], (uint32_t)g * kGroup + 64u * v);
         }
     };
-    auto load_scales4 = [&](float4 (&dst)[SW4 ? kNF : 1], int blk) {  // local groups 4blk..4blk+3
+    auto load_scales4 = [&](float4 (&dst)[SW4 ? kNF : 1], int blk) {  // groups 4blk..4blk+3
         if (SW4) {
-            const uint32_t ab = (uint32_t)(gbase / 4 + blk);  // gbase % 4 == 0 with SW4
 #pragma unroll
             for (int f = 0; f < kNF; ++f)
-                dst[f] = __builtin_bit_cast(float4, bload16(rs, vs[f], ab * (PK ? 256u : 16u)));
+                dst[f] = __builtin_bit_cast(float4, bload16(rs, vs[f], (uint32_t)blk * (PK ? 256u : 16u)));
         }
     };
     __builtin_amdgcn_sched_barrier(0);
@@ -360,7 +351,7 @@ __global__ __launch_bounds__(256, NT == 2 ? 2 : 1) void gemm_skinny_kernel(GemmA
             auto act16 = [&](int t, int v) {  // the lane's chunk 4v + q of row 16t + c16
                 if constexpr (ST)  // (padding rows read row 0)
                     return *(const v4i*)(stage + (16 * t + c16 < rows ? 16 * t + c16 : 0) * KS +
-                                         (int64_t)(gbase + gl) * kGroup + 16 * (4 * v + q));
+                                         (int64_t)gl * kGroup + 16 * (4 * v + q));
                 else if constexpr (SHARED)
                     return *(const v4i*)(sa + 16 * ((16 * t + c16) * 8 + ((4 * v + q) ^ (c16 & 7))));
                 else
@@ -599,7 +590,7 @@ __global__ __launch_bounds__(256, NT == 2 ? 2 : 1) void gemm_skinny_kernel(GemmA
     }
 
     // ---- epilogues ----  output element (row 16t+4q+r of the block, weight row nrow[f])
-    if (EPI == EPI_F32 || EPI == EPI_BF16) {
+    if (EPI == EPI_F32) {
 #pragma unroll
         for (int f = 0; f < kNF; ++f) {
             if (!nvalid[f])
@@ -610,11 +601,7 @@ __global__ __launch_bounds__(256, NT == 2 ? 2 : 1) void gemm_skinny_kernel(GemmA
                 for (int r = 0; r < 4; ++r) {
                     const int row = 16 * t + 4 * q + r;
                     if (row < rows) {
-                        const int64_t o = (int64_t)blockIdx.z * a.split_stride + (int64_t)(row0 + row) * N + nrow[f];
-                        if (EPI == EPI_F32)
-                            a.out_f32[o] = acc[f][t][r];
-                        else
-                            a.out_bf16[o] = f32_to_bf16(acc[f][t][r]);
+                        a.out_f32[(int64_t)(row0 + row) * N + nrow[f]] = acc[f][t][r];
                     }
                 }
         }
@@ -720,19 +707,15 @@ template <int NT, int EPI, int DW, bool F16, bool SW4, bool PK, bool FP4, int NF
 static hipError_t launch_one(const GemmArgs& a0, hipStream_t s)
 {
     const int64_t G = a0.K / kGroup;
-    const int64_t Gw = a0.split_groups > 0 && a0.split_groups < G ? a0.split_groups : G;  // groups per workgroup
-    const size_t side = (size_t)Gw * (EPI == EPI_F32 ? 128 / SG : 1) * 16 * NT * sizeof(float2);
+    const size_t side = (size_t)G * (EPI == EPI_F32 ? 128 / SG : 1) * 16 * NT * sizeof(float2);
     // 16-row blocks of the down and dense GEMMs: LDS for the whole-K
     // activation rows of up to stage_rows rows (1 KB pieces, so K % 1024 ==
     // 0), within a quarter of the CU's LDS (the down instance runs four
     // workgroups per CU) less the side data, the shared-rows ring of the
     // fallback loop (static LDS) and 4 KB of other static LDS
     GemmArgs a = a0;
-    if (a.split_groups <= 0 || a.split_groups > G)
-        a.split_groups = (int32_t)G;  // no K split
-    const int64_t splits = (G + a.split_groups - 1) / a.split_groups;
     a.stage_rows = 0;
-    if (NT == 1 && SG == 128 && EPI != EPI_SWIGLU_Q && a.K % 1024 == 0 && splits == 1) {
+    if (NT == 1 && SG == 128 && EPI != EPI_SWIGLU_Q && a.K % 1024 == 0) {
         const int64_t ring = EPI == EPI_F32 ? (DW + 1) * 16 * kGroup : 0;
         const int64_t share = 160 * 1024 / 4 - 4096 - (int64_t)side - ring;
         const int64_t r = share / (a.K + 16);
@@ -745,7 +728,7 @@ static hipError_t launch_one(const GemmArgs& a0, hipStream_t s)
     else
         grid.x = (unsigned)((a.N + 64 * NF - 1) / (64 * NF));
     grid.y = (unsigned)a.max_blocks;
-    grid.z = (unsigned)splits;
+    grid.z = 1;
     if (grid.x == 0 || grid.y == 0)
         return hipSuccess;
     hipLaunchKernelGGL((gemm_skinny_kernel<NT, EPI, DW, F16, SW4, PK, FP4, NF, SG>), grid, dim3(256), lds, s, a);
@@ -769,20 +752,12 @@ static hipError_t launch_one(const GemmArgs& a0, hipStream_t s)
 template <int NT, int DW, bool PK, bool FP4, int SG>
 static hipError_t launch_nt(const GemmArgs& a, int epilogue, hipStream_t s)
 {
-    // float4 scale blocks: every workgroup's groups start and end on a block
-    const bool g4 = (a.K / kGroup) % 4 == 0 && (a.split_groups <= 0 || a.split_groups % 4 == 0);
+    const bool g4 = (a.K / kGroup) % 4 == 0;
     constexpr int NFD = NT == 1 ? W4A8_DOWN_NF16 : 4;
     switch (epilogue) {
     case EPI_F32:
         return g4 && NT != 2 ? launch_one<NT, EPI_F32, DW, false, 4 % DW == 0, PK, FP4, NFD, SG>(a, s)
                   : launch_one<NT, EPI_F32, DW, false, false, PK, FP4, NFD, SG>(a, s);
-    case EPI_BF16:
-        if constexpr (PK || SG != 128) {
-            return hipErrorInvalidValue;  // the dense GEMM: canonical weights, per-128 scales
-        } else {
-            return g4 ? launch_one<NT, EPI_BF16, DW, false, 4 % DW == 0, false, false>(a, s)
-                      : launch_one<NT, EPI_BF16, DW, false, false, false, false>(a, s);
-        }
     default:
         return g4 && NT != 2 ? launch_one<NT, EPI_SWIGLU_Q, DW, true, 4 % DW == 0, PK, FP4, 4, SG>(a, s)
                   : launch_one<NT, EPI_SWIGLU_Q, DW, true, false, PK, FP4, 4, SG>(a, s);
@@ -809,39 +784,6 @@ static hipError_t launch_layout(const GemmArgs& a, int epilogue, hipStream_t s)
     if (a.fp4 || a.sub_group != 128)
         return hipErrorInvalidValue;
     return launch_nt<NT, DW, false, false, 128>(a, epilogue, s);
-}
-
-// Partial sums of a K-split dense GEMM -> bf16: out[m, n] = bf16(sum over
-// splits z ascending of part[z][m, n]), one rounding.  Four columns per thread.
-__global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restrict__ part, int32_t splits,
-                                                           int64_t MN, uint16_t* __restrict__ out)
-{
-    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
-    if (i >= MN)
-        return;
-    float4 acc = *(const float4*)(part + i);
-    for (int z = 1; z < splits; ++z) {
-        const float4 v = *(const float4*)(part + (int64_t)z * MN + i);
-        acc.x += v.x;
-        acc.y += v.y;
-        acc.z += v.z;
-        acc.w += v.w;
-    }
-    uint2 o;
-    o.x = (uint32_t)f32_to_bf16(acc.x) | ((uint32_t)f32_to_bf16(acc.y) << 16);
-    o.y = (uint32_t)f32_to_bf16(acc.z) | ((uint32_t)f32_to_bf16(acc.w) << 16);
-    *(uint2*)(out + i) = o;
-}
-
-hipError_t launch_split_reduce(const float* part, int32_t splits, int64_t M, int64_t N, uint16_t* out,
-                               hipStream_t s)
-{
-    const int64_t MN = M * N;  // N % 4 == 0 (checked by the caller)
-    if (MN == 0)
-        return hipSuccess;
-    hipLaunchKernelGGL(split_reduce_kernel, dim3((unsigned)((MN / 4 + 255) / 256)), dim3(256), 0, s, part,
-                       splits, MN, out);
-    return hipGetLastError();
 }
 
 hipError_t launch_gemm_skinny(const GemmArgs& a, int epilogue, int block_m, hipStream_t s)

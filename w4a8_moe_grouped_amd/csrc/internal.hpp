@@ -17,9 +17,6 @@ namespace w4a8 {
 hipError_t launch_quant_bf16(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
                              float* scales, float2* side, int mode, const float* fixed_scale,
                              hipStream_t s);
-// canonical codes + scales (from w4a8_quantize_act) -> interleaved codes + side data
-hipError_t launch_prep_codes(const uint8_t* q, const float* scales, int64_t M, int64_t K,
-                             uint8_t* q_il, float2* side, hipStream_t s);
 
 // ---- routing permutation (align.hip) ----
 struct AlignOut {
@@ -87,15 +84,20 @@ struct GemmArgs {
     // skinny kernel, 16-row m-blocks: blocks of at most this many rows read
     // their activations from a whole-K copy in LDS (set by the launcher)
     int32_t stage_rows;
-    // skinny kernel, K split over grid.z (dense GEMM): each workgroup reduces
-    // split_groups 128-groups of K (0 = all of them) and the store epilogue
-    // writes split z at out_f32 + z * split_stride
-    int32_t split_groups;
-    int64_t split_stride;
 };
-enum Epilogue { EPI_F32 = 0, EPI_BF16 = 1, EPI_SWIGLU_Q = 2 };
+enum Epilogue { EPI_F32 = 0, EPI_SWIGLU_Q = 2 };
 hipError_t launch_gemm_skinny(const GemmArgs& a, int epilogue, int block_m, hipStream_t s);
-// out[M, N] bf16 = sum over `splits` fp32 partials part[z][M, N] (N % 4 == 0)
+
+// ---- dense linear (dense.hip) ----
+// canonical codes [M, K] + scales [M, K/128] x packed int4 [N, K/2] + scales
+// [N, K/128]; K cut in slices of split_groups 128-groups (at most
+// dense_max_split_groups()); one slice: bf16 out, else fp32 partials
+// part[slice][M, N]
+int dense_max_split_groups();
+hipError_t launch_dense_gemm(const uint8_t* a, const float* sa, int64_t M, int64_t K, const uint8_t* w,
+                             const float* sw, int64_t N, int32_t split_groups, float* part,
+                             uint16_t* out, hipStream_t s);
+// out[M, N] bf16 = sum over `splits` fp32 partials part[z][M, N], in z order
 hipError_t launch_split_reduce(const float* part, int32_t splits, int64_t M, int64_t N, uint16_t* out,
                                hipStream_t s);
 
