@@ -15,6 +15,8 @@ against the CPU oracle, at the same bars as test_gpu_parity.py).
   than 24 binades (the exact f16 conversion of the small blocks underflows).
 * Full-size prefill and its EP8 rank share, with one token from every 16-row
   slice of every 160-row m-block of every local expert.
+* The block-tiled down GEMM with several tiles per workgroup (its stage ring
+  runs across tile boundaries).
 """
 import concurrent.futures
 
@@ -98,8 +100,8 @@ def biased_hidden(cfg, seed):
 
 @pytest.mark.parametrize("M,N", [(128, 2048), (4, 256)])
 def test_gemm_same_sign_activations(dev, M, N):
-    """Dense linear (fp8 MFMA, biased weight codes) on x = |N(0,1)| + 3 at
-    K = 7168; M = 4 takes the 16-row whole-K staged path."""
+    """Dense linear (fp8 MFMA) on x = |N(0,1)| + 3 at K = 7168; M = 4 is a
+    partial 128-row block."""
     K = 7168
     z = synth.draw_normal(40 + M, synth.STREAM_X, 0, M * K)
     x = synth.to_bf16_bits(np.abs(z) + 3.0).reshape(M, K)
@@ -229,3 +231,38 @@ def test_fused_prefill_every_slice(dev, name):
     ids = d["topk_ids"]
     none_local = ~np.any((ids >= cfg.expert_begin) & (ids < cfg.expert_begin + cfg.E_local), axis=1)
     assert np.all(got[none_local] == 0)
+
+
+# ---------------------------------------------------------------------------
+# block-tiled down GEMM: several tiles per workgroup, the stage ring running
+# across tile boundaries (down K of 4 groups or more)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("fp4", [False, True])
+def test_fused_tile_stream_across_tiles(dev, fp4):
+    """2048 tokens, top-2 of 16 experts, all local (256 pairs per expert on
+    average: the block-tiled path), H = 7168 (28 down weight blocks), I = 512
+    (4 groups): 29 m-blocks x 28 = 812 down tiles, about 4 per workgroup.
+    Experts 0..3 get 80, 81, 160 and 161 rows (an idle row half, a one-row
+    half, a full block, a one-row block), the others share the rest; one token
+    from every 16-row slice of every m-block is compared."""
+    make = synth.random_moe_fp4 if fp4 else synth.random_moe
+    cfg, d = make(2048, 7168, 512, 16, 2, 0, 16, seed=89)
+    rng = np.random.default_rng(89)
+    counts = [80, 81, 160, 161]
+    rest = cfg.T * cfg.topk - sum(counts)
+    counts += [rest // 12 + (1 if i < rest % 12 else 0) for i in range(12)]
+    # expert ids sorted, token t takes entries t and t + T (distinct: no
+    # expert has T entries), then the tokens are shuffled
+    flat = np.concatenate([np.full(c, e) for e, c in enumerate(counts)])
+    ids = np.stack([flat[:cfg.T], flat[cfg.T:]], axis=1)[rng.permutation(cfg.T)]
+    assert np.all(ids[:, 0] != ids[:, 1])
+    d["topk_ids"] = np.ascontiguousarray(ids.astype(np.int32))
+    assert np.array_equal(np.bincount(d["topk_ids"].ravel(), minlength=16), counts)
+    lay = w4.fused_moe_workspace_layout(cfg.T, cfg.H, cfg.topk, cfg.E_local, cfg.I)
+    assert lay["block_m"] == 160
+    got = run_fused(d, cfg, dev, fp4=fp4)
+    rows = slice_rows(d, cfg, seed=90)
+    ref = oracle_rows_parallel(d, cfg, rows, fn=oracle.fused_moe_fp4 if fp4 else None)
+    assert_bf16_close(got[rows], ref, "tile stream%s, 812 down tiles (%d tokens)"
+                      % (" fp4" if fp4 else "", rows.size))

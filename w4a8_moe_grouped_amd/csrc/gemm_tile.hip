@@ -488,6 +488,342 @@ __global__ __launch_bounds__(kTThreads) void gemm_tile_kernel(GemmArgs a)
     }
 }
 
+// ---------------------------------------------------------------------------
+// The down GEMM as one stream of (tile, group) stages per workgroup.
+//
+// Per tile the loop above pays an expert lookup, a cold start of its stage
+// ring (three groups' loads before the first MFMA) and the fp32 epilogue
+// before the next tile's first load (measured: ~2850 cycles per wave and
+// group against ~31 us per tile on the EP8 share, ~12 us of it outside the
+// main loop).  Here the ring runs on across tiles: while the last groups of
+// a tile are computed, the first groups of the workgroup's next tile are
+// already loading into the stages freed behind them, and the epilogue's
+// stores overlap those loads.  Every tile's expert, weight block and rows
+// are found once at the start (block_start and offsets copied into LDS, a
+// binary search per tile), so no global load that the compiler would wait on
+// sits inside the stream.
+// ---------------------------------------------------------------------------
+constexpr int kMaxStreamTiles = 256;
+
+template <bool PK, bool FP4>
+__device__ __forceinline__ void down_stream(const GemmArgs& a, uint8_t* smem, int4* s_meta, int nt,
+                                            int first_L, int stride)
+{
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, q = lane >> 4, c16 = lane & 15;
+    const int wm = wave >> 2, wn = wave & 3;
+    const int64_t K = a.K, N = a.N;
+    const int G = (int)(K / kGroup);
+    const int E = a.num_experts;
+    const int nbn = (int)((N + kTBN - 1) / kTBN);
+    const int64_t G4 = packed_groups4(G);
+
+    // ---- the tiles' metadata: expert, weight block, first row, rows ----
+    {
+        int* s_bs = (int*)smem;        // [E + 1] (the stages are not in use yet)
+        int* s_off = s_bs + (E + 1);   // [E + 1]
+        for (int i = tid; i <= E; i += kTThreads) {
+            s_bs[i] = a.block_start[i];
+            s_off[i] = a.offsets[i];
+        }
+        __syncthreads();
+        if (tid < nt) {
+            const int L = first_L + tid * stride;
+            int lo = 0, hi = E;  // the largest e with block_start[e] * nbn <= L owns tile L
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if (s_bs[mid] * nbn <= L)
+                    lo = mid;
+                else
+                    hi = mid;
+            }
+            const int bs = s_bs[lo], nbe = s_bs[lo + 1] - bs;
+            const int local = L - bs * nbn;
+            const int nb = local / nbe;
+            const int row0 = s_off[lo] + (local - nb * nbe) * kTBM;  // the expert's m-blocks are consecutive
+            s_meta[tid] = make_int4(lo, nb, row0, min(kTBM, s_off[lo + 1] - row0));
+        }
+        __syncthreads();
+    }
+
+    // ---- per-tile load addresses (as tile_body) ----
+    const v4i ra = sgpr_rsrc(a.act, (uint32_t)(a.act_rows * K));
+    const v4i rsd = sgpr_rsrc(a.act_side, (uint32_t)(a.act_rows * G * 8));
+    struct Ctx {
+        v4i rw, rws;
+        uint32_t va[3], vb[2], vx[2];
+        int nb, row0, rows;
+    };
+    auto make_ctx = [&](int k) {
+        Ctx c;
+        const int4 m = s_meta[k];
+        const int e = __builtin_amdgcn_readfirstlane(m.x);
+        c.nb = __builtin_amdgcn_readfirstlane(m.y);
+        c.row0 = __builtin_amdgcn_readfirstlane(m.z);
+        c.rows = __builtin_amdgcn_readfirstlane(m.w);
+        c.rw = sgpr_rsrc(a.w + (int64_t)e * a.w_estride, (uint32_t)(N * (K / 2)));
+        c.rws = sgpr_rsrc(a.ws + (int64_t)e * a.s_estride, (uint32_t)(PK ? N * G4 * 16 : N * G * 4));
+        auto act_row = [&](int i) { return c.row0 + (i < c.rows ? i : 0); };
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+            const int sl = (wave + 8 * j) * 64 + lane;
+            const int r = min(sl >> 3, kTBM - 1), ca = (sl & 7) ^ (r & 7);
+            c.va[j] = (uint32_t)((int64_t)act_row(r) * K + 16 * ca);
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int sl = (wave + 8 * j) * 64 + lane;
+            const int wr = sl >> 2, cb = (sl & 3) ^ ((wr >> 1) & 3);
+            int64_t n = (int64_t)c.nb * kTBN + wr;
+            n = n < N ? n : N - 1;
+            c.vb[j] = PK ? (uint32_t)(((n >> 4) * G * 16 + (n & 15)) * 64 + 16 * cb)
+                         : (uint32_t)(n * (K / 2) + 16 * cb);
+        }
+        c.vx[0] = c.vx[1] = 0u;
+        if (wave < 4) {
+            int64_t n = (int64_t)c.nb * kTBN + wave * 64 + lane;
+            n = n < N ? n : N - 1;
+            c.vx[0] = PK ? (uint32_t)(((n >> 4) * G4 * 16 + (n & 15)) * 16) : (uint32_t)(n * G * 4);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int d = min((wave - 4 + 4 * j) * 64 + lane, 2 * kTBM - 1);
+                c.vx[j] = (uint32_t)(((int64_t)act_row(d >> 1) * G) * 8 + 4 * (d & 1));
+            }
+        }
+        return c;
+    };
+    const uint32_t smem_lds = (uint32_t)(uintptr_t)(lds_ptr_t)smem;
+    auto issue = [&](const Ctx& c, int g, int st) {
+        const uint32_t base = smem_lds + (uint32_t)(st * kStageBytes);
+#pragma unroll
+        for (int j = 0; j < 3; ++j)
+            if (wave + 8 * j < kALoads)
+                lds_load16(ra, base + kAOff + (uint32_t)(wave + 8 * j) * 1024u, c.va[j], (uint32_t)g * kGroup);
+        const uint32_t gw = (uint32_t)g * (PK ? 1024u : 64u);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            lds_load16(c.rw, base + kBOff + (uint32_t)(wave + 8 * j) * 1024u, c.vb[j], gw);
+        if (wave < 4) {
+            lds_load4(c.rws, base + kSwOff + wave * 256, c.vx[0],
+                      PK ? (uint32_t)(g >> 2) * 256u + (uint32_t)(g & 3) * 4u : (uint32_t)g * 4u);
+        } else {
+            lds_load4(rsd, base + kSideOff + (wave - 4) * 256, c.vx[0], (uint32_t)g * 8u);
+            if (wave == 4)
+                lds_load4(rsd, base + kSideOff + 4 * 256, c.vx[1], (uint32_t)g * 8u);
+        }
+    };
+    // this wave's loads per stage: waves 0-4 issue 6, waves 5-7 issue 5
+    const bool six_loads = wave <= 4;
+    auto wait_behind = [&](int behind) {  // the stage `behind` stages before the newest landed
+        if (behind >= 2) {
+            if (six_loads)
+                wait_vmcnt<12>();
+            else
+                wait_vmcnt<10>();
+        } else if (behind == 1) {
+            if (six_loads)
+                wait_vmcnt<6>();
+            else
+                wait_vmcnt<5>();
+        } else {
+            wait_vmcnt<0>();
+        }
+    };
+
+    int wrow_f[4];
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+        wrow_f[f] = 64 * wn + 16 * f + c16;
+    auto read_b = [&](const uint8_t* base, v4i (&wb)[4], float (&sw)[4]) {
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+            wb[f] = *(const v4i*)(base + kBOff + 16 * b_slot(wrow_f[f], q));
+            sw[f] = *(const float*)(base + kSwOff + 4 * wrow_f[f]);
+        }
+    };
+    auto read_a = [&](const uint8_t* base, int m, v4i& a0, v4i& a1) {
+        const int trow = kHalf * wm + 16 * m;
+        a0 = *(const v4i*)(base + kAOff + 16 * a_slot(trow + c16, q));
+        a1 = *(const v4i*)(base + kAOff + 16 * a_slot(trow + c16, 4 + q));
+    };
+    auto read_side = [&](const uint8_t* base, int m, float4& s01, float4& s23) {
+        const float4* sd = (const float4*)(base + kSideOff + 8 * (kHalf * wm + 16 * m + 4 * q));
+        s01 = sd[0];
+        s23 = sd[1];
+    };
+
+    float acc[kSlices][4][4];
+#pragma unroll
+    for (int m = 0; m < kSlices; ++m)
+#pragma unroll
+        for (int f = 0; f < 4; ++f)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                acc[m][f][r] = 0;
+
+    Ctx cur = make_ctx(0);
+    bool has_nxt = nt > 1;
+    Ctx nxt = make_ctx(has_nxt ? 1 : 0);
+    // prologue (G >= 4: positions 0..3 belong to the first tile)
+#pragma unroll
+    for (int p = 0; p < kStages - 1; ++p)
+        issue(cur, p, p);
+    wait_behind(2);
+    barrier();
+    issue(cur, kStages - 1, kStages - 1);
+
+    bool idle = kHalf * wm >= cur.rows;  // this wave's row half of the tile is empty
+    v4i wb[4], a0 = {}, a1 = {};
+    float sw[4];
+    float4 s01 = {}, s23 = {};
+    read_b(smem, wb, sw);
+    read_a(smem, 0, a0, a1);
+    read_side(smem, 0, s01, s23);
+
+    int base = 0;  // stream position of the current tile's group 0
+    for (int k = 0;;) {
+        for (int g = 0; g < G; ++g) {
+            const uint8_t* sp = smem + ((base + g) & 3) * kStageBytes;
+            if (!idle) {
+                int eq[4];
+                float swc[4];
+                v8i b8[4];
+#pragma unroll
+                for (int f = 0; f < 4; ++f) {
+                    if (FP4) {
+                        eq[f] = (int)((__builtin_bit_cast(uint32_t, sw[f]) >> (8 * q)) & 0xFFu);
+                    } else {
+                        swc[f] = sw[f];
+                        b8[f] = unpack_int4_u(wb[f]);
+                    }
+                }
+#pragma unroll
+                for (int m = 0; m < kSlices; ++m) {
+                    const v4i ca0 = a0, ca1 = a1;
+                    const float4 cs01 = s01, cs23 = s23;
+                    if (m + 1 < kSlices) {
+                        read_a(sp, m + 1, a0, a1);
+                        read_side(sp, m + 1, s01, s23);
+                    }
+                    const v8i av = {ca0[0], ca0[1], ca0[2], ca0[3], ca1[0], ca1[1], ca1[2], ca1[3]};
+                    v4f raw[4];
+#pragma unroll
+                    for (int f = 0; f < 4; ++f)
+                        raw[f] = FP4 ? mfma16x16x128_fp4(av, wb[f], eq[f])
+                                     : mfma16x16x128(av, b8[f], v4f{0.0f, 0.0f, 0.0f, 0.0f});
+                    const float c1[4] = {cs01.x, cs01.z, cs23.x, cs23.z};
+                    const float c0[4] = {cs01.y, cs01.w, cs23.y, cs23.w};
+#pragma unroll
+                    for (int f = 0; f < 4; ++f)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            if (FP4)  // weight scales inside raw: y += sa * raw
+                                acc[m][f][r] = fmaf(raw[f][r], c1[r] * 0x1p-9f, acc[m][f][r]);
+                            else
+                                acc[m][f][r] = fmaf(swc[f], fmaf(raw[f][r], c1[r], c0[r]), acc[m][f][r]);
+                        }
+                }
+            }
+            if (g + 1 < G) {
+                // position g + 1 landed for everyone; the stage of group g is
+                // free: refill it with position base + g + 4 (the next tile's
+                // first groups once this tile's are all issued)
+                wait_behind(min(2, G - 2 - g + (has_nxt ? G : 0)));
+                barrier();
+                const int p = g + kStages;
+                if (p < G)
+                    issue(cur, p, (base + g) & 3);
+                else if (has_nxt)
+                    issue(nxt, p - G, (base + g) & 3);
+                const uint8_t* np = smem + ((base + g + 1) & 3) * kStageBytes;
+                if (!idle) {
+                    read_b(np, wb, sw);
+                    read_a(np, 0, a0, a1);
+                    read_side(np, 0, s01, s23);
+                }
+            }
+        }
+        // epilogue: element (tile row 80wm + 16m + 4q + r, fragment f); the
+        // next tile's groups 0..2 are in flight meanwhile
+        if (!idle) {
+#pragma unroll
+            for (int f = 0; f < 4; ++f) {
+                const int64_t n = (int64_t)cur.nb * kTBN + wrow_f[f];
+                if (n >= N)
+                    continue;
+#pragma unroll
+                for (int m = 0; m < kSlices; ++m)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int row = kHalf * wm + 16 * m + 4 * q + r;
+                        if (row < cur.rows)
+                            a.out_f32[(int64_t)(cur.row0 + row) * N + n] = acc[m][f][r];
+                    }
+            }
+        }
+        if (!has_nxt)
+            break;
+        // Stores may complete out of order with the loads, so no vmcnt count
+        // below zero is exact while they are pending: wait for everything
+        // (the stores and the next tile's groups 0..2), then go on with exact
+        // counts.  The stage of this tile's last group is free after the
+        // barrier: refill it with the next tile's group 3.
+        wait_vmcnt<0>();
+        barrier();
+        issue(nxt, kStages - 1, (base + G - 1) & 3);
+#pragma unroll
+        for (int m = 0; m < kSlices; ++m)
+#pragma unroll
+            for (int f = 0; f < 4; ++f)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    acc[m][f][r] = 0;
+        base += G;
+        ++k;
+        cur = nxt;
+        idle = kHalf * wm >= cur.rows;
+        has_nxt = k + 1 < nt;
+        if (has_nxt)
+            nxt = make_ctx(k + 1);
+        if (!idle) {
+            const uint8_t* np = smem + (base & 3) * kStageBytes;
+            read_b(np, wb, sw);
+            read_a(np, 0, a0, a1);
+            read_side(np, 0, s01, s23);
+        }
+    }
+}
+
+template <bool PK, bool FP4>
+__global__ __launch_bounds__(kTThreads) void gemm_down_stream_kernel(GemmArgs a)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
+    __shared__ int4 s_meta[kMaxStreamTiles];
+    __shared__ int s_expert;
+    const int G = (int)(a.K / kGroup);
+    const int nbn = (int)((a.N + kTBN - 1) / kTBN);
+    const int total = *a.num_blocks * nbn;
+    const int per_xcd = (total + 7) >> 3;
+    const int x = (int)(blockIdx.x & 7);
+    const int stride = (int)(gridDim.x >> 3);
+    const int t0 = (int)(blockIdx.x >> 3);
+    // this workgroup's tiles: L = x * per_xcd + t, t = t0, t0 + stride, ...
+    const int tend = min(per_xcd, total - x * per_xcd);
+    const int nt = tend > t0 ? (tend - t0 + stride - 1) / stride : 0;
+    if (nt == 0)
+        return;
+    if (G >= kStages && nt <= kMaxStreamTiles) {
+        down_stream<PK, FP4>(a, smem, s_meta, nt, x * per_xcd + t0, stride);
+        return;
+    }
+    for (int t = t0; t < tend; t += stride) {  // short K or very many tiles: tile by tile
+        tile_body<TILE_DOWN, PK, FP4>(a, x * per_xcd + t, smem, &s_expert);
+        __syncthreads();
+    }
+}
+
 hipError_t launch_gemm_tile(const GemmArgs& a, int mode, hipStream_t s)
 {
     const int64_t nbn = mode == TILE_GATEUP ? a.I / kGroup : (a.N + kTBN - 1) / kTBN;
@@ -513,11 +849,11 @@ hipError_t launch_gemm_tile(const GemmArgs& a, int mode, hipStream_t s)
             hipLaunchKernelGGL((gemm_tile_kernel<TILE_GATEUP, false, false>), grid, block, 0, s, a);
     } else {
         if (a.fp4)
-            hipLaunchKernelGGL((gemm_tile_kernel<TILE_DOWN, true, true>), grid, block, 0, s, a);
+            hipLaunchKernelGGL((gemm_down_stream_kernel<true, true>), grid, block, 0, s, a);
         else if (a.packed)
-            hipLaunchKernelGGL((gemm_tile_kernel<TILE_DOWN, true, false>), grid, block, 0, s, a);
+            hipLaunchKernelGGL((gemm_down_stream_kernel<true, false>), grid, block, 0, s, a);
         else
-            hipLaunchKernelGGL((gemm_tile_kernel<TILE_DOWN, false, false>), grid, block, 0, s, a);
+            hipLaunchKernelGGL((gemm_down_stream_kernel<false, false>), grid, block, 0, s, a);
     }
     return hipGetLastError();
 }
