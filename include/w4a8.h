@@ -376,7 +376,14 @@ int w4a8_fused_moe_prepacked_noalloc(const void* hidden_bf16, int64_t T, int64_t
  *               decoded codes} ([T*topk, I/g] under w4a8_fused_moe_recipe with
  *               a group g of 64 or 32; the region has room for I/32)
  *   offsets[11] down output fp32 [T*topk, H] (pair rows in permuted order)
- * n must be 12; *block_m receives the m-block height the call uses.
+ *   offsets[12..14] (n = 15) the second m-block list: block_expert2,
+ *               block_row2 int32 [nb2], num_blocks2 int32 [1]; 0 when the
+ *               call keeps one list
+ * n must be 12 or 15; *block_m receives the height of the m-blocks in the
+ * first list.  Calls whose pairs per local expert (T*topk/E_l, every pair
+ * counted as local) lie between 16 and 256 choose the height per expert on
+ * the device: experts with at most 16 local pairs get 16-row blocks in the
+ * first list, the others 32-row blocks in the second.
  */
 int w4a8_fused_moe_workspace_layout(int64_t T, int64_t H, int64_t topk,
                                     int64_t num_local_experts, int64_t I,

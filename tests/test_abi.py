@@ -268,24 +268,31 @@ def test_fused_moe_recipe_rejects_bad_arguments(L):
     assert f(group=32, nbytes=ctypes.c_size_t(16)) == WORKSPACE
 
 
-@pytest.mark.parametrize("T,topk,E,want", [
-    (64, 8, 32, 16),      # decode share: 16 pairs per local expert if all were local
-    (1, 8, 256, 16),
-    (128, 8, 32, 32),
-    (256, 8, 32, 64),
-    (1023, 8, 32, 64),    # 8184 pairs: one short of 256 per expert
-    (1024, 8, 32, 160),   # 8192 pairs: the block-tiled kernel's 160-row m-blocks
-    (4096, 8, 32, 160),
+@pytest.mark.parametrize("T,topk,E,want,two", [
+    (64, 8, 32, 16, False),     # decode share: 16 pairs per local expert if all were local
+    (1, 8, 256, 16, False),
+    (128, 8, 32, 16, True),     # 32: per-expert 16 / 32-row blocks, chosen on the device
+    (256, 8, 32, 16, True),
+    (1023, 8, 32, 16, True),    # 8184 pairs: one short of 256 per expert
+    (1024, 8, 32, 160, False),  # 8192 pairs: the block-tiled kernel's 160-row m-blocks
+    (4096, 8, 32, 160, False),
 ])
-def test_block_height_rule(L, T, topk, E, want):
-    """The m-block height the fused call picks from the pairs per local expert
-    (host-side, from the shapes alone), and a layout consistent with it."""
+def test_block_height_rule(L, T, topk, E, want, two):
+    """The m-block height(s) the fused call picks from the pairs per local
+    expert (host-side, from the shapes alone), and a layout consistent with
+    it: the first list's blocks of `want` rows, and with two lists a second
+    list of 32-row blocks behind the other buffers."""
     lay = w4.fused_moe_workspace_layout(T, 7168, topk, E, 2048)
     assert lay["block_m"] == want
+    assert lay["two_lists"] == two
     F = T * topk
-    keys = list(w4.LAYOUT_KEYS)
+    keys = list(w4.LAYOUT_KEYS) if two else list(w4.LAYOUT_KEYS)[:12]
     offs = [lay[k] for k in keys]
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
     # block lists hold at most ceil(F / block_m) + E entries
     nb_max = (F + want - 1) // want + E
     assert lay["block_row"] - lay["block_expert"] >= 4 * nb_max
+    if two:
+        assert lay["block_row2"] - lay["block_expert2"] >= 4 * ((F + 31) // 32 + E)
+    else:
+        assert lay["block_expert2"] == lay["block_row2"] == lay["num_blocks2"] == 0

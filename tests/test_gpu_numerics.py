@@ -18,8 +18,6 @@ against the CPU oracle, at the same bars as test_gpu_parity.py).
 * The block-tiled down GEMM with several tiles per workgroup (its stage ring
   runs across tile boundaries).
 """
-import concurrent.futures
-
 import numpy as np
 import pytest
 import torch
@@ -28,33 +26,15 @@ import oracle
 from w4a8_moe_grouped_amd import lib as w4
 from w4a8_moe_grouped_amd import synth
 
-from test_gpu_parity import assert_bf16_close, bf16_dev, bf16_host, dput
+from test_gpu_parity import assert_bf16_close, bf16_dev, bf16_host, dput, oracle_rows_parallel
 
 pytestmark = pytest.mark.gpu
-
-ORACLE_THREADS = 16  # the host's share of the box
-
 
 @pytest.fixture(scope="module")
 def dev():
     assert torch.cuda.is_available(), "the gpu tests need an MI355X"
     w4.load()
     return torch.device("cuda:0")
-
-
-def oracle_rows_parallel(d, cfg, rows, fn=None, threads=ORACLE_THREADS):
-    """The oracle on the given tokens, split over threads (every output row
-    depends only on its own token, so the slices' rows equal one call's)."""
-    fn = fn or oracle.fused_moe
-    rows = np.asarray(rows)
-    parts = [p for p in np.array_split(rows, min(threads, rows.size)) if p.size]
-
-    def run(r):
-        return fn(d["hidden"][r], d["topk_ids"][r], d["topk_weights"][r], cfg.expert_begin,
-                  cfg.E_local, d["w13"], d["s13"], d["w2"], d["s2"])
-    with concurrent.futures.ThreadPoolExecutor(len(parts)) as ex:
-        outs = list(ex.map(run, parts))
-    return np.concatenate(outs, axis=0)
 
 
 def run_fused(d, cfg, dev, fp4=False):
@@ -168,7 +148,8 @@ def test_fused_zero_blocks(dev, path):
     x[2, ::2] = 0x8000  # -0 entries inside otherwise normal blocks
     d["hidden"] = x
     lay = w4.fused_moe_workspace_layout(cfg.T, cfg.H, cfg.topk, cfg.E_local, cfg.I)
-    assert lay["block_m"] == (160 if path == "tile" else 32)
+    assert lay["block_m"] == (160 if path == "tile" else 16)
+    assert lay["two_lists"] == (path == "skinny")
     got = run_fused(d, cfg, dev)
     ref = oracle_rows_parallel(d, cfg, np.arange(cfg.T))
     assert_bf16_close(got, ref, "zero blocks (%s)" % path)

@@ -233,6 +233,25 @@ def oracle_rows(d, cfg, rows):
                             cfg.expert_begin, cfg.E_local, d["w13"], d["s13"], d["w2"], d["s2"])
 
 
+ORACLE_THREADS = 16  # the host's share of the box
+
+
+def oracle_rows_parallel(d, cfg, rows, fn=None, threads=ORACLE_THREADS):
+    """The oracle on the given tokens, split over threads (every output row
+    depends only on its own token, so the slices' rows equal one call's)."""
+    import concurrent.futures
+    fn = fn or oracle.fused_moe
+    rows = np.asarray(rows)
+    parts = [p for p in np.array_split(rows, min(threads, rows.size)) if p.size]
+
+    def run(r):
+        return fn(d["hidden"][r], d["topk_ids"][r], d["topk_weights"][r], cfg.expert_begin,
+                  cfg.E_local, d["w13"], d["s13"], d["w2"], d["s2"])
+    with concurrent.futures.ThreadPoolExecutor(len(parts)) as ex:
+        outs = list(ex.map(run, parts))
+    return np.concatenate(outs, axis=0)
+
+
 @pytest.mark.parametrize("name", ["tiny", "decode"])
 def test_fused_moe_full(dev, name):
     cfg, d = moe_inputs(name)
@@ -257,18 +276,26 @@ def test_fused_moe_sampled_tokens(dev, name, nsample):
     assert np.all(got[none_local] == 0)
 
 
-# 32-row m-blocks at the model's dimensions (H=7168, I=2048: 56 and 16 K-groups),
-# the path whose activation rows go through LDS once per workgroup
-def test_fused_moe_32_row_blocks_full_dims(dev):
-    cfg, d = synth.random_moe(128, 7168, 2048, 256, 8, 0, 32, seed=71)
+# Per-expert block heights at the model's dimensions (H=7168, I=2048: 56 and
+# 16 K-groups): Zipf routing with rank = expert id puts 1..60 pairs on the
+# local experts, so both m-block lists (16 rows for experts with at most 16
+# pairs, 32 rows -- activation rows through LDS once per workgroup -- for the
+# others) hold blocks; one token of every local expert is compared.
+def test_fused_moe_two_block_lists_full_dims(dev):
+    cfg, d = synth.random_moe(128, 7168, 2048, 256, 8, 0, 32, seed=71, routing="zipf_id")
     lay = w4.fused_moe_workspace_layout(cfg.T, cfg.H, cfg.topk, cfg.E_local, cfg.I)
-    assert lay["block_m"] == 32, lay["block_m"]
+    assert lay["block_m"] == 16 and lay["two_lists"], lay
+    counts = np.bincount(d["topk_ids"].ravel(), minlength=cfg.E_total)[:cfg.E_local]
+    assert np.any((counts > 0) & (counts <= 16)) and np.any(counts > 16), counts
     got = run_fused(d, cfg, dev)
-    rng = np.random.default_rng(72)
-    rows = np.sort(rng.choice(cfg.T, size=16, replace=False))
-    rows[0], rows[-1] = 0, cfg.T - 1
-    ref = oracle_rows(d, cfg, rows)
-    assert_bf16_close(got[rows], ref, "T=128 32-row blocks (16 sampled tokens)")
+    rows = set()
+    for e in range(cfg.E_local):  # the first and the last token of every local expert
+        toks = np.nonzero(np.any(d["topk_ids"] == e, axis=1))[0]
+        if toks.size:
+            rows.update((int(toks[0]), int(toks[-1])))
+    rows = np.array(sorted(rows))
+    ref = oracle_rows_parallel(d, cfg, rows)
+    assert_bf16_close(got[rows], ref, "T=128 per-expert 16 / 32-row blocks (%d tokens)" % rows.size)
 
 
 @pytest.mark.parametrize("case", ["one_expert_many_rows", "single_token", "k1_e1",
@@ -352,11 +379,13 @@ def test_fused_moe_repeatable_and_workspace_reuse(dev):
 # expert, must be written by the call, and the summation counters of the
 # fused combine must be cleared by the call itself.  Two calls in a row on the
 # same buffers, the second with other routing and fewer tokens.
-@pytest.mark.parametrize("case", ["skinny16", "skinny32", "skinny64", "tile"])
+@pytest.mark.parametrize("case", ["skinny16", "lists_small", "lists_large", "tile"])
 def test_fused_moe_poisoned_buffers(dev, case):
+    # skinny16: one list of 16-row blocks; lists_small / lists_large: per-expert
+    # 16 / 32-row blocks with ~12 / ~40 pairs per local expert; tile: 160 rows
     shapes = {"skinny16": (64, 256, 128, 64, 8, 0, 32),
-              "skinny32": (96, 256, 128, 32, 4, 8, 16),
-              "skinny64": (160, 256, 128, 16, 4, 0, 8),
+              "lists_small": (96, 256, 128, 32, 4, 8, 16),
+              "lists_large": (160, 256, 128, 16, 4, 0, 8),
               "tile": (512, 256, 256, 8, 2, 0, 4)}[case]
     T, H, I, E, k, eb, El = shapes
     cfg1, d1 = synth.random_moe(T, H, I, E, k, eb, El, seed=61)
@@ -366,7 +395,8 @@ def test_fused_moe_poisoned_buffers(dev, case):
     ws = torch.full((need,), 0xFF, dtype=torch.uint8, device=dev)
     out = torch.full((T, H), -1, dtype=torch.int16, device=dev).view(torch.bfloat16)
     lay = w4.fused_moe_workspace_layout(T, H, k, El, I)
-    assert lay["block_m"] == {"skinny16": 16, "skinny32": 32, "skinny64": 64, "tile": 160}[case]
+    assert lay["block_m"] == {"skinny16": 16, "lists_small": 16, "lists_large": 16, "tile": 160}[case]
+    assert lay["two_lists"] == (case in ("lists_small", "lists_large"))
     w = [tuple(dput(d[n], dev) for n in ("w13", "s13", "w2", "s2")) for d in (d1, d2)]
     for cfg, d, wt in ((cfg1, d1, w[0]), (cfg2, d2, w[1])):
         o = out[:cfg.T]

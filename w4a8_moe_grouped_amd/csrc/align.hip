@@ -116,25 +116,34 @@ __device__ int block_exclusive_scan(int* vals, int n, int* scratch /* >= kAlignW
     return total;
 }
 
-// counts[] (LDS, E entries) -> offsets, counts and block list in global memory;
-// leaves the exclusive offsets in counts_lds.  All threads call it.
-__device__ void finish_scan(int* counts_lds, int* tmp_lds, int* scratch, int64_t E,
+// counts[] (LDS, E entries) -> offsets, counts and block list(s) in global
+// memory; leaves the exclusive offsets in counts_lds.  With two lists
+// (o.block_expert2 != null) an expert's blocks go to the first list (block_m
+// rows) when it has at most o.small_rows pairs, else to the second
+// (o.block_m2 rows).  All threads call it.
+__device__ void finish_scan(int* counts_lds, int* tmp_lds, int* tmp2_lds, int* scratch, int64_t E,
                             int64_t block_m, const AlignOut& o)
 {
     const int t = threadIdx.x;
+    const bool dual = o.block_expert2 != nullptr;
     for (int e = t; e < E; e += kAlignThreads) {
         const int c = counts_lds[e];
         o.counts[e] = c;
-        tmp_lds[e] = (int)((c + block_m - 1) / block_m);  // m-blocks of expert e
+        const bool second = dual && c > o.small_rows;
+        tmp_lds[e] = second ? 0 : (int)((c + block_m - 1) / block_m);  // m-blocks of expert e
+        tmp2_lds[e] = second ? (c + o.block_m2 - 1) / o.block_m2 : 0;
     }
     __syncthreads();
     const int P = block_exclusive_scan(counts_lds, (int)E, scratch);
     const int nb = block_exclusive_scan(tmp_lds, (int)E, scratch);
+    const int nb2 = dual ? block_exclusive_scan(tmp2_lds, (int)E, scratch) : 0;
     for (int e = t; e < E; e += kAlignThreads)
         o.offsets[e] = counts_lds[e];
     if (t == 0) {
         o.offsets[E] = P;
         *o.num_blocks = nb;
+        if (dual)
+            *o.num_blocks2 = nb2;
         if (o.block_start != nullptr)
             o.block_start[E] = nb;
     }
@@ -148,6 +157,14 @@ __device__ void finish_scan(int* counts_lds, int* tmp_lds, int* scratch, int64_t
             for (int b = first; b < last; ++b) {
                 o.block_expert[b] = e;
                 o.block_row[b] = counts_lds[e] + (int)((b - first) * block_m);
+            }
+            if (dual) {
+                const int first2 = tmp2_lds[e];
+                const int last2 = (e + 1 < E) ? tmp2_lds[e + 1] : nb2;
+                for (int b = first2; b < last2; ++b) {
+                    o.block_expert2[b] = e;
+                    o.block_row2[b] = counts_lds[e] + (b - first2) * o.block_m2;
+                }
             }
         }
     }
@@ -208,6 +225,7 @@ __device__ void scatter_chunk(const int (&keys)[R], int64_t f0, int64_t f1, int6
 struct AlignLds {
     int a[kMaxLocalExperts];
     int b[kMaxLocalExperts];
+    int c[kMaxLocalExperts];
     int wcnt[kAlignWaves * kMaxLocalExperts];
     int scratch[kAlignWaves + 1];
 };
@@ -240,7 +258,7 @@ __device__ __forceinline__ void align_single_body(const int32_t* __restrict__ id
         if (keys[r] >= 0)
             atomicAdd(&L.a[keys[r]], 1);
     __syncthreads();
-    finish_scan(L.a, L.b, L.scratch, E, block_m, o);  // L.a now holds the offsets
+    finish_scan(L.a, L.b, L.c, L.scratch, E, block_m, o);  // L.a now holds the offsets
     scatter_chunk(keys, 0, F, E, L.a, L.wcnt, align_masks, o);
 }
 
@@ -337,7 +355,7 @@ __global__ __launch_bounds__(kAlignThreads) void align_scan_kernel(int32_t* __re
         L.a[e] = run;
     }
     __syncthreads();
-    finish_scan(L.a, L.b, L.scratch, E, block_m, o);  // L.a now holds the experts' offsets
+    finish_scan(L.a, L.b, L.c, L.scratch, E, block_m, o);  // L.a now holds the experts' offsets
     for (int i = t; i < ng * E; i += kAlignThreads) {
         const int g = i / (int)E, e = i - g * (int)E;
         const int64_t c0 = g * cpg, c1 = c0 + cpg < nchunks ? c0 + cpg : nchunks;

@@ -56,6 +56,24 @@ int64_t ceil_div(int64_t a, int64_t b)
     return (a + b - 1) / b;
 }
 
+// Between the decode regime (at most 16 pairs per expert: 16-row blocks) and
+// the block-tiled one, the block height is chosen per expert on the device,
+// from the counts: the align writes two m-block lists, blocks of 16 rows for
+// experts with at most 16 pairs and of 32 rows for the others, and the
+// skinny GEMM runs once over each.  The host's figure T*topk/E_l counts every
+// pair as local; on an expert-parallel share only E_l/E of them are (8x
+// fewer rows), and skewed routing puts 5 rows on one expert and 250 on the
+// next.  Measured per fused call against one height for all experts (32 of
+// 256 experts, top-8; 16 / 32 / 64-row blocks everywhere): 128 tokens 133 /
+// 152 / 202 us, 256 tokens 172 / 179 / 222, 512 tokens 202 / 193 / 244,
+// Zipf routing with rank = expert id 470 / 401 / 443.
+constexpr int kSmallExpertRows = 16;
+constexpr int kLargeBlockRows = 32;
+bool use_two_lists(int64_t pairs, int64_t experts)
+{
+    return pairs > 16 * experts;
+}
+
 // Many rows per expert: the block-tiled GEMM (160-row m-blocks, weights
 // reused across the rows of an m-block from LDS) beats streaming the weights
 // once per small m-block.  Decided from the pairs per expert if every pair
@@ -70,8 +88,9 @@ bool use_tile(int64_t pairs, int64_t experts)
 // per-pair buffer is sized for F = T*topk pairs.
 struct MoePlan {
     bool tile;
+    bool two_lists;  // per-expert 16 / 32-row blocks (see use_two_lists)
     int block_m;
-    int64_t F, nb_max;
+    int64_t F, nb_max, nb2_max;
     w4a8::AlignOut al;
     void* align_ws;
     uint8_t* qa;
@@ -89,8 +108,10 @@ size_t plan_moe(void* ws, int64_t T, int64_t H, int64_t topk, int64_t E, int64_t
     Carve c(ws);
     p.F = T * topk;
     p.tile = down_group == W4A8_GROUP && use_tile(p.F, E);
-    p.block_m = p.tile ? w4a8::kTileRows : pick_block_m(p.F, E);
+    p.two_lists = down_group == W4A8_GROUP && !p.tile && use_two_lists(p.F, E);
+    p.block_m = p.tile ? w4a8::kTileRows : p.two_lists ? kSmallExpertRows : pick_block_m(p.F, E);
     p.nb_max = ceil_div(p.F, p.block_m) + E;
+    p.nb2_max = p.two_lists ? ceil_div(p.F, kLargeBlockRows) + E : 0;
     p.al.counts = c.take<int32_t>(E);
     p.al.offsets = c.take<int32_t>(E + 1);
     p.al.sorted = c.take<int32_t>(p.F);
@@ -108,6 +129,11 @@ size_t plan_moe(void* ws, int64_t T, int64_t H, int64_t topk, int64_t E, int64_t
     p.y2 = c.take<float>(p.F * H);
     p.al.block_start = c.take<int32_t>(E + 1);
     p.block_start = p.al.block_start;
+    p.al.block_expert2 = p.two_lists ? c.take<int32_t>(p.nb2_max) : nullptr;
+    p.al.block_row2 = p.two_lists ? c.take<int32_t>(p.nb2_max) : nullptr;
+    p.al.num_blocks2 = p.two_lists ? c.take<int32_t>(1) : nullptr;
+    p.al.small_rows = kSmallExpertRows;
+    p.al.block_m2 = kLargeBlockRows;
     return c.used;
 }
 
@@ -301,6 +327,17 @@ namespace {
 // weight formats of the fused forward
 enum WeightFormat { kInt4 = 0, kInt4Packed = 1, kFp4Packed = 2 };
 
+// the same GEMM's arguments for the second m-block list (32-row blocks)
+w4a8::GemmArgs second_list(const w4a8::GemmArgs& g, const MoePlan& p)
+{
+    w4a8::GemmArgs g2 = g;
+    g2.block_expert = p.al.block_expert2;
+    g2.block_row = p.al.block_row2;
+    g2.num_blocks = p.al.num_blocks2;
+    g2.max_blocks = p.nb2_max;
+    return g2;
+}
+
 // ev: the stage events to record (null: none)
 int fused_moe_run(const void* hidden_bf16, int64_t T, int64_t H, const int32_t* topk_ids,
                   const float* topk_weights, int64_t topk, int64_t expert_begin,
@@ -329,7 +366,9 @@ int fused_moe_run(const void* hidden_bf16, int64_t T, int64_t H, const int32_t* 
     MoePlan p;
     const size_t need = plan_moe(nullptr, T, H, topk, E, I, p, down_group);
     if (!p.tile && (!skinny_k_ok(H, p.block_m) || !skinny_k_ok(I, p.block_m, down_group) ||
-                    p.nb_max > kMaxGridY))
+                    p.nb_max > kMaxGridY ||
+                    (p.two_lists && (!skinny_k_ok(H, kLargeBlockRows) || !skinny_k_ok(I, kLargeBlockRows) ||
+                                     p.nb_max + p.nb2_max > kMaxGridY))))
         return W4A8_ERR_UNSUPPORTED;
     const int ws_rc = check_workspace(workspace, workspace_bytes, need);
     if (ws_rc >= 0)
@@ -400,8 +439,9 @@ int fused_moe_run(const void* hidden_bf16, int64_t T, int64_t H, const int32_t* 
     g.out_side = p.qh_side;
     g.requant_scale = a2_scale;
     g.sub_group = down_group;
-    e = p.tile ? w4a8::launch_gemm_tile(g, w4a8::TILE_GATEUP, stream)
-               : w4a8::launch_gemm_skinny(g, w4a8::EPI_SWIGLU_Q, p.block_m, stream);
+    e = p.tile        ? w4a8::launch_gemm_tile(g, w4a8::TILE_GATEUP, stream)
+        : p.two_lists ? w4a8::launch_gemm_skinny_two_lists(g, second_list(g, p), w4a8::EPI_SWIGLU_Q, stream)
+                      : w4a8::launch_gemm_skinny(g, w4a8::EPI_SWIGLU_Q, p.block_m, stream);
     if (e != hipSuccess)
         return W4A8_ERR_HIP;
     mark(ev, 3, stream);
@@ -418,8 +458,9 @@ int fused_moe_run(const void* hidden_bf16, int64_t T, int64_t H, const int32_t* 
     g.K = I;
     g.N = H;
     g.out_f32 = p.y2;
-    e = p.tile ? w4a8::launch_gemm_tile(g, w4a8::TILE_DOWN, stream)
-               : w4a8::launch_gemm_skinny(g, w4a8::EPI_F32, p.block_m, stream);
+    e = p.tile        ? w4a8::launch_gemm_tile(g, w4a8::TILE_DOWN, stream)
+        : p.two_lists ? w4a8::launch_gemm_skinny_two_lists(g, second_list(g, p), w4a8::EPI_F32, stream)
+                      : w4a8::launch_gemm_skinny(g, w4a8::EPI_F32, p.block_m, stream);
     if (e != hipSuccess)
         return W4A8_ERR_HIP;
     mark(ev, 4, stream);
@@ -610,17 +651,18 @@ int w4a8_fused_moe_workspace_layout(int64_t T, int64_t H, int64_t topk,
                                     int64_t* block_m)
 {
     if (T < 0 || H <= 0 || I <= 0 || topk < 1 || num_local_experts < 1 || offsets == nullptr ||
-        n != 12 || block_m == nullptr)
+        (n != 12 && n != 15) || block_m == nullptr)
         return W4A8_ERR_INVALID_ARG;
     MoePlan p;
     // carve from a fake base so that pointers equal byte offsets (base != null)
     char* const base = (char*)(uintptr_t)4096;
     plan_moe(base, T, H, topk, num_local_experts, I, p);
-    const void* ptrs[12] = {p.al.counts, p.al.offsets, p.al.sorted, p.al.src2dst,
+    const void* ptrs[15] = {p.al.counts, p.al.offsets, p.al.sorted, p.al.src2dst,
                             p.al.block_expert, p.al.block_row, p.al.num_blocks, p.qa,
-                            p.qa_side, p.qh, p.qh_side, p.y2};
-    for (int i = 0; i < 12; ++i)
-        offsets[i] = (size_t)((const char*)ptrs[i] - base);
+                            p.qa_side, p.qh, p.qh_side, p.y2,
+                            p.al.block_expert2, p.al.block_row2, p.al.num_blocks2};
+    for (int i = 0; i < n; ++i)
+        offsets[i] = ptrs[i] != nullptr ? (size_t)((const char*)ptrs[i] - base) : 0;
     *block_m = p.block_m;
     return W4A8_OK;
 }

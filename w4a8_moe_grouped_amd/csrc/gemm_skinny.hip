@@ -32,6 +32,10 @@
 namespace w4a8 {
 
 constexpr int kWaves = 4;
+// 16-row m-blocks: ring depth, and weight fragments per wave of the down GEMM
+// (128 weight rows per workgroup: see launch_nt)
+constexpr int kDW16 = 4;
+constexpr int kDownNF16 = 2;
 
 
 // NF: weight fragments (16 rows) per wave.  FP4: prepacked fp4 e2m1 weights
@@ -43,8 +47,9 @@ constexpr int kWaves = 4;
 // per 64 or 32 K of the down GEMM's input instead of 128).  The SwiGLU
 // epilogue then emits SG-blocks, and the down GEMM splits each 128-K group into
 // 128/SG lane-masked MFMAs, each promoted with its own block scale.
+// One workgroup's work: m-block `by` of the block list, weight block `bx`.
 template <int NT, int EPI, int DW, bool F16, bool SW4, bool PK, bool FP4, int NF, int SG>
-__global__ __launch_bounds__(256, NT == 2 ? 2 : 1) void gemm_skinny_kernel(GemmArgs a)
+__device__ __forceinline__ void skinny_body(const GemmArgs& a, const int by, const int bx)
 {
     constexpr int kNF = NF;
     static_assert(SG == 128 || SG == 64 || SG == 32, "activation block of 128, 64 or 32 K");
@@ -66,14 +71,14 @@ __global__ __launch_bounds__(256, NT == 2 ? 2 : 1) void gemm_skinny_kernel(GemmA
 
     int e, row0, rows;
     if (a.offsets != nullptr) {
-        if ((int)blockIdx.y >= *a.num_blocks)
+        if (by >= *a.num_blocks)
             return;
-        e = a.block_expert[blockIdx.y];
-        row0 = a.block_row[blockIdx.y];
+        e = a.block_expert[by];
+        row0 = a.block_row[by];
         rows = min(BM, a.offsets[e + 1] - row0);
     } else {
         e = 0;
-        row0 = (int)blockIdx.y * BM;
+        row0 = by * BM;
         if (row0 >= a.dense_rows)
             return;
         rows = min(BM, a.dense_rows - row0);
@@ -90,9 +95,9 @@ __global__ __launch_bounds__(256, NT == 2 ? 2 : 1) void gemm_skinny_kernel(GemmA
     for (int f = 0; f < kNF; ++f) {
         int64_t n;
         if (EPI == EPI_SWIGLU_Q)
-            n = (f >= 2 ? a.I : 0) + (int64_t)blockIdx.x * kGroup + 32 * wave + 16 * (f & 1) + c16;
+            n = (f >= 2 ? a.I : 0) + (int64_t)bx * kGroup + 32 * wave + 16 * (f & 1) + c16;
         else
-            n = (int64_t)blockIdx.x * (64 * NF) + 16 * NF * wave + 16 * f + c16;
+            n = (int64_t)bx * (64 * NF) + 16 * NF * wave + 16 * f + c16;
         nvalid[f] = n < N;
         nrow[f] = nvalid[f] ? n : N - 1;
     }
@@ -687,7 +692,7 @@ __global__ __launch_bounds__(256, NT == 2 ? 2 : 1) void gemm_skinny_kernel(GemmA
             const int row = i >> 3, chunk = i & 7;
             if (row < rows) {
                 const int64_t p = row0 + row;
-                *(v4i*)(a.out_q + p * a.I + (int64_t)blockIdx.x * kGroup + chunk * 16) =
+                *(v4i*)(a.out_q + p * a.I + (int64_t)bx * kGroup + chunk * 16) =
                     *(const v4i*)(s_q + row * kGroup + chunk * 16);
             }
         }
@@ -696,24 +701,51 @@ __global__ __launch_bounds__(256, NT == 2 ? 2 : 1) void gemm_skinny_kernel(GemmA
             if (row < rows) {
                 const float sum = block_sum(ob, row);
                 const float sc = fixed ? *fixed : scale_of(clamp_amax(block_amax(ob, row)));
-                a.out_side[(int64_t)(row0 + row) * GI + (int64_t)blockIdx.x * OSPG + ob] =
+                a.out_side[(int64_t)(row0 + row) * GI + (int64_t)bx * OSPG + ob] =
                     make_float2(512.0f * sc, -8.0f * (sc * sum));
             }
         }
     }
 }
 
-template <int NT, int EPI, int DW, bool F16, bool SW4, bool PK, bool FP4, int NF = 4, int SG = 128>
-static hipError_t launch_one(const GemmArgs& a0, hipStream_t s)
+template <int NT, int EPI, int DW, bool F16, bool SW4, bool PK, bool FP4, int NF, int SG>
+__global__ __launch_bounds__(256, NT == 2 ? 2 : 1) void gemm_skinny_kernel(GemmArgs a)
 {
-    const int64_t G = a0.K / kGroup;
+    skinny_body<NT, EPI, DW, F16, SW4, PK, FP4, NF, SG>(a, (int)blockIdx.y, (int)blockIdx.x);
+}
+
+// Two m-block lists in one launch (per-expert block heights): grid.y rows
+// [0, nb2) run list a2's 32-row blocks, the rest list a1's 16-row blocks
+// (workgroups are dispatched in grid order, so the longer ones start first
+// and the short ones fill in around them); each list has its own
+// weight-block count along grid.x (gx1, gx2).  Two waves per SIMD, as each
+// instance alone.
+template <int EPI, bool F16, bool SW4, bool PK, bool FP4, int NF1, int NF2>
+__global__ __launch_bounds__(256, 2) void gemm_skinny_two_lists_kernel(GemmArgs a1, GemmArgs a2, int nb2,
+                                                                       int gx1, int gx2)
+{
+    const int by = (int)blockIdx.y, bx = (int)blockIdx.x;
+    if (by < nb2) {
+        if (bx < gx2)
+            skinny_body<2, EPI, 2, F16, false, PK, FP4, NF2, 128>(a2, by, bx);
+    } else if (bx < gx1) {
+        skinny_body<1, EPI, kDW16, F16, SW4, PK, FP4, NF1, 128>(a1, by - nb2, bx);
+    }
+}
+
+// Dynamic LDS of one workgroup (side data of the block's rows for every
+// group; for 16-row down blocks also the whole-K activation rows of up to
+// a.stage_rows rows, which this sets).
+template <int NT, int EPI, int DW, int SG>
+static size_t skinny_lds(GemmArgs& a)
+{
+    const int64_t G = a.K / kGroup;
     const size_t side = (size_t)G * (EPI == EPI_F32 ? 128 / SG : 1) * 16 * NT * sizeof(float2);
-    // 16-row blocks of the down and dense GEMMs: LDS for the whole-K
-    // activation rows of up to stage_rows rows (1 KB pieces, so K % 1024 ==
-    // 0), within a quarter of the CU's LDS (the down instance runs four
-    // workgroups per CU) less the side data, the shared-rows ring of the
-    // fallback loop (static LDS) and 4 KB of other static LDS
-    GemmArgs a = a0;
+    // 16-row blocks of the down GEMM: LDS for the whole-K activation rows of
+    // up to stage_rows rows (1 KB pieces, so K % 1024 == 0), within a quarter
+    // of the CU's LDS (the down instance runs four workgroups per CU) less
+    // the side data, the shared-rows ring of the fallback loop (static LDS)
+    // and 4 KB of other static LDS
     a.stage_rows = 0;
     if (NT == 1 && SG == 128 && EPI != EPI_SWIGLU_Q && a.K % 1024 == 0) {
         const int64_t ring = EPI == EPI_F32 ? (DW + 1) * 16 * kGroup : 0;
@@ -721,7 +753,14 @@ static hipError_t launch_one(const GemmArgs& a0, hipStream_t s)
         const int64_t r = share / (a.K + 16);
         a.stage_rows = (int32_t)(r < 16 ? (r > 0 ? r : 0) : 16);
     }
-    const size_t lds = side + (a.stage_rows > 0 ? 16 + (size_t)a.stage_rows * (size_t)(a.K + 16) : 0);
+    return side + (a.stage_rows > 0 ? 16 + (size_t)a.stage_rows * (size_t)(a.K + 16) : 0);
+}
+
+template <int NT, int EPI, int DW, bool F16, bool SW4, bool PK, bool FP4, int NF = 4, int SG = 128>
+static hipError_t launch_one(const GemmArgs& a0, hipStream_t s)
+{
+    GemmArgs a = a0;
+    const size_t lds = skinny_lds<NT, EPI, DW, SG>(a);
     dim3 grid;
     if (EPI == EPI_SWIGLU_Q)
         grid.x = (unsigned)(a.I / kGroup);
@@ -743,17 +782,11 @@ static hipError_t launch_one(const GemmArgs& a0, hipStream_t s)
 // groups and one scale load per group (the float4 scale blocks would not fit
 // the register budget); measured against one wave per SIMD with a ring of 3,
 // 128 tokens on 32 of 256 experts: 202 -> 181 us per fused call.
-#ifndef W4A8_DW16
-#define W4A8_DW16 4
-#endif
-#ifndef W4A8_DOWN_NF16
-#define W4A8_DOWN_NF16 2
-#endif
 template <int NT, int DW, bool PK, bool FP4, int SG>
 static hipError_t launch_nt(const GemmArgs& a, int epilogue, hipStream_t s)
 {
     const bool g4 = (a.K / kGroup) % 4 == 0;
-    constexpr int NFD = NT == 1 ? W4A8_DOWN_NF16 : 4;
+    constexpr int NFD = NT == 1 ? kDownNF16 : 4;
     switch (epilogue) {
     case EPI_F32:
         return g4 && NT != 2 ? launch_one<NT, EPI_F32, DW, false, 4 % DW == 0, PK, FP4, NFD, SG>(a, s)
@@ -789,10 +822,52 @@ static hipError_t launch_layout(const GemmArgs& a, int epilogue, hipStream_t s)
 hipError_t launch_gemm_skinny(const GemmArgs& a, int epilogue, int block_m, hipStream_t s)
 {
     if (block_m <= 16)
-        return launch_layout<1, W4A8_DW16>(a, epilogue, s);
+        return launch_layout<1, kDW16>(a, epilogue, s);
     if (block_m <= 32)
         return launch_layout<2, 2>(a, epilogue, s);
     return launch_layout<4, 2>(a, epilogue, s);
+}
+
+template <int EPI, bool PK, bool FP4, bool SW4>
+static hipError_t launch_two_lists_t(const GemmArgs& a10, const GemmArgs& a20, hipStream_t s)
+{
+    constexpr bool F16 = EPI == EPI_SWIGLU_Q;
+    constexpr int NF1 = EPI == EPI_F32 ? kDownNF16 : 4;
+    GemmArgs a1 = a10, a2 = a20;
+    const size_t l1 = skinny_lds<1, EPI, kDW16, 128>(a1);
+    const size_t l2 = skinny_lds<2, EPI, 2, 128>(a2);
+    const int gx1 = EPI == EPI_SWIGLU_Q ? (int)(a1.I / kGroup) : (int)((a1.N + 64 * NF1 - 1) / (64 * NF1));
+    const int gx2 = EPI == EPI_SWIGLU_Q ? (int)(a2.I / kGroup) : (int)((a2.N + 255) / 256);
+    const dim3 grid((unsigned)(gx1 > gx2 ? gx1 : gx2), (unsigned)(a1.max_blocks + a2.max_blocks));
+    if (grid.x == 0 || grid.y == 0)
+        return hipSuccess;
+    hipLaunchKernelGGL((gemm_skinny_two_lists_kernel<EPI, F16, SW4, PK, FP4, NF1, 4>), grid, dim3(256),
+                       l1 > l2 ? l1 : l2, s, a1, a2, (int)a2.max_blocks, gx1, gx2);
+    return hipGetLastError();
+}
+
+template <int EPI, bool PK, bool FP4>
+static hipError_t launch_two_lists_e(const GemmArgs& a1, const GemmArgs& a2, hipStream_t s)
+{
+    // float4 scale blocks for the 16-row instance when G % 4 == 0 (as launch_nt)
+    if ((a1.K / kGroup) % 4 == 0 && 4 % kDW16 == 0)
+        return launch_two_lists_t<EPI, PK, FP4, true>(a1, a2, s);
+    return launch_two_lists_t<EPI, PK, FP4, false>(a1, a2, s);
+}
+
+hipError_t launch_gemm_skinny_two_lists(const GemmArgs& a1, const GemmArgs& a2, int epilogue, hipStream_t s)
+{
+    if (a1.sub_group != 128 || a2.sub_group != 128 || (a1.fp4 && !a1.packed))
+        return hipErrorInvalidValue;
+    const bool f32 = epilogue == EPI_F32;
+    if (a1.fp4)
+        return f32 ? launch_two_lists_e<EPI_F32, true, true>(a1, a2, s)
+                   : launch_two_lists_e<EPI_SWIGLU_Q, true, true>(a1, a2, s);
+    if (a1.packed)
+        return f32 ? launch_two_lists_e<EPI_F32, true, false>(a1, a2, s)
+                   : launch_two_lists_e<EPI_SWIGLU_Q, true, false>(a1, a2, s);
+    return f32 ? launch_two_lists_e<EPI_F32, false, false>(a1, a2, s)
+               : launch_two_lists_e<EPI_SWIGLU_Q, false, false>(a1, a2, s);
 }
 
 } // namespace w4a8

@@ -28,6 +28,15 @@ struct AlignOut {
     int32_t* block_row;     // [nb_max] or null
     int32_t* num_blocks;    // [1]
     int32_t* block_start;   // [E+1] index of each expert's first m-block, or null
+    // Two block lists (block_expert2 != null): experts with at most
+    // small_rows pairs get blocks of block_m rows in the first list, the
+    // others blocks of block_m2 rows in the second (per-expert block height
+    // from the device-side counts)
+    int32_t* block_expert2;  // [nb2_max] or null
+    int32_t* block_row2;     // [nb2_max]
+    int32_t* num_blocks2;    // [1]
+    int32_t small_rows;
+    int32_t block_m2;
 };
 int64_t align_chunk_count(int64_t F);
 size_t align_workspace_bytes(int64_t F, int64_t E);
@@ -87,6 +96,10 @@ struct GemmArgs {
 };
 enum Epilogue { EPI_F32 = 0, EPI_SWIGLU_Q = 2 };
 hipError_t launch_gemm_skinny(const GemmArgs& a, int epilogue, int block_m, hipStream_t s);
+// per-expert block heights: list a1 of 16-row blocks and list a2 of 32-row
+// blocks (same operands otherwise) in one launch
+hipError_t launch_gemm_skinny_two_lists(const GemmArgs& a1, const GemmArgs& a2, int epilogue,
+                                        hipStream_t s);
 
 // ---- dense linear (dense.hip) ----
 // canonical codes [M, K] + scales [M, K/128] x packed int4 [N, K/2] + scales

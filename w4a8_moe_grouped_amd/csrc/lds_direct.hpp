@@ -29,17 +29,25 @@ __device__ __forceinline__ v4i sgpr_rsrc(const void* base, uint32_t bytes)
 // as reserved and ignores the clobber; it sets M0 itself right before any
 // instruction of its own that reads it, and in these kernels M0 appears only
 // in these sequences, so no value of the compiler's is live across them.
+// The scalar offset is wave-uniform by contract; it is made an SGPR value
+// (readfirstlane: the compiler may hold a uniform value in a VGPR) and copied
+// inside the block (a value it folds to a constant would otherwise be printed
+// as a literal, which the soffset field does not take).
 __device__ __forceinline__ void lds_load16(const v4i& r, uint32_t lds, uint32_t voff, uint32_t soff)
 {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                 :
+    uint32_t so;
+    soff = __builtin_amdgcn_readfirstlane(soff);
+    asm volatile("s_mov_b32 m0, %1\n\ts_mov_b32 %0, %4\n\ts_nop 0\n\tbuffer_load_dwordx4 %2, %3, %0 offen lds"
+                 : "=&s"(so)
                  : "s"(lds), "v"(voff), "s"(r), "s"(soff)
                  : "memory", "m0");
 }
 __device__ __forceinline__ void lds_load4(const v4i& r, uint32_t lds, uint32_t voff, uint32_t soff)
 {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
-                 :
+    uint32_t so;
+    soff = __builtin_amdgcn_readfirstlane(soff);
+    asm volatile("s_mov_b32 m0, %1\n\ts_mov_b32 %0, %4\n\ts_nop 0\n\tbuffer_load_dword %2, %3, %0 offen lds"
+                 : "=&s"(so)
                  : "s"(lds), "v"(voff), "s"(r), "s"(soff)
                  : "memory", "m0");
 }

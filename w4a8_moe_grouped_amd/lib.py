@@ -136,18 +136,20 @@ def fused_moe_workspace_bytes(T: int, H: int, topk: int, num_local_experts: int,
 
 
 LAYOUT_KEYS = ("counts", "offsets", "sorted_pair_ids", "src2dst", "block_expert", "block_row",
-               "num_blocks", "qa16", "qa_side", "qh", "qh_side", "y2")
+               "num_blocks", "qa16", "qa_side", "qh", "qh_side", "y2", "block_expert2", "block_row2",
+               "num_blocks2")
 
 
 def fused_moe_workspace_layout(T: int, H: int, topk: int, num_local_experts: int, I: int):
     """Byte offsets of the intermediates inside the fused forward's workspace."""
-    offs = (ctypes.c_size_t * 12)()
+    offs = (ctypes.c_size_t * 15)()
     bm = ctypes.c_int64(0)
-    _check(load().w4a8_fused_moe_workspace_layout(T, H, topk, num_local_experts, I, offs, 12,
+    _check(load().w4a8_fused_moe_workspace_layout(T, H, topk, num_local_experts, I, offs, 15,
                                                   ctypes.byref(bm)),
            "w4a8_fused_moe_workspace_layout")
     d = dict(zip(LAYOUT_KEYS, [int(o) for o in offs]))
     d["block_m"] = int(bm.value)
+    d["two_lists"] = d["num_blocks2"] != 0
     return d
 
 
