@@ -312,19 +312,11 @@ def copy_bandwidth(nbytes=1 << 30, reps=10):
     return 2 * nbytes / s / 1e9
 
 
-def extra_workloads(dev, steps):
-    """The skewed-routing MoE configs and the dense linear: µs and rates."""
+def dense_linear(dev, steps):
+    """The dense W4AFP8 linear (w4a8_gemm on w4a8_quantize_act's codes):
+    µs of the GEMM and of the quantisation, TFLOP/s and GB/s of the GEMM."""
     import torch
     from w4a8_moe_grouped_amd import lib, synth
-    res = {}
-    for name in ("skew_perm", "skew_id"):
-        q = Workload(name, nsets=2, dev=dev)
-        us = time_steps(q, steps, 5)
-        res[name] = {"workload": q.cfg.desc, "us": round(us, 2), "P": q.stats["P"], "A": q.stats["A"],
-                     "hbm_gbs": round(moe_bytes(q.cfg, q.stats) / (us * 1e-6) / 1e9, 1),
-                     "frac_hbm": round(moe_bytes(q.cfg, q.stats) / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
-        log("[bench] %s: %s" % (name, res[name]))
-        del q
     cfg = synth.CONFIGS["dense"]
     x, w, sw = synth.gen_dense(cfg)
     put = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
@@ -349,10 +341,27 @@ def extra_workloads(dev, steps):
     q_us = a.elapsed_time(b) * 1e3 / steps
     M, K, N = cfg.M, cfg.K, cfg.N
     byts = N * K // 2 + N * (K // 128) * 4 + M * K + M * (K // 128) * 4 + M * N * 2
-    res["dense"] = {"workload": cfg.desc, "gemm_us": round(g_us, 2), "quant_us": round(q_us, 2),
-                    "gemm_tflops": round(2.0 * M * N * K / (g_us * 1e-6) / 1e12, 2),
-                    "gemm_hbm_gbs": round(byts / (g_us * 1e-6) / 1e9, 1)}
-    log("[bench] dense: %s" % res["dense"])
+    res = {"workload": cfg.desc, "gemm_us": round(g_us, 2), "quant_us": round(q_us, 2),
+           "gemm_tflops": round(2.0 * M * N * K / (g_us * 1e-6) / 1e12, 2),
+           "gemm_hbm_gbs": round(byts / (g_us * 1e-6) / 1e9, 1)}
+    log("[bench] dense: %s" % res)
+    return res
+
+
+def extra_workloads(dev, steps):
+    """The skewed-routing MoE configs and the dense linear: µs and rates."""
+    import torch
+    from w4a8_moe_grouped_amd import lib, synth
+    res = {}
+    for name in ("skew_perm", "skew_id"):
+        q = Workload(name, nsets=2, dev=dev)
+        us = time_steps(q, steps, 5)
+        res[name] = {"workload": q.cfg.desc, "us": round(us, 2), "P": q.stats["P"], "A": q.stats["A"],
+                     "hbm_gbs": round(moe_bytes(q.cfg, q.stats) / (us * 1e-6) / 1e9, 1),
+                     "frac_hbm": round(moe_bytes(q.cfg, q.stats) / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        log("[bench] %s: %s" % (name, res[name]))
+        del q
+    res["dense"] = dense_linear(dev, steps)
     return res
 
 
@@ -420,6 +429,9 @@ def main():
     dev = torch.device("cuda:0")
     lib.load()
 
+    if args.only == "dense":  # the dense linear alone (for profiling it)
+        print(json.dumps({"dense": dense_linear(torch.device("cuda:0"), args.steps)}), flush=True)
+        return
     primary = args.only or "decode"
     packed = args.layout == "prepacked"
     wl = Workload(primary, nsets=2, dev=dev, prepack=packed)
