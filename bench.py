@@ -358,7 +358,8 @@ def extra_workloads(dev, steps):
         us = time_steps(q, steps, 5)
         res[name] = {"workload": q.cfg.desc, "us": round(us, 2), "P": q.stats["P"], "A": q.stats["A"],
                      "hbm_gbs": round(moe_bytes(q.cfg, q.stats) / (us * 1e-6) / 1e9, 1),
-                     "frac_hbm": round(moe_bytes(q.cfg, q.stats) / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+                     "frac_hbm": round(moe_bytes(q.cfg, q.stats) / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                     "stages_us": {k: round(v, 1) for k, v in stage_breakdown(q, 5).items()}}
         log("[bench] %s: %s" % (name, res[name]))
         del q
     res["dense"] = dense_linear(dev, steps)

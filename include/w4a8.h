@@ -53,8 +53,9 @@
  *  - Size limits (W4A8_ERR_UNSUPPORTED beyond them): the kernels address each
  *    operand through a buffer resource with 32-bit extent and offsets, so the
  *    byte size of every activation matrix a GEMM reads (M*K for w4a8_gemm;
- *    T*H and T*topk*I for the fused forward, every pair counted as local) and
- *    of one expert's weights (N*K/2; I*H for w13) must stay below 2^32.
+ *    T*H and T*topk*I for the fused forward, every pair counted as local,
+ *    or max_local_pairs*I under w4a8_fused_moe_bounded) and of one expert's
+ *    weights (N*K/2; I*H for w13) must stay below 2^32.
  */
 #ifndef W4A8_H
 #define W4A8_H
@@ -267,6 +268,7 @@ int w4a8_fused_moe_prepacked_static(const void* hidden_bf16, int64_t T, int64_t 
  * call runs on the few-rows-per-expert GEMM at every size, and the side data
  * at offsets[10] is [T*topk, I/down_act_group].
  */
+#define W4A8_WEIGHTS_INT4 0 /* canonical int4 layout, as w4a8_fused_moe reads it */
 #define W4A8_WEIGHTS_INT4_PACKED 1
 #define W4A8_WEIGHTS_FP4_PACKED 2
 int w4a8_fused_moe_recipe(const void* hidden_bf16, int64_t T, int64_t H, const int32_t* topk_ids,
@@ -325,6 +327,41 @@ int w4a8_fused_moe_fp4_prepacked(const void* hidden_bf16, int64_t T, int64_t H,
                                  const uint8_t* w2_packed, const uint32_t* w2_scales_packed,
                                  void* out_bf16, void* workspace, size_t* workspace_bytes,
                                  hipStream_t stream);
+
+/*
+ * w4a8_fused_moe_bounded -- the fused forward with its per-pair buffers sized
+ * for a caller's bound on the LOCAL pairs instead of T*topk.  On an
+ * expert-parallel rank only the top-k slots that name one of its E_l experts
+ * are computed (SGLang PR #7762, review thread on expert_map), about E_l/E of
+ * them; a workspace sized for every slot (the other exports: at T = 32768,
+ * topk = 8, H = 7168, I = 2048 about 8.4 GB, 7.5 GB of it the fp32 down
+ * output) then holds mostly unused rows.  The caller, who knows its share
+ * from the dispatch, passes a bound; the workspace query scales with it.
+ *   weight_format    W4A8_WEIGHTS_INT4 (canonical, as w4a8_fused_moe),
+ *                    W4A8_WEIGHTS_INT4_PACKED (as w4a8_fused_moe_prepacked) or
+ *                    W4A8_WEIGHTS_FP4_PACKED (as w4a8_fused_moe_fp4_prepacked)
+ *   max_local_pairs  >= 1: the bound on the pairs whose expert is local
+ *                    (values above T*topk count as T*topk)
+ *   local_pairs      device int32, written on the stream with the number of
+ *                    local pairs the call found (required unless T == 0 or
+ *                    workspace == NULL; 4-byte aligned)
+ * Within the bound the output equals that of the export of the same weight
+ * format (bit for bit when both take the same kernels: the path and the
+ * m-block heights are chosen from min(max_local_pairs, T*topk) per local
+ * expert instead of T*topk per local expert).  Beyond it nothing is computed
+ * out of bounds: every output row is +0 and *local_pairs tells the caller the
+ * count, so a caller that cannot guarantee its bound checks *local_pairs
+ * after the call.  The byte range max_local_pairs*I (not T*topk*I) must stay
+ * below 2^32.  Other arguments and errors as w4a8_fused_moe; INVALID_ARG for
+ * an unknown format, a bound below 1 or a missing local_pairs.  T == 0
+ * launches nothing and leaves *local_pairs untouched.
+ */
+int w4a8_fused_moe_bounded(const void* hidden_bf16, int64_t T, int64_t H, const int32_t* topk_ids,
+                           const float* topk_weights, int64_t topk, int64_t expert_begin,
+                           int64_t num_local_experts, int64_t I, int weight_format,
+                           const uint8_t* w13, const void* w13_scales, const uint8_t* w2,
+                           const void* w2_scales, int64_t max_local_pairs, int32_t* local_pairs,
+                           void* out_bf16, void* workspace, size_t* workspace_bytes, hipStream_t stream);
 
 /*
  * w4a8_fused_moe_prepacked_noalloc -- w4a8_fused_moe_prepacked for callers

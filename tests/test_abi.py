@@ -296,3 +296,50 @@ def test_block_height_rule(L, T, topk, E, want, two):
         assert lay["block_row2"] - lay["block_expert2"] >= 4 * ((F + 31) // 32 + E)
     else:
         assert lay["block_expert2"] == lay["block_row2"] == lay["num_blocks2"] == 0
+
+
+def _bounded(L, T=4, H=256, k=2, E=4, I=128, fmt=1, bound=8, pairs=BOGUS, ws=BOGUS, nbytes=None):
+    n = ctypes.c_size_t(1 << 62) if nbytes is None else nbytes
+    return L.w4a8_fused_moe_bounded(BOGUS, T, H, BOGUS, BOGUS, k, 0, E, I, fmt, BOGUS, BOGUS, BOGUS,
+                                    BOGUS, bound, pairs, BOGUS, ws, ctypes.byref(n), None)
+
+
+def test_fused_moe_bounded_rejects_bad_arguments(L):
+    assert _bounded(L, fmt=3) == INVALID
+    assert _bounded(L, fmt=-1) == INVALID
+    assert _bounded(L, bound=0) == INVALID
+    assert _bounded(L, pairs=None) == INVALID          # the pair count has nowhere to go
+    assert _bounded(L, pairs=ctypes.c_void_p(0x1002)) == UNSUPPORTED  # int32 needs 4-byte alignment
+    assert _bounded(L, nbytes=ctypes.c_size_t(16)) == WORKSPACE
+    # the query needs no pair-count pointer
+    n = ctypes.c_size_t(0)
+    assert _bounded(L, pairs=None, ws=None, nbytes=n) == OK and n.value > 0
+
+
+def test_fused_moe_bounded_workspace_scales_with_the_bound(L):
+    """The per-pair buffers follow the bound: the EP8 share of a 32768-token
+    prefill (32 of 256 experts, top-8: ~33000 local pairs of 262144) needs
+    about an eighth of the unbounded workspace; a bound at or above T*topk
+    sizes it like the unbounded call."""
+    T, H, k, E, I = 32768, 7168, 8, 32, 2048
+    full = w4.fused_moe_workspace_bytes(T, H, k, E, I)
+    assert full > 8.4e9  # 8.4 GB, 7.5 GB of it the fp32 down output
+    b = w4.fused_moe_bounded_workspace_bytes(T, H, k, E, I, 40000)
+    assert b < full / 5
+    # the fp32 down output dominates: about bound * H * 4 bytes plus T*H fp8 codes
+    assert 40000 * H * 4 < b < 40000 * (H * 4 + I * 2) + T * (H + 8 * H // 128) + (64 << 20)
+    for fmt in (0, 1, 2):
+        assert w4.fused_moe_bounded_workspace_bytes(T, H, k, E, I, T * k, fmt) == full
+        assert w4.fused_moe_bounded_workspace_bytes(T, H, k, E, I, 1 << 40, fmt) == full
+    small = w4.fused_moe_bounded_workspace_bytes(64, H, k, E, I, 64)
+    assert small < w4.fused_moe_workspace_bytes(64, H, k, E, I)
+
+
+def test_fused_moe_bounded_range_check_uses_the_bound(L):
+    """The down GEMM's activation rows are bound*I bytes: T*topk*I >= 2^32 is
+    accepted under a bound that keeps it below, rejected under one that does
+    not (validation returns before any launch: the query path)."""
+    n = ctypes.c_size_t(0)
+    assert _bounded(L, T=262144, H=128, k=8, E=32, I=2048, bound=100000, ws=None, nbytes=n) == OK
+    assert _bounded(L, T=262144, H=128, k=8, E=32, I=2048, bound=1 << 21, ws=None,
+                    nbytes=ctypes.c_size_t(0)) == UNSUPPORTED

@@ -120,8 +120,11 @@ __device__ int block_exclusive_scan(int* vals, int n, int* scratch /* >= kAlignW
 // memory; leaves the exclusive offsets in counts_lds.  With two lists
 // (o.block_expert2 != null) an expert's blocks go to the first list (block_m
 // rows) when it has at most o.small_rows pairs, else to the second
-// (o.block_m2 rows).  All threads call it.
-__device__ void finish_scan(int* counts_lds, int* tmp_lds, int* tmp2_lds, int* scratch, int64_t E,
+// (o.block_m2 rows).  Returns true (in every thread) when the local pairs
+// exceed o.max_pairs: then the offsets, block counts and block_start are
+// zero, no block is listed, and the caller must scatter no pair.  All
+// threads call it.
+__device__ bool finish_scan(int* counts_lds, int* tmp_lds, int* tmp2_lds, int* scratch, int64_t E,
                             int64_t block_m, const AlignOut& o)
 {
     const int t = threadIdx.x;
@@ -137,20 +140,23 @@ __device__ void finish_scan(int* counts_lds, int* tmp_lds, int* tmp2_lds, int* s
     const int P = block_exclusive_scan(counts_lds, (int)E, scratch);
     const int nb = block_exclusive_scan(tmp_lds, (int)E, scratch);
     const int nb2 = dual ? block_exclusive_scan(tmp2_lds, (int)E, scratch) : 0;
+    const bool over = o.max_pairs > 0 && P > o.max_pairs;  // P is the same in every thread
     for (int e = t; e < E; e += kAlignThreads)
-        o.offsets[e] = counts_lds[e];
+        o.offsets[e] = over ? 0 : counts_lds[e];
     if (t == 0) {
-        o.offsets[E] = P;
-        *o.num_blocks = nb;
+        o.offsets[E] = over ? 0 : P;
+        *o.num_blocks = over ? 0 : nb;
         if (dual)
-            *o.num_blocks2 = nb2;
+            *o.num_blocks2 = over ? 0 : nb2;
         if (o.block_start != nullptr)
-            o.block_start[E] = nb;
+            o.block_start[E] = over ? 0 : nb;
+        if (o.pairs_out != nullptr)
+            *o.pairs_out = P;
     }
     if (o.block_start != nullptr)
         for (int e = t; e < E; e += kAlignThreads)
-            o.block_start[e] = tmp_lds[e];
-    if (o.block_expert != nullptr) {
+            o.block_start[e] = over ? 0 : tmp_lds[e];
+    if (o.block_expert != nullptr && !over) {
         for (int e = t; e < E; e += kAlignThreads) {
             const int first = tmp_lds[e];
             const int last = (e + 1 < E) ? tmp_lds[e + 1] : nb;
@@ -169,6 +175,7 @@ __device__ void finish_scan(int* counts_lds, int* tmp_lds, int* tmp2_lds, int* s
         }
     }
     __syncthreads();
+    return over;
 }
 
 // the local ids of pairs f0 + r * kAlignThreads + t, r < R (-1 past f1),
@@ -258,7 +265,12 @@ __device__ __forceinline__ void align_single_body(const int32_t* __restrict__ id
         if (keys[r] >= 0)
             atomicAdd(&L.a[keys[r]], 1);
     __syncthreads();
-    finish_scan(L.a, L.b, L.c, L.scratch, E, block_m, o);  // L.a now holds the offsets
+    // L.a now holds the offsets
+    if (finish_scan(L.a, L.b, L.c, L.scratch, E, block_m, o)) {
+#pragma unroll
+        for (int r = 0; r < kSingleRounds; ++r)
+            keys[r] = -1;  // over capacity: no pair is placed, src2dst = -1
+    }
     scatter_chunk(keys, 0, F, E, L.a, L.wcnt, align_masks, o);
 }
 
@@ -388,6 +400,13 @@ __global__ __launch_bounds__(kAlignThreads) void align_scatter_kernel(const int3
     const int64_t f1 = f0 + kAlignChunk < F ? f0 + kAlignChunk : F;
     int keys[kChunkRounds];
     load_keys(ids, f0, f1, eb, E, keys);
+    // offsets[E] == 0: no local pair, or more than the buffers hold (the scan
+    // then zeroed the offsets); either way no pair is placed
+    if (o.offsets[E] == 0) {
+#pragma unroll
+        for (int r = 0; r < kChunkRounds; ++r)
+            keys[r] = -1;
+    }
     for (int e = t; e < E; e += kAlignThreads)
         base[e] = hist[(int64_t)blockIdx.x * E + e];
     for (int i = t; i < kAlignWaves * E; i += kAlignThreads) {

@@ -84,13 +84,26 @@ bool use_tile(int64_t pairs, int64_t experts)
     return pairs >= kTilePairsPerExpert * experts;
 }
 
+// With a caller's bound on the local pairs (w4a8_fused_moe_bounded) the
+// host's estimate is close to the real count rather than 8x above it (on an
+// expert-parallel share of 32 of 256 experts the rules above see T*topk/E_l
+// where the experts get about T*topk/256), so the path is chosen from real
+// rows per local expert.  Measured per call with the bound = pairs + 8 (32
+// of 256 experts, top-8, H = 7168, I = 2048; two-list skinny vs block-tiled):
+// ~16 rows per expert 192 vs 330 us, ~32 rows 296 vs 336, ~64 rows 454 vs
+// 406; Zipf routing with rank = expert id (61 rows per expert on average,
+// 5 to 252) 381 vs 632.
+constexpr int64_t kBoundedTileRows = 64;     // block-tiled from this many rows per expert
+constexpr int64_t kBoundedTwoListRows = 2;   // per-expert 16 / 32-row blocks above this
+
 // The fused forward's workspace.  P is unknown on the host, so every
-// per-pair buffer is sized for F = T*topk pairs.
+// per-pair buffer is sized for `cap` pairs: F = T*topk, or the caller's bound
+// on the local pairs (w4a8_fused_moe_bounded), which the align enforces.
 struct MoePlan {
     bool tile;
     bool two_lists;  // per-expert 16 / 32-row blocks (see use_two_lists)
     int block_m;
-    int64_t F, nb_max, nb2_max;
+    int64_t F, cap, nb_max, nb2_max;
     w4a8::AlignOut al;
     void* align_ws;
     uint8_t* qa;
@@ -101,20 +114,28 @@ struct MoePlan {
     int32_t* block_start;
 };
 
-// down_group < 128 (the finer activation recipes) runs on the skinny kernel
+// down_group < 128 (the finer activation recipes) runs on the skinny kernel.
+// max_pairs: the caller's bound on the local pairs (0: none).  The path and
+// block heights are chosen from the bounded count, the closer estimate.
 size_t plan_moe(void* ws, int64_t T, int64_t H, int64_t topk, int64_t E, int64_t I, MoePlan& p,
-                int down_group = W4A8_GROUP)
+                int down_group = W4A8_GROUP, int64_t max_pairs = 0)
 {
     Carve c(ws);
     p.F = T * topk;
-    p.tile = down_group == W4A8_GROUP && use_tile(p.F, E);
-    p.two_lists = down_group == W4A8_GROUP && !p.tile && use_two_lists(p.F, E);
-    p.block_m = p.tile ? w4a8::kTileRows : p.two_lists ? kSmallExpertRows : pick_block_m(p.F, E);
-    p.nb_max = ceil_div(p.F, p.block_m) + E;
-    p.nb2_max = p.two_lists ? ceil_div(p.F, kLargeBlockRows) + E : 0;
+    p.cap = max_pairs > 0 && max_pairs < p.F ? max_pairs : p.F;
+    const bool bounded = p.cap < p.F;
+    p.tile = down_group == W4A8_GROUP &&
+             (bounded ? p.cap >= kBoundedTileRows * E : use_tile(p.F, E));
+    p.two_lists = down_group == W4A8_GROUP && !p.tile &&
+                  (bounded ? p.cap > kBoundedTwoListRows * E : use_two_lists(p.F, E));
+    p.block_m = p.tile ? w4a8::kTileRows : p.two_lists ? kSmallExpertRows : pick_block_m(p.cap, E);
+    p.nb_max = ceil_div(p.cap, p.block_m) + E;
+    p.nb2_max = p.two_lists ? ceil_div(p.cap, kLargeBlockRows) + E : 0;
+    p.al.max_pairs = p.cap < p.F ? (int32_t)p.cap : 0;
+    p.al.pairs_out = nullptr;
     p.al.counts = c.take<int32_t>(E);
     p.al.offsets = c.take<int32_t>(E + 1);
-    p.al.sorted = c.take<int32_t>(p.F);
+    p.al.sorted = c.take<int32_t>(p.cap);
     p.al.src2dst = c.take<int32_t>(p.F);
     p.al.block_expert = c.take<int32_t>(p.nb_max);
     p.al.block_row = c.take<int32_t>(p.nb_max);
@@ -122,11 +143,11 @@ size_t plan_moe(void* ws, int64_t T, int64_t H, int64_t topk, int64_t E, int64_t
     p.align_ws = c.take<char>(w4a8::align_workspace_bytes(p.F, E));
     p.qa = c.take<uint8_t>(T * H);  // fp8 gate_up operand
     p.qa_side = c.take<float2>(T * (H / W4A8_GROUP));
-    p.qh = c.take<uint8_t>(p.F * I);
+    p.qh = c.take<uint8_t>(p.cap * I);
     // side data of the requantised intermediate: room for the finest recipe
     // (one block per 32 K), whatever the call uses
-    p.qh_side = c.take<float2>(p.F * (I / 32));
-    p.y2 = c.take<float>(p.F * H);
+    p.qh_side = c.take<float2>(p.cap * (I / 32));
+    p.y2 = c.take<float>(p.cap * H);
     p.al.block_start = c.take<int32_t>(E + 1);
     p.block_start = p.al.block_start;
     p.al.block_expert2 = p.two_lists ? c.take<int32_t>(p.nb2_max) : nullptr;
@@ -338,14 +359,15 @@ w4a8::GemmArgs second_list(const w4a8::GemmArgs& g, const MoePlan& p)
     return g2;
 }
 
-// ev: the stage events to record (null: none)
+// ev: the stage events to record (null: none); max_pairs, pairs_out: the
+// bound on the local pairs and where their count goes (0 / null: none)
 int fused_moe_run(const void* hidden_bf16, int64_t T, int64_t H, const int32_t* topk_ids,
                   const float* topk_weights, int64_t topk, int64_t expert_begin,
                   int64_t num_local_experts, int64_t I, const uint8_t* w13_int4,
                   const void* w13_scales, const uint8_t* w2_int4, const void* w2_scales,
                   void* out_bf16, void* workspace, size_t* workspace_bytes, hipStream_t stream,
                   WeightFormat format, const float* a1_scale, const float* a2_scale, int down_group,
-                  void* const* ev)
+                  void* const* ev, int64_t max_pairs = 0, int32_t* pairs_out = nullptr)
 {
     const bool packed = format != kInt4;
     if (down_group != 128 && down_group != 64 && down_group != 32)
@@ -358,13 +380,12 @@ int fused_moe_run(const void* hidden_bf16, int64_t T, int64_t H, const int32_t* 
     if (H % W4A8_GROUP != 0 || I % W4A8_GROUP != 0 || topk > W4A8_MAX_TOPK ||
         E > kMaxLocalExperts || mul_sat(T, topk) > INT32_MAX / 2)
         return W4A8_ERR_UNSUPPORTED;
-    // 32-bit buffer ranges: the gate_up operand [T, H], the down operand
-    // [T*topk, I] (every pair may be local), one expert's w13 [2I, H/2]
-    if (!below_u32(mul_sat(T, H)) || !below_u32(mul_sat(mul_sat(T, topk), I)) ||
-        !below_u32(mul_sat(I, H)))
-        return W4A8_ERR_UNSUPPORTED;
     MoePlan p;
-    const size_t need = plan_moe(nullptr, T, H, topk, E, I, p, down_group);
+    const size_t need = plan_moe(nullptr, T, H, topk, E, I, p, down_group, max_pairs);
+    // 32-bit buffer ranges: the gate_up operand [T, H], the down operand
+    // [cap, I] (cap = T*topk unless bounded), one expert's w13 [2I, H/2]
+    if (!below_u32(mul_sat(T, H)) || !below_u32(mul_sat(p.cap, I)) || !below_u32(mul_sat(I, H)))
+        return W4A8_ERR_UNSUPPORTED;
     if (!p.tile && (!skinny_k_ok(H, p.block_m) || !skinny_k_ok(I, p.block_m, down_group) ||
                     p.nb_max > kMaxGridY ||
                     (p.two_lists && (!skinny_k_ok(H, kLargeBlockRows) || !skinny_k_ok(I, kLargeBlockRows) ||
@@ -383,7 +404,8 @@ int fused_moe_run(const void* hidden_bf16, int64_t T, int64_t H, const int32_t* 
         return W4A8_ERR_UNSUPPORTED;
     if (T == 0)
         return W4A8_OK;
-    plan_moe(workspace, T, H, topk, E, I, p, down_group);
+    plan_moe(workspace, T, H, topk, E, I, p, down_group, max_pairs);
+    p.al.pairs_out = pairs_out;
 
     mark(ev, 0, stream);
     hipError_t e;
@@ -447,7 +469,7 @@ int fused_moe_run(const void* hidden_bf16, int64_t T, int64_t H, const int32_t* 
     mark(ev, 3, stream);
     // down: rows in pair order, fp8 MFMA path
     g.act = p.qh;
-    g.act_rows = p.F;
+    g.act_rows = p.cap;
     g.f16 = 0;
     g.act_side = p.qh_side;
     g.sorted = nullptr;
@@ -486,12 +508,14 @@ int fused_moe_impl(const void* hidden_bf16, int64_t T, int64_t H, const int32_t*
                    const void* w13_scales, const uint8_t* w2_int4, const void* w2_scales,
                    void* out_bf16, void* workspace, size_t* workspace_bytes, hipStream_t stream,
                    WeightFormat format, const float* a1_scale = nullptr,
-                   const float* a2_scale = nullptr, int down_group = W4A8_GROUP)
+                   const float* a2_scale = nullptr, int down_group = W4A8_GROUP,
+                   int64_t max_pairs = 0, int32_t* pairs_out = nullptr)
 {
     void* const* ev = take_stage_events();
     return fused_moe_run(hidden_bf16, T, H, topk_ids, topk_weights, topk, expert_begin,
                          num_local_experts, I, w13_int4, w13_scales, w2_int4, w2_scales, out_bf16,
-                         workspace, workspace_bytes, stream, format, a1_scale, a2_scale, down_group, ev);
+                         workspace, workspace_bytes, stream, format, a1_scale, a2_scale, down_group, ev,
+                         max_pairs, pairs_out);
 }
 
 }  // namespace
@@ -530,8 +554,10 @@ int w4a8_fused_moe_prepacked_static(const void* hidden_bf16, int64_t T, int64_t 
                                     const float* a1_scale, const float* a2_scale, void* out_bf16,
                                     void* workspace, size_t* workspace_bytes, hipStream_t stream)
 {
-    if (((uintptr_t)a1_scale & 3u) != 0 || ((uintptr_t)a2_scale & 3u) != 0)
+    if (((uintptr_t)a1_scale & 3u) != 0 || ((uintptr_t)a2_scale & 3u) != 0) {
+        (void)take_stage_events();  // a rejected call disarms the stage events too
         return W4A8_ERR_UNSUPPORTED;
+    }
     return fused_moe_impl(hidden_bf16, T, H, topk_ids, topk_weights, topk, expert_begin,
                           num_local_experts, I, w13_packed, w13_scales_packed, w2_packed,
                           w2_scales_packed, out_bf16, workspace, workspace_bytes, stream, kInt4Packed,
@@ -545,8 +571,10 @@ int w4a8_fused_moe_recipe(const void* hidden_bf16, int64_t T, int64_t H, const i
                           const uint8_t* w2_packed, const void* w2_scales_packed, int down_act_group,
                           void* out_bf16, void* workspace, size_t* workspace_bytes, hipStream_t stream)
 {
-    if (weight_format != W4A8_WEIGHTS_INT4_PACKED && weight_format != W4A8_WEIGHTS_FP4_PACKED)
+    if (weight_format != W4A8_WEIGHTS_INT4_PACKED && weight_format != W4A8_WEIGHTS_FP4_PACKED) {
+        (void)take_stage_events();  // a rejected call disarms the stage events too
         return W4A8_ERR_INVALID_ARG;
+    }
     return fused_moe_impl(hidden_bf16, T, H, topk_ids, topk_weights, topk, expert_begin,
                           num_local_experts, I, w13_packed, w13_scales_packed, w2_packed,
                           w2_scales_packed, out_bf16, workspace, workspace_bytes, stream,
@@ -565,6 +593,30 @@ int w4a8_fused_moe_fp4_prepacked(const void* hidden_bf16, int64_t T, int64_t H,
     return fused_moe_impl(hidden_bf16, T, H, topk_ids, topk_weights, topk, expert_begin,
                           num_local_experts, I, w13_packed, w13_scales_packed, w2_packed,
                           w2_scales_packed, out_bf16, workspace, workspace_bytes, stream, kFp4Packed);
+}
+
+int w4a8_fused_moe_bounded(const void* hidden_bf16, int64_t T, int64_t H, const int32_t* topk_ids,
+                           const float* topk_weights, int64_t topk, int64_t expert_begin,
+                           int64_t num_local_experts, int64_t I, int weight_format,
+                           const uint8_t* w13, const void* w13_scales, const uint8_t* w2,
+                           const void* w2_scales, int64_t max_local_pairs, int32_t* local_pairs,
+                           void* out_bf16, void* workspace, size_t* workspace_bytes, hipStream_t stream)
+{
+    void* const* ev = take_stage_events();  // consumed by rejected calls too
+    if (weight_format != W4A8_WEIGHTS_INT4 && weight_format != W4A8_WEIGHTS_INT4_PACKED &&
+        weight_format != W4A8_WEIGHTS_FP4_PACKED)
+        return W4A8_ERR_INVALID_ARG;
+    if (max_local_pairs < 1 || (workspace != nullptr && T > 0 && local_pairs == nullptr))
+        return W4A8_ERR_INVALID_ARG;
+    if (((uintptr_t)local_pairs & 3u) != 0)
+        return W4A8_ERR_UNSUPPORTED;
+    const WeightFormat f = weight_format == W4A8_WEIGHTS_FP4_PACKED    ? kFp4Packed
+                           : weight_format == W4A8_WEIGHTS_INT4_PACKED ? kInt4Packed
+                                                                       : kInt4;
+    return fused_moe_run(hidden_bf16, T, H, topk_ids, topk_weights, topk, expert_begin,
+                         num_local_experts, I, w13, w13_scales, w2, w2_scales, out_bf16, workspace,
+                         workspace_bytes, stream, f, nullptr, nullptr, W4A8_GROUP, ev, max_local_pairs,
+                         local_pairs);
 }
 
 int w4a8_prepack_weights(const uint8_t* w_int4, const float* w_scales, int64_t E, int64_t N,

@@ -37,6 +37,12 @@ struct AlignOut {
     int32_t* num_blocks2;    // [1]
     int32_t small_rows;
     int32_t block_m2;
+    // Capacity of the per-pair buffers (sorted, the GEMMs' rows), <= 0 for
+    // none.  When the local pairs exceed it no expert is computed: offsets,
+    // block counts and block_start are written as zero and every src2dst
+    // entry as -1, so the GEMMs do nothing and the combine writes +0.
+    int32_t max_pairs;
+    int32_t* pairs_out;  // [1] receives the number of local pairs, or null
 };
 int64_t align_chunk_count(int64_t F);
 size_t align_workspace_bytes(int64_t F, int64_t E);
