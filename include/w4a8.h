@@ -342,13 +342,18 @@ int w4a8_fused_moe_fp4_prepacked(const void* hidden_bf16, int64_t T, int64_t H,
  *                    W4A8_WEIGHTS_FP4_PACKED (as w4a8_fused_moe_fp4_prepacked)
  *   max_local_pairs  >= 1: the bound on the pairs whose expert is local
  *                    (values above T*topk count as T*topk)
- *   local_pairs      device int32, written on the stream with the number of
- *                    local pairs the call found (required unless T == 0 or
- *                    workspace == NULL; 4-byte aligned)
+ *   local_pairs      device int32[2], written on the stream: [0] the number
+ *                    of local pairs the call found, [1] 1 if the block-tiled
+ *                    GEMM kernels ran, 0 if the few-rows ones did (required
+ *                    unless T == 0 or workspace == NULL; 8-byte aligned)
  * Within the bound the output equals that of the export of the same weight
- * format (bit for bit when both take the same kernels: the path and the
- * m-block heights are chosen from min(max_local_pairs, T*topk) per local
- * expert instead of T*topk per local expert).  Beyond it nothing is computed
+ * format (bit for bit when both take the same kernels).  The path follows
+ * min(max_local_pairs, T*topk) per local expert: at most 2 rows per expert
+ * the few-rows kernel with 16-row m-blocks; above that, while the few-rows
+ * kernel's m-block lists stay below 4096 blocks, the align chooses on the
+ * device between per-expert 16 / 32-row blocks and the block-tiled kernels
+ * from the real per-expert counts (a cost model fitted on MI355X); beyond,
+ * the block-tiled kernels.  Beyond the bound nothing is computed
  * out of bounds: every output row is +0 and *local_pairs tells the caller the
  * count, so a caller that cannot guarantee its bound checks *local_pairs
  * after the call.  The byte range max_local_pairs*I (not T*topk*I) must stay
@@ -416,11 +421,16 @@ int w4a8_fused_moe_prepacked_noalloc(const void* hidden_bf16, int64_t T, int64_t
  *   offsets[12..14] (n = 15) the second m-block list: block_expert2,
  *               block_row2 int32 [nb2], num_blocks2 int32 [1]; 0 when the
  *               call keeps one list
- * n must be 12 or 15; *block_m receives the height of the m-blocks in the
+ * n must be 12, 15 or 18; *block_m receives the height of the m-blocks in the
  * first list.  Calls whose pairs per local expert (T*topk/E_l, every pair
  * counted as local) lie between 16 and 256 choose the height per expert on
  * the device: experts with at most 16 local pairs get 16-row blocks in the
- * first list, the others 32-row blocks in the second.
+ * first list, the others 32-row blocks in the second; and, while those lists
+ * stay below 4096 blocks, the path too: with n = 18,
+ *   offsets[15..17] block_row3 int32 [nb3] (160-row blocks), num_blocks3
+ *               int32 [1], path int32 [1]: 1 if the call ran the block-tiled
+ *               kernels on the third list, 0 if the skinny kernel on the
+ *               first two; 0 when the call does not choose on the device
  */
 int w4a8_fused_moe_workspace_layout(int64_t T, int64_t H, int64_t topk,
                                     int64_t num_local_experts, int64_t I,

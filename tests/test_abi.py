@@ -285,6 +285,9 @@ def test_block_height_rule(L, T, topk, E, want, two):
     lay = w4.fused_moe_workspace_layout(T, 7168, topk, E, 2048)
     assert lay["block_m"] == want
     assert lay["two_lists"] == two
+    # between the two host rules the path is chosen on the device (a third,
+    # 160-row list and the path flag behind the others)
+    assert lay["device_path"] == two
     F = T * topk
     keys = list(w4.LAYOUT_KEYS) if two else list(w4.LAYOUT_KEYS)[:12]
     offs = [lay[k] for k in keys]
@@ -294,8 +297,10 @@ def test_block_height_rule(L, T, topk, E, want, two):
     assert lay["block_row"] - lay["block_expert"] >= 4 * nb_max
     if two:
         assert lay["block_row2"] - lay["block_expert2"] >= 4 * ((F + 31) // 32 + E)
+        assert lay["num_blocks3"] - lay["block_row3"] >= 4 * ((F + 159) // 160 + E)
     else:
         assert lay["block_expert2"] == lay["block_row2"] == lay["num_blocks2"] == 0
+        assert lay["block_row3"] == lay["num_blocks3"] == lay["path"] == 0
 
 
 def _bounded(L, T=4, H=256, k=2, E=4, I=128, fmt=1, bound=8, pairs=BOGUS, ws=BOGUS, nbytes=None):
@@ -309,7 +314,7 @@ def test_fused_moe_bounded_rejects_bad_arguments(L):
     assert _bounded(L, fmt=-1) == INVALID
     assert _bounded(L, bound=0) == INVALID
     assert _bounded(L, pairs=None) == INVALID          # the pair count has nowhere to go
-    assert _bounded(L, pairs=ctypes.c_void_p(0x1002)) == UNSUPPORTED  # int32 needs 4-byte alignment
+    assert _bounded(L, pairs=ctypes.c_void_p(0x1004)) == UNSUPPORTED  # int32[2] needs 8-byte alignment
     assert _bounded(L, nbytes=ctypes.c_size_t(16)) == WORKSPACE
     # the query needs no pair-count pointer
     n = ctypes.c_size_t(0)

@@ -5,8 +5,11 @@
   16-row m-blocks either way), the output is bit-identical to the unbounded
   export of the same weight format (canonical int4, prepacked int4, fp4), and
   the call reports the local pair count.
-* Where the bound changes the path (the per-expert estimate becomes the
-  bounded count), both paths are held to the oracle's bar.
+* Where the counts decide the path on the device (the align's cost model:
+  per-expert 16 / 32-row skinny blocks or the block-tiled kernels), the call
+  reports the path it took, the clear cases take the expected one, and both
+  are held to the oracle's bar; the unbounded export chooses the same way
+  between its two host rules (its path flag read from the workspace).
 * Beyond the bound nothing is computed: every output row is +0 (the output
   starts poisoned), the reported count is the real one, and the same
   workspace then serves a call within the bound (single-block align for few
@@ -67,7 +70,9 @@ def bounded(d, cfg, dev, fmt, ws, bound, out=None, workspace=None):
                                   dput(d["topk_weights"], dev), cfg.expert_begin, cfg.E_local, cfg.I,
                                   ws, fmt, bound, out=out, workspace=workspace)
     torch.cuda.synchronize()
-    return out, int(n.item())
+    n = n.cpu().numpy()
+    bounded.last_path = int(n[1])
+    return out, int(n[0])
 
 
 @pytest.mark.parametrize("fmt", [w4.WEIGHTS_INT4, w4.WEIGHTS_INT4_PACKED, w4.WEIGHTS_FP4_PACKED])
@@ -85,7 +90,7 @@ def test_bounded_equals_unbounded_decode(dev, fmt):
         assert torch.equal(got.view(torch.int16), ref.view(torch.int16)), bound
 
 
-# single-block align and 16-row blocks / chunked align and the block-tiled path
+# single-block align and 16-row blocks / chunked align and the path chosen on the device
 @pytest.mark.parametrize("T,seed", [(64, 102), (2048, 103)])
 def test_bounded_overflow_writes_zeros_then_recovers(dev, T, seed):
     cfg, d = synth.random_moe(T, 7168, 2048, 256, 8, 0, 32, seed=seed)
@@ -118,28 +123,68 @@ def test_bounded_overflow_writes_zeros_then_recovers(dev, T, seed):
     assert_bf16_close(bf16_host(out2)[rows], ref, "bounded after overflow (T=%d, P=%d)" % (t2, P2))
 
 
-@pytest.mark.parametrize("T,routing,slack", [
-    (512, "uniform", 1.05),   # ~16 local pairs per expert: per-expert 16 / 32-row blocks
-    (512, "uniform", 4.1),    # the same routing bounded loosely: the block-tiled path
-    (256, "zipf_id", 1.02),   # skewed: 1..250 pairs per expert
+def first_last_tokens(cfg, d):
+    rows = set()
+    for e in range(cfg.E_local):  # the first and the last token of every local expert
+        toks = np.nonzero(np.any(d["topk_ids"] == e + cfg.expert_begin, axis=1))[0]
+        if toks.size:
+            rows.update((int(toks[0]), int(toks[-1])))
+    return np.array(sorted(rows))
+
+
+@pytest.mark.parametrize("T,E_total,routing,slack,want", [
+    (512, 256, "uniform", 1.05, 0),   # ~16 pairs per expert: skinny 16 / 32-row blocks
+    (512, 256, "uniform", 4.1, 0),    # a loose bound: the counts still decide
+    (512, 32, "uniform", 1.02, 1),    # every expert local, ~128 pairs each: block-tiled
+    (256, 256, "zipf_id", 1.02, 0),   # skewed, 5..250 pairs per expert: skinny
 ])
-def test_bounded_paths_match_oracle(dev, T, routing, slack):
-    cfg, d = synth.random_moe(T, 7168, 2048, 256, 8, 0, 32, seed=104, routing=routing)
+def test_bounded_paths_match_oracle(dev, T, E_total, routing, slack, want):
+    cfg, d = synth.random_moe(T, 7168, 2048, E_total, 8, 0, 32, seed=104, routing=routing)
     P = local_pairs_of(cfg, d)
     bound = int(P * slack) + 1
-    print("bounded path: T=%d %s P=%d bound=%d" % (T, routing, P, bound), flush=True)
+    print("bounded path: T=%d E=%d %s P=%d bound=%d" % (T, E_total, routing, P, bound), flush=True)
     ws = weights(d, dev, w4.WEIGHTS_INT4_PACKED)
     got, n = bounded(d, cfg, dev, w4.WEIGHTS_INT4_PACKED, ws, bound)
     assert n == P
+    assert bounded.last_path == want
     got = bf16_host(got)
-    rows = set()
-    for e in range(cfg.E_local):  # the first and the last token of every local expert
-        toks = np.nonzero(np.any(d["topk_ids"] == e, axis=1))[0]
-        if toks.size:
-            rows.update((int(toks[0]), int(toks[-1])))
-    rows = np.array(sorted(rows))
+    rows = first_last_tokens(cfg, d)
     ref = oracle_rows_parallel(d, cfg, rows)
-    assert_bf16_close(got[rows], ref, "bounded T=%d %s bound=%d (%d tokens)" % (T, routing, bound, rows.size))
+    assert_bf16_close(got[rows], ref, "bounded T=%d %s bound=%d path %d (%d tokens)"
+                      % (T, routing, bound, want, rows.size))
     ids = d["topk_ids"]
     none_local = ~np.any((ids >= 0) & (ids < cfg.E_local), axis=1)
     assert np.all(got[none_local] == 0)
+
+
+@pytest.mark.parametrize("T,E_total,routing,want", [
+    (512, 32, "uniform", 1),    # T*topk/E_l = 128: between the host rules; ~128 real rows: tiled
+    (256, 256, "zipf_id", 0),   # T*topk/E_l = 64; 5..250 real rows: skinny
+])
+def test_unbounded_device_path_choice(dev, T, E_total, routing, want):
+    cfg, d = synth.random_moe(T, 7168, 2048, E_total, 8, 0, 32, seed=105, routing=routing)
+    lay = w4.fused_moe_workspace_layout(T, cfg.H, cfg.topk, cfg.E_local, cfg.I)
+    assert lay["device_path"] and lay["two_lists"]
+    ws = torch.zeros(w4.fused_moe_workspace_bytes(T, cfg.H, cfg.topk, cfg.E_local, cfg.I),
+                     dtype=torch.uint8, device=dev)
+    print("unbounded device path: T=%d E=%d %s" % (T, E_total, routing), flush=True)
+    packed = weights(d, dev, w4.WEIGHTS_INT4_PACKED)
+    out = unbounded_with_workspace(d, cfg, dev, packed, ws)
+    torch.cuda.synchronize()
+    path = int(ws[lay["path"]:lay["path"] + 4].view(torch.int32).item())
+    assert path == want
+    got = bf16_host(out)
+    rows = first_last_tokens(cfg, d)
+    ref = oracle_rows_parallel(d, cfg, rows)
+    assert_bf16_close(got[rows], ref, "unbounded T=%d %s device path %d (%d tokens)"
+                      % (T, routing, path, rows.size))
+
+
+def unbounded_with_workspace(d, cfg, dev, packed, ws):
+    shapes = (torch.empty((cfg.E_local, 2 * cfg.I, cfg.H // 2), dtype=torch.uint8, device=dev),
+              torch.empty((cfg.E_local, 2 * cfg.I, cfg.H // 128), dtype=torch.float32, device=dev),
+              torch.empty((cfg.E_local, cfg.H, cfg.I // 2), dtype=torch.uint8, device=dev),
+              torch.empty((cfg.E_local, cfg.H, cfg.I // 128), dtype=torch.float32, device=dev))
+    return w4.fused_moe(bf16_dev(d["hidden"], dev), dput(d["topk_ids"], dev),
+                        dput(d["topk_weights"], dev), cfg.expert_begin, cfg.E_local, *shapes,
+                        workspace=ws, prepacked=packed)

@@ -124,23 +124,41 @@ __device__ int block_exclusive_scan(int* vals, int n, int* scratch /* >= kAlignW
 // exceed o.max_pairs: then the offsets, block counts and block_start are
 // zero, no block is listed, and the caller must scatter no pair.  All
 // threads call it.
-__device__ bool finish_scan(int* counts_lds, int* tmp_lds, int* tmp2_lds, int* scratch, int64_t E,
-                            int64_t block_m, const AlignOut& o)
+// Predicted us of the two GEMMs on the block-tiled path minus the skinny
+// one (see PathCost): < 0 picks the block-tiled kernels.
+__device__ float tiled_minus_skinny(const PathCost& c, int P, int nb_skinny, int nb_tiled)
+{
+    const float rows = nb_tiled > 0 ? (float)P / (float)nb_tiled : 0.0f;
+    const float gu = ceilf(c.tiles_gu * (float)nb_tiled / c.cus) * c.groups_gu * (c.gu0 + c.gu1 * rows);
+    const float dn = c.tiles_dn * (float)nb_tiled / c.cus * c.groups_dn * (c.dn0 + c.dn1 * rows);
+    return gu + dn - (float)nb_skinny * c.skinny_block_us;
+}
+
+__device__ bool finish_scan(int* counts_lds, int* tmp_lds, int* tmp2_lds, int* tmp3_lds, int* scratch,
+                            int64_t E, int64_t block_m, const AlignOut& o)
 {
     const int t = threadIdx.x;
     const bool dual = o.block_expert2 != nullptr;
+    const bool choose = o.path != nullptr;  // also the kTileRows-row list
     for (int e = t; e < E; e += kAlignThreads) {
         const int c = counts_lds[e];
         o.counts[e] = c;
         const bool second = dual && c > o.small_rows;
         tmp_lds[e] = second ? 0 : (int)((c + block_m - 1) / block_m);  // m-blocks of expert e
         tmp2_lds[e] = second ? (c + o.block_m2 - 1) / o.block_m2 : 0;
+        tmp3_lds[e] = choose ? (c + kTileRows - 1) / kTileRows : 0;
     }
     __syncthreads();
     const int P = block_exclusive_scan(counts_lds, (int)E, scratch);
     const int nb = block_exclusive_scan(tmp_lds, (int)E, scratch);
     const int nb2 = dual ? block_exclusive_scan(tmp2_lds, (int)E, scratch) : 0;
+    const int nb3 = choose ? block_exclusive_scan(tmp3_lds, (int)E, scratch) : 0;
     const bool over = o.max_pairs > 0 && P > o.max_pairs;  // P is the same in every thread
+    const int path = !choose ? o.static_path
+                             : (!over && tiled_minus_skinny(o.cost, P, nb + nb2, nb3) < 0.0f ? 1 : 0);
+    // block_start belongs to the list the block-tiled kernels read
+    const int* bs_lds = choose ? tmp3_lds : tmp_lds;
+    const int nbs = choose ? nb3 : nb;
     for (int e = t; e < E; e += kAlignThreads)
         o.offsets[e] = over ? 0 : counts_lds[e];
     if (t == 0) {
@@ -148,14 +166,28 @@ __device__ bool finish_scan(int* counts_lds, int* tmp_lds, int* tmp2_lds, int* s
         *o.num_blocks = over ? 0 : nb;
         if (dual)
             *o.num_blocks2 = over ? 0 : nb2;
+        if (choose) {
+            *o.num_blocks3 = over ? 0 : nb3;
+            *o.path = path;
+        }
         if (o.block_start != nullptr)
-            o.block_start[E] = over ? 0 : nb;
-        if (o.pairs_out != nullptr)
-            *o.pairs_out = P;
+            o.block_start[E] = over ? 0 : nbs;
+        if (o.pairs_out != nullptr) {
+            o.pairs_out[0] = P;
+            o.pairs_out[1] = path;
+        }
     }
     if (o.block_start != nullptr)
         for (int e = t; e < E; e += kAlignThreads)
-            o.block_start[e] = over ? 0 : tmp_lds[e];
+            o.block_start[e] = over ? 0 : bs_lds[e];
+    if (choose && !over) {
+        for (int e = t; e < E; e += kAlignThreads) {
+            const int first = tmp3_lds[e];
+            const int last = (e + 1 < E) ? tmp3_lds[e + 1] : nb3;
+            for (int b = first; b < last; ++b)
+                o.block_row3[b] = counts_lds[e] + (b - first) * kTileRows;
+        }
+    }
     if (o.block_expert != nullptr && !over) {
         for (int e = t; e < E; e += kAlignThreads) {
             const int first = tmp_lds[e];
@@ -233,6 +265,7 @@ struct AlignLds {
     int a[kMaxLocalExperts];
     int b[kMaxLocalExperts];
     int c[kMaxLocalExperts];
+    int d[kMaxLocalExperts];
     int wcnt[kAlignWaves * kMaxLocalExperts];
     int scratch[kAlignWaves + 1];
 };
@@ -266,7 +299,7 @@ __device__ __forceinline__ void align_single_body(const int32_t* __restrict__ id
             atomicAdd(&L.a[keys[r]], 1);
     __syncthreads();
     // L.a now holds the offsets
-    if (finish_scan(L.a, L.b, L.c, L.scratch, E, block_m, o)) {
+    if (finish_scan(L.a, L.b, L.c, L.d, L.scratch, E, block_m, o)) {
 #pragma unroll
         for (int r = 0; r < kSingleRounds; ++r)
             keys[r] = -1;  // over capacity: no pair is placed, src2dst = -1
@@ -367,7 +400,7 @@ __global__ __launch_bounds__(kAlignThreads) void align_scan_kernel(int32_t* __re
         L.a[e] = run;
     }
     __syncthreads();
-    finish_scan(L.a, L.b, L.c, L.scratch, E, block_m, o);  // L.a now holds the experts' offsets
+    finish_scan(L.a, L.b, L.c, L.d, L.scratch, E, block_m, o);  // L.a now holds the experts' offsets
     for (int i = t; i < ng * E; i += kAlignThreads) {
         const int g = i / (int)E, e = i - g * (int)E;
         const int64_t c0 = g * cpg, c1 = c0 + cpg < nchunks ? c0 + cpg : nchunks;

@@ -96,14 +96,49 @@ bool use_tile(int64_t pairs, int64_t experts)
 constexpr int64_t kBoundedTileRows = 64;     // block-tiled from this many rows per expert
 constexpr int64_t kBoundedTwoListRows = 2;   // per-expert 16 / 32-row blocks above this
 
+// Between these regimes the counts decide (DeepGEMM PR #53 commit notes: an
+// expected-cost argmin over the per-expert token counts replaces hand-set
+// boundaries; there the counts are Poisson expectations, here the align has
+// the real ones).  The align writes the block-tiled path's m-block list
+// beside the two skinny lists and predicts both paths' GEMM time; both GEMM
+// kernels are launched and the one not chosen exits at once.  Fitted on
+// MI355X (32 of 256 experts, top-8, H = 7168, I = 2048; uniform routing at 8
+// to 64 rows per expert, Zipf routing, T = 4096): a skinny m-block streams
+// one expert's weights (1.5*H*I bytes) at ~4.5 TB/s; a 160 x 256 tile costs
+// per 128-K group 1.8 us + 0.0108 us per real row (gate_up, rounds of one
+// tile per CU) and 1.16 + 0.0085 us per row (down, streamed across tiles).
+// The choice is offered while the skinny lists stay below kChoiceMaxBlocks
+// m-blocks (the launch not taken then costs a few us).
+constexpr int64_t kChoiceMaxBlocks = 4096;
+w4a8::PathCost path_cost(int64_t H, int64_t I)
+{
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+        cus = 256;
+    w4a8::PathCost c;
+    c.skinny_block_us = (float)(1.5 * (double)H * (double)I / 4.5e6);
+    c.tiles_gu = (float)(I / W4A8_GROUP);
+    c.tiles_dn = (float)((H + 255) / 256);
+    c.groups_gu = (float)(H / W4A8_GROUP);
+    c.groups_dn = (float)(I / W4A8_GROUP);
+    c.gu0 = 1.8f;
+    c.gu1 = 0.0108f;
+    c.dn0 = 1.16f;
+    c.dn1 = 0.0085f;
+    c.cus = (float)cus;
+    return c;
+}
+
 // The fused forward's workspace.  P is unknown on the host, so every
 // per-pair buffer is sized for `cap` pairs: F = T*topk, or the caller's bound
 // on the local pairs (w4a8_fused_moe_bounded), which the align enforces.
 struct MoePlan {
     bool tile;
     bool two_lists;  // per-expert 16 / 32-row blocks (see use_two_lists)
+    bool choose;     // two lists and the block-tiled list, the path chosen on the device
     int block_m;
-    int64_t F, cap, nb_max, nb2_max;
+    int64_t F, cap, nb_max, nb2_max, nb3_max;
     w4a8::AlignOut al;
     void* align_ws;
     uint8_t* qa;
@@ -124,15 +159,29 @@ size_t plan_moe(void* ws, int64_t T, int64_t H, int64_t topk, int64_t E, int64_t
     p.F = T * topk;
     p.cap = max_pairs > 0 && max_pairs < p.F ? max_pairs : p.F;
     const bool bounded = p.cap < p.F;
-    p.tile = down_group == W4A8_GROUP &&
-             (bounded ? p.cap >= kBoundedTileRows * E : use_tile(p.F, E));
-    p.two_lists = down_group == W4A8_GROUP && !p.tile &&
-                  (bounded ? p.cap > kBoundedTwoListRows * E : use_two_lists(p.F, E));
+    // the skinny lists' m-block bound if the two lists were used
+    const int64_t lists_max = ceil_div(p.cap, kSmallExpertRows) + ceil_div(p.cap, kLargeBlockRows) + 2 * E;
+    if (down_group != W4A8_GROUP) {
+        p.tile = p.two_lists = p.choose = false;
+    } else if (bounded) {
+        // the counts decide above 2 rows per expert while the skinny grid stays small
+        p.choose = p.cap > kBoundedTwoListRows * E && lists_max <= kChoiceMaxBlocks;
+        p.tile = !p.choose && p.cap >= kBoundedTileRows * E;
+        p.two_lists = p.choose || (!p.tile && p.cap > kBoundedTwoListRows * E);
+    } else {
+        // between the decode and the prefill rule the counts decide
+        p.tile = use_tile(p.F, E);
+        p.two_lists = !p.tile && use_two_lists(p.F, E);
+        p.choose = p.two_lists && lists_max <= kChoiceMaxBlocks;
+    }
     p.block_m = p.tile ? w4a8::kTileRows : p.two_lists ? kSmallExpertRows : pick_block_m(p.cap, E);
     p.nb_max = ceil_div(p.cap, p.block_m) + E;
     p.nb2_max = p.two_lists ? ceil_div(p.cap, kLargeBlockRows) + E : 0;
+    p.nb3_max = p.choose ? ceil_div(p.cap, w4a8::kTileRows) + E : 0;
     p.al.max_pairs = p.cap < p.F ? (int32_t)p.cap : 0;
     p.al.pairs_out = nullptr;
+    p.al.static_path = p.tile ? 1 : 0;
+    p.al.cost = p.choose ? path_cost(H, I) : w4a8::PathCost{};
     p.al.counts = c.take<int32_t>(E);
     p.al.offsets = c.take<int32_t>(E + 1);
     p.al.sorted = c.take<int32_t>(p.cap);
@@ -155,6 +204,9 @@ size_t plan_moe(void* ws, int64_t T, int64_t H, int64_t topk, int64_t E, int64_t
     p.al.num_blocks2 = p.two_lists ? c.take<int32_t>(1) : nullptr;
     p.al.small_rows = kSmallExpertRows;
     p.al.block_m2 = kLargeBlockRows;
+    p.al.block_row3 = p.choose ? c.take<int32_t>(p.nb3_max) : nullptr;
+    p.al.num_blocks3 = p.choose ? c.take<int32_t>(1) : nullptr;
+    p.al.path = p.choose ? c.take<int32_t>(1) : nullptr;
     return c.used;
 }
 
@@ -359,6 +411,41 @@ w4a8::GemmArgs second_list(const w4a8::GemmArgs& g, const MoePlan& p)
     return g2;
 }
 
+// the same GEMM's arguments for the block-tiled list of a device-chosen path
+w4a8::GemmArgs tiled_list(const w4a8::GemmArgs& g, const MoePlan& p)
+{
+    w4a8::GemmArgs g3 = g;
+    g3.block_expert = nullptr;
+    g3.block_row = p.al.block_row3;
+    g3.num_blocks = p.al.num_blocks3;
+    g3.max_blocks = p.nb3_max;
+    g3.path = p.al.path;
+    g3.path_want = 1;
+    return g3;
+}
+
+// one GEMM stage on the plan's path(s): the block-tiled kernel, the skinny
+// kernel over one or two lists, or (device-chosen) both, one of which exits
+hipError_t launch_stage(const w4a8::GemmArgs& g, const MoePlan& p, bool gate_up, hipStream_t s)
+{
+    const int tile_mode = gate_up ? w4a8::TILE_GATEUP : w4a8::TILE_DOWN;
+    const int epi = gate_up ? w4a8::EPI_SWIGLU_Q : w4a8::EPI_F32;
+    if (p.tile)
+        return w4a8::launch_gemm_tile(g, tile_mode, s);
+    if (!p.two_lists)
+        return w4a8::launch_gemm_skinny(g, epi, p.block_m, s);
+    if (p.choose) {
+        const hipError_t e = w4a8::launch_gemm_tile(tiled_list(g, p), tile_mode, s);
+        if (e != hipSuccess)
+            return e;
+        w4a8::GemmArgs g1 = g;
+        g1.path = p.al.path;
+        g1.path_want = 0;
+        return w4a8::launch_gemm_skinny_two_lists(g1, second_list(g1, p), epi, s);
+    }
+    return w4a8::launch_gemm_skinny_two_lists(g, second_list(g, p), epi, s);
+}
+
 // ev: the stage events to record (null: none); max_pairs, pairs_out: the
 // bound on the local pairs and where their count goes (0 / null: none)
 int fused_moe_run(const void* hidden_bf16, int64_t T, int64_t H, const int32_t* topk_ids,
@@ -461,9 +548,7 @@ int fused_moe_run(const void* hidden_bf16, int64_t T, int64_t H, const int32_t* 
     g.out_side = p.qh_side;
     g.requant_scale = a2_scale;
     g.sub_group = down_group;
-    e = p.tile        ? w4a8::launch_gemm_tile(g, w4a8::TILE_GATEUP, stream)
-        : p.two_lists ? w4a8::launch_gemm_skinny_two_lists(g, second_list(g, p), w4a8::EPI_SWIGLU_Q, stream)
-                      : w4a8::launch_gemm_skinny(g, w4a8::EPI_SWIGLU_Q, p.block_m, stream);
+    e = launch_stage(g, p, true, stream);
     if (e != hipSuccess)
         return W4A8_ERR_HIP;
     mark(ev, 3, stream);
@@ -480,9 +565,7 @@ int fused_moe_run(const void* hidden_bf16, int64_t T, int64_t H, const int32_t* 
     g.K = I;
     g.N = H;
     g.out_f32 = p.y2;
-    e = p.tile        ? w4a8::launch_gemm_tile(g, w4a8::TILE_DOWN, stream)
-        : p.two_lists ? w4a8::launch_gemm_skinny_two_lists(g, second_list(g, p), w4a8::EPI_F32, stream)
-                      : w4a8::launch_gemm_skinny(g, w4a8::EPI_F32, p.block_m, stream);
+    e = launch_stage(g, p, false, stream);
     if (e != hipSuccess)
         return W4A8_ERR_HIP;
     mark(ev, 4, stream);
@@ -608,7 +691,7 @@ int w4a8_fused_moe_bounded(const void* hidden_bf16, int64_t T, int64_t H, const 
         return W4A8_ERR_INVALID_ARG;
     if (max_local_pairs < 1 || (workspace != nullptr && T > 0 && local_pairs == nullptr))
         return W4A8_ERR_INVALID_ARG;
-    if (((uintptr_t)local_pairs & 3u) != 0)
+    if (((uintptr_t)local_pairs & 7u) != 0)
         return W4A8_ERR_UNSUPPORTED;
     const WeightFormat f = weight_format == W4A8_WEIGHTS_FP4_PACKED    ? kFp4Packed
                            : weight_format == W4A8_WEIGHTS_INT4_PACKED ? kInt4Packed
@@ -703,16 +786,17 @@ int w4a8_fused_moe_workspace_layout(int64_t T, int64_t H, int64_t topk,
                                     int64_t* block_m)
 {
     if (T < 0 || H <= 0 || I <= 0 || topk < 1 || num_local_experts < 1 || offsets == nullptr ||
-        (n != 12 && n != 15) || block_m == nullptr)
+        (n != 12 && n != 15 && n != 18) || block_m == nullptr)
         return W4A8_ERR_INVALID_ARG;
     MoePlan p;
     // carve from a fake base so that pointers equal byte offsets (base != null)
     char* const base = (char*)(uintptr_t)4096;
     plan_moe(base, T, H, topk, num_local_experts, I, p);
-    const void* ptrs[15] = {p.al.counts, p.al.offsets, p.al.sorted, p.al.src2dst,
+    const void* ptrs[18] = {p.al.counts, p.al.offsets, p.al.sorted, p.al.src2dst,
                             p.al.block_expert, p.al.block_row, p.al.num_blocks, p.qa,
                             p.qa_side, p.qh, p.qh_side, p.y2,
-                            p.al.block_expert2, p.al.block_row2, p.al.num_blocks2};
+                            p.al.block_expert2, p.al.block_row2, p.al.num_blocks2,
+                            p.al.block_row3, p.al.num_blocks3, p.al.path};
     for (int i = 0; i < n; ++i)
         offsets[i] = ptrs[i] != nullptr ? (size_t)((const char*)ptrs[i] - base) : 0;
     *block_m = p.block_m;

@@ -711,6 +711,8 @@ __device__ __forceinline__ void skinny_body(const GemmArgs& a, const int by, con
 template <int NT, int EPI, int DW, bool F16, bool SW4, bool PK, bool FP4, int NF, int SG>
 __global__ __launch_bounds__(256, NT == 2 ? 2 : 1) void gemm_skinny_kernel(GemmArgs a)
 {
+    if (path_not_taken(a))
+        return;
     skinny_body<NT, EPI, DW, F16, SW4, PK, FP4, NF, SG>(a, (int)blockIdx.y, (int)blockIdx.x);
 }
 
@@ -724,6 +726,8 @@ template <int EPI, bool F16, bool SW4, bool PK, bool FP4, int NF1, int NF2>
 __global__ __launch_bounds__(256, 2) void gemm_skinny_two_lists_kernel(GemmArgs a1, GemmArgs a2, int nb2,
                                                                        int gx1, int gx2)
 {
+    if (path_not_taken(a1))
+        return;
     const int by = (int)blockIdx.y, bx = (int)blockIdx.x;
     if (by < nb2) {
         if (bx < gx2)

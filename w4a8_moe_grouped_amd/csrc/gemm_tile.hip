@@ -474,6 +474,8 @@ __global__ __launch_bounds__(kTThreads) void gemm_tile_kernel(GemmArgs a)
 {
     __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
     __shared__ int s_expert;
+    if (path_not_taken(a))
+        return;
     const int nbn = MODE == TILE_GATEUP ? (int)(a.I / kGroup) : (int)((a.N + kTBN - 1) / kTBN);
     const int total = *a.num_blocks * nbn;
     const int per_xcd = (total + 7) >> 3;
@@ -802,6 +804,8 @@ __global__ __launch_bounds__(kTThreads) void gemm_down_stream_kernel(GemmArgs a)
     __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
     __shared__ int4 s_meta[kMaxStreamTiles];
     __shared__ int s_expert;
+    if (path_not_taken(a))
+        return;
     const int G = (int)(a.K / kGroup);
     const int nbn = (int)((a.N + kTBN - 1) / kTBN);
     const int total = *a.num_blocks * nbn;

@@ -19,6 +19,20 @@ hipError_t launch_quant_bf16(const uint16_t* x, int64_t M, int64_t K, int64_t ld
                              hipStream_t s);
 
 // ---- routing permutation (align.hip) ----
+// Predicted time (us) of the two GEMMs of one fused call on either path, from
+// the m-block counts the align finds (constants set on the host):
+//   skinny: (blocks of both lists) * skinny_block_us (every m-block streams
+//           one expert's gate_up and down weights);
+//   tiled:  ceil(tiles_gu * nb / cus) * groups_gu * (gu0 + gu1 * rows)
+//         +      tiles_dn * nb / cus  * groups_dn * (dn0 + dn1 * rows),
+// nb = kTileRows-row m-blocks, rows = pairs / nb (real rows per m-block).
+struct PathCost {
+    float skinny_block_us;
+    float tiles_gu, tiles_dn;    // tiles per m-block (gate_up, down)
+    float groups_gu, groups_dn;  // 128-K groups per tile
+    float gu0, gu1, dn0, dn1;    // us per group of one tile: constant + per real row
+    float cus;
+};
 struct AlignOut {
     int32_t* counts;        // [E]
     int32_t* offsets;       // [E+1]
@@ -42,7 +56,17 @@ struct AlignOut {
     // block counts and block_start are written as zero and every src2dst
     // entry as -1, so the GEMMs do nothing and the combine writes +0.
     int32_t max_pairs;
-    int32_t* pairs_out;  // [1] receives the number of local pairs, or null
+    int32_t* pairs_out;  // [2] receives the number of local pairs and the path, or null
+    // Path chosen on the device (path != null): besides the two lists above,
+    // a list of kTileRows-row blocks (block_row3, num_blocks3, and
+    // block_start for it) is written, and *path receives 1 when the
+    // block-tiled GEMMs are predicted faster than the two skinny lists, else
+    // 0 (cost model below).  With path == null, static_path is reported.
+    int32_t* block_row3;   // [nb3_max]
+    int32_t* num_blocks3;  // [1]
+    int32_t* path;         // [1]
+    int32_t static_path;
+    PathCost cost;
 };
 int64_t align_chunk_count(int64_t F);
 size_t align_workspace_bytes(int64_t F, int64_t E);
@@ -99,7 +123,16 @@ struct GemmArgs {
     // skinny kernel, 16-row m-blocks: blocks of at most this many rows read
     // their activations from a whole-K copy in LDS (set by the launcher)
     int32_t stage_rows;
+    // path chosen on the device: the kernel runs only if *path == path_want
+    // (path == null: always)
+    const int32_t* path;
+    int32_t path_want;
 };
+// a workgroup's early exit when the device chose the other path
+__device__ __forceinline__ bool path_not_taken(const GemmArgs& a)
+{
+    return a.path != nullptr && *a.path != a.path_want;
+}
 enum Epilogue { EPI_F32 = 0, EPI_SWIGLU_Q = 2 };
 hipError_t launch_gemm_skinny(const GemmArgs& a, int epilogue, int block_m, hipStream_t s);
 // per-expert block heights: list a1 of 16-row blocks and list a2 of 32-row

@@ -140,19 +140,20 @@ def fused_moe_workspace_bytes(T: int, H: int, topk: int, num_local_experts: int,
 
 LAYOUT_KEYS = ("counts", "offsets", "sorted_pair_ids", "src2dst", "block_expert", "block_row",
                "num_blocks", "qa16", "qa_side", "qh", "qh_side", "y2", "block_expert2", "block_row2",
-               "num_blocks2")
+               "num_blocks2", "block_row3", "num_blocks3", "path")
 
 
 def fused_moe_workspace_layout(T: int, H: int, topk: int, num_local_experts: int, I: int):
     """Byte offsets of the intermediates inside the fused forward's workspace."""
-    offs = (ctypes.c_size_t * 15)()
+    offs = (ctypes.c_size_t * 18)()
     bm = ctypes.c_int64(0)
-    _check(load().w4a8_fused_moe_workspace_layout(T, H, topk, num_local_experts, I, offs, 15,
+    _check(load().w4a8_fused_moe_workspace_layout(T, H, topk, num_local_experts, I, offs, 18,
                                                   ctypes.byref(bm)),
            "w4a8_fused_moe_workspace_layout")
     d = dict(zip(LAYOUT_KEYS, [int(o) for o in offs]))
     d["block_m"] = int(bm.value)
     d["two_lists"] = d["num_blocks2"] != 0
+    d["device_path"] = d["path"] != 0  # the path is chosen on the device
     return d
 
 
@@ -280,8 +281,9 @@ def fused_moe_bounded(hidden: torch.Tensor, topk_ids: torch.Tensor, topk_weights
     """w4a8_fused_moe_bounded: the fused forward with per-pair buffers sized
     for max_local_pairs local pairs.  weights = (w13, s13, w2, s2) in the
     layout weight_format names.  Returns (out, local_pairs), the latter a
-    one-element int32 device tensor the call writes with the local pair count
-    (out is all +0 when it exceeds the bound)."""
+    two-element int32 device tensor the call writes with the local pair count
+    (out is all +0 when it exceeds the bound) and the path (1: block-tiled
+    kernels, 0: few-rows kernels)."""
     w13, s13, w2, s2 = weights
     _need_cuda(hidden, topk_ids, topk_weights, w13, s13, w2, s2)
     T, H = hidden.shape
@@ -295,8 +297,8 @@ def fused_moe_bounded(hidden: torch.Tensor, topk_ids: torch.Tensor, topk_weights
         assert t.is_contiguous()
     out = out if out is not None else torch.empty((T, H), dtype=torch.bfloat16, device=hidden.device)
     if local_pairs is None:
-        local_pairs = torch.full((1,), -1, dtype=torch.int32, device=hidden.device)
-    assert local_pairs.is_cuda and local_pairs.dtype == torch.int32 and local_pairs.numel() >= 1
+        local_pairs = torch.full((2,), -1, dtype=torch.int32, device=hidden.device)
+    assert local_pairs.is_cuda and local_pairs.dtype == torch.int32 and local_pairs.numel() >= 2
     if workspace is None:
         need = fused_moe_bounded_workspace_bytes(T, H, k, E, I, max_local_pairs, weight_format)
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=hidden.device)
