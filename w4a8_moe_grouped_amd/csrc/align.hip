@@ -124,14 +124,72 @@ __device__ int block_exclusive_scan(int* vals, int n, int* scratch /* >= kAlignW
 // exceed o.max_pairs: then the offsets, block counts and block_start are
 // zero, no block is listed, and the caller must scatter no pair.  All
 // threads call it.
-// Predicted us of the two GEMMs on the block-tiled path minus the skinny
-// one (see PathCost): < 0 picks the block-tiled kernels.
-__device__ float tiled_minus_skinny(const PathCost& c, int P, int nb_skinny, int nb_tiled)
+// Rows a block-tiled wave pair computes for a tile of r rows: each 80-row
+// half is computed in whole 16-row slices.
+__device__ __forceinline__ float tile_rows16(int r)
 {
-    const float rows = nb_tiled > 0 ? (float)P / (float)nb_tiled : 0.0f;
-    const float gu = ceilf(c.tiles_gu * (float)nb_tiled / c.cus) * c.groups_gu * (c.gu0 + c.gu1 * rows);
-    const float dn = c.tiles_dn * (float)nb_tiled / c.cus * c.groups_dn * (c.dn0 + c.dn1 * rows);
-    return gu + dn - (float)nb_skinny * c.skinny_block_us;
+    const int h0 = min(r, kTileRows / 2), h1 = max(r - kTileRows / 2, 0);
+    return 16.0f * (float)((h0 + 15) / 16 + (h1 + 15) / 16);
+}
+
+// Predicted us of the slowest workgroup of one block-tiled launch: nb
+// m-blocks (bstart [E] their exclusive prefix per expert, off [E] the
+// experts' first rows, P rows in all), nbn tiles per m-block, wgs
+// workgroups walking the tiles in the launchers' order (tile L = expert
+// major, then weight block, m-block fastest; XCD x = w % 8 takes the x-th
+// eighth, its workgroups every (wgs / 8)-th tile of it).  red: 1 int of LDS.
+// All threads call it.
+__device__ float tiled_launch_us(const int* bstart, const int* off, int P, int64_t E, int nb, int nbn,
+                                 int wgs, float groups, float c0, float c1, int* red)
+{
+    const int total = nb * nbn;
+    const int per_xcd = (total + 7) >> 3;
+    const int stride = wgs >> 3;
+    float tmax = 0.0f;
+    for (int w = threadIdx.x; w < wgs; w += kAlignThreads) {
+        const int x = w & 7;
+        float tw = 0.0f;
+        for (int t = w >> 3; t < per_xcd; t += stride) {
+            const int L = x * per_xcd + t;
+            if (L >= total)
+                break;
+            int lo = 0, hi = (int)E;  // the largest e with bstart[e] * nbn <= L
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if (bstart[mid] * nbn <= L)
+                    lo = mid;
+                else
+                    hi = mid;
+            }
+            const int bs = bstart[lo];
+            const int nbe = (lo + 1 < E ? bstart[lo + 1] : nb) - bs;
+            const int mb = (L - bs * nbn) % nbe;
+            const int c = (lo + 1 < E ? off[lo + 1] : P) - off[lo];
+            tw += groups * (c0 + c1 * tile_rows16(min(kTileRows, c - kTileRows * mb)));
+        }
+        tmax = fmaxf(tmax, tw);
+    }
+    if (threadIdx.x == 0)
+        *red = 0;
+    __syncthreads();
+    atomicMax(red, __float_as_int(tmax));  // non-negative floats order like their bits
+    __syncthreads();
+    const float r = __int_as_float(*red);
+    __syncthreads();
+    return r;
+}
+
+// Predicted us of the two GEMMs on the block-tiled path minus the skinny one
+// (see PathCost): < 0 picks the block-tiled kernels.  bstart / off: LDS, as
+// in tiled_launch_us.  All threads call it.
+__device__ float tiled_minus_skinny(const PathCost& c, const int* bstart, const int* off, int P,
+                                    int64_t E, int nb_skinny, int nb_tiled, int* red)
+{
+    const float gu = tiled_launch_us(bstart, off, P, E, nb_tiled, c.nbn_gu, c.wgs_gu, c.groups_gu,
+                                     c.gu0, c.gu1, red);
+    const float dn = tiled_launch_us(bstart, off, P, E, nb_tiled, c.nbn_dn, c.wgs_dn, c.groups_dn,
+                                     c.dn0, c.dn1, red);
+    return gu + dn - (c.skinny_fixed_us + (float)nb_skinny * c.skinny_block_us);
 }
 
 __device__ bool finish_scan(int* counts_lds, int* tmp_lds, int* tmp2_lds, int* tmp3_lds, int* scratch,
@@ -154,8 +212,11 @@ __device__ bool finish_scan(int* counts_lds, int* tmp_lds, int* tmp2_lds, int* t
     const int nb2 = dual ? block_exclusive_scan(tmp2_lds, (int)E, scratch) : 0;
     const int nb3 = choose ? block_exclusive_scan(tmp3_lds, (int)E, scratch) : 0;
     const bool over = o.max_pairs > 0 && P > o.max_pairs;  // P is the same in every thread
+    // (the scans leave the exclusive prefixes in counts_lds and tmp3_lds)
     const int path = !choose ? o.static_path
-                             : (!over && tiled_minus_skinny(o.cost, P, nb + nb2, nb3) < 0.0f ? 1 : 0);
+                     : over  ? 0
+                             : (tiled_minus_skinny(o.cost, tmp3_lds, counts_lds, P, E, nb + nb2, nb3, scratch) < 0.0f
+                                    ? 1 : 0);
     // block_start belongs to the list the block-tiled kernels read
     const int* bs_lds = choose ? tmp3_lds : tmp_lds;
     const int nbs = choose ? nb3 : nb;

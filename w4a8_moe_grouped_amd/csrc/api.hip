@@ -100,33 +100,34 @@ constexpr int64_t kBoundedTwoListRows = 2;   // per-expert 16 / 32-row blocks ab
 // expected-cost argmin over the per-expert token counts replaces hand-set
 // boundaries; there the counts are Poisson expectations, here the align has
 // the real ones).  The align writes the block-tiled path's m-block list
-// beside the two skinny lists and predicts both paths' GEMM time; both GEMM
-// kernels are launched and the one not chosen exits at once.  Fitted on
-// MI355X (32 of 256 experts, top-8, H = 7168, I = 2048; uniform routing at 8
-// to 64 rows per expert, Zipf routing, T = 4096): a skinny m-block streams
-// one expert's weights (1.5*H*I bytes) at ~4.5 TB/s; a 160 x 256 tile costs
-// per 128-K group 1.8 us + 0.0108 us per real row (gate_up, rounds of one
-// tile per CU) and 1.16 + 0.0085 us per row (down, streamed across tiles).
+// beside the two skinny lists and predicts both paths' GEMM time;
+// both GEMM kernels are launched and the one not chosen exits at once.
+// Fitted by least squares on MI355X (32 local experts, top-8, H = 7168,
+// I = 2048; uniform routing at 8 to 128 rows per expert, two Zipf routings,
+// T = 4096): the two skinny GEMMs cost 39.8 us plus, per m-block, one
+// expert's weights (1.5*H*I bytes) at 4.95 TB/s; a 160 x 256 tile costs per
+// 128-K group 0.815 us + 0.01327 us per computed row in gate_up and
+// 0.776 + 0.00833 in the down GEMM, summed over the tiles of the slowest
+// workgroup (predictions within 3% of the tiled and 8% of the skinny times
+// measured; the faster path picked on all eight workloads).
 // The choice is offered while the skinny lists stay below kChoiceMaxBlocks
 // m-blocks (the launch not taken then costs a few us).
 constexpr int64_t kChoiceMaxBlocks = 4096;
-w4a8::PathCost path_cost(int64_t H, int64_t I)
+w4a8::PathCost path_cost(int64_t H, int64_t I, int64_t nb3_max)
 {
-    int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
-        cus = 256;
     w4a8::PathCost c;
-    c.skinny_block_us = (float)(1.5 * (double)H * (double)I / 4.5e6);
-    c.tiles_gu = (float)(I / W4A8_GROUP);
-    c.tiles_dn = (float)((H + 255) / 256);
+    c.skinny_fixed_us = 39.8f;
+    c.skinny_block_us = (float)(1.5 * (double)H * (double)I / 4.95e6);
     c.groups_gu = (float)(H / W4A8_GROUP);
     c.groups_dn = (float)(I / W4A8_GROUP);
-    c.gu0 = 1.8f;
-    c.gu1 = 0.0108f;
-    c.dn0 = 1.16f;
-    c.dn1 = 0.0085f;
-    c.cus = (float)cus;
+    c.nbn_gu = (int32_t)(I / W4A8_GROUP);
+    c.nbn_dn = (int32_t)((H + 255) / 256);
+    c.wgs_gu = (int32_t)w4a8::tile_launch_workgroups(c.nbn_gu * nb3_max);
+    c.wgs_dn = (int32_t)w4a8::tile_launch_workgroups(c.nbn_dn * nb3_max);
+    c.gu0 = 0.815f;
+    c.gu1 = 0.01327f;
+    c.dn0 = 0.776f;
+    c.dn1 = 0.00833f;
     return c;
 }
 
@@ -181,7 +182,7 @@ size_t plan_moe(void* ws, int64_t T, int64_t H, int64_t topk, int64_t E, int64_t
     p.al.max_pairs = p.cap < p.F ? (int32_t)p.cap : 0;
     p.al.pairs_out = nullptr;
     p.al.static_path = p.tile ? 1 : 0;
-    p.al.cost = p.choose ? path_cost(H, I) : w4a8::PathCost{};
+    p.al.cost = p.choose ? path_cost(H, I, p.nb3_max) : w4a8::PathCost{};
     p.al.counts = c.take<int32_t>(E);
     p.al.offsets = c.take<int32_t>(E + 1);
     p.al.sorted = c.take<int32_t>(p.cap);

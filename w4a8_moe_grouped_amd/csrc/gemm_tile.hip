@@ -46,6 +46,8 @@
 //                i: h = silu(gate) * up (fp64, rounded once to fp32), then the
 //                fp8 requant of the block (DeepGEMM PR #53 "Changes": SwiGLU ->
 //                per-token FP8 requant).
+#include <type_traits>
+
 #include "common.hpp"
 #include "internal.hpp"
 #include "lds_direct.hpp"
@@ -208,19 +210,16 @@ __device__ __forceinline__ void tile_body(const GemmArgs& a, const int L, uint8_
         wrow_f[f] = MODE == TILE_GATEUP ? (f >= 2 ? 128 : 0) + 32 * wn + 16 * (f & 1) + c16
                                         : 64 * wn + 16 * f + c16;
 
-    // a wave whose half holds no row of the m-block skips the K loop; the
-    // others compute all five slices (skipping the slices past the last row
-    // measured slower: the branches split the MFMA/VALU schedule)
-    const bool wave_idle = kHalf * wm >= rows;
+    // A wave computes the 16-row slices of its half that hold a row of the
+    // m-block: the K loop and the epilogue below are instantiated for every
+    // slice count and chosen once per tile (a branch per slice inside the
+    // loop measured slower: it splits the MFMA/VALU schedule); a wave whose
+    // half holds no row only loads and meets the barriers.  The compute also
+    // stays behind a run-time test of that: without the branch the compiler
+    // schedules the five-slice loop as straight-line code and spills.
+    const int nsl = min(kSlices, max(0, (rows - kHalf * wm + 15) / 16));
+    const bool wave_idle = nsl == 0;
 
-    float acc[kSlices][4][4];
-#pragma unroll
-    for (int m = 0; m < kSlices; ++m)
-#pragma unroll
-        for (int f = 0; f < 4; ++f)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                acc[m][f][r] = 0;
 
     // this wave's loads of group h landed (the younger groups in flight may
     // stay so: loads retire in order)
@@ -278,193 +277,214 @@ __device__ __forceinline__ void tile_body(const GemmArgs& a, const int L, uint8_
     if (kStages - 1 < G)
         issue(kStages - 1, kStages - 1);
 
-    v4i wb[4], a0 = {}, a1 = {};
-    float sw[4];
-    float4 s01 = {}, s23 = {};  // prefetched side data (down GEMM)
-    if (!wave_idle) {
-        read_b(smem, wb, sw);
-        read_a(smem, 0, a0, a1);
-        if (kSidePre)
-            read_side(smem, 0, s01, s23);
-    }
+    // the K loop and the epilogue of a wave that computes NSL slices
+    auto kloop = [&](auto nsl_c) {
+        constexpr int NSL = decltype(nsl_c)::value;
+        float acc[NSL > 0 ? NSL : 1][4][4];
+#pragma unroll
+        for (int m = 0; m < NSL; ++m)
+#pragma unroll
+            for (int f = 0; f < 4; ++f)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    acc[m][f][r] = 0;
+        v4i wb[4], a0 = {}, a1 = {};
+        float sw[4];
+        float4 s01 = {}, s23 = {};  // prefetched side data (down GEMM)
+        if (NSL > 0 && !wave_idle) {
+            read_b(smem, wb, sw);
+            read_a(smem, 0, a0, a1);
+            if (kSidePre)
+                read_side(smem, 0, s01, s23);
+        }
 
-    for (int g = 0; g < G; ++g) {
-        const uint8_t* base = smem + (g % kStages) * kStageBytes;
-        if (!wave_idle) {
-            // int4: weight scales; fp4: gate_up promotion scales 2^(e_max - 136)
-            float swc[4];
-            int eq[4];  // fp4 down: the lane's UE8M0 byte
-            v8i b8[4];
-            v8h bh[MODE == TILE_GATEUP ? 4 : 1][4];
+        for (int g = 0; g < G; ++g) {
+            const uint8_t* base = smem + (g % kStages) * kStageBytes;
+            if (NSL > 0 && !wave_idle) {
+                // int4: weight scales; fp4: gate_up promotion scales 2^(e_max - 136)
+                float swc[4];
+                int eq[4];  // fp4 down: the lane's UE8M0 byte
+                v8i b8[4];
+                v8h bh[MODE == TILE_GATEUP ? 4 : 1][4];
 #pragma unroll
-            for (int f = 0; f < 4; ++f) {
-                const uint32_t sd = __builtin_bit_cast(uint32_t, sw[f]);
-                if (FP4 && MODE == TILE_GATEUP) {
-                    const Fp4GroupScale fs = fp4_group_scale(sd, q);
-                    swc[f] = fs.promote;
-#pragma unroll
-                    for (int c = 0; c < 4; ++c)
-                        bh[f][c] = fp4x8_to_f16((uint32_t)wb[f][c], fs.conv);
-                } else if (FP4) {
-                    eq[f] = (int)((sd >> (8 * q)) & 0xFFu);
-                } else {
-                    swc[f] = sw[f];
-                    b8[f] = unpack_int4_u(wb[f]);
-                    if (MODE == TILE_GATEUP) {
+                for (int f = 0; f < 4; ++f) {
+                    const uint32_t sd = __builtin_bit_cast(uint32_t, sw[f]);
+                    if (FP4 && MODE == TILE_GATEUP) {
+                        const Fp4GroupScale fs = fp4_group_scale(sd, q);
+                        swc[f] = fs.promote;
 #pragma unroll
                         for (int c = 0; c < 4; ++c)
-                            bh[f][c] = fp8x8_to_f16((uint32_t)b8[f][2 * c], (uint32_t)b8[f][2 * c + 1]);
+                            bh[f][c] = fp4x8_to_f16((uint32_t)wb[f][c], fs.conv);
+                    } else if (FP4) {
+                        eq[f] = (int)((sd >> (8 * q)) & 0xFFu);
+                    } else {
+                        swc[f] = sw[f];
+                        b8[f] = unpack_int4_u(wb[f]);
+                        if (MODE == TILE_GATEUP) {
+#pragma unroll
+                            for (int c = 0; c < 4; ++c)
+                                bh[f][c] = fp8x8_to_f16((uint32_t)b8[f][2 * c], (uint32_t)b8[f][2 * c + 1]);
+                        }
                     }
                 }
-            }
-            // all five slices (padding rows are computed and dropped at the
-            // store)
+                // the slices that hold rows (padding rows among them are
+                // computed and dropped at the store)
 #pragma unroll
-            for (int m = 0; m < kSlices; ++m) {
-                const v4i ca0 = a0, ca1 = a1;
-                float4 cs01 = s01, cs23 = s23;
-                if (!kSidePre)
-                    read_side(base, m, cs01, cs23);
-                if (m + 1 < kSlices) {
-                    read_a(base, m + 1, a0, a1);
-                    if (kSidePre)
-                        read_side(base, m + 1, s01, s23);
-                }
-                v4f raw[4];
-                if (MODE == TILE_GATEUP) {
-#pragma unroll
-                    for (int f = 0; f < 4; ++f)
-                        raw[f] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-                    // one 32-K step at a time: its converted fragment feeds
-                    // the four MFMAs right away
-#pragma unroll
-                    for (int c = 0; c < 4; ++c) {
-                        const v4i& src = c < 2 ? ca0 : ca1;
-                        const v8h ah = fp8x8_to_f16((uint32_t)src[2 * (c & 1)], (uint32_t)src[2 * (c & 1) + 1]);
+                for (int m = 0; m < NSL; ++m) {
+                    const v4i ca0 = a0, ca1 = a1;
+                    float4 cs01 = s01, cs23 = s23;
+                    if (!kSidePre)
+                        read_side(base, m, cs01, cs23);
+                    if (m + 1 < NSL) {
+                        read_a(base, m + 1, a0, a1);
+                        if (kSidePre)
+                            read_side(base, m + 1, s01, s23);
+                    }
+                    v4f raw[4];
+                    if (MODE == TILE_GATEUP) {
 #pragma unroll
                         for (int f = 0; f < 4; ++f)
-                            raw[f] = mfma16x16x32_f16(ah, bh[f][c], raw[f]);
+                            raw[f] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+                        // one 32-K step at a time: its converted fragment feeds
+                        // the four MFMAs right away
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) {
+                            const v4i& src = c < 2 ? ca0 : ca1;
+                            const v8h ah = fp8x8_to_f16((uint32_t)src[2 * (c & 1)], (uint32_t)src[2 * (c & 1) + 1]);
+#pragma unroll
+                            for (int f = 0; f < 4; ++f)
+                                raw[f] = mfma16x16x32_f16(ah, bh[f][c], raw[f]);
+                        }
+                    } else {
+                        const v8i av = {ca0[0], ca0[1], ca0[2], ca0[3], ca1[0], ca1[1], ca1[2], ca1[3]};
+#pragma unroll
+                        for (int f = 0; f < 4; ++f)
+                            raw[f] = FP4 ? mfma16x16x128_fp4(av, wb[f], eq[f])
+                                         : mfma16x16x128(av, b8[f], v4f{0.0f, 0.0f, 0.0f, 0.0f});
                     }
-                } else {
-                    const v8i av = {ca0[0], ca0[1], ca0[2], ca0[3], ca1[0], ca1[1], ca1[2], ca1[3]};
+                    const float c1[4] = {cs01.x, cs01.z, cs23.x, cs23.z};
+                    const float c0[4] = {cs01.y, cs01.w, cs23.y, cs23.w};
 #pragma unroll
                     for (int f = 0; f < 4; ++f)
-                        raw[f] = FP4 ? mfma16x16x128_fp4(av, wb[f], eq[f])
-                                     : mfma16x16x128(av, b8[f], v4f{0.0f, 0.0f, 0.0f, 0.0f});
-                }
-                const float c1[4] = {cs01.x, cs01.z, cs23.x, cs23.z};
-                const float c0[4] = {cs01.y, cs01.w, cs23.y, cs23.w};
 #pragma unroll
-                for (int f = 0; f < 4; ++f)
+                        for (int r = 0; r < 4; ++r) {
+                            if (FP4 && MODE == TILE_GATEUP)  // y += 2^(e_max - 136) * (raw * 512 sa)
+                                acc[m][f][r] = fmaf(raw[f][r] * c1[r], swc[f], acc[m][f][r]);
+                            else if (FP4)  // weight scales inside raw: y += sa * raw
+                                acc[m][f][r] = fmaf(raw[f][r], c1[r] * 0x1p-9f, acc[m][f][r]);
+                            else
+                                acc[m][f][r] = fmaf(swc[f], fmaf(raw[f][r], c1[r], c0[r]), acc[m][f][r]);
+                        }
+                }
+            }
+            if (g + 1 < G) {
+                wait_group(g + 1);
+                // everyone's loads of group g+1 landed, and every wave's reads of
+                // stage g are complete: refill it with group g+4
+                barrier();
+                if (g + kStages < G)
+                    issue(g + kStages, g % kStages);
+                if (NSL > 0 && !wave_idle) {
+                    const uint8_t* nbase = smem + ((g + 1) % kStages) * kStageBytes;
+                    read_b(nbase, wb, sw);
+                    read_a(nbase, 0, a0, a1);
+                    if (kSidePre)
+                        read_side(nbase, 0, s01, s23);
+                }
+            }
+        }
+
+        // ---- epilogues: element (tile row 80wm + 16m + 4q + r, fragment f) ----
+        if (MODE == TILE_DOWN) {
+#pragma unroll
+            for (int f = 0; f < 4; ++f) {
+                const int64_t n = (int64_t)nb * kTBN + wrow_f[f];
+                if (n >= N)
+                    continue;
+#pragma unroll
+                for (int m = 0; m < NSL; ++m)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        if (FP4 && MODE == TILE_GATEUP)  // y += 2^(e_max - 136) * (raw * 512 sa)
-                            acc[m][f][r] = fmaf(raw[f][r] * c1[r], swc[f], acc[m][f][r]);
-                        else if (FP4)  // weight scales inside raw: y += sa * raw
-                            acc[m][f][r] = fmaf(raw[f][r], c1[r] * 0x1p-9f, acc[m][f][r]);
-                        else
-                            acc[m][f][r] = fmaf(swc[f], fmaf(raw[f][r], c1[r], c0[r]), acc[m][f][r]);
+                        const int row = kHalf * wm + 16 * m + 4 * q + r;
+                        if (row < rows)
+                            a.out_f32[(int64_t)(row0 + row) * N + n] = (float)acc[m][f][r];
                     }
             }
+            return;
         }
-        if (g + 1 < G) {
-            wait_group(g + 1);
-            // everyone's loads of group g+1 landed, and every wave's reads of
-            // stage g are complete: refill it with group g+4
-            barrier();
-            if (g + kStages < G)
-                issue(g + kStages, g % kStages);
-            if (!wave_idle) {
-                const uint8_t* nbase = smem + ((g + 1) % kStages) * kStageBytes;
-                read_b(nbase, wb, sw);
-                read_a(nbase, 0, a0, a1);
-                if (kSidePre)
-                    read_side(nbase, 0, s01, s23);
-            }
-        }
-    }
 
-    // ---- epilogues: element (tile row 80wm + 16m + 4q + r, fragment f) ----
-    if (MODE == TILE_DOWN) {
+        // TILE_GATEUP: fragments f and f + 2 hold gate and up of i = 32wn + 16f + c16
+        barrier();  // every wave is done with the stages (no load is in flight)
+        float* s_red = (float*)smem;                        // [4][kTBM] amax per wave column
+        float* s_sum = s_red + 4 * kTBM;                    // [4][kTBM] sum of decoded codes
+        uint8_t* s_q = (uint8_t*)(s_sum + 4 * kTBM);        // [kTBM][128] codes
+        float h[NSL > 0 ? NSL : 1][2][4];
 #pragma unroll
-        for (int f = 0; f < 4; ++f) {
-            const int64_t n = (int64_t)nb * kTBN + wrow_f[f];
-            if (n >= N)
-                continue;
+        for (int m = 0; m < NSL; ++m)
 #pragma unroll
-            for (int m = 0; m < kSlices; ++m)
+            for (int j = 0; j < 2; ++j)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int row = kHalf * wm + 16 * m + 4 * q + r;
-                    if (row < rows)
-                        a.out_f32[(int64_t)(row0 + row) * N + n] = (float)acc[m][f][r];
+                    const double gt = (double)acc[m][j][r], up = (double)acc[m][j + 2][r];
+                    h[m][j][r] = (float)(gt / (1.0 + exp(-gt)) * up);
                 }
-        }
-        return;
-    }
-
-    // TILE_GATEUP: fragments f and f + 2 hold gate and up of i = 32wn + 16f + c16
-    barrier();  // every wave is done with the stages (no load is in flight)
-    float* s_red = (float*)smem;                        // [4][kTBM] amax per wave column
-    float* s_sum = s_red + 4 * kTBM;                    // [4][kTBM] sum of decoded codes
-    uint8_t* s_q = (uint8_t*)(s_sum + 4 * kTBM);        // [kTBM][128] codes
-    float h[kSlices][2][4];
 #pragma unroll
-    for (int m = 0; m < kSlices; ++m)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int m = 0; m < NSL; ++m)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const double gt = (double)acc[m][j][r], up = (double)acc[m][j + 2][r];
-                h[m][j][r] = (float)(gt / (1.0 + exp(-gt)) * up);
+                float mx = fmaxf(fabsf(h[m][0][r]), fabsf(h[m][1][r]));
+                mx = group_max<16>(mx);
+                if (c16 == 0)
+                    s_red[wn * kTBM + kHalf * wm + 16 * m + 4 * q + r] = mx;
             }
+        __syncthreads();
 #pragma unroll
-    for (int m = 0; m < kSlices; ++m)
+        for (int m = 0; m < NSL; ++m)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            float mx = fmaxf(fabsf(h[m][0][r]), fabsf(h[m][1][r]));
-            mx = group_max<16>(mx);
-            if (c16 == 0)
-                s_red[wn * kTBM + kHalf * wm + 16 * m + 4 * q + r] = mx;
+            for (int r = 0; r < 4; ++r) {
+                const int row = kHalf * wm + 16 * m + 4 * q + r;
+                const float mx = fmaxf(fmaxf(s_red[row], s_red[kTBM + row]),
+                                       fmaxf(s_red[2 * kTBM + row], s_red[3 * kTBM + row]));
+                const float inv = a.requant_scale ? recip_static(*a.requant_scale) : recip448(clamp_amax(mx));
+                const uint32_t cc = cvt_e4m3x2(h[m][0][r] * inv, h[m][1][r] * inv);
+                const float2 dv = dec_e4m3x2(cc);
+                const float sum = group_sum<16>(dv.x + dv.y);
+                if (c16 == 0)
+                    s_sum[wn * kTBM + row] = sum;
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    // int4 down GEMM: the interleaved operand order; fp4: natural K order
+                    const int il = 32 * wn + 16 * j + c16;
+                    const int b = il & 7;
+                    const int pos = FP4 ? il : fp8_group_pos(il >> 3) + ((b & 1) ? 4 + (b >> 1) : (b >> 1));
+                    s_q[row * kGroup + pos] = (uint8_t)((cc >> (8 * j)) & 0xFFu);
+                }
+            }
+        __syncthreads();
+        const int64_t GI = a.I / kGroup;
+        for (int i = tid; i < kTBM * 8; i += kTThreads) {
+            const int row = i >> 3, chunk = i & 7;
+            if (row < rows)
+                *(v4i*)(a.out_q + (int64_t)(row0 + row) * a.I + (int64_t)nb * kGroup + chunk * 16) =
+                    *(const v4i*)(s_q + row * kGroup + chunk * 16);
         }
-    __syncthreads();
-#pragma unroll
-    for (int m = 0; m < kSlices; ++m)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int row = kHalf * wm + 16 * m + 4 * q + r;
+        if (tid < kTBM && tid < rows) {
+            const int row = tid;
+            const float sum = s_sum[row] + s_sum[kTBM + row] + s_sum[2 * kTBM + row] + s_sum[3 * kTBM + row];
             const float mx = fmaxf(fmaxf(s_red[row], s_red[kTBM + row]),
                                    fmaxf(s_red[2 * kTBM + row], s_red[3 * kTBM + row]));
-            const float inv = a.requant_scale ? recip_static(*a.requant_scale) : recip448(clamp_amax(mx));
-            const uint32_t cc = cvt_e4m3x2(h[m][0][r] * inv, h[m][1][r] * inv);
-            const float2 dv = dec_e4m3x2(cc);
-            const float sum = group_sum<16>(dv.x + dv.y);
-            if (c16 == 0)
-                s_sum[wn * kTBM + row] = sum;
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                // int4 down GEMM: the interleaved operand order; fp4: natural K order
-                const int il = 32 * wn + 16 * j + c16;
-                const int b = il & 7;
-                const int pos = FP4 ? il : fp8_group_pos(il >> 3) + ((b & 1) ? 4 + (b >> 1) : (b >> 1));
-                s_q[row * kGroup + pos] = (uint8_t)((cc >> (8 * j)) & 0xFFu);
-            }
+            const float sc = a.requant_scale ? *a.requant_scale : scale_of(clamp_amax(mx));
+            a.out_side[(int64_t)(row0 + row) * GI + nb] = make_float2(512.0f * sc, -8.0f * (sc * sum));
         }
-    __syncthreads();
-    const int64_t GI = a.I / kGroup;
-    for (int i = tid; i < kTBM * 8; i += kTThreads) {
-        const int row = i >> 3, chunk = i & 7;
-        if (row < rows)
-            *(v4i*)(a.out_q + (int64_t)(row0 + row) * a.I + (int64_t)nb * kGroup + chunk * 16) =
-                *(const v4i*)(s_q + row * kGroup + chunk * 16);
-    }
-    if (tid < kTBM && tid < rows) {
-        const int row = tid;
-        const float sum = s_sum[row] + s_sum[kTBM + row] + s_sum[2 * kTBM + row] + s_sum[3 * kTBM + row];
-        const float mx = fmaxf(fmaxf(s_red[row], s_red[kTBM + row]),
-                               fmaxf(s_red[2 * kTBM + row], s_red[3 * kTBM + row]));
-        const float sc = a.requant_scale ? *a.requant_scale : scale_of(clamp_amax(mx));
-        a.out_side[(int64_t)(row0 + row) * GI + nb] = make_float2(512.0f * sc, -8.0f * (sc * sum));
+    };
+    static_assert(kSlices == 5, "one K-loop instance per slice count 0..5");
+    switch (nsl) {
+    case 0: kloop(std::integral_constant<int, 0>{}); break;
+    case 1: kloop(std::integral_constant<int, 1>{}); break;
+    case 2: kloop(std::integral_constant<int, 2>{}); break;
+    case 3: kloop(std::integral_constant<int, 3>{}); break;
+    case 4: kloop(std::integral_constant<int, 4>{}); break;
+    default: kloop(std::integral_constant<int, 5>{}); break;
     }
 }
 
@@ -656,15 +676,6 @@ __device__ __forceinline__ void down_stream(const GemmArgs& a, uint8_t* smem, in
         s23 = sd[1];
     };
 
-    float acc[kSlices][4][4];
-#pragma unroll
-    for (int m = 0; m < kSlices; ++m)
-#pragma unroll
-        for (int f = 0; f < 4; ++f)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                acc[m][f][r] = 0;
-
     Ctx cur = make_ctx(0);
     bool has_nxt = nt > 1;
     Ctx nxt = make_ctx(has_nxt ? 1 : 0);
@@ -677,93 +688,122 @@ __device__ __forceinline__ void down_stream(const GemmArgs& a, uint8_t* smem, in
     issue(cur, kStages - 1, kStages - 1);
 
     bool idle = kHalf * wm >= cur.rows;  // this wave's row half of the tile is empty
-    v4i wb[4], a0 = {}, a1 = {};
-    float sw[4];
-    float4 s01 = {}, s23 = {};
-    read_b(smem, wb, sw);
-    read_a(smem, 0, a0, a1);
-    read_side(smem, 0, s01, s23);
 
     int base = 0;  // stream position of the current tile's group 0
     for (int k = 0;;) {
-        for (int g = 0; g < G; ++g) {
-            const uint8_t* sp = smem + ((base + g) & 3) * kStageBytes;
-            if (!idle) {
-                int eq[4];
-                float swc[4];
-                v8i b8[4];
+        // the tile's K loop and epilogue for a wave that computes NSL of its
+        // half's 16-row slices (as in tile_body: one instance per count,
+        // chosen once per tile, the compute behind a run-time test too)
+        const int nsl = min(kSlices, max(0, (cur.rows - kHalf * wm + 15) / 16));
+        auto pass = [&](auto nsl_c) {
+            constexpr int NSL = decltype(nsl_c)::value;
+            float acc[NSL > 0 ? NSL : 1][4][4];
 #pragma unroll
-                for (int f = 0; f < 4; ++f) {
-                    if (FP4) {
-                        eq[f] = (int)((__builtin_bit_cast(uint32_t, sw[f]) >> (8 * q)) & 0xFFu);
-                    } else {
-                        swc[f] = sw[f];
-                        b8[f] = unpack_int4_u(wb[f]);
+            for (int m = 0; m < NSL; ++m)
+#pragma unroll
+                for (int f = 0; f < 4; ++f)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        acc[m][f][r] = 0;
+            // group 0's fragments (read here rather than at the end of the
+            // previous tile, so that no fragment register lives across the
+            // choice of instance)
+            v4i wb[4], a0 = {}, a1 = {};
+            float sw[4];
+            float4 s01 = {}, s23 = {};
+            if (NSL > 0 && !idle) {
+                const uint8_t* np = smem + (base & 3) * kStageBytes;
+                read_b(np, wb, sw);
+                read_a(np, 0, a0, a1);
+                read_side(np, 0, s01, s23);
+            }
+            for (int g = 0; g < G; ++g) {
+                const uint8_t* sp = smem + ((base + g) & 3) * kStageBytes;
+                if (NSL > 0 && !idle) {
+                    int eq[4];
+                    float swc[4];
+                    v8i b8[4];
+#pragma unroll
+                    for (int f = 0; f < 4; ++f) {
+                        if (FP4) {
+                            eq[f] = (int)((__builtin_bit_cast(uint32_t, sw[f]) >> (8 * q)) & 0xFFu);
+                        } else {
+                            swc[f] = sw[f];
+                            b8[f] = unpack_int4_u(wb[f]);
+                        }
+                    }
+#pragma unroll
+                    for (int m = 0; m < NSL; ++m) {
+                        const v4i ca0 = a0, ca1 = a1;
+                        const float4 cs01 = s01, cs23 = s23;
+                        if (m + 1 < NSL) {
+                            read_a(sp, m + 1, a0, a1);
+                            read_side(sp, m + 1, s01, s23);
+                        }
+                        const v8i av = {ca0[0], ca0[1], ca0[2], ca0[3], ca1[0], ca1[1], ca1[2], ca1[3]};
+                        v4f raw[4];
+#pragma unroll
+                        for (int f = 0; f < 4; ++f)
+                            raw[f] = FP4 ? mfma16x16x128_fp4(av, wb[f], eq[f])
+                                         : mfma16x16x128(av, b8[f], v4f{0.0f, 0.0f, 0.0f, 0.0f});
+                        const float c1[4] = {cs01.x, cs01.z, cs23.x, cs23.z};
+                        const float c0[4] = {cs01.y, cs01.w, cs23.y, cs23.w};
+#pragma unroll
+                        for (int f = 0; f < 4; ++f)
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) {
+                                if (FP4)  // weight scales inside raw: y += sa * raw
+                                    acc[m][f][r] = fmaf(raw[f][r], c1[r] * 0x1p-9f, acc[m][f][r]);
+                                else
+                                    acc[m][f][r] = fmaf(swc[f], fmaf(raw[f][r], c1[r], c0[r]), acc[m][f][r]);
+                            }
                     }
                 }
-#pragma unroll
-                for (int m = 0; m < kSlices; ++m) {
-                    const v4i ca0 = a0, ca1 = a1;
-                    const float4 cs01 = s01, cs23 = s23;
-                    if (m + 1 < kSlices) {
-                        read_a(sp, m + 1, a0, a1);
-                        read_side(sp, m + 1, s01, s23);
+                if (g + 1 < G) {
+                    // position g + 1 landed for everyone; the stage of group g is
+                    // free: refill it with position base + g + 4 (the next tile's
+                    // first groups once this tile's are all issued)
+                    wait_behind(min(2, G - 2 - g + (has_nxt ? G : 0)));
+                    barrier();
+                    const int p = g + kStages;
+                    if (p < G)
+                        issue(cur, p, (base + g) & 3);
+                    else if (has_nxt)
+                        issue(nxt, p - G, (base + g) & 3);
+                    const uint8_t* np = smem + ((base + g + 1) & 3) * kStageBytes;
+                    if (NSL > 0 && !idle) {
+                        read_b(np, wb, sw);
+                        read_a(np, 0, a0, a1);
+                        read_side(np, 0, s01, s23);
                     }
-                    const v8i av = {ca0[0], ca0[1], ca0[2], ca0[3], ca1[0], ca1[1], ca1[2], ca1[3]};
-                    v4f raw[4];
+                }
+            }
+            // epilogue: element (tile row 80wm + 16m + 4q + r, fragment f); the
+            // next tile's groups 0..2 are in flight meanwhile
+            if (NSL > 0 && !idle) {
 #pragma unroll
-                    for (int f = 0; f < 4; ++f)
-                        raw[f] = FP4 ? mfma16x16x128_fp4(av, wb[f], eq[f])
-                                     : mfma16x16x128(av, b8[f], v4f{0.0f, 0.0f, 0.0f, 0.0f});
-                    const float c1[4] = {cs01.x, cs01.z, cs23.x, cs23.z};
-                    const float c0[4] = {cs01.y, cs01.w, cs23.y, cs23.w};
+                for (int f = 0; f < 4; ++f) {
+                    const int64_t n = (int64_t)cur.nb * kTBN + wrow_f[f];
+                    if (n >= N)
+                        continue;
 #pragma unroll
-                    for (int f = 0; f < 4; ++f)
+                    for (int m = 0; m < NSL; ++m)
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
-                            if (FP4)  // weight scales inside raw: y += sa * raw
-                                acc[m][f][r] = fmaf(raw[f][r], c1[r] * 0x1p-9f, acc[m][f][r]);
-                            else
-                                acc[m][f][r] = fmaf(swc[f], fmaf(raw[f][r], c1[r], c0[r]), acc[m][f][r]);
+                            const int row = kHalf * wm + 16 * m + 4 * q + r;
+                            if (row < cur.rows)
+                                a.out_f32[(int64_t)(cur.row0 + row) * N + n] = acc[m][f][r];
                         }
                 }
             }
-            if (g + 1 < G) {
-                // position g + 1 landed for everyone; the stage of group g is
-                // free: refill it with position base + g + 4 (the next tile's
-                // first groups once this tile's are all issued)
-                wait_behind(min(2, G - 2 - g + (has_nxt ? G : 0)));
-                barrier();
-                const int p = g + kStages;
-                if (p < G)
-                    issue(cur, p, (base + g) & 3);
-                else if (has_nxt)
-                    issue(nxt, p - G, (base + g) & 3);
-                const uint8_t* np = smem + ((base + g + 1) & 3) * kStageBytes;
-                if (!idle) {
-                    read_b(np, wb, sw);
-                    read_a(np, 0, a0, a1);
-                    read_side(np, 0, s01, s23);
-                }
-            }
-        }
-        // epilogue: element (tile row 80wm + 16m + 4q + r, fragment f); the
-        // next tile's groups 0..2 are in flight meanwhile
-        if (!idle) {
-#pragma unroll
-            for (int f = 0; f < 4; ++f) {
-                const int64_t n = (int64_t)cur.nb * kTBN + wrow_f[f];
-                if (n >= N)
-                    continue;
-#pragma unroll
-                for (int m = 0; m < kSlices; ++m)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int row = kHalf * wm + 16 * m + 4 * q + r;
-                        if (row < cur.rows)
-                            a.out_f32[(int64_t)(cur.row0 + row) * N + n] = acc[m][f][r];
-                    }
-            }
+        };
+        switch (nsl) {
+        case 0: pass(std::integral_constant<int, 0>{}); break;
+        case 1: pass(std::integral_constant<int, 1>{}); break;
+        case 2: pass(std::integral_constant<int, 2>{}); break;
+        case 3: pass(std::integral_constant<int, 3>{}); break;
+        case 4: pass(std::integral_constant<int, 4>{}); break;
+        default: pass(std::integral_constant<int, 5>{}); break;
         }
         if (!has_nxt)
             break;
@@ -775,13 +815,6 @@ __device__ __forceinline__ void down_stream(const GemmArgs& a, uint8_t* smem, in
         wait_vmcnt<0>();
         barrier();
         issue(nxt, kStages - 1, (base + G - 1) & 3);
-#pragma unroll
-        for (int m = 0; m < kSlices; ++m)
-#pragma unroll
-            for (int f = 0; f < 4; ++f)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    acc[m][f][r] = 0;
         base += G;
         ++k;
         cur = nxt;
@@ -789,12 +822,6 @@ __device__ __forceinline__ void down_stream(const GemmArgs& a, uint8_t* smem, in
         has_nxt = k + 1 < nt;
         if (has_nxt)
             nxt = make_ctx(k + 1);
-        if (!idle) {
-            const uint8_t* np = smem + (base & 3) * kStageBytes;
-            read_b(np, wb, sw);
-            read_a(np, 0, a0, a1);
-            read_side(np, 0, s01, s23);
-        }
     }
 }
 
@@ -828,19 +855,24 @@ __global__ __launch_bounds__(kTThreads) void gemm_down_stream_kernel(GemmArgs a)
     }
 }
 
-hipError_t launch_gemm_tile(const GemmArgs& a, int mode, hipStream_t s)
+int64_t tile_launch_workgroups(int64_t tiles)
 {
-    const int64_t nbn = mode == TILE_GATEUP ? a.I / kGroup : (a.N + kTBN - 1) / kTBN;
-    const int64_t tiles = nbn * a.max_blocks;
-    if (tiles == 0)
-        return hipSuccess;
     // one workgroup per CU (the LDS stages allow no more), a multiple of the 8 XCDs
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 8)
         cus = 256;
     const int64_t wgs = tiles < cus ? tiles : cus;
-    const dim3 grid((unsigned)((wgs + 7) / 8 * 8));
+    return (wgs + 7) / 8 * 8;
+}
+
+hipError_t launch_gemm_tile(const GemmArgs& a, int mode, hipStream_t s)
+{
+    const int64_t nbn = mode == TILE_GATEUP ? a.I / kGroup : (a.N + kTBN - 1) / kTBN;
+    const int64_t tiles = nbn * a.max_blocks;
+    if (tiles == 0)
+        return hipSuccess;
+    const dim3 grid((unsigned)tile_launch_workgroups(tiles));
     if ((a.fp4 && !a.packed) || a.sub_group != 128)
         return hipErrorInvalidValue;  // the finer activation recipes run on the skinny kernel
     const dim3 block(kTThreads);

@@ -20,18 +20,19 @@ hipError_t launch_quant_bf16(const uint16_t* x, int64_t M, int64_t K, int64_t ld
 
 // ---- routing permutation (align.hip) ----
 // Predicted time (us) of the two GEMMs of one fused call on either path, from
-// the m-block counts the align finds (constants set on the host):
-//   skinny: (blocks of both lists) * skinny_block_us (every m-block streams
-//           one expert's gate_up and down weights);
-//   tiled:  ceil(tiles_gu * nb / cus) * groups_gu * (gu0 + gu1 * rows)
-//         +      tiles_dn * nb / cus  * groups_dn * (dn0 + dn1 * rows),
-// nb = kTileRows-row m-blocks, rows = pairs / nb (real rows per m-block).
+// the per-expert counts the align finds (constants set on the host):
+//   skinny: skinny_fixed_us + (m-blocks of both lists) * skinny_block_us
+//           (every m-block streams one expert's gate_up and down weights);
+//   tiled:  for each of the two tile launches, the slowest workgroup's sum
+//           over the tiles it walks (the launchers' static tile order) of
+//           groups * (c0 + c1 * rows computed), a tile's rows rounded up to
+//           16-row slices in each 80-row half.
 struct PathCost {
-    float skinny_block_us;
-    float tiles_gu, tiles_dn;    // tiles per m-block (gate_up, down)
+    float skinny_fixed_us, skinny_block_us;
     float groups_gu, groups_dn;  // 128-K groups per tile
-    float gu0, gu1, dn0, dn1;    // us per group of one tile: constant + per real row
-    float cus;
+    int32_t nbn_gu, nbn_dn;      // tiles per m-block
+    int32_t wgs_gu, wgs_dn;      // workgroups of the two tile launches
+    float gu0, gu1, dn0, dn1;    // us per group of one tile: constant + per computed row
 };
 struct AlignOut {
     int32_t* counts;        // [E]
@@ -158,6 +159,9 @@ hipError_t launch_split_reduce(const float* part, int32_t splits, int64_t M, int
 constexpr int kTileRows = 160;
 enum TileMode { TILE_DOWN = 0, TILE_GATEUP = 1 };
 hipError_t launch_gemm_tile(const GemmArgs& a, int mode, hipStream_t s);
+// workgroups launch_gemm_tile starts for `tiles` tiles (at most one per CU,
+// a multiple of the 8 XCDs)
+int64_t tile_launch_workgroups(int64_t tiles);
 
 // ---- weight prepack (prepack.hip) ----
 // [E, N, K/2] int4 + [E, N, K/128] fp32 or bf16 scales (or fp4 + [E, N, K/32]
