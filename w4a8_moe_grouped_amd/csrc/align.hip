@@ -134,45 +134,71 @@ __device__ __forceinline__ float tile_rows16(int r)
 
 // Predicted us of the slowest workgroup of one block-tiled launch: nb
 // m-blocks (bstart [E] their exclusive prefix per expert, off [E] the
-// experts' first rows, P rows in all), nbn tiles per m-block, wgs
-// workgroups walking the tiles in the launchers' order (tile L = expert
-// major, then weight block, m-block fastest; XCD x = w % 8 takes the x-th
-// eighth, its workgroups every (wgs / 8)-th tile of it).  red: 1 int of LDS.
+// experts' first rows, P rows in all), nbn tiles per m-block, wgs <=
+// kAlignThreads workgroups walking the tiles in the launchers' order (tile L
+// = expert major, then weight block, m-block fastest; XCD x = w % 8 takes
+// the x-th eighth, its workgroups every (wgs / 8)-th tile of it).  Each
+// expert's tiles are split over threads, which add every tile's cost to its
+// workgroup's sum in LDS (wg_cost, kAlignThreads floats; red: 1 int of LDS).
 // All threads call it.
 __device__ float tiled_launch_us(const int* bstart, const int* off, int P, int64_t E, int nb, int nbn,
-                                 int wgs, float groups, float c0, float c1, int* red)
+                                 int wgs, float groups, float c0, float c1, float* wg_cost, int* red)
 {
+    const int t = threadIdx.x;
     const int total = nb * nbn;
     const int per_xcd = (total + 7) >> 3;
     const int stride = wgs >> 3;
-    float tmax = 0.0f;
-    for (int w = threadIdx.x; w < wgs; w += kAlignThreads) {
-        const int x = w & 7;
-        float tw = 0.0f;
-        for (int t = w >> 3; t < per_xcd; t += stride) {
-            const int L = x * per_xcd + t;
-            if (L >= total)
-                break;
-            int lo = 0, hi = (int)E;  // the largest e with bstart[e] * nbn <= L
-            while (hi - lo > 1) {
-                const int mid = (lo + hi) >> 1;
-                if (bstart[mid] * nbn <= L)
-                    lo = mid;
-                else
-                    hi = mid;
-            }
-            const int bs = bstart[lo];
-            const int nbe = (lo + 1 < E ? bstart[lo + 1] : nb) - bs;
-            const int mb = (L - bs * nbn) % nbe;
-            const int c = (lo + 1 < E ? off[lo + 1] : P) - off[lo];
-            tw += groups * (c0 + c1 * tile_rows16(min(kTileRows, c - kTileRows * mb)));
-        }
-        tmax = fmaxf(tmax, tw);
-    }
-    if (threadIdx.x == 0)
+    if (t < kAlignThreads)
+        wg_cost[t] = 0.0f;
+    if (t == 0)
         *red = 0;
     __syncthreads();
-    atomicMax(red, __float_as_int(tmax));  // non-negative floats order like their bits
+    const int parts = E < kAlignThreads ? kAlignThreads / (int)E : 1;  // threads per expert
+    for (int i = t; i < E * parts; i += kAlignThreads) {
+        const int e = i / parts, part = i - e * parts;
+        const int bs = bstart[e];
+        const int nbe = (e + 1 < E ? bstart[e + 1] : nb) - bs;
+        if (nbe == 0)
+            continue;
+        const int c = (e + 1 < E ? off[e + 1] : P) - off[e];
+        const float full = groups * (c0 + c1 * tile_rows16(kTileRows));
+        const float last = groups * (c0 + c1 * tile_rows16(c - kTileRows * (nbe - 1)));
+        const int n = nbe * nbn;
+        if (part >= n)
+            continue;
+        // tile L = bs * nbn + j (j = part, part + parts, ...): its XCD x, its
+        // place tx in that XCD's range and its workgroup's slot tm = tx %
+        // stride, and its m-block mb = j % nbe, all stepped without a
+        // division per tile (the block runs one wave per SIMD, so a division
+        // chain per tile would sit on the align's critical path)
+        const int L = bs * nbn + part;
+        int x = L / per_xcd, tx = L - x * per_xcd, tm = tx % stride, mb = part % nbe;
+        const int step_t = parts % stride, step_m = parts % nbe;
+        for (int j = part;;) {
+            atomicAdd(&wg_cost[(tm << 3) | x], mb == nbe - 1 ? last : full);
+            j += parts;
+            if (j >= n)
+                break;
+            mb += step_m;
+            if (mb >= nbe)
+                mb -= nbe;
+            tx += parts;
+            if (tx >= per_xcd) {
+                while (tx >= per_xcd) {
+                    tx -= per_xcd;
+                    ++x;
+                }
+                tm = tx % stride;
+            } else {
+                tm += step_t;
+                if (tm >= stride)
+                    tm -= stride;
+            }
+        }
+    }
+    __syncthreads();
+    if (t < wgs)
+        atomicMax(red, __float_as_int(wg_cost[t]));  // non-negative floats order like their bits
     __syncthreads();
     const float r = __int_as_float(*red);
     __syncthreads();
@@ -180,20 +206,20 @@ __device__ float tiled_launch_us(const int* bstart, const int* off, int P, int64
 }
 
 // Predicted us of the two GEMMs on the block-tiled path minus the skinny one
-// (see PathCost): < 0 picks the block-tiled kernels.  bstart / off: LDS, as
-// in tiled_launch_us.  All threads call it.
+// (see PathCost): < 0 picks the block-tiled kernels.  bstart / off /
+// wg_cost: LDS, as in tiled_launch_us.  All threads call it.
 __device__ float tiled_minus_skinny(const PathCost& c, const int* bstart, const int* off, int P,
-                                    int64_t E, int nb_skinny, int nb_tiled, int* red)
+                                    int64_t E, int nb_skinny, int nb_tiled, float* wg_cost, int* red)
 {
     const float gu = tiled_launch_us(bstart, off, P, E, nb_tiled, c.nbn_gu, c.wgs_gu, c.groups_gu,
-                                     c.gu0, c.gu1, red);
+                                     c.gu0, c.gu1, wg_cost, red);
     const float dn = tiled_launch_us(bstart, off, P, E, nb_tiled, c.nbn_dn, c.wgs_dn, c.groups_dn,
-                                     c.dn0, c.dn1, red);
+                                     c.dn0, c.dn1, wg_cost, red);
     return gu + dn - (c.skinny_fixed_us + (float)nb_skinny * c.skinny_block_us);
 }
 
 __device__ bool finish_scan(int* counts_lds, int* tmp_lds, int* tmp2_lds, int* tmp3_lds, int* scratch,
-                            int64_t E, int64_t block_m, const AlignOut& o)
+                            float* wg_cost, int64_t E, int64_t block_m, const AlignOut& o)
 {
     const int t = threadIdx.x;
     const bool dual = o.block_expert2 != nullptr;
@@ -215,7 +241,7 @@ __device__ bool finish_scan(int* counts_lds, int* tmp_lds, int* tmp2_lds, int* t
     // (the scans leave the exclusive prefixes in counts_lds and tmp3_lds)
     const int path = !choose ? o.static_path
                      : over  ? 0
-                             : (tiled_minus_skinny(o.cost, tmp3_lds, counts_lds, P, E, nb + nb2, nb3, scratch) < 0.0f
+                             : (tiled_minus_skinny(o.cost, tmp3_lds, counts_lds, P, E, nb + nb2, nb3, wg_cost, scratch) < 0.0f
                                     ? 1 : 0);
     // block_start belongs to the list the block-tiled kernels read
     const int* bs_lds = choose ? tmp3_lds : tmp_lds;
@@ -327,6 +353,7 @@ struct AlignLds {
     int b[kMaxLocalExperts];
     int c[kMaxLocalExperts];
     int d[kMaxLocalExperts];
+    float wg_cost[kAlignThreads];
     int wcnt[kAlignWaves * kMaxLocalExperts];
     int scratch[kAlignWaves + 1];
 };
@@ -339,33 +366,82 @@ size_t align_mask_bytes(int64_t E)
     return (size_t)kAlignWaves * (size_t)E * sizeof(unsigned long long);
 }
 
-// everything in one block (F <= kAlignSingle)
+// everything in one block (F <= kAlignSingle).  Wave w owns the pairs
+// [w * seg, (w + 1) * seg) in 64-lane rounds, so f order is (wave, round,
+// lane) order and a pair's place among the pairs of its expert is: the
+// expert's offset + the expert's pairs in earlier waves + in this wave's
+// earlier rounds + its rank in its round.  The waves count their own
+// pairs per expert without any barrier (a wave's LDS operations complete in
+// order); one barrier then joins the counts, and the scan and the per-wave
+// bases follow before each lane writes its pairs.
 __device__ __forceinline__ void align_single_body(const int32_t* __restrict__ ids, int64_t F,
                                                   int64_t eb, int64_t E, int64_t block_m,
                                                   const AlignOut& o, AlignLds& L)
 {
-    const int t = threadIdx.x;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int64_t seg = ((F + kAlignWaves - 1) / kAlignWaves + 63) / 64 * 64;  // <= 1024
+    const int64_t f0 = wave * seg;
     int keys[kSingleRounds];
-    load_keys(ids, 0, F, eb, E, keys);
-    for (int e = t; e < E; e += kAlignThreads)
-        L.a[e] = 0;
+#pragma unroll
+    for (int r = 0; r < kSingleRounds; ++r) {
+        const int64_t f = f0 + r * 64 + lane;
+        keys[r] = (r * 64 < seg) ? local_id(ids, f, F, eb, E) : -1;
+    }
     for (int i = t; i < kAlignWaves * E; i += kAlignThreads) {
         L.wcnt[i] = 0;
         align_masks[i] = 0ull;
     }
     __syncthreads();
+    // this wave's pairs per expert, and each lane's place among them
+    int* cnt = L.wcnt + wave * E;
+    int pos[kSingleRounds];
 #pragma unroll
-    for (int r = 0; r < kSingleRounds; ++r)
-        if (keys[r] >= 0)
-            atomicAdd(&L.a[keys[r]], 1);
+    for (int r = 0; r < kSingleRounds; ++r) {
+        pos[r] = 0;
+        if (r * 64 >= seg)
+            break;
+        int rank, count;
+        wave_rank(keys[r], align_masks + wave * E, rank, count);
+        if (keys[r] >= 0) {
+            pos[r] = cnt[keys[r]] + rank;
+            if (rank == 0)
+                cnt[keys[r]] += count;  // after every lane's read: in order
+        }
+    }
+    __syncthreads();
+    for (int e = t; e < E; e += kAlignThreads) {
+        int c = 0;
+        for (int w = 0; w < kAlignWaves; ++w)
+            c += L.wcnt[w * E + e];
+        L.a[e] = c;
+    }
     __syncthreads();
     // L.a now holds the offsets
-    if (finish_scan(L.a, L.b, L.c, L.d, L.scratch, E, block_m, o)) {
-#pragma unroll
-        for (int r = 0; r < kSingleRounds; ++r)
-            keys[r] = -1;  // over capacity: no pair is placed, src2dst = -1
+    const bool over = finish_scan(L.a, L.b, L.c, L.d, L.scratch, L.wg_cost, E, block_m, o);
+    for (int e = t; e < E; e += kAlignThreads) {  // the waves' bases per expert
+        int run = L.a[e];
+        for (int w = 0; w < kAlignWaves; ++w) {
+            const int c = L.wcnt[w * E + e];
+            L.wcnt[w * E + e] = run;
+            run += c;
+        }
     }
-    scatter_chunk(keys, 0, F, E, L.a, L.wcnt, align_masks, o);
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kSingleRounds; ++r) {
+        if (r * 64 >= seg)
+            break;
+        const int64_t f = f0 + r * 64 + lane;
+        if (f >= F)
+            break;
+        if (keys[r] >= 0 && !over) {  // over capacity: no pair is placed, src2dst = -1
+            const int p = cnt[keys[r]] + pos[r];
+            o.sorted[p] = (int32_t)f;
+            o.src2dst[f] = p;
+        } else {
+            o.src2dst[f] = -1;
+        }
+    }
 }
 
 __global__ __launch_bounds__(kAlignThreads) void align_single_kernel(const int32_t* __restrict__ ids,
@@ -461,7 +537,7 @@ __global__ __launch_bounds__(kAlignThreads) void align_scan_kernel(int32_t* __re
         L.a[e] = run;
     }
     __syncthreads();
-    finish_scan(L.a, L.b, L.c, L.d, L.scratch, E, block_m, o);  // L.a now holds the experts' offsets
+    finish_scan(L.a, L.b, L.c, L.d, L.scratch, L.wg_cost, E, block_m, o);  // L.a now holds the experts' offsets
     for (int i = t; i < ng * E; i += kAlignThreads) {
         const int g = i / (int)E, e = i - g * (int)E;
         const int64_t c0 = g * cpg, c1 = c0 + cpg < nchunks ? c0 + cpg : nchunks;

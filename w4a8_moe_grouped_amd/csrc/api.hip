@@ -7,6 +7,7 @@
 
 #include "internal.hpp"
 
+#include <algorithm>
 #include <mutex>
 #include <stddef.h>
 #include <stdint.h>
@@ -122,8 +123,11 @@ w4a8::PathCost path_cost(int64_t H, int64_t I, int64_t nb3_max)
     c.groups_dn = (float)(I / W4A8_GROUP);
     c.nbn_gu = (int32_t)(I / W4A8_GROUP);
     c.nbn_dn = (int32_t)((H + 255) / 256);
-    c.wgs_gu = (int32_t)w4a8::tile_launch_workgroups(c.nbn_gu * nb3_max);
-    c.wgs_dn = (int32_t)w4a8::tile_launch_workgroups(c.nbn_dn * nb3_max);
+    // the align sums the cost of at most 256 workgroups per launch (one LDS
+    // slot per thread); a GPU with more CUs is modelled with 256
+    const int64_t wgs_cap = 256;
+    c.wgs_gu = (int32_t)std::min(w4a8::tile_launch_workgroups(c.nbn_gu * nb3_max), wgs_cap);
+    c.wgs_dn = (int32_t)std::min(w4a8::tile_launch_workgroups(c.nbn_dn * nb3_max), wgs_cap);
     c.gu0 = 0.815f;
     c.gu1 = 0.01327f;
     c.dn0 = 0.776f;
