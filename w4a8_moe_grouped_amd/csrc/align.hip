@@ -68,52 +68,65 @@ __device__ __forceinline__ void wave_rank(int key, unsigned long long* masks, in
     }
 }
 
-// block-wide exclusive scan of vals[0..n) in LDS (n <= 4 * kAlignThreads);
-// returns the total.  All threads must call it.
-__device__ int block_exclusive_scan(int* vals, int n, int* scratch /* >= kAlignWaves + 1 */)
+// The exclusive scans of up to four arrays of n values in LDS (n <= 4 *
+// kAlignThreads, a null array skipped) with one set of barriers; totals[i]
+// receives array i's total.  scratch: 4 * (kAlignWaves + 1) ints.  All
+// threads must call it.
+__device__ void block_exclusive_scan4(int* const (&vals)[4], int n, int* scratch, int (&totals)[4])
 {
     const int t = threadIdx.x;
     const int lane = t & 63, wave = t >> 6;
-    int local[4];
-    int sum = 0;
+    int local[4][4], sum[4], incl[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int idx = 4 * t + i;
-        local[i] = idx < n ? vals[idx] : 0;
-        sum += local[i];
-    }
-    // inclusive scan of the per-thread sums within the wave
-    int incl = sum;
+    for (int a = 0; a < 4; ++a) {
+        sum[a] = 0;
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(incl, o, 64);
-        if (lane >= o)
-            incl += y;
+        for (int i = 0; i < 4; ++i) {
+            const int idx = 4 * t + i;
+            local[a][i] = (vals[a] != nullptr && idx < n) ? vals[a][idx] : 0;
+            sum[a] += local[a][i];
+        }
+        incl[a] = sum[a];
     }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            const int y = __shfl_up(incl[a], o, 64);
+            if (lane >= o)
+                incl[a] += y;
+        }
     if (lane == 63)
-        scratch[wave] = incl;
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+            scratch[a * (kAlignWaves + 1) + wave] = incl[a];
     __syncthreads();
-    if (t == 0) {
+    if (t < 4) {
+        int* sc = scratch + t * (kAlignWaves + 1);
         int run = 0;
         for (int w = 0; w < kAlignWaves; ++w) {
-            const int c = scratch[w];
-            scratch[w] = run;
+            const int c = sc[w];
+            sc[w] = run;
             run += c;
         }
-        scratch[kAlignWaves] = run;
+        sc[kAlignWaves] = run;
     }
     __syncthreads();
-    int run = scratch[wave] + incl - sum;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int idx = 4 * t + i;
-        if (idx < n)
-            vals[idx] = run;
-        run += local[i];
+    for (int a = 0; a < 4; ++a) {
+        const int* sc = scratch + a * (kAlignWaves + 1);
+        int run = sc[wave] + incl[a] - sum[a];
+        if (vals[a] != nullptr)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int idx = 4 * t + i;
+                if (idx < n)
+                    vals[a][idx] = run;
+                run += local[a][i];
+            }
+        totals[a] = sc[kAlignWaves];
     }
-    const int total = scratch[kAlignWaves];
     __syncthreads();
-    return total;
 }
 
 // counts[] (LDS, E entries) -> offsets, counts and block list(s) in global
@@ -132,90 +145,104 @@ __device__ __forceinline__ float tile_rows16(int r)
     return 16.0f * (float)((h0 + 15) / 16 + (h1 + 15) / 16);
 }
 
-// Predicted us of the slowest workgroup of one block-tiled launch: nb
-// m-blocks (bstart [E] their exclusive prefix per expert, off [E] the
-// experts' first rows, P rows in all), nbn tiles per m-block, wgs <=
-// kAlignThreads workgroups walking the tiles in the launchers' order (tile L
-// = expert major, then weight block, m-block fastest; XCD x = w % 8 takes
-// the x-th eighth, its workgroups every (wgs / 8)-th tile of it).  Each
-// expert's tiles are split over threads, which add every tile's cost to its
-// workgroup's sum in LDS (wg_cost, kAlignThreads floats; red: 1 int of LDS).
-// All threads call it.
-__device__ float tiled_launch_us(const int* bstart, const int* off, int P, int64_t E, int nb, int nbn,
-                                 int wgs, float groups, float c0, float c1, float* wg_cost, int* red)
+// Predicted us of the slowest workgroup of each of the two block-tiled
+// launches (gate_up, down): nb m-blocks (bstart [E] their exclusive prefix
+// per expert, off [E] the experts' first rows, P rows in all); launch k has
+// nbn[k] tiles per m-block and wgs[k] <= kAlignThreads workgroups walking the
+// tiles in the launchers' order (tile L = expert major, then weight block,
+// m-block fastest; XCD x = w % 8 takes the x-th eighth, its workgroups every
+// (wgs / 8)-th tile of it).  Each expert's tiles are split over threads,
+// which add every tile's cost to its workgroup's sum in LDS (wg_cost: 2 x
+// kAlignThreads floats; red: 2 ints of LDS).  All threads call it.
+__device__ void tiled_launches_us(const PathCost& c, const int* bstart, const int* off, int P, int64_t E,
+                                  int nb, float* wg_cost, int* red, float (&us)[2])
 {
     const int t = threadIdx.x;
-    const int total = nb * nbn;
-    const int per_xcd = (total + 7) >> 3;
-    const int stride = wgs >> 3;
-    if (t < kAlignThreads)
-        wg_cost[t] = 0.0f;
-    if (t == 0)
-        *red = 0;
+    const int nbn[2] = {c.nbn_gu, c.nbn_dn}, wgs[2] = {c.wgs_gu, c.wgs_dn};
+    const float groups[2] = {c.groups_gu, c.groups_dn}, c0[2] = {c.gu0, c.dn0}, c1[2] = {c.gu1, c.dn1};
+    wg_cost[t] = 0.0f;
+    wg_cost[kAlignThreads + t] = 0.0f;
+    if (t < 2)
+        red[t] = 0;
     __syncthreads();
     const int parts = E < kAlignThreads ? kAlignThreads / (int)E : 1;  // threads per expert
     for (int i = t; i < E * parts; i += kAlignThreads) {
         const int e = i / parts, part = i - e * parts;
         const int bs = bstart[e];
         const int nbe = (e + 1 < E ? bstart[e + 1] : nb) - bs;
-        if (nbe == 0)
+        if (nbe == 0 || part >= nbe * max(nbn[0], nbn[1]))
             continue;
-        const int c = (e + 1 < E ? off[e + 1] : P) - off[e];
-        const float full = groups * (c0 + c1 * tile_rows16(kTileRows));
-        const float last = groups * (c0 + c1 * tile_rows16(c - kTileRows * (nbe - 1)));
-        const int n = nbe * nbn;
-        if (part >= n)
-            continue;
-        // tile L = bs * nbn + j (j = part, part + parts, ...): its XCD x, its
-        // place tx in that XCD's range and its workgroup's slot tm = tx %
-        // stride, and its m-block mb = j % nbe, all stepped without a
-        // division per tile (the block runs one wave per SIMD, so a division
-        // chain per tile would sit on the align's critical path)
-        const int L = bs * nbn + part;
-        int x = L / per_xcd, tx = L - x * per_xcd, tm = tx % stride, mb = part % nbe;
-        const int step_t = parts % stride, step_m = parts % nbe;
-        for (int j = part;;) {
-            atomicAdd(&wg_cost[(tm << 3) | x], mb == nbe - 1 ? last : full);
-            j += parts;
-            if (j >= n)
-                break;
-            mb += step_m;
-            if (mb >= nbe)
-                mb -= nbe;
-            tx += parts;
-            if (tx >= per_xcd) {
-                while (tx >= per_xcd) {
-                    tx -= per_xcd;
-                    ++x;
+        const int cnt = (e + 1 < E ? off[e + 1] : P) - off[e];
+        const float rows_full = tile_rows16(kTileRows);
+        const float rows_last = tile_rows16(cnt - kTileRows * (nbe - 1));
+        const int step_m = parts % nbe;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int n = nbe * nbn[k];
+            if (part >= n)
+                continue;
+            const int total = nb * nbn[k], per_xcd = (total + 7) >> 3, stride = wgs[k] >> 3;
+            const float full = groups[k] * (c0[k] + c1[k] * rows_full);
+            const float last = groups[k] * (c0[k] + c1[k] * rows_last);
+            float* acc = wg_cost + k * kAlignThreads;
+            // tile L = bs * nbn + j (j = part, part + parts, ...): its XCD x,
+            // its place tx in that XCD's range and its workgroup's slot tm =
+            // tx % stride, and its m-block mb = j % nbe, all stepped without a
+            // division per tile (the block runs one wave per SIMD, so a
+            // division chain per tile would sit on the align's critical path)
+            const int L = bs * nbn[k] + part;
+            int x = L / per_xcd, tx = L - x * per_xcd, tm = tx % stride, mb = part % nbe;
+            const int step_t = parts % stride;
+            for (int j = part;;) {
+                atomicAdd(&acc[(tm << 3) | x], mb == nbe - 1 ? last : full);
+                j += parts;
+                if (j >= n)
+                    break;
+                mb += step_m;
+                if (mb >= nbe)
+                    mb -= nbe;
+                tx += parts;
+                if (tx >= per_xcd) {
+                    while (tx >= per_xcd) {
+                        tx -= per_xcd;
+                        ++x;
+                    }
+                    tm = tx % stride;
+                } else {
+                    tm += step_t;
+                    if (tm >= stride)
+                        tm -= stride;
                 }
-                tm = tx % stride;
-            } else {
-                tm += step_t;
-                if (tm >= stride)
-                    tm -= stride;
             }
         }
     }
     __syncthreads();
-    if (t < wgs)
-        atomicMax(red, __float_as_int(wg_cost[t]));  // non-negative floats order like their bits
+    // the slowest workgroup of each launch: a max over the wave by shuffles,
+    // then over the waves (256 atomics on one LDS word measured ~2.5 us)
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        float m = t < wgs[k] ? wg_cost[k * kAlignThreads + t] : 0.0f;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1)
+            m = fmaxf(m, __shfl_xor(m, o, 64));
+        if ((t & 63) == 0)
+            atomicMax(&red[k], __float_as_int(m));  // non-negative floats order like their bits
+    }
     __syncthreads();
-    const float r = __int_as_float(*red);
+    us[0] = __int_as_float(red[0]);
+    us[1] = __int_as_float(red[1]);
     __syncthreads();
-    return r;
 }
 
 // Predicted us of the two GEMMs on the block-tiled path minus the skinny one
 // (see PathCost): < 0 picks the block-tiled kernels.  bstart / off /
-// wg_cost: LDS, as in tiled_launch_us.  All threads call it.
+// wg_cost / red: LDS, as in tiled_launches_us.  All threads call it.
 __device__ float tiled_minus_skinny(const PathCost& c, const int* bstart, const int* off, int P,
                                     int64_t E, int nb_skinny, int nb_tiled, float* wg_cost, int* red)
 {
-    const float gu = tiled_launch_us(bstart, off, P, E, nb_tiled, c.nbn_gu, c.wgs_gu, c.groups_gu,
-                                     c.gu0, c.gu1, wg_cost, red);
-    const float dn = tiled_launch_us(bstart, off, P, E, nb_tiled, c.nbn_dn, c.wgs_dn, c.groups_dn,
-                                     c.dn0, c.dn1, wg_cost, red);
-    return gu + dn - (c.skinny_fixed_us + (float)nb_skinny * c.skinny_block_us);
+    float us[2];
+    tiled_launches_us(c, bstart, off, P, E, nb_tiled, wg_cost, red, us);
+    return us[0] + us[1] - (c.skinny_fixed_us + (float)nb_skinny * c.skinny_block_us);
 }
 
 __device__ bool finish_scan(int* counts_lds, int* tmp_lds, int* tmp2_lds, int* tmp3_lds, int* scratch,
@@ -225,18 +252,17 @@ __device__ bool finish_scan(int* counts_lds, int* tmp_lds, int* tmp2_lds, int* t
     const bool dual = o.block_expert2 != nullptr;
     const bool choose = o.path != nullptr;  // also the kTileRows-row list
     for (int e = t; e < E; e += kAlignThreads) {
-        const int c = counts_lds[e];
-        o.counts[e] = c;
+        const int c = counts_lds[e];  // written out after the scans (no store pending at their barriers)
         const bool second = dual && c > o.small_rows;
         tmp_lds[e] = second ? 0 : (int)((c + block_m - 1) / block_m);  // m-blocks of expert e
         tmp2_lds[e] = second ? (c + o.block_m2 - 1) / o.block_m2 : 0;
         tmp3_lds[e] = choose ? (c + kTileRows - 1) / kTileRows : 0;
     }
     __syncthreads();
-    const int P = block_exclusive_scan(counts_lds, (int)E, scratch);
-    const int nb = block_exclusive_scan(tmp_lds, (int)E, scratch);
-    const int nb2 = dual ? block_exclusive_scan(tmp2_lds, (int)E, scratch) : 0;
-    const int nb3 = choose ? block_exclusive_scan(tmp3_lds, (int)E, scratch) : 0;
+    int tot[4];
+    int* const arrs[4] = {counts_lds, tmp_lds, dual ? tmp2_lds : nullptr, choose ? tmp3_lds : nullptr};
+    block_exclusive_scan4(arrs, (int)E, scratch, tot);
+    const int P = tot[0], nb = tot[1], nb2 = tot[2], nb3 = tot[3];
     const bool over = o.max_pairs > 0 && P > o.max_pairs;  // P is the same in every thread
     // (the scans leave the exclusive prefixes in counts_lds and tmp3_lds)
     const int path = !choose ? o.static_path
@@ -246,8 +272,10 @@ __device__ bool finish_scan(int* counts_lds, int* tmp_lds, int* tmp2_lds, int* t
     // block_start belongs to the list the block-tiled kernels read
     const int* bs_lds = choose ? tmp3_lds : tmp_lds;
     const int nbs = choose ? nb3 : nb;
-    for (int e = t; e < E; e += kAlignThreads)
+    for (int e = t; e < E; e += kAlignThreads) {
         o.offsets[e] = over ? 0 : counts_lds[e];
+        o.counts[e] = (e + 1 < E ? counts_lds[e + 1] : P) - counts_lds[e];
+    }
     if (t == 0) {
         o.offsets[E] = over ? 0 : P;
         *o.num_blocks = over ? 0 : nb;
@@ -298,14 +326,24 @@ __device__ bool finish_scan(int* counts_lds, int* tmp_lds, int* tmp2_lds, int* t
 }
 
 // the local ids of pairs f0 + r * kAlignThreads + t, r < R (-1 past f1),
-// loaded once: every round below uses registers
+// loaded once: every round below uses registers.  All R loads are issued
+// before any is used (addresses clamped into [f0, f1), f1 > f0).
 template <int R>
 __device__ __forceinline__ void load_keys(const int32_t* ids, int64_t f0, int64_t f1, int64_t eb,
                                           int64_t E, int (&keys)[R])
 {
+    int32_t raw[R];
 #pragma unroll
-    for (int r = 0; r < R; ++r)
-        keys[r] = local_id(ids, f0 + (int64_t)r * kAlignThreads + threadIdx.x, f1, eb, E);
+    for (int r = 0; r < R; ++r) {
+        const int64_t f = f0 + (int64_t)r * kAlignThreads + threadIdx.x;
+        raw[r] = ids[f < f1 ? f : f1 - 1];
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int64_t f = f0 + (int64_t)r * kAlignThreads + threadIdx.x;
+        const int64_t l = (int64_t)raw[r] - eb;
+        keys[r] = (f < f1 && l >= 0 && l < E) ? (int)l : -1;
+    }
 }
 
 // scatter one chunk [f0, f1) (at most R rounds of kAlignThreads pairs, keys
@@ -353,9 +391,9 @@ struct AlignLds {
     int b[kMaxLocalExperts];
     int c[kMaxLocalExperts];
     int d[kMaxLocalExperts];
-    float wg_cost[kAlignThreads];
+    float wg_cost[2 * kAlignThreads];
     int wcnt[kAlignWaves * kMaxLocalExperts];
-    int scratch[kAlignWaves + 1];
+    int scratch[4 * (kAlignWaves + 1)];
 };
 constexpr int kSingleRounds = kAlignSingle / kAlignThreads;  // 16
 constexpr int kChunkRounds = kAlignChunk / kAlignThreads;    // 4
@@ -381,11 +419,20 @@ __device__ __forceinline__ void align_single_body(const int32_t* __restrict__ id
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int64_t seg = ((F + kAlignWaves - 1) / kAlignWaves + 63) / 64 * 64;  // <= 1024
     const int64_t f0 = wave * seg;
+    // every load issued before any is used (a load per round behind a
+    // branch made them wait one by one: ~0.8 us per round)
+    int32_t raw[kSingleRounds];
+#pragma unroll
+    for (int r = 0; r < kSingleRounds; ++r) {
+        const int64_t f = f0 + r * 64 + lane;
+        raw[r] = ids[f < F ? f : F - 1];
+    }
     int keys[kSingleRounds];
 #pragma unroll
     for (int r = 0; r < kSingleRounds; ++r) {
         const int64_t f = f0 + r * 64 + lane;
-        keys[r] = (r * 64 < seg) ? local_id(ids, f, F, eb, E) : -1;
+        const int64_t l = (int64_t)raw[r] - eb;
+        keys[r] = (r * 64 < seg && f < F && l >= 0 && l < E) ? (int)l : -1;
     }
     for (int i = t; i < kAlignWaves * E; i += kAlignThreads) {
         L.wcnt[i] = 0;
