@@ -527,16 +527,17 @@ __global__ __launch_bounds__(kAlignThreads) void align_count_kernel(const int32_
 {
     __shared__ int cnt[kMaxLocalExperts];
     const int t = threadIdx.x;
+    const int64_t f0 = (int64_t)blockIdx.x * kAlignChunk;
+    const int64_t f1 = f0 + kAlignChunk < F ? f0 + kAlignChunk : F;
+    int keys[kChunkRounds];
+    load_keys(ids, f0, f1, eb, E, keys);  // the loads overlap the clearing below
     for (int e = t; e < E; e += kAlignThreads)
         cnt[e] = 0;
     __syncthreads();
-    const int64_t f0 = (int64_t)blockIdx.x * kAlignChunk;
-    const int64_t f1 = f0 + kAlignChunk < F ? f0 + kAlignChunk : F;
-    for (int64_t f = f0 + t; f < f1; f += kAlignThreads) {
-        const int key = local_id(ids, f, f1, eb, E);
-        if (key >= 0)
-            atomicAdd(&cnt[key], 1);
-    }
+#pragma unroll
+    for (int r = 0; r < kChunkRounds; ++r)
+        if (keys[r] >= 0)
+            atomicAdd(&cnt[keys[r]], 1);
     __syncthreads();
     for (int e = t; e < E; e += kAlignThreads)
         hist[(int64_t)blockIdx.x * E + e] = cnt[e];
