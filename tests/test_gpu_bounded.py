@@ -19,6 +19,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 from w4a8_moe_grouped_amd import lib as w4
 from w4a8_moe_grouped_amd import synth
 
@@ -188,3 +189,25 @@ def unbounded_with_workspace(d, cfg, dev, packed, ws):
     return w4.fused_moe(bf16_dev(d["hidden"], dev), dput(d["topk_ids"], dev),
                         dput(d["topk_weights"], dev), cfg.expert_begin, cfg.E_local, *shapes,
                         workspace=ws, prepacked=packed)
+
+
+@pytest.mark.parametrize("fmt,E_total,routing,want", [
+    (w4.WEIGHTS_FP4_PACKED, 32, "uniform", 1),   # fp4 weights, ~128 rows per expert: tiled
+    (w4.WEIGHTS_FP4_PACKED, 256, "zipf_id", 0),  # fp4 weights, skewed: skinny
+    (w4.WEIGHTS_INT4, 32, "uniform", 1),         # canonical int4 layout on the tiled kernels
+])
+def test_device_path_choice_weight_formats(dev, fmt, E_total, routing, want):
+    """The device-chosen path with the other weight formats, bounded by the
+    exact local pair count, against the oracle of the same format."""
+    T = 512 if routing == "uniform" else 256
+    gen = synth.random_moe_fp4 if fmt == w4.WEIGHTS_FP4_PACKED else synth.random_moe
+    cfg, d = gen(T, 7168, 2048, E_total, 8, 0, 32, seed=106, routing=routing)
+    P = local_pairs_of(cfg, d)
+    print("device path, format %d: T=%d E=%d %s P=%d" % (fmt, T, E_total, routing, P), flush=True)
+    ws = weights(d, dev, fmt)
+    got, n = bounded(d, cfg, dev, fmt, ws, P)
+    assert n == P and bounded.last_path == want
+    rows = first_last_tokens(cfg, d)
+    fn = oracle.fused_moe_fp4 if fmt == w4.WEIGHTS_FP4_PACKED else None
+    ref = oracle_rows_parallel(d, cfg, rows, fn=fn)
+    assert_bf16_close(bf16_host(got)[rows], ref, "format %d %s path %d (%d tokens)" % (fmt, routing, want, rows.size))
