@@ -444,8 +444,8 @@ int w4a8_fused_moe_workspace_layout(int64_t T, int64_t H, int64_t topk,
  * Arms the NEXT w4a8_fused_moe call made on the calling host thread to
  * record events[i] (hipEvent_t handles created by the caller) on its stream:
  *   [0] before align  [1] after align  [2] after the input quantisation
- *   (with T*topk <= 4096 align and quantisation are one launch, so [1] and
- *   [2] are both recorded after it)
+ *   (the quantisation runs inside the align's launches, so [1] and [2] are
+ *   both recorded after them)
  *   [3] after gate_up+SwiGLU+requant   [4] after down  [5] after combine
  * A null entry is skipped (so a caller can time one stage with two events).
  * n must be 6 (or 0 to disarm).  The six handles are copied, so the array

@@ -511,15 +511,14 @@ int fused_moe_run(const void* hidden_bf16, int64_t T, int64_t H, const int32_t* 
             return W4A8_ERR_HIP;
         mark(ev, 1, stream);
     } else {
+        // many pairs: the quantisation's blocks ride along with the align's
+        // count and scatter launches (both stage events after them)
+        const w4a8::QuantJob qj = {(const uint16_t*)hidden_bf16, T, H, H, p.qa, p.qa_side, a1_scale};
         e = w4a8::launch_align(topk_ids, T, topk, expert_begin, E, p.block_m, p.al, p.align_ws,
-                               stream);
+                               stream, qj);
         if (e != hipSuccess)
             return W4A8_ERR_HIP;
         mark(ev, 1, stream);
-        e = w4a8::launch_quant_bf16((const uint16_t*)hidden_bf16, T, H, H, p.qa, nullptr,
-                                    p.qa_side, 1, a1_scale, stream);
-        if (e != hipSuccess)
-            return W4A8_ERR_HIP;
     }
     mark(ev, 2, stream);
 

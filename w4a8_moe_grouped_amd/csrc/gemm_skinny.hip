@@ -278,7 +278,11 @@ __device__ __forceinline__ void skinny_body(const GemmArgs& a, const int by, con
         }
 #pragma unroll
         for (int f = 0; f < kNF; ++f) {
-            wb[s][f] = bload16_nt(rw, vw[f], (uint32_t)g * (PK ? 1024u : 64u));
+            // prepacked: a group's 1 KB per fragment is contiguous, streamed
+            // with the non-temporal policy; canonical rows: each lane's 16 B
+            // lies in a 128-byte line shared with the next group, which
+            // default loads keep in L2 for it (decode 187.7 -> 172.3 us per call)
+            wb[s][f] = PK ? bload16_nt(rw, vw[f], (uint32_t)g * 1024u) : bload16(rw, vw[f], (uint32_t)g * 64u);
             if (!SW4)
                 sb[s][f] = bload4f(rs, vs[f], PK ? (uint32_t)(g >> 2) * 256u + (uint32_t)(g & 3) * 4u
                                                   : (uint32_t)g * 4u);

@@ -71,8 +71,19 @@ struct AlignOut {
 };
 int64_t align_chunk_count(int64_t F);
 size_t align_workspace_bytes(int64_t F, int64_t E);
+// The mode-1 quantisation of x [M, K] (row stride ldx) riding along with
+// the chunked align: its blocks of 16 x 128 values are split between the
+// count and the scatter launch (x == null: none).
+struct QuantJob {
+    const uint16_t* x;
+    int64_t M, K, ldx;
+    uint8_t* q;
+    float2* side;
+    const float* fixed_scale;
+};
 hipError_t launch_align(const int32_t* ids, int64_t T, int64_t topk, int64_t expert_begin,
-                        int64_t E, int64_t block_m, const AlignOut& o, void* ws, hipStream_t s);
+                        int64_t E, int64_t block_m, const AlignOut& o, void* ws, hipStream_t s,
+                        const QuantJob& qj = QuantJob{});
 // align (single chunk: align_chunk_count(T*topk) == 1) and the mode-1
 // quantisation of x [T, H] in one launch; also zeroes clear[0, nclear)
 hipError_t launch_align_quant(const int32_t* ids, int64_t T, int64_t topk, int64_t expert_begin,
