@@ -501,19 +501,16 @@ __global__ __launch_bounds__(kAlignThreads) void align_single_kernel(const int32
 }
 
 // The routing permutation and the activation quantisation are independent:
-// one launch does both.  Block 0 runs the single-block align (and clears
-// `clear`, counters a later kernel of the call may use); blocks 1.. quantise
-// (mode 1).
+// one launch does both.  Block 0 runs the single-block align; blocks 1..
+// quantise (mode 1).
 __global__ __launch_bounds__(kAlignThreads) void align_quant_kernel(
     const int32_t* __restrict__ ids, int64_t F, int64_t eb, int64_t E, int64_t block_m, AlignOut o,
-    int32_t* __restrict__ clear, int32_t nclear, const uint16_t* __restrict__ x, int64_t M,
+    const uint16_t* __restrict__ x, int64_t M,
     int64_t K, int64_t ldx, uint8_t* __restrict__ q, float2* __restrict__ side,
     const float* __restrict__ fixed_scale)
 {
     __shared__ AlignLds L;
     if (blockIdx.x == 0) {
-        for (int i = threadIdx.x; i < nclear; i += kAlignThreads)
-            clear[i] = 0;
         align_single_body(ids, F, eb, E, block_m, o, L);
         return;
     }
@@ -657,15 +654,15 @@ __global__ __launch_bounds__(kAlignThreads) void align_scatter_kernel(const int3
 }
 
 hipError_t launch_align_quant(const int32_t* ids, int64_t T, int64_t topk, int64_t expert_begin,
-                              int64_t E, int64_t block_m, const AlignOut& o, int32_t* clear,
-                              int32_t nclear, const uint16_t* x, int64_t H, uint8_t* q,
+                              int64_t E, int64_t block_m, const AlignOut& o, const uint16_t* x,
+                              int64_t H, uint8_t* q,
                               float2* side, const float* fixed_scale, hipStream_t s)
 {
     const int64_t F = T * topk;
     const int64_t qblocks = (T * (H / kGroup) + 15) / 16;
     hipLaunchKernelGGL(align_quant_kernel, dim3((unsigned)(1 + qblocks)), dim3(kAlignThreads),
                        (unsigned)align_mask_bytes(E), s,
-                       ids, F, expert_begin, E, block_m, o, clear, nclear, x, T, H, H, q, side,
+                       ids, F, expert_begin, E, block_m, o, x, T, H, H, q, side,
                        fixed_scale);
     return hipGetLastError();
 }

@@ -504,8 +504,8 @@ int fused_moe_run(const void* hidden_bf16, int64_t T, int64_t H, const int32_t* 
     if (w4a8::align_chunk_count(p.F) == 1) {
         // few pairs: align and quantisation in one launch (both stage events
         // are recorded after it)
-        e = w4a8::launch_align_quant(topk_ids, T, topk, expert_begin, E, p.block_m, p.al, nullptr,
-                                     0, (const uint16_t*)hidden_bf16, H, p.qa, p.qa_side, a1_scale,
+        e = w4a8::launch_align_quant(topk_ids, T, topk, expert_begin, E, p.block_m, p.al,
+                                     (const uint16_t*)hidden_bf16, H, p.qa, p.qa_side, a1_scale,
                                      stream);
         if (e != hipSuccess)
             return W4A8_ERR_HIP;

@@ -85,11 +85,11 @@ hipError_t launch_align(const int32_t* ids, int64_t T, int64_t topk, int64_t exp
                         int64_t E, int64_t block_m, const AlignOut& o, void* ws, hipStream_t s,
                         const QuantJob& qj = QuantJob{});
 // align (single chunk: align_chunk_count(T*topk) == 1) and the mode-1
-// quantisation of x [T, H] in one launch; also zeroes clear[0, nclear)
+// quantisation of x [T, H] in one launch
 hipError_t launch_align_quant(const int32_t* ids, int64_t T, int64_t topk, int64_t expert_begin,
-                              int64_t E, int64_t block_m, const AlignOut& o, int32_t* clear,
-                              int32_t nclear, const uint16_t* x, int64_t H, uint8_t* q,
-                              float2* side, const float* fixed_scale, hipStream_t s);
+                              int64_t E, int64_t block_m, const AlignOut& o, const uint16_t* x,
+                              int64_t H, uint8_t* q, float2* side, const float* fixed_scale,
+                              hipStream_t s);
 
 // ---- grouped GEMMs (gemm_skinny.hip) ----
 struct GemmArgs {
