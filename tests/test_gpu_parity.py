@@ -379,14 +379,20 @@ def test_fused_moe_repeatable_and_workspace_reuse(dev):
 # expert, must be written by the call, and the summation counters of the
 # fused combine must be cleared by the call itself.  Two calls in a row on the
 # same buffers, the second with other routing and fewer tokens.
-@pytest.mark.parametrize("case", ["skinny16", "lists_small", "lists_large", "tile"])
+@pytest.mark.parametrize("case", ["skinny16", "lists_small", "lists_large", "tile", "chunked_tile",
+                                  "chunked_lists"])
 def test_fused_moe_poisoned_buffers(dev, case):
     # skinny16: one list of 16-row blocks; lists_small / lists_large: per-expert
-    # 16 / 32-row blocks with ~12 / ~40 pairs per local expert; tile: 160 rows
+    # 16 / 32-row blocks with ~12 / ~40 pairs per local expert; tile: 160 rows;
+    # chunked_tile / chunked_lists: more than 4096 pairs (the chunked align)
+    # with top-6 (tokens straddle the 1024-pair chunks) and 1/8 of the
+    # experts local (block-tiled / device-chosen path)
     shapes = {"skinny16": (64, 256, 128, 64, 8, 0, 32),
               "lists_small": (96, 256, 128, 32, 4, 8, 16),
               "lists_large": (160, 256, 128, 16, 4, 0, 8),
-              "tile": (512, 256, 256, 8, 2, 0, 4)}[case]
+              "tile": (512, 256, 256, 8, 2, 0, 4),
+              "chunked_tile": (1000, 256, 128, 64, 6, 8, 8),
+              "chunked_lists": (900, 256, 128, 256, 6, 0, 32)}[case]
     T, H, I, E, k, eb, El = shapes
     cfg1, d1 = synth.random_moe(T, H, I, E, k, eb, El, seed=61)
     cfg2, d2 = synth.random_moe(T - 7, H, I, E, k, eb, El, seed=62)
@@ -395,8 +401,9 @@ def test_fused_moe_poisoned_buffers(dev, case):
     ws = torch.full((need,), 0xFF, dtype=torch.uint8, device=dev)
     out = torch.full((T, H), -1, dtype=torch.int16, device=dev).view(torch.bfloat16)
     lay = w4.fused_moe_workspace_layout(T, H, k, El, I)
-    assert lay["block_m"] == {"skinny16": 16, "lists_small": 16, "lists_large": 16, "tile": 160}[case]
-    assert lay["two_lists"] == (case in ("lists_small", "lists_large"))
+    assert lay["block_m"] == {"skinny16": 16, "lists_small": 16, "lists_large": 16, "tile": 160,
+                              "chunked_tile": 160, "chunked_lists": 16}[case]
+    assert lay["two_lists"] == (case in ("lists_small", "lists_large", "chunked_lists"))
     w = [tuple(dput(d[n], dev) for n in ("w13", "s13", "w2", "s2")) for d in (d1, d2)]
     for cfg, d, wt in ((cfg1, d1, w[0]), (cfg2, d2, w[1])):
         o = out[:cfg.T]
