@@ -110,6 +110,8 @@ class Workload:
                 del w13, s13, w2, s2
             self.sets = self.psets
             self.use_packed = True
+            self.persistent = False
+            self.ws_p = None
             log("[bench] %s fp4: T=%d P=%d A=%d, %d weight set(s), inputs in %.1fs"
                 % (name, cfg.T, self.stats["P"], self.stats["A"], nsets, time.time() - t0))
             return
@@ -122,6 +124,8 @@ class Workload:
         self.psets = [lib.prepack_weights(w13, s13) + lib.prepack_weights(w2, s2)
                       for (w13, s13, w2, s2) in self.sets] if prepack else None
         self.use_packed = prepack
+        self.persistent = False  # w4a8_fused_moe_persistent (one launch after the align)
+        self.ws_p = None
         log("[bench] %s: T=%d P=%d A=%d, %d weight set(s), inputs in %.1fs"
             % (name, cfg.T, self.stats["P"], self.stats["A"], nsets, time.time() - t0))
 
@@ -133,6 +137,17 @@ class Workload:
                                  self.psets[i % len(self.psets)],
                                  lib.WEIGHTS_FP4_PACKED if self.fp4 else lib.WEIGHTS_INT4_PACKED,
                                  self.recipe, out=self.out, workspace=self.ws)
+            return
+        if self.persistent:
+            if self.ws_p is None:
+                import torch
+                fmt = lib.WEIGHTS_FP4_PACKED if self.fp4 else lib.WEIGHTS_INT4_PACKED
+                n = lib.fused_moe_persistent_workspace_bytes(cfg.T, cfg.H, cfg.topk, cfg.E_local, cfg.I, fmt)
+                self.ws_p = torch.empty(n, dtype=torch.uint8, device=self.out.device)
+            lib.fused_moe_persistent(self.hidden, self.ids, self.w, cfg.expert_begin, cfg.E_local, cfg.I,
+                                     self.psets[i % len(self.psets)],
+                                     lib.WEIGHTS_FP4_PACKED if self.fp4 else lib.WEIGHTS_INT4_PACKED,
+                                     out=self.out, workspace=self.ws_p)
             return
         if self.fp4:
             lib.fused_moe_fp4(self.hidden, self.ids, self.w, cfg.expert_begin, cfg.E_local, cfg.I,
@@ -442,11 +457,15 @@ def main():
     gpu_warmup()  # the inputs were drawn on the host meanwhile: the GPU sat idle
     us = time_steps(wl, args.steps, args.warmup)
     graph_us = graph_steps(wl, args.steps, args.warmup)
-    other_us = None
+    other_us = single_us = None
     if packed:  # the same calls on the canonical [E, N, K/2] weights, for comparison
         wl.use_packed = False
         other_us = time_steps(wl, args.steps, args.warmup)
         wl.use_packed = True
+        # and through the single-launch export (block-tiled kernels at any size)
+        wl.persistent = True
+        single_us = time_steps(wl, args.steps, min(args.warmup, 50))
+        wl.persistent = False
     # The dominant kernel of the decode step is gate_up (stage hook events
     # 2 -> 3).  Recording events costs GPU time of its own (a few µs each on
     # this stack), so its launches are timed in a second pass of the same
@@ -464,7 +483,8 @@ def main():
     log("[bench] %s: %.1f us/call (%s weights; %.1f us/call replayed from HIP graphs), stages %s"
         % (primary, us, args.layout, graph_us, {k: round(v, 1) for k, v in stages.items()}))
     if other_us is not None:
-        log("[bench] %s: %.1f us/call on the canonical weight layout" % (primary, other_us))
+        log("[bench] %s: %.1f us/call on the canonical weight layout, %.1f us/call as one launch "
+            "after the align" % (primary, other_us, single_us))
     byts, flops = moe_bytes(cfg, st), moe_flops(cfg, st)
     gb_s = byts / (us * 1e-6) / 1e9
     tflops = flops / (us * 1e-6) / 1e12
@@ -494,6 +514,7 @@ def main():
                   "the same calls replayed from HIP graphs (one captured call per weight set)",
         "graph_us": round(graph_us, 2),
         "canonical_layout_us": None if other_us is None else round(other_us, 2),
+        "single_launch_us": None if single_us is None else round(single_us, 2),
         "tflops": round(tflops, 2),
         "hbm_gbs": round(gb_s, 1),
         "roofline_frac_call": round(gb_s / HBM_PEAK_GBS, 4),
@@ -519,6 +540,9 @@ def main():
             pu = time_steps(p, steps, warm)
             pst = stage_breakdown(p, 2)
             ent = prefill_entry(p.cfg, p.stats, pu)
+            p.persistent = True  # the same calls through the single-launch export
+            ent["single_launch_us"] = round(time_steps(p, steps, warm), 2)
+            p.persistent = False
             result[name] = ent
             result[name + "_stages_us"] = {k: round(v, 1) for k, v in pst.items()}
             log("[bench] %s: %s stages %s" % (name, ent, result[name + "_stages_us"]))

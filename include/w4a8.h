@@ -369,6 +369,38 @@ int w4a8_fused_moe_bounded(const void* hidden_bf16, int64_t T, int64_t H, const 
                            void* out_bf16, void* workspace, size_t* workspace_bytes, hipStream_t stream);
 
 /*
+ * w4a8_fused_moe_persistent -- the fused forward with everything after the
+ * align in ONE kernel launch (DeepGEMM PR #53, "Changes": a single persistent
+ * kernel runs L1 GEMM -> SwiGLU -> per-token FP8 requant -> L2 GEMM ->
+ * combine).  The align with the input quantisation runs first, as in
+ * w4a8_fused_moe; then one cooperative launch of one workgroup per CU walks
+ * the block-tiled gate_up tiles (160-row m-blocks, at every T), passes a
+ * grid barrier, walks the down GEMM's tiles, passes a second barrier and
+ * sums the tokens' rows.  Each barrier is an agent-scope release (the XCD's
+ * L2 written back), an atomic arrival on a counter in the workspace (set to
+ * 0 by the align), a wait bounded to ~2 s of wall-clock time, and an
+ * agent-scope acquire.
+ *   The output is bit-identical to w4a8_fused_moe's (or the prepacked /
+ *   fp4 exports') on the block-tiled path, i.e. whenever T*topk/E_l >= 256;
+ *   below that it is the block-tiled path's result for the same inputs
+ *   (same arithmetic per element; the multi-launch exports use the skinny
+ *   kernel there).
+ *   weight_format, w13/w2 and their scales as w4a8_fused_moe_bounded; other
+ *   arguments, the workspace query (workspace == NULL) and errors as
+ *   w4a8_fused_moe; W4A8_ERR_UNSUPPORTED also for H > 2^24.  W4A8_ERR_HIP
+ *   also when the device cannot hold one workgroup per CU at once (the
+ *   cooperative launch is refused).
+ *   Calls with one workspace must not overlap (the barrier counter lives in
+ *   it); the launch cannot be captured into a HIP graph.
+ */
+int w4a8_fused_moe_persistent(const void* hidden_bf16, int64_t T, int64_t H, const int32_t* topk_ids,
+                              const float* topk_weights, int64_t topk, int64_t expert_begin,
+                              int64_t num_local_experts, int64_t I, int weight_format,
+                              const uint8_t* w13, const void* w13_scales, const uint8_t* w2,
+                              const void* w2_scales, void* out_bf16, void* workspace,
+                              size_t* workspace_bytes, hipStream_t stream);
+
+/*
  * w4a8_fused_moe_prepacked_noalloc -- w4a8_fused_moe_prepacked for callers
  * that cannot allocate device memory or pass a workspace: code recorded into
  * a HIP graph, tight serving loops, harnesses that forbid hipMalloc.  The

@@ -348,3 +348,36 @@ def test_fused_moe_bounded_range_check_uses_the_bound(L):
     assert _bounded(L, T=262144, H=128, k=8, E=32, I=2048, bound=100000, ws=None, nbytes=n) == OK
     assert _bounded(L, T=262144, H=128, k=8, E=32, I=2048, bound=1 << 21, ws=None,
                     nbytes=ctypes.c_size_t(0)) == UNSUPPORTED
+
+
+def _persistent(L, T=4, H=256, k=2, E=4, I=128, fmt=1, ws=BOGUS, nbytes=None, out=BOGUS):
+    n = ctypes.c_size_t(1 << 62) if nbytes is None else nbytes
+    return L.w4a8_fused_moe_persistent(BOGUS, T, H, BOGUS, BOGUS, k, 0, E, I, fmt, BOGUS, BOGUS,
+                                       BOGUS, BOGUS, out, ws, ctypes.byref(n), None)
+
+
+def test_fused_moe_persistent_rejects_bad_arguments(L):
+    assert _persistent(L, fmt=3) == INVALID
+    assert _persistent(L, fmt=-1) == INVALID
+    assert _persistent(L, H=200) == UNSUPPORTED
+    assert _persistent(L, k=0) == INVALID
+    assert _persistent(L, out=None) == INVALID
+    assert _persistent(L, out=MISALIGNED) == UNSUPPORTED
+    assert _persistent(L, nbytes=ctypes.c_size_t(16)) == WORKSPACE
+    assert _persistent(L, T=1, H=(1 << 24) + 128, ws=None, nbytes=ctypes.c_size_t(0)) == UNSUPPORTED
+
+
+def test_fused_moe_persistent_workspace(L):
+    """The single-launch call always runs the block-tiled kernels (160-row
+    m-blocks): its workspace is the block-tiled plan's plus the grid-barrier
+    counter, so at a shape the multi-launch call also runs tiled (T*topk/E_l
+    >= 256) it is that call's size plus one 256-byte slot, and at decode it
+    differs from the skinny plan's only in the block lists."""
+    H, k, E, I = 7168, 8, 32, 2048
+    for fmt in (0, 1, 2):
+        n = ctypes.c_size_t(0)
+        assert _persistent(L, T=4096, H=H, k=k, E=E, I=I, fmt=fmt, ws=None, nbytes=n) == OK
+        assert n.value == w4.fused_moe_workspace_bytes(4096, H, k, E, I) + 256
+    n = ctypes.c_size_t(0)
+    assert _persistent(L, T=64, H=H, k=k, E=E, I=I, ws=None, nbytes=n) == OK
+    assert abs(n.value - w4.fused_moe_workspace_bytes(64, H, k, E, I)) < (1 << 16)

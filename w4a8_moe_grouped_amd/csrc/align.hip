@@ -251,6 +251,8 @@ __device__ bool finish_scan(int* counts_lds, int* tmp_lds, int* tmp2_lds, int* t
     const int t = threadIdx.x;
     const bool dual = o.block_expert2 != nullptr;
     const bool choose = o.path != nullptr;  // also the kTileRows-row list
+    if (t == 0 && o.barrier != nullptr)
+        o.barrier[0] = 0;
     for (int e = t; e < E; e += kAlignThreads) {
         const int c = counts_lds[e];  // written out after the scans (no store pending at their barriers)
         const bool second = dual && c > o.small_rows;

@@ -157,8 +157,10 @@ struct MoePlan {
 // down_group < 128 (the finer activation recipes) runs on the skinny kernel.
 // max_pairs: the caller's bound on the local pairs (0: none).  The path and
 // block heights are chosen from the bounded count, the closer estimate.
+// persistent: the single-launch tail (block-tiled kernels at any size, plus
+// its grid-barrier counter).
 size_t plan_moe(void* ws, int64_t T, int64_t H, int64_t topk, int64_t E, int64_t I, MoePlan& p,
-                int down_group = W4A8_GROUP, int64_t max_pairs = 0)
+                int down_group = W4A8_GROUP, int64_t max_pairs = 0, bool persistent = false)
 {
     Carve c(ws);
     p.F = T * topk;
@@ -168,6 +170,9 @@ size_t plan_moe(void* ws, int64_t T, int64_t H, int64_t topk, int64_t E, int64_t
     const int64_t lists_max = ceil_div(p.cap, kSmallExpertRows) + ceil_div(p.cap, kLargeBlockRows) + 2 * E;
     if (down_group != W4A8_GROUP) {
         p.tile = p.two_lists = p.choose = false;
+    } else if (persistent) {
+        p.tile = true;
+        p.two_lists = p.choose = false;
     } else if (bounded) {
         // the counts decide above 2 rows per expert while the skinny grid stays small
         p.choose = p.cap > kBoundedTwoListRows * E && lists_max <= kChoiceMaxBlocks;
@@ -212,6 +217,7 @@ size_t plan_moe(void* ws, int64_t T, int64_t H, int64_t topk, int64_t E, int64_t
     p.al.block_row3 = p.choose ? c.take<int32_t>(p.nb3_max) : nullptr;
     p.al.num_blocks3 = p.choose ? c.take<int32_t>(1) : nullptr;
     p.al.path = p.choose ? c.take<int32_t>(1) : nullptr;
+    p.al.barrier = persistent ? c.take<int32_t>(1) : nullptr;
     return c.used;
 }
 
@@ -245,6 +251,7 @@ size_t plan_gemm(void* ws, int64_t M, int64_t K, int64_t N, float** part)
 // below 2^32.  The skinny GEMM puts m-blocks on grid.y (at most 65535).
 constexpr int64_t kRangeLimit = (int64_t)1 << 32;
 constexpr int64_t kMaxGridY = 65535;
+constexpr int64_t kMaxPersistentH = (int64_t)1 << 24;
 inline bool below_u32(int64_t bytes)
 {
     return bytes >= 0 && bytes < kRangeLimit;
@@ -459,7 +466,8 @@ int fused_moe_run(const void* hidden_bf16, int64_t T, int64_t H, const int32_t* 
                   const void* w13_scales, const uint8_t* w2_int4, const void* w2_scales,
                   void* out_bf16, void* workspace, size_t* workspace_bytes, hipStream_t stream,
                   WeightFormat format, const float* a1_scale, const float* a2_scale, int down_group,
-                  void* const* ev, int64_t max_pairs = 0, int32_t* pairs_out = nullptr)
+                  void* const* ev, int64_t max_pairs = 0, int32_t* pairs_out = nullptr,
+                  bool persistent = false)
 {
     const bool packed = format != kInt4;
     if (down_group != 128 && down_group != 64 && down_group != 32)
@@ -473,10 +481,14 @@ int fused_moe_run(const void* hidden_bf16, int64_t T, int64_t H, const int32_t* 
         E > kMaxLocalExperts || mul_sat(T, topk) > INT32_MAX / 2)
         return W4A8_ERR_UNSUPPORTED;
     MoePlan p;
-    const size_t need = plan_moe(nullptr, T, H, topk, E, I, p, down_group, max_pairs);
+    const size_t need = plan_moe(nullptr, T, H, topk, E, I, p, down_group, max_pairs, persistent);
     // 32-bit buffer ranges: the gate_up operand [T, H], the down operand
     // [cap, I] (cap = T*topk unless bounded), one expert's w13 [2I, H/2]
     if (!below_u32(mul_sat(T, H)) || !below_u32(mul_sat(p.cap, I)) || !below_u32(mul_sat(I, H)))
+        return W4A8_ERR_UNSUPPORTED;
+    // the single-launch combine counts (token, 8-column) items of a block of
+    // 64 tokens in 32 bits
+    if (persistent && H > kMaxPersistentH)
         return W4A8_ERR_UNSUPPORTED;
     if (!p.tile && (!skinny_k_ok(H, p.block_m) || !skinny_k_ok(I, p.block_m, down_group) ||
                     p.nb_max > kMaxGridY ||
@@ -496,7 +508,7 @@ int fused_moe_run(const void* hidden_bf16, int64_t T, int64_t H, const int32_t* 
         return W4A8_ERR_UNSUPPORTED;
     if (T == 0)
         return W4A8_OK;
-    plan_moe(workspace, T, H, topk, E, I, p, down_group, max_pairs);
+    plan_moe(workspace, T, H, topk, E, I, p, down_group, max_pairs, persistent);
     p.al.pairs_out = pairs_out;
 
     mark(ev, 0, stream);
@@ -552,10 +564,13 @@ int fused_moe_run(const void* hidden_bf16, int64_t T, int64_t H, const int32_t* 
     g.out_side = p.qh_side;
     g.requant_scale = a2_scale;
     g.sub_group = down_group;
-    e = launch_stage(g, p, true, stream);
-    if (e != hipSuccess)
-        return W4A8_ERR_HIP;
-    mark(ev, 3, stream);
+    const w4a8::GemmArgs gu = g;
+    if (!persistent) {
+        e = launch_stage(g, p, true, stream);
+        if (e != hipSuccess)
+            return W4A8_ERR_HIP;
+        mark(ev, 3, stream);
+    }
     // down: rows in pair order, fp8 MFMA path
     g.act = p.qh;
     g.act_rows = p.cap;
@@ -569,6 +584,18 @@ int fused_moe_run(const void* hidden_bf16, int64_t T, int64_t H, const int32_t* 
     g.K = I;
     g.N = H;
     g.out_f32 = p.y2;
+    if (persistent) {
+        // gate_up, down and combine in one launch (the stage events after it)
+        const w4a8::TailArgs tail = {p.y2, p.al.src2dst, topk_weights, T, topk, H,
+                                     (uint16_t*)out_bf16, p.al.barrier};
+        e = w4a8::launch_fused_tail(gu, g, tail, stream);
+        if (e != hipSuccess)
+            return W4A8_ERR_HIP;
+        mark(ev, 3, stream);
+        mark(ev, 4, stream);
+        mark(ev, 5, stream);
+        return W4A8_OK;
+    }
     e = launch_stage(g, p, false, stream);
     if (e != hipSuccess)
         return W4A8_ERR_HIP;
@@ -596,13 +623,13 @@ int fused_moe_impl(const void* hidden_bf16, int64_t T, int64_t H, const int32_t*
                    void* out_bf16, void* workspace, size_t* workspace_bytes, hipStream_t stream,
                    WeightFormat format, const float* a1_scale = nullptr,
                    const float* a2_scale = nullptr, int down_group = W4A8_GROUP,
-                   int64_t max_pairs = 0, int32_t* pairs_out = nullptr)
+                   int64_t max_pairs = 0, int32_t* pairs_out = nullptr, bool persistent = false)
 {
     void* const* ev = take_stage_events();
     return fused_moe_run(hidden_bf16, T, H, topk_ids, topk_weights, topk, expert_begin,
                          num_local_experts, I, w13_int4, w13_scales, w2_int4, w2_scales, out_bf16,
                          workspace, workspace_bytes, stream, format, a1_scale, a2_scale, down_group, ev,
-                         max_pairs, pairs_out);
+                         max_pairs, pairs_out, persistent);
 }
 
 }  // namespace
@@ -704,6 +731,26 @@ int w4a8_fused_moe_bounded(const void* hidden_bf16, int64_t T, int64_t H, const 
                          num_local_experts, I, w13, w13_scales, w2, w2_scales, out_bf16, workspace,
                          workspace_bytes, stream, f, nullptr, nullptr, W4A8_GROUP, ev, max_local_pairs,
                          local_pairs);
+}
+
+int w4a8_fused_moe_persistent(const void* hidden_bf16, int64_t T, int64_t H, const int32_t* topk_ids,
+                              const float* topk_weights, int64_t topk, int64_t expert_begin,
+                              int64_t num_local_experts, int64_t I, int weight_format,
+                              const uint8_t* w13, const void* w13_scales, const uint8_t* w2,
+                              const void* w2_scales, void* out_bf16, void* workspace,
+                              size_t* workspace_bytes, hipStream_t stream)
+{
+    void* const* ev = take_stage_events();  // consumed by rejected calls too
+    if (weight_format != W4A8_WEIGHTS_INT4 && weight_format != W4A8_WEIGHTS_INT4_PACKED &&
+        weight_format != W4A8_WEIGHTS_FP4_PACKED)
+        return W4A8_ERR_INVALID_ARG;
+    const WeightFormat f = weight_format == W4A8_WEIGHTS_FP4_PACKED    ? kFp4Packed
+                           : weight_format == W4A8_WEIGHTS_INT4_PACKED ? kInt4Packed
+                                                                       : kInt4;
+    return fused_moe_run(hidden_bf16, T, H, topk_ids, topk_weights, topk, expert_begin,
+                         num_local_experts, I, w13, w13_scales, w2, w2_scales, out_bf16, workspace,
+                         workspace_bytes, stream, f, nullptr, nullptr, W4A8_GROUP, ev, 0, nullptr,
+                         true);
 }
 
 int w4a8_prepack_weights(const uint8_t* w_int4, const float* w_scales, int64_t E, int64_t N,

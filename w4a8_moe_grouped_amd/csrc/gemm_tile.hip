@@ -48,6 +48,7 @@
 //                per-token FP8 requant).
 #include <type_traits>
 
+#include "w4a8.h"
 #include "common.hpp"
 #include "internal.hpp"
 #include "lds_direct.hpp"
@@ -490,12 +491,8 @@ __device__ __forceinline__ void tile_body(const GemmArgs& a, const int L, uint8_
 
 // Persistent: each workgroup walks the tiles of its XCD's range.
 template <int MODE, bool PK, bool FP4>
-__global__ __launch_bounds__(kTThreads) void gemm_tile_kernel(GemmArgs a)
+__device__ __forceinline__ void tile_phase(const GemmArgs& a, uint8_t* smem, int* s_expert)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
-    __shared__ int s_expert;
-    if (path_not_taken(a))
-        return;
     const int nbn = MODE == TILE_GATEUP ? (int)(a.I / kGroup) : (int)((a.N + kTBN - 1) / kTBN);
     const int total = *a.num_blocks * nbn;
     const int per_xcd = (total + 7) >> 3;
@@ -505,9 +502,19 @@ __global__ __launch_bounds__(kTThreads) void gemm_tile_kernel(GemmArgs a)
         const int L = x * per_xcd + t;
         if (L >= total)
             break;
-        tile_body<MODE, PK, FP4>(a, L, smem, &s_expert);
+        tile_body<MODE, PK, FP4>(a, L, smem, s_expert);
         __syncthreads();  // the next tile's loads overwrite LDS the epilogue may still read
     }
+}
+
+template <int MODE, bool PK, bool FP4>
+__global__ __launch_bounds__(kTThreads) void gemm_tile_kernel(GemmArgs a)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
+    __shared__ int s_expert;
+    if (path_not_taken(a))
+        return;
+    tile_phase<MODE, PK, FP4>(a, smem, &s_expert);
 }
 
 // ---------------------------------------------------------------------------
@@ -826,13 +833,8 @@ __device__ __forceinline__ void down_stream(const GemmArgs& a, uint8_t* smem, in
 }
 
 template <bool PK, bool FP4>
-__global__ __launch_bounds__(kTThreads) void gemm_down_stream_kernel(GemmArgs a)
+__device__ __forceinline__ void down_phase(const GemmArgs& a, uint8_t* smem, int4* s_meta, int* s_expert)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
-    __shared__ int4 s_meta[kMaxStreamTiles];
-    __shared__ int s_expert;
-    if (path_not_taken(a))
-        return;
     const int G = (int)(a.K / kGroup);
     const int nbn = (int)((a.N + kTBN - 1) / kTBN);
     const int total = *a.num_blocks * nbn;
@@ -850,9 +852,215 @@ __global__ __launch_bounds__(kTThreads) void gemm_down_stream_kernel(GemmArgs a)
         return;
     }
     for (int t = t0; t < tend; t += stride) {  // short K or very many tiles: tile by tile
-        tile_body<TILE_DOWN, PK, FP4>(a, x * per_xcd + t, smem, &s_expert);
+        tile_body<TILE_DOWN, PK, FP4>(a, x * per_xcd + t, smem, s_expert);
         __syncthreads();
     }
+}
+
+template <bool PK, bool FP4>
+__global__ __launch_bounds__(kTThreads) void gemm_down_stream_kernel(GemmArgs a)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
+    __shared__ int4 s_meta[kMaxStreamTiles];
+    __shared__ int s_expert;
+    if (path_not_taken(a))
+        return;
+    down_phase<PK, FP4>(a, smem, s_meta, &s_expert);
+}
+
+// ---------------------------------------------------------------------------
+// gate_up, down and the combine in one launch (DeepGEMM PR #53, "Changes":
+// one persistent kernel runs L1 GEMM -> SwiGLU -> FP8 requant -> L2 GEMM ->
+// combine).  One workgroup per CU, all resident at once (cooperative
+// launch), walks the gate_up tiles, the down stream and then tokens of the
+// combine exactly as the three launches do; between the phases every
+// workgroup passes a grid barrier.  The arithmetic is the launches' own, so
+// the output is bit-identical to the block-tiled path's.
+// ---------------------------------------------------------------------------
+
+// wall-clock bound of one barrier wait: s_memrealtime counts at 100 MHz
+constexpr uint64_t kBarrierTicks = 200000000ull;  // 2 s
+
+// Every workgroup arrives, then waits until `target` arrivals are counted.
+// The agent-scope release before the arrival writes this XCD's dirty L2
+// lines back, so the phase's outputs are visible to every XCD; the acquire
+// after the wait drops stale cached lines.  The other threads are ordered by
+// the workgroup barriers around thread 0's wait.  A wait longer than
+// kBarrierTicks gives up (false), so that a launch whose workgroups were not
+// all resident ends instead of spinning.
+__device__ bool grid_barrier(int32_t* counter, int target, int* s_flag)
+{
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+        int ok = 1;
+        while (__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+            if (__builtin_amdgcn_s_memrealtime() - t0 > kBarrierTicks) {
+                ok = 0;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        *s_flag = ok;
+    }
+    __syncthreads();
+    return *s_flag != 0;
+}
+
+// The combine phase.  At one workgroup per CU a thread that sums one token's
+// rows at a time waits on a chain of loads per token (slot indices, then
+// rows): measured 2.4-2.7x the combine launch's time.  Here the tokens go
+// in blocks (at most kCombineTokens, fewer when T is small, so that every
+// workgroup gets one): the block's slots and weights are read by all threads
+// at once, each token's local slots are listed in LDS in j order, and a
+// thread then takes kCombineItems (token, 8 columns) items at a time, loading
+// the rows of one slot step for all of them before the FMAs.  Per token the
+// sum is the combine launch's (local slots in j order, one FMA each, one
+// bf16 rounding).  Measured against the combine launch: 64 vs 33 us at
+// T = 4096, 340 vs 286 us on the EP8 share (prefetching the next step's rows
+// during the FMAs changed nothing).
+constexpr int kCombineTokens = 64;
+constexpr int kCombineItems = 8;
+static_assert(kCombineTokens * (1 + 4 * W4A8_MAX_TOPK) * 4 <= kSmemBytes, "combine lists exceed LDS");
+
+__device__ __forceinline__ void combine_phase(const TailArgs& t, uint8_t* smem)
+{
+    const int tid = threadIdx.x;
+    const int64_t k = t.topk, cg = t.H / 8;  // 8-column groups per token
+    const int64_t per = min((int64_t)kCombineTokens, max((int64_t)1, (t.T + gridDim.x - 1) / gridDim.x));
+    int* s_n = (int*)smem;                            // [per] local slots per token
+    int* s_p = s_n + kCombineTokens;                  // [per][k] their pair rows, in j order
+    float* s_w = (float*)(s_p + kCombineTokens * k);  // [per][k] their weights
+    int* s_raw = (int*)(s_w + kCombineTokens * k);    // [per * k] the slots as read
+    float* s_rw = (float*)(s_raw + kCombineTokens * k);  // [per * k] the weights as read
+    const int64_t nblk = (t.T + per - 1) / per;
+    for (int64_t blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
+        const int64_t t0 = blk * per;
+        const int nt = (int)min(per, t.T - t0);
+        __syncthreads();  // the previous block's lists are read
+        for (int i = tid; i < nt * k; i += kTThreads) {
+            s_raw[i] = t.src2dst[t0 * k + i];
+            s_rw[i] = t.topk_w[t0 * k + i];
+        }
+        __syncthreads();
+        if (tid < nt) {
+            int n = 0;
+            for (int64_t j = 0; j < k; ++j) {
+                const int p = s_raw[tid * k + j];
+                if (p >= 0) {
+                    s_p[tid * k + n] = p;
+                    s_w[tid * k + n] = s_rw[tid * k + j];
+                    ++n;
+                }
+            }
+            s_n[tid] = n;
+        }
+        __syncthreads();
+        // items are (token, 8 columns) pairs, columns fastest; the loads of a
+        // slot step are issued for all of a thread's items without a branch
+        // (an item past its token's local slots reads row 0 and discards it),
+        // so they are all in flight before the first FMA waits
+        const int items = nt * (int)cg;
+        for (int i0 = 0; i0 < items; i0 += kTThreads * kCombineItems) {
+            int tl[kCombineItems], n[kCombineItems], col[kCombineItems];
+            int nmax = 0;
+#pragma unroll
+            for (int u = 0; u < kCombineItems; ++u) {
+                const int i = i0 + tid + u * kTThreads;
+                const bool in = i < items;
+                tl[u] = in ? i / (int)cg : 0;
+                col[u] = in ? (i - tl[u] * (int)cg) * 8 : 0;
+                n[u] = in ? s_n[tl[u]] : -1;  // -1: no item
+                nmax = max(nmax, n[u]);
+            }
+            float acc[kCombineItems][8];
+#pragma unroll
+            for (int u = 0; u < kCombineItems; ++u)
+#pragma unroll
+                for (int c = 0; c < 8; ++c)
+                    acc[u][c] = 0.0f;
+            for (int j = 0; j < nmax; ++j) {
+                float w[kCombineItems];
+                float4 lo[kCombineItems], hi[kCombineItems];
+#pragma unroll
+                for (int u = 0; u < kCombineItems; ++u) {
+                    const bool on = j < n[u];
+                    const int slot = tl[u] * (int)k + (on ? j : 0);
+                    const int row = on ? s_p[slot] : 0;
+                    w[u] = s_w[slot];
+                    const float4* src = (const float4*)(t.y2 + (int64_t)row * t.H + col[u]);
+                    lo[u] = src[0];
+                    hi[u] = src[1];
+                }
+#pragma unroll
+                for (int u = 0; u < kCombineItems; ++u) {
+                    const bool on = j < n[u];
+                    acc[u][0] = on ? fmaf(w[u], lo[u].x, acc[u][0]) : acc[u][0];
+                    acc[u][1] = on ? fmaf(w[u], lo[u].y, acc[u][1]) : acc[u][1];
+                    acc[u][2] = on ? fmaf(w[u], lo[u].z, acc[u][2]) : acc[u][2];
+                    acc[u][3] = on ? fmaf(w[u], lo[u].w, acc[u][3]) : acc[u][3];
+                    acc[u][4] = on ? fmaf(w[u], hi[u].x, acc[u][4]) : acc[u][4];
+                    acc[u][5] = on ? fmaf(w[u], hi[u].y, acc[u][5]) : acc[u][5];
+                    acc[u][6] = on ? fmaf(w[u], hi[u].z, acc[u][6]) : acc[u][6];
+                    acc[u][7] = on ? fmaf(w[u], hi[u].w, acc[u][7]) : acc[u][7];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < kCombineItems; ++u)
+                if (n[u] >= 0) {
+                    uint4 o;
+                    o.x = (uint32_t)f32_to_bf16(acc[u][0]) | ((uint32_t)f32_to_bf16(acc[u][1]) << 16);
+                    o.y = (uint32_t)f32_to_bf16(acc[u][2]) | ((uint32_t)f32_to_bf16(acc[u][3]) << 16);
+                    o.z = (uint32_t)f32_to_bf16(acc[u][4]) | ((uint32_t)f32_to_bf16(acc[u][5]) << 16);
+                    o.w = (uint32_t)f32_to_bf16(acc[u][6]) | ((uint32_t)f32_to_bf16(acc[u][7]) << 16);
+                    *(uint4*)(t.out + (t0 + tl[u]) * t.H + col[u]) = o;
+                }
+        }
+    }
+}
+
+// The three phases' arguments are read from the kernel-argument segment at
+// the start of their phase (through a pointer the compiler cannot see
+// through), so that the down GEMM's and the combine's arguments do not sit in
+// scalar registers during gate_up: loaded at entry they pushed the kernel's
+// scalar-register spills from ~90 to ~180 and slowed both GEMM phases.
+struct FusedArgs {
+    GemmArgs gu, dn;
+    TailArgs t;
+};
+typedef __attribute__((address_space(4))) const FusedArgs* KernargPtr;
+
+__device__ __forceinline__ const FusedArgs* fused_args()
+{
+    KernargPtr p = (KernargPtr)__builtin_amdgcn_kernarg_segment_ptr();
+    asm volatile("" : "+s"(p));
+    return (const FusedArgs*)p;
+}
+
+template <bool PK, bool FP4>
+__global__ __launch_bounds__(kTThreads) void fused_tail_kernel(FusedArgs)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
+    __shared__ int4 s_meta[kMaxStreamTiles];
+    __shared__ int s_expert, s_flag;
+    const int wgs = (int)gridDim.x;
+    {
+        const GemmArgs gu = fused_args()->gu;
+        tile_phase<TILE_GATEUP, PK, FP4>(gu, smem, &s_expert);
+    }
+    if (!grid_barrier(fused_args()->t.barrier, wgs, &s_flag))
+        return;
+    {
+        const GemmArgs dn = fused_args()->dn;
+        down_phase<PK, FP4>(dn, smem, s_meta, &s_expert);
+    }
+    if (!grid_barrier(fused_args()->t.barrier, 2 * wgs, &s_flag))
+        return;
+    const TailArgs t = fused_args()->t;
+    combine_phase(t, smem);
 }
 
 int64_t tile_launch_workgroups(int64_t tiles)
@@ -864,6 +1072,30 @@ int64_t tile_launch_workgroups(int64_t tiles)
         cus = 256;
     const int64_t wgs = tiles < cus ? tiles : cus;
     return (wgs + 7) / 8 * 8;
+}
+
+hipError_t launch_fused_tail(const GemmArgs& gu, const GemmArgs& dn, const TailArgs& t, hipStream_t s)
+{
+    if ((gu.fp4 && !gu.packed) || gu.sub_group != 128 || dn.sub_group != 128)
+        return hipErrorInvalidValue;
+    const void* fn = gu.fp4      ? reinterpret_cast<const void*>(&fused_tail_kernel<true, true>)
+                     : gu.packed ? reinterpret_cast<const void*>(&fused_tail_kernel<true, false>)
+                                 : reinterpret_cast<const void*>(&fused_tail_kernel<false, false>);
+    int dev = 0, cus = 0, per_cu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess)
+        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess)
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kTThreads, 0);
+    if (e != hipSuccess)
+        return e;
+    // one workgroup per CU (the LDS stages allow no more), a multiple of the 8 XCDs
+    const int wgs = cus / 8 * 8;
+    if (per_cu < 1 || wgs < 8)
+        return hipErrorInvalidConfiguration;
+    FusedArgs fa = {gu, dn, t};
+    void* args[] = {&fa};
+    return hipLaunchCooperativeKernel(fn, dim3((unsigned)wgs), dim3(kTThreads), args, 0, s);
 }
 
 hipError_t launch_gemm_tile(const GemmArgs& a, int mode, hipStream_t s)

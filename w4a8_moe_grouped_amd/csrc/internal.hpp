@@ -68,6 +68,9 @@ struct AlignOut {
     int32_t* path;         // [1]
     int32_t static_path;
     PathCost cost;
+    // the single-launch tail's grid-barrier counter, set to 0 here (the
+    // launch after the align counts on it), or null
+    int32_t* barrier;
 };
 int64_t align_chunk_count(int64_t F);
 size_t align_workspace_bytes(int64_t F, int64_t E);
@@ -179,6 +182,20 @@ int64_t tile_launch_workgroups(int64_t tiles);
 // UE8M0 bytes) -> the prepacked layouts (common.hpp); 4-byte scale elements
 hipError_t launch_prepack(const uint8_t* w, const void* ws, int64_t E, int64_t N, int64_t K,
                           bool shuffle_nibbles, bool bf16_scales, uint8_t* wp, void* sp, hipStream_t s);
+
+// ---- single-launch tail (gemm_tile.hip) ----
+// gate_up (gu, block-tiled), down (dn, block-tiled stream) and the combine
+// in one cooperative launch of one workgroup per CU, with a grid barrier
+// between the phases on the counter `barrier` (0 at entry: the align sets it)
+struct TailArgs {
+    const float* y2;
+    const int32_t* src2dst;
+    const float* topk_w;
+    int64_t T, topk, H;
+    uint16_t* out;
+    int32_t* barrier;
+};
+hipError_t launch_fused_tail(const GemmArgs& gu, const GemmArgs& dn, const TailArgs& t, hipStream_t s);
 
 // ---- combine (combine.hip) ----
 hipError_t launch_combine(const float* y2, const int32_t* src2dst, const float* topk_w,

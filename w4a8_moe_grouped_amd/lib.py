@@ -24,7 +24,8 @@ EXPORTS = ("w4a8_version", "w4a8_status_string", "w4a8_quantize_act", "w4a8_gemm
            "w4a8_fused_moe_stage_events", "w4a8_prepack_weights", "w4a8_prepacked_scale_count",
            "w4a8_fused_moe_prepacked", "w4a8_prepack_weights_fp4", "w4a8_fused_moe_fp4_prepacked",
            "w4a8_prepack_weights_bf16_scales", "w4a8_fused_moe_prepacked_static",
-           "w4a8_fused_moe_recipe", "w4a8_fused_moe_prepacked_noalloc", "w4a8_fused_moe_bounded")
+           "w4a8_fused_moe_recipe", "w4a8_fused_moe_prepacked_noalloc", "w4a8_fused_moe_bounded",
+           "w4a8_fused_moe_persistent")
 
 _lock = threading.Lock()
 _lib = None
@@ -73,6 +74,9 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         L.w4a8_fused_moe_recipe.restype = ctypes.c_int
         L.w4a8_fused_moe_recipe.argtypes = [vp, i64, i64, vp, vp, i64, i64, i64, i64, ctypes.c_int,
                                             vp, vp, vp, vp, ctypes.c_int, vp, vp, sz, vp]
+        L.w4a8_fused_moe_persistent.restype = ctypes.c_int
+        L.w4a8_fused_moe_persistent.argtypes = [vp, i64, i64, vp, vp, i64, i64, i64, i64, ctypes.c_int,
+                                                vp, vp, vp, vp, vp, vp, sz, vp]
         L.w4a8_fused_moe_bounded.restype = ctypes.c_int
         L.w4a8_fused_moe_bounded.argtypes = [vp, i64, i64, vp, vp, i64, i64, i64, i64, ctypes.c_int,
                                              vp, vp, vp, vp, i64, vp, vp, vp, sz, vp]
@@ -309,6 +313,47 @@ def fused_moe_bounded(hidden: torch.Tensor, topk_ids: torch.Tensor, topk_weights
         _ptr(local_pairs), _ptr(out), _ptr(workspace), ctypes.byref(n), _stream(hidden.device)),
         "w4a8_fused_moe_bounded")
     return out, local_pairs
+
+
+def fused_moe_persistent_workspace_bytes(T: int, H: int, topk: int, num_local_experts: int, I: int,
+                                         weight_format: int = WEIGHTS_INT4_PACKED) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load().w4a8_fused_moe_persistent(None, T, H, None, None, topk, 0, num_local_experts, I,
+                                            int(weight_format), None, None, None, None, None, None,
+                                            ctypes.byref(n), None),
+           "w4a8_fused_moe_persistent(query)")
+    return n.value
+
+
+def fused_moe_persistent(hidden: torch.Tensor, topk_ids: torch.Tensor, topk_weights: torch.Tensor,
+                         expert_begin: int, num_local_experts: int, I: int, weights: tuple,
+                         weight_format: int, out: Optional[torch.Tensor] = None,
+                         workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """w4a8_fused_moe_persistent: the align launch, then gate_up, down and
+    the combine in one cooperative launch.  weights = (w13, s13, w2, s2) in
+    the layout weight_format names."""
+    w13, s13, w2, s2 = weights
+    _need_cuda(hidden, topk_ids, topk_weights, w13, s13, w2, s2)
+    T, H = hidden.shape
+    k = topk_ids.shape[1]
+    E = num_local_experts
+    assert hidden.dtype == torch.bfloat16 and topk_ids.dtype == torch.int32 \
+        and topk_weights.dtype == torch.float32
+    assert topk_ids.shape == (T, k) and topk_weights.shape == (T, k)
+    assert w13.numel() == E * 2 * I * H // 2 and w2.numel() == E * H * I // 2
+    for t in (hidden, topk_ids, topk_weights, w13, s13, w2, s2):
+        assert t.is_contiguous()
+    out = out if out is not None else torch.empty((T, H), dtype=torch.bfloat16, device=hidden.device)
+    if workspace is None:
+        need = fused_moe_persistent_workspace_bytes(T, H, k, E, I, weight_format)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=hidden.device)
+    n = ctypes.c_size_t(workspace.numel())
+    _check(load().w4a8_fused_moe_persistent(
+        _ptr(hidden), T, H, _ptr(topk_ids), _ptr(topk_weights), k, expert_begin, E, I,
+        int(weight_format), _ptr(w13), _ptr(s13), _ptr(w2), _ptr(s2), _ptr(out), _ptr(workspace),
+        ctypes.byref(n), _stream(hidden.device)),
+        "w4a8_fused_moe_persistent")
+    return out
 
 
 def fused_moe_recipe(hidden: torch.Tensor, topk_ids: torch.Tensor, topk_weights: torch.Tensor,
