@@ -910,114 +910,72 @@ __device__ bool grid_barrier(int32_t* counter, int target, int* s_flag)
     return *s_flag != 0;
 }
 
-// The combine phase.  At one workgroup per CU a thread that sums one token's
-// rows at a time waits on a chain of loads per token (slot indices, then
-// rows): measured 2.4-2.7x the combine launch's time.  Here the tokens go
-// in blocks (at most kCombineTokens, fewer when T is small, so that every
-// workgroup gets one): the block's slots and weights are read by all threads
-// at once, each token's local slots are listed in LDS in j order, and a
-// thread then takes kCombineItems (token, 8 columns) items at a time, loading
-// the rows of one slot step for all of them before the FMAs.  Per token the
-// sum is the combine launch's (local slots in j order, one FMA each, one
-// bf16 rounding).  Measured against the combine launch: 64 vs 33 us at
-// T = 4096, 340 vs 286 us on the EP8 share (prefetching the next step's rows
-// during the FMAs changed nothing).
-constexpr int kCombineTokens = 64;
-constexpr int kCombineItems = 8;
-static_assert(kCombineTokens * (1 + 4 * W4A8_MAX_TOPK) * 4 <= kSmemBytes, "combine lists exceed LDS");
+// The combine phase, one token per wave.  The token's slots are read by the
+// wave's first topk lanes; the local ones (a ballot) are walked in j order as
+// a wave-uniform list; each lane owns 8 columns of every 512-column stripe,
+// and the wave takes kCombineStripes stripes at a time, so that a lane has
+// 2 * kCombineStripes row loads in flight per local slot, each wave load
+// covering 2 KB of one row.  Per token the sum is the combine launch's (local
+// slots in j order, one FMA each from +0, one bf16 rounding).  Measured
+// against the combine launch: 54 vs 31 us at T = 4096, 322 vs 287 us on the
+// EP8 share (at one workgroup per CU; a thread per (token, 8 columns) item
+// with the slots listed in LDS reached 64 / 340 us).
+constexpr int kCombineStripes = 8;
+static_assert(W4A8_MAX_TOPK <= 64, "a token's slots fit one wave");
 
-__device__ __forceinline__ void combine_phase(const TailArgs& t, uint8_t* smem)
+__device__ __forceinline__ void combine_phase(const TailArgs& t)
 {
-    const int tid = threadIdx.x;
-    const int64_t k = t.topk, cg = t.H / 8;  // 8-column groups per token
-    const int64_t per = min((int64_t)kCombineTokens, max((int64_t)1, (t.T + gridDim.x - 1) / gridDim.x));
-    int* s_n = (int*)smem;                            // [per] local slots per token
-    int* s_p = s_n + kCombineTokens;                  // [per][k] their pair rows, in j order
-    float* s_w = (float*)(s_p + kCombineTokens * k);  // [per][k] their weights
-    int* s_raw = (int*)(s_w + kCombineTokens * k);    // [per * k] the slots as read
-    float* s_rw = (float*)(s_raw + kCombineTokens * k);  // [per * k] the weights as read
-    const int64_t nblk = (t.T + per - 1) / per;
-    for (int64_t blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
-        const int64_t t0 = blk * per;
-        const int nt = (int)min(per, t.T - t0);
-        __syncthreads();  // the previous block's lists are read
-        for (int i = tid; i < nt * k; i += kTThreads) {
-            s_raw[i] = t.src2dst[t0 * k + i];
-            s_rw[i] = t.topk_w[t0 * k + i];
-        }
-        __syncthreads();
-        if (tid < nt) {
-            int n = 0;
-            for (int64_t j = 0; j < k; ++j) {
-                const int p = s_raw[tid * k + j];
-                if (p >= 0) {
-                    s_p[tid * k + n] = p;
-                    s_w[tid * k + n] = s_rw[tid * k + j];
-                    ++n;
-                }
-            }
-            s_n[tid] = n;
-        }
-        __syncthreads();
-        // items are (token, 8 columns) pairs, columns fastest; the loads of a
-        // slot step are issued for all of a thread's items without a branch
-        // (an item past its token's local slots reads row 0 and discards it),
-        // so they are all in flight before the first FMA waits
-        const int items = nt * (int)cg;
-        for (int i0 = 0; i0 < items; i0 += kTThreads * kCombineItems) {
-            int tl[kCombineItems], n[kCombineItems], col[kCombineItems];
-            int nmax = 0;
+    const int lane = threadIdx.x & 63;
+    const int waves = kTThreads / 64;
+    const int64_t k = t.topk, H = t.H;
+    const int64_t stride = (int64_t)gridDim.x * waves;
+    for (int64_t tok = (int64_t)blockIdx.x * waves + (threadIdx.x >> 6); tok < t.T; tok += stride) {
+        const int p_l = lane < k ? t.src2dst[tok * k + lane] : -1;
+        const float w_l = lane < k ? t.topk_w[tok * k + lane] : 0.0f;
+        const uint64_t local = __ballot(p_l >= 0);  // bit j: slot j is local
+        for (int64_t c0 = (int64_t)lane * 8; c0 < H; c0 += 512 * kCombineStripes) {
+            float acc[kCombineStripes][8];
 #pragma unroll
-            for (int u = 0; u < kCombineItems; ++u) {
-                const int i = i0 + tid + u * kTThreads;
-                const bool in = i < items;
-                tl[u] = in ? i / (int)cg : 0;
-                col[u] = in ? (i - tl[u] * (int)cg) * 8 : 0;
-                n[u] = in ? s_n[tl[u]] : -1;  // -1: no item
-                nmax = max(nmax, n[u]);
-            }
-            float acc[kCombineItems][8];
-#pragma unroll
-            for (int u = 0; u < kCombineItems; ++u)
+            for (int s = 0; s < kCombineStripes; ++s)
 #pragma unroll
                 for (int c = 0; c < 8; ++c)
-                    acc[u][c] = 0.0f;
-            for (int j = 0; j < nmax; ++j) {
-                float w[kCombineItems];
-                float4 lo[kCombineItems], hi[kCombineItems];
+                    acc[s][c] = 0.0f;
+            for (uint64_t m = local; m != 0; m &= m - 1) {
+                const int j = __builtin_ctzll(m);  // ascending j
+                const int64_t p = __shfl(p_l, j, 64);
+                const float w = __shfl(w_l, j, 64);
+                float4 lo[kCombineStripes], hi[kCombineStripes];
 #pragma unroll
-                for (int u = 0; u < kCombineItems; ++u) {
-                    const bool on = j < n[u];
-                    const int slot = tl[u] * (int)k + (on ? j : 0);
-                    const int row = on ? s_p[slot] : 0;
-                    w[u] = s_w[slot];
-                    const float4* src = (const float4*)(t.y2 + (int64_t)row * t.H + col[u]);
-                    lo[u] = src[0];
-                    hi[u] = src[1];
+                for (int s = 0; s < kCombineStripes; ++s) {
+                    const int64_t col = c0 + s * 512;
+                    const float4* src = (const float4*)(t.y2 + p * H + (col < H ? col : 0));
+                    lo[s] = src[0];
+                    hi[s] = src[1];
                 }
 #pragma unroll
-                for (int u = 0; u < kCombineItems; ++u) {
-                    const bool on = j < n[u];
-                    acc[u][0] = on ? fmaf(w[u], lo[u].x, acc[u][0]) : acc[u][0];
-                    acc[u][1] = on ? fmaf(w[u], lo[u].y, acc[u][1]) : acc[u][1];
-                    acc[u][2] = on ? fmaf(w[u], lo[u].z, acc[u][2]) : acc[u][2];
-                    acc[u][3] = on ? fmaf(w[u], lo[u].w, acc[u][3]) : acc[u][3];
-                    acc[u][4] = on ? fmaf(w[u], hi[u].x, acc[u][4]) : acc[u][4];
-                    acc[u][5] = on ? fmaf(w[u], hi[u].y, acc[u][5]) : acc[u][5];
-                    acc[u][6] = on ? fmaf(w[u], hi[u].z, acc[u][6]) : acc[u][6];
-                    acc[u][7] = on ? fmaf(w[u], hi[u].w, acc[u][7]) : acc[u][7];
+                for (int s = 0; s < kCombineStripes; ++s) {
+                    acc[s][0] = fmaf(w, lo[s].x, acc[s][0]);
+                    acc[s][1] = fmaf(w, lo[s].y, acc[s][1]);
+                    acc[s][2] = fmaf(w, lo[s].z, acc[s][2]);
+                    acc[s][3] = fmaf(w, lo[s].w, acc[s][3]);
+                    acc[s][4] = fmaf(w, hi[s].x, acc[s][4]);
+                    acc[s][5] = fmaf(w, hi[s].y, acc[s][5]);
+                    acc[s][6] = fmaf(w, hi[s].z, acc[s][6]);
+                    acc[s][7] = fmaf(w, hi[s].w, acc[s][7]);
                 }
             }
 #pragma unroll
-            for (int u = 0; u < kCombineItems; ++u)
-                if (n[u] >= 0) {
+            for (int s = 0; s < kCombineStripes; ++s) {
+                const int64_t col = c0 + s * 512;
+                if (col < H) {
                     uint4 o;
-                    o.x = (uint32_t)f32_to_bf16(acc[u][0]) | ((uint32_t)f32_to_bf16(acc[u][1]) << 16);
-                    o.y = (uint32_t)f32_to_bf16(acc[u][2]) | ((uint32_t)f32_to_bf16(acc[u][3]) << 16);
-                    o.z = (uint32_t)f32_to_bf16(acc[u][4]) | ((uint32_t)f32_to_bf16(acc[u][5]) << 16);
-                    o.w = (uint32_t)f32_to_bf16(acc[u][6]) | ((uint32_t)f32_to_bf16(acc[u][7]) << 16);
-                    *(uint4*)(t.out + (t0 + tl[u]) * t.H + col[u]) = o;
+                    o.x = (uint32_t)f32_to_bf16(acc[s][0]) | ((uint32_t)f32_to_bf16(acc[s][1]) << 16);
+                    o.y = (uint32_t)f32_to_bf16(acc[s][2]) | ((uint32_t)f32_to_bf16(acc[s][3]) << 16);
+                    o.z = (uint32_t)f32_to_bf16(acc[s][4]) | ((uint32_t)f32_to_bf16(acc[s][5]) << 16);
+                    o.w = (uint32_t)f32_to_bf16(acc[s][6]) | ((uint32_t)f32_to_bf16(acc[s][7]) << 16);
+                    *(uint4*)(t.out + tok * H + col) = o;
                 }
+            }
         }
     }
 }
@@ -1060,7 +1018,7 @@ __global__ __launch_bounds__(kTThreads) void fused_tail_kernel(FusedArgs)
     if (!grid_barrier(fused_args()->t.barrier, 2 * wgs, &s_flag))
         return;
     const TailArgs t = fused_args()->t;
-    combine_phase(t, smem);
+    combine_phase(t);
 }
 
 int64_t tile_launch_workgroups(int64_t tiles)
