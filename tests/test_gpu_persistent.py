@@ -105,6 +105,9 @@ SMALL = {
     "ragged": (700, 384, 256, 5, 2, 1, 3, 82),
     "one_expert": (300, 256, 128, 8, 3, 5, 1, 83),
     "many_pairs": (1500, 256, 128, 16, 4, 0, 8, 84),  # > 4096 pairs: the chunked align
+    # H = 128 with top-32: a token's 32 slots sit in lanes the narrow column
+    # loop leaves without columns (the combine phase's shuffles read them)
+    "h128_top32": (160, 128, 128, 64, 32, 0, 32, 85),
 }
 
 

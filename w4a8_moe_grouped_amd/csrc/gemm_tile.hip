@@ -933,7 +933,10 @@ __device__ __forceinline__ void combine_phase(const TailArgs& t)
         const int p_l = lane < k ? t.src2dst[tok * k + lane] : -1;
         const float w_l = lane < k ? t.topk_w[tok * k + lane] : 0.0f;
         const uint64_t local = __ballot(p_l >= 0);  // bit j: slot j is local
-        for (int64_t c0 = (int64_t)lane * 8; c0 < H; c0 += 512 * kCombineStripes) {
+        // the column loop is wave-uniform (every lane takes part in the
+        // shuffles below; a lane past H loads column 0 and stores nothing)
+        for (int64_t cb = 0; cb < H; cb += 512 * kCombineStripes) {
+            const int64_t c0 = cb + (int64_t)lane * 8;
             float acc[kCombineStripes][8];
 #pragma unroll
             for (int s = 0; s < kCombineStripes; ++s)
