@@ -379,7 +379,10 @@ int w4a8_fused_moe_bounded(const void* hidden_bf16, int64_t T, int64_t H, const 
  * sums the tokens' rows.  Each barrier is an agent-scope release (the XCD's
  * L2 written back), an atomic arrival on a counter in the workspace (set to
  * 0 by the align), a wait bounded to ~2 s of wall-clock time, and an
- * agent-scope acquire.
+ * agent-scope acquire.  (The bound only guarantees that the launch ends: all
+ * workgroups are resident under the cooperative launch, so no wait comes
+ * near it; were one to pass it, the launch would end without writing the
+ * rest of the output.)
  *   The output is bit-identical to w4a8_fused_moe's (or the prepacked /
  *   fp4 exports') on the block-tiled path, i.e. whenever T*topk/E_l >= 256;
  *   below that it is the block-tiled path's result for the same inputs
