@@ -872,10 +872,10 @@ __global__ __launch_bounds__(kTThreads) void gemm_down_stream_kernel(GemmArgs a)
 // gate_up, down and the combine in one launch (DeepGEMM PR #53, "Changes":
 // one persistent kernel runs L1 GEMM -> SwiGLU -> FP8 requant -> L2 GEMM ->
 // combine).  One workgroup per CU, all resident at once (cooperative
-// launch), walks the gate_up tiles, the down stream and then tokens of the
-// combine exactly as the three launches do; between the phases every
-// workgroup passes a grid barrier.  The arithmetic is the launches' own, so
-// the output is bit-identical to the block-tiled path's.
+// launch), walks the gate_up tiles and the down stream exactly as their
+// launches do, then the combine's tokens (one per wave, below); between the
+// phases every workgroup passes a grid barrier.  The arithmetic is the
+// launches' own, so the output is bit-identical to the block-tiled path's.
 // ---------------------------------------------------------------------------
 
 // wall-clock bound of one barrier wait: s_memrealtime counts at 100 MHz
