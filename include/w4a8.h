@@ -394,7 +394,8 @@ int w4a8_fused_moe_bounded(const void* hidden_bf16, int64_t T, int64_t H, const 
  *   also when the device cannot hold one workgroup per CU at once (the
  *   cooperative launch is refused).
  *   Calls with one workspace must not overlap (the barrier counter lives in
- *   it); the launch cannot be captured into a HIP graph.
+ *   it).  The call records into a HIP graph like the other exports (the
+ *   align clears the counter on every replay).
  */
 int w4a8_fused_moe_persistent(const void* hidden_bf16, int64_t T, int64_t H, const int32_t* topk_ids,
                               const float* topk_weights, int64_t topk, int64_t expert_begin,
