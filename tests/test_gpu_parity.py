@@ -417,3 +417,24 @@ def test_fused_moe_poisoned_buffers(dev, case):
         none_local = ~np.any((ids >= cfg.expert_begin) & (ids < cfg.expert_begin + cfg.E_local), axis=1)
         assert np.all(got[none_local] == 0), case
         assert_bf16_close(got, ref, case)
+
+
+# Many local experts (beyond the align's 256 threads per pass): 600 local
+# experts with ~40 pairs each take the device-chosen path (the align sums the
+# cost of every expert's tiles over several passes), 1024 (the largest E_l)
+# the two skinny lists; every token is compared.
+@pytest.mark.parametrize("E", [600, 1024])
+def test_fused_moe_many_local_experts(dev, E):
+    cfg, d = synth.random_moe(3000, 256, 128, E, 8, 0, E, seed=121)
+    lay = w4.fused_moe_workspace_layout(cfg.T, cfg.H, cfg.topk, cfg.E_local, cfg.I)
+    assert lay["two_lists"] and lay["device_path"] == (E == 600), lay
+    need = w4.fused_moe_workspace_bytes(cfg.T, cfg.H, cfg.topk, cfg.E_local, cfg.I)
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device=dev)
+    out = torch.full((cfg.T, cfg.H), -1, dtype=torch.int16, device=dev).view(torch.bfloat16)
+    w4.fused_moe(bf16_dev(d["hidden"], dev), dput(d["topk_ids"], dev), dput(d["topk_weights"], dev),
+                 cfg.expert_begin, cfg.E_local, dput(d["w13"], dev), dput(d["s13"], dev),
+                 dput(d["w2"], dev), dput(d["s2"], dev), out=out, workspace=ws)
+    torch.cuda.synchronize()
+    got = bf16_host(out)
+    ref = oracle_rows_parallel(d, cfg, np.arange(cfg.T))
+    assert_bf16_close(got, ref, "E_l=%d" % E)

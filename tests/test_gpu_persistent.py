@@ -108,6 +108,8 @@ SMALL = {
     # H = 128 with top-32: a token's 32 slots sit in lanes the narrow column
     # loop leaves without columns (the combine phase's shuffles read them)
     "h128_top32": (160, 128, 128, 64, 32, 0, 32, 85),
+    # the largest E_l: 1024 experts of ~16 rows, one mostly empty m-block each
+    "many_experts": (2000, 256, 128, 1024, 8, 0, 1024, 86),
 }
 
 
